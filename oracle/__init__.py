@@ -1,0 +1,227 @@
+"""CPU oracle for the CSA / HCA hybrid compressed attention path.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+baseline leg of the benchmark may import this package.  It shares no code with
+the HIP library and never imports it.
+
+The arithmetic lives in ``csa_oracle.c`` (plain loops, fp64 accumulation);
+this module builds it with gcc, loads it with ctypes and marshals numpy
+arrays.  Every input is converted to float64 first, which is exact for bf16 and
+fp32 values.
+
+Pinning status (what checks each function against the pages or mathematics,
+see tests/test_oracle_*.py):
+  num_entries / num_visible   pinned (counts from the pages, the Block-24 example)
+  compress                    pinned (mean pooling, identity, convexity, shift
+                              invariance, scipy softmax brute force, two-path
+                              causality); the two-path bias row layout is a
+                              convention: parity unpinned for the bias layout
+  index_scores                pinned (the 8 / -7 ReLU example, brute force via
+                              numpy einsum); absence of a scale: parity unpinned
+  topk                        pinned (O(L^2) rank-count brute force, ties, +-0)
+  sparse_attn / dense_attn    pinned (torch SDPA textbook MQA incl. sink as an
+                              extra logit, one-hot probability mass, sink limits,
+                              the 0.15 / 0.85 example, order invariance)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "csa_oracle.c")
+_LIB = os.path.join(_HERE, "libcsa_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_d = ctypes.POINTER(ctypes.c_double)
+_i64 = ctypes.c_int64
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, IEEE fp64, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB)
+            lib.oracle_num_entries.restype = _i64
+            lib.oracle_num_entries.argtypes = [_i64, _i64]
+            lib.oracle_num_visible.restype = _i64
+            lib.oracle_num_visible.argtypes = [_i64, _i64]
+            lib.oracle_compress.restype = ctypes.c_int
+            lib.oracle_compress.argtypes = [_d, _d, _d, _d, _d] + [_i64] * 8 + [_d]
+            lib.oracle_index_scores.restype = None
+            lib.oracle_index_scores.argtypes = [_d, _d, _d, _i64, _i64,
+                                                ctypes.POINTER(_i64), _i64, _i64,
+                                                _i64, _i64, _d]
+            lib.oracle_topk.restype = None
+            lib.oracle_topk.argtypes = [_d, ctypes.POINTER(_i64), _i64, _i64, _i64,
+                                        ctypes.POINTER(ctypes.c_int32)]
+            lib.oracle_sparse_attn.restype = ctypes.c_int
+            lib.oracle_sparse_attn.argtypes = [
+                _d, _d, _d, _i64, ctypes.POINTER(ctypes.c_int32), _i64, _d, _d, _i64,
+                _i64, _d, ctypes.c_double, _i64, _i64, ctypes.POINTER(_i64), _i64,
+                _i64, _i64, _d, _d]
+            lib.oracle_dense_attn.restype = ctypes.c_int
+            lib.oracle_dense_attn.argtypes = [
+                _d, _d, _d, _i64, _i64, _d, _d, _i64, _i64, _d, ctypes.c_double,
+                _i64, _i64, ctypes.POINTER(_i64), _i64, _i64, _i64, _d, _d]
+            _lib = lib
+    return _lib
+
+
+def _f64(a):
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor on the CPU
+        a = a.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(_d)
+
+
+def num_entries(n: int, m: int) -> int:
+    return int(_load().oracle_num_entries(n, m))
+
+
+def num_visible(t: int, m: int) -> int:
+    return int(_load().oracle_num_visible(t, m))
+
+
+def compress(x_a, z_a, m, *, x_b=None, z_b=None, bias=None, n=None, p0=0,
+             e0=0, e1=None):
+    """Block-weighted compression; arrays [B][n_raw][D] for positions p0...
+
+    Returns float64 [B][e1-e0][D]."""
+    x_a, z_a, x_b, z_b, bias = map(_f64, (x_a, z_a, x_b, z_b, bias))
+    B, n_raw, D = x_a.shape
+    if n is None:
+        n = p0 + n_raw
+    if e1 is None:
+        e1 = num_entries(n, m)
+    if (x_b is None) != (z_b is None):
+        raise ValueError("x_b and z_b go together")
+    out = np.zeros((B, e1 - e0, D), dtype=np.float64)
+    rc = _load().oracle_compress(_p(x_a), _p(z_a), _p(x_b), _p(z_b), _p(bias), B, n,
+                                 D, m, p0, n_raw, e0, e1, _p(out))
+    if rc != 0:
+        raise ValueError("oracle_compress: raw rows do not cover the entries (%d)" % rc)
+    return out
+
+
+def _tpos(T, n_ctx, tpos):
+    if tpos is None:
+        tpos = np.arange(n_ctx - T, n_ctx, dtype=np.int64)
+    return np.ascontiguousarray(np.asarray(tpos, dtype=np.int64))
+
+
+def index_scores(q_idx, k_idx, m, *, w=None, n_ctx=None, tpos=None):
+    """Indexer scores float64 [B][T][L]; invisible entries are -inf."""
+    q_idx, k_idx, w = map(_f64, (q_idx, k_idx, w))
+    B, T, HI, dI = q_idx.shape
+    L = k_idx.shape[1]
+    tp = _tpos(T, n_ctx, tpos)
+    out = np.empty((B, T, L), dtype=np.float64)
+    _load().oracle_index_scores(_p(q_idx), _p(w), _p(k_idx), B, T,
+                                tp.ctypes.data_as(ctypes.POINTER(_i64)), L, HI, dI, m,
+                                _p(out))
+    return out
+
+
+def topk(scores, nvis, k):
+    """Top-k per row of scores [..., L] over the first nvis entries.
+
+    Returns int32 [..., k], ascending indices, -1 padded."""
+    s = _f64(scores)
+    lead = s.shape[:-1]
+    L = s.shape[-1]
+    R = int(np.prod(lead)) if lead else 1
+    nv = np.ascontiguousarray(np.broadcast_to(np.asarray(nvis, dtype=np.int64), lead).reshape(-1))
+    if np.isnan(s).any():
+        raise ValueError("scores contain NaN")
+    out = np.empty((R, k), dtype=np.int32)
+    _load().oracle_topk(_p(s.reshape(R, L)), nv.ctypes.data_as(ctypes.POINTER(_i64)), R, L,
+                        k, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    return out.reshape(lead + (k,))
+
+
+def index_topk(q_idx, k_idx, m, k, *, w=None, n_ctx=None, tpos=None):
+    """Scores then selection; returns (idx int32 [B][T][k], scores float64 [B][T][L])."""
+    q = _f64(q_idx)
+    T = q.shape[1]
+    tp = _tpos(T, n_ctx, tpos)
+    sc = index_scores(q, k_idx, m, w=w, n_ctx=n_ctx, tpos=tp)
+    L = sc.shape[-1]
+    nv = np.minimum(tp // m, L)
+    idx = topk(sc, np.broadcast_to(nv, sc.shape[:-1]), k)
+    return idx, sc
+
+
+def sparse_attn(q, kc, vc, idx, kr, vr, W, *, sink=None, scale=None, n_ctx=None,
+                tpos=None):
+    """CSA attention; returns (out float64 [B][T][H][d], lse float64 [B][T][H])."""
+    q, kc, vc, kr, vr, sink = map(_f64, (q, kc, vc, kr, vr, sink))
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+    B, T, H, d = q.shape
+    L = kc.shape[1]
+    R = 0 if kr is None else kr.shape[1]
+    if kr is None:
+        kr = vr = np.zeros((B, 1, d))
+    k = idx.shape[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    if n_ctx is None:
+        raise ValueError("n_ctx is required")
+    tp = _tpos(T, n_ctx, tpos)
+    out = np.zeros((B, T, H, d))
+    lse = np.zeros((B, T, H))
+    rc = _load().oracle_sparse_attn(_p(q), _p(kc), _p(vc), L,
+                                    idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), k,
+                                    _p(kr), _p(vr), R, W, _p(sink), float(scale), B, T,
+                                    tp.ctypes.data_as(ctypes.POINTER(_i64)), n_ctx, H, d,
+                                    _p(out), _p(lse))
+    if rc != 0:
+        raise ValueError("oracle_sparse_attn: bad index or window position")
+    return out, lse
+
+
+def dense_attn(q, kc, vc, m, kr, vr, W, *, sink=None, scale=None, n_ctx=None,
+               tpos=None):
+    """HCA attention; returns (out float64 [B][T][H][d], lse float64 [B][T][H])."""
+    q, kc, vc, kr, vr, sink = map(_f64, (q, kc, vc, kr, vr, sink))
+    B, T, H, d = q.shape
+    L = kc.shape[1]
+    R = 0 if kr is None else kr.shape[1]
+    if kr is None:
+        kr = vr = np.zeros((B, 1, d))
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    if n_ctx is None:
+        raise ValueError("n_ctx is required")
+    tp = _tpos(T, n_ctx, tpos)
+    out = np.zeros((B, T, H, d))
+    lse = np.zeros((B, T, H))
+    rc = _load().oracle_dense_attn(_p(q), _p(kc), _p(vc), L, m, _p(kr), _p(vr), R, W,
+                                   _p(sink), float(scale), B, T,
+                                   tp.ctypes.data_as(ctypes.POINTER(_i64)), n_ctx, H, d,
+                                   _p(out), _p(lse))
+    if rc != 0:
+        raise ValueError("oracle_dense_attn: bad window position")
+    return out, lse
