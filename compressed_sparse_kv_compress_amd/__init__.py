@@ -1,0 +1,245 @@
+"""MI355X (gfx950) hybrid compressed attention: CSA and HCA hot path.
+
+A thin Python binding over the C ABI in ``include/csa.h`` (libcsa.so): it only
+marshals arguments.  Tensors are torch device tensors used as memory; every
+step of the computation runs in the HIP kernels.  If libcsa.so has not been
+built, importing this package raises: there is no fallback.
+
+Functions mirror the C entry points: csa_compress, hca_compress,
+csa_index_score, csa_topk_select, csa_index_topk, csa_sparse_attn and
+hca_dense_attn.  Outputs and workspaces are allocated with torch on the
+inputs' device unless passed in; work is enqueued on the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libcsa.so is not built: run `python -m compressed_sparse_kv_compress_amd.build` "
+        "(the HIP library is the only implementation)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+CSA_F32, CSA_BF16 = 0, 1
+_STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED",
+           3: "CSA_ERR_WORKSPACE", 4: "CSA_ERR_HIP"}
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+_i32 = ctypes.c_int
+_f32 = ctypes.c_float
+
+
+def _sig(name, args, res=_i32):
+    fn = getattr(_lib, name)
+    fn.argtypes = args
+    fn.restype = res
+    return fn
+
+
+_csa_compress = _sig("csa_compress", [_vp] * 6 + [_i64] * 9 + [_i32, _vp])
+_hca_compress = _sig("hca_compress", [_vp] * 4 + [_i64] * 9 + [_i32, _vp])
+_csa_index_score = _sig("csa_index_score", [_vp] * 3 + [_i64] * 7 + [_vp, _i32, _vp])
+_csa_topk_select = _sig("csa_topk_select", [_vp] + [_i64] * 6 + [_vp, _vp, _vp])
+_csa_index_topk_workspace = _sig("csa_index_topk_workspace", [_i64] * 3, _sz)
+_csa_index_topk = _sig("csa_index_topk", [_vp] * 3 + [_i64] * 8 + [_vp, _vp, _vp, _sz, _i32, _vp])
+_csa_sparse_attn_workspace = _sig("csa_sparse_attn_workspace", [_i64] * 6 + [_i32], _sz)
+_csa_sparse_attn = _sig("csa_sparse_attn", [_vp] * 3 + [_i64, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _f32]
+                        + [_i64] * 5 + [_vp, _vp, _vp, _sz, _i32, _vp])
+_hca_dense_attn_workspace = _sig("hca_dense_attn_workspace", [_i64] * 8 + [_i32], _sz)
+_hca_dense_attn = _sig("hca_dense_attn", [_vp] * 3 + [_i64, _i64, _vp, _vp, _i64, _i64, _vp, _f32]
+                       + [_i64] * 5 + [_vp, _vp, _vp, _sz, _i32, _vp])
+_csa_status_string = _sig("csa_status_string", [_i32], ctypes.c_char_p)
+_csa_last_error = _sig("csa_last_error", [], ctypes.c_char_p)
+
+
+class CsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        detail = _csa_last_error().decode(errors="replace")
+        super().__init__("%s: %s (%s)" % (where, _STATUS.get(status, status), detail))
+
+
+def _check(st, where):
+    if st != 0:
+        raise CsaError(st, where)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    if t.dtype == torch.float32:
+        return CSA_F32
+    raise TypeError("storage dtype must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(dev=None):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def status_string(st: int) -> str:
+    return _csa_status_string(st).decode()
+
+
+# ---------------------------------------------------------------------------
+# compression
+# ---------------------------------------------------------------------------
+
+def csa_compress(x_a, z_a, m, *, x_b=None, z_b=None, bias=None, n=None, p0=0, e0=0, e1=None,
+                 out=None, out_ld=None):
+    """Block-weighted compression of [B][n_raw][D] raw rows (positions p0..).
+
+    Returns out [B][e1-e0][D] (or writes into ``out`` with row stride out_ld)."""
+    B, n_raw, D = x_a.shape
+    n = p0 + n_raw if n is None else n
+    e1 = -(-n // m) if e1 is None else e1
+    if out is None:
+        out = torch.empty((B, e1 - e0, D), dtype=x_a.dtype, device=x_a.device)
+        out_ld = e1 - e0
+    elif out_ld is None:
+        out_ld = out.shape[1]
+    st = _csa_compress(_ptr(x_a), _ptr(z_a), _ptr(x_b), _ptr(z_b), _ptr(bias), out.data_ptr(), B, n, D,
+                       m, p0, n_raw, e0, e1, out_ld, _dt(x_a), _stream(x_a.device))
+    _check(st, "csa_compress")
+    return out
+
+
+def hca_compress(x, z, m=128, *, bias=None, n=None, p0=0, e0=0, e1=None, out=None, out_ld=None):
+    B, n_raw, D = x.shape
+    n = p0 + n_raw if n is None else n
+    e1 = -(-n // m) if e1 is None else e1
+    if out is None:
+        out = torch.empty((B, e1 - e0, D), dtype=x.dtype, device=x.device)
+        out_ld = e1 - e0
+    elif out_ld is None:
+        out_ld = out.shape[1]
+    st = _hca_compress(_ptr(x), _ptr(z), _ptr(bias), out.data_ptr(), B, n, D, m, p0, n_raw, e0, e1,
+                       out_ld, _dt(x), _stream(x.device))
+    _check(st, "hca_compress")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# indexer and top-k
+# ---------------------------------------------------------------------------
+
+def csa_index_score(q_idx, k_idx, m, *, w_idx=None, n_ctx, out=None):
+    B, T, HI, dI = q_idx.shape
+    L = k_idx.shape[1]
+    if out is None:
+        out = torch.empty((B, T, L), dtype=torch.float32, device=q_idx.device)
+    st = _csa_index_score(_ptr(q_idx), _ptr(w_idx), _ptr(k_idx), B, T, n_ctx, L, HI, dI, m,
+                          out.data_ptr(), _dt(q_idx), _stream(q_idx.device))
+    _check(st, "csa_index_score")
+    return out
+
+
+def csa_topk_select(score, m, k, *, n_ctx, idx=None, out_score=None, want_scores=False):
+    B, T, L = score.shape
+    if idx is None:
+        idx = torch.empty((B, T, k), dtype=torch.int32, device=score.device)
+    if want_scores and out_score is None:
+        out_score = torch.empty((B, T, k), dtype=torch.float32, device=score.device)
+    st = _csa_topk_select(_ptr(score), B, T, n_ctx, L, m, k, idx.data_ptr(), _ptr(out_score),
+                          _stream(score.device))
+    _check(st, "csa_topk_select")
+    return (idx, out_score) if want_scores else idx
+
+
+def csa_index_topk_workspace(B, T, L) -> int:
+    return int(_csa_index_topk_workspace(B, T, L))
+
+
+def csa_index_topk(q_idx, k_idx, m, k, *, w_idx=None, n_ctx, ws=None, idx=None, out_score=None,
+                   want_scores=False):
+    B, T, HI, dI = q_idx.shape
+    L = k_idx.shape[1]
+    if idx is None:
+        idx = torch.empty((B, T, k), dtype=torch.int32, device=q_idx.device)
+    if want_scores and out_score is None:
+        out_score = torch.empty((B, T, k), dtype=torch.float32, device=q_idx.device)
+    if ws is None:
+        nb = max(16, csa_index_topk_workspace(B, T, L))
+        ws = torch.empty(nb, dtype=torch.uint8, device=q_idx.device)
+    st = _csa_index_topk(_ptr(q_idx), _ptr(w_idx), _ptr(k_idx), B, T, n_ctx, L, HI, dI, m, k,
+                         idx.data_ptr(), _ptr(out_score), ws.data_ptr(), ws.numel() * ws.element_size(),
+                         _dt(q_idx), _stream(q_idx.device))
+    _check(st, "csa_index_topk")
+    return (idx, out_score) if want_scores else idx
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def _attn_out(q, out, lse, want_lse):
+    B, T, H, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    return out, lse
+
+
+def csa_sparse_attn_workspace(B, T, H, d, k, W, dtype) -> int:
+    return int(_csa_sparse_attn_workspace(B, T, H, d, k, W, dtype))
+
+
+def hca_dense_attn_workspace(B, T, H, d, L, m, n_ctx, W, dtype) -> int:
+    return int(_hca_dense_attn_workspace(B, T, H, d, L, m, n_ctx, W, dtype))
+
+
+def _ws(nbytes, dev, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def csa_sparse_attn(q, kc, vc, idx, *, kr=None, vr=None, W=0, sink=None, scale=None, n_ctx,
+                    out=None, lse=None, want_lse=False, ws=None):
+    B, T, H, d = q.shape
+    L = kc.shape[1]
+    k = idx.shape[-1]
+    R = 0 if kr is None else kr.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    out, lse = _attn_out(q, out, lse, want_lse)
+    wp, wn = _ws(csa_sparse_attn_workspace(B, T, H, d, k, W, _dt(q)), q.device, ws)
+    st = _csa_sparse_attn(_ptr(q), _ptr(kc), _ptr(vc), L, _ptr(idx), k, _ptr(kr), _ptr(vr), R, W,
+                          _ptr(sink), scale, B, T, n_ctx, H, d, out.data_ptr(), _ptr(lse), wp, wn,
+                          _dt(q), _stream(q.device))
+    _check(st, "csa_sparse_attn")
+    return (out, lse) if want_lse else out
+
+
+def hca_dense_attn(q, kc, vc, m, *, kr=None, vr=None, W=0, sink=None, scale=None, n_ctx, out=None,
+                   lse=None, want_lse=False, ws=None):
+    B, T, H, d = q.shape
+    L = kc.shape[1]
+    R = 0 if kr is None else kr.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    out, lse = _attn_out(q, out, lse, want_lse)
+    wp, wn = _ws(hca_dense_attn_workspace(B, T, H, d, L, m, n_ctx, W, _dt(q)), q.device, ws)
+    st = _hca_dense_attn(_ptr(q), _ptr(kc), _ptr(vc), L, m, _ptr(kr), _ptr(vr), R, W, _ptr(sink),
+                         scale, B, T, n_ctx, H, d, out.data_ptr(), _ptr(lse), wp, wn, _dt(q),
+                         _stream(q.device))
+    _check(st, "hca_dense_attn")
+    return (out, lse) if want_lse else out

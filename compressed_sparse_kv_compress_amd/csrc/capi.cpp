@@ -1,0 +1,301 @@
+// C ABI of libcsa: argument validation, launch configuration, workspace
+// sizing.  Every check runs before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "../../include/csa.h"
+#include "kernels.hpp"
+
+namespace csa {
+bool index_shape_supported(int64_t HI, int64_t dI, bool bf16);
+bool attn_shape_supported(int64_t H, int64_t d, bool bf16);
+}  // namespace csa
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+csa_status_t fail(csa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+csa_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) {
+    g_err[0] = '\0';
+    return CSA_OK;
+  }
+  return fail(CSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE(cond, ...)                                  \
+  do {                                                      \
+    if (!(cond)) return fail(CSA_ERR_INVALID_ARG, __VA_ARGS__); \
+  } while (0)
+#define REQUIRE_PTR(p)                                                       \
+  do {                                                                       \
+    if ((p) == nullptr) return fail(CSA_ERR_INVALID_ARG, "%s is NULL", #p);  \
+    if (!aligned16(p)) return fail(CSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); \
+  } while (0)
+#define OPT_PTR(p)                                                           \
+  do {                                                                       \
+    if ((p) != nullptr && !aligned16(p))                                     \
+      return fail(CSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p);    \
+  } while (0)
+
+bool dtype_ok(csa_dtype_t dt) { return dt == CSA_F32 || dt == CSA_BF16; }
+
+csa_status_t compress_common(const void* x_a, const void* z_a, const void* x_b, const void* z_b,
+                             const float* bias, void* out, int64_t B, int64_t n, int64_t D,
+                             int64_t m, int64_t p0, int64_t n_raw, int64_t e0, int64_t e1,
+                             int64_t out_ld, csa_dtype_t dt, void* stream) {
+  REQUIRE(dtype_ok(dt), "unknown dtype %d", static_cast<int>(dt));
+  REQUIRE(B >= 0 && n >= 1 && m >= 1 && D >= 8 && D % 8 == 0,
+          "need B >= 0, n >= 1, m >= 1, D a positive multiple of 8 (B=%lld n=%lld m=%lld D=%lld)",
+          (long long)B, (long long)n, (long long)m, (long long)D);
+  const int64_t L = (n + m - 1) / m;
+  REQUIRE(e0 >= 0 && e0 <= e1 && e1 <= L, "entry range [%lld, %lld) outside [0, %lld]",
+          (long long)e0, (long long)e1, (long long)L);
+  REQUIRE(out_ld >= e1 - e0, "out_ld %lld < e1-e0", (long long)out_ld);
+  REQUIRE((x_b == nullptr) == (z_b == nullptr), "x_b and z_b must both be given or both be NULL");
+  if (B == 0 || e1 == e0) return CSA_OK;
+  REQUIRE_PTR(x_a);
+  REQUIRE_PTR(z_a);
+  OPT_PTR(x_b);
+  OPT_PTR(z_b);
+  REQUIRE_PTR(out);
+  if (bias != nullptr && (reinterpret_cast<uintptr_t>(bias) & 3u))
+    return fail(CSA_ERR_INVALID_ARG, "bias is not 4-byte aligned");
+  const bool two = x_b != nullptr;
+  const int64_t lo = (two && e0 >= 1) ? (e0 - 1) * m : e0 * m;
+  const int64_t hi = e1 * m < n ? e1 * m : n;
+  REQUIRE(p0 >= 0 && n_raw >= 0 && p0 <= lo && p0 + n_raw >= hi && p0 + n_raw <= n,
+          "raw rows [%lld, %lld) do not cover the positions [%lld, %lld) the entries read",
+          (long long)p0, (long long)(p0 + n_raw), (long long)lo, (long long)hi);
+  csa::CompressArgs a{x_a, z_a, x_b, z_b, bias, out, B, n, D, m, p0, n_raw, e0, e1, out_ld};
+  return hip_status(csa::launch_compress(a, dt == CSA_BF16, static_cast<hipStream_t>(stream)),
+                    "compress launch");
+}
+
+csa_status_t index_common(const void* q_idx, const float* w_idx, const void* k_idx, int64_t B,
+                          int64_t T, int64_t n_ctx, int64_t L, int64_t HI, int64_t dI, int64_t m,
+                          csa_dtype_t dt) {
+  REQUIRE(dtype_ok(dt), "unknown dtype %d", static_cast<int>(dt));
+  REQUIRE(B >= 0 && T >= 1 && n_ctx >= T && L >= 0 && m >= 1 && HI >= 1 && dI >= 1,
+          "need B >= 0, 1 <= T <= n_ctx, L >= 0, m >= 1, H_I >= 1, d_I >= 1");
+  if (!csa::index_shape_supported(HI, dI, dt == CSA_BF16))
+    return fail(CSA_ERR_UNSUPPORTED, "no indexer kernel for H_I=%lld d_I=%lld dtype=%d", (long long)HI,
+                (long long)dI, static_cast<int>(dt));
+  if (B == 0) return CSA_OK;
+  REQUIRE_PTR(q_idx);
+  if (L > 0) REQUIRE_PTR(k_idx);
+  if (w_idx != nullptr && (reinterpret_cast<uintptr_t>(w_idx) & 3u))
+    return fail(CSA_ERR_INVALID_ARG, "w_idx is not 4-byte aligned");
+  return CSA_OK;
+}
+
+csa_status_t attn_common(const void* q, const void* kc, const void* vc, int64_t L, const void* kr,
+                         const void* vr, int64_t R, int64_t W, const float* sink, float scale,
+                         int64_t B, int64_t T, int64_t n_ctx, int64_t H, int64_t d, void* out,
+                         float* lse, csa_dtype_t dt) {
+  REQUIRE(dtype_ok(dt), "unknown dtype %d", static_cast<int>(dt));
+  REQUIRE(B >= 0 && T >= 1 && n_ctx >= T && L >= 0 && H >= 1 && d >= 1 && W >= 0,
+          "need B >= 0, 1 <= T <= n_ctx, L >= 0, H >= 1, d >= 1, W >= 0");
+  REQUIRE(std::isfinite(scale), "scale is not finite");
+  if (!csa::attn_shape_supported(H, d, dt == CSA_BF16))
+    return fail(CSA_ERR_UNSUPPORTED, "no attention kernel for H=%lld d=%lld dtype=%d", (long long)H,
+                (long long)d, static_cast<int>(dt));
+  if (W > 0) {
+    REQUIRE(R >= T + W - 1 || R == n_ctx, "window needs R >= T+W-1 raw rows (R=%lld)", (long long)R);
+    REQUIRE(R <= n_ctx, "R=%lld exceeds n_ctx", (long long)R);
+  }
+  if (B == 0) return CSA_OK;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(out);
+  if (L > 0) {
+    REQUIRE_PTR(kc);
+    REQUIRE_PTR(vc);
+  }
+  if (W > 0) {
+    REQUIRE_PTR(kr);
+    REQUIRE_PTR(vr);
+  }
+  if (sink != nullptr && (reinterpret_cast<uintptr_t>(sink) & 3u))
+    return fail(CSA_ERR_INVALID_ARG, "sink is not 4-byte aligned");
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(CSA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  return CSA_OK;
+}
+
+int64_t dense_max_rows(int64_t L, int64_t m, int64_t n_ctx, int64_t W) {
+  int64_t nv = (n_ctx - 1) / m;
+  if (nv > L) nv = L;
+  return nv + W;
+}
+
+}  // namespace
+
+extern "C" {
+
+csa_status_t csa_compress(const void* x_a, const void* z_a, const void* x_b, const void* z_b,
+                          const float* bias, void* out, int64_t B, int64_t n, int64_t D, int64_t m,
+                          int64_t p0, int64_t n_raw, int64_t e0, int64_t e1, int64_t out_ld,
+                          csa_dtype_t dtype, void* stream) {
+  return compress_common(x_a, z_a, x_b, z_b, bias, out, B, n, D, m, p0, n_raw, e0, e1, out_ld, dtype,
+                         stream);
+}
+
+csa_status_t hca_compress(const void* x, const void* z, const float* bias, void* out, int64_t B,
+                          int64_t n, int64_t D, int64_t m, int64_t p0, int64_t n_raw, int64_t e0,
+                          int64_t e1, int64_t out_ld, csa_dtype_t dtype, void* stream) {
+  return compress_common(x, z, nullptr, nullptr, bias, out, B, n, D, m, p0, n_raw, e0, e1, out_ld,
+                         dtype, stream);
+}
+
+csa_status_t csa_index_score(const void* q_idx, const float* w_idx, const void* k_idx, int64_t B,
+                             int64_t T, int64_t n_ctx, int64_t L, int64_t H_I, int64_t d_I,
+                             int64_t m, float* score, csa_dtype_t dtype, void* stream) {
+  csa_status_t st = index_common(q_idx, w_idx, k_idx, B, T, n_ctx, L, H_I, d_I, m, dtype);
+  if (st != CSA_OK || B == 0 || L == 0) return st;
+  REQUIRE_PTR(score);
+  csa::IndexScoreArgs a{q_idx, w_idx, k_idx, score, L, 0, B * T, B, T, n_ctx, L, H_I, d_I, m};
+  return hip_status(csa::launch_index_score(a, dtype == CSA_BF16, static_cast<hipStream_t>(stream)),
+                    "index score launch");
+}
+
+csa_status_t csa_topk_select(const float* score, int64_t B, int64_t T, int64_t n_ctx, int64_t L,
+                             int64_t m, int64_t k, int32_t* idx, float* out_score, void* stream) {
+  REQUIRE(B >= 0 && T >= 1 && n_ctx >= T && L >= 0 && m >= 1, "need B >= 0, 1 <= T <= n_ctx, L >= 0, m >= 1");
+  REQUIRE(k >= 1 && k <= (1 << 20), "k=%lld outside [1, 2^20]", (long long)k);
+  if (B == 0) return CSA_OK;
+  if (L > 0) REQUIRE_PTR(score);
+  REQUIRE_PTR(idx);
+  OPT_PTR(out_score);
+  csa::TopkArgs a{score, L, 0, B * T, T, n_ctx, L, m, k, idx, out_score};
+  return hip_status(csa::launch_topk(a, static_cast<hipStream_t>(stream)), "top-k launch");
+}
+
+size_t csa_index_topk_workspace(int64_t B, int64_t T, int64_t L) {
+  if (B <= 0 || T <= 0 || L <= 0) return 0;
+  return static_cast<size_t>(B) * T * L * sizeof(float);
+}
+
+csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int64_t B,
+                            int64_t T, int64_t n_ctx, int64_t L, int64_t H_I, int64_t d_I, int64_t m,
+                            int64_t k, int32_t* idx, float* out_score, void* ws, size_t ws_bytes,
+                            csa_dtype_t dtype, void* stream) {
+  csa_status_t st = index_common(q_idx, w_idx, k_idx, B, T, n_ctx, L, H_I, d_I, m, dtype);
+  if (st != CSA_OK) return st;
+  REQUIRE(k >= 1 && k <= (1 << 20), "k=%lld outside [1, 2^20]", (long long)k);
+  if (B == 0) return CSA_OK;
+  REQUIRE_PTR(idx);
+  OPT_PTR(out_score);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t rows = B * T;
+  int64_t chunk = rows;
+  if (L > 0) {
+    if (ws == nullptr || ws_bytes < static_cast<size_t>(L) * sizeof(float))
+      return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes is below the minimum %zu", ws_bytes,
+                  static_cast<size_t>(L) * sizeof(float));
+    if (!aligned16(ws)) return fail(CSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+    chunk = static_cast<int64_t>(ws_bytes / (static_cast<size_t>(L) * sizeof(float)));
+    if (chunk > rows) chunk = rows;
+  }
+  float* sc = static_cast<float*>(ws);
+  for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
+    const int64_t nr = r0 + chunk < rows ? chunk : rows - r0;
+    if (L > 0) {
+      csa::IndexScoreArgs a{q_idx, w_idx, k_idx, sc, L, r0, nr, B, T, n_ctx, L, H_I, d_I, m};
+      st = hip_status(csa::launch_index_score(a, dtype == CSA_BF16, s), "index score launch");
+      if (st != CSA_OK) return st;
+    }
+    csa::TopkArgs t{sc, L, r0, nr, T, n_ctx, L, m, k, idx + r0 * k,
+                    out_score ? out_score + r0 * k : nullptr};
+    st = hip_status(csa::launch_topk(t, s), "top-k launch");
+    if (st != CSA_OK) return st;
+  }
+  return CSA_OK;
+}
+
+size_t csa_sparse_attn_workspace(int64_t B, int64_t T, int64_t H, int64_t d, int64_t k, int64_t W,
+                                 csa_dtype_t dtype) {
+  if (B <= 0 || T <= 0) return 0;
+  const int ns = csa::attn_splits(B, T, H, d, k + W, dtype == CSA_BF16);
+  return csa::attn_ws_bytes(B, T, H, d, ns);
+}
+
+size_t hca_dense_attn_workspace(int64_t B, int64_t T, int64_t H, int64_t d, int64_t L, int64_t m,
+                                int64_t n_ctx, int64_t W, csa_dtype_t dtype) {
+  if (B <= 0 || T <= 0 || m <= 0) return 0;
+  const int ns = csa::attn_splits(B, T, H, d, dense_max_rows(L, m, n_ctx, W), dtype == CSA_BF16);
+  return csa::attn_ws_bytes(B, T, H, d, ns);
+}
+
+static csa_status_t attn_launch(const csa::AttnArgs& a, bool sparse, int64_t max_rows, csa_dtype_t dt,
+                                void* ws, size_t ws_bytes, void* stream) {
+  const bool bf16 = dt == CSA_BF16;
+  const int ns = csa::attn_splits(a.B, a.T, a.H, a.d, max_rows, bf16);
+  const size_t need = csa::attn_ws_bytes(a.B, a.T, a.H, a.d, ns);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need)
+      return fail(CSA_ERR_WORKSPACE, "attention needs %zu workspace bytes, got %zu", need, ws_bytes);
+    if (!aligned16(ws)) return fail(CSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+  }
+  csa::AttnArgs b = a;
+  b.ws = static_cast<float*>(ws);
+  b.ws_bytes = ws_bytes;
+  return hip_status(csa::launch_attn(b, sparse, bf16, ns, static_cast<hipStream_t>(stream)),
+                    "attention launch");
+}
+
+csa_status_t csa_sparse_attn(const void* q, const void* kc, const void* vc, int64_t L,
+                             const int32_t* idx, int64_t k, const void* kr, const void* vr, int64_t R,
+                             int64_t W, const float* sink, float scale, int64_t B, int64_t T,
+                             int64_t n_ctx, int64_t H, int64_t d, void* out, float* lse, void* ws,
+                             size_t ws_bytes, csa_dtype_t dtype, void* stream) {
+  csa_status_t st = attn_common(q, kc, vc, L, kr, vr, R, W, sink, scale, B, T, n_ctx, H, d, out, lse, dtype);
+  if (st != CSA_OK) return st;
+  REQUIRE(k >= 0, "k < 0");
+  if (B == 0) return CSA_OK;
+  if (k > 0) REQUIRE_PTR(idx);
+  csa::AttnArgs a{q, kc, vc, L, 1, idx, k, kr, vr, R, W, sink, scale, B, T, n_ctx, H, d, out, lse,
+                  nullptr, 0};
+  return attn_launch(a, true, k + W, dtype, ws, ws_bytes, stream);
+}
+
+csa_status_t hca_dense_attn(const void* q, const void* kc, const void* vc, int64_t L, int64_t m,
+                            const void* kr, const void* vr, int64_t R, int64_t W, const float* sink,
+                            float scale, int64_t B, int64_t T, int64_t n_ctx, int64_t H, int64_t d,
+                            void* out, float* lse, void* ws, size_t ws_bytes, csa_dtype_t dtype,
+                            void* stream) {
+  csa_status_t st = attn_common(q, kc, vc, L, kr, vr, R, W, sink, scale, B, T, n_ctx, H, d, out, lse, dtype);
+  if (st != CSA_OK) return st;
+  REQUIRE(m >= 1, "m < 1");
+  if (B == 0) return CSA_OK;
+  csa::AttnArgs a{q, kc, vc, L, m, nullptr, 0, kr, vr, R, W, sink, scale, B, T, n_ctx, H, d, out, lse,
+                  nullptr, 0};
+  return attn_launch(a, false, dense_max_rows(L, m, n_ctx, W), dtype, ws, ws_bytes, stream);
+}
+
+const char* csa_status_string(csa_status_t status) {
+  switch (status) {
+    case CSA_OK: return "CSA_OK";
+    case CSA_ERR_INVALID_ARG: return "CSA_ERR_INVALID_ARG";
+    case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED";
+    case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE";
+    case CSA_ERR_HIP: return "CSA_ERR_HIP";
+  }
+  return "CSA_ERR_UNKNOWN";
+}
+
+const char* csa_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,164 @@
+// Block-weighted compression: one compressed entry per block of m raw tokens.
+//
+// Method: shareware.cn Hybrid Attention article, section 四 (per-dimension,
+// token-dependent softmax weights instead of a plain mean) and section 五
+// (two-path overlap: the current block through stream A, the previous block
+// through stream B, one joint softmax per channel); trdm.cn attention
+// article, section 4.3 改进二 (two streams with their own position biases).
+//
+// Design (gfx950): a pure HBM stream at ~2 flop per byte.  One thread owns
+// 16 bytes of channels (8 bf16 or 4 fp32) of one entry, so a wavefront reads
+// 1 KiB contiguous per raw row (fully coalesced 16-byte loads).  Candidates are
+// taken 8 tokens at a time: all 8 logit/value loads are issued before any use
+// (memory-level parallelism), the chunk maximum is formed in registers and the
+// running sums are rescaled once per chunk, so there is about one exp2 per
+// element.  Weights are never materialised.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace csa {
+
+namespace {
+
+constexpr int kChunk = 8;
+
+template <bool BF16>
+struct Io;
+
+template <>
+struct Io<true> {
+  static constexpr int VEC = 8;
+  __device__ static void load(const void* base, int64_t off, float* v) {
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    v[0] = lo_bf16(w.x); v[1] = hi_bf16(w.x);
+    v[2] = lo_bf16(w.y); v[3] = hi_bf16(w.y);
+    v[4] = lo_bf16(w.z); v[5] = hi_bf16(w.z);
+    v[6] = lo_bf16(w.w); v[7] = hi_bf16(w.w);
+  }
+  __device__ static void store(void* base, int64_t off, const float* v) {
+    uint4 w;
+    w.x = pack_bf16x2(v[0], v[1]);
+    w.y = pack_bf16x2(v[2], v[3]);
+    w.z = pack_bf16x2(v[4], v[5]);
+    w.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off) = w;
+  }
+};
+
+template <>
+struct Io<false> {
+  static constexpr int VEC = 4;
+  __device__ static void load(const void* base, int64_t off, float* v) {
+    const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+  }
+  __device__ static void store(void* base, int64_t off, const float* v) {
+    *reinterpret_cast<float4*>(static_cast<float*>(base) + off) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
+// Fold the candidate tokens [lo, hi) of one stream into the running
+// (max, denominator, numerator) of VEC channels.  Logits are in log2 units.
+template <bool BF16>
+__device__ __forceinline__ void fold_segment(const void* x, const void* z, const float* bias,
+                                             int64_t bias_row0, int64_t lo, int64_t hi,
+                                             int64_t row_base, int64_t p0, int64_t D,
+                                             int64_t c0, float* mx, float* den, float* acc) {
+  constexpr int VEC = Io<BF16>::VEC;
+  for (int64_t u0 = lo; u0 < hi; u0 += kChunk) {
+    float xv[kChunk][VEC], lv[kChunk][VEC];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      if (u0 + i < hi) {
+        const int64_t off = (row_base + (u0 + i - p0)) * D + c0;
+        Io<BF16>::load(x, off, xv[i]);
+        Io<BF16>::load(z, off, lv[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      if (u0 + i < hi) {
+        if (bias) {
+          const float* br = bias + (bias_row0 + (u0 + i - lo)) * D + c0;
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) lv[i][c] += br[c];
+        }
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) lv[i][c] *= kLog2e;
+      } else {
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) { lv[i][c] = -INFINITY; xv[i][c] = 0.f; }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+      float cm = lv[0][c];
+#pragma unroll
+      for (int i = 1; i < kChunk; ++i) cm = fmaxf(cm, lv[i][c]);
+      const float nm = fmaxf(mx[c], cm);
+      if (nm == -INFINITY) continue;  // nothing finite yet in this channel
+      const float a = fast_exp2(mx[c] - nm);
+      float s = 0.f, t = 0.f;
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        const float e = fast_exp2(lv[i][c] - nm);
+        s += e;
+        t = fmaf(e, xv[i][c], t);
+      }
+      den[c] = fmaf(den[c], a, s);
+      acc[c] = fmaf(acc[c], a, t);
+      mx[c] = nm;
+    }
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
+  constexpr int VEC = Io<BF16>::VEC;
+  const int64_t nvec = a.D / VEC;
+  const int64_t ne = a.e1 - a.e0;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= a.B * ne * nvec) return;
+  const int64_t cv = gid % nvec;
+  const int64_t tmp = gid / nvec;
+  const int64_t jj = tmp % ne;
+  const int64_t b = tmp / ne;
+  const int64_t j = a.e0 + jj;
+  const int64_t c0 = cv * VEC;
+  const int64_t row_base = b * a.n_raw;
+
+  float mx[VEC], den[VEC], acc[VEC];
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) { mx[c] = -INFINITY; den[c] = 0.f; acc[c] = 0.f; }
+
+  const bool two = a.x_b != nullptr;
+  if (two && j >= 1) {  // stream B: previous block, bias rows 0..m-1
+    fold_segment<BF16>(a.x_b, a.z_b, a.bias, 0, (j - 1) * a.m, j * a.m, row_base, a.p0, a.D, c0,
+                       mx, den, acc);
+  }
+  const int64_t lo = j * a.m;
+  const int64_t hi = (j + 1) * a.m < a.n ? (j + 1) * a.m : a.n;
+  fold_segment<BF16>(a.x_a, a.z_a, a.bias, two ? a.m : 0, lo, hi, row_base, a.p0, a.D, c0, mx,
+                     den, acc);
+
+  float o[VEC];
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) o[c] = den[c] > 0.f ? acc[c] / den[c] : 0.f;
+  Io<BF16>::store(a.out, (b * a.out_ld + jj) * a.D + c0, o);
+}
+
+}  // namespace
+
+hipError_t launch_compress(const CompressArgs& a, bool bf16, hipStream_t s) {
+  const int vec = bf16 ? 8 : 4;
+  const int64_t total = a.B * (a.e1 - a.e0) * (a.D / vec);
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  if (bf16)
+    hipLaunchKernelGGL(compress_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(compress_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,68 @@
+// Internal launch interface between the C-ABI layer and the gfx950 kernels.
+// Arguments are validated by the C-ABI layer before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+struct CompressArgs {
+  const void* x_a;
+  const void* z_a;
+  const void* x_b;  // null: single path
+  const void* z_b;
+  const float* bias;  // null or [span][D]
+  void* out;          // [B][out_ld][D], entry j at row j - e0
+  int64_t B, n, D, m, p0, n_raw, e0, e1, out_ld;
+};
+hipError_t launch_compress(const CompressArgs& a, bool bf16, hipStream_t s);
+
+struct IndexScoreArgs {
+  const void* q;      // [rows][HI][dI], rows = B*T (b-major)
+  const float* w;     // [rows][HI] or null
+  const void* k;      // [B][L][dI]
+  float* score;       // [rows][ld]
+  int64_t ld;
+  int64_t row0;       // first (b,t) row handled by this launch
+  int64_t nrows;      // rows handled
+  int64_t B, T, n_ctx, L, HI, dI, m;
+};
+hipError_t launch_index_score(const IndexScoreArgs& a, bool bf16, hipStream_t s);
+
+struct TopkArgs {
+  const float* score;  // row r of this launch at score + r*ld
+  int64_t ld;
+  int64_t row0;        // global (b,t) row of the first row (for positions)
+  int64_t nrows;
+  int64_t T, n_ctx, L, m, k;
+  int32_t* idx;        // [rows][k] (offset to row0 already)
+  float* out_score;    // [rows][k] or null
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const void* q;        // [B*T][H][d]
+  const void* kc;       // [B][L][d]
+  const void* vc;
+  int64_t L, m;
+  const int32_t* idx;   // sparse: [B*T][k]; dense: null
+  int64_t k;
+  const void* kr;       // [B][R][d], positions n_ctx-R .. n_ctx-1
+  const void* vr;
+  int64_t R, W;
+  const float* sink;    // [H] or null
+  float scale;
+  int64_t B, T, n_ctx, H, d;
+  void* out;            // [B*T][H][d]
+  float* lse;           // [B*T][H] or null
+  float* ws;            // split partials
+  size_t ws_bytes;
+};
+// Number of row splits the attention launch uses, and its workspace bytes.
+int attn_splits(int64_t B, int64_t T, int64_t H, int64_t d, int64_t max_rows, bool bf16);
+size_t attn_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t d, int nsplit);
+hipError_t launch_attn(const AttnArgs& a, bool sparse, bool bf16, int nsplit, hipStream_t s);
+bool attn_shape_supported(int64_t H, int64_t d, bool bf16);
+bool index_shape_supported(int64_t HI, int64_t dI, bool bf16);
+
+}  // namespace csa

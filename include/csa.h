@@ -1,0 +1,176 @@
+/*
+ * csa.h -- C ABI of libcsa, the gfx950 (MI355X) kernels of the DeepSeek-V4
+ * hybrid compressed attention hot path: CSA (4:1 compression, Lightning
+ * Indexer, top-k, sparse MQA attention with a raw window and a sink) and HCA
+ * (128:1 compression, dense MQA attention with a sink).
+ *
+ * Sources (cited by page and section):
+ *   shareware.cn, DeepSeek V4 Hybrid Attention architecture article,
+ *     sections 二-十二 (compression ratios, the three-level memory, adaptive
+ *     compression, two-path overlap, Lightning Indexer, ReLU, dense HCA,
+ *     causality and the window, MQA, the attention sink);
+ *   trdm.cn, "从 MLA 到 CSA，聊聊大模型 Attention 的瘦身与闪送",
+ *     sections 2.1 (MQA), 3.1 (online softmax), 4.2 (Lightning Indexer),
+ *     4.3 (V4 hybrid attention: two streams, window concatenation, HCA);
+ *   aimodeling.com news item on V4 hybrid attention (CSA: 4:1, top 1024,
+ *     128-token window; HCA: 128:1, dense).
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense, row-major, in caller-owned DEVICE memory, 16-byte
+ *     aligned.  The library never allocates, frees or synchronises: work is
+ *     enqueued on `stream` (a hipStream_t; NULL = the null stream) and CSA_OK
+ *     means it was enqueued.  Calls may be captured into a HIP graph.
+ *   - Arguments are validated before anything is enqueued; on an error no
+ *     output is touched.  Launch failures return CSA_ERR_HIP;
+ *     csa_last_error() gives a thread-local detail string.
+ *   - dtype selects the storage type of every bf16/fp32 tensor argument
+ *     (declared `void*`).  Accumulation is fp32.  Scores, sinks, biases,
+ *     head weights and lse are always fp32; indices are int32.
+ *   - Positions: a batch holds B sequences of n_ctx tokens (uniform length).
+ *     The T queries of a sequence sit at positions t_i = n_ctx - T + i.
+ *     Compressed entry s covers tokens [s*m, (s+1)*m) and is visible to the
+ *     query at t iff (s+1)*m <= t (the block is complete and strictly
+ *     earlier), i.e. s < floor(t/m).
+ *   - Raw-window buffers kr / vr [B][R][d] hold positions n_ctx-R .. n_ctx-1;
+ *     the window of query t is the raw tokens max(0, t-W+1) .. t.
+ *   - Inputs and outputs must not alias.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype_t;
+
+typedef enum csa_status {
+  CSA_OK = 0,
+  CSA_ERR_INVALID_ARG = 1, /* null / misaligned pointer, inconsistent sizes */
+  CSA_ERR_UNSUPPORTED = 2, /* shape or dtype this build has no kernel for */
+  CSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  CSA_ERR_HIP = 4          /* a HIP launch failed; see csa_last_error() */
+} csa_status_t;
+
+/* ---------------------------------------------------------------------------
+ * csa_compress -- block-weighted compression of one K/V/index-key stream.
+ * shareware.cn article, section 四 (each entry is a dynamic, per-dimension
+ * softmax-weighted sum of its block's raw rows) and section 五 / trdm.cn
+ * section 4.3 改进二 (two-path overlap).  For entry j and channel c:
+ *   candidates: stream A tokens u in [j*m, min((j+1)*m, n)) with value
+ *     x_a[u][c] and logit z_a[u][c] (+ bias[m + u - j*m][c] in two-path mode,
+ *     + bias[u - j*m][c] in single-path mode);
+ *   two-path (x_b, z_b non-NULL) also stream B tokens u in [(j-1)*m, j*m) for
+ *     j >= 1, value x_b[u][c], logit z_b[u][c] (+ bias[u - (j-1)*m][c]);
+ *   out[j][c] = sum softmax(logits) * values   (one joint softmax).
+ * A trailing partial block is compressed over the tokens present.
+ *   x_a, z_a, x_b, z_b : [B][n_raw][D] dtype, raw positions p0 .. p0+n_raw-1
+ *                        of sequences of n tokens (z = learned logits)
+ *   bias               : NULL, or fp32 [m][D] (single) / [2m][D] (two-path)
+ *   out                : entries e0 .. e1-1; entry j of sequence b at
+ *                        out + ((b*out_ld) + (j - e0)) * D  (out_ld >= e1-e0)
+ * Requires D % 8 == 0, 0 <= e0 <= e1 <= ceil(n/m), and the raw rows each
+ * requested entry reads to lie in [p0, p0+n_raw).  With p0 = 0, n_raw = n,
+ * e0 = 0, e1 = ceil(n/m) this is the bulk compression of whole sequences; a
+ * decode step passes the last raw tokens and e0 = e1-1.
+ * ------------------------------------------------------------------------- */
+csa_status_t csa_compress(const void* x_a, const void* z_a, const void* x_b, const void* z_b,
+                          const float* bias, void* out, int64_t B, int64_t n, int64_t D,
+                          int64_t m, int64_t p0, int64_t n_raw, int64_t e0, int64_t e1,
+                          int64_t out_ld, csa_dtype_t dtype, void* stream);
+
+/* hca_compress -- the same operator with one stream and m = 128 in HCA
+ * (shareware.cn article, sections 二 and 三.3; trdm.cn section 4.3, HCA
+ * paragraph: no second stream).  Arguments as csa_compress single path. */
+csa_status_t hca_compress(const void* x, const void* z, const float* bias, void* out, int64_t B,
+                          int64_t n, int64_t D, int64_t m, int64_t p0, int64_t n_raw,
+                          int64_t e0, int64_t e1, int64_t out_ld, csa_dtype_t dtype,
+                          void* stream);
+
+/* ---------------------------------------------------------------------------
+ * csa_index_score -- Lightning Indexer scores (shareware.cn article,
+ * sections 六-七; trdm.cn section 4.2):
+ *   score[b][t][s] = sum_h w[b][t][h] * max(0, sum_c q_idx[b][t][h][c]*k_idx[b][s][c])
+ * for visible s (s < floor(t/m)); -inf for the other s < L.  No scale.
+ *   q_idx : [B][T][H_I][d_I] dtype      w_idx : fp32 [B][T][H_I] or NULL (= 1)
+ *   k_idx : [B][L][d_I] dtype (one key per compressed entry, shared by heads)
+ *   score : fp32 [B][T][L]
+ * bf16 needs H_I in {32, 64, 128} with d_I = 128, or H_I in {32, 64} with
+ * d_I = 64; fp32 needs H_I*d_I <= 16384.
+ * ------------------------------------------------------------------------- */
+csa_status_t csa_index_score(const void* q_idx, const float* w_idx, const void* k_idx, int64_t B,
+                             int64_t T, int64_t n_ctx, int64_t L, int64_t H_I, int64_t d_I,
+                             int64_t m, float* score, csa_dtype_t dtype, void* stream);
+
+/* csa_topk_select -- per query keep the min(k, V) highest of the V = min(L,
+ * floor(t/m)) visible scores (shareware.cn article, section 六; aimodeling.com
+ * CSA paragraph: 1024 per query).  Equal scores (-0 == +0) go to the lower
+ * entry index.  idx int32 [B][T][k] receives the kept indices in ascending
+ * order, -1 padded; out_score (NULL or fp32 [B][T][k]) their scores (-inf in
+ * padded slots).  score is fp32 [B][T][L] and must hold no NaN among the
+ * visible entries.  1 <= k <= 1048576. */
+csa_status_t csa_topk_select(const float* score, int64_t B, int64_t T, int64_t n_ctx, int64_t L,
+                             int64_t m, int64_t k, int32_t* idx, float* out_score, void* stream);
+
+/* csa_index_topk -- csa_index_score followed by csa_topk_select, with the
+ * fp32 score matrix kept in the caller's workspace.  When ws_bytes is below
+ * csa_index_topk_workspace(B, T, L) the queries are processed in groups that
+ * fit; ws_bytes must be at least 4*L.  Results do not depend on ws_bytes. */
+size_t csa_index_topk_workspace(int64_t B, int64_t T, int64_t L);
+csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int64_t B,
+                            int64_t T, int64_t n_ctx, int64_t L, int64_t H_I, int64_t d_I,
+                            int64_t m, int64_t k, int32_t* idx, float* out_score, void* ws,
+                            size_t ws_bytes, csa_dtype_t dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * csa_sparse_attn -- CSA main attention (shareware.cn article, sections 三.1,
+ * 十, 十一, 十二; trdm.cn section 4.3 改进三).  Per query (b, t) and head h the
+ * rows are the selected compressed entries kc/vc[b][idx[b][t][j]] (slots
+ * holding -1 are skipped) followed by the raw window rows; one shared K/V
+ * head (MQA).  l_i = scale * q[b][t][h] . k_i, sink logit sigma_h with no
+ * value:
+ *   out[b][t][h] = sum_i e^{l_i} v_i / (e^{sigma_h} + sum_i e^{l_i})
+ *   lse[b][t][h] = log(e^{sigma_h} + sum_i e^{l_i})        (natural log)
+ *   q   : [B][T][H][d] dtype        kc, vc : [B][L][d] dtype
+ *   idx : int32 [B][T][k], entries in [0, L) or -1
+ *   kr, vr : [B][R][d] raw positions n_ctx-R .. n_ctx-1 (NULL when W == 0);
+ *            R >= T + W - 1 and R <= n_ctx when W > 0
+ *   sink: fp32 [H] or NULL (= no sink)   out : [B][T][H][d] dtype
+ *   lse : fp32 [B][T][H] or NULL
+ *   ws  : csa_sparse_attn_workspace(...) bytes (may be 0 => ws may be NULL)
+ * bf16 needs H % 64 == 0 and d in {128, 256, 512}; fp32 needs d <= 512.
+ * ------------------------------------------------------------------------- */
+size_t csa_sparse_attn_workspace(int64_t B, int64_t T, int64_t H, int64_t d, int64_t k, int64_t W,
+                                 csa_dtype_t dtype);
+csa_status_t csa_sparse_attn(const void* q, const void* kc, const void* vc, int64_t L,
+                             const int32_t* idx, int64_t k, const void* kr, const void* vr,
+                             int64_t R, int64_t W, const float* sink, float scale, int64_t B,
+                             int64_t T, int64_t n_ctx, int64_t H, int64_t d, void* out,
+                             float* lse, void* ws, size_t ws_bytes, csa_dtype_t dtype,
+                             void* stream);
+
+/* hca_dense_attn -- HCA attention: every visible compressed entry s <
+ * min(L, floor(t/m)) densely, no indexer (shareware.cn article, section 八;
+ * aimodeling.com HCA paragraph), followed by the optional raw window (W = 0
+ * for none; trdm.cn section 4.3, HCA paragraph), with the same sink softmax and
+ * argument conventions as csa_sparse_attn. */
+size_t hca_dense_attn_workspace(int64_t B, int64_t T, int64_t H, int64_t d, int64_t L, int64_t m,
+                                int64_t n_ctx, int64_t W, csa_dtype_t dtype);
+csa_status_t hca_dense_attn(const void* q, const void* kc, const void* vc, int64_t L, int64_t m,
+                            const void* kr, const void* vr, int64_t R, int64_t W,
+                            const float* sink, float scale, int64_t B, int64_t T, int64_t n_ctx,
+                            int64_t H, int64_t d, void* out, float* lse, void* ws,
+                            size_t ws_bytes, csa_dtype_t dtype, void* stream);
+
+/* Status names and the calling thread's last error detail (never NULL). */
+const char* csa_status_string(csa_status_t status);
+const char* csa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H */

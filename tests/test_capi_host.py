@@ -1,0 +1,104 @@
+"""Host-side checks of the C ABI: the library loads and exports every entry
+point declared in include/csa.h, and argument validation rejects bad calls
+before anything reaches the GPU (these calls enqueue no work)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "compressed_sparse_kv_compress_amd", "libcsa.so")
+HDR = os.path.join(ROOT, "include", "csa.h")
+
+
+def _declared():
+    src = open(HDR).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^(?:csa_status_t|size_t|const char\*)\s+(\w+)\s*\(", src, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libcsa.so is not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_hot_path_calls():
+    names = _declared()
+    for n in ("csa_compress", "hca_compress", "csa_index_topk", "csa_sparse_attn", "hca_dense_attn",
+              "csa_index_score", "csa_topk_select"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def _call(lib, name, argtypes, *args):
+    fn = getattr(lib, name)
+    fn.argtypes = argtypes
+    fn.restype = ctypes.c_int
+    return fn(*args)
+
+
+V, I, Z, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def test_status_strings(lib):
+    lib.csa_status_string.restype = ctypes.c_char_p
+    lib.csa_status_string.argtypes = [ctypes.c_int]
+    assert lib.csa_status_string(0) == b"CSA_OK"
+    assert lib.csa_status_string(3) == b"CSA_ERR_WORKSPACE"
+
+
+def test_compress_rejects_bad_arguments(lib):
+    args = [V] * 6 + [I] * 9 + [ctypes.c_int, V]
+    # D not a multiple of 8
+    assert _call(lib, "csa_compress", args, FAKE, FAKE, None, None, None, FAKE,
+                 1, 16, 12, 4, 0, 16, 0, 4, 4, 1, None) == 1
+    # entry range beyond ceil(n/m)
+    assert _call(lib, "csa_compress", args, FAKE, FAKE, None, None, None, FAKE,
+                 1, 16, 16, 4, 0, 16, 0, 5, 5, 1, None) == 1
+    # two-path needs the previous block: raw rows starting at 8 cannot serve entry 2
+    assert _call(lib, "csa_compress", args, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                 1, 16, 16, 4, 8, 8, 2, 4, 2, 1, None) == 1
+    # misaligned pointer
+    assert _call(lib, "csa_compress", args, FAKE + 2, FAKE, None, None, None, FAKE,
+                 1, 16, 16, 4, 0, 16, 0, 4, 4, 1, None) == 1
+    # unknown dtype
+    assert _call(lib, "csa_compress", args, FAKE, FAKE, None, None, None, FAKE,
+                 1, 16, 16, 4, 0, 16, 0, 4, 4, 7, None) == 1
+    # nothing to do is fine and enqueues nothing
+    assert _call(lib, "csa_compress", args, None, None, None, None, None, None,
+                 1, 16, 16, 4, 0, 16, 2, 2, 0, 1, None) == 0
+
+
+def test_index_and_attention_reject_bad_arguments(lib):
+    idx_args = [V] * 3 + [I] * 8 + [V, V, V, Z, ctypes.c_int, V]
+    # unsupported indexer shape for bf16 (H_I = 48)
+    assert _call(lib, "csa_index_topk", idx_args, FAKE, None, FAKE, 1, 1, 100, 25, 48, 128, 4, 8,
+                 FAKE, None, FAKE, 1 << 20, 1, None) == 2
+    # workspace below one row of scores
+    assert _call(lib, "csa_index_topk", idx_args, FAKE, None, FAKE, 1, 1, 100, 25, 64, 128, 4, 8,
+                 FAKE, None, FAKE, 16, 1, None) == 3
+    # k = 0
+    assert _call(lib, "csa_index_topk", idx_args, FAKE, None, FAKE, 1, 1, 100, 25, 64, 128, 4, 0,
+                 FAKE, None, FAKE, 1 << 20, 1, None) == 1
+    attn = [V] * 3 + [I, V, I, V, V, I, I, V, F] + [I] * 5 + [V, V, V, Z, ctypes.c_int, V]
+    # window without enough raw rows
+    assert _call(lib, "csa_sparse_attn", attn, FAKE, FAKE, FAKE, 10, FAKE, 4, FAKE, FAKE, 8, 128,
+                 None, 0.1, 1, 1, 400, 64, 512, FAKE, None, FAKE, 1 << 30, 1, None) == 1
+    # unsupported head count for the bf16 MFMA kernel
+    assert _call(lib, "csa_sparse_attn", attn, FAKE, FAKE, FAKE, 10, FAKE, 4, None, None, 0, 0,
+                 None, 0.1, 1, 1, 40, 8, 512, FAKE, None, None, 0, 1, None) == 2
+    dense = [V] * 3 + [I, I, V, V, I, I, V, F] + [I] * 5 + [V, V, V, Z, ctypes.c_int, V]
+    # missing split workspace for a decode-shaped dense call
+    assert _call(lib, "hca_dense_attn", dense, FAKE, FAKE, FAKE, 7813, 128, None, None, 0, 0, None,
+                 0.04, 4, 1, 1000000, 64, 512, FAKE, None, None, 0, 1, None) == 3
+    # non-finite scale
+    assert _call(lib, "hca_dense_attn", dense, FAKE, FAKE, FAKE, 7813, 128, None, None, 0, 0, None,
+                 float("inf"), 4, 1, 1000000, 64, 512, FAKE, None, None, 0, 1, None) == 1

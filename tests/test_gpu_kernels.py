@@ -1,0 +1,258 @@
+"""GPU parity of each kernel against the fp64 oracle on small seeded inputs
+that span several tiles and a ragged tail, plus edge cases.
+
+Inputs are generated independently on each device by ``synthetic`` (bit-
+identical), never copied from the GPU to the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import BF16_TOL, F32_TOL, both, gen, index_eps, max_abs, near_tie_check, to_np
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import compressed_sparse_kv_compress_amd as csa
+else:  # collected on the CPU, skipped by the marker selection
+    csa = None
+
+DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+TOL = {"bf16": BF16_TOL, "f32": F32_TOL}
+
+
+# ---------------------------------------------------------------------------
+# compression
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("n,m,D,two", [(1003, 4, 512, True), (1003, 4, 128, False),
+                                       (1000, 128, 512, False), (77, 128, 64, False),
+                                       (4096, 4, 64, False), (40, 4, 32, True)])
+def test_compress_matches_oracle(dt, n, m, D, two):
+    seed = 100 + n + D
+    B = 2
+    xa, xa_c = both((B, n, D), seed, "k", dtype=DT[dt], scale=D ** -0.5)
+    za, za_c = both((B, n, D), seed, "z_k", dtype=DT[dt], scale=0.5)
+    bias = bias_c = None
+    kw, kw_c = {}, {}
+    if two:
+        xb, xb_c = both((B, n, D), seed, "xb_k", dtype=DT[dt], scale=D ** -0.5)
+        zb, zb_c = both((B, n, D), seed, "zb_k", dtype=DT[dt], scale=0.5)
+        kw, kw_c = dict(x_b=xb, z_b=zb), dict(x_b=xb_c, z_b=zb_c)
+        bias, bias_c = both((2 * m, D), seed, "bias", dtype=torch.float32, scale=0.3)
+    got = csa.csa_compress(xa, za, m, bias=bias, **kw)
+    torch.cuda.synchronize()
+    want = oracle.compress(xa_c, za_c, m, bias=bias_c, **kw_c)
+    assert got.shape == want.shape
+    assert max_abs(to_np(got), want) <= TOL[dt]
+
+
+def test_compress_decode_slot_equals_bulk():
+    # one new entry written into a cache slot from the last raw tokens only
+    B, n, D, m = 3, 4096 + 8, 512, 4
+    xa = gen((B, n, D), 7, "k", dtype=torch.bfloat16, device="cuda", scale=D ** -0.5)
+    za = gen((B, n, D), 7, "z_k", dtype=torch.bfloat16, device="cuda", scale=0.5)
+    xb = gen((B, n, D), 7, "xb_k", dtype=torch.bfloat16, device="cuda", scale=D ** -0.5)
+    zb = gen((B, n, D), 7, "zb_k", dtype=torch.bfloat16, device="cuda", scale=0.5)
+    bulk = csa.csa_compress(xa, za, m, x_b=xb, z_b=zb)
+    L = n // m
+    cache = torch.zeros((B, L + 5, D), dtype=torch.bfloat16, device="cuda")
+    p0 = n - 2 * m
+    tail = lambda t: t[:, p0:].contiguous()
+    csa.csa_compress(tail(xa), tail(za), m, x_b=tail(xb), z_b=tail(zb), n=n, p0=p0, e0=L - 1, e1=L,
+                     out=cache[:, L - 1:], out_ld=L + 5)
+    torch.cuda.synchronize()
+    assert torch.equal(cache[:, L - 1], bulk[:, L - 1])
+    assert torch.count_nonzero(cache[:, : L - 1]) == 0 and torch.count_nonzero(cache[:, L:]) == 0
+
+
+# ---------------------------------------------------------------------------
+# indexer scores and top-k
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt,HI,dI", [("bf16", 64, 128), ("bf16", 32, 128), ("bf16", 64, 64),
+                                      ("f32", 4, 32)])
+def test_index_scores_match_oracle(dt, HI, dI):
+    B, T, m = 2, 3, 4
+    n_ctx = 4 * 3001 + 2
+    L = -(-n_ctx // m)
+    seed = 11 + HI + dI
+    q, q_c = both((B, T, HI, dI), seed, "q_idx", dtype=DT[dt], scale=dI ** -0.5)
+    k, k_c = both((B, L, dI), seed, "k_idx", dtype=DT[dt], scale=dI ** -0.5)
+    w, w_c = both((B, T, HI), seed, "w_idx", dtype=torch.float32, kind="uniform")
+    got = to_np(csa.csa_index_score(q, k, m, w_idx=w, n_ctx=n_ctx))
+    want = oracle.index_scores(q_c, k_c, m, w=w_c, n_ctx=n_ctx)
+    fin = np.isfinite(want)
+    assert np.array_equal(fin, np.isfinite(got))
+    assert np.all(np.isneginf(got[~fin]))
+    for b in range(B):
+        for t in range(T):
+            eps = index_eps(q_c[b, t], w_c[b, t], k_c[b])
+            f = fin[b, t]
+            assert np.all(np.abs(got[b, t][f] - want[b, t][f]) <= eps[f] + 1e-30)
+
+
+def test_index_scores_exact_on_grid_inputs():
+    # grid values k/16 (|k| <= 8) and w in {1, 2}: every fp32 partial sum is exact
+    B, T, HI, dI, m = 2, 2, 64, 128, 4
+    n_ctx = 4 * 2050
+    L = n_ctx // m
+    q, q_c = both((B, T, HI, dI), 3, "q_idx", dtype=torch.bfloat16, kind="grid", scale=2.0 ** -4)
+    k, k_c = both((B, L, dI), 3, "k_idx", dtype=torch.bfloat16, kind="grid", scale=2.0 ** -4)
+    w = gen((B, T, HI), 3, "w_idx", dtype=torch.float32, device="cuda", kind="grid", grid=1).abs() + 1.0
+    w_c = (gen((B, T, HI), 3, "w_idx", dtype=torch.float32, device="cpu", kind="grid", grid=1).abs()
+           + 1.0).double().numpy()
+    got = to_np(csa.csa_index_score(q, k, m, w_idx=w, n_ctx=n_ctx))
+    want = oracle.index_scores(q_c, k_c, m, w=w_c, n_ctx=n_ctx)
+    assert np.array_equal(got, want)
+
+
+def _seeded_scores(B, T, L, seed, device):
+    """Scores with many exact ties, signed zeros and negatives."""
+    s = gen((B, T, L), seed, "scores", dtype=torch.float32, device=device, kind="grid", grid=40,
+            scale=0.25)
+    z = gen((B, T, L), seed + 1, "scores", dtype=torch.float32, device=device, kind="uniform")
+    s = torch.where((s == 0) & (z < 0.5), torch.tensor(-0.0, device=device), s)
+    return s
+
+
+@pytest.mark.parametrize("B,T,L,m,k", [(2, 3, 5000, 1, 64), (1, 4, 250000, 4, 1024),
+                                      (3, 1, 33000, 4, 1024), (2, 5, 700, 1, 1024), (1, 2, 9000, 1, 1)])
+def test_topk_select_bit_exact_on_seeded_scores(B, T, L, m, k):
+    n_ctx = L * m
+    sg = _seeded_scores(B, T, L, 5 + L, "cuda")
+    sc = _seeded_scores(B, T, L, 5 + L, "cpu").double().numpy()
+    idx, osc = csa.csa_topk_select(sg, m, k, n_ctx=n_ctx, want_scores=True)
+    torch.cuda.synchronize()
+    tpos = np.arange(n_ctx - T, n_ctx)
+    nv = np.minimum(tpos // m, L)
+    want = oracle.topk(sc, np.broadcast_to(nv, (B, T)), k)
+    got = idx.cpu().numpy()
+    assert np.array_equal(got, want)
+    gs = osc.cpu().double().numpy()
+    for b in range(B):
+        for t in range(T):
+            sel = want[b, t] >= 0
+            assert np.array_equal(gs[b, t][sel], sc[b, t][want[b, t][sel]])
+            assert np.all(np.isneginf(gs[b, t][~sel]))
+
+
+def test_index_topk_bit_exact_on_grid_inputs():
+    B, T, HI, dI, m, k = 2, 2, 64, 128, 4, 256
+    n_ctx = 4 * 6000 + 3
+    L = -(-n_ctx // m)
+    q, q_c = both((B, T, HI, dI), 9, "q_idx", dtype=torch.bfloat16, kind="grid", scale=2.0 ** -4)
+    kk, k_c = both((B, L, dI), 9, "k_idx", dtype=torch.bfloat16, kind="grid", scale=2.0 ** -4)
+    got = csa.csa_index_topk(q, kk, m, k, n_ctx=n_ctx).cpu().numpy()
+    want, _ = oracle.index_topk(q_c, k_c, m, k, n_ctx=n_ctx)
+    assert np.array_equal(got, want)
+    # a workspace holding one row at a time gives the same result
+    ws = torch.empty(L * 4, dtype=torch.uint8, device="cuda")
+    got2 = csa.csa_index_topk(q, kk, m, k, n_ctx=n_ctx, ws=ws).cpu().numpy()
+    assert np.array_equal(got2, want)
+
+
+@pytest.mark.parametrize("dt,HI,dI,k", [("bf16", 64, 128, 1024), ("f32", 4, 32, 64)])
+def test_index_topk_gaussian_exact_up_to_near_ties(dt, HI, dI, k):
+    B, T, m = 2, 3, 4
+    n_ctx = 4 * 20000 + 1
+    L = -(-n_ctx // m)
+    q, q_c = both((B, T, HI, dI), 21, "q_idx", dtype=DT[dt], scale=dI ** -0.5)
+    kk, k_c = both((B, L, dI), 21, "k_idx", dtype=DT[dt], scale=dI ** -0.5)
+    got = csa.csa_index_topk(q, kk, m, k, n_ctx=n_ctx).cpu().numpy()
+    want, sc = oracle.index_topk(q_c, k_c, m, k, n_ctx=n_ctx)
+    ties = 0
+    for b in range(B):
+        for t in range(T):
+            nv = min(L, (n_ctx - T + t) // m)
+            ties += near_tie_check(got[b, t], want[b, t], sc[b, t], nv, k,
+                                   index_eps(q_c[b, t], None, k_c[b])[:nv])
+    assert ties <= 1
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def _attn_inputs(dt, B, T, H, d, L, R, seed):
+    q, q_c = both((B, T, H, d), seed, "q", dtype=DT[dt], scale=d ** -0.5)
+    kc, kc_c = both((B, L, d), seed, "kc", dtype=DT[dt], scale=d ** -0.5)
+    vc, vc_c = both((B, L, d), seed, "vc", dtype=DT[dt], scale=d ** -0.5)
+    kr, kr_c = both((B, R, d), seed, "kr", dtype=DT[dt], scale=d ** -0.5)
+    vr, vr_c = both((B, R, d), seed, "vr", dtype=DT[dt], scale=d ** -0.5)
+    sk, sk_c = both((H,), seed, "sink", dtype=torch.float32)
+    return (q, kc, vc, kr, vr, sk), (q_c, kc_c, vc_c, kr_c, vr_c, sk_c)
+
+
+@pytest.mark.parametrize("dt,B,T,H,d,L,k,W,use_sink", [
+    ("bf16", 2, 1, 64, 512, 4000, 1024, 128, True),
+    ("bf16", 1, 3, 64, 256, 300, 100, 7, False),
+    ("bf16", 2, 2, 128, 128, 900, 64, 0, True),
+    ("bf16", 1, 2, 64, 128, 50, 64, 16, True),
+    ("bf16", 1, 520, 64, 128, 300, 64, 16, True),
+    ("f32", 1, 16, 8, 64, 1024, 64, 128, True),
+])
+def test_sparse_attn_matches_oracle(dt, B, T, H, d, L, k, W, use_sink):
+    import synthetic as syn
+    m = 4
+    n_ctx = L * m
+    R = T + max(W, 1) - 1
+    g, c = _attn_inputs(dt, B, T, H, d, L, R, 31 + d)
+    q, kc, vc, kr, vr, sk = g
+    q_c, kc_c, vc_c, kr_c, vr_c, sk_c = c
+    tpos = np.arange(n_ctx - T, n_ctx)
+    nv = np.minimum(tpos // m, L)
+    idx_c = syn.sample_indices(7, syn.TID["idx"], B * T, k, np.tile(nv, B) - 3).reshape(B, T, k)
+    idx = idx_c.cuda()
+    out, lse = csa.csa_sparse_attn(q, kc, vc, idx, kr=kr if W else None, vr=vr if W else None, W=W,
+                                   sink=sk if use_sink else None, n_ctx=n_ctx, want_lse=True)
+    torch.cuda.synchronize()
+    o_w, l_w = oracle.sparse_attn(q_c, kc_c, vc_c, idx_c.numpy(), kr_c, vr_c, W,
+                                  sink=sk_c if use_sink else None, n_ctx=n_ctx)
+    assert max_abs(to_np(out), o_w) <= TOL[dt]
+    assert max_abs(to_np(lse), l_w) <= 1e-3
+
+
+@pytest.mark.parametrize("dt,B,T,H,d,L,m,W", [
+    ("bf16", 2, 1, 64, 512, 3000, 128, 0),
+    ("bf16", 1, 2, 64, 512, 700, 4, 128),
+    ("bf16", 1, 40, 64, 128, 100, 4, 16),
+    ("bf16", 1, 520, 64, 128, 200, 4, 16),
+    ("f32", 1, 2, 8, 64, 500, 4, 128),
+])
+def test_dense_attn_matches_oracle(dt, B, T, H, d, L, m, W):
+    n_ctx = L * m - (m // 2)
+    R = T + max(W, 1) - 1
+    g, c = _attn_inputs(dt, B, T, H, d, L, R, 41 + L)
+    q, kc, vc, kr, vr, sk = g
+    q_c, kc_c, vc_c, kr_c, vr_c, sk_c = c
+    out, lse = csa.hca_dense_attn(q, kc, vc, m, kr=kr if W else None, vr=vr if W else None, W=W, sink=sk,
+                                  n_ctx=n_ctx, want_lse=True)
+    torch.cuda.synchronize()
+    o_w, l_w = oracle.dense_attn(q_c, kc_c, vc_c, m, kr_c, vr_c, W, sink=sk_c, n_ctx=n_ctx)
+    assert max_abs(to_np(out), o_w) <= TOL[dt]
+    assert max_abs(to_np(lse), l_w) <= 1e-3
+
+
+def test_sparse_with_all_entries_equals_dense_on_gpu():
+    B, T, H, d, L, m, W = 2, 1, 64, 512, 600, 4, 128
+    n_ctx = L * m
+    R = T + W - 1
+    g, _ = _attn_inputs("bf16", B, T, H, d, L, R, 77)
+    q, kc, vc, kr, vr, sk = g
+    nv = (n_ctx - 1) // m
+    idx = torch.full((B, T, 640), -1, dtype=torch.int32, device="cuda")
+    idx[..., :nv] = torch.arange(nv, dtype=torch.int32, device="cuda")
+    a = csa.csa_sparse_attn(q, kc, vc, idx, kr=kr, vr=vr, W=W, sink=sk, n_ctx=n_ctx)
+    b = csa.hca_dense_attn(q, kc, vc, m, kr=kr, vr=vr, W=W, sink=sk, n_ctx=n_ctx)
+    torch.cuda.synchronize()
+    assert max_abs(to_np(a), to_np(b)) <= 4e-3
+
+
+def test_generator_is_bit_identical_on_both_devices():
+    import synthetic as syn
+    for kind in ("normal", "uniform", "grid"):
+        a = syn.make((3, 1000, 72), 9, 4, dtype=torch.bfloat16, device="cuda", kind=kind, scale=0.25)
+        b = syn.make((3, 1000, 72), 9, 4, dtype=torch.bfloat16, device="cpu", kind=kind, scale=0.25)
+        assert torch.equal(a.cpu(), b)
