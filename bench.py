@@ -1,0 +1,413 @@
+#!/usr/bin/env python3
+"""Decode benchmark of the CSA / HCA hybrid attention hot path on one MI355X.
+
+Workload (the 1M-context configuration): an interleaved stack of 8 attention
+layers, CSA (m = 4, two-path compression, Lightning Indexer with 64 heads x
+128, top-1024, 128-token window, sinks) alternating with HCA (m = 128, dense,
+128-token window, sinks); 64 query heads x d = 512 sharing one KV head; bf16
+storage, fp32 accumulation; n_ctx = 1,000,000 tokens; batch 16.  All eight
+layers' compressed caches are resident in HBM (about 2.4 GB per sequence).
+
+One step decodes the token at position t = n_ctx - 1 of every sequence
+through all 8 layers.  Per CSA layer: csa_compress writes the entry whose
+block the new token completes (K, V and index keys, two-path), then the
+indexer scores every visible entry, top-k selects 1024 and csa_sparse_attn
+attends over them plus the window.  Per HCA layer: hca_compress refreshes the
+newest complete 128-token entry (K and V) and hca_dense_attn attends over all
+7812 visible entries plus the window.
+
+Metric: queries/s, a query being one token of one sequence through the whole
+8-layer stack (B queries per step), plus achieved HBM GB/s of the step and
+the roofline of the dominant kernel (the indexer scan), timed with HIP events
+on the stream the kernels run on.  The CPU oracle is timed on a bounded
+sample of the same step (a few sequences) as a reported baseline.
+
+Usage: python bench.py [--steps K] [--warmup W] [--batch B] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import synthetic as syn  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+SEED = 5
+
+
+class Stack:
+    """Shapes of the 8-layer decode workload."""
+
+    def __init__(self, B=16, n_ctx=1_000_000, layers=8):
+        self.B, self.n_ctx, self.layers = B, n_ctx, layers
+        self.H, self.d = 64, 512
+        self.HI, self.dI = 64, 128
+        self.k, self.W = 1024, 128
+        self.m_csa, self.m_hca = 4, 128
+        self.L_csa = -(-n_ctx // self.m_csa)
+        self.L_hca = -(-n_ctx // self.m_hca)
+        self.t = n_ctx - 1
+        self.nv_csa = min(self.L_csa, self.t // self.m_csa)
+        self.nv_hca = min(self.L_hca, self.t // self.m_hca)
+        # CSA: the block holding t is complete after t arrives; its entry is new.
+        self.csa_new = self.t // self.m_csa if (self.t + 1) % self.m_csa == 0 else self.nv_csa - 1
+        # HCA: the newest complete 128-token entry (visible to t).
+        self.hca_new = self.nv_hca - 1
+        self.scale = 1.0 / math.sqrt(self.d)
+
+    def kinds(self):
+        return ["csa" if i % 2 == 0 else "hca" for i in range(self.layers)]
+
+    # ---- algorithmic bytes (what the method must move), per query ----------
+    def index_bytes(self):
+        return self.nv_csa * self.dI * 2 + self.HI * self.dI * 2
+
+    def csa_bytes(self):
+        b = self.index_bytes()
+        b += self.k * self.d * 2 * 2            # gathered compressed K and V rows
+        b += self.W * self.d * 2 * 2            # raw window K and V
+        b += 2 * self.H * self.d * 2            # q and out
+        b += self.k * 4                         # selected indices
+        m = self.m_csa
+        b += 4 * 2 * m * (2 * self.d + self.dI) * 2 // 2  # compress: x/z, A and B paths, K V I
+        b += (2 * self.d + self.dI) * 2         # new entries
+        return b
+
+    def hca_bytes(self):
+        b = self.nv_hca * self.d * 2 * 2 + self.W * self.d * 2 * 2 + 2 * self.H * self.d * 2
+        b += 2 * 2 * self.m_hca * self.d * 2 + 2 * self.d * 2  # compress K, V
+        return b
+
+    def step_bytes(self):
+        per = sum(self.csa_bytes() if k == "csa" else self.hca_bytes() for k in self.kinds())
+        return per * self.B
+
+
+def raw_rows(st: Stack, name, layer, p0, cnt, D, device, scale):
+    """Rows p0 .. p0+cnt-1 of a virtual raw stream [B][n_ctx][D]."""
+    b = torch.arange(st.B, dtype=torch.int64, device=device).reshape(-1, 1)
+    p = torch.arange(p0, p0 + cnt, dtype=torch.int64, device=device).reshape(1, -1)
+    r = (b * st.n_ctx + p).reshape(-1)
+    return syn.rows((st.B, st.n_ctx, D), r, SEED, syn.TID[name], dtype=torch.bfloat16, device=device,
+                    scale=scale, layer=layer).reshape(st.B, cnt, D)
+
+
+class GpuState:
+    """All device buffers of the workload, generated in place on the GPU."""
+
+    def __init__(self, st: Stack, device="cuda"):
+        import compressed_sparse_kv_compress_amd as csa
+        self.csa = csa
+        self.st = st
+        bf = torch.bfloat16
+        B, d, dI, H = st.B, st.d, st.dI, st.H
+        sd, si = d ** -0.5, dI ** -0.5
+        self.layers = []
+        for li, kind in enumerate(st.kinds()):
+            L = st.L_csa if kind == "csa" else st.L_hca
+            lay = {"kind": kind}
+
+            def gen(shape, name, scale, dtype=bf, li=li):
+                t = torch.empty(shape, dtype=dtype, device=device)
+                return syn.fill_(t, SEED, syn.TID[name], scale=scale, layer=li)
+
+            lay["kc"] = gen((B, L, d), "kc", sd)
+            lay["vc"] = gen((B, L, d), "vc", sd)
+            lay["q"] = gen((B, 1, H, d), "q", sd)
+            lay["sink"] = gen((H,), "sink", 1.0, torch.float32)
+            lay["kr"] = raw_rows(st, "kr", li, st.n_ctx - st.W, st.W, d, device, sd)
+            lay["vr"] = raw_rows(st, "vr", li, st.n_ctx - st.W, st.W, d, device, sd)
+            lay["out"] = torch.empty((B, 1, H, d), dtype=bf, device=device)
+            if kind == "csa":
+                m = st.m_csa
+                lay["ki"] = gen((B, L, dI), "kic", si)
+                lay["qi"] = gen((B, 1, st.HI, dI), "q_idx", si)
+                p0 = (st.csa_new - 1) * m
+                for s, D, sc in (("k", d, sd), ("v", d, sd), ("idx", dI, si)):
+                    xa = "k" if s == "k" else ("v" if s == "v" else "k_idx")
+                    lay["raw_" + s] = (
+                        raw_rows(st, xa, li, p0, 2 * m, D, device, sc),
+                        raw_rows(st, "z_" + s, li, p0, 2 * m, D, device, 0.5),
+                        raw_rows(st, "xb_" + s, li, p0, 2 * m, D, device, sc),
+                        raw_rows(st, "zb_" + s, li, p0, 2 * m, D, device, 0.5))
+                lay["p0"] = p0
+                lay["idx"] = torch.empty((B, 1, st.k), dtype=torch.int32, device=device)
+                lay["score"] = torch.empty((B, 1, L), dtype=torch.float32, device=device)
+                lay["topk_ws"] = torch.empty(max(16, csa.csa_topk_select_workspace(B, 1, L, st.k)),
+                                             dtype=torch.uint8, device=device)
+                nb = csa.csa_sparse_attn_workspace(B, 1, H, d, st.k, st.W, csa.CSA_BF16)
+            else:
+                m = st.m_hca
+                p0 = st.hca_new * m
+                lay["raw_k"] = (raw_rows(st, "k", li, p0, m, d, device, sd),
+                                raw_rows(st, "z_k", li, p0, m, d, device, 0.5))
+                lay["raw_v"] = (raw_rows(st, "v", li, p0, m, d, device, sd),
+                                raw_rows(st, "z_v", li, p0, m, d, device, 0.5))
+                lay["p0"] = p0
+                nb = csa.hca_dense_attn_workspace(B, 1, H, d, L, m, st.n_ctx, st.W, csa.CSA_BF16)
+            lay["ws"] = torch.empty(max(nb, 16), dtype=torch.uint8, device=device)
+            self.layers.append(lay)
+        torch.cuda.synchronize()
+
+    def step(self, ev=None):
+        """One decode step through all layers.  ev: optional dict of event lists
+        keyed by call name; events bracket each call on the current stream."""
+        csa, st = self.csa, self.st
+
+        def mark(name):
+            if ev is None:
+                return None
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            ev.setdefault(name, []).append(e)
+            return e
+
+        for lay in self.layers:
+            if lay["kind"] == "csa":
+                m = st.m_csa
+                mark("csa_compress")
+                for s, cache in (("k", "kc"), ("v", "vc"), ("idx", "ki")):
+                    xa, za, xb, zb = lay["raw_" + s]
+                    L = lay[cache].shape[1]
+                    csa.csa_compress(xa, za, m, x_b=xb, z_b=zb, n=st.n_ctx, p0=lay["p0"],
+                                     e0=st.csa_new, e1=st.csa_new + 1, out=lay[cache][:, st.csa_new:],
+                                     out_ld=L)
+                mark("csa_compress_end")
+                mark("index_score")
+                csa.csa_index_score(lay["qi"], lay["ki"], m, n_ctx=st.n_ctx, out=lay["score"])
+                mark("index_score_end")
+                mark("topk_select")
+                csa.csa_topk_select(lay["score"], m, st.k, n_ctx=st.n_ctx, idx=lay["idx"], ws=lay["topk_ws"])
+                mark("topk_select_end")
+                mark("csa_sparse_attn")
+                csa.csa_sparse_attn(lay["q"], lay["kc"], lay["vc"], lay["idx"], kr=lay["kr"], vr=lay["vr"],
+                                    W=st.W, sink=lay["sink"], n_ctx=st.n_ctx, out=lay["out"], ws=lay["ws"])
+                mark("csa_sparse_attn_end")
+            else:
+                m = st.m_hca
+                mark("hca_compress")
+                for s, cache in (("k", "kc"), ("v", "vc")):
+                    x, z = lay["raw_" + s]
+                    L = lay[cache].shape[1]
+                    csa.hca_compress(x, z, m, n=st.n_ctx, p0=lay["p0"], e0=st.hca_new,
+                                     e1=st.hca_new + 1, out=lay[cache][:, st.hca_new:], out_ld=L)
+                mark("hca_compress_end")
+                mark("hca_dense_attn")
+                csa.hca_dense_attn(lay["q"], lay["kc"], lay["vc"], m, kr=lay["kr"], vr=lay["vr"], W=st.W,
+                                   sink=lay["sink"], n_ctx=st.n_ctx, out=lay["out"], ws=lay["ws"])
+                mark("hca_dense_attn_end")
+
+
+def event_means_ms(ev):
+    """Average duration per call name (ms) from start/end event pairs."""
+    res = {}
+    for name, starts in ev.items():
+        if name.endswith("_end"):
+            continue
+        ends = ev[name + "_end"]
+        ts = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+        res[name] = sum(ts) / len(ts)
+    return res
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic(kernel_src, per_launch_units):
+    """HBM bytes per launch of the indexer scan from the committed rocprofv3
+    counter summary, or None when it is missing or the kernel source changed."""
+    path = os.path.join(ROOT, "profiles", "index_score_stack8_b16_counters.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_src = re.search(r"^source_sha256_16:\s*(\w+)", txt, re.M)
+    m_b = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    m_u = re.search(r"^queries_per_launch:\s*(\d+)", txt, re.M)
+    if not (m_src and m_b and m_u) or m_src.group(1) != source_hash(kernel_src):
+        return None
+    return float(m_b.group(1)) * per_launch_units / int(m_u.group(1))
+
+
+def cpu_baseline(st: Stack, sample: int):
+    """Time the CPU oracle on `sample` sequences of the same decode step.
+
+    Inputs are regenerated on the CPU from the same seeds (not timed); the
+    oracle calls (compression of the new entries, indexer + top-k, sparse
+    attention, dense attention) are timed."""
+    import numpy as np
+
+    import oracle
+    bf = torch.bfloat16
+    S = min(sample, st.B)
+    sd, si = st.d ** -0.5, st.dI ** -0.5
+    total = 0.0
+
+    def full(shape, name, scale, li, rows=None, dtype=bf):
+        D = shape[-1]
+        if rows is None:
+            return syn.make(shape, SEED, syn.TID[name], dtype=dtype, scale=scale, layer=li).double().numpy()
+        return syn.rows(shape, rows, SEED, syn.TID[name], dtype=dtype, scale=scale,
+                        layer=li).double().numpy().reshape(-1, D)
+
+    sub = Stack(B=S, n_ctx=st.n_ctx, layers=st.layers)
+    for li, kind in enumerate(st.kinds()):
+        L = st.L_csa if kind == "csa" else st.L_hca
+        seq_rows = lambda b, n: np.arange(b * n, (b + 1) * n)  # noqa: E731
+        q = np.stack([full((st.B, 1, st.H, st.d), "q", sd, li, rows=np.arange(b * st.H, (b + 1) * st.H))
+                      for b in range(S)]).reshape(S, 1, st.H, st.d)
+        sink = full((st.H,), "sink", 1.0, li, dtype=torch.float32)
+        kr = np.stack([raw_rows(sub, "kr", li, st.n_ctx - st.W, st.W, st.d, "cpu", sd)[b].double().numpy()
+                       for b in range(S)])
+        vr = np.stack([raw_rows(sub, "vr", li, st.n_ctx - st.W, st.W, st.d, "cpu", sd)[b].double().numpy()
+                       for b in range(S)])
+        if kind == "csa":
+            m = st.m_csa
+            p0 = (st.csa_new - 1) * m
+            raws = {}
+            for s, D, sc in (("k", st.d, sd), ("v", st.d, sd), ("idx", st.dI, si)):
+                xa = "k" if s == "k" else ("v" if s == "v" else "k_idx")
+                raws[s] = [raw_rows(sub, nm, li, p0, 2 * m, D, "cpu", scl).double().numpy()
+                           for nm, scl in ((xa, sc), ("z_" + s, 0.5), ("xb_" + s, sc), ("zb_" + s, 0.5))]
+            ki = np.stack([full((st.B, L, st.dI), "kic", si, li, rows=seq_rows(b, L)) for b in range(S)])
+            qi = np.stack([full((st.B, 1, st.HI, st.dI), "q_idx", si, li,
+                                rows=np.arange(b * st.HI, (b + 1) * st.HI)) for b in range(S)])
+            qi = qi.reshape(S, 1, st.HI, st.dI)
+            t0 = time.perf_counter()
+            for s in ("k", "v", "idx"):
+                xa, za, xb, zb = raws[s]
+                oracle.compress(xa, za, m, x_b=xb, z_b=zb, n=st.n_ctx, p0=p0, e0=st.csa_new,
+                                e1=st.csa_new + 1)
+            idx, _ = oracle.index_topk(qi, ki, m, st.k, n_ctx=st.n_ctx)
+            total += time.perf_counter() - t0
+            # gather only the selected rows of the compressed K/V caches
+            kc = np.zeros((S, st.k, st.d))
+            vc = np.zeros((S, st.k, st.d))
+            loc = np.full_like(idx, -1)
+            for b in range(S):
+                sel = idx[b, 0][idx[b, 0] >= 0]
+                kc[b, :len(sel)] = full((st.B, L, st.d), "kc", sd, li, rows=b * L + sel)
+                vc[b, :len(sel)] = full((st.B, L, st.d), "vc", sd, li, rows=b * L + sel)
+                loc[b, 0, :len(sel)] = np.arange(len(sel))
+            t0 = time.perf_counter()
+            oracle.sparse_attn(q, kc, vc, loc, kr, vr, st.W, sink=sink, n_ctx=st.n_ctx)
+            total += time.perf_counter() - t0
+        else:
+            m = st.m_hca
+            p0 = st.hca_new * m
+            raws = [raw_rows(sub, nm, li, p0, m, st.d, "cpu", scl).double().numpy()
+                    for nm, scl in (("k", sd), ("z_k", 0.5), ("v", sd), ("z_v", 0.5))]
+            kc = np.stack([full((st.B, L, st.d), "kc", sd, li, rows=seq_rows(b, L)) for b in range(S)])
+            vc = np.stack([full((st.B, L, st.d), "vc", sd, li, rows=seq_rows(b, L)) for b in range(S)])
+            t0 = time.perf_counter()
+            oracle.compress(raws[0], raws[1], m, n=st.n_ctx, p0=p0, e0=st.hca_new, e1=st.hca_new + 1)
+            oracle.compress(raws[2], raws[3], m, n=st.n_ctx, p0=p0, e0=st.hca_new, e1=st.hca_new + 1)
+            oracle.dense_attn(q, kc, vc, m, kr, vr, st.W, sink=sink, n_ctx=st.n_ctx)
+            total += time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": S / total, "unit": "queries/s", "cores": min(S, threads), "kind": "oracle",
+            "sample": "%d of %d sequences, one decode step through all %d layers (%.1f s of oracle time)"
+                      % (S, st.B, st.layers, total)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--batch", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=4)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sharding and collectives are out of scope); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    torch.cuda.set_device(0)
+    st = Stack(B=args.batch)
+    t_gen = time.perf_counter()
+    state = GpuState(st)
+    t_gen = time.perf_counter() - t_gen
+    print("# inputs generated on the GPU in %.1f s" % t_gen, file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        state.step()
+    torch.cuda.synchronize()
+    print("# warmup done", file=sys.stderr, flush=True)
+
+    ev = {}
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        state.step(ev)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(stop) / args.steps
+    per_call = event_means_ms(ev)
+    print("# timed %d steps: %.3f ms/step (wall %.3f ms/step)" % (args.steps, ms_step, 1e3 * wall / args.steps),
+          file=sys.stderr, flush=True)
+
+    value = st.B / (ms_step * 1e-3)
+    step_gbps = st.step_bytes() / (ms_step * 1e-3) / 1e9
+    idx_ms = per_call["index_score"]
+    idx_bytes = st.index_bytes() * st.B
+    idx_gbps = idx_bytes / (idx_ms * 1e-3) / 1e9
+    traffic = counter_traffic(os.path.join(ROOT, "compressed_sparse_kv_compress_amd", "csrc", "index.hip"),
+                              st.B)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(st, args.cpu_sample)
+
+    line = {
+        "metric": "CSA/HCA decode queries/s at 1M ctx + achieved HBM GB/s (% peak)",
+        "value": value,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/sqrt(dim) tensors, compressed caches generated in HBM)",
+        "config": {
+            "workload": "csa_hca_stack8_decode_1M",
+            "query": "one token of one sequence through all 8 layers",
+            "batch": st.B, "n_ctx": st.n_ctx, "layers": "4 CSA (two-path m=4) + 4 HCA (m=128), alternating",
+            "heads": st.H, "head_dim": st.d, "index_heads": st.HI, "index_dim": st.dI, "top_k": st.k,
+            "window": st.W, "csa_entries": st.L_csa, "hca_entries": st.L_hca,
+        },
+        "hbm": {"algorithmic_bytes_per_step": st.step_bytes(), "achieved_GBps": step_gbps,
+                "frac_of_peak": step_gbps / HBM_PEAK_GBPS},
+        "roofline": {"kernel": "index_score (csa_index_score)", "bound": "hbm", "achieved": idx_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": idx_gbps / HBM_PEAK_GBPS,
+                     "traffic": traffic, "avg_launch_ms": idx_ms,
+                     "algorithmic_bytes_per_launch": idx_bytes},
+        "per_call_ms": per_call,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

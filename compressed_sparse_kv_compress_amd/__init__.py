@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        "libcsa.so is not built: run `python -m compressed_sparse_kv_compress_amd.build` "
+        "libcsa.so is not built: run `python compressed_sparse_kv_compress_amd/build.py` "
         "(the HIP library is the only implementation)")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -49,8 +49,9 @@ def _sig(name, args, res=_i32):
 _csa_compress = _sig("csa_compress", [_vp] * 6 + [_i64] * 9 + [_i32, _vp])
 _hca_compress = _sig("hca_compress", [_vp] * 4 + [_i64] * 9 + [_i32, _vp])
 _csa_index_score = _sig("csa_index_score", [_vp] * 3 + [_i64] * 7 + [_vp, _i32, _vp])
-_csa_topk_select = _sig("csa_topk_select", [_vp] + [_i64] * 6 + [_vp, _vp, _vp])
-_csa_index_topk_workspace = _sig("csa_index_topk_workspace", [_i64] * 3, _sz)
+_csa_topk_select_workspace = _sig("csa_topk_select_workspace", [_i64] * 4, _sz)
+_csa_topk_select = _sig("csa_topk_select", [_vp] + [_i64] * 6 + [_vp, _vp, _vp, _sz, _vp])
+_csa_index_topk_workspace = _sig("csa_index_topk_workspace", [_i64] * 4, _sz)
 _csa_index_topk = _sig("csa_index_topk", [_vp] * 3 + [_i64] * 8 + [_vp, _vp, _vp, _sz, _i32, _vp])
 _csa_sparse_attn_workspace = _sig("csa_sparse_attn_workspace", [_i64] * 6 + [_i32], _sz)
 _csa_sparse_attn = _sig("csa_sparse_attn", [_vp] * 3 + [_i64, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _f32]
@@ -151,20 +152,27 @@ def csa_index_score(q_idx, k_idx, m, *, w_idx=None, n_ctx, out=None):
     return out
 
 
-def csa_topk_select(score, m, k, *, n_ctx, idx=None, out_score=None, want_scores=False):
+def csa_topk_select_workspace(B, T, L, k) -> int:
+    return int(_csa_topk_select_workspace(B, T, L, k))
+
+
+def csa_topk_select(score, m, k, *, n_ctx, idx=None, out_score=None, want_scores=False, ws=None):
     B, T, L = score.shape
     if idx is None:
         idx = torch.empty((B, T, k), dtype=torch.int32, device=score.device)
     if want_scores and out_score is None:
         out_score = torch.empty((B, T, k), dtype=torch.float32, device=score.device)
+    if ws is None:
+        ws = torch.empty(max(16, csa_topk_select_workspace(B, T, L, k)), dtype=torch.uint8,
+                         device=score.device)
     st = _csa_topk_select(_ptr(score), B, T, n_ctx, L, m, k, idx.data_ptr(), _ptr(out_score),
-                          _stream(score.device))
+                          ws.data_ptr(), ws.numel() * ws.element_size(), _stream(score.device))
     _check(st, "csa_topk_select")
     return (idx, out_score) if want_scores else idx
 
 
-def csa_index_topk_workspace(B, T, L) -> int:
-    return int(_csa_index_topk_workspace(B, T, L))
+def csa_index_topk_workspace(B, T, L, k) -> int:
+    return int(_csa_index_topk_workspace(B, T, L, k))
 
 
 def csa_index_topk(q_idx, k_idx, m, k, *, w_idx=None, n_ctx, ws=None, idx=None, out_score=None,
@@ -176,7 +184,7 @@ def csa_index_topk(q_idx, k_idx, m, k, *, w_idx=None, n_ctx, ws=None, idx=None, 
     if want_scores and out_score is None:
         out_score = torch.empty((B, T, k), dtype=torch.float32, device=q_idx.device)
     if ws is None:
-        nb = max(16, csa_index_topk_workspace(B, T, L))
+        nb = max(16, csa_index_topk_workspace(B, T, L, k))
         ws = torch.empty(nb, dtype=torch.uint8, device=q_idx.device)
     st = _csa_index_topk(_ptr(q_idx), _ptr(w_idx), _ptr(k_idx), B, T, n_ctx, L, HI, dI, m, k,
                          idx.data_ptr(), _ptr(out_score), ws.data_ptr(), ws.numel() * ws.element_size(),

@@ -1,6 +1,6 @@
 """Build libcsa.so (the gfx950 HIP kernels and their C ABI) in-tree.
 
-    python -m compressed_sparse_kv_compress_amd.build
+    python compressed_sparse_kv_compress_amd/build.py
 
 Compiles every csrc/*.hip and csrc/*.cpp with hipcc for gfx950 only and links
 them into compressed_sparse_kv_compress_amd/libcsa.so.  Always rebuilds.
@@ -30,9 +30,9 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+def _compile(src: str, obj_dir: str = OBJ, extra=()) -> str:
+    obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,21 +41,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, extra=()) -> str:
+    """Compile and link; `extra` adds compiler flags (e.g. -D tuning constants)."""
+    obj_dir = OBJ if out == LIB else os.path.join(os.path.dirname(os.path.abspath(out)), "_obj")
+    os.makedirs(obj_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     workers = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda f: _compile(f, obj_dir, tuple(extra)), srcs))
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -171,21 +171,36 @@ csa_status_t csa_index_score(const void* q_idx, const float* w_idx, const void* 
                     "index score launch");
 }
 
+size_t csa_topk_select_workspace(int64_t B, int64_t T, int64_t L, int64_t k) {
+  if (B <= 0 || T <= 0 || k <= 0) return 0;
+  return static_cast<size_t>(B) * T * csa::topk_ws_bytes_per_row(L, k);
+}
+
 csa_status_t csa_topk_select(const float* score, int64_t B, int64_t T, int64_t n_ctx, int64_t L,
-                             int64_t m, int64_t k, int32_t* idx, float* out_score, void* stream) {
+                             int64_t m, int64_t k, int32_t* idx, float* out_score, void* ws,
+                             size_t ws_bytes, void* stream) {
   REQUIRE(B >= 0 && T >= 1 && n_ctx >= T && L >= 0 && m >= 1, "need B >= 0, 1 <= T <= n_ctx, L >= 0, m >= 1");
   REQUIRE(k >= 1 && k <= (1 << 20), "k=%lld outside [1, 2^20]", (long long)k);
   if (B == 0) return CSA_OK;
   if (L > 0) REQUIRE_PTR(score);
   REQUIRE_PTR(idx);
   OPT_PTR(out_score);
+  const size_t need = csa_topk_select_workspace(B, T, L, k);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "top-k needs %zu workspace bytes, got %zu", need, ws_bytes);
+  if (!aligned16(ws)) return fail(CSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
   csa::TopkArgs a{score, L, 0, B * T, T, n_ctx, L, m, k, idx, out_score};
-  return hip_status(csa::launch_topk(a, static_cast<hipStream_t>(stream)), "top-k launch");
+  return hip_status(csa::launch_topk(a, ws, static_cast<hipStream_t>(stream)), "top-k launch");
 }
 
-size_t csa_index_topk_workspace(int64_t B, int64_t T, int64_t L) {
-  if (B <= 0 || T <= 0 || L <= 0) return 0;
-  return static_cast<size_t>(B) * T * L * sizeof(float);
+static size_t index_topk_row_bytes(int64_t L, int64_t k) {
+  const size_t sc = (static_cast<size_t>(L > 0 ? L : 0) * sizeof(float) + 255) / 256 * 256;
+  return sc + csa::topk_ws_bytes_per_row(L, k);
+}
+
+size_t csa_index_topk_workspace(int64_t B, int64_t T, int64_t L, int64_t k) {
+  if (B <= 0 || T <= 0 || k <= 0) return 0;
+  return static_cast<size_t>(B) * T * index_topk_row_bytes(L, k);
 }
 
 csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int64_t B,
@@ -200,16 +215,15 @@ csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k
   OPT_PTR(out_score);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t rows = B * T;
-  int64_t chunk = rows;
-  if (L > 0) {
-    if (ws == nullptr || ws_bytes < static_cast<size_t>(L) * sizeof(float))
-      return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes is below the minimum %zu", ws_bytes,
-                  static_cast<size_t>(L) * sizeof(float));
-    if (!aligned16(ws)) return fail(CSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
-    chunk = static_cast<int64_t>(ws_bytes / (static_cast<size_t>(L) * sizeof(float)));
-    if (chunk > rows) chunk = rows;
-  }
+  const size_t per_row = index_topk_row_bytes(L, k);
+  if (ws == nullptr || ws_bytes < per_row)
+    return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes is below the one-query minimum %zu", ws_bytes, per_row);
+  if (!aligned16(ws)) return fail(CSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+  int64_t chunk = static_cast<int64_t>(ws_bytes / per_row);
+  if (chunk > rows) chunk = rows;
+  const size_t sc_bytes = (static_cast<size_t>(chunk) * (L > 0 ? L : 0) * sizeof(float) + 255) / 256 * 256;
   float* sc = static_cast<float*>(ws);
+  void* sel_ws = static_cast<char*>(ws) + sc_bytes;
   for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
     const int64_t nr = r0 + chunk < rows ? chunk : rows - r0;
     if (L > 0) {
@@ -219,7 +233,7 @@ csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k
     }
     csa::TopkArgs t{sc, L, r0, nr, T, n_ctx, L, m, k, idx + r0 * k,
                     out_score ? out_score + r0 * k : nullptr};
-    st = hip_status(csa::launch_topk(t, s), "top-k launch");
+    st = hip_status(csa::launch_topk(t, sel_ws, s), "top-k launch");
     if (st != CSA_OK) return st;
   }
   return CSA_OK;

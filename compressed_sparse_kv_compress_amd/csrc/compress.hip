@@ -57,11 +57,12 @@ struct Io<false> {
   }
 };
 
-// Fold the candidate tokens [lo, hi) of one stream into the running
-// (max, denominator, numerator) of VEC channels.  Logits are in log2 units.
+// Fold the candidate tokens [lo, hi) of one stream (whose block starts at
+// seg_lo; bias row = bias_row0 + u - seg_lo) into the running (max,
+// denominator, numerator) of VEC channels.  Logits are in log2 units.
 template <bool BF16>
 __device__ __forceinline__ void fold_segment(const void* x, const void* z, const float* bias,
-                                             int64_t bias_row0, int64_t lo, int64_t hi,
+                                             int64_t bias_row0, int64_t seg_lo, int64_t lo, int64_t hi,
                                              int64_t row_base, int64_t p0, int64_t D,
                                              int64_t c0, float* mx, float* den, float* acc) {
   constexpr int VEC = Io<BF16>::VEC;
@@ -79,7 +80,7 @@ __device__ __forceinline__ void fold_segment(const void* x, const void* z, const
     for (int i = 0; i < kChunk; ++i) {
       if (u0 + i < hi) {
         if (bias) {
-          const float* br = bias + (bias_row0 + (u0 + i - lo)) * D + c0;
+          const float* br = bias + (bias_row0 + (u0 + i - seg_lo)) * D + c0;
 #pragma unroll
           for (int c = 0; c < VEC; ++c) lv[i][c] += br[c];
         }
@@ -112,15 +113,23 @@ __device__ __forceinline__ void fold_segment(const void* x, const void* z, const
   }
 }
 
-template <bool BF16>
+// S = 1: one thread per (entry, 16-byte channel group), for bulk launches.
+// S > 1: the candidate tokens of each segment are split over S thread slices
+// whose partial (max, denominator, numerator) are merged through LDS; used
+// when a launch has too few entries to fill the GPU (decode-time refresh).
+template <bool BF16, int S>
 __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
   constexpr int VEC = Io<BF16>::VEC;
+  constexpr int LANES = 256 / S;
+  const int slice = threadIdx.x / LANES;
+  const int lane = threadIdx.x % LANES;
   const int64_t nvec = a.D / VEC;
   const int64_t ne = a.e1 - a.e0;
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (gid >= a.B * ne * nvec) return;
-  const int64_t cv = gid % nvec;
-  const int64_t tmp = gid / nvec;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * LANES + lane;
+  const bool live = gid < a.B * ne * nvec;
+  const int64_t g = live ? gid : 0;
+  const int64_t cv = g % nvec;
+  const int64_t tmp = g / nvec;
   const int64_t jj = tmp % ne;
   const int64_t b = tmp / ne;
   const int64_t j = a.e0 + jj;
@@ -131,16 +140,52 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
 #pragma unroll
   for (int c = 0; c < VEC; ++c) { mx[c] = -INFINITY; den[c] = 0.f; acc[c] = 0.f; }
 
+  auto fold = [&](const void* x, const void* z, int64_t bias_row0, int64_t lo, int64_t hi) {
+    int64_t sl = lo, sh = hi;
+    if (S > 1) {
+      const int64_t per = (hi - lo + S - 1) / S;
+      sl = lo + slice * per;
+      sh = sl + per < hi ? sl + per : hi;
+    }
+    if (live && sl < sh)
+      fold_segment<BF16>(x, z, a.bias, bias_row0, lo, sl, sh, row_base, a.p0, a.D, c0, mx, den, acc);
+  };
   const bool two = a.x_b != nullptr;
-  if (two && j >= 1) {  // stream B: previous block, bias rows 0..m-1
-    fold_segment<BF16>(a.x_b, a.z_b, a.bias, 0, (j - 1) * a.m, j * a.m, row_base, a.p0, a.D, c0,
-                       mx, den, acc);
-  }
-  const int64_t lo = j * a.m;
+  if (two && j >= 1) fold(a.x_b, a.z_b, 0, (j - 1) * a.m, j * a.m);  // stream B, bias rows 0..m-1
   const int64_t hi = (j + 1) * a.m < a.n ? (j + 1) * a.m : a.n;
-  fold_segment<BF16>(a.x_a, a.z_a, a.bias, two ? a.m : 0, lo, hi, row_base, a.p0, a.D, c0, mx,
-                     den, acc);
+  fold(a.x_a, a.z_a, two ? a.m : 0, j * a.m, hi);
 
+  if (S > 1) {
+    __shared__ float part[3][S][LANES][VEC];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+      part[0][slice][lane][c] = mx[c];
+      part[1][slice][lane][c] = den[c];
+      part[2][slice][lane][c] = acc[c];
+    }
+    __syncthreads();
+    if (slice != 0) return;
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, part[0][s2][lane][c]);
+      float dd = 0.f, aa = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int s2 = 0; s2 < S; ++s2) {
+          const float ms = part[0][s2][lane][c];
+          if (ms == -INFINITY) continue;
+          const float f = fast_exp2(ms - M);
+          dd = fmaf(part[1][s2][lane][c], f, dd);
+          aa = fmaf(part[2][s2][lane][c], f, aa);
+        }
+      }
+      den[c] = dd;
+      acc[c] = aa;
+    }
+  }
+  if (!live) return;
   float o[VEC];
 #pragma unroll
   for (int c = 0; c < VEC; ++c) o[c] = den[c] > 0.f ? acc[c] / den[c] : 0.f;
@@ -153,11 +198,17 @@ hipError_t launch_compress(const CompressArgs& a, bool bf16, hipStream_t s) {
   const int vec = bf16 ? 8 : 4;
   const int64_t total = a.B * (a.e1 - a.e0) * (a.D / vec);
   if (total == 0) return hipSuccess;
-  const int64_t blocks = (total + 255) / 256;
-  if (bf16)
-    hipLaunchKernelGGL(compress_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(compress_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, a);
+  // Few entries with long blocks: spread each block's tokens over 16 slices.
+  const bool sliced = total < 32768 && a.m >= 32;
+  if (sliced) {
+    const dim3 grid(static_cast<uint32_t>((total + 15) / 16));
+    if (bf16) hipLaunchKernelGGL((compress_kernel<true, 16>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((compress_kernel<false, 16>), grid, dim3(256), 0, s, a);
+  } else {
+    const dim3 grid(static_cast<uint32_t>((total + 255) / 256));
+    if (bf16) hipLaunchKernelGGL((compress_kernel<true, 1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((compress_kernel<false, 1>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

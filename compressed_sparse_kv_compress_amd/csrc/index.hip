@@ -17,7 +17,7 @@
 // 32x32 output layout a lane holds one key column and 16 head rows, so the
 // ReLU and the weighted head sum are in-register FMAs plus one cross-half
 // lane exchange; the epilogue writes 32 fp32 scores (128 B) per tile.
-// The next tile's loads are issued before the current tile's MFMAs.
+// Each wavefront keeps three tiles (24 KiB) of keys in flight.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -25,10 +25,17 @@ namespace csa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kTilesPerWave = 8;
+#ifndef CSA_INDEX_TILES
+#define CSA_INDEX_TILES 8
+#endif
+#ifndef CSA_INDEX_DEPTH
+#define CSA_INDEX_DEPTH 3
+#endif
+constexpr int kTilesPerWave = CSA_INDEX_TILES;  // 32-key tiles streamed by one wavefront
+constexpr int kDepth = CSA_INDEX_DEPTH;         // tiles in flight per wavefront
 constexpr int kKeysPerWg = kWaves * kTilesPerWave * 32;
 
-template <int MB, int KS>
+template <int MB, int KS, bool HAS_W>
 __global__ __launch_bounds__(256) void index_score_mfma(IndexScoreArgs a, int64_t parts) {
   constexpr int HI = 32 * MB;
   constexpr int DI = 16 * KS;
@@ -56,6 +63,22 @@ __global__ __launch_bounds__(256) void index_score_mfma(IndexScoreArgs a, int64_
     return;
   }
 
+  // Key loads are unconditional (rows past the end are clamped to the last
+  // one), so the stream has no control flow and every tile of the prefetch
+  // window really is in flight.
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.L * DI + half * 8;
+  const int64_t s_last = a.L - 1;
+  auto load_tile = [&](int it, bf16x8* frag) {
+    int64_t s = wave_begin + it * 32 + col;
+    s = s < s_last ? s : s_last;
+    const uint16_t* p = kbase + s * DI;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) frag[ks] = *reinterpret_cast<const bf16x8*>(p + ks * 16);
+  };
+  bf16x8 buf[kDepth][KS];
+#pragma unroll
+  for (int i = 0; i < kDepth - 1; ++i) load_tile(i, buf[i]);
+
   // A operand: query heads (rows) x index dims, resident for the whole kernel.
   const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + row * HI * DI;
   bf16x8 afrag[MB][KS];
@@ -66,56 +89,41 @@ __global__ __launch_bounds__(256) void index_score_mfma(IndexScoreArgs a, int64_
       afrag[mb][ks] = *reinterpret_cast<const bf16x8*>(qrow + (mb * 32 + col) * DI + ks * 16 + half * 8);
 
   // Head weights for the 16 head rows this lane holds in each 32x32 block.
-  float wr[MB][16];
+  float wr[MB][HAS_W ? 16 : 1];
+  if (HAS_W) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int h = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-      wr[mb][r] = a.w ? a.w[row * HI + h] : 1.0f;
-    }
+      for (int r = 0; r < (HAS_W ? 16 : 1); ++r) {
+        const int h = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        wr[mb][r] = a.w[row * HI + h];
+      }
+  }
 
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.L * DI + half * 8;
-  auto load_tile = [&](int64_t s0, bf16x8* frag) {
-    int64_t s = s0 + col;
-    if (s >= a.L) s = a.L - 1;
-    const uint16_t* p = kbase + s * DI;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) frag[ks] = *reinterpret_cast<const bf16x8*>(p + ks * 16);
-  };
-
-  bf16x8 cur[KS], nxt[KS];
-  load_tile(wave_begin, cur);
 #pragma unroll
   for (int it = 0; it < kTilesPerWave; ++it) {
-    const int64_t s0 = wave_begin + it * 32;
-    const bool more = (it + 1 < kTilesPerWave) && (s0 + 32 < nv);
-    if (more) load_tile(s0 + 32, nxt);
-    if (s0 < nv) {
-      f32x16 acc[MB];
+    if (it + kDepth - 1 < kTilesPerWave) load_tile(it + kDepth - 1, buf[(it + kDepth - 1) % kDepth]);
+    const bf16x8* cur = buf[it % kDepth];
+    f32x16 acc[MB];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[mb][ks], cur[ks], acc[mb], 0, 0, 0);
-      float part_sum = 0.f;
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[mb][ks], cur[ks], acc[mb], 0, 0, 0);
+    float part_sum = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) part_sum = fmaf(wr[mb][r], fmaxf(acc[mb][r], 0.f), part_sum);
-      part_sum += __shfl_xor(part_sum, 32, 64);
-      const int64_t s = s0 + col;
-      if (half == 0 && s < a.L) srow[s] = (s < nv) ? part_sum : -INFINITY;
-    } else {
-      const int64_t s = s0 + col;
-      if (half == 0 && s < a.L) srow[s] = -INFINITY;
-    }
-    if (more) {
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) cur[ks] = nxt[ks];
-    }
+      for (int r = 0; r < 16; ++r) {
+        const float rl = fmaxf(acc[mb][r], 0.f);
+        part_sum = HAS_W ? fmaf(wr[mb][HAS_W ? r : 0], rl, part_sum) : part_sum + rl;
+      }
+    part_sum += __shfl_xor(part_sum, 32, 64);
+    const int64_t s = wave_begin + it * 32 + col;
+    const float val = s < nv ? part_sum : -INFINITY;
+    if (half == 0 && s < a.L) srow[s] = val;
   }
 }
 
@@ -158,12 +166,19 @@ hipError_t launch_index_score(const IndexScoreArgs& a, bool bf16, hipStream_t s)
     const int64_t parts = (a.L + kKeysPerWg - 1) / kKeysPerWg;
     const dim3 grid(static_cast<uint32_t>(a.nrows * parts));
     const int mb = static_cast<int>(a.HI / 32), ks = static_cast<int>(a.dI / 16);
-    if (mb == 2 && ks == 8) hipLaunchKernelGGL((index_score_mfma<2, 8>), grid, dim3(256), 0, s, a, parts);
-    else if (mb == 1 && ks == 8) hipLaunchKernelGGL((index_score_mfma<1, 8>), grid, dim3(256), 0, s, a, parts);
-    else if (mb == 2 && ks == 4) hipLaunchKernelGGL((index_score_mfma<2, 4>), grid, dim3(256), 0, s, a, parts);
-    else if (mb == 1 && ks == 4) hipLaunchKernelGGL((index_score_mfma<1, 4>), grid, dim3(256), 0, s, a, parts);
-    else if (mb == 4 && ks == 8) hipLaunchKernelGGL((index_score_mfma<4, 8>), grid, dim3(256), 0, s, a, parts);
-    else return hipErrorInvalidValue;
+    const bool w = a.w != nullptr;
+#define CSA_INDEX_LAUNCH(MB_, KS_)                                                                    \
+  if (mb == MB_ && ks == KS_) {                                                                       \
+    if (w) hipLaunchKernelGGL((index_score_mfma<MB_, KS_, true>), grid, dim3(256), 0, s, a, parts);   \
+    else hipLaunchKernelGGL((index_score_mfma<MB_, KS_, false>), grid, dim3(256), 0, s, a, parts);    \
+  } else
+    CSA_INDEX_LAUNCH(2, 8)
+    CSA_INDEX_LAUNCH(1, 8)
+    CSA_INDEX_LAUNCH(2, 4)
+    CSA_INDEX_LAUNCH(1, 4)
+    CSA_INDEX_LAUNCH(4, 8)
+    { return hipErrorInvalidValue; }
+#undef CSA_INDEX_LAUNCH
   } else {
     const int64_t parts = (a.L + 255) / 256;
     const size_t lds = static_cast<size_t>(a.HI * a.dI) * sizeof(float);

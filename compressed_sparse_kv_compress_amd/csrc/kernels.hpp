@@ -38,7 +38,9 @@ struct TopkArgs {
   int32_t* idx;        // [rows][k] (offset to row0 already)
   float* out_score;    // [rows][k] or null
 };
-hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+// ws: topk_ws_bytes_per_row(L, k) bytes per row of the launch.
+size_t topk_ws_bytes_per_row(int64_t L, int64_t k);
+hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t s);
 
 struct AttnArgs {
   const void* q;        // [B*T][H][d]

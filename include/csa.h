@@ -111,15 +111,19 @@ csa_status_t csa_index_score(const void* q_idx, const float* w_idx, const void* 
  * entry index.  idx int32 [B][T][k] receives the kept indices in ascending
  * order, -1 padded; out_score (NULL or fp32 [B][T][k]) their scores (-inf in
  * padded slots).  score is fp32 [B][T][L] and must hold no NaN among the
- * visible entries.  1 <= k <= 1048576. */
+ * visible entries.  1 <= k <= 1048576.  ws: csa_topk_select_workspace(B, T, L, k)
+ * bytes of device scratch for the per-part candidates. */
+size_t csa_topk_select_workspace(int64_t B, int64_t T, int64_t L, int64_t k);
 csa_status_t csa_topk_select(const float* score, int64_t B, int64_t T, int64_t n_ctx, int64_t L,
-                             int64_t m, int64_t k, int32_t* idx, float* out_score, void* stream);
+                             int64_t m, int64_t k, int32_t* idx, float* out_score, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* csa_index_topk -- csa_index_score followed by csa_topk_select, with the
- * fp32 score matrix kept in the caller's workspace.  When ws_bytes is below
- * csa_index_topk_workspace(B, T, L) the queries are processed in groups that
- * fit; ws_bytes must be at least 4*L.  Results do not depend on ws_bytes. */
-size_t csa_index_topk_workspace(int64_t B, int64_t T, int64_t L);
+ * fp32 score matrix and the selection scratch kept in the caller's workspace.
+ * When ws_bytes is below csa_index_topk_workspace(B, T, L, k) the queries are
+ * processed in groups that fit; ws_bytes must cover at least one query
+ * (csa_index_topk_workspace(1, 1, L, k)).  Results do not depend on ws_bytes. */
+size_t csa_index_topk_workspace(int64_t B, int64_t T, int64_t L, int64_t k);
 csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int64_t B,
                             int64_t T, int64_t n_ctx, int64_t L, int64_t H_I, int64_t d_I,
                             int64_t m, int64_t k, int32_t* idx, float* out_score, void* ws,

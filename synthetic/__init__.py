@@ -35,7 +35,7 @@ TID = {
     "z_k": 7, "z_v": 8, "z_idx": 9,
     "xb_k": 10, "xb_v": 11, "xb_idx": 12, "zb_k": 13, "zb_v": 14, "zb_idx": 15,
     "sink": 16, "kr": 17, "vr": 18, "kc": 19, "vc": 20, "bias": 21, "idx": 22,
-    "scores": 23,
+    "scores": 23, "kic": 24,
 }
 
 

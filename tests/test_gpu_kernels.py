@@ -67,6 +67,22 @@ def test_compress_decode_slot_equals_bulk():
     assert torch.count_nonzero(cache[:, : L - 1]) == 0 and torch.count_nonzero(cache[:, L:]) == 0
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,D,m,n", [(16, 512, 128, 1_000_000), (3, 128, 128, 5000), (2, 64, 64, 130)])
+def test_compress_single_entry_decode_refresh(dt, B, D, m, n):
+    # few entries with long blocks take the token-sliced path; raw rows cover
+    # only the newest complete block
+    e = n // m - 1
+    p0 = e * m
+    xs, xs_c = both((B, m, D), 3 + D, "k", dtype=DT[dt], scale=D ** -0.5)
+    zs, zs_c = both((B, m, D), 3 + D, "z_k", dtype=DT[dt], scale=0.5)
+    bias, bias_c = both((m, D), 3 + D, "bias", dtype=torch.float32, scale=0.3)
+    got = csa.hca_compress(xs, zs, m, bias=bias, n=n, p0=p0, e0=e, e1=e + 1)
+    torch.cuda.synchronize()
+    want = oracle.compress(xs_c, zs_c, m, bias=bias_c, n=n, p0=p0, e0=e, e1=e + 1)
+    assert max_abs(to_np(got), want) <= TOL[dt]
+
+
 # ---------------------------------------------------------------------------
 # indexer scores and top-k
 # ---------------------------------------------------------------------------
@@ -148,7 +164,7 @@ def test_index_topk_bit_exact_on_grid_inputs():
     want, _ = oracle.index_topk(q_c, k_c, m, k, n_ctx=n_ctx)
     assert np.array_equal(got, want)
     # a workspace holding one row at a time gives the same result
-    ws = torch.empty(L * 4, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(csa.csa_index_topk_workspace(1, 1, L, k), dtype=torch.uint8, device="cuda")
     got2 = csa.csa_index_topk(q, kk, m, k, n_ctx=n_ctx, ws=ws).cpu().numpy()
     assert np.array_equal(got2, want)
 
