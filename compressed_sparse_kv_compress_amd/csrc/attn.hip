@@ -169,8 +169,8 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a, int nsplit) {
       const int64_t off = (cmp ? s : v + win0) * D + pc * 8;
       const uint16_t* kb = ok ? (cmp ? kcb : krb) + off : dummy + pc * 8;
       const uint16_t* vb = ok ? (cmp ? vcb : vrb) + off : dummy + pc * 8;
-      kp[i] = *reinterpret_cast<const u32x4*>(kb);
-      vp[i] = *reinterpret_cast<const u32x4*>(vb);
+      kp[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb));
+      vp[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb));
       okmask |= static_cast<uint32_t>(ok) << i;
     }
   };

@@ -57,38 +57,48 @@ struct Io<false> {
   }
 };
 
-// Fold the candidate tokens [lo, hi) of one stream (whose block starts at
-// seg_lo; bias row = bias_row0 + u - seg_lo) into the running (max,
+// The candidates of entry j form one virtual list: stream-B tokens
+// (j-1)*m .. j*m-1 first (two-path, j >= 1), then stream-A tokens
+// j*m .. min((j+1)*m, n)-1.  Candidate i maps to its stream, raw row and
+// bias row here.
+struct Cands {
+  int64_t nb, na, b_lo, a_lo, a_bias0;
+};
+
+// Fold candidates [lo, hi) of the virtual list into the running (max,
 // denominator, numerator) of VEC channels.  Logits are in log2 units.
 template <bool BF16>
-__device__ __forceinline__ void fold_segment(const void* x, const void* z, const float* bias,
-                                             int64_t bias_row0, int64_t seg_lo, int64_t lo, int64_t hi,
-                                             int64_t row_base, int64_t p0, int64_t D,
-                                             int64_t c0, float* mx, float* den, float* acc) {
+__device__ __forceinline__ void fold_range(const CompressArgs& a, const Cands& cd, int64_t lo, int64_t hi,
+                                           int64_t row_base, int64_t c0, float* mx, float* den, float* acc) {
   constexpr int VEC = Io<BF16>::VEC;
-  for (int64_t u0 = lo; u0 < hi; u0 += kChunk) {
+  for (int64_t i0 = lo; i0 < hi; i0 += kChunk) {
+    // All 2 x kChunk loads are issued unconditionally (candidates past the
+    // end re-read the last one and are masked below), so they are all in
+    // flight together instead of being serialised by control flow.
     float xv[kChunk][VEC], lv[kChunk][VEC];
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
-      if (u0 + i < hi) {
-        const int64_t off = (row_base + (u0 + i - p0)) * D + c0;
-        Io<BF16>::load(x, off, xv[i]);
-        Io<BF16>::load(z, off, lv[i]);
-      }
+      const int64_t ci = i0 + i < hi ? i0 + i : hi - 1;
+      const bool from_b = ci < cd.nb;
+      const int64_t u = from_b ? cd.b_lo + ci : cd.a_lo + (ci - cd.nb);
+      const int64_t off = (row_base + (u - a.p0)) * a.D + c0;
+      Io<BF16>::load(from_b ? a.x_b : a.x_a, off, xv[i]);
+      Io<BF16>::load(from_b ? a.z_b : a.z_a, off, lv[i]);
     }
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
-      if (u0 + i < hi) {
-        if (bias) {
-          const float* br = bias + (bias_row0 + (u0 + i - seg_lo)) * D + c0;
+      const bool ok = i0 + i < hi;
+      if (a.bias) {
+        const int64_t ci = ok ? i0 + i : hi - 1;
+        const int64_t brow = ci < cd.nb ? ci : cd.a_bias0 + (ci - cd.nb);
+        const float* br = a.bias + brow * a.D + c0;
 #pragma unroll
-          for (int c = 0; c < VEC; ++c) lv[i][c] += br[c];
-        }
+        for (int c = 0; c < VEC; ++c) lv[i][c] += br[c];
+      }
 #pragma unroll
-        for (int c = 0; c < VEC; ++c) lv[i][c] *= kLog2e;
-      } else {
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) { lv[i][c] = -INFINITY; xv[i][c] = 0.f; }
+      for (int c = 0; c < VEC; ++c) {
+        lv[i][c] = ok ? lv[i][c] * kLog2e : -INFINITY;
+        xv[i][c] = ok ? xv[i][c] : 0.f;
       }
     }
 #pragma unroll
@@ -98,16 +108,16 @@ __device__ __forceinline__ void fold_segment(const void* x, const void* z, const
       for (int i = 1; i < kChunk; ++i) cm = fmaxf(cm, lv[i][c]);
       const float nm = fmaxf(mx[c], cm);
       if (nm == -INFINITY) continue;  // nothing finite yet in this channel
-      const float a = fast_exp2(mx[c] - nm);
-      float s = 0.f, t = 0.f;
+      const float f = fast_exp2(mx[c] - nm);
+      float sd = 0.f, sa = 0.f;
 #pragma unroll
       for (int i = 0; i < kChunk; ++i) {
         const float e = fast_exp2(lv[i][c] - nm);
-        s += e;
-        t = fmaf(e, xv[i][c], t);
+        sd += e;
+        sa = fmaf(e, xv[i][c], sa);
       }
-      den[c] = fmaf(den[c], a, s);
-      acc[c] = fmaf(acc[c], a, t);
+      den[c] = fmaf(den[c], f, sd);
+      acc[c] = fmaf(acc[c], f, sa);
       mx[c] = nm;
     }
   }
@@ -140,20 +150,21 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
 #pragma unroll
   for (int c = 0; c < VEC; ++c) { mx[c] = -INFINITY; den[c] = 0.f; acc[c] = 0.f; }
 
-  auto fold = [&](const void* x, const void* z, int64_t bias_row0, int64_t lo, int64_t hi) {
-    int64_t sl = lo, sh = hi;
-    if (S > 1) {
-      const int64_t per = (hi - lo + S - 1) / S;
-      sl = lo + slice * per;
-      sh = sl + per < hi ? sl + per : hi;
-    }
-    if (live && sl < sh)
-      fold_segment<BF16>(x, z, a.bias, bias_row0, lo, sl, sh, row_base, a.p0, a.D, c0, mx, den, acc);
-  };
   const bool two = a.x_b != nullptr;
-  if (two && j >= 1) fold(a.x_b, a.z_b, 0, (j - 1) * a.m, j * a.m);  // stream B, bias rows 0..m-1
-  const int64_t hi = (j + 1) * a.m < a.n ? (j + 1) * a.m : a.n;
-  fold(a.x_a, a.z_a, two ? a.m : 0, j * a.m, hi);
+  Cands cd;
+  cd.nb = (two && j >= 1) ? a.m : 0;
+  cd.b_lo = (j - 1) * a.m;
+  cd.a_lo = j * a.m;
+  cd.na = ((j + 1) * a.m < a.n ? (j + 1) * a.m : a.n) - cd.a_lo;
+  cd.a_bias0 = two ? a.m : 0;
+  const int64_t total = cd.nb + cd.na;
+  int64_t lo = 0, hi = total;
+  if (S > 1) {
+    const int64_t per = (total + S - 1) / S;
+    lo = slice * per;
+    hi = lo + per < total ? lo + per : total;
+  }
+  if (live && lo < hi) fold_range<BF16>(a, cd, lo, hi, row_base, c0, mx, den, acc);
 
   if (S > 1) {
     __shared__ float part[3][S][LANES][VEC];

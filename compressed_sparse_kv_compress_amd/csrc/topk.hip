@@ -11,9 +11,9 @@
 // of 250K scores is spread over many workgroups:
 //   1. part kernel: the row is cut into parts of 16384 scores; one 1024-thread
 //      workgroup holds a part in registers (16 consecutive scores per thread),
-//      selects the part's own top-min(k, part) with three LDS histogram passes
-//      (11, 11, 10 bits) and writes the kept (score, index) pairs in index
-//      order.  Any entry of the row's top-k is in its part's top-k, ties
+//      selects the part's own top-min(k, part) with LDS histogram passes of up
+//      to 11 bits that start below the common bit prefix of the part's keys,
+//      and writes the kept (score, index) pairs in index order.  Any entry of the row's top-k is in its part's top-k, ties
 //      included, because fewer entries beat it inside the part than in the
 //      whole row.
 //   2. merge kernel: one workgroup per row runs the same selection over the
@@ -36,6 +36,7 @@ constexpr int64_t kPart = static_cast<int64_t>(kThreads) * kItems;  // 16384
 struct Shared {
   uint32_t hist[2048];
   uint64_t scan[2 * kWaves];
+  uint32_t red[kWaves];
   uint32_t sel_bin, sel_above;
 };
 
@@ -66,6 +67,36 @@ __device__ __forceinline__ uint64_t block_scan_incl(uint64_t v, Shared& sh, uint
   return v + before;
 }
 
+__device__ __forceinline__ uint32_t block_min(uint32_t v, Shared& sh) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t y = __shfl_xor(v, o, 64);
+    v = y < v ? y : v;
+  }
+  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t r = sh.red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = sh.red[w] < r ? sh.red[w] : r;
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ uint32_t block_max(uint32_t v, Shared& sh) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t y = __shfl_xor(v, o, 64);
+    v = y > v ? y : v;
+  }
+  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t r = sh.red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = sh.red[w] > r ? sh.red[w] : r;
+  __syncthreads();
+  return r;
+}
+
 // Radix select over the valid keys held in registers by the workgroup
 // (keys[j] valid iff bit j of vmask is set).  Finds the key of the sel-th
 // largest (1-based) and how many keys equal to it are kept (the
@@ -73,13 +104,28 @@ __device__ __forceinline__ uint64_t block_scan_incl(uint64_t v, Shared& sh, uint
 __device__ __forceinline__ void radix_select(const uint32_t* keys, uint32_t vmask, uint32_t sel, Shared& sh,
                                              uint32_t* thr_out, uint32_t* take_eq_out) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0, remaining = sel;
-  const int shifts[3] = {21, 10, 0};
-  const int widths[3] = {11, 11, 10};
+  // The valid keys share every bit above the highest bit where their min and
+  // max differ; histogramming starts just below that common prefix, so the
+  // first pass spreads concentrated scores over all bins instead of piling
+  // them onto a few (LDS atomics to one bin serialise).
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = shifts[pass];
-    const int nb = 1 << widths[pass];
+  for (int j = 0; j < kItems; ++j)
+    if ((vmask >> j) & 1u) {
+      kmin = keys[j] < kmin ? keys[j] : kmin;
+      kmax = keys[j] > kmax ? keys[j] : kmax;
+    }
+  kmin = block_min(kmin, sh);
+  kmax = block_max(kmax, sh);
+  const uint32_t diff = kmin ^ kmax;
+  uint32_t prefix = diff ? (kmax & ~((2u << (31 - __clz(diff))) - 1u)) : kmax;
+  uint32_t mask = diff ? ~((2u << (31 - __clz(diff))) - 1u) : 0xffffffffu;
+  uint32_t remaining = sel;
+  int top = diff ? 31 - __clz(diff) : -1;  // highest undecided bit
+  while (top >= 0) {
+    const int width = top + 1 < 11 ? top + 1 : 11;
+    const int shift = top + 1 - width;
+    const int nb = 1 << width;
     for (int i = tid; i < 2048; i += kThreads) sh.hist[i] = 0;
     __syncthreads();
 #pragma unroll
@@ -105,6 +151,7 @@ __device__ __forceinline__ void radix_select(const uint32_t* keys, uint32_t vmas
     mask |= static_cast<uint32_t>(nb - 1) << shift;
     remaining -= sh.sel_above;
     __syncthreads();
+    top = shift - 1;
   }
   *thr_out = prefix;
   *take_eq_out = remaining;

@@ -98,7 +98,7 @@ csa_status_t hca_compress(const void* x, const void* z, const float* bias, void*
  *   q_idx : [B][T][H_I][d_I] dtype      w_idx : fp32 [B][T][H_I] or NULL (= 1)
  *   k_idx : [B][L][d_I] dtype (one key per compressed entry, shared by heads)
  *   score : fp32 [B][T][L]
- * bf16 needs H_I in {32, 64, 128} with d_I = 128, or H_I in {32, 64} with
+ * bf16 needs H_I in {16, 32, 64, 128} with d_I = 128, or H_I in {32, 64} with
  * d_I = 64; fp32 needs H_I*d_I <= 16384.
  * ------------------------------------------------------------------------- */
 csa_status_t csa_index_score(const void* q_idx, const float* w_idx, const void* k_idx, int64_t B,
