@@ -354,6 +354,8 @@ def main():
     ap.add_argument("--batch", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=12)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="first run a plain device copy of BYTES bytes 3 times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -361,6 +363,14 @@ def main():
         sys.exit(2)
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print("# calibration copy of %d bytes done" % args.copy_calibration, file=sys.stderr, flush=True)
     st = Stack(B=args.batch)
     t_gen = time.perf_counter()
     state = GpuState(st)
