@@ -28,11 +28,17 @@ CFLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wall", "-Wno-unused-function",
 ]
+# Per-source flags.  attn.hip: MFMA accumulators in ordinary VGPRs, so the
+# (rare) re-scaling of the output accumulators does not make the compiler copy
+# all of them between AGPRs and VGPRs on every loop iteration.
+FILE_FLAGS = {
+    "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _compile(src: str, obj_dir: str = OBJ, extra=()) -> str:
     obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -17,24 +17,25 @@
 // and 4.3 (compressed rows concatenated with the uncompressed window).
 //
 // Design (gfx950, bf16): 64 query heads share every K/V row, so QK^T and PV
-// are dense contractions with the heads as the M dimension: MFMA
-// v_mfma_f32_16x16x32_bf16, one wavefront per 16 heads, four wavefronts
-// (64 heads) per workgroup.  Rows are staged 32 at a time into LDS (K and V
-// row-major, padded pitches so the MFMA operand reads are bank-conflict
-// free), gathered through the index list for CSA or streamed contiguously for
-// HCA; one staged row serves all 64 heads.  The softmax is online in log2
-// units, P goes back through a small per-wave LDS tile to MFMA A layout, and
-// the 16 heads x d output accumulators live in VGPRs (d = 512: 128 per lane).
-// Decode queries are split over the row list (flash-decoding) and merged by a
-// log-sum-exp combine kernel that also applies the sink; prefill-sized launches
-// use one workgroup per (query, 64 heads) and finish in place.
+// are dense contractions: MFMA v_mfma_f32_16x16x32_bf16, one wavefront per 16
+// heads, four wavefronts (64 heads) per workgroup.  Rows are staged 32 at a
+// time straight into LDS with direct-to-LDS loads (two stages in flight),
+// gathered through the index list for CSA or streamed contiguously for HCA;
+// one staged row serves all 64 heads.  Scores are computed transposed
+// (S^T = K Q^T), which leaves every lane holding exactly the P values that the
+// A operand of O += P V needs, and the V operand comes from the LDS transpose
+// load (ds_read_b64_tr_b16), so neither P nor V is shuffled.  The softmax is
+// online in log2 units with a lazily re-based running max; the 16 heads x d
+// output accumulators live in VGPRs.  Decode queries are split over the row
+// list (flash-decoding) and merged by a log-sum-exp combine kernel that also
+// applies the sink; prefill-sized launches use one workgroup per (query, 64
+// heads) and finish in place.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace csa {
 namespace {
 
-constexpr int kRows = 32;  // rows staged per chunk
 constexpr int kHeadsPerWave = 16;
 constexpr int kWaves = 4;
 constexpr int kHeadsPerWg = kHeadsPerWave * kWaves;
@@ -85,39 +86,109 @@ __device__ __forceinline__ int64_t row_offset(const AttnArgs& a, bool sparse, co
   return (b * a.R + u) * a.d;
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 hbf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 (low half = a), round to nearest even, on the
+// hardware converter (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), hbf16x2));
+}
+
+// Staging geometry.  Rows move global -> LDS by direct-to-LDS loads
+// (global_load_lds: one wave instruction = 64 lanes x ESZ bytes of one row,
+// landing contiguously), 32 rows of K and 32 of V per stage, two stages.
+// K rows are read as MFMA A operands (16 rows x 16 bytes per 16-lane group):
+// a pitch of 4 banks past a multiple of the bank count keeps them apart.  V
+// rows are read by the LDS transpose load (4 rows x 32 bytes per 16-lane
+// group): a pitch of 8 banks past a multiple does the same for them.
 template <int D>
-struct __attribute__((aligned(16))) Lds {
-  static constexpr int KP = D + 8;  // row pitch (elements) of staged K and V rows
-  static constexpr int PP = kRows + 8;
-  uint16_t k[kRows * KP];
-  uint16_t v[kRows * KP];
-  uint16_t p[kWaves][kHeadsPerWave * PP];
-  int ok[kRows];
+struct Ring {
+  static constexpr int ESZ = D == 512 ? 16 : 4;       // bytes per lane per load
+  static constexpr int IPR = D * 2 / (64 * ESZ);      // loads per row
+  static constexpr int ROWS = 32;                     // rows per stage
+  static constexpr int PK = D * 2 + 16;               // K row pitch (bytes)
+  static constexpr int PV = D * 2 + 32;               // V row pitch (bytes)
+  static constexpr int KBYTES = ROWS * PK;
+  static constexpr int STAGE = ROWS * (PK + PV);
+  static constexpr int NS = 2;
+  static constexpr int NI = 16 * IPR;                 // loads per wave per stage (16 rows)
+  static_assert(2 * ROWS == 16 * kWaves, "each wave stages 16 rows of K or V");
+  static constexpr int OP = D + 4;                    // epilogue LDS row pitch (floats)
+  static_assert(kWaves * kHeadsPerWave * OP * 4 <= NS * STAGE, "epilogue tile fits the ring");
 };
+constexpr int kMaxIdx = 2048;  // cached row indices per split (CSA)
 
-// Output-column layout of PV: dims are taken in slabs of 128; inside a slab,
-// lane column c (0..15) of N-block e (0..7) is dim 8c + e.  A lane then reads
-// 8 consecutive dims of a staged V row with one 16-byte LDS load and
-// transposes 8 such rows in registers into the 8 B operands of the slab.
-__device__ __forceinline__ uint32_t lo_pair(uint32_t x, uint32_t y) {
-  return __builtin_amdgcn_perm(y, x, 0x05040100u);  // (x.lo, y.lo)
-}
-__device__ __forceinline__ uint32_t hi_pair(uint32_t x, uint32_t y) {
-  return __builtin_amdgcn_perm(y, x, 0x07060302u);  // (x.hi, y.hi)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Stage loader for one wave: 16 consecutive virtual rows c0 .. c0+15 of one
+// matrix (K or V) go straight into LDS (global_load_lds), IPR loads per row.
+// All addressing is wave-uniform (scalar) except the lane's byte offset.  CSA
+// row indices come from the split's index cache with one vector LDS read.  An
+// empty row (past the split's end, or a -1 / out-of-range index) is read from
+// the dummy row and flagged in okrow (K waves only), so its logit is masked.
+template <int D, bool SPARSE>
+__device__ __forceinline__ void issue_rows(const char* cbase, const char* rbase, const char* dummy, const int* sidx,
+                                           uint8_t* lds, int pitch, int c0, int n_cmp, int r_begin, int r_end,
+                                           int win0, int L, int lane, int* okrow) {
+  using C = Ring<D>;
+  int sv = 0;
+  if (SPARSE) {
+    const int v = c0 + (lane & 15);
+    sv = (v < n_cmp && v < r_end) ? sidx[v - r_begin] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int v = c0 + j;
+    const bool cmp = v < n_cmp;
+    int s = v;
+    if (SPARSE) s = cmp ? __builtin_amdgcn_readlane(sv, j) : 0;
+    const bool ok = v < r_end && (!SPARSE || !cmp || (s >= 0 && s < L));
+    const char* row = cmp ? cbase + static_cast<int64_t>(s) * (2 * D) : rbase + static_cast<int64_t>(v + win0) * (2 * D);
+    const char* src = ok ? row : dummy;
+#pragma unroll
+    for (int p = 0; p < C::IPR; ++p)
+      __builtin_amdgcn_global_load_lds(src + p * 64 * C::ESZ + lane * C::ESZ, lds + j * pitch + p * 64 * C::ESZ,
+                                       C::ESZ, 0, 0);
+  }
+  if (okrow && lane < 16) {
+    const int v = c0 + lane;
+    const bool cmp = v < n_cmp;
+    okrow[lane] = v < r_end && (!SPARSE || !cmp || (sv >= 0 && sv < L));
+  }
+}
+
+__device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
+  typedef s16x4 __attribute__((address_space(3))) lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+// One workgroup = 64 heads of one query over one split of its row list.
+// Per 32-row stage a wave computes S^T = K Q^T (rows x its 16 heads, two
+// 16x16x32 tiles), so lane (g, c) holds head c at rows 4g..4g+3 and
+// 16+4g..16+4g+3: exactly the A operand of O += P V with k = 32 rows, no
+// data movement.  V's B operand comes from the LDS transpose load: for
+// 16-lane group g, lanes 4j..4j+3 address row r0+j, 16 dims, and lane c
+// receives dim c of those four rows.
 template <int D, bool SPARSE>
 __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a, int nsplit) {
-  constexpr int KSQ = D / 32;    // k-steps of QK^T
-  constexpr int NB = D / 16;     // 16-column output blocks
-  constexpr int SLABS = D / 128;
-  constexpr int PIECES = D / 8;  // 16-byte pieces per row
-  constexpr int PER = kRows * PIECES / 256;  // pieces per thread per chunk
+  using C = Ring<D>;
+  constexpr int KSQ = D / 32;  // k-steps of Q K^T
+  constexpr int NB = D / 16;   // 16-dim output blocks
   constexpr float kRebase = 8.f;  // re-base the running max only when it grows by > 2^8
-  __shared__ Lds<D> sm;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[C::NS * C::STAGE];
+  __shared__ int sidx[SPARSE ? kMaxIdx : 1];
+  __shared__ __attribute__((aligned(16))) int okf[C::NS][C::ROWS];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int g = lane >> 4;     // 16-lane group
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;  // 16-lane group
   const int c16 = lane & 15;
 
   const int64_t hgroups = a.H / kHeadsPerWg;
@@ -131,214 +202,192 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a, int nsplit) {
   const RowMap rm = row_map(a, SPARSE, t);
   const int64_t n_rows = rm.n_cmp + rm.n_win;
   int64_t per = (n_rows + nsplit - 1) / nsplit;
-  per = (per + kRows - 1) / kRows * kRows;
+  per = (per + C::ROWS - 1) / C::ROWS * C::ROWS;
   const int64_t r_begin = split * per;
   const int64_t r_end = r_begin + per < n_rows ? r_begin + per : n_rows;
 
-  // Register staging of one 32-row chunk: every global load of the chunk is
-  // issued back to back with no control flow around it (an empty row loads
-  // from a valid dummy address and is zeroed afterwards); the chunk after the
-  // current one is in flight while the current one is being computed.
-  const uint16_t* dummy = static_cast<const uint16_t*>(a.q) + bt * a.H * D;
-  const uint16_t* kcb = static_cast<const uint16_t*>(a.kc) + b * a.L * D;
-  const uint16_t* vcb = static_cast<const uint16_t*>(a.vc) + b * a.L * D;
-  const uint16_t* krb = static_cast<const uint16_t*>(a.kr) + b * a.R * D;
-  const uint16_t* vrb = static_cast<const uint16_t*>(a.vr) + b * a.R * D;
-  const int64_t win0 = rm.win_lo - (a.n_ctx - a.R) - rm.n_cmp;  // raw row of virtual row v is v + win0
-  const int pc = threadIdx.x % PIECES;
-  const int r0 = threadIdx.x / PIECES;
-  u32x4 kp[PER], vp[PER];
-  uint32_t okmask = 0;
-  auto issue = [&](int64_t c0) {
-    int32_t sid[PER];
-    if (SPARSE && a.k > 0) {
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        int64_t v = c0 + r0 + (256 / PIECES) * i;
-        v = v < a.k - 1 ? v : a.k - 1;
-        sid[i] = a.idx[bt * a.k + v];
-      }
-    }
-    okmask = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int64_t v = c0 + r0 + (256 / PIECES) * i;
-      const bool cmp = v < rm.n_cmp;
-      const int64_t s = SPARSE ? (a.k > 0 ? static_cast<int64_t>(sid[i]) : -1) : v;
-      const bool ok = v < r_end && (cmp ? (!SPARSE || (s >= 0 && s < a.L)) : true);
-      const int64_t off = (cmp ? s : v + win0) * D + pc * 8;
-      const uint16_t* kb = ok ? (cmp ? kcb : krb) + off : dummy + pc * 8;
-      const uint16_t* vb = ok ? (cmp ? vcb : vrb) + off : dummy + pc * 8;
-      kp[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb));
-      vp[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb));
-      okmask |= static_cast<uint32_t>(ok) << i;
-    }
-  };
-  auto stash = [&]() {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int r = r0 + (256 / PIECES) * i;
-      const bool ok = (okmask >> i) & 1u;
-      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&sm.k[r * Lds<D>::KP + pc * 8]) = ok ? kp[i] : z;
-      *reinterpret_cast<u32x4*>(&sm.v[r * Lds<D>::KP + pc * 8]) = ok ? vp[i] : z;
-      if (pc == 0) sm.ok[r] = ok;
-    }
-  };
-  // Q is loaded before the first chunk so that the chunk's wait also covers it
-  // (otherwise the wait counter can not prove Q complete inside the loop and
-  // every chunk would wait for its own prefetch).
+  // Row indices of this split (CSA) go to LDS once, so that the staging loop
+  // issues no loads into registers (their waits would also drain the ring).
+  if (SPARSE) {
+    const int64_t ce = r_end < rm.n_cmp ? r_end : rm.n_cmp;
+    for (int64_t v = r_begin + threadIdx.x; v < ce; v += 256) sidx[v - r_begin] = a.idx[bt * a.k + v];
+  }
   const int h0 = static_cast<int>(hg * kHeadsPerWg + wave * kHeadsPerWave);
-  // Q fragments (A operand): head h0 + c16, dims ks*32 + 8g .. +8.
+  // Q fragments (B operand of K Q^T): head h0 + c16, dims ks*32 + 8g .. +8.
   bf16x8 qf[KSQ];
   {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (bt * a.H + h0 + c16) * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KSQ; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
   }
-  if (r_begin < r_end) issue(r_begin);
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // Waves 0, 1 stage K rows 0-15 / 16-31 of each stage; waves 2, 3 the V rows.
+  const int mat = wave >> 1;
+  const int row0 = (wave & 1) * 16;
+  const uint16_t* cb = static_cast<const uint16_t*>(mat ? a.vc : a.kc) + b * a.L * D;
+  const uint16_t* rb = static_cast<const uint16_t*>(mat ? a.vr : a.kr) + b * a.R * D;
+  const char* cbase = reinterpret_cast<const char*>(cb);
+  const char* rbase = reinterpret_cast<const char*>(rb);
+  const char* dummy = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.q) + bt * a.H * D);
+  const int pitch = mat ? C::PV : C::PK;
+  const int moff = (mat ? C::KBYTES : 0) + row0 * pitch;
+  const int n_cmp = static_cast<int>(rm.n_cmp);
+  const int rb0 = static_cast<int>(r_begin), re0 = static_cast<int>(r_end);
+  const int win0 = static_cast<int>(rm.win_lo - (a.n_ctx - a.R) - rm.n_cmp);  // raw row of virtual row v is v + win0
+  const int Lc = static_cast<int>(a.L);
 
   f32x4 oacc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[4], l_run[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.f; }
+  float m_run = -INFINITY, l_run = 0.f;  // head c16; m_run is the same in all four groups
   const float sl2 = a.scale * kLog2e;
 
-  for (int64_t c0 = r_begin; c0 < r_end; c0 += kRows) {
-    stash();
-    __syncthreads();
-    if (c0 + kRows < r_end) issue(c0 + kRows);
+  const int nst = static_cast<int>((r_end - r_begin + C::ROWS - 1) / C::ROWS);
+  if (nst > 0)
+    issue_rows<D, SPARSE>(cbase, rbase, dummy, sidx, ring + moff, pitch, rb0 + row0, n_cmp, rb0, re0, win0, Lc, lane,
+                          mat ? nullptr : okf[0] + row0);
 
-    // ---- S = Q K^T for 16 heads x 32 rows ---------------------------------
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  for (int c = 0; c < nst; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nst) {
+      issue_rows<D, SPARSE>(cbase, rbase, dummy, sidx, ring + (buf ^ 1) * C::STAGE + moff, pitch,
+                            rb0 + (c + 1) * C::ROWS + row0, n_cmp, rb0, re0, win0, Lc, lane,
+                            mat ? nullptr : okf[buf ^ 1] + row0);
+      wait_vmcnt<C::NI>();  // this stage's loads are done (each wave its own)
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    const uint8_t* Ks = ring + buf * C::STAGE;
+    const uint8_t* Vs = Ks + C::KBYTES;
+
+    // ---- S^T = K Q^T: two 16-row tiles x 16 heads -------------------------
+    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const bf16x8 kb =
-            *reinterpret_cast<const bf16x8*>(&sm.k[(rb * 16 + c16) * Lds<D>::KP + ks * 32 + 8 * g]);
-        sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], kb, sacc[rb], 0, 0, 0);
-      }
-    // lane holds S[head 4g + r][row rb*16 + c16]; online softmax in log2
-    // units against a lazily re-based running max.
-    const bool ok0 = sm.ok[c16] != 0, ok1 = sm.ok[16 + c16] != 0;
-    float s0[4], s1[4], mnew[4];
-    bool grow = false;
+    for (int ks = 0; ks < KSQ; ++ks) {
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Ks + c16 * C::PK + ks * 64 + g * 16);
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Ks + (16 + c16) * C::PK + ks * 64 + g * 16);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks], s1, 0, 0, 0);
+    }
+    // Online softmax (log2 units) for head c16 over its 8 rows here and the
+    // other groups' 24, against a lazily re-based running max.
+    const i32x4 ok0 = *reinterpret_cast<const i32x4*>(&okf[buf][4 * g]);
+    const i32x4 ok1 = *reinterpret_cast<const i32x4*>(&okf[buf][16 + 4 * g]);
+    float sv[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      s0[r] = ok0 ? sacc[0][r] * sl2 : -INFINITY;
-      s1[r] = ok1 ? sacc[1][r] * sl2 : -INFINITY;
-      float cm = fmaxf(s0[r], s1[r]);
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) cm = fmaxf(cm, __shfl_xor(cm, o, 64));
-      mnew[r] = fmaxf(m_run[r], cm);
-      grow |= m_run[r] != -INFINITY && mnew[r] > m_run[r] + kRebase;
+      sv[r] = ok0[r] ? s0[r] * sl2 : -INFINITY;
+      sv[4 + r] = ok1[r] ? s1[r] * sl2 : -INFINITY;
     }
-    if (__any(grow)) {  // rare: re-base output and sums to the new max
+    float cm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    const float mnew = fmaxf(m_run, cm);
+    if (__any(m_run != -INFINITY && mnew > m_run + kRebase)) {
+      // rare: re-base this head's sum and the output rows (heads 4g+r) to the new max
+      const float alpha = m_run == -INFINITY ? 1.f : fast_exp2(m_run - mnew);
+      l_run *= alpha;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float alpha = m_run[r] == -INFINITY ? 1.f : fast_exp2(m_run[r] - mnew[r]);
-        l_run[r] *= alpha;
+        const float ar = __shfl(alpha, 4 * g + r, 64);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) oacc[nb][r] *= alpha;
-        m_run[r] = mnew[r];
+        for (int nb = 0; nb < NB; ++nb) oacc[nb][r] *= ar;
       }
+      m_run = mnew;
     }
-    float pv[2][4];
+    if (m_run == -INFINITY) m_run = mnew;  // first rows of this head: nothing to re-base
+    const float mu = m_run == -INFINITY ? 0.f : m_run;
+    float pr[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (m_run[r] == -INFINITY) m_run[r] = mnew[r];  // first rows of this head: nothing to re-base
-      const float mu = m_run[r] == -INFINITY ? 0.f : m_run[r];
-      pv[0][r] = fast_exp2(s0[r] - mu);
-      pv[1][r] = fast_exp2(s1[r] - mu);
-      l_run[r] += pv[0][r] + pv[1][r];
+    for (int j = 0; j < 8; ++j) {
+      pr[j] = fast_exp2(sv[j] - mu);
+      l_run += pr[j];
     }
-    // P (bf16) to LDS as [head][row] for the A operand of PV.
-    uint16_t* pw = sm.p[wave];
+    bf16x8 pa;
+    {
+      u32x4 w;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pw[(4 * g + r) * Lds<D>::PP + rb * 16 + c16] = f32_to_bf16(pv[rb][r]);
-    __syncthreads();
+      for (int u = 0; u < 4; ++u) w[u] = cvt_bf16x2(pr[2 * u], pr[2 * u + 1]);
+      pa = __builtin_bit_cast(bf16x8, w);
+    }
 
-    // ---- O += P V -----------------------------------------------------------
-    const bf16x8 pf = *reinterpret_cast<const bf16x8*>(&pw[c16 * Lds<D>::PP + 8 * g]);
+    // ---- O += P V over the 32 rows: k slot 8g+j <-> row 4g+j (j < 4) or
+    // row 16+4g+(j-4) -------------------------------------------------------
+    const uint8_t* v0 = Vs + (4 * g + (c16 >> 2)) * C::PV + (c16 & 3) * 8;
+    const uint8_t* v1 = v0 + 16 * C::PV;
 #pragma unroll
-    for (int sb = 0; sb < SLABS; ++sb) {
-      u32x4 rowv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        rowv[j] = *reinterpret_cast<const u32x4*>(&sm.v[(8 * g + j) * Lds<D>::KP + sb * 128 + 8 * c16]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        u32x4 ev, od;  // dims 8c16 + 2w (even) and + 2w+1 (odd), rows 8g .. 8g+7
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          ev[u] = lo_pair(rowv[2 * u][w], rowv[2 * u + 1][w]);
-          od[u] = hi_pair(rowv[2 * u][w], rowv[2 * u + 1][w]);
-        }
-        oacc[sb * 8 + 2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            pf, __builtin_bit_cast(bf16x8, ev), oacc[sb * 8 + 2 * w], 0, 0, 0);
-        oacc[sb * 8 + 2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            pf, __builtin_bit_cast(bf16x8, od), oacc[sb * 8 + 2 * w + 1], 0, 0, 0);
-      }
+    for (int nb = 0; nb < NB; ++nb) {
+      const s16x4 lo = lds_tr16(v0 + nb * 32);
+      const s16x4 hi = lds_tr16(v1 + nb * 32);
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bv, oacc[nb], 0, 0, 0);
     }
-    __syncthreads();
+    __syncthreads();  // every wave is done with this stage before it is refilled
   }
 
-  // ---- epilogue: oacc[sb*8 + e][r] = O[head 4g+r][dim sb*128 + 8*c16 + e] ----
-  float l_tot[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float sum = l_run[r];
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
-    l_tot[r] = sum;
-  }
+  // ---- epilogue: oacc[nb][r] = O[head 4g+r][dim 16nb + c16] -----------------
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  float* ot = reinterpret_cast<float*>(ring) + wave * kHeadsPerWave * C::OP;  // this wave's 16 x D tile
   if (nsplit == 1) {
+    const float sig = a.sink ? a.sink[h0 + c16] * kLog2e : -INFINITY;
+    const float M = fmaxf(m_run, sig);
+    float den = 0.f, f = 0.f;
+    if (M != -INFINITY) {
+      f = m_run == -INFINITY ? 0.f : fast_exp2(m_run - M);
+      den = l_tot * f + (sig == -INFINITY ? 0.f : fast_exp2(sig - M));
+    }
+    const float inv = den > 0.f ? f / den : 0.f;
+    if (a.lse && g == 0) a.lse[bt * a.H + h0 + c16] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int h = h0 + 4 * g + r;
-      const float sig = a.sink ? a.sink[h] * kLog2e : -INFINITY;
-      const float M = fmaxf(m_run[r], sig);
-      float den = 0.f, f = 0.f;
-      if (M != -INFINITY) {
-        f = m_run[r] == -INFINITY ? 0.f : fast_exp2(m_run[r] - M);
-        den = l_tot[r] * f + (sig == -INFINITY ? 0.f : fast_exp2(sig - M));
-      }
-      const float inv = den > 0.f ? f / den : 0.f;
-      uint16_t* op = static_cast<uint16_t*>(a.out) + (bt * a.H + h) * D + 8 * c16;
+      const float ir = __shfl(inv, 4 * g + r, 64);
 #pragma unroll
-      for (int sb = 0; sb < SLABS; ++sb) {
-        u32x4 w;
+      for (int nb = 0; nb < NB; ++nb) ot[(4 * g + r) * C::OP + nb * 16 + c16] = oacc[nb][r] * ir;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // 16 rows x D bf16, 8 dims (16 bytes) per lane and step
+    uint16_t* ob = static_cast<uint16_t*>(a.out) + (bt * a.H + h0) * D;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          w[u] = pack_bf16x2(oacc[sb * 8 + 2 * u][r] * inv, oacc[sb * 8 + 2 * u + 1][r] * inv);
-        *reinterpret_cast<u32x4*>(op + sb * 128) = w;
-      }
-      if (a.lse && c16 == 0) a.lse[bt * a.H + h] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
+    for (int it = 0; it < kHeadsPerWave * D / (64 * 8); ++it) {
+      const int e = it * 64 * 8 + lane * 8;
+      const int hl = e / D, dd = e % D;
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(ot + hl * C::OP + dd);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(ot + hl * C::OP + dd + 4);
+      u32x4 w;
+      w[0] = cvt_bf16x2(x0[0], x0[1]);
+      w[1] = cvt_bf16x2(x0[2], x0[3]);
+      w[2] = cvt_bf16x2(x1[0], x1[1]);
+      w[3] = cvt_bf16x2(x1[2], x1[3]);
+      *reinterpret_cast<u32x4*>(ob + e) = w;
     }
   } else {
-    float* wo = a.ws + ((bt * nsplit + split) * a.H + h0) * D;
-    float* wml = a.ws + static_cast<int64_t>(a.B * a.T) * nsplit * a.H * D +
-                 ((bt * nsplit + split) * a.H + h0) * 2;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int hl = 4 * g + r;
 #pragma unroll
-      for (int sb = 0; sb < SLABS; ++sb) {
-        f32x4 lo = f32x4{oacc[sb * 8 + 0][r], oacc[sb * 8 + 1][r], oacc[sb * 8 + 2][r], oacc[sb * 8 + 3][r]};
-        f32x4 hi = f32x4{oacc[sb * 8 + 4][r], oacc[sb * 8 + 5][r], oacc[sb * 8 + 6][r], oacc[sb * 8 + 7][r]};
-        float* dst = wo + hl * D + sb * 128 + 8 * c16;
-        *reinterpret_cast<f32x4*>(dst) = lo;
-        *reinterpret_cast<f32x4*>(dst + 4) = hi;
-      }
-      if (c16 == 0) {
-        wml[hl * 2 + 0] = m_run[r];
-        wml[hl * 2 + 1] = l_tot[r];
-      }
+      for (int nb = 0; nb < NB; ++nb) ot[(4 * g + r) * C::OP + nb * 16 + c16] = oacc[nb][r];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float* wo = a.ws + ((bt * nsplit + split) * a.H + h0) * D;
+#pragma unroll
+    for (int it = 0; it < kHeadsPerWave * D / (64 * 4); ++it) {
+      const int e = it * 64 * 4 + lane * 4;
+      const int hl = e / D, dd = e % D;
+      *reinterpret_cast<f32x4*>(wo + e) = *reinterpret_cast<const f32x4*>(ot + hl * C::OP + dd);
+    }
+    if (g == 0) {
+      float* wml = a.ws + static_cast<int64_t>(a.B * a.T) * nsplit * a.H * D +
+                   ((bt * nsplit + split) * a.H + h0 + c16) * 2;
+      wml[0] = m_run;
+      wml[1] = l_tot;
     }
   }
 }
@@ -468,7 +517,7 @@ __global__ __launch_bounds__(64) void attn_f32(AttnArgs a, int sparse_i) {
 
 }  // namespace
 
-int attn_splits(int64_t B, int64_t T, int64_t H, int64_t d, int64_t max_rows, bool bf16) {
+int attn_splits(int64_t B, int64_t T, int64_t H, int64_t d, int64_t max_rows, bool bf16, bool sparse) {
   (void)d;
   if (!bf16) return 1;
   const int64_t base = B * T * (H / kHeadsPerWg);
@@ -480,6 +529,10 @@ int attn_splits(int64_t B, int64_t T, int64_t H, int64_t d, int64_t max_rows, bo
   const int64_t cap = (max_rows + 63) / 64;  // keep >= 64 rows per split
   if (ns > cap) ns = cap;
   if (ns > 64) ns = 64;
+  if (sparse) {  // a split caches at most kMaxIdx row indices
+    const int64_t need = (max_rows + kMaxIdx - 1) / kMaxIdx;
+    if (ns < need) ns = need;
+  }
   if (ns < 1) ns = 1;
   return static_cast<int>(ns);
 }

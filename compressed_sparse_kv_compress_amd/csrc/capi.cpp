@@ -242,21 +242,21 @@ csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k
 size_t csa_sparse_attn_workspace(int64_t B, int64_t T, int64_t H, int64_t d, int64_t k, int64_t W,
                                  csa_dtype_t dtype) {
   if (B <= 0 || T <= 0) return 0;
-  const int ns = csa::attn_splits(B, T, H, d, k + W, dtype == CSA_BF16);
+  const int ns = csa::attn_splits(B, T, H, d, k + W, dtype == CSA_BF16, true);
   return csa::attn_ws_bytes(B, T, H, d, ns);
 }
 
 size_t hca_dense_attn_workspace(int64_t B, int64_t T, int64_t H, int64_t d, int64_t L, int64_t m,
                                 int64_t n_ctx, int64_t W, csa_dtype_t dtype) {
   if (B <= 0 || T <= 0 || m <= 0) return 0;
-  const int ns = csa::attn_splits(B, T, H, d, dense_max_rows(L, m, n_ctx, W), dtype == CSA_BF16);
+  const int ns = csa::attn_splits(B, T, H, d, dense_max_rows(L, m, n_ctx, W), dtype == CSA_BF16, false);
   return csa::attn_ws_bytes(B, T, H, d, ns);
 }
 
 static csa_status_t attn_launch(const csa::AttnArgs& a, bool sparse, int64_t max_rows, csa_dtype_t dt,
                                 void* ws, size_t ws_bytes, void* stream) {
   const bool bf16 = dt == CSA_BF16;
-  const int ns = csa::attn_splits(a.B, a.T, a.H, a.d, max_rows, bf16);
+  const int ns = csa::attn_splits(a.B, a.T, a.H, a.d, max_rows, bf16, sparse);
   const size_t need = csa::attn_ws_bytes(a.B, a.T, a.H, a.d, ns);
   if (need > 0) {
     if (ws == nullptr || ws_bytes < need)

@@ -61,7 +61,7 @@ struct AttnArgs {
   size_t ws_bytes;
 };
 // Number of row splits the attention launch uses, and its workspace bytes.
-int attn_splits(int64_t B, int64_t T, int64_t H, int64_t d, int64_t max_rows, bool bf16);
+int attn_splits(int64_t B, int64_t T, int64_t H, int64_t d, int64_t max_rows, bool bf16, bool sparse);
 size_t attn_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t d, int nsplit);
 hipError_t launch_attn(const AttnArgs& a, bool sparse, bool bf16, int nsplit, hipStream_t s);
 bool attn_shape_supported(int64_t H, int64_t d, bool bf16);
