@@ -37,8 +37,9 @@ namespace csa {
 namespace {
 
 constexpr int kHeadsPerWave = 16;
-constexpr int kWaves = 4;
-constexpr int kHeadsPerWg = kHeadsPerWave * kWaves;
+constexpr int kHeadGroups = 4;                            // 16-head groups per workgroup
+constexpr int kWaves = 2 * kHeadGroups;                   // each group split over two halves of d
+constexpr int kHeadsPerWg = kHeadsPerWave * kHeadGroups;  // 64
 
 struct RowMap {
   int64_t n_cmp;   // compressed slots (sparse: k, dense: visible count)
@@ -97,29 +98,39 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), hbf16x2));
 }
 
+// Split workspace: bf16 partial rows [B*T][nsplit][H][d], then fp32 (m, l)
+// pairs [B*T][nsplit][H][2].
+__device__ __forceinline__ uint16_t* attn_ws_o(const AttnArgs& a) { return reinterpret_cast<uint16_t*>(a.ws); }
+__device__ __forceinline__ float* attn_ws_ml(const AttnArgs& a, int nsplit) {
+  return reinterpret_cast<float*>(attn_ws_o(a) + static_cast<int64_t>(a.B * a.T) * nsplit * a.H * a.d);
+}
+
 // Staging geometry.  Rows move global -> LDS by direct-to-LDS loads
 // (global_load_lds: one wave instruction = 64 lanes x ESZ bytes of one row,
-// landing contiguously), 32 rows of K and 32 of V per stage, two stages.
-// K rows are read as MFMA A operands (16 rows x 16 bytes per 16-lane group):
-// a pitch of 4 banks past a multiple of the bank count keeps them apart.  V
-// rows are read by the LDS transpose load (4 rows x 32 bytes per 16-lane
-// group): a pitch of 8 banks past a multiple does the same for them.
+// landing contiguously), 32 rows of K and 32 of V per stage, two stages; each
+// of the 8 waves stages 8 rows.  K rows are read as MFMA A operands (16 rows x
+// 16 bytes per 16-lane group): a pitch of 4 banks past a multiple of the bank
+// count keeps them apart.  V rows are read by the LDS transpose load (4 rows x
+// 32 bytes per 16-lane group): a pitch of 8 banks past a multiple does the
+// same for them.
 template <int D>
 struct Ring {
   static constexpr int ESZ = D == 512 ? 16 : 4;       // bytes per lane per load
   static constexpr int IPR = D * 2 / (64 * ESZ);      // loads per row
   static constexpr int ROWS = 32;                     // rows per stage
+  static constexpr int RPW = 2 * ROWS / kWaves;       // rows staged per wave
   static constexpr int PK = D * 2 + 16;               // K row pitch (bytes)
   static constexpr int PV = D * 2 + 32;               // V row pitch (bytes)
   static constexpr int KBYTES = ROWS * PK;
   static constexpr int STAGE = ROWS * (PK + PV);
   static constexpr int NS = 2;
-  static constexpr int NI = 16 * IPR;                 // loads per wave per stage (16 rows)
-  static_assert(2 * ROWS == 16 * kWaves, "each wave stages 16 rows of K or V");
-  static constexpr int OP = D + 4;                    // epilogue LDS row pitch (floats)
+  static constexpr int NI = RPW * IPR;                // loads per wave per stage
+  static constexpr int DH = D / 2;                    // dims per wave
+  static constexpr int OP = DH + 4;                   // epilogue LDS row pitch (floats)
   static_assert(kWaves * kHeadsPerWave * OP * 4 <= NS * STAGE, "epilogue tile fits the ring");
+  static_assert(NI < 64, "vmcnt range");
 };
-constexpr int kMaxIdx = 2048;  // cached row indices per split (CSA)
+constexpr int kMaxIdx = kAttnMaxIdx;  // cached row indices per split (CSA)
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -128,10 +139,34 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Stage loader for one wave: 16 consecutive virtual rows c0 .. c0+15 of one
-// matrix (K or V) go straight into LDS (global_load_lds), IPR loads per row.
-// All addressing is wave-uniform (scalar) except the lane's byte offset.  CSA
-// row indices come from the split's index cache with one vector LDS read.  An
+// Direct global -> LDS load of one row piece: lane i's ESZ bytes at g land at
+// LDS byte address lds + ESZ * i (lds wave-uniform, through M0).  Issued as
+// inline asm on purpose: the compiler does not then see an asynchronous LDS
+// write, so it adds no "wait for every outstanding load" before each later LDS
+// read (which would drain the prefetch ring); completion is instead awaited
+// explicitly (vmcnt) and published with a barrier.  The instruction writes no
+// registers, and its address registers are read when it issues.
+template <int ESZ>
+__device__ __forceinline__ void dma_row(const char* g, const uint8_t* lds) {
+  typedef const uint8_t __attribute__((address_space(3))) * lds_ptr;
+  const uint32_t la = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(lds)));
+  uint32_t saved;  // M0 is restored, so the compiler's own uses of it are unaffected
+  if constexpr (ESZ == 16)
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(g), "s"(la)
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(g), "s"(la)
+                 : "memory");
+}
+
+// Stage loader for one wave: RPW consecutive virtual rows c0 .. of one matrix
+// (K or V) go straight into LDS (global_load_lds), IPR loads per row.  All
+// addressing is wave-uniform (scalar) except the lane's byte offset.  CSA row
+// indices come from the split's index cache with one vector LDS read.  An
 // empty row (past the split's end, or a -1 / out-of-range index) is read from
 // the dummy row and flagged in okrow (K waves only), so its logit is masked.
 template <int D, bool SPARSE>
@@ -141,11 +176,11 @@ __device__ __forceinline__ void issue_rows(const char* cbase, const char* rbase,
   using C = Ring<D>;
   int sv = 0;
   if (SPARSE) {
-    const int v = c0 + (lane & 15);
-    sv = (v < n_cmp && v < r_end) ? sidx[v - r_begin] : 0;
+    const int v = c0 + lane;
+    sv = (lane < C::RPW && v < n_cmp && v < r_end) ? sidx[v - r_begin] : 0;
   }
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < C::RPW; ++j) {
     const int v = c0 + j;
     const bool cmp = v < n_cmp;
     int s = v;
@@ -155,10 +190,9 @@ __device__ __forceinline__ void issue_rows(const char* cbase, const char* rbase,
     const char* src = ok ? row : dummy;
 #pragma unroll
     for (int p = 0; p < C::IPR; ++p)
-      __builtin_amdgcn_global_load_lds(src + p * 64 * C::ESZ + lane * C::ESZ, lds + j * pitch + p * 64 * C::ESZ,
-                                       C::ESZ, 0, 0);
+      dma_row<C::ESZ>(src + p * 64 * C::ESZ + lane * C::ESZ, lds + j * pitch + p * 64 * C::ESZ);
   }
-  if (okrow && lane < 16) {
+  if (okrow && lane < C::RPW) {
     const int v = c0 + lane;
     const bool cmp = v < n_cmp;
     okrow[lane] = v < r_end && (!SPARSE || !cmp || (sv >= 0 && sv < L));
@@ -170,25 +204,31 @@ __device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
-// One workgroup = 64 heads of one query over one split of its row list.
-// Per 32-row stage a wave computes S^T = K Q^T (rows x its 16 heads, two
-// 16x16x32 tiles), so lane (g, c) holds head c at rows 4g..4g+3 and
-// 16+4g..16+4g+3: exactly the A operand of O += P V with k = 32 rows, no
-// data movement.  V's B operand comes from the LDS transpose load: for
-// 16-lane group g, lanes 4j..4j+3 address row r0+j, 16 dims, and lane c
-// receives dim c of those four rows.
+// One workgroup = 64 heads of one query over one split of its row list;
+// wave w takes heads 16(w%4) .. +16 and half w/4 of d.  Per 32-row stage a
+// wave computes its half of S^T = K Q^T (rows x 16 heads, two 16x16x32 tiles)
+// and adds the other half's partial sums from LDS; both halves then hold the
+// same scores bit for bit (one addition, commutative) and run the same
+// softmax.  Lane (g, c) holds head c at rows 4g..4g+3 and 16+4g..16+4g+3:
+// exactly the A operand of O += P V with k = 32 rows, no data movement.  V's B
+// operand comes from the LDS transpose load: for 16-lane group g, lanes
+// 4j..4j+3 address row r0+j, 16 dims, and lane c receives dim c of those four
+// rows.  Two waves per SIMD hide each other's LDS and MFMA latency.
 template <int D, bool SPARSE>
-__global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a, int nsplit) {
+__global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
   using C = Ring<D>;
-  constexpr int KSQ = D / 32;  // k-steps of Q K^T
-  constexpr int NB = D / 16;   // 16-dim output blocks
-  constexpr float kRebase = 8.f;  // re-base the running max only when it grows by > 2^8
+  constexpr int KSQ = C::DH / 32;  // k-steps of the wave's half of Q K^T
+  constexpr int NB = C::DH / 16;   // 16-dim output blocks of the wave
+  constexpr float kRebase = 8.f;   // re-base the running max only when it grows by > 2^8
   __shared__ __attribute__((aligned(16))) uint8_t ring[C::NS * C::STAGE];
+  __shared__ __attribute__((aligned(16))) f32x4 xs[kWaves][2][64];  // partial scores
   __shared__ int sidx[SPARSE ? kMaxIdx : 1];
-  __shared__ __attribute__((aligned(16))) int okf[C::NS][C::ROWS];
+  __shared__ __attribute__((aligned(16))) int okf[3][C::ROWS];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4;  // 16-lane group
+  const int hq = wave % kHeadGroups;  // head group
+  const int dh = wave / kHeadGroups;  // half of d
+  const int g = lane >> 4;            // 16-lane group
   const int c16 = lane & 15;
 
   const int64_t hgroups = a.H / kHeadsPerWg;
@@ -206,26 +246,9 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a, int nsplit) {
   const int64_t r_begin = split * per;
   const int64_t r_end = r_begin + per < n_rows ? r_begin + per : n_rows;
 
-  // Row indices of this split (CSA) go to LDS once, so that the staging loop
-  // issues no loads into registers (their waits would also drain the ring).
-  if (SPARSE) {
-    const int64_t ce = r_end < rm.n_cmp ? r_end : rm.n_cmp;
-    for (int64_t v = r_begin + threadIdx.x; v < ce; v += 256) sidx[v - r_begin] = a.idx[bt * a.k + v];
-  }
-  const int h0 = static_cast<int>(hg * kHeadsPerWg + wave * kHeadsPerWave);
-  // Q fragments (B operand of K Q^T): head h0 + c16, dims ks*32 + 8g .. +8.
-  bf16x8 qf[KSQ];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (bt * a.H + h0 + c16) * D + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
-  }
-  wait_vmcnt<0>();
-  __syncthreads();
-
-  // Waves 0, 1 stage K rows 0-15 / 16-31 of each stage; waves 2, 3 the V rows.
-  const int mat = wave >> 1;
-  const int row0 = (wave & 1) * 16;
+  // Waves 0-3 stage K rows 8w .. 8w+7 of each stage; waves 4-7 the V rows.
+  const int mat = wave / (kWaves / 2);
+  const int row0 = (wave % (kWaves / 2)) * C::RPW;
   const uint16_t* cb = static_cast<const uint16_t*>(mat ? a.vc : a.kc) + b * a.L * D;
   const uint16_t* rb = static_cast<const uint16_t*>(mat ? a.vr : a.kr) + b * a.R * D;
   const char* cbase = reinterpret_cast<const char*>(cb);
@@ -237,6 +260,43 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a, int nsplit) {
   const int rb0 = static_cast<int>(r_begin), re0 = static_cast<int>(r_end);
   const int win0 = static_cast<int>(rm.win_lo - (a.n_ctx - a.R) - rm.n_cmp);  // raw row of virtual row v is v + win0
   const int Lc = static_cast<int>(a.L);
+  const int nst = static_cast<int>((r_end - r_begin + C::ROWS - 1) / C::ROWS);
+
+  // Pipeline: K of stage c+2 is issued as soon as every wave is done with
+  // QK of stage c (barrier B), V of stage c+1 once every wave is done with PV
+  // of stage c-1 (barrier A); K therefore keeps two stages in flight.  The
+  // row flags have three buffers because K(c+2) sets them while stage c still
+  // reads its own.
+  auto issue = [&](int st) {
+    issue_rows<D, SPARSE>(cbase, rbase, dummy, sidx, ring + (st & 1) * C::STAGE + moff, pitch,
+                          rb0 + st * C::ROWS + row0, n_cmp, rb0, re0, win0, Lc, lane,
+                          mat ? nullptr : okf[st % 3] + row0);
+  };
+  auto prime = [&]() {
+    if (nst > 0) issue(0);
+    if (mat == 0 && nst > 1) issue(1);
+  };
+
+  // HCA rows need nothing but their position, so the first stages are on
+  // their way before Q is even requested; CSA rows need the split's indices
+  // (cached in LDS once, so that the staging loop issues no loads into
+  // registers, whose waits would also drain the ring).
+  if (!SPARSE) prime();
+  if (SPARSE) {
+    const int64_t ce = r_end < rm.n_cmp ? r_end : rm.n_cmp;
+    for (int64_t v = r_begin + threadIdx.x; v < ce; v += 64 * kWaves) sidx[v - r_begin] = a.idx[bt * a.k + v];
+  }
+  const int h0 = static_cast<int>(hg * kHeadsPerWg + hq * kHeadsPerWave);
+  // Q fragments (B operand of K Q^T): head h0 + c16, dims dh*DH + ks*32 + 8g .. +8.
+  bf16x8 qf[KSQ];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (bt * a.H + h0 + c16) * D + dh * C::DH + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KSQ; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (SPARSE) prime();
 
   f32x4 oacc[NB];
 #pragma unroll
@@ -244,38 +304,42 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a, int nsplit) {
   float m_run = -INFINITY, l_run = 0.f;  // head c16; m_run is the same in all four groups
   const float sl2 = a.scale * kLog2e;
 
-  const int nst = static_cast<int>((r_end - r_begin + C::ROWS - 1) / C::ROWS);
-  if (nst > 0)
-    issue_rows<D, SPARSE>(cbase, rbase, dummy, sidx, ring + moff, pitch, rb0 + row0, n_cmp, rb0, re0, win0, Lc, lane,
-                          mat ? nullptr : okf[0] + row0);
-
   for (int c = 0; c < nst; ++c) {
     const int buf = c & 1;
-    if (c + 1 < nst) {
-      issue_rows<D, SPARSE>(cbase, rbase, dummy, sidx, ring + (buf ^ 1) * C::STAGE + moff, pitch,
-                            rb0 + (c + 1) * C::ROWS + row0, n_cmp, rb0, re0, win0, Lc, lane,
-                            mat ? nullptr : okf[buf ^ 1] + row0);
-      wait_vmcnt<C::NI>();  // this stage's loads are done (each wave its own)
-    } else {
-      wait_vmcnt<0>();
+    if (mat == 0) {  // this wave's K rows of stage c (K of c+1 may stay in flight)
+      if (c + 1 < nst) wait_vmcnt<C::NI>();
+      else wait_vmcnt<0>();
     }
-    __syncthreads();
+    __syncthreads();  // A: K(c) in LDS; every wave is done with PV(c-1)
+    if (mat == 1 && c + 1 < nst) issue(c + 1);
     const uint8_t* Ks = ring + buf * C::STAGE;
     const uint8_t* Vs = Ks + C::KBYTES;
 
-    // ---- S^T = K Q^T: two 16-row tiles x 16 heads -------------------------
+    // ---- this half's S^T = K Q^T: two 16-row tiles x 16 heads --------------
     f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    const uint8_t* kp = Ks + c16 * C::PK + dh * C::DH * 2 + g * 16;
 #pragma unroll
     for (int ks = 0; ks < KSQ; ++ks) {
-      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Ks + c16 * C::PK + ks * 64 + g * 16);
-      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Ks + (16 + c16) * C::PK + ks * 64 + g * 16);
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kp + ks * 64);
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kp + 16 * C::PK + ks * 64);
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks], s1, 0, 0, 0);
     }
+    xs[wave][0][lane] = s0;
+    xs[wave][1][lane] = s1;
+    if (mat == 1) {  // this wave's V rows of stage c (V of c+1 may stay in flight)
+      if (c + 1 < nst) wait_vmcnt<C::NI>();
+      else wait_vmcnt<0>();
+    }
+    __syncthreads();  // B: V(c) in LDS; every wave is done with K(c)
+    if (mat == 0 && c + 2 < nst) issue(c + 2);
+    s0 += xs[wave ^ kHeadGroups][0][lane];
+    s1 += xs[wave ^ kHeadGroups][1][lane];
+
     // Online softmax (log2 units) for head c16 over its 8 rows here and the
     // other groups' 24, against a lazily re-based running max.
-    const i32x4 ok0 = *reinterpret_cast<const i32x4*>(&okf[buf][4 * g]);
-    const i32x4 ok1 = *reinterpret_cast<const i32x4*>(&okf[buf][16 + 4 * g]);
+    const i32x4 ok0 = *reinterpret_cast<const i32x4*>(&okf[c % 3][4 * g]);
+    const i32x4 ok1 = *reinterpret_cast<const i32x4*>(&okf[c % 3][16 + 4 * g]);
     float sv[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -316,7 +380,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a, int nsplit) {
 
     // ---- O += P V over the 32 rows: k slot 8g+j <-> row 4g+j (j < 4) or
     // row 16+4g+(j-4) -------------------------------------------------------
-    const uint8_t* v0 = Vs + (4 * g + (c16 >> 2)) * C::PV + (c16 & 3) * 8;
+    const uint8_t* v0 = Vs + (4 * g + (c16 >> 2)) * C::PV + (c16 & 3) * 8 + dh * C::DH * 2;
     const uint8_t* v1 = v0 + 16 * C::PV;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -325,14 +389,17 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a, int nsplit) {
       const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bv, oacc[nb], 0, 0, 0);
     }
-    __syncthreads();  // every wave is done with this stage before it is refilled
   }
+  __syncthreads();  // the ring is reused below
 
-  // ---- epilogue: oacc[nb][r] = O[head 4g+r][dim 16nb + c16] -----------------
+  // ---- epilogue: oacc[nb][r] = O[head 4g+r][dim dh*DH + 16nb + c16] --------
   float l_tot = l_run;
   l_tot += __shfl_xor(l_tot, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
-  float* ot = reinterpret_cast<float*>(ring) + wave * kHeadsPerWave * C::OP;  // this wave's 16 x D tile
+  float* ot = reinterpret_cast<float*>(ring) + wave * kHeadsPerWave * C::OP;  // this wave's 16 x DH tile
+  // One workgroup finishes in place (sink, normalisation, lse); a split
+  // writes its unnormalised bf16 rows and (m, l) for the combine kernel.
+  float sc = 1.f;  // per head c16
   if (nsplit == 1) {
     const float sig = a.sink ? a.sink[h0 + c16] * kLog2e : -INFINITY;
     const float M = fmaxf(m_run, sig);
@@ -341,101 +408,85 @@ __global__ __launch_bounds__(256, 1) void attn_mfma(AttnArgs a, int nsplit) {
       f = m_run == -INFINITY ? 0.f : fast_exp2(m_run - M);
       den = l_tot * f + (sig == -INFINITY ? 0.f : fast_exp2(sig - M));
     }
-    const float inv = den > 0.f ? f / den : 0.f;
-    if (a.lse && g == 0) a.lse[bt * a.H + h0 + c16] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
+    sc = den > 0.f ? f / den : 0.f;
+    if (a.lse && dh == 0 && g == 0) a.lse[bt * a.H + h0 + c16] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
+  } else if (dh == 0 && g == 0) {
+    float* wml = attn_ws_ml(a, nsplit) + ((bt * nsplit + split) * a.H + h0 + c16) * 2;
+    wml[0] = m_run;
+    wml[1] = l_tot;
+  }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float ir = __shfl(inv, 4 * g + r, 64);
+  for (int r = 0; r < 4; ++r) {
+    const float ir = __shfl(sc, 4 * g + r, 64);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) ot[(4 * g + r) * C::OP + nb * 16 + c16] = oacc[nb][r] * ir;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // 16 rows x D bf16, 8 dims (16 bytes) per lane and step
-    uint16_t* ob = static_cast<uint16_t*>(a.out) + (bt * a.H + h0) * D;
+    for (int nb = 0; nb < NB; ++nb) ot[(4 * g + r) * C::OP + nb * 16 + c16] = oacc[nb][r] * ir;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // 16 rows x DH bf16, 8 dims (16 bytes) per lane and step
+  uint16_t* ob = nsplit == 1 ? static_cast<uint16_t*>(a.out) + (bt * a.H + h0) * D
+                             : attn_ws_o(a) + ((bt * nsplit + split) * a.H + h0) * D;
+  ob += dh * C::DH;
 #pragma unroll
-    for (int it = 0; it < kHeadsPerWave * D / (64 * 8); ++it) {
-      const int e = it * 64 * 8 + lane * 8;
-      const int hl = e / D, dd = e % D;
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(ot + hl * C::OP + dd);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(ot + hl * C::OP + dd + 4);
-      u32x4 w;
-      w[0] = cvt_bf16x2(x0[0], x0[1]);
-      w[1] = cvt_bf16x2(x0[2], x0[3]);
-      w[2] = cvt_bf16x2(x1[0], x1[1]);
-      w[3] = cvt_bf16x2(x1[2], x1[3]);
-      *reinterpret_cast<u32x4*>(ob + e) = w;
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) ot[(4 * g + r) * C::OP + nb * 16 + c16] = oacc[nb][r];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float* wo = a.ws + ((bt * nsplit + split) * a.H + h0) * D;
-#pragma unroll
-    for (int it = 0; it < kHeadsPerWave * D / (64 * 4); ++it) {
-      const int e = it * 64 * 4 + lane * 4;
-      const int hl = e / D, dd = e % D;
-      *reinterpret_cast<f32x4*>(wo + e) = *reinterpret_cast<const f32x4*>(ot + hl * C::OP + dd);
-    }
-    if (g == 0) {
-      float* wml = a.ws + static_cast<int64_t>(a.B * a.T) * nsplit * a.H * D +
-                   ((bt * nsplit + split) * a.H + h0 + c16) * 2;
-      wml[0] = m_run;
-      wml[1] = l_tot;
-    }
+  for (int it = 0; it < kHeadsPerWave * C::DH / (64 * 8); ++it) {
+    const int e = it * 64 * 8 + lane * 8;
+    const int hl = e / C::DH, dd = e % C::DH;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(ot + hl * C::OP + dd);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(ot + hl * C::OP + dd + 4);
+    u32x4 w;
+    w[0] = cvt_bf16x2(x0[0], x0[1]);
+    w[1] = cvt_bf16x2(x0[2], x0[3]);
+    w[2] = cvt_bf16x2(x1[0], x1[1]);
+    w[3] = cvt_bf16x2(x1[2], x1[3]);
+    *reinterpret_cast<u32x4*>(ob + hl * D + dd) = w;
   }
 }
 
 // Merge split partials: O = sum_s 2^{m_s-M} O_s / (sum_s 2^{m_s-M} l_s + 2^{sig-M}).
-// One 256-thread workgroup per (query, head): the split weights go to LDS
-// once, then every thread merges two adjacent output dims across the splits.
-template <bool BF16>
+// One wavefront per (query, head), four per workgroup: lane s reads split s's
+// (m, l), then each lane merges 8 adjacent output dims (16-byte loads of the
+// bf16 partial rows) across the splits.
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int nsplit) {
-  __shared__ float fac[64];
-  __shared__ float inv_sh, lse_sh;
-  const int64_t bh = blockIdx.x;  // (bt, h)
+  __shared__ float fac[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t bh = static_cast<int64_t>(blockIdx.x) * 4 + w;  // (bt, h)
   const int64_t bt = bh / a.H;
   const int64_t h = bh % a.H;
   const int64_t D = a.d;
-  const float* wml = a.ws + static_cast<int64_t>(a.B * a.T) * nsplit * a.H * D;
-  if (threadIdx.x < 64) {
-    const int s = threadIdx.x;
-    const float ms = s < nsplit ? wml[((bt * nsplit + s) * a.H + h) * 2] : -INFINITY;
-    const float ls = s < nsplit ? wml[((bt * nsplit + s) * a.H + h) * 2 + 1] : 0.f;
-    const float sig = a.sink ? a.sink[h] * kLog2e : -INFINITY;
-    const float M = fmaxf(wave_max(ms), sig);
-    const float f = (M == -INFINITY || ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
-    fac[s] = f;
-    float den = wave_sum(ls * f);
-    if (M != -INFINITY && sig != -INFINITY) den += fast_exp2(sig - M);
-    if (s == 0) {
-      inv_sh = den > 0.f ? 1.f / den : 0.f;
-      lse_sh = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
-    }
-  }
-  __syncthreads();
-  const float inv = inv_sh;
-  for (int64_t c = 2 * threadIdx.x; c < D; c += 512) {
-    float a0 = 0.f, a1 = 0.f;
-    const float* src = a.ws + (bt * nsplit * a.H + h) * D + c;
+  const float* wml = attn_ws_ml(a, nsplit);
+  const float ms = lane < nsplit ? wml[((bt * nsplit + lane) * a.H + h) * 2] : -INFINITY;
+  const float ls = lane < nsplit ? wml[((bt * nsplit + lane) * a.H + h) * 2 + 1] : 0.f;
+  const float sig = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+  const float M = fmaxf(wave_max(ms), sig);
+  const float f = (M == -INFINITY || ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
+  fac[w][lane] = f;
+  float den = wave_sum(ls * f);
+  if (M != -INFINITY && sig != -INFINITY) den += fast_exp2(sig - M);
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane * 8 < D) {
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    const uint16_t* src = attn_ws_o(a) + (bt * nsplit * a.H + h) * D + lane * 8;
     for (int s = 0; s < nsplit; ++s) {
-      const float2 v = *reinterpret_cast<const float2*>(src + static_cast<int64_t>(s) * a.H * D);
-      a0 = fmaf(v.x, fac[s], a0);
-      a1 = fmaf(v.y, fac[s], a1);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(s) * a.H * D);
+      const float fs = fac[w][s];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc[2 * u] = fmaf(lo_bf16(v[u]), fs, acc[2 * u]);
+        acc[2 * u + 1] = fmaf(hi_bf16(v[u]), fs, acc[2 * u + 1]);
+      }
     }
-    if (BF16) {
-      *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + bh * D + c) = pack_bf16x2(a0 * inv, a1 * inv);
-    } else {
-      *reinterpret_cast<float2*>(static_cast<float*>(a.out) + bh * D + c) = make_float2(a0 * inv, a1 * inv);
-    }
+    u32x4 o;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = cvt_bf16x2(acc[2 * u] * inv, acc[2 * u + 1] * inv);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + bh * D + lane * 8) = o;
   }
-  if (a.lse && threadIdx.x == 0) a.lse[bh] = lse_sh;
+  if (a.lse && lane == 0) a.lse[bh] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
 }
 
 // fp32 storage: one wavefront per (query, head), VALU, 64 rows per step.
@@ -528,7 +579,7 @@ int attn_splits(int64_t B, int64_t T, int64_t H, int64_t d, int64_t max_rows, bo
   int64_t ns = (target + base - 1) / base;
   const int64_t cap = (max_rows + 63) / 64;  // keep >= 64 rows per split
   if (ns > cap) ns = cap;
-  if (ns > 64) ns = 64;
+  if (ns > kAttnMaxSplits) ns = kAttnMaxSplits;
   if (sparse) {  // a split caches at most kMaxIdx row indices
     const int64_t need = (max_rows + kMaxIdx - 1) / kMaxIdx;
     if (ns < need) ns = need;
@@ -539,7 +590,7 @@ int attn_splits(int64_t B, int64_t T, int64_t H, int64_t d, int64_t max_rows, bo
 
 size_t attn_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t d, int nsplit) {
   if (nsplit <= 1) return 0;
-  return static_cast<size_t>(B * T) * nsplit * H * (d + 2) * sizeof(float);
+  return static_cast<size_t>(B * T) * nsplit * H * (d * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
 hipError_t launch_attn(const AttnArgs& a, bool sparse, bool bf16, int nsplit, hipStream_t s) {
@@ -552,8 +603,8 @@ hipError_t launch_attn(const AttnArgs& a, bool sparse, bool bf16, int nsplit, hi
   const dim3 grid(static_cast<uint32_t>(a.B * a.T * (a.H / kHeadsPerWg) * nsplit));
 #define CSA_ATTN_LAUNCH(D_)                                                                            \
   case D_:                                                                                             \
-    if (sparse) hipLaunchKernelGGL((attn_mfma<D_, true>), grid, dim3(256), 0, s, a, nsplit);           \
-    else hipLaunchKernelGGL((attn_mfma<D_, false>), grid, dim3(256), 0, s, a, nsplit);                 \
+    if (sparse) hipLaunchKernelGGL((attn_mfma<D_, true>), grid, dim3(64 * kWaves), 0, s, a, nsplit);           \
+    else hipLaunchKernelGGL((attn_mfma<D_, false>), grid, dim3(64 * kWaves), 0, s, a, nsplit);                 \
     break;
   switch (a.d) {
     CSA_ATTN_LAUNCH(128)
@@ -564,7 +615,7 @@ hipError_t launch_attn(const AttnArgs& a, bool sparse, bool bf16, int nsplit, hi
 #undef CSA_ATTN_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
-  hipLaunchKernelGGL(attn_combine<true>, dim3(static_cast<uint32_t>(a.B * a.T * a.H)), dim3(256), 0, s, a,
+  hipLaunchKernelGGL(attn_combine, dim3(static_cast<uint32_t>(a.B * a.T * a.H / 4)), dim3(256), 0, s, a,
                      nsplit);
   return hipGetLastError();
 }

@@ -110,6 +110,8 @@ csa_status_t attn_common(const void* q, const void* kc, const void* vc, int64_t 
   REQUIRE(B >= 0 && T >= 1 && n_ctx >= T && L >= 0 && H >= 1 && d >= 1 && W >= 0,
           "need B >= 0, 1 <= T <= n_ctx, L >= 0, H >= 1, d >= 1, W >= 0");
   REQUIRE(std::isfinite(scale), "scale is not finite");
+  REQUIRE(L <= (int64_t(1) << 30) && R <= (int64_t(1) << 30) && W <= (int64_t(1) << 30),
+          "L, R and W must not exceed 2^30 rows");
   if (!csa::attn_shape_supported(H, d, dt == CSA_BF16))
     return fail(CSA_ERR_UNSUPPORTED, "no attention kernel for H=%lld d=%lld dtype=%d", (long long)H,
                 (long long)d, static_cast<int>(dt));
@@ -278,6 +280,9 @@ csa_status_t csa_sparse_attn(const void* q, const void* kc, const void* vc, int6
   csa_status_t st = attn_common(q, kc, vc, L, kr, vr, R, W, sink, scale, B, T, n_ctx, H, d, out, lse, dtype);
   if (st != CSA_OK) return st;
   REQUIRE(k >= 0, "k < 0");
+  if (dtype == CSA_BF16 && k + W > int64_t(csa::kAttnMaxSplits) * csa::kAttnMaxIdx)
+    return fail(CSA_ERR_UNSUPPORTED, "bf16 sparse attention supports k + W <= %lld rows (got %lld)",
+                (long long)csa::kAttnMaxSplits * csa::kAttnMaxIdx, (long long)(k + W));
   if (B == 0) return CSA_OK;
   if (k > 0) REQUIRE_PTR(idx);
   csa::AttnArgs a{q, kc, vc, L, 1, idx, k, kr, vr, R, W, sink, scale, B, T, n_ctx, H, d, out, lse,

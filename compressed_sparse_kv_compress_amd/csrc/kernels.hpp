@@ -61,6 +61,11 @@ struct AttnArgs {
   size_t ws_bytes;
 };
 // Number of row splits the attention launch uses, and its workspace bytes.
+// bf16 attention: at most kAttnMaxSplits splits per query (the combine kernel
+// gives one lane to each), and a CSA split caches at most kAttnMaxIdx row
+// indices, so a sparse row list (k + W) is limited to their product.
+constexpr int kAttnMaxSplits = 64;
+constexpr int kAttnMaxIdx = 2048;
 int attn_splits(int64_t B, int64_t T, int64_t H, int64_t d, int64_t max_rows, bool bf16, bool sparse);
 size_t attn_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t d, int nsplit);
 hipError_t launch_attn(const AttnArgs& a, bool sparse, bool bf16, int nsplit, hipStream_t s);

@@ -144,8 +144,12 @@ csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k
  *            R >= T + W - 1 and R <= n_ctx when W > 0
  *   sink: fp32 [H] or NULL (= no sink)   out : [B][T][H][d] dtype
  *   lse : fp32 [B][T][H] or NULL
- *   ws  : csa_sparse_attn_workspace(...) bytes (may be 0 => ws may be NULL)
- * bf16 needs H % 64 == 0 and d in {128, 256, 512}; fp32 needs d <= 512.
+ *   ws  : csa_sparse_attn_workspace(...) bytes (may be 0 => ws may be NULL),
+ *         16-byte aligned; holds the per-split partial rows of a launch
+ *         split over the row list (its contents are scratch)
+ * bf16 needs H % 64 == 0, d in {128, 256, 512} and k + W <= 131072;
+ * fp32 needs d <= 512.  L, R and W are at most 2^30.  Unsupported shapes
+ * return CSA_ERR_UNSUPPORTED, nothing is launched.
  * ------------------------------------------------------------------------- */
 size_t csa_sparse_attn_workspace(int64_t B, int64_t T, int64_t H, int64_t d, int64_t k, int64_t W,
                                  csa_dtype_t dtype);
