@@ -140,7 +140,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Direct global -> LDS load of one row piece: lane i's ESZ bytes at g land at
-// LDS byte address lds + ESZ * i (lds wave-uniform, through M0).  Issued as
+// LDS byte address lds + ESZ * i (lds wave-uniform, through M0), nontemporal
+// (each row is read once per launch).  Issued as
 // inline asm on purpose: the compiler does not then see an asynchronous LDS
 // write, so it adds no "wait for every outstanding load" before each later LDS
 // read (which would drain the prefetch ring); completion is instead awaited
@@ -152,12 +153,12 @@ __device__ __forceinline__ void dma_row(const char* g, const uint8_t* lds) {
   const uint32_t la = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(lds)));
   uint32_t saved;  // M0 is restored, so the compiler's own uses of it are unaffected
   if constexpr (ESZ == 16)
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
                  : "=&s"(saved)
                  : "v"(g), "s"(la)
                  : "memory");
   else
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off nt\n\ts_mov_b32 m0, %0"
                  : "=&s"(saved)
                  : "v"(g), "s"(la)
                  : "memory");

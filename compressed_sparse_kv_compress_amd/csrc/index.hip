@@ -9,15 +9,17 @@
 // Design (gfx950, bf16): in decode the scan over all index keys is the
 // dominant HBM stream (256 B per key at d_I = 128) while each key costs
 // H_I * d_I MACs, i.e. 64 flop per byte at H_I = 64: above the fp32 VALU
-// ridge, so the dot products run on MFMA.  One wavefront owns 16 keys at a
-// time: A = the query's H_I x d_I indexer block (held in VGPRs for the whole
-// kernel), B = 16 keys x d_I loaded straight from HBM into MFMA operand
-// layout (no LDS round trip: every key is used by exactly one wavefront),
-// v_mfma_f32_16x16x32_bf16 accumulates 16 heads x 16 keys per block.  In the
-// 16x16 output layout a lane holds one key column and 4 head rows per block,
-// so the ReLU and the weighted head sum are in-register FMAs plus two lane
-// exchanges; the epilogue writes 16 fp32 scores (64 B) per tile.
-// Each wavefront keeps three tiles (24 KiB) of keys in flight.
+// ridge, so the dot products run on MFMA (v_mfma_f32_16x16x32_bf16, A = the
+// query's H_I x d_I indexer block held in VGPRs, B = 16 keys, 16 heads x 16
+// keys per block).  Each wavefront streams one contiguous key range through a
+// private LDS ring of 16-key tiles filled by direct-to-LDS loads (a 4 KiB
+// tile = four 1 KiB wave loads, several tiles in flight); the 16-byte pieces
+// of each key are placed XOR-swizzled by the load addresses so that the MFMA
+// operand reads hit distinct LDS banks.  In the 16x16 output layout a lane
+// holds one key column and 4 head rows per block, so the ReLU and the
+// weighted head sum are in-register FMAs plus two lane exchanges; the
+// epilogue writes 16 fp32 scores (64 B) per tile.  The grid is about one
+// workgroup per CU, so every wavefront streams megabytes with one prologue.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -25,34 +27,96 @@ namespace csa {
 namespace {
 
 constexpr int kWaves = 4;
-#ifndef CSA_INDEX_TILES
-#define CSA_INDEX_TILES 16
-#endif
 #ifndef CSA_INDEX_DEPTH
-#define CSA_INDEX_DEPTH 3
+#define CSA_INDEX_DEPTH 6
 #endif
-#ifndef CSA_INDEX_NT
-#define CSA_INDEX_NT 1
-#endif
-constexpr int kTileKeys = 16;                   // keys per MFMA tile (the N dimension)
-constexpr int kTilesPerWave = CSA_INDEX_TILES;  // tiles streamed by one wavefront
-constexpr int kDepth = CSA_INDEX_DEPTH;         // tiles in flight per wavefront
-constexpr int kKeysPerWg = kWaves * kTilesPerWave * kTileKeys;
+constexpr int kTileKeys = 16;                 // keys per MFMA tile (the N dimension)
+constexpr int kDepth = CSA_INDEX_DEPTH;       // ring slots per wavefront (kDepth - 1 tiles in flight)
+constexpr int kTileBytes = kTileKeys * 256;   // d_I = 128 bf16 keys
+constexpr int kMinKeysPerWave = 256;
+constexpr int kMaxKeysPerWave = 3968;         // scores of a workgroup stay in LDS (62 KiB)
+constexpr int kMaxTiles = kMaxKeysPerWave / kTileKeys;
+constexpr int kDirectTiles = 16;  // tiles per wavefront of the d_I = 64 kernel
+constexpr int kDirectKeysPerWg = kWaves * kDirectTiles * kTileKeys;
 
-// MB = H_I / 16 head blocks (the M dimension), KS = d_I / 32 k-steps.
-// Only d_I = 128 (KS = 4: one key = 16 granules of 16 B) uses the coalesced
-// LDS re-layout below; it is the shape of every CSA configuration.
-template <int MB, int KS, bool HAS_W>
-__global__ __launch_bounds__(256) void index_score_mfma(IndexScoreArgs a, int64_t parts) {
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until at most 4 * n of this wave's loads are outstanding (n < kDepth).
+__device__ __forceinline__ void wait_tiles(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<4>(); break;
+    case 2: wait_vmcnt<8>(); break;
+    case 3: wait_vmcnt<12>(); break;
+    case 4: wait_vmcnt<16>(); break;
+    case 5: wait_vmcnt<20>(); break;
+    case 6: wait_vmcnt<24>(); break;
+    default: wait_vmcnt<28>(); break;
+  }
+  asm volatile("" ::: "memory");
+}
+static_assert(kDepth >= 2 && kDepth <= 8, "wait_tiles covers up to 7 tiles in flight");
+
+// 16 bytes per lane, global -> LDS at lds + 16 * lane (lds wave-uniform, via
+// M0), nontemporal (every key is read once: streaming through the caches
+// with nt measured 7.1 TB/s against 5.8 TB/s without on a 1 GiB scan).
+// Inline asm on purpose: the compiler then adds no implicit "drain all
+// loads" before later LDS reads; completion is awaited with explicit vmcnt
+// waits.  The instruction writes no registers; M0 is restored.  The first
+// form takes a wave-uniform base and a 32-bit lane offset, the second a full
+// per-lane address.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* lds) {
+  typedef const uint8_t __attribute__((address_space(3))) * lds_ptr;
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(lds)));
+}
+__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, const uint8_t* lds) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2 nt\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(voff), "s"(sbase), "s"(lds_addr(lds))
+               : "memory");
+}
+__device__ __forceinline__ void dma16(const void* g, const uint8_t* lds) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(g), "s"(lds_addr(lds))
+               : "memory");
+}
+
+// Sum of x over the four 16-lane groups (lanes c, c+16, c+32, c+48), in every
+// lane, by the gfx950 row-swap permutes (no LDS round trip).
+__device__ __forceinline__ float group_sum4(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const uint32_t v = __float_as_uint(y);
+  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// d_I = 128 (KS = 4), MB = H_I / 16 head blocks.  Workgroup (row, part)
+// scores keys [part * 4 * per_wave, +4 * per_wave); its wavefront w takes
+// tiles w, w+4, w+8, ... so that the four stream through adjacent memory.
+// Scores collect in LDS and leave in one coalesced pass at the end, so the
+// loop issues no stores (their completions would share the load counter the
+// ring waits on).
+template <int MB, bool HAS_W>
+__global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, int64_t parts, int64_t per_wave) {
   constexpr int HI = 16 * MB;
-  constexpr int DI = 32 * KS;
-  constexpr int GRAN = DI / 8;                 // 16-byte granules per key
-  constexpr int TILE_BYTES = kTileKeys * DI * 2;
-  constexpr int LOADS = TILE_BYTES / 1024;     // 1 KiB wave-wide loads per tile
-  static_assert(GRAN == 16 && LOADS == 4, "coalesced tile layout assumes d_I = 128");
-  __shared__ __attribute__((aligned(16))) uint32_t lds[kWaves][2][TILE_BYTES / 4];
+  constexpr int DI = 128;
+  constexpr int KS = 4;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][kDepth][kTileBytes];
+  __shared__ float sbuf[kWaves][kMaxTiles * kTileKeys];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;    // 16-lane group: k-slots 8g .. 8g+7 of every k-step
+  const int c16 = lane & 15;  // key column within the tile
   const int64_t lrow = blockIdx.x / parts;
   const int64_t part = blockIdx.x % parts;
   const int64_t row = a.row0 + lrow;
@@ -62,37 +126,43 @@ __global__ __launch_bounds__(256) void index_score_mfma(IndexScoreArgs a, int64_
   if (nv > a.L) nv = a.L;
   float* srow = a.score + lrow * a.ld;
 
-  const int64_t wave_begin = part * kKeysPerWg + wave * (kTilesPerWave * kTileKeys);
-  if (wave_begin >= a.L) return;
-  const int g = lane >> 4;    // 16-lane group: k-slots 8g .. 8g+7 of every k-step
-  const int c16 = lane & 15;  // key column within the tile
+  const int64_t kb = part * kWaves * per_wave;  // first key of the workgroup
+  const int64_t ke = kb + kWaves * per_wave < a.L ? kb + kWaves * per_wave : a.L;
+  const int64_t kv = ke < nv ? ke : nv;  // keys [kb, kv) are visible
+  const int ntiles = kv > kb ? static_cast<int>((kv - kb + kTileKeys - 1) / kTileKeys) : 0;
+  const int ntv = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+  const int64_t k0 = kb + static_cast<int64_t>(wave) * kTileKeys;  // first key of this wave's tile 0
+  constexpr int64_t kStride = kWaves * kTileKeys;                    // keys between its tiles
 
-  if (wave_begin >= nv) {  // nothing visible in this wavefront's range
-    for (int i = 0; i < kTilesPerWave; ++i) {
-      const int64_t s = wave_begin + i * kTileKeys + c16;
-      if (g == 0 && s < a.L) srow[s] = -INFINITY;
-    }
-    return;
-  }
-
-  // Coalesced key stream: load i of a tile covers keys 4i .. 4i+3 (1 KiB
-  // contiguous); lane l holds granule l%16 of key 4i + l/16.  Loads are
-  // unconditional (rows past the end are clamped to the last one), so the
-  // stream has no control flow and the whole prefetch window is in flight.
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.L * DI;
-  const int64_t s_last = a.L - 1;
-  auto load_tile = [&](int it, u32x4* frag) {
+  // Tile layout in LDS: key kk (0..15) at kk*256; its 16-byte piece p at
+  // slot p ^ kk.  Load j of a tile covers keys 4j .. 4j+3 (1 KiB contiguous
+  // in HBM); lane l writes slot l%16 of key 4j + l/16, so it fetches piece
+  // (l%16) ^ kk.  Only a tile that runs past the last key (the very end of a
+  // row) takes per-lane clamped addresses.
+  const char* kbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + b * a.L * DI);
+  uint32_t voff[4];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      int64_t s = wave_begin + it * kTileKeys + 4 * i + g;
-      s = s < s_last ? s : s_last;
-      const u32x4* p = reinterpret_cast<const u32x4*>(kbase + s * DI) + c16;
-      frag[i] = CSA_INDEX_NT ? __builtin_nontemporal_load(p) : *p;
+  for (int j = 0; j < 4; ++j) voff[j] = (4 * j + g) * 256 + ((c16 ^ (4 * j + g)) << 4);
+  uint8_t* myring = &ring[wave][0][0];
+  auto issue = [&](int it) {
+    uint8_t* slot = myring + (it % kDepth) * kTileBytes;
+    const int64_t t0 = k0 + static_cast<int64_t>(it) * kStride;
+    if (t0 + kTileKeys <= a.L) {
+      const char* tb = kbase + t0 * (DI * 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma16(tb, voff[j], slot + j * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int64_t s = t0 + 4 * j + g;
+        s = s < a.L - 1 ? s : a.L - 1;
+        dma16(kbase + s * (DI * 2) + ((c16 ^ (4 * j + g)) << 4), slot + j * 1024);
+      }
     }
   };
-  u32x4 buf[kDepth][LOADS];
 #pragma unroll
-  for (int i = 0; i < kDepth - 1; ++i) load_tile(i, buf[i]);
+  for (int i = 0; i < kDepth - 1; ++i)
+    if (i < ntv) issue(i);
 
   // A operand: query heads (rows) x index dims, resident for the whole kernel.
   const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + row * HI * DI;
@@ -102,7 +172,6 @@ __global__ __launch_bounds__(256) void index_score_mfma(IndexScoreArgs a, int64_
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       afrag[mb][ks] = *reinterpret_cast<const bf16x8*>(qrow + (mb * 16 + c16) * DI + ks * 32 + g * 8);
-
   // Head weights for the 4 head rows this lane holds in each 16x16 block.
   float wr[MB][HAS_W ? 4 : 1];
   if (HAS_W) {
@@ -111,26 +180,23 @@ __global__ __launch_bounds__(256) void index_score_mfma(IndexScoreArgs a, int64_
 #pragma unroll
       for (int r = 0; r < (HAS_W ? 4 : 1); ++r) wr[mb][r] = a.w[row * HI + mb * 16 + 4 * g + r];
   }
+  // Everything above is in registers / LDS before the loop (so the compiler
+  // places no waits inside it); the first tiles have landed too.
+  wait_vmcnt<0>();
+  asm volatile("" ::: "memory");
 
-#pragma unroll
-  for (int it = 0; it < kTilesPerWave; ++it) {
-    if (it + kDepth - 1 < kTilesPerWave) load_tile(it + kDepth - 1, buf[(it + kDepth - 1) % kDepth]);
-    // Re-layout through a wave-private LDS tile.  Granule p of key kk sits in
-    // slot kk*16 + (p ^ kk): the stores (16 lanes per key) and the MFMA-layout
-    // loads (16 keys per granule) both touch 16 distinct bank groups.
-    uint32_t* t = lds[wave][it & 1];
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int kk = 4 * i + g;
-      *reinterpret_cast<u32x4*>(t + 4 * (kk * 16 + (c16 ^ kk))) = buf[it % kDepth][i];
+  float* sb = sbuf[wave];
+  for (int it = 0; it < ntv; ++it) {
+    if (it + kDepth - 1 < ntv) {
+      issue(it + kDepth - 1);
+      wait_tiles(kDepth - 1);
+    } else {
+      wait_tiles(ntv - 1 - it);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint8_t* t = myring + (it % kDepth) * kTileBytes + c16 * 256;
     bf16x8 cur[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      cur[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(t + 4 * (c16 * 16 + ((4 * ks + g) ^ c16))));
+    for (int ks = 0; ks < KS; ++ks) cur[ks] = *reinterpret_cast<const bf16x8*>(t + (((4 * ks + g) ^ c16) << 4));
     f32x4 acc[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -140,20 +206,30 @@ __global__ __launch_bounds__(256) void index_score_mfma(IndexScoreArgs a, int64_
       for (int mb = 0; mb < MB; ++mb)
         acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[mb][ks], cur[ks], acc[mb], 0, 0, 0);
     // lane holds S[head mb*16 + 4g + r][key c16]: ReLU, head weights, and the
-    // sum over heads (in-lane, then across the four lane groups).
-    float part_sum = 0.f;
+    // sum over heads (a short tree in-lane, then across the four lane groups).
+    float ps[MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb) {
+      float x[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float rl = fmaxf(acc[mb][r], 0.f);
-        part_sum = HAS_W ? fmaf(wr[mb][HAS_W ? r : 0], rl, part_sum) : part_sum + rl;
-      }
-    part_sum += __shfl_xor(part_sum, 16, 64);
-    part_sum += __shfl_xor(part_sum, 32, 64);
-    const int64_t s = wave_begin + it * kTileKeys + c16;
-    const float val = s < nv ? part_sum : -INFINITY;
-    if (g == 0 && s < a.L) srow[s] = val;
+      for (int r = 0; r < 4; ++r) x[r] = HAS_W ? wr[mb][HAS_W ? r : 0] * fmaxf(acc[mb][r], 0.f) : fmaxf(acc[mb][r], 0.f);
+      ps[mb] = (x[0] + x[1]) + (x[2] + x[3]);
+    }
+#pragma unroll
+    for (int w = 1; w < MB; w <<= 1)
+#pragma unroll
+      for (int mb = 0; mb + w < MB; mb += 2 * w) ps[mb] += ps[mb + w];
+    const float tot = group_sum4(ps[0]);
+    const int64_t s = k0 + static_cast<int64_t>(it) * kStride + c16;
+    if (g == 0) sb[it * kTileKeys + c16] = s < nv ? tot : -INFINITY;
+  }
+
+  // Write the workgroup's scores [kb, ke) in key order; keys past the visible
+  // ones (none in decode) are -inf.  Tile T of the range is tile T/4 of wave T%4.
+  __syncthreads();
+  for (int64_t o = threadIdx.x; o < ke - kb; o += 64 * kWaves) {
+    const int64_t T = o / kTileKeys;
+    srow[kb + o] = T < ntiles ? sbuf[T % kWaves][(T / kWaves) * kTileKeys + o % kTileKeys] : -INFINITY;
   }
 }
 
@@ -173,7 +249,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_direct(IndexScoreArgs a,
   int64_t nv = tpos / a.m;
   if (nv > a.L) nv = a.L;
   float* srow = a.score + lrow * a.ld;
-  const int64_t wave_begin = part * kKeysPerWg + wave * (kTilesPerWave * kTileKeys);
+  const int64_t wave_begin = part * kDirectKeysPerWg + wave * (kDirectTiles * kTileKeys);
   if (wave_begin >= a.L) return;
   const int g = lane >> 4;
   const int c16 = lane & 15;
@@ -185,7 +261,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_direct(IndexScoreArgs a,
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       afrag[mb][ks] = *reinterpret_cast<const bf16x8*>(qrow + (mb * 16 + c16) * DI + ks * 32 + g * 8);
-  for (int it = 0; it < kTilesPerWave; ++it) {
+  for (int it = 0; it < kDirectTiles; ++it) {
     int64_t s = wave_begin + it * kTileKeys + c16;
     const int64_t sc = s < a.L - 1 ? s : a.L - 1;
     bf16x8 cur[KS];
@@ -250,23 +326,49 @@ __global__ __launch_bounds__(256) void index_score_f32(IndexScoreArgs a, int64_t
 hipError_t launch_index_score(const IndexScoreArgs& a, bool bf16, hipStream_t s) {
   if (a.nrows == 0 || a.L == 0) return hipSuccess;
   if (bf16) {
-    const int64_t parts = (a.L + kKeysPerWg - 1) / kKeysPerWg;
-    const dim3 grid(static_cast<uint32_t>(a.nrows * parts));
     const int mb = static_cast<int>(a.HI / 16), ks = static_cast<int>(a.dI / 32);
     const bool w = a.w != nullptr;
-#define CSA_INDEX_LAUNCH(K_, MB_, KS_)                                                                \
-  if (mb == MB_ && ks == KS_) {                                                                       \
-    if (w) hipLaunchKernelGGL((K_<MB_, KS_, true>), grid, dim3(256), 0, s, a, parts);                 \
-    else hipLaunchKernelGGL((K_<MB_, KS_, false>), grid, dim3(256), 0, s, a, parts);                  \
-  } else
-    CSA_INDEX_LAUNCH(index_score_mfma, 4, 4)
-    CSA_INDEX_LAUNCH(index_score_mfma, 2, 4)
-    CSA_INDEX_LAUNCH(index_score_mfma, 8, 4)
-    CSA_INDEX_LAUNCH(index_score_mfma, 1, 4)
-    CSA_INDEX_LAUNCH(index_score_mfma_direct, 4, 2)
-    CSA_INDEX_LAUNCH(index_score_mfma_direct, 2, 2)
-    { return hipErrorInvalidValue; }
+    if (ks == 4) {
+      // About one workgroup per CU in one round; every wavefront streams
+      // kMinKeysPerWave .. kMaxKeysPerWave keys.
+      const int64_t target = 256;
+      int64_t parts = (target + a.nrows - 1) / a.nrows;
+      int64_t per_wave = (a.L + kWaves * parts - 1) / (kWaves * parts);
+      per_wave = (per_wave + kTileKeys - 1) / kTileKeys * kTileKeys;
+      if (per_wave < kMinKeysPerWave) per_wave = kMinKeysPerWave;
+      if (per_wave > kMaxKeysPerWave) per_wave = kMaxKeysPerWave;
+      parts = (a.L + kWaves * per_wave - 1) / (kWaves * per_wave);
+      const dim3 grid(static_cast<uint32_t>(a.nrows * parts));
+#define CSA_INDEX_LAUNCH(MB_)                                                                          \
+  case MB_:                                                                                            \
+    if (w) hipLaunchKernelGGL((index_score_stream<MB_, true>), grid, dim3(256), 0, s, a, parts, per_wave); \
+    else hipLaunchKernelGGL((index_score_stream<MB_, false>), grid, dim3(256), 0, s, a, parts, per_wave); \
+    break;
+      switch (mb) {
+        CSA_INDEX_LAUNCH(1)
+        CSA_INDEX_LAUNCH(2)
+        CSA_INDEX_LAUNCH(4)
+        CSA_INDEX_LAUNCH(8)
+        default: return hipErrorInvalidValue;
+      }
 #undef CSA_INDEX_LAUNCH
+    } else if (ks == 2) {
+      const int64_t parts = (a.L + kDirectKeysPerWg - 1) / kDirectKeysPerWg;
+      const dim3 grid(static_cast<uint32_t>(a.nrows * parts));
+#define CSA_INDEX_LAUNCH(MB_)                                                                             \
+  case MB_:                                                                                               \
+    if (w) hipLaunchKernelGGL((index_score_mfma_direct<MB_, 2, true>), grid, dim3(256), 0, s, a, parts);  \
+    else hipLaunchKernelGGL((index_score_mfma_direct<MB_, 2, false>), grid, dim3(256), 0, s, a, parts);   \
+    break;
+      switch (mb) {
+        CSA_INDEX_LAUNCH(2)
+        CSA_INDEX_LAUNCH(4)
+        default: return hipErrorInvalidValue;
+      }
+#undef CSA_INDEX_LAUNCH
+    } else {
+      return hipErrorInvalidValue;
+    }
   } else {
     const int64_t parts = (a.L + 255) / 256;
     const size_t lds = static_cast<size_t>(a.HI * a.dI) * sizeof(float);
