@@ -46,7 +46,6 @@ struct Shared {
   uint32_t wsum[kWaves];
   uint32_t sel_bin, sel_above;
   int32_t pcnt[kMaxMergeParts];
-  float sv[kStage];
   int32_t si[kStage];
   uint32_t ck[kSmall];  // keys of the threshold bin
   uint32_t ncand, thr, take;
@@ -250,13 +249,13 @@ __device__ __forceinline__ void radix_select(const uint32_t (&keys)[kItems], uin
 // first take_eq such items of the whole sequence of tiles) get consecutive
 // output slots in entry order after *base_gt / *base_eq earlier ones.  A tile
 // holds at most 16384 entries, so both counts fit 16-bit halves of one scan.
+// emit(j, slot) runs only for kept items (a few per thread): the thread's kept
+// mask is built first and its set bits are walked.
 template <typename Emit>
 __device__ __forceinline__ void compact_tile(const uint32_t (&keys)[kItems], uint32_t vmask, uint32_t thr,
                                              uint32_t take_eq, Shared& sh, uint32_t* base_gt, uint32_t* base_eq,
                                              Emit emit) {
   const int wave = threadIdx.x >> 6;
-  // Per-item flags as two 32-bit masks (held in one VGPR each, rather than 64
-  // lane masks in SGPRs across the scan).
   uint32_t gtm = 0, eqm = 0;
 #pragma unroll
   for (int j = 0; j < kItems; ++j) {
@@ -265,7 +264,8 @@ __device__ __forceinline__ void compact_tile(const uint32_t (&keys)[kItems], uin
   }
   gtm &= vmask;
   eqm &= vmask;
-  const uint32_t packed = (static_cast<uint32_t>(__popc(eqm)) << 16) | static_cast<uint32_t>(__popc(gtm));
+  const uint32_t neq = __popc(eqm);
+  const uint32_t packed = (neq << 16) | static_cast<uint32_t>(__popc(gtm));
   const uint32_t incl = wave_incl_scan(packed);
   if (lane_id() == 63) sh.wsum[wave] = incl;
   __syncthreads();
@@ -275,16 +275,22 @@ __device__ __forceinline__ void compact_tile(const uint32_t (&keys)[kItems], uin
     excl += w < wave ? sh.wsum[w] : 0u;
     total += sh.wsum[w];
   }
-  const uint32_t gt0 = *base_gt + (excl & 0xffffu);
-  const uint32_t eq0 = *base_eq + (excl >> 16);
-#pragma unroll
-  for (int j = 0; j < kItems; ++j) {
-    const uint32_t below = (1u << j) - 1u;
-    const uint32_t gt_before = gt0 + __popc(gtm & below);
-    const uint32_t eq_before = eq0 + __popc(eqm & below);
-    const bool gt = (gtm >> j) & 1u;
-    const bool eq = (eqm >> j) & 1u;
-    if (gt || (eq && eq_before < take_eq)) emit(j, gt_before + (eq_before < take_eq ? eq_before : take_eq));
+  const uint32_t gt0 = *base_gt + (excl & 0xffffu);  // greater items before this thread
+  const uint32_t eq0 = *base_eq + (excl >> 16);      // equal items before this thread
+  // This thread keeps its lowest min(neq, take_eq - eq0) equal items.
+  uint32_t keq = take_eq > eq0 ? take_eq - eq0 : 0u;
+  uint32_t em = eqm, km = gtm;
+  while (keq > 0 && em) {
+    const uint32_t bit = em & (0u - em);
+    km |= bit;
+    em ^= bit;
+    --keq;
+  }
+  uint32_t slot = gt0 + (eq0 < take_eq ? eq0 : take_eq);  // kept items before this thread
+  while (km) {
+    const int j = __builtin_ctz(km);
+    km &= km - 1u;
+    emit(j, slot++);
   }
   *base_gt += total & 0xffffu;
   *base_eq += total >> 16;
@@ -356,18 +362,17 @@ __global__ __launch_bounds__(kThreads) void topk_part_kernel(TopkArgs a, int64_t
   uint32_t thr, take_eq;
   radix_select(keys, vmask, static_cast<uint32_t>(cap), sh, &thr, &take_eq);
   uint32_t bg = 0, be = 0;
-  if (cap <= kStage) {  // stage the kept pairs in LDS, then store them coalesced
-    compact_tile(keys, vmask, thr, take_eq, sh, &bg, &be, [&](int j, uint32_t pos) {
-      sh.sv[pos] = v[j];
-      sh.si[pos] = static_cast<int32_t>(base + i0 + j);
-    });
+  if (cap <= kStage) {  // stage the kept entries in LDS, then store them coalesced
+    compact_tile(keys, vmask, thr, take_eq, sh, &bg, &be,
+                 [&](int j, uint32_t pos) { sh.si[pos] = i0 + j; });
     for (int i = tid; i < cap; i += kThreads) {
-      ov[i] = sh.sv[i];
-      oi[i] = sh.si[i];
+      const int li = sh.si[i];
+      ov[i] = s[li];
+      oi[i] = static_cast<int32_t>(base + li);
     }
   } else {
     compact_tile(keys, vmask, thr, take_eq, sh, &bg, &be, [&](int j, uint32_t pos) {
-      ov[pos] = v[j];
+      ov[pos] = s[i0 + j];
       oi[pos] = static_cast<int32_t>(base + i0 + j);
     });
   }
@@ -445,19 +450,18 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a, int np
   uint32_t thr, take_eq;
   radix_select(keys, vmask, static_cast<uint32_t>(a.k), sh, &thr, &take_eq);
   uint32_t bg = 0, be = 0;
-  if (a.k <= kStage) {  // stage in LDS, then store coalesced
-    compact_tile(keys, vmask, thr, take_eq, sh, &bg, &be, [&](int j, uint32_t pos) {
-      sh.sv[pos] = v[j];
-      sh.si[pos] = ix[j];
-    });
+  if (a.k <= kStage) {  // stage the kept slots in LDS, then store coalesced
+    compact_tile(keys, vmask, thr, take_eq, sh, &bg, &be,
+                 [&](int j, uint32_t pos) { sh.si[pos] = s0 + j; });
     for (int i = tid; i < a.k; i += kThreads) {
-      o[i] = sh.si[i];
-      if (os) os[i] = sh.sv[i];
+      const int sl = sh.si[i];
+      o[i] = ri[sl];
+      if (os) os[i] = rv[sl];
     }
   } else {
     compact_tile(keys, vmask, thr, take_eq, sh, &bg, &be, [&](int j, uint32_t pos) {
-      o[pos] = ix[j];
-      if (os) os[pos] = v[j];
+      o[pos] = ri[s0 + j];
+      if (os) os[pos] = rv[s0 + j];
     });
   }
 }
@@ -538,9 +542,10 @@ __global__ __launch_bounds__(kThreads) void topk_merge_general(TopkArgs a, int64
       ix[j] = ok ? ri[sl] : 0;
       keys[j] = float_key(v[j]);
     }
+    const int64_t sl0 = t0 + static_cast<int64_t>(tid) * kItems;
     compact_tile(keys, vmask, prefix, remaining, sh, &bg, &be, [&](int j, uint32_t pos) {
-      o[pos] = ix[j];
-      if (os) os[pos] = v[j];
+      o[pos] = ri[sl0 + j];
+      if (os) os[pos] = rv[sl0 + j];
     });
   }
 }
