@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
   constexpr int DI = 128;
   constexpr int KS = 4;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][kDepth][kTileBytes];
-  __shared__ float sbuf[kWaves][kMaxTiles * kTileKeys];
+  __shared__ __attribute__((aligned(16))) float sbuf[kWaves][kMaxTiles * kTileKeys];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;    // 16-lane group: k-slots 8g .. 8g+7 of every k-step
@@ -225,11 +225,26 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
   }
 
   // Write the workgroup's scores [kb, ke) in key order; keys past the visible
-  // ones (none in decode) are -inf.  Tile T of the range is tile T/4 of wave T%4.
+  // ones (none in decode) are -inf.  Tile T of the range is tile T/4 of wave
+  // T%4; four consecutive keys share a tile, so they move as one 16-byte
+  // piece (one LDS read, one store when the row is 16-byte aligned).
   __syncthreads();
-  for (int64_t o = threadIdx.x; o < ke - kb; o += 64 * kWaves) {
-    const int64_t T = o / kTileKeys;
-    srow[kb + o] = T < ntiles ? sbuf[T % kWaves][(T / kWaves) * kTileKeys + o % kTileKeys] : -INFINITY;
+  const int nk = static_cast<int>(ke - kb);
+  float* dst = srow + kb;
+  const bool aligned = (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
+  for (int o = 4 * static_cast<int>(threadIdx.x); o < nk; o += 4 * 64 * kWaves) {
+    const int T = o / kTileKeys;
+    f32x4 x = *reinterpret_cast<const f32x4*>(&sbuf[T % kWaves][(T / kWaves) * kTileKeys + o % kTileKeys]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((o + e) / kTileKeys >= ntiles) x[e] = -INFINITY;
+    if (aligned && o + 4 <= nk) {
+      *reinterpret_cast<f32x4*>(dst + o) = x;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (o + e < nk) dst[o + e] = x[e];
+    }
   }
 }
 
