@@ -134,6 +134,7 @@ class GpuState:
                 m = st.m_csa
                 lay["ki"] = gen((B, L, dI), "kic", si)
                 lay["qi"] = gen((B, 1, st.HI, dI), "q_idx", si)
+                lay["wi"] = gen((B, 1, st.HI), "w_idx", st.HI ** -0.5, torch.float32)
                 p0 = (st.csa_new - 1) * m
                 for s, D, sc in (("k", d, sd), ("v", d, sd), ("idx", dI, si)):
                     xa = "k" if s == "k" else ("v" if s == "v" else "k_idx")
@@ -214,7 +215,7 @@ class GpuState:
             if lay["kind"] == "csa":
                 m = st.m_csa
                 mark("index_score")
-                csa.csa_index_score(lay["qi"], lay["ki"], m, n_ctx=st.n_ctx, out=lay["score"])
+                csa.csa_index_score(lay["qi"], lay["ki"], m, w_idx=lay["wi"], n_ctx=st.n_ctx, out=lay["score"])
                 mark("index_score_end")
                 mark("topk_select")
                 csa.csa_topk_select(lay["score"], m, st.k, n_ctx=st.n_ctx, idx=lay["idx"], ws=lay["topk_ws"])
@@ -309,12 +310,14 @@ def cpu_baseline(st: Stack, sample: int):
             qi = np.stack([full((st.B, 1, st.HI, st.dI), "q_idx", si, li,
                                 rows=np.arange(b * st.HI, (b + 1) * st.HI)) for b in range(S)])
             qi = qi.reshape(S, 1, st.HI, st.dI)
+            wi = np.stack([full((st.B, 1, st.HI), "w_idx", st.HI ** -0.5, li, dtype=torch.float32,
+                                rows=np.arange(b, b + 1)) for b in range(S)]).reshape(S, 1, st.HI)
             t0 = time.perf_counter()
             for s in ("k", "v", "idx"):
                 xa, za, xb, zb = raws[s]
                 oracle.compress(xa, za, m, x_b=xb, z_b=zb, n=st.n_ctx, p0=p0, e0=st.csa_new,
                                 e1=st.csa_new + 1)
-            idx, _ = oracle.index_topk(qi, ki, m, st.k, n_ctx=st.n_ctx)
+            idx, _ = oracle.index_topk(qi, ki, m, st.k, w=wi, n_ctx=st.n_ctx)
             total += time.perf_counter() - t0
             # gather only the selected rows of the compressed K/V caches
             kc = np.zeros((S, st.k, st.d))

@@ -447,7 +447,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
 // Merge split partials: O = sum_s 2^{m_s-M} O_s / (sum_s 2^{m_s-M} l_s + 2^{sig-M}).
 // One wavefront per (query, head), four per workgroup: lane s reads split s's
 // (m, l), then each lane merges 8 adjacent output dims (16-byte loads of the
-// bf16 partial rows) across the splits.
+// bf16 partial rows) across the splits, eight splits per round trip.
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int nsplit) {
   __shared__ float fac[4][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -473,13 +473,24 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int nsplit) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     const uint16_t* src = attn_ws_o(a) + (bt * nsplit * a.H + h) * D + lane * 8;
-    for (int s = 0; s < nsplit; ++s) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(s) * a.H * D);
-      const float fs = fac[w][s];
+    const int64_t sstride = a.H * D;
+    // Eight splits' rows are requested together (one memory round trip per
+    // eight); missing splits of the last group read split 0 with weight 0.
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+      u32x4 v[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        acc[2 * u] = fmaf(lo_bf16(v[u]), fs, acc[2 * u]);
-        acc[2 * u + 1] = fmaf(hi_bf16(v[u]), fs, acc[2 * u + 1]);
+      for (int q = 0; q < 8; ++q) {
+        const int s = s0 + q < nsplit ? s0 + q : 0;
+        v[q] = *reinterpret_cast<const u32x4*>(src + s * sstride);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float fs = s0 + q < nsplit ? fac[w][s0 + q] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          acc[2 * u] = fmaf(lo_bf16(v[q][u]), fs, acc[2 * u]);
+          acc[2 * u + 1] = fmaf(hi_bf16(v[q][u]), fs, acc[2 * u + 1]);
+        }
       }
     }
     u32x4 o;

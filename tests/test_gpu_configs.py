@@ -66,9 +66,10 @@ def test_config1_csa_fp32_end_to_end():
     xi, zi = g_make((B, n, dI), seed, "k_idx", f32, si, dev), g_make((B, n, dI), seed, "z_idx", f32, 0.5, dev)
     q = g_make((B, T, H, d), seed, "q", f32, sd, dev)
     qi = g_make((B, T, HI, dI), seed, "q_idx", f32, si, dev)
+    wi = g_make((B, T, HI), seed, "w_idx", f32, HI ** -0.5, dev)
     sink = g_make((H,), seed, "sink", f32, 1.0, dev)
     kc, vc, ki = csa.csa_compress(xk, zk, m), csa.csa_compress(xv, zv, m), csa.csa_compress(xi, zi, m)
-    idx = csa.csa_index_topk(qi, ki, m, k, n_ctx=n)
+    idx = csa.csa_index_topk(qi, ki, m, k, w_idx=wi, n_ctx=n)
     R = T + W - 1
     out, lse = csa.csa_sparse_attn(q, kc, vc, idx, kr=xk[:, n - R:].contiguous(), vr=xv[:, n - R:].contiguous(),
                                    W=W, sink=sink, n_ctx=n, want_lse=True)
@@ -77,15 +78,17 @@ def test_config1_csa_fp32_end_to_end():
     cpu = lambda t: t.cpu().double().numpy()  # noqa: E731  (regenerate on the CPU)
     C = {nm: g_make(t.shape, seed, nm, f32, sc, "cpu").double().numpy()
          for nm, t, sc in (("k", xk, sd), ("v", xv, sd), ("z_k", zk, 0.5), ("z_v", zv, 0.5),
-                           ("k_idx", xi, si), ("z_idx", zi, 0.5), ("q", q, sd), ("q_idx", qi, si))}
+                           ("k_idx", xi, si), ("z_idx", zi, 0.5), ("q", q, sd), ("q_idx", qi, si),
+                           ("w_idx", wi, HI ** -0.5))}
     sink_c = g_make((H,), seed, "sink", f32, 1.0, "cpu").double().numpy()
     kc_c = round_to(oracle.compress(C["k"], C["z_k"], m), f32)
     vc_c = round_to(oracle.compress(C["v"], C["z_v"], m), f32)
     ki_c = round_to(oracle.compress(C["k_idx"], C["z_idx"], m), f32)
     assert max_abs(cpu(kc), kc_c) <= F32_TOL and max_abs(cpu(ki), ki_c) <= F32_TOL
-    idx_c, sc = oracle.index_topk(C["q_idx"], ki_c, m, k, n_ctx=n)
+    idx_c, sc = oracle.index_topk(C["q_idx"], ki_c, m, k, w=C["w_idx"], n_ctx=n)
     nvis = np.array([(n - T + i) // m for i in range(T)])
-    ties = check_topk_rows(idx.cpu().numpy()[0], idx_c[0], sc[0], C["q_idx"][0], ki_c[0], nvis, k)
+    ties = check_topk_rows(idx.cpu().numpy()[0], idx_c[0], sc[0], C["q_idx"][0], ki_c[0], nvis, k,
+                           w_c=C["w_idx"][0])
     assert ties == 0, "near-tie disagreements: %d" % ties
     o_c, l_c = oracle.sparse_attn(C["q"], kc_c, vc_c, idx_c, C["k"][:, n - R:], C["v"][:, n - R:], W,
                                   sink=sink_c, n_ctx=n)
@@ -111,12 +114,13 @@ def test_config2_csa_decode_128k():
         del x, z
     q = g_make((B, 1, H, d), seed, "q", BF, sd, dev)
     qi = g_make((B, 1, HI, dI), seed, "q_idx", BF, si, dev)
+    wi = g_make((B, 1, HI), seed, "w_idx", torch.float32, HI ** -0.5, dev)
     sink = g_make((H,), seed, "sink", torch.float32, 1.0, dev)
     kr = syn.rows((B, n, d), np.concatenate([seq_rows(b, n, n - W) for b in range(B)]), seed, syn.TID["k"],
                   dtype=BF, device=dev, scale=sd).reshape(B, W, d)
     vr = syn.rows((B, n, d), np.concatenate([seq_rows(b, n, n - W) for b in range(B)]), seed, syn.TID["v"],
                   dtype=BF, device=dev, scale=sd).reshape(B, W, d)
-    idx = csa.csa_index_topk(qi, caches["k_idx"], m, k, n_ctx=n)
+    idx = csa.csa_index_topk(qi, caches["k_idx"], m, k, w_idx=wi, n_ctx=n)
     out, lse = csa.csa_sparse_attn(q, caches["k"], caches["v"], idx, kr=kr, vr=vr, W=W, sink=sink, n_ctx=n,
                                    want_lse=True)
     torch.cuda.synchronize()
@@ -128,8 +132,10 @@ def test_config2_csa_decode_128k():
                                         m), BF)
         assert max_abs(to_np(caches["k_idx"][b:b + 1]), ki_c) <= BF16_TOL
         qi_c = c_rows((B, 1, HI, dI), np.arange(b * HI, (b + 1) * HI), seed, "q_idx", BF, si).reshape(1, 1, HI, dI)
-        idx_c, sc = oracle.index_topk(qi_c, ki_c, m, k, n_ctx=n)
-        ties = check_topk_rows(idx_g[b], idx_c[0], sc[0], qi_c[0], ki_c[0], np.array([(n - 1) // m]), k)
+        wi_c = c_rows((B, 1, HI), np.arange(b, b + 1), seed, "w_idx", torch.float32, HI ** -0.5).reshape(1, 1, HI)
+        idx_c, sc = oracle.index_topk(qi_c, ki_c, m, k, w=wi_c, n_ctx=n)
+        ties = check_topk_rows(idx_g[b], idx_c[0], sc[0], qi_c[0], ki_c[0], np.array([(n - 1) // m]), k,
+                               w_c=wi_c[0])
         assert ties <= 1
         kc_c = round_to(oracle.compress(c_rows((B, n, d), seq_rows(b, n), seed, "k", BF, sd).reshape(1, n, d),
                                         c_rows((B, n, d), seq_rows(b, n), seed, "z_k", BF, 0.5).reshape(1, n, d),
@@ -216,12 +222,14 @@ def test_config4_csa_prefill_chunk(where):
                  device=dev, scale=sd).reshape(1, Tq, H, d)
     qi = syn.rows((1, chunk, HI, dI), np.arange(q0 * HI, (q0 + Tq) * HI), seed, syn.TID["q_idx"], dtype=BF,
                   device=dev, scale=si).reshape(1, Tq, HI, dI)
+    wi = syn.rows((1, chunk, HI), np.arange(q0, q0 + Tq), seed, syn.TID["w_idx"], dtype=torch.float32,
+                  device=dev, scale=HI ** -0.5).reshape(1, Tq, HI)
     R = Tq + W - 1
     raw = np.arange(n_ctx - R, n_ctx)
     kr = syn.rows((1, n_full, d), raw, seed, syn.TID["kr"], dtype=BF, device=dev, scale=sd).reshape(1, R, d)
     vr = syn.rows((1, n_full, d), raw, seed, syn.TID["vr"], dtype=BF, device=dev, scale=sd).reshape(1, R, d)
     sink = g_make((H,), seed, "sink", torch.float32, 1.0, dev)
-    idx = csa.csa_index_topk(qi, ki, m, k, n_ctx=n_ctx)
+    idx = csa.csa_index_topk(qi, ki, m, k, w_idx=wi, n_ctx=n_ctx)
     out = csa.csa_sparse_attn(q, kc, vc, idx, kr=kr, vr=vr, W=W, sink=sink, n_ctx=n_ctx)
     torch.cuda.synchronize()
     idx_g = idx.cpu().numpy()[0]
@@ -230,9 +238,12 @@ def test_config4_csa_prefill_chunk(where):
     ki_c = g_make((1, L, dI), seed, "kic", BF, si, "cpu").double().numpy()
     qi_c = syn.rows((1, chunk, HI, dI), np.concatenate([np.arange((q0 + s) * HI, (q0 + s + 1) * HI) for s in sample]),
                     seed, syn.TID["q_idx"], dtype=BF, scale=si).double().numpy().reshape(1, len(sample), HI, dI)
+    wi_c = syn.rows((1, chunk, HI), np.array([q0 + s for s in sample]), seed, syn.TID["w_idx"],
+                    dtype=torch.float32, scale=HI ** -0.5).double().numpy().reshape(1, len(sample), HI)
     tpos = np.array([n_ctx - Tq + s for s in sample])
-    idx_c, sc = oracle.index_topk(qi_c, ki_c, m, k, tpos=tpos)
-    ties = check_topk_rows(idx_g[sample], idx_c[0], sc[0], qi_c[0], ki_c[0], np.minimum(tpos // m, L), k)
+    idx_c, sc = oracle.index_topk(qi_c, ki_c, m, k, w=wi_c, tpos=tpos)
+    ties = check_topk_rows(idx_g[sample], idx_c[0], sc[0], qi_c[0], ki_c[0], np.minimum(tpos // m, L), k,
+                           w_c=wi_c[0])
     assert ties <= 1
     same = [i for i, s in enumerate(sample) if np.array_equal(idx_g[s], idx_c[0, i])]
     assert len(same) >= len(sample) - 1
@@ -287,9 +298,12 @@ def test_config5_stack_step_sampled():
             ki_c = ki_c.reshape(1, L, st.dI)
             qi_c = c_rows((st.B, 1, st.HI, st.dI), np.arange(b * st.HI, (b + 1) * st.HI), SEED, "q_idx", bf, si,
                           layer=li).reshape(1, 1, st.HI, st.dI)
-            idx_c, sc = oracle.index_topk(qi_c, ki_c, m, st.k, n_ctx=st.n_ctx)
+            wi_c = c_rows((st.B, 1, st.HI), np.arange(b, b + 1), SEED, "w_idx", torch.float32, st.HI ** -0.5,
+                          layer=li).reshape(1, 1, st.HI)
+            idx_c, sc = oracle.index_topk(qi_c, ki_c, m, st.k, w=wi_c, n_ctx=st.n_ctx)
             got_idx = lay["idx"].cpu().numpy()[b]
-            ties = check_topk_rows(got_idx, idx_c[0], sc[0], qi_c[0], ki_c[0], np.array([st.nv_csa]), st.k)
+            ties = check_topk_rows(got_idx, idx_c[0], sc[0], qi_c[0], ki_c[0], np.array([st.nv_csa]), st.k,
+                                   w_c=wi_c[0])
             assert ties <= 1
             sel = idx_c[0, 0][idx_c[0, 0] >= 0]
             kc_c = np.zeros((1, L, st.d))
