@@ -266,12 +266,13 @@ def counter_traffic(kernel_src, per_launch_units):
     return float(m_b.group(1)) * per_launch_units / int(m_u.group(1))
 
 
-def cpu_baseline(st: Stack, sample: int):
+def cpu_baseline(st: Stack, sample: int, min_seconds: float = 10.0, max_rounds: int = 6):
     """Time the CPU oracle on `sample` sequences of the same decode step.
 
     Inputs are regenerated on the CPU from the same seeds (not timed); the
     oracle calls (compression of the new entries, indexer + top-k, sparse
-    attention, dense attention) are timed."""
+    attention, dense attention) are timed.  The step is repeated until at
+    least min_seconds of oracle time (at most max_rounds rounds)."""
     import numpy as np
 
     import oracle
@@ -288,6 +289,24 @@ def cpu_baseline(st: Stack, sample: int):
                         layer=li).double().numpy().reshape(-1, D)
 
     sub = Stack(B=S, n_ctx=st.n_ctx, layers=st.layers)
+    rounds = 0
+    while rounds < max_rounds and (rounds == 0 or total < min_seconds):
+        rounds += 1
+        _oracle_step(st, sub, S, full, sd, si)
+        total += _oracle_step.last
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": S * rounds / total, "unit": "queries/s", "cores": min(S, threads), "kind": "oracle",
+            "sample": "%d of %d sequences, %d round(s) of one decode step through all %d layers "
+                      "(%.1f s of oracle time)" % (S, st.B, rounds, st.layers, total)}
+
+
+def _oracle_step(st, sub, S, full, sd, si):
+    """One decode step of the oracle for S sequences; sets _oracle_step.last
+    to the oracle time in seconds (input regeneration excluded)."""
+    import numpy as np
+
+    import oracle
+    total = 0.0
     for li, kind in enumerate(st.kinds()):
         L = st.L_csa if kind == "csa" else st.L_hca
         seq_rows = lambda b, n: np.arange(b * n, (b + 1) * n)  # noqa: E731
@@ -343,10 +362,7 @@ def cpu_baseline(st: Stack, sample: int):
             oracle.compress(raws[2], raws[3], m, n=st.n_ctx, p0=p0, e0=st.hca_new, e1=st.hca_new + 1)
             oracle.dense_attn(q, kc, vc, m, kr, vr, st.W, sink=sink, n_ctx=st.n_ctx)
             total += time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": S / total, "unit": "queries/s", "cores": min(S, threads), "kind": "oracle",
-            "sample": "%d of %d sequences, one decode step through all %d layers (%.1f s of oracle time)"
-                      % (S, st.B, st.layers, total)}
+    _oracle_step.last = total
 
 
 def main():
@@ -356,7 +372,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--batch", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=12)
+    ap.add_argument("--cpu-sample", type=int, default=16)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the oracle step until at least this much oracle time")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run a plain device copy of BYTES bytes 3 times (counter calibration)")
     args = ap.parse_args()
@@ -418,7 +436,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(st, args.cpu_sample)
+        cpu = cpu_baseline(st, args.cpu_sample, args.cpu_seconds)
 
     line = {
         "metric": "CSA/HCA decode queries/s at 1M ctx + achieved HBM GB/s (% peak)",
