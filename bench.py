@@ -11,15 +11,17 @@ layers' compressed caches are resident in HBM (about 2.4 GB per sequence).
 One step decodes the token at position t = n_ctx - 1 of every sequence
 through all 8 layers.  Per CSA layer: csa_compress writes the entry whose
 block the new token completes (K, V and index keys, two-path), then the
-indexer scores every visible entry, top-k selects 1024 and csa_sparse_attn
-attends over them plus the window.  Per HCA layer: hca_compress refreshes the
+indexer scores every visible entry and keeps the top 1024 (csa_index_topk:
+one scan kernel that also selects each part's candidates, then a merge
+kernel), and csa_sparse_attn attends over them plus the window.  Per HCA layer: hca_compress refreshes the
 newest complete 128-token entry (K and V) and hca_dense_attn attends over all
 7812 visible entries plus the window.
 
 Metric: queries/s, a query being one token of one sequence through the whole
 8-layer stack (B queries per step), plus achieved HBM GB/s of the step and
-the roofline of the dominant kernel (the indexer scan), timed with HIP events
-on the stream the kernels run on.  The CPU oracle is timed on a bounded
+the roofline of the dominant call (csa_index_topk: its scan kernel streams
+the index keys and takes about nine tenths of the call), timed with HIP
+events on the stream the kernels run on.  The CPU oracle is timed on a bounded
 sample of the same step (a few sequences) as a reported baseline.
 
 Usage: python bench.py [--steps K] [--warmup W] [--batch B] [--no-cpu-baseline]
@@ -72,14 +74,16 @@ class Stack:
 
     # ---- algorithmic bytes (what the method must move), per query ----------
     def index_bytes(self):
-        return self.nv_csa * self.dI * 2 + self.HI * self.dI * 2
+        """csa_index_topk per query: the visible indexer keys, the query's
+        index heads and head weights, the selected indices written."""
+        return self.nv_csa * self.dI * 2 + self.HI * self.dI * 2 + self.HI * 4 + self.k * 4
 
     def csa_bytes(self):
         b = self.index_bytes()
         b += self.k * self.d * 2 * 2            # gathered compressed K and V rows
         b += self.W * self.d * 2 * 2            # raw window K and V
         b += 2 * self.H * self.d * 2            # q and out
-        b += self.k * 4                         # selected indices
+        b += self.k * 4                         # selected indices, read by the attention
         m = self.m_csa
         b += 4 * 2 * m * (2 * self.d + self.dI) * 2 // 2  # compress: x/z, A and B paths, K V I
         b += (2 * self.d + self.dI) * 2         # new entries
@@ -145,9 +149,8 @@ class GpuState:
                         raw_rows(st, "zb_" + s, li, p0, 2 * m, D, device, 0.5))
                 lay["p0"] = p0
                 lay["idx"] = torch.empty((B, 1, st.k), dtype=torch.int32, device=device)
-                lay["score"] = torch.empty((B, 1, L), dtype=torch.float32, device=device)
-                lay["topk_ws"] = torch.empty(max(16, csa.csa_topk_select_workspace(B, 1, L, st.k)),
-                                             dtype=torch.uint8, device=device)
+                lay["itk_ws"] = torch.empty(max(16, csa.csa_index_topk_workspace(B, 1, L, st.k)),
+                                            dtype=torch.uint8, device=device)
                 nb = csa.csa_sparse_attn_workspace(B, 1, H, d, st.k, st.W, csa.CSA_BF16)
             else:
                 m = st.m_hca
@@ -214,12 +217,10 @@ class GpuState:
         for lay, done in zip(self.layers, joins):
             if lay["kind"] == "csa":
                 m = st.m_csa
-                mark("index_score")
-                csa.csa_index_score(lay["qi"], lay["ki"], m, w_idx=lay["wi"], n_ctx=st.n_ctx, out=lay["score"])
-                mark("index_score_end")
-                mark("topk_select")
-                csa.csa_topk_select(lay["score"], m, st.k, n_ctx=st.n_ctx, idx=lay["idx"], ws=lay["topk_ws"])
-                mark("topk_select_end")
+                mark("index_topk")
+                csa.csa_index_topk(lay["qi"], lay["ki"], m, st.k, w_idx=lay["wi"], n_ctx=st.n_ctx, idx=lay["idx"],
+                                   ws=lay["itk_ws"])
+                mark("index_topk_end")
                 mark("csa_sparse_attn")
                 csa.csa_sparse_attn(lay["q"], lay["kc"], lay["vc"], lay["idx"], kr=lay["kr"], vr=lay["vr"],
                                     W=st.W, sink=lay["sink"], n_ctx=st.n_ctx, out=lay["out"], ws=lay["ws"])
@@ -246,15 +247,23 @@ def event_means_ms(ev):
     return res
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+INDEX_TOPK_SOURCES = [os.path.join(ROOT, "compressed_sparse_kv_compress_amd", "csrc", f)
+                      for f in ("index.hip", "topk.hip", "select.hpp", "common.hpp")]
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def counter_traffic(kernel_src, per_launch_units):
-    """HBM bytes per launch of the indexer scan from the committed rocprofv3
-    counter summary, or None when it is missing or the kernel source changed."""
-    path = os.path.join(ROOT, "profiles", "index_score_stack8_b16_counters.txt")
+    """HBM bytes per csa_index_topk call (its two kernels) from the committed
+    rocprofv3 counter summary, or None when it is missing or the kernels'
+    sources changed since."""
+    path = os.path.join(ROOT, "profiles", "index_topk_stack8_b16_counters.txt")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
@@ -266,20 +275,18 @@ def counter_traffic(kernel_src, per_launch_units):
     return float(m_b.group(1)) * per_launch_units / int(m_u.group(1))
 
 
-def cpu_baseline(st: Stack, sample: int, min_seconds: float = 10.0, max_rounds: int = 6):
+def cpu_baseline(st: Stack, sample: int, min_seconds: float = 10.0, max_reps: int = 8):
     """Time the CPU oracle on `sample` sequences of the same decode step.
 
-    Inputs are regenerated on the CPU from the same seeds (not timed); the
-    oracle calls (compression of the new entries, indexer + top-k, sparse
-    attention, dense attention) are timed.  The step is repeated until at
-    least min_seconds of oracle time (at most max_rounds rounds)."""
-    import numpy as np
-
-    import oracle
+    Inputs are regenerated on the CPU from the same seeds, layer by layer (not
+    timed); the oracle calls of a layer (compression of the new entries,
+    indexer + top-k and sparse attention, or dense attention) are timed and
+    repeated on the same inputs until the layer has had its share of
+    min_seconds (at most max_reps times).  The step time is the sum over
+    layers of the mean time per repetition."""
     bf = torch.bfloat16
     S = min(sample, st.B)
     sd, si = st.d ** -0.5, st.dI ** -0.5
-    total = 0.0
 
     def full(shape, name, scale, li, rows=None, dtype=bf):
         D = shape[-1]
@@ -289,48 +296,56 @@ def cpu_baseline(st: Stack, sample: int, min_seconds: float = 10.0, max_rounds: 
                         layer=li).double().numpy().reshape(-1, D)
 
     sub = Stack(B=S, n_ctx=st.n_ctx, layers=st.layers)
-    rounds = 0
-    while rounds < max_rounds and (rounds == 0 or total < min_seconds):
-        rounds += 1
-        _oracle_step(st, sub, S, full, sd, si)
-        total += _oracle_step.last
+    per_layer = min_seconds / st.layers
+    step_s, total, reps_all = 0.0, 0.0, []
+    for li, kind in enumerate(st.kinds()):
+        t_layer, reps = _oracle_layer(st, sub, S, full, sd, si, li, kind, per_layer, max_reps)
+        step_s += t_layer / reps
+        total += t_layer
+        reps_all.append(reps)
+        print("# cpu oracle: layer %d (%s) %.2f s over %d repetition(s)" % (li, kind, t_layer, reps),
+              file=sys.stderr, flush=True)
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": S * rounds / total, "unit": "queries/s", "cores": min(S, threads), "kind": "oracle",
-            "sample": "%d of %d sequences, %d round(s) of one decode step through all %d layers "
-                      "(%.1f s of oracle time)" % (S, st.B, rounds, st.layers, total)}
+    return {"value": S / step_s, "unit": "queries/s", "cores": min(S, threads), "kind": "oracle",
+            "sample": "%d of %d sequences, one decode step through all %d layers, each layer's oracle calls "
+                      "repeated %s times on the same inputs (%.1f s of oracle time)"
+                      % (S, st.B, st.layers, "/".join(map(str, reps_all)), total)}
 
 
-def _oracle_step(st, sub, S, full, sd, si):
-    """One decode step of the oracle for S sequences; sets _oracle_step.last
-    to the oracle time in seconds (input regeneration excluded)."""
+def _oracle_layer(st, sub, S, full, sd, si, li, kind, min_seconds, max_reps):
+    """Oracle calls of one layer of the decode step for S sequences, repeated
+    until min_seconds (at most max_reps times); returns (seconds, repetitions),
+    input regeneration excluded."""
     import numpy as np
 
     import oracle
-    total = 0.0
-    for li, kind in enumerate(st.kinds()):
-        L = st.L_csa if kind == "csa" else st.L_hca
-        seq_rows = lambda b, n: np.arange(b * n, (b + 1) * n)  # noqa: E731
-        q = np.stack([full((st.B, 1, st.H, st.d), "q", sd, li, rows=np.arange(b * st.H, (b + 1) * st.H))
-                      for b in range(S)]).reshape(S, 1, st.H, st.d)
-        sink = full((st.H,), "sink", 1.0, li, dtype=torch.float32)
-        kr = np.stack([raw_rows(sub, "kr", li, st.n_ctx - st.W, st.W, st.d, "cpu", sd)[b].double().numpy()
-                       for b in range(S)])
-        vr = np.stack([raw_rows(sub, "vr", li, st.n_ctx - st.W, st.W, st.d, "cpu", sd)[b].double().numpy()
-                       for b in range(S)])
-        if kind == "csa":
-            m = st.m_csa
-            p0 = (st.csa_new - 1) * m
-            raws = {}
-            for s, D, sc in (("k", st.d, sd), ("v", st.d, sd), ("idx", st.dI, si)):
-                xa = "k" if s == "k" else ("v" if s == "v" else "k_idx")
-                raws[s] = [raw_rows(sub, nm, li, p0, 2 * m, D, "cpu", scl).double().numpy()
-                           for nm, scl in ((xa, sc), ("z_" + s, 0.5), ("xb_" + s, sc), ("zb_" + s, 0.5))]
-            ki = np.stack([full((st.B, L, st.dI), "kic", si, li, rows=seq_rows(b, L)) for b in range(S)])
-            qi = np.stack([full((st.B, 1, st.HI, st.dI), "q_idx", si, li,
-                                rows=np.arange(b * st.HI, (b + 1) * st.HI)) for b in range(S)])
-            qi = qi.reshape(S, 1, st.HI, st.dI)
-            wi = np.stack([full((st.B, 1, st.HI), "w_idx", st.HI ** -0.5, li, dtype=torch.float32,
-                                rows=np.arange(b, b + 1)) for b in range(S)]).reshape(S, 1, st.HI)
+    L = st.L_csa if kind == "csa" else st.L_hca
+    seq_rows = lambda b, n: np.arange(b * n, (b + 1) * n)  # noqa: E731
+    q = np.stack([full((st.B, 1, st.H, st.d), "q", sd, li, rows=np.arange(b * st.H, (b + 1) * st.H))
+                  for b in range(S)]).reshape(S, 1, st.H, st.d)
+    sink = full((st.H,), "sink", 1.0, li, dtype=torch.float32)
+    kr = np.stack([raw_rows(sub, "kr", li, st.n_ctx - st.W, st.W, st.d, "cpu", sd)[b].double().numpy()
+                   for b in range(S)])
+    vr = np.stack([raw_rows(sub, "vr", li, st.n_ctx - st.W, st.W, st.d, "cpu", sd)[b].double().numpy()
+                   for b in range(S)])
+    total, reps = 0.0, 0
+    if kind == "csa":
+        m = st.m_csa
+        p0 = (st.csa_new - 1) * m
+        raws = {}
+        for s, D, sc in (("k", st.d, sd), ("v", st.d, sd), ("idx", st.dI, si)):
+            xa = "k" if s == "k" else ("v" if s == "v" else "k_idx")
+            raws[s] = [raw_rows(sub, nm, li, p0, 2 * m, D, "cpu", scl).double().numpy()
+                       for nm, scl in ((xa, sc), ("z_" + s, 0.5), ("xb_" + s, sc), ("zb_" + s, 0.5))]
+        ki = np.stack([full((st.B, L, st.dI), "kic", si, li, rows=seq_rows(b, L)) for b in range(S)])
+        qi = np.stack([full((st.B, 1, st.HI, st.dI), "q_idx", si, li,
+                            rows=np.arange(b * st.HI, (b + 1) * st.HI)) for b in range(S)])
+        qi = qi.reshape(S, 1, st.HI, st.dI)
+        wi = np.stack([full((st.B, 1, st.HI), "w_idx", st.HI ** -0.5, li, dtype=torch.float32,
+                            rows=np.arange(b, b + 1)) for b in range(S)]).reshape(S, 1, st.HI)
+        kc = vc = loc = None
+        while reps < max_reps and (reps == 0 or total < min_seconds):
+            reps += 1
             t0 = time.perf_counter()
             for s in ("k", "v", "idx"):
                 xa, za, xb, zb = raws[s]
@@ -338,31 +353,33 @@ def _oracle_step(st, sub, S, full, sd, si):
                                 e1=st.csa_new + 1)
             idx, _ = oracle.index_topk(qi, ki, m, st.k, w=wi, n_ctx=st.n_ctx)
             total += time.perf_counter() - t0
-            # gather only the selected rows of the compressed K/V caches
-            kc = np.zeros((S, st.k, st.d))
-            vc = np.zeros((S, st.k, st.d))
-            loc = np.full_like(idx, -1)
-            for b in range(S):
-                sel = idx[b, 0][idx[b, 0] >= 0]
-                kc[b, :len(sel)] = full((st.B, L, st.d), "kc", sd, li, rows=b * L + sel)
-                vc[b, :len(sel)] = full((st.B, L, st.d), "vc", sd, li, rows=b * L + sel)
-                loc[b, 0, :len(sel)] = np.arange(len(sel))
+            if kc is None:  # gather only the selected rows of the compressed K/V caches (not timed)
+                kc = np.zeros((S, st.k, st.d))
+                vc = np.zeros((S, st.k, st.d))
+                loc = np.full_like(idx, -1)
+                for b in range(S):
+                    sel = idx[b, 0][idx[b, 0] >= 0]
+                    kc[b, :len(sel)] = full((st.B, L, st.d), "kc", sd, li, rows=b * L + sel)
+                    vc[b, :len(sel)] = full((st.B, L, st.d), "vc", sd, li, rows=b * L + sel)
+                    loc[b, 0, :len(sel)] = np.arange(len(sel))
             t0 = time.perf_counter()
             oracle.sparse_attn(q, kc, vc, loc, kr, vr, st.W, sink=sink, n_ctx=st.n_ctx)
             total += time.perf_counter() - t0
-        else:
-            m = st.m_hca
-            p0 = st.hca_new * m
-            raws = [raw_rows(sub, nm, li, p0, m, st.d, "cpu", scl).double().numpy()
-                    for nm, scl in (("k", sd), ("z_k", 0.5), ("v", sd), ("z_v", 0.5))]
-            kc = np.stack([full((st.B, L, st.d), "kc", sd, li, rows=seq_rows(b, L)) for b in range(S)])
-            vc = np.stack([full((st.B, L, st.d), "vc", sd, li, rows=seq_rows(b, L)) for b in range(S)])
+    else:
+        m = st.m_hca
+        p0 = st.hca_new * m
+        raws = [raw_rows(sub, nm, li, p0, m, st.d, "cpu", scl).double().numpy()
+                for nm, scl in (("k", sd), ("z_k", 0.5), ("v", sd), ("z_v", 0.5))]
+        kc = np.stack([full((st.B, L, st.d), "kc", sd, li, rows=seq_rows(b, L)) for b in range(S)])
+        vc = np.stack([full((st.B, L, st.d), "vc", sd, li, rows=seq_rows(b, L)) for b in range(S)])
+        while reps < max_reps and (reps == 0 or total < min_seconds):
+            reps += 1
             t0 = time.perf_counter()
             oracle.compress(raws[0], raws[1], m, n=st.n_ctx, p0=p0, e0=st.hca_new, e1=st.hca_new + 1)
             oracle.compress(raws[2], raws[3], m, n=st.n_ctx, p0=p0, e0=st.hca_new, e1=st.hca_new + 1)
             oracle.dense_attn(q, kc, vc, m, kr, vr, st.W, sink=sink, n_ctx=st.n_ctx)
             total += time.perf_counter() - t0
-    _oracle_step.last = total
+    return total, reps
 
 
 def main():
@@ -372,7 +389,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--batch", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=16)
+    ap.add_argument("--cpu-sample", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle step until at least this much oracle time")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -403,8 +420,8 @@ def main():
     torch.cuda.synchronize()
     print("# warmup done", file=sys.stderr, flush=True)
 
-    # Timed region: K steps; HIP events bracket only the indexer scan (the
-    # dominant kernel) on the stream it runs on.
+    # Timed region: K steps; HIP events bracket only the csa_index_topk calls
+    # (the dominant call) on the stream they run on.
     ev = {}
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -412,12 +429,12 @@ def main():
     wall0 = time.perf_counter()
     start.record()
     for _ in range(args.steps):
-        state.step(ev, only=("index_score",))
+        state.step(ev, only=("index_topk",))
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = start.elapsed_time(stop) / args.steps
-    idx_ms = event_means_ms(ev)["index_score"]
+    idx_ms = event_means_ms(ev)["index_topk"]
     print("# timed %d steps: %.3f ms/step (wall %.3f ms/step)" % (args.steps, ms_step, 1e3 * wall / args.steps),
           file=sys.stderr, flush=True)
     # Untimed breakdown pass: every call bracketed by events.
@@ -431,8 +448,7 @@ def main():
     step_gbps = st.step_bytes() / (ms_step * 1e-3) / 1e9
     idx_bytes = st.index_bytes() * st.B
     idx_gbps = idx_bytes / (idx_ms * 1e-3) / 1e9
-    traffic = counter_traffic(os.path.join(ROOT, "compressed_sparse_kv_compress_amd", "csrc", "index.hip"),
-                              st.B)
+    traffic = counter_traffic(INDEX_TOPK_SOURCES, st.B)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -460,7 +476,8 @@ def main():
         },
         "hbm": {"algorithmic_bytes_per_step": st.step_bytes(), "achieved_GBps": step_gbps,
                 "frac_of_peak": step_gbps / HBM_PEAK_GBPS},
-        "roofline": {"kernel": "index_score (csa_index_score)", "bound": "hbm", "achieved": idx_gbps,
+        "roofline": {"kernel": "csa_index_topk (index_score_stream<4,true,true> then topk_merge_kernel)",
+                     "bound": "hbm", "achieved": idx_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": idx_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "avg_launch_ms": idx_ms,
                      "algorithmic_bytes_per_launch": idx_bytes},

@@ -242,8 +242,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
   const int64_t t = a.n_ctx - a.T + bt % a.T;
   const RowMap rm = row_map(a, SPARSE, t);
   const int64_t n_rows = rm.n_cmp + rm.n_win;
-  int64_t per = (n_rows + nsplit - 1) / nsplit;
-  per = (per + C::ROWS - 1) / C::ROWS * C::ROWS;
+  const int64_t per = (n_rows + nsplit - 1) / nsplit;  // rows per split (the last stage may be partial)
   const int64_t r_begin = split * per;
   const int64_t r_end = r_begin + per < n_rows ? r_begin + per : n_rows;
 

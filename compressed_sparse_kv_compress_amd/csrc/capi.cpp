@@ -202,7 +202,9 @@ static size_t index_topk_row_bytes(int64_t L, int64_t k) {
 
 size_t csa_index_topk_workspace(int64_t B, int64_t T, int64_t L, int64_t k) {
   if (B <= 0 || T <= 0 || k <= 0) return 0;
-  return static_cast<size_t>(B) * T * index_topk_row_bytes(L, k);
+  const size_t chunked = static_cast<size_t>(B) * T * index_topk_row_bytes(L, k);
+  const size_t fused = L > 0 ? csa::index_topk_fused_ws_bytes(B * T, L, k) : 0;
+  return chunked > fused ? chunked : fused;
 }
 
 csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int64_t B,
@@ -217,6 +219,14 @@ csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k
   OPT_PTR(out_score);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t rows = B * T;
+  if (ws != nullptr && L > 0 && csa::index_topk_fusable(rows, L, H_I, d_I, k, dtype == CSA_BF16) &&
+      ws_bytes >= csa::index_topk_fused_ws_bytes(rows, L, k)) {
+    // The scan's workgroups keep their parts' candidates; no score matrix.
+    if (!aligned16(ws)) return fail(CSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+    csa::IndexScoreArgs a{q_idx, w_idx, k_idx, nullptr, L, 0, rows, B, T, n_ctx, L, H_I, d_I, m};
+    csa::TopkArgs t{nullptr, L, 0, rows, T, n_ctx, L, m, k, idx, out_score};
+    return hip_status(csa::launch_index_topk_fused(a, t, ws, s), "fused index/top-k launch");
+  }
   const size_t per_row = index_topk_row_bytes(L, k);
   if (ws == nullptr || ws_bytes < per_row)
     return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes is below the one-query minimum %zu", ws_bytes, per_row);

@@ -22,6 +22,7 @@
 // workgroup per CU, so every wavefront streams megabytes with one prologue.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace csa {
 namespace {
@@ -100,14 +101,80 @@ __device__ __forceinline__ float group_sum4(float x) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// Fused top-k, part stage: the workgroup's part of the row (nkv visible keys
+// starting at key kb, scores in LDS in the tile layout of the scan) keeps its
+// top-min(cap, nkv) entries, written as index-ordered (score, index) pairs in
+// candidate slot `slot`, with their count.  Any entry of the row's top-k is
+// in its part's top-k (fewer entries beat it inside the part than in the whole
+// row), ties included.  The tile ring is free at this point and holds the
+// selection's state.
+using PartSel = sel::Filter<64 * kWaves, 64, 16>;
+constexpr int kPartKeys = 64 * kWaves * 64;  // 16384 >= 4 * kMaxKeysPerWave
+constexpr int kCandStage = 2048;             // largest cap staged in LDS
+static_assert(4 * kMaxKeysPerWave <= kPartKeys, "a part fits the selection tile");
+static_assert(sizeof(PartSel::Shared) + kCandStage * 4 <= kWaves * kDepth * kTileBytes, "selection state fits the ring");
+
+__device__ __forceinline__ float part_score(const float (*sbuf)[kMaxTiles * kTileKeys], int o) {
+  const int T = o / kTileKeys;
+  return sbuf[T % kWaves][(T / kWaves) * kTileKeys + o % kTileKeys];
+}
+
+__device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t slot, int64_t kb, int nkv,
+                                            const float (*sbuf)[kMaxTiles * kTileKeys], uint8_t* scratch) {
+  const int tid = threadIdx.x;
+  const int cap = static_cast<int>(co.cap);
+  float* ov = co.cval + slot * co.cap;
+  int32_t* oi = co.cidx + slot * co.cap;
+  if (nkv <= cap) {  // the whole part is kept
+    for (int o = tid; o < nkv; o += 64 * kWaves) {
+      ov[o] = part_score(sbuf, o);
+      oi[o] = static_cast<int32_t>(kb + o);
+    }
+    if (tid == 0) co.ccnt[slot] = nkv;
+    return;
+  }
+  PartSel::Shared& ss = *reinterpret_cast<PartSel::Shared*>(scratch);
+  int32_t* si = reinterpret_cast<int32_t*>(scratch + sizeof(PartSel::Shared));
+  PartSel::zero(ss);
+  // Thread t holds entries 64t .. 64t+63 of the part: tiles 4t .. 4t+3, i.e.
+  // tile t of each wavefront's list, 16 consecutive scores each; entries past
+  // the visible ones are NaN (never selected).
+  float x[64];
+  const int o0 = tid * 64;
+  const int tl = tid < kMaxTiles ? tid : kMaxTiles - 1;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&sbuf[w][tl * kTileKeys + 4 * q]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[w * 16 + 4 * q + e] = v[e];
+    }
+#pragma unroll
+  for (int j = 0; j < 64; ++j) x[j] = o0 + j < nkv ? x[j] : __builtin_nanf("");
+  float vmin, vmax;
+  PartSel::block_range(x, ss, &vmin, &vmax);
+  PartSel::run(
+      x, [&](int j) { return static_cast<uint32_t>(o0 + j); }, static_cast<uint32_t>(nkv),
+      static_cast<uint32_t>(cap), vmin, vmax, ss, [&](uint32_t pos, float, uint32_t e) { si[pos] = static_cast<int32_t>(e); },
+      [&](int j, uint32_t pos) { si[pos] = o0 + j; });
+  for (int i = tid; i < cap; i += 64 * kWaves) {
+    const int o = si[i];
+    ov[i] = part_score(sbuf, o);
+    oi[i] = static_cast<int32_t>(kb + o);
+  }
+  if (tid == 0) co.ccnt[slot] = cap;
+}
+
 // d_I = 128 (KS = 4), MB = H_I / 16 head blocks.  Workgroup (row, part)
 // scores keys [part * 4 * per_wave, +4 * per_wave); its wavefront w takes
 // tiles w, w+4, w+8, ... so that the four stream through adjacent memory.
 // Scores collect in LDS and leave in one coalesced pass at the end, so the
 // loop issues no stores (their completions would share the load counter the
 // ring waits on).
-template <int MB, bool HAS_W>
-__global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, int64_t parts, int64_t per_wave) {
+template <int MB, bool HAS_W, bool TOPK>
+__global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, int64_t parts, int64_t per_wave,
+                                                             IndexCandidates co) {
   constexpr int HI = 16 * MB;
   constexpr int DI = 128;
   constexpr int KS = 4;
@@ -224,11 +291,16 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
     if (g == 0) sb[it * kTileKeys + c16] = s < nv ? tot : -INFINITY;
   }
 
+  __syncthreads();
+  if constexpr (TOPK) {
+    part_select(co, lrow * parts + part, kb, ntiles > 0 ? static_cast<int>(kv - kb) : 0, sbuf,
+                &ring[0][0][0]);
+    return;
+  }
   // Write the workgroup's scores [kb, ke) in key order; keys past the visible
   // ones (none in decode) are -inf.  Tile T of the range is tile T/4 of wave
   // T%4; four consecutive keys share a tile, so they move as one 16-byte
   // piece (one LDS read, one store when the row is 16-byte aligned).
-  __syncthreads();
   const int nk = static_cast<int>(ke - kb);
   float* dst = srow + kb;
   const bool aligned = (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
@@ -338,36 +410,53 @@ __global__ __launch_bounds__(256) void index_score_f32(IndexScoreArgs a, int64_t
 
 }  // namespace
 
+void index_plan(int64_t nrows, int64_t L, int64_t* parts_out, int64_t* per_wave_out) {
+  // About one workgroup per CU in one round; every wavefront streams
+  // kMinKeysPerWave .. kMaxKeysPerWave keys.
+  const int64_t target = 256;
+  int64_t parts = (target + nrows - 1) / nrows;
+  int64_t per_wave = (L + kWaves * parts - 1) / (kWaves * parts);
+  per_wave = (per_wave + kTileKeys - 1) / kTileKeys * kTileKeys;
+  if (per_wave < kMinKeysPerWave) per_wave = kMinKeysPerWave;
+  if (per_wave > kMaxKeysPerWave) per_wave = kMaxKeysPerWave;
+  *parts_out = (L + kWaves * per_wave - 1) / (kWaves * per_wave);
+  *per_wave_out = per_wave;
+}
+
+namespace {
+
+template <bool TOPK>
+hipError_t launch_stream(const IndexScoreArgs& a, const IndexCandidates& co, hipStream_t s) {
+  int64_t parts, per_wave;
+  index_plan(a.nrows, a.L, &parts, &per_wave);
+  const dim3 grid(static_cast<uint32_t>(a.nrows * parts));
+  const int mb = static_cast<int>(a.HI / 16);
+  const bool w = a.w != nullptr;
+#define CSA_INDEX_LAUNCH(MB_)                                                                                   \
+  case MB_:                                                                                                     \
+    if (w) hipLaunchKernelGGL((index_score_stream<MB_, true, TOPK>), grid, dim3(256), 0, s, a, parts, per_wave, co); \
+    else hipLaunchKernelGGL((index_score_stream<MB_, false, TOPK>), grid, dim3(256), 0, s, a, parts, per_wave, co); \
+    break;
+  switch (mb) {
+    CSA_INDEX_LAUNCH(1)
+    CSA_INDEX_LAUNCH(2)
+    CSA_INDEX_LAUNCH(4)
+    CSA_INDEX_LAUNCH(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef CSA_INDEX_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_index_score(const IndexScoreArgs& a, bool bf16, hipStream_t s) {
   if (a.nrows == 0 || a.L == 0) return hipSuccess;
   if (bf16) {
     const int mb = static_cast<int>(a.HI / 16), ks = static_cast<int>(a.dI / 32);
     const bool w = a.w != nullptr;
-    if (ks == 4) {
-      // About one workgroup per CU in one round; every wavefront streams
-      // kMinKeysPerWave .. kMaxKeysPerWave keys.
-      const int64_t target = 256;
-      int64_t parts = (target + a.nrows - 1) / a.nrows;
-      int64_t per_wave = (a.L + kWaves * parts - 1) / (kWaves * parts);
-      per_wave = (per_wave + kTileKeys - 1) / kTileKeys * kTileKeys;
-      if (per_wave < kMinKeysPerWave) per_wave = kMinKeysPerWave;
-      if (per_wave > kMaxKeysPerWave) per_wave = kMaxKeysPerWave;
-      parts = (a.L + kWaves * per_wave - 1) / (kWaves * per_wave);
-      const dim3 grid(static_cast<uint32_t>(a.nrows * parts));
-#define CSA_INDEX_LAUNCH(MB_)                                                                          \
-  case MB_:                                                                                            \
-    if (w) hipLaunchKernelGGL((index_score_stream<MB_, true>), grid, dim3(256), 0, s, a, parts, per_wave); \
-    else hipLaunchKernelGGL((index_score_stream<MB_, false>), grid, dim3(256), 0, s, a, parts, per_wave); \
-    break;
-      switch (mb) {
-        CSA_INDEX_LAUNCH(1)
-        CSA_INDEX_LAUNCH(2)
-        CSA_INDEX_LAUNCH(4)
-        CSA_INDEX_LAUNCH(8)
-        default: return hipErrorInvalidValue;
-      }
-#undef CSA_INDEX_LAUNCH
-    } else if (ks == 2) {
+    if (ks == 4) return launch_stream<false>(a, IndexCandidates{}, s);
+    if (ks == 2) {
       const int64_t parts = (a.L + kDirectKeysPerWg - 1) / kDirectKeysPerWg;
       const dim3 grid(static_cast<uint32_t>(a.nrows * parts));
 #define CSA_INDEX_LAUNCH(MB_)                                                                             \
@@ -381,16 +470,43 @@ hipError_t launch_index_score(const IndexScoreArgs& a, bool bf16, hipStream_t s)
         default: return hipErrorInvalidValue;
       }
 #undef CSA_INDEX_LAUNCH
-    } else {
-      return hipErrorInvalidValue;
+      return hipGetLastError();
     }
-  } else {
-    const int64_t parts = (a.L + 255) / 256;
-    const size_t lds = static_cast<size_t>(a.HI * a.dI) * sizeof(float);
-    hipLaunchKernelGGL(index_score_f32, dim3(static_cast<uint32_t>(a.nrows * parts)), dim3(256), lds, s,
-                       a, parts);
+    return hipErrorInvalidValue;
   }
+  const int64_t parts = (a.L + 255) / 256;
+  const size_t lds = static_cast<size_t>(a.HI * a.dI) * sizeof(float);
+  hipLaunchKernelGGL(index_score_f32, dim3(static_cast<uint32_t>(a.nrows * parts)), dim3(256), lds, s, a, parts);
   return hipGetLastError();
+}
+
+bool index_topk_fusable(int64_t nrows, int64_t L, int64_t HI, int64_t dI, int64_t k, bool bf16) {
+  if (!bf16 || dI != 128 || nrows <= 0 || L <= 0 || k < 1 || k > kCandStage) return false;
+  if (!(HI == 16 || HI == 32 || HI == 64 || HI == 128)) return false;
+  int64_t parts, per_wave;
+  index_plan(nrows, L, &parts, &per_wave);
+  return parts <= 256 && parts * k <= 16384;
+}
+
+size_t index_topk_fused_ws_bytes(int64_t nrows, int64_t L, int64_t k) {
+  int64_t parts, per_wave;
+  index_plan(nrows, L, &parts, &per_wave);
+  const size_t b = static_cast<size_t>(nrows) * parts * (static_cast<size_t>(k) * 8 + 4);
+  return (b + 255) / 256 * 256;
+}
+
+hipError_t launch_index_topk_fused(const IndexScoreArgs& a, const TopkArgs& t, void* ws, hipStream_t s) {
+  if (a.nrows == 0) return hipSuccess;
+  int64_t parts, per_wave;
+  index_plan(a.nrows, a.L, &parts, &per_wave);
+  IndexCandidates co;
+  co.cap = t.k;
+  co.cval = static_cast<float*>(ws);
+  co.cidx = reinterpret_cast<int32_t*>(co.cval + a.nrows * parts * t.k);
+  co.ccnt = co.cidx + a.nrows * parts * t.k;
+  const hipError_t e = launch_stream<true>(a, co, s);
+  if (e != hipSuccess) return e;
+  return launch_topk_merge(t, parts, t.k, co.cval, co.cidx, co.ccnt, true, s);
 }
 
 bool index_shape_supported(int64_t HI, int64_t dI, bool bf16) {

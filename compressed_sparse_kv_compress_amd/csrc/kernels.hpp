@@ -29,6 +29,18 @@ struct IndexScoreArgs {
 };
 hipError_t launch_index_score(const IndexScoreArgs& a, bool bf16, hipStream_t s);
 
+// Per-part top-k candidates: part p of row r keeps ccnt[r][p] <= cap
+// (score, index) pairs in index order at [r][p][0 ..].
+struct IndexCandidates {
+  float* cval;    // [rows][parts][cap]
+  int32_t* cidx;  // [rows][parts][cap]
+  int32_t* ccnt;  // [rows][parts]
+  int64_t cap;
+};
+// Geometry of the streaming indexer (d_I = 128, bf16): key-range parts per
+// row (one workgroup each) and keys per wavefront.
+void index_plan(int64_t nrows, int64_t L, int64_t* parts, int64_t* per_wave);
+
 struct TopkArgs {
   const float* score;  // row r of this launch at score + r*ld
   int64_t ld;
@@ -41,6 +53,19 @@ struct TopkArgs {
 // ws: topk_ws_bytes_per_row(L, k) bytes per row of the launch.
 size_t topk_ws_bytes_per_row(int64_t L, int64_t k);
 hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t s);
+// Merge stage alone over part candidates (fast path: nparts * cap <= 16384,
+// nparts <= 256).  fused: the candidates cover every visible entry of rows
+// with at most k of them (there is no score matrix to read).
+hipError_t launch_topk_merge(const TopkArgs& a, int64_t nparts, int64_t cap, const float* cval,
+                             const int32_t* cidx, const int32_t* ccnt, bool fused, hipStream_t s);
+
+// Indexer scan fused with the part stage of the top-k (no score matrix): the
+// scan's workgroups select their parts' candidates from LDS, then the merge
+// runs.  Available for bf16, d_I = 128, k <= 2048 when the scan's parts give
+// the merge's fast path; ws: index_topk_fused_ws_bytes(nrows, L, k).
+bool index_topk_fusable(int64_t nrows, int64_t L, int64_t HI, int64_t dI, int64_t k, bool bf16);
+size_t index_topk_fused_ws_bytes(int64_t nrows, int64_t L, int64_t k);
+hipError_t launch_index_topk_fused(const IndexScoreArgs& a, const TopkArgs& t, void* ws, hipStream_t s);
 
 struct AttnArgs {
   const void* q;        // [B*T][H][d]

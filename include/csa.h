@@ -118,11 +118,16 @@ csa_status_t csa_topk_select(const float* score, int64_t B, int64_t T, int64_t n
                              int64_t m, int64_t k, int32_t* idx, float* out_score, void* ws,
                              size_t ws_bytes, void* stream);
 
-/* csa_index_topk -- csa_index_score followed by csa_topk_select, with the
- * fp32 score matrix and the selection scratch kept in the caller's workspace.
- * When ws_bytes is below csa_index_topk_workspace(B, T, L, k) the queries are
- * processed in groups that fit; ws_bytes must cover at least one query
- * (csa_index_topk_workspace(1, 1, L, k)).  Results do not depend on ws_bytes. */
+/* csa_index_topk -- csa_index_score followed by csa_topk_select, same
+ * results bit for bit.  For bf16, d_I = 128 and decode-like shapes (the scan's
+ * key ranges times k at most 16384, k <= 2048) with a full-size workspace the
+ * scan keeps each key range's top-k candidates itself and no score matrix is
+ * written (two kernels); otherwise the fp32 score matrix and the selection
+ * scratch are kept in the caller's workspace.  When ws_bytes is below
+ * csa_index_topk_workspace(B, T, L, k) the queries are processed in groups
+ * that fit; ws_bytes must cover at least one query
+ * (csa_index_topk_workspace(1, 1, L, k)).  Results do not depend on ws_bytes.
+ * The workspace is scratch: its contents on entry do not matter. */
 size_t csa_index_topk_workspace(int64_t B, int64_t T, int64_t L, int64_t k);
 csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int64_t B,
                             int64_t T, int64_t n_ctx, int64_t L, int64_t H_I, int64_t d_I,

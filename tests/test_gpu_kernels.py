@@ -154,6 +154,40 @@ def test_topk_select_bit_exact_on_seeded_scores(B, T, L, m, k):
             assert np.all(np.isneginf(gs[b, t][~sel]))
 
 
+def _structured(s, pattern):
+    """Periodic structure that defeats a sampled threshold estimate (the
+    samples sit at fixed offsets of each thread's entries), so the exact
+    selection has to fall back to all keys, or sees a skewed survivor set."""
+    pos = torch.arange(s.shape[-1], device=s.device)
+    if pattern == "boost32":    # every 32nd entry far above the rest
+        return s + 8.0 * (pos % 32 == 0).to(s.dtype)
+    if pattern == "sink16":     # every 16th entry far below the rest
+        return s - 8.0 * (pos % 16 == 0).to(s.dtype)
+    if pattern == "steps":      # a handful of levels, long runs of exact ties
+        return torch.floor(s * 2.0) + (pos % 3 == 0).to(s.dtype)
+    if pattern == "ramp":       # increasing with the index, tiny noise
+        return pos.to(s.dtype) * 1e-3 + s * 1e-6
+    raise ValueError(pattern)
+
+
+@pytest.mark.parametrize("pattern", ["boost32", "sink16", "steps", "ramp"])
+@pytest.mark.parametrize("L,k", [(250000, 1024), (40000, 2048), (20000, 64)])
+def test_topk_select_exact_on_structured_scores(pattern, L, k):
+    B, T, m = 2, 2, 1
+    n_ctx = L * m
+    sg = _structured(gen((B, T, L), 70 + L, "scores", dtype=torch.float32, device="cuda"), pattern)
+    sc = _structured(gen((B, T, L), 70 + L, "scores", dtype=torch.float32, device="cpu"), pattern)
+    idx, osc = csa.csa_topk_select(sg, m, k, n_ctx=n_ctx, want_scores=True)
+    torch.cuda.synchronize()
+    nv = np.minimum(np.arange(n_ctx - T, n_ctx) // m, L)
+    want = oracle.topk(sc.double().numpy(), np.broadcast_to(nv, (B, T)), k)
+    assert np.array_equal(idx.cpu().numpy(), want)
+    gs, sv = osc.cpu().numpy(), sc.numpy()
+    for b in range(B):
+        for t in range(T):
+            assert np.array_equal(gs[b, t], sv[b, t][want[b, t]])
+
+
 def test_index_topk_bit_exact_on_grid_inputs():
     B, T, HI, dI, m, k = 2, 2, 64, 128, 4, 256
     n_ctx = 4 * 6000 + 3
@@ -167,6 +201,43 @@ def test_index_topk_bit_exact_on_grid_inputs():
     ws = torch.empty(csa.csa_index_topk_workspace(1, 1, L, k), dtype=torch.uint8, device="cuda")
     got2 = csa.csa_index_topk(q, kk, m, k, n_ctx=n_ctx, ws=ws).cpu().numpy()
     assert np.array_equal(got2, want)
+
+
+@pytest.mark.parametrize("B,T,L,HI,k,wts,boost", [(16, 1, 250000, 64, 1024, True, 1), (4, 3, 9000, 32, 512, False, 1),
+                                                   (2, 2, 700, 64, 1024, True, 1), (4, 16, 60000, 128, 2048, True, 1),
+                                                   (2, 8, 30000, 16, 256, False, 1), (4, 1, 250000, 64, 1024, True, 32),
+                                                   (4, 1, 250000, 64, 1024, False, 16)])
+def test_index_topk_single_pass_equals_score_then_select(B, T, L, HI, k, wts, boost):
+    """Shapes where the indexer selects its parts' candidates itself (no score
+    matrix) give the same indices and scores, bit for bit, as the scores
+    written out and selected by the stand-alone top-k (rows with fewer
+    visible entries than k are padded alike).  boost > 1: every boost-th key
+    row is scaled by 4 (exact in bf16), a periodic structure that misleads a
+    sampled threshold."""
+    dI, m = 128, 4
+    n_ctx = m * L
+    seed = 40 + L
+    q, q_c = both((B, T, HI, dI), seed, "q_idx", dtype=torch.bfloat16, scale=dI ** -0.5)
+    kk, k_c = both((B, L, dI), seed, "k_idx", dtype=torch.bfloat16, scale=dI ** -0.5)
+    if boost > 1:
+        kk[:, ::boost] *= 4
+        k_c[:, ::boost] *= 4
+    w = w_c = None
+    if wts:
+        w, w_c = both((B, T, HI), seed, "w_idx", dtype=torch.float32, scale=HI ** -0.5)
+    idx1, s1 = csa.csa_index_topk(q, kk, m, k, w_idx=w, n_ctx=n_ctx, want_scores=True)
+    sc = csa.csa_index_score(q, kk, m, w_idx=w, n_ctx=n_ctx)
+    idx2, s2 = csa.csa_topk_select(sc, m, k, n_ctx=n_ctx, want_scores=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx1, idx2)
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    # one row against the oracle (exact up to certified near ties)
+    b, t = B - 1, T - 1
+    nv = min(L, (n_ctx - T + t) // m)
+    want, osc = oracle.index_topk(q_c[b:b + 1, t:t + 1], k_c[b:b + 1], m, k, n_ctx=n_ctx,
+                                  tpos=np.array([n_ctx - T + t]), w=None if w_c is None else w_c[b:b + 1, t:t + 1])
+    eps = index_eps(q_c[b, t], None if w_c is None else w_c[b, t], k_c[b])[:nv]
+    assert near_tie_check(idx1[b, t].cpu().numpy(), want[0, 0], osc[0, 0], nv, k, eps) <= 1
 
 
 @pytest.mark.parametrize("dt,HI,dI,k", [("bf16", 64, 128, 1024), ("f32", 4, 32, 64)])
