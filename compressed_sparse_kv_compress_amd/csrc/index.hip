@@ -108,15 +108,23 @@ __device__ __forceinline__ float group_sum4(float x) {
 // in its part's top-k (fewer entries beat it inside the part than in the whole
 // row), ties included.  The tile ring is free at this point and holds the
 // selection's state.
-using PartSel = sel::Filter<64 * kWaves, 64, 16>;
+using PartSel = sel::Filter<64 * kWaves, 64, 24>;
 constexpr int kPartKeys = 64 * kWaves * 64;  // 16384 >= 4 * kMaxKeysPerWave
 constexpr int kCandStage = 2048;             // largest cap staged in LDS
 static_assert(4 * kMaxKeysPerWave <= kPartKeys, "a part fits the selection tile");
-static_assert(sizeof(PartSel::Shared) + kCandStage * 4 <= kWaves * kDepth * kTileBytes, "selection state fits the ring");
+static_assert(sizeof(PartSel::Shared) + kCandStage * 8 <= kWaves * kDepth * kTileBytes, "selection state fits the ring");
 
+// Position of key c (0..15) of a wavefront's tile `it` in its score list: the
+// four 4-key chunks of a tile are rotated by the tile number, so that 16 lanes
+// reading chunk q of 16 consecutive tiles (one 16-byte read each) hit 16
+// different bank groups.
+__device__ __forceinline__ int sb_pos(int it, int c) { return it * kTileKeys + ((((c >> 2) + it) & 3) << 2) + (c & 3); }
+
+// Score of key o of the workgroup's range: tile T = o / 16 is tile T / 4 of
+// wavefront T % 4.
 __device__ __forceinline__ float part_score(const float (*sbuf)[kMaxTiles * kTileKeys], int o) {
   const int T = o / kTileKeys;
-  return sbuf[T % kWaves][(T / kWaves) * kTileKeys + o % kTileKeys];
+  return sbuf[T % kWaves][sb_pos(T / kWaves, o % kTileKeys)];
 }
 
 __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t slot, int64_t kb, int nkv,
@@ -125,16 +133,17 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
   const int cap = static_cast<int>(co.cap);
   float* ov = co.cval + slot * co.cap;
   int32_t* oi = co.cidx + slot * co.cap;
-  if (nkv <= cap) {  // the whole part is kept
-    for (int o = tid; o < nkv; o += 64 * kWaves) {
-      ov[o] = part_score(sbuf, o);
-      oi[o] = static_cast<int32_t>(kb + o);
+  if (nkv <= cap) {  // the whole part is kept; the rest of the slots hold NaN (no candidate)
+    for (int o = tid; o < cap; o += 64 * kWaves) {
+      ov[o] = o < nkv ? part_score(sbuf, o) : __builtin_nanf("");
+      if (o < nkv) oi[o] = static_cast<int32_t>(kb + o);
     }
     if (tid == 0) co.ccnt[slot] = nkv;
     return;
   }
   PartSel::Shared& ss = *reinterpret_cast<PartSel::Shared*>(scratch);
   int32_t* si = reinterpret_cast<int32_t*>(scratch + sizeof(PartSel::Shared));
+  float* sv = reinterpret_cast<float*>(si + kCandStage);
   PartSel::zero(ss);
   // Thread t holds entries 64t .. 64t+63 of the part: tiles 4t .. 4t+3, i.e.
   // tile t of each wavefront's list, 16 consecutive scores each; entries past
@@ -146,7 +155,7 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
   for (int w = 0; w < kWaves; ++w)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(&sbuf[w][tl * kTileKeys + 4 * q]);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&sbuf[w][sb_pos(tl, 4 * q)]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[w * 16 + 4 * q + e] = v[e];
     }
@@ -155,13 +164,20 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
   float vmin, vmax;
   PartSel::block_range(x, ss, &vmin, &vmax);
   PartSel::run(
-      x, [&](int j) { return static_cast<uint32_t>(o0 + j); }, static_cast<uint32_t>(nkv),
-      static_cast<uint32_t>(cap), vmin, vmax, ss, [&](uint32_t pos, float, uint32_t e) { si[pos] = static_cast<int32_t>(e); },
-      [&](int j, uint32_t pos) { si[pos] = o0 + j; });
+      x, [&](uint32_t e) { return part_score(sbuf, static_cast<int>(e) < nkv ? static_cast<int>(e) : 0); },
+      static_cast<uint32_t>(nkv),
+      static_cast<uint32_t>(cap), vmin, vmax, ss,
+      [&](uint32_t pos, float v, uint32_t e) {
+        si[pos] = static_cast<int32_t>(e);
+        sv[pos] = v;
+      },
+      [&](int j, uint32_t pos) {
+        si[pos] = o0 + j;
+        sv[pos] = part_score(sbuf, o0 + j);
+      });
   for (int i = tid; i < cap; i += 64 * kWaves) {
-    const int o = si[i];
-    ov[i] = part_score(sbuf, o);
-    oi[i] = static_cast<int32_t>(kb + o);
+    ov[i] = sv[i];
+    oi[i] = static_cast<int32_t>(kb + si[i]);
   }
   if (tid == 0) co.ccnt[slot] = cap;
 }
@@ -288,7 +304,7 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
       for (int mb = 0; mb + w < MB; mb += 2 * w) ps[mb] += ps[mb + w];
     const float tot = group_sum4(ps[0]);
     const int64_t s = k0 + static_cast<int64_t>(it) * kStride + c16;
-    if (g == 0) sb[it * kTileKeys + c16] = s < nv ? tot : -INFINITY;
+    if (g == 0) sb[sb_pos(it, c16)] = s < nv ? tot : -INFINITY;
   }
 
   __syncthreads();
@@ -306,10 +322,9 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
   const bool aligned = (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
   for (int o = 4 * static_cast<int>(threadIdx.x); o < nk; o += 4 * 64 * kWaves) {
     const int T = o / kTileKeys;
-    f32x4 x = *reinterpret_cast<const f32x4*>(&sbuf[T % kWaves][(T / kWaves) * kTileKeys + o % kTileKeys]);
+    f32x4 x = *reinterpret_cast<const f32x4*>(&sbuf[T % kWaves][sb_pos(T / kWaves, o % kTileKeys)]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if ((o + e) / kTileKeys >= ntiles) x[e] = -INFINITY;
+    for (int e = 0; e < 4; ++e) x[e] = (o + e) / kTileKeys < ntiles ? x[e] : -INFINITY;
     if (aligned && o + 4 <= nk) {
       *reinterpret_cast<f32x4*>(dst + o) = x;
     } else {

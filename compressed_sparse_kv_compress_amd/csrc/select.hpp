@@ -383,48 +383,51 @@ __device__ __forceinline__ float wave_fmax(float v) {
 // Selection through a sampled threshold, in the float domain, for sel well
 // below the number of valid scores (a part or a merge tile keeps about one
 // score in sixteen).  Thread t holds ITEMS scores, entries t*ITEMS ..
-// t*ITEMS+ITEMS-1 of the tile; invalid entries are NaN (so every comparison
-// drops them and min / max skip them), and each entry has a 32-bit payload.
-// Scores are ordered as floats (-0 ties +0); the lower entry wins ties.
+// t*ITEMS+ITEMS-1 of the tile, in registers, and the caller can read entry e
+// again from LDS (src(e)); invalid entries are NaN, so every comparison drops
+// them and min / max skip them.  Scores are ordered as floats (-0 ties +0);
+// the lower entry wins ties.
 //   1. a value-linear histogram of kNs scores per thread (about 1024 in all,
 //      spread evenly over each thread's entries) gives a value t0 whose share
 //      of the samples at or above it is the expected share of sel plus five
 //      standard deviations of a binomial count;
-//   2. the scores >= t0 ("survivors") are counted; when there are at least
-//      sel and at most kCap of them they go to LDS with their payloads in
-//      entry order (every score equal to the sel-th largest is among them);
+//   2. the scores >= t0 ("survivors") are counted per thread (a bitmask) and
+//      over the workgroup; when there are at least sel of them (so every
+//      score equal to the sel-th largest is one) and no thread holds more than
+//      SMAX, each thread keeps its own survivors in registers, still in entry
+//      order, so thread order is entry order;
 //   3. a value-linear histogram of the survivors between t0 and the max gives
-//      the bin of the sel-th largest, whose scores are gathered and ranked by
-//      counting;
-//   4. ordered compaction of the survivors.
+//      the bin of the sel-th largest, whose scores are gathered and ranked
+//      (ballots over one wavefront's lanes);
+//   4. ordered compaction of the survivors: one workgroup scan of per-thread
+//      (greater, equal) counts packed in 16-bit halves.
 // Histograms have kFBins bins, few enough that every wavefront scans them on
-// its own (no broadcast barrier); cross-lane steps use DPP; the passes over
-// all scores cost one or two VALU operations per score.  When the survivors
-// are too few or too many (ties, small ranges, structured inputs) the radix
-// selection on order-preserving keys runs on all scores instead, with the
-// same result: the sample only decides how much work the exact steps see.
-template <int THREADS, int ITEMS, int SITEMS>
+// its own (no broadcast barrier); cross-lane steps use DPP; passes over all
+// scores keep several independent accumulators (one wavefront per SIMD leaves
+// no other latency hiding).  When the survivors are too few or too crowded in
+// one thread (ties, very small ranges, structured inputs) the radix selection
+// on order-preserving keys runs on all scores instead, with the same result:
+// the sample only decides how much work the exact steps see.
+template <int THREADS, int ITEMS, int SMAX>
 struct Filter {
   using Big = Select<THREADS, ITEMS>;
-  using Small = Select<THREADS, SITEMS>;
+  using Small = Select<THREADS, SMAX>;
   using Mask = typename Big::Mask;
   using SMask = typename Small::Mask;
   static constexpr int kNs = 1024 / THREADS;  // samples per thread
-  static_assert(kNs >= 1 && kNs <= 32 && ITEMS % kNs == 0, "sampling");
-  static constexpr int kCap = THREADS * SITEMS;  // survivor capacity
-  static constexpr int kSlots = kCap + kCap / 16;  // survivor s sits at s + s/16 (strided reads avoid bank conflicts)
+  static_assert(kNs >= 1 && kNs <= 32 && ITEMS % kNs == 0 && ITEMS % 8 == 0, "sampling");
+  static_assert(SMAX <= 32, "survivor bitmask");
   static constexpr int kWaves = THREADS / 64;
   static constexpr int kFBins = 256;  // four bins per lane
 
   struct Shared {
-    SelectShared<THREADS> core;  // state of the radix selection (fallback)
+    SelectShared<THREADS> core;          // radix selection state (fallback)
     alignas(16) uint32_t shist[kFBins];  // sample histogram
     alignas(16) uint32_t hist2[kFBins];  // survivor histogram
     alignas(16) float ck[kSmall + 64];   // scores of the threshold bin; 64 lane-private dump slots after them
     uint32_t wsum[kWaves];
     float red[2][kWaves];
     uint32_t ncand;
-    uint2 surv[kSlots + 64];  // (score bits, payload) of the survivors; 64 dump slots after them
   };
 
   // Zero what run() expects zeroed; a barrier must follow (block_range has one).
@@ -439,28 +442,38 @@ struct Filter {
   // Min and max of the non-NaN scores of the workgroup (one barrier).
   static __device__ __forceinline__ void block_range(const float (&x)[ITEMS], Shared& sh, float* vmin, float* vmax) {
     const int wave = threadIdx.x >> 6;
-    float lo = __builtin_inff(), hi = -__builtin_inff();
+    float lo[8], hi[8];
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-      lo = __builtin_fminf(lo, x[j]);
-      hi = __builtin_fmaxf(hi, x[j]);
+    for (int a = 0; a < 8; ++a) {
+      lo[a] = x[a];
+      hi[a] = x[a];
     }
-    lo = wave_fmin(lo);
-    hi = wave_fmax(hi);
+#pragma unroll
+    for (int j = 8; j < ITEMS; ++j) {
+      lo[j & 7] = __builtin_fminf(lo[j & 7], x[j]);
+      hi[j & 7] = __builtin_fmaxf(hi[j & 7], x[j]);
+    }
+#pragma unroll
+    for (int a = 4; a >= 1; a >>= 1)
+#pragma unroll
+      for (int b = 0; b < a; ++b) {
+        lo[b] = __builtin_fminf(lo[b], lo[b + a]);
+        hi[b] = __builtin_fmaxf(hi[b], hi[b + a]);
+      }
+    const float l = wave_fmin(lo[0]), h = wave_fmax(hi[0]);
     if (lane_id() == 0) {
-      sh.red[0][wave] = lo;
-      sh.red[1][wave] = hi;
+      sh.red[0][wave] = l;
+      sh.red[1][wave] = h;
     }
     __syncthreads();
-    lo = sh.red[0][0];
-    hi = sh.red[1][0];
+    float rl = sh.red[0][0], rh = sh.red[1][0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) {
-      lo = __builtin_fminf(lo, sh.red[0][w]);
-      hi = __builtin_fmaxf(hi, sh.red[1][w]);
+      rl = __builtin_fminf(rl, sh.red[0][w]);
+      rh = __builtin_fmaxf(rh, sh.red[1][w]);
     }
-    *vmin = lo;
-    *vmax = hi;
+    *vmin = rl;
+    *vmax = rh;
   }
 
   // Bin (top first) of the r-th largest of a kFBins histogram, found by every
@@ -497,34 +510,45 @@ struct Filter {
     *cnt = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(cb), src));
   }
 
-  // The rem-th largest of the n (<= kSmall) scores in ck and how many scores
-  // equal to it rank within the first rem, computed by every wavefront.
+  // The rem-th largest of the n (1 <= rem <= n <= kSmall) scores in ck and
+  // how many scores equal to it rank within the first rem, computed by every
+  // wavefront.  Up to 64 scores: one per lane, and candidate i is ranked with
+  // two ballots (stops at the answer); more: each lane counts over all.
   static __device__ __forceinline__ void rank_small(const float* ck, uint32_t n, uint32_t rem, float* thr,
                                                     uint32_t* take) {
     const uint32_t lane = lane_id();
+    if (n <= 64) {
+      const float mine = lane < n ? ck[lane] : -__builtin_inff();
+      for (uint32_t i = 0; i < n; ++i) {
+        const float ci = __uint_as_float(static_cast<uint32_t>(
+            __builtin_amdgcn_readlane(static_cast<int>(__float_as_uint(mine)), static_cast<int>(i))));
+        const uint32_t gt = static_cast<uint32_t>(__popcll(__ballot(mine > ci)));
+        const uint32_t ge = static_cast<uint32_t>(__popcll(__ballot(mine >= ci)));
+        if (gt < rem && ge >= rem) {
+          *thr = ci;
+          *take = rem - gt;
+          return;
+        }
+      }
+      *thr = 0.f;  // not reached: some score has rank rem
+      *take = 0;
+      return;
+    }
     constexpr int kQ = kSmall / 64;
     float mk[kQ];
     uint32_t gt[kQ], ge[kQ];
-    const int nq = static_cast<int>((n + 63) / 64);  // uniform
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
       mk[q] = lane + 64 * q < n ? ck[lane + 64 * q] : -__builtin_inff();
       gt[q] = 0;
       ge[q] = 0;
     }
-    const uint32_t n4 = (n + 3) & ~3u;  // scores past n read as -inf (no count)
-    for (uint32_t i = 0; i < n4; i += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(ck + i);
-      const float e[4] = {v.x, i + 1 < n ? v.y : -__builtin_inff(), i + 2 < n ? v.z : -__builtin_inff(),
-                          i + 3 < n ? v.w : -__builtin_inff()};
+    for (uint32_t i = 0; i < n; ++i) {
+      const float e = ck[i];
 #pragma unroll
       for (int q = 0; q < kQ; ++q) {
-        if (q >= nq) break;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          gt[q] += e[u] > mk[q];
-          ge[q] += e[u] >= mk[q];
-        }
+        gt[q] += e > mk[q];
+        ge[q] += e >= mk[q];
       }
     }
     float tk = 0.f;
@@ -539,17 +563,54 @@ struct Filter {
       }
     const uint64_t bal = __ballot(hit);
     const int src = bal ? __builtin_ctzll(bal) : 0;
-    *thr = __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(__float_as_uint(tk)), src)));
+    *thr = __uint_as_float(static_cast<uint32_t>(
+        __builtin_amdgcn_readlane(static_cast<int>(__float_as_uint(tk)), src)));
     *take = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tt), src));
+  }
+
+  // Ordered compaction of the survivors y[0 .. cnt) of every thread (thread
+  // order = entry order): kept are the scores > thr and the first `take`
+  // scores == thr; emit(pos, score, entry).  Ends with a barrier.
+  template <typename Emit>
+  static __device__ __forceinline__ void compact_survivors(const float (&y)[SMAX], const uint32_t (&ent)[SMAX],
+                                                           float thr, uint32_t take, Shared& sh, Emit emit) {
+    const int wave = threadIdx.x >> 6;
+    SMask gtm = 0, eqm = 0;
+#pragma unroll
+    for (int k = 0; k < SMAX; ++k) {
+      gtm |= static_cast<SMask>(y[k] > thr) << k;
+      eqm |= static_cast<SMask>(y[k] == thr) << k;
+    }
+    const uint32_t packed = (Small::popc(eqm) << 16) | Small::popc(gtm);
+    const uint32_t pin = wave_incl_scan(packed);
+    if (lane_id() == 63) sh.core.wsum[wave] = pin;
+    __syncthreads();
+    uint32_t excl = pin - packed;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) excl += w < wave ? sh.core.wsum[w] : 0u;
+    const uint32_t gt0 = excl & 0xffffu, eq0 = excl >> 16;
+    uint32_t keq = take > eq0 ? take - eq0 : 0u;
+    SMask km = gtm, em = eqm;
+    while (keq > 0 && em) {
+      const SMask lb = em & (0 - em);
+      km |= lb;
+      em ^= lb;
+      --keq;
+    }
+    uint32_t slot = gt0 + (eq0 < take ? eq0 : take);
+#pragma unroll
+    for (int k = 0; k < SMAX; ++k)
+      if (Small::bit(km, k)) emit(slot++, y[k], ent[k]);
+    __syncthreads();
   }
 
   // Keeps the sel largest valid scores (1 <= sel <= nvalid = valid scores of
   // the workgroup, vmin / vmax their min and max).  Kept items get slots in
-  // entry order: emit(pos, score, payload) on the sampled path,
-  // emit_item(j, pos) (item j of this thread) on the radix path.  Ends with a
-  // barrier.
-  template <typename Pay, typename Emit, typename EmitItem>
-  static __device__ __forceinline__ void run(const float (&x)[ITEMS], Pay pay, uint32_t nvalid, uint32_t sel,
+  // entry order: emit(pos, score, entry) on the sampled path, emit_item(j,
+  // pos) (item j of this thread) on the radix path.  src(e) returns the score
+  // of entry e.  Ends with a barrier.
+  template <typename Src, typename Emit, typename EmitItem>
+  static __device__ __forceinline__ void run(const float (&x)[ITEMS], Src src, uint32_t nvalid, uint32_t sel,
                                              float vmin, float vmax, Shared& sh, Emit emit, EmitItem emit_item) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -557,9 +618,8 @@ struct Filter {
     const float range = vmax - vmin;
     const float scale = static_cast<float>(kFBins) / range;
     // uniform: every operand is
-    bool filt = sel * 4u <= nvalid && 2u * sel <= static_cast<uint32_t>(kCap) && vmin < vmax &&
-                __builtin_isfinite(vmin) && __builtin_isfinite(vmax) && __builtin_isfinite(range) &&
-                __builtin_isfinite(scale);
+    bool filt = sel * 4u <= nvalid && vmin < vmax && __builtin_isfinite(vmin) && __builtin_isfinite(vmax) &&
+                __builtin_isfinite(range) && __builtin_isfinite(scale);
     float t0 = 0.f;
     if (filt) {
 #pragma unroll
@@ -580,22 +640,25 @@ struct Filter {
       filt = ns >= 64;
       t0 = vmin + static_cast<float>(b) / scale;  // about the lower edge of that bin
     }
-    // Survivors: count and workgroup scan.
-    uint32_t c = 0;
+    // Survivors: a bitmask per thread (four independent partial masks), the
+    // count and an overflow flag (more than SMAX) summed over the workgroup.
+    Mask gm = 0;
     if (filt) {
+      Mask g4[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int j = 0; j < ITEMS; ++j) c += x[j] >= t0;
+      for (int j = 0; j < ITEMS; ++j) g4[j & 3] |= static_cast<Mask>(x[j] >= t0) << j;
+      gm = (g4[0] | g4[1]) | (g4[2] | g4[3]);
     }
-    const uint32_t incl = wave_incl_scan(c);
+    const uint32_t c = Big::popc(gm);
+    const uint32_t packed = c | (static_cast<uint32_t>(c > static_cast<uint32_t>(SMAX)) << 20);
+    const uint32_t incl = wave_incl_scan(packed);
     if (lane == 63) sh.wsum[wave] = incl;
     __syncthreads();
-    uint32_t pos = incl - c, total = 0;
+    uint32_t tot = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      pos += w < wave ? sh.wsum[w] : 0u;
-      total += sh.wsum[w];
-    }
-    if (!(filt && total >= sel && total <= static_cast<uint32_t>(kCap))) {
+    for (int w = 0; w < kWaves; ++w) tot += sh.wsum[w];
+    const uint32_t total = tot & 0xfffffu;
+    if (!(filt && total >= sel && (tot >> 20) == 0)) {
       uint32_t keys[ITEMS];
       Mask vm = 0;
 #pragma unroll
@@ -610,103 +673,71 @@ struct Filter {
       Big::compact(keys, vm, thr, take, sh.core, &bg, &be, emit_item);
       return;
     }
+    // This thread's survivors, in entry order, into registers (scores read
+    // back from LDS: the loads are independent).
+    uint32_t ent[SMAX];
+    float y[SMAX];
+    Mask m = gm;
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-      const bool in = x[j] >= t0;
-      sh.surv[in ? pos + (pos >> 4) : kSlots + lane] = make_uint2(__float_as_uint(x[j]), pay(j));
-      pos += in;
+    for (int k = 0; k < SMAX; ++k) {
+      const int j = m ? static_cast<int>(Big::ctz(m)) : 0;
+      m &= m - 1;
+      ent[k] = static_cast<uint32_t>(tid * ITEMS + j);
     }
-    __syncthreads();
-    // Survivor s = tid * SITEMS + i.
-    float y[SITEMS];
 #pragma unroll
-    for (int i = 0; i < SITEMS; ++i) {
-      const uint32_t si = static_cast<uint32_t>(tid * SITEMS + i);
-      y[i] = si < total ? __uint_as_float(sh.surv[si + (si >> 4)].x) : __builtin_nanf("");
+    for (int k = 0; k < SMAX; ++k) {
+      const float v = src(ent[k]);
+      y[k] = static_cast<uint32_t>(k) < c ? v : __builtin_nanf("");
     }
     const float range2 = vmax - t0;
     const float scale2 = static_cast<float>(kFBins) / range2;
+    const bool spread = range2 > 0.f && __builtin_isfinite(range2) && __builtin_isfinite(scale2);  // uniform
+    int bn[SMAX];
     uint32_t cb2 = 0, ab2 = 0, b2 = 0;
-    const bool spread = range2 > 0.f && __builtin_isfinite(range2) && __builtin_isfinite(scale2);
-    int bn[SITEMS];
     if (spread) {
 #pragma unroll
-      for (int i = 0; i < SITEMS; ++i) {
-        const int bb = static_cast<int>((y[i] - t0) * scale2);
-        bn[i] = y[i] == y[i] ? (bb < kFBins - 1 ? bb : kFBins - 1) : -1;
-        if (bn[i] >= 0) atomicAdd(&sh.hist2[bn[i]], 1u);
+      for (int k = 0; k < SMAX; ++k) {
+        const int bb = static_cast<int>((y[k] - t0) * scale2);
+        bn[k] = static_cast<uint32_t>(k) < c ? (bb < kFBins - 1 ? bb : kFBins - 1) : -1;
+        if (bn[k] >= 0) atomicAdd(&sh.hist2[bn[k]], 1u);
       }
       __syncthreads();
       uint32_t n2;
       hist_find(sh.hist2, [&](uint32_t) { return sel; }, &n2, &b2, &ab2, &cb2);
     }
-    if (!spread || cb2 > static_cast<uint32_t>(kSmall)) {  // one value or a crowded bin: radix passes on the survivors
-      uint32_t k2[SITEMS];
+    float thr;
+    uint32_t take;
+    if (!spread || cb2 > static_cast<uint32_t>(kSmall)) {
+      // One value or a crowded bin: radix passes over the survivors' keys.
+      uint32_t k2[SMAX];
       SMask v2 = 0;
 #pragma unroll
-      for (int i = 0; i < SITEMS; ++i) {
-        k2[i] = float_key(y[i]);
-        v2 |= static_cast<SMask>(y[i] == y[i]) << i;
+      for (int k = 0; k < SMAX; ++k) {
+        k2[k] = float_key(y[k]);
+        v2 |= static_cast<SMask>(static_cast<uint32_t>(k) < c) << k;
       }
       Big::zero(sh.core);
       __syncthreads();
-      uint32_t thr, take, bg = 0, be = 0;
-      Small::radix_select(k2, v2, sel, sh.core, &thr, &take);
-      Small::compact(k2, v2, thr, take, sh.core, &bg, &be, [&](int i, uint32_t p) {
-        const uint32_t si = static_cast<uint32_t>(tid * SITEMS + i);
-        const uint2 rec = sh.surv[si + (si >> 4)];
-        emit(p, __uint_as_float(rec.x), rec.y);
-      });
-      return;
-    }
-    // Gather the threshold bin's scores; every wavefront then ranks them.
-    SMask m2 = 0;
+      uint32_t tk;
+      Small::radix_select(k2, v2, sel, sh.core, &tk, &take);
+      thr = key_float(tk);
+    } else {
+      // Gather the threshold bin's scores (one LDS atomic per wavefront
+      // reserves the space); every wavefront then ranks them.
+      SMask m2 = 0;
 #pragma unroll
-    for (int i = 0; i < SITEMS; ++i) m2 |= static_cast<SMask>(bn[i] == static_cast<int>(b2)) << i;
-    const uint32_t c2 = Small::popc(m2);
-    const uint32_t in2 = wave_incl_scan(c2);
-    uint32_t base = 0;
-    if (lane == 63 && in2 != 0) base = atomicAdd(&sh.ncand, in2);
-    base = last_lane(base);
-    if (last_lane(in2) != 0)
-      scatter_flagged<SITEMS>(m2, base + in2 - c2, kSmall, kSmall + lane, sh.ck, [&](int i) { return y[i]; });
-    __syncthreads();
-    float thr;
-    uint32_t take;
-    rank_small(sh.ck, cb2, sel - ab2, &thr, &take);
-    // Ordered compaction of the survivors: greater-than and equal counts
-    // packed in 16-bit halves, one workgroup scan.
-    SMask gtm = 0, eqm = 0;
-#pragma unroll
-    for (int i = 0; i < SITEMS; ++i) {
-      gtm |= static_cast<SMask>(y[i] > thr) << i;
-      eqm |= static_cast<SMask>(y[i] == thr) << i;
+      for (int k = 0; k < SMAX; ++k) m2 |= static_cast<SMask>(bn[k] == static_cast<int>(b2)) << k;
+      const uint32_t c2 = Small::popc(m2);
+      const uint32_t in2 = wave_incl_scan(c2);
+      uint32_t base = 0;
+      if (lane == 63 && in2 != 0) base = atomicAdd(&sh.ncand, in2);
+      base = last_lane(base);
+      if (last_lane(in2) != 0)
+        scatter_flagged<SMAX>(m2, base + in2 - c2, kSmall, kSmall + lane, sh.ck, [&](int k) { return y[k]; });
+      __syncthreads();
+      rank_small(sh.ck, cb2, sel - ab2, &thr, &take);
     }
-    const uint32_t packed = (Small::popc(eqm) << 16) | Small::popc(gtm);
-    const uint32_t pin = wave_incl_scan(packed);
-    if (lane == 63) sh.core.wsum[wave] = pin;
-    __syncthreads();
-    uint32_t excl = pin - packed;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) excl += w < wave ? sh.core.wsum[w] : 0u;
-    const uint32_t gt0 = excl & 0xffffu, eq0 = excl >> 16;
-    uint32_t keq = take > eq0 ? take - eq0 : 0u;
-    SMask km = gtm, em = eqm;
-    while (keq > 0 && em) {
-      const SMask lb = em & (0 - em);
-      km |= lb;
-      em ^= lb;
-      --keq;
-    }
-    uint32_t slot = gt0 + (eq0 < take ? eq0 : take);
-    while (km) {
-      const int i = Small::ctz(km);
-      km &= km - 1;
-      const uint32_t si = static_cast<uint32_t>(tid * SITEMS + i);
-      const uint2 rec = sh.surv[si + (si >> 4)];
-      emit(slot++, __uint_as_float(rec.x), rec.y);
-    }
-    __syncthreads();
+    compact_survivors(y, ent, thr, take, sh, emit);
   }
 };
 

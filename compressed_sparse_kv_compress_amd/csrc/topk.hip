@@ -36,19 +36,52 @@ constexpr int kThreads = 512;
 constexpr int kItems = 32;
 constexpr int64_t kPart = static_cast<int64_t>(kThreads) * kItems;  // 16384
 constexpr int kBins = sel::kBins;
-constexpr int kMaxMergeParts = 256;  // part counts cached in LDS by the merge
+constexpr int kMaxMergeParts = 256;  // one part count per merge thread
 constexpr int kStage = 2048;         // outputs up to this size are staged in LDS, then stored coalesced
 using Sel = sel::Select<kThreads, kItems>;
-using Filt = sel::Filter<kThreads, kItems, 8>;
+using Filt = sel::Filter<kThreads, kItems, 16>;
 using sel::lane_id;
 using sel::wave_incl_scan;
+constexpr int kStagePitch = kItems + 4;  // a thread's 32 staged scores, then 4 pad words (no bank conflicts)
 
 struct Shared {
   Filt::Shared fs;
-  int32_t pcnt[kMaxMergeParts];
-  int32_t si[kStage];  // staged output: payload (entry or index) and score
+  int32_t si[kStage];  // staged output: entry and score
   float sv[kStage];
+  alignas(16) float stage[kThreads * kStagePitch];  // the tile's scores, entry e at e + 4 * (e / 32)
 };
+
+__device__ __forceinline__ int stage_pos(int e) { return e + 4 * (e / kItems); }
+
+// Scores [0, n) of a tile into LDS with coalesced 16-byte loads (entries at
+// and past n read as NaN), then thread t's entries t*32 .. t*32+31 into x.
+// Ends with the barrier that makes the staged tile visible.
+__device__ __forceinline__ void stage_tile(const float* src, int n, float* stage, float (&x)[kItems]) {
+  const int tid = threadIdx.x;
+  const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+#pragma unroll
+  for (int r = 0; r < kItems / 4; ++r) {
+    const int e = 4 * (r * kThreads + tid);
+    f32x4 v;
+    if (vec && e + 4 <= n) {
+      v = *reinterpret_cast<const f32x4*>(src + e);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float t = src[e + u < n ? e + u : 0];
+        v[u] = e + u < n ? t : __builtin_nanf("");
+      }
+    }
+    *reinterpret_cast<f32x4*>(stage + stage_pos(e)) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kItems / 4; ++q) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(stage + tid * kStagePitch + 4 * q);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[4 * q + u] = v[u];
+  }
+}
 
 __device__ __forceinline__ int64_t row_visible(const TopkArgs& a, int64_t row) {
   const int64_t tpos = a.n_ctx - a.T + row % a.T;
@@ -70,56 +103,42 @@ __global__ __launch_bounds__(kThreads) void topk_part_kernel(TopkArgs a, int64_t
   int64_t cnt = nv - base;
   if (cnt > kPart) cnt = kPart;
   int32_t* cc = ccnt + lrow * nparts + part;
-  if (cnt <= 0) {
-    if (threadIdx.x == 0) *cc = 0;
+  float* ov = cval + (lrow * nparts + part) * cap;
+  int32_t* oi = cidx + (lrow * nparts + part) * cap;
+  const int tid = threadIdx.x;
+  if (cnt <= 0) {  // no candidate: every slot NaN
+    for (int64_t i = tid; i < cap; i += kThreads) ov[i] = __builtin_nanf("");
+    if (tid == 0) *cc = 0;
     return;
   }
   Filt::zero(sh.fs);
   const float* s = a.score + lrow * a.ld + base;
-  float* ov = cval + (lrow * nparts + part) * cap;
-  int32_t* oi = cidx + (lrow * nparts + part) * cap;
-  const int tid = threadIdx.x;
-  const int i0 = tid * kItems;  // this thread's entries i0 .. i0+31 of the part
   float v[kItems];
-  const int nvalid = cnt - i0 <= 0 ? 0 : (cnt - i0 >= kItems ? kItems : static_cast<int>(cnt - i0));
-  if (nvalid == kItems && (reinterpret_cast<uintptr_t>(s) & 15) == 0) {
-#pragma unroll
-    for (int q = 0; q < kItems / 4; ++q) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(s + i0 + 4 * q);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+  stage_tile(s, static_cast<int>(cnt), sh.stage, v);
+  const int i0 = tid * kItems;  // this thread's entries i0 .. i0+31 of the part
+  if (cnt <= cap) {  // the whole part is kept; slots past it hold NaN
+    for (int64_t i = tid; i < cap; i += kThreads) {
+      const float t = sh.stage[stage_pos(static_cast<int>(i < kPart ? i : 0))];
+      ov[i] = i < cnt ? t : __builtin_nanf("");
+      if (i < cnt) oi[i] = static_cast<int32_t>(base + i);
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kItems; ++j) {
-      const float t = s[j < nvalid ? i0 + j : 0];  // in range: the part has at least one entry
-      v[j] = j < nvalid ? t : __builtin_nanf("");
-    }
-  }
-  if (cnt <= cap) {  // the whole part is kept
-#pragma unroll
-    for (int j = 0; j < kItems; ++j)
-      if (j < nvalid) {
-        ov[i0 + j] = v[j];
-        oi[i0 + j] = static_cast<int32_t>(base + i0 + j);
-      }
     if (tid == 0) *cc = static_cast<int32_t>(cnt);
     return;
   }
   float vmin, vmax;
   Filt::block_range(v, sh.fs, &vmin, &vmax);
   const uint32_t ncnt = static_cast<uint32_t>(cnt), ucap = static_cast<uint32_t>(cap);
-  auto pay = [&](int j) { return static_cast<uint32_t>(i0 + j); };
+  auto src = [&](uint32_t e) { return sh.stage[stage_pos(static_cast<int>(e))]; };
   if (cap <= kStage) {  // stage the kept entries in LDS, then store them coalesced
     Filt::run(
-        v, pay, ncnt, ucap, vmin, vmax, sh.fs,
+        v, src, ncnt, ucap, vmin, vmax, sh.fs,
         [&](uint32_t pos, float val, uint32_t e) {
           sh.si[pos] = static_cast<int>(e);
           sh.sv[pos] = val;
         },
         [&](int j, uint32_t pos) {
           sh.si[pos] = i0 + j;
-          sh.sv[pos] = s[i0 + j];
+          sh.sv[pos] = sh.stage[stage_pos(i0 + j)];
         });
     for (int i = tid; i < cap; i += kThreads) {
       ov[i] = sh.sv[i];
@@ -127,13 +146,13 @@ __global__ __launch_bounds__(kThreads) void topk_part_kernel(TopkArgs a, int64_t
     }
   } else {
     Filt::run(
-        v, pay, ncnt, ucap, vmin, vmax, sh.fs,
+        v, src, ncnt, ucap, vmin, vmax, sh.fs,
         [&](uint32_t pos, float val, uint32_t e) {
           ov[pos] = val;
           oi[pos] = static_cast<int32_t>(base + e);
         },
         [&](int j, uint32_t pos) {
-          ov[pos] = s[i0 + j];
+          ov[pos] = sh.stage[stage_pos(i0 + j)];
           oi[pos] = static_cast<int32_t>(base + i0 + j);
         });
   }
@@ -155,9 +174,9 @@ __device__ __forceinline__ bool merge_trivial(const TopkArgs& a, int64_t lrow) {
   return true;
 }
 
-// Fast merge: nparts * cap <= 16384 slots and nparts <= 256.  Thread t holds
-// slots 32t .. 32t+31; part counts come from LDS, and the part of a slot is an
-// exact multiply-high (slot * cap < 2^32 here).
+// Fast merge: nparts * cap <= 16384 slots and nparts <= 256.  The candidate
+// values are staged in LDS with coalesced loads and thread t holds slots
+// 32t .. 32t+31; slots without a candidate hold NaN.
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a, int nparts, int cap, const float* cval,
                                                               const int32_t* cidx, const int32_t* ccnt, bool fused) {
   __shared__ Shared sh;
@@ -173,54 +192,18 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a, int np
   const int32_t* rc = ccnt + lrow * nparts;
   Filt::zero(sh.fs);
   static_assert(kMaxMergeParts <= kThreads, "one part count per thread");
-  int pc = 0;
-  if (tid < nparts) {
-    pc = rc[tid];
-    sh.pcnt[tid] = pc;
-  }
+  int pc = tid < nparts ? rc[tid] : 0;
   pc = static_cast<int>(sel::wave_sum(static_cast<uint32_t>(pc)));
   if (lane_id() == 0) wtot[tid >> 6] = pc;
   __syncthreads();
   int total = 0;  // valid candidates of the row
 #pragma unroll
   for (int w = 0; w < kThreads / 64; ++w) total += wtot[w];
-  const uint32_t ucap = static_cast<uint32_t>(cap);
-  const uint32_t magic = static_cast<uint32_t>((0x100000000ull + ucap - 1) / ucap);
+  // Candidate slots past their part's count hold NaN (written so by the part
+  // stage), as does everything past the last part: no validity test here.
   float v[kItems];
-  uint32_t ix[kItems];
+  stage_tile(rv, ns, sh.stage, v);
   const int s0 = tid * kItems;
-  if (s0 + kItems <= ns && ((reinterpret_cast<uintptr_t>(rv + s0) | reinterpret_cast<uintptr_t>(ri + s0)) & 15) == 0) {
-#pragma unroll
-    for (int q = 0; q < kItems / 4; ++q) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(rv + s0 + 4 * q);
-      const u32x4 y = *reinterpret_cast<const u32x4*>(ri + s0 + 4 * q);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[4 * q + e] = x[e];
-        ix[4 * q + e] = y[e];
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kItems; ++j) {
-      const int sc = s0 + j < ns ? s0 + j : ns - 1;
-      v[j] = rv[sc];
-      ix[j] = static_cast<uint32_t>(ri[sc]);
-    }
-  }
-  // Slots past their part's count hold no candidate: NaN (never selected).
-  // Branch-free on purpose (the part count is read for every slot, clamped
-  // in range): a conditional store into the register array here has been
-  // compiled into code that loses the store for the first item.
-#pragma unroll
-  for (int j = 0; j < kItems; ++j) {
-    const int sl = s0 + j;
-    const int sc = sl < ns ? sl : ns - 1;
-    const uint32_t pp = __umulhi(static_cast<uint32_t>(sc), magic);
-    const int pcount = sh.pcnt[pp];
-    const bool ok = (sl < ns) & (static_cast<int>(static_cast<uint32_t>(sc) - pp * ucap) < pcount);
-    v[j] = ok ? v[j] : __builtin_nanf("");
-  }
   if (total <= a.k) {  // every valid candidate is kept, in slot order; -1 padding after them
     for (int64_t i = total + tid; i < a.k; i += kThreads) {
       o[i] = -1;
@@ -237,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a, int np
 #pragma unroll
     for (int j = 0; j < kItems; ++j)
       if (v[j] == v[j]) {
-        o[pos] = static_cast<int32_t>(ix[j]);
+        o[pos] = ri[s0 + j];
         if (os) os[pos] = v[j];
         ++pos;
       }
@@ -246,32 +229,32 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a, int np
   const uint32_t uk = static_cast<uint32_t>(a.k);
   float vmin, vmax;
   Filt::block_range(v, sh.fs, &vmin, &vmax);
-  auto pay = [&](int j) { return ix[j]; };
+  auto src = [&](uint32_t e) { return sh.stage[stage_pos(static_cast<int>(e))]; };
   if (a.k <= kStage) {  // stage the kept candidates in LDS, then store coalesced
     Filt::run(
-        v, pay, static_cast<uint32_t>(total), uk, vmin, vmax, sh.fs,
-        [&](uint32_t pos, float val, uint32_t idx) {
-          sh.si[pos] = static_cast<int32_t>(idx);
+        v, src, static_cast<uint32_t>(total), uk, vmin, vmax, sh.fs,
+        [&](uint32_t pos, float val, uint32_t e) {
+          sh.si[pos] = static_cast<int32_t>(e);
           sh.sv[pos] = val;
         },
         [&](int j, uint32_t pos) {
-          sh.si[pos] = ri[s0 + j];
-          sh.sv[pos] = rv[s0 + j];
+          sh.si[pos] = s0 + j;
+          sh.sv[pos] = sh.stage[stage_pos(s0 + j)];
         });
     for (int i = tid; i < a.k; i += kThreads) {
-      o[i] = sh.si[i];
+      o[i] = ri[sh.si[i]];
       if (os) os[i] = sh.sv[i];
     }
   } else {
     Filt::run(
-        v, pay, static_cast<uint32_t>(total), uk, vmin, vmax, sh.fs,
-        [&](uint32_t pos, float val, uint32_t idx) {
-          o[pos] = static_cast<int32_t>(idx);
+        v, src, static_cast<uint32_t>(total), uk, vmin, vmax, sh.fs,
+        [&](uint32_t pos, float val, uint32_t e) {
+          o[pos] = ri[e];
           if (os) os[pos] = val;
         },
         [&](int j, uint32_t pos) {
           o[pos] = ri[s0 + j];
-          if (os) os[pos] = rv[s0 + j];
+          if (os) os[pos] = sh.stage[stage_pos(s0 + j)];
         });
   }
 }
