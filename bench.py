@@ -382,6 +382,61 @@ def _oracle_layer(st, sub, S, full, sd, si, li, kind, min_seconds, max_reps):
     return total, reps
 
 
+def prefill_sparse_attn(queries: int, reps: int = 3):
+    """Prefill-chunk sparse attention (the CSA prefill shape: `queries` new
+    tokens after a 262,144-token prefix, m = 4, 64 heads x 512 on one KV head,
+    top-1024 + 128-token window, sinks).  The index lists are seeded uniform
+    draws of 1024 visible entries per query, ascending (what the top-k of the
+    seeded random indexer inputs is, statistically); inputs are generated on
+    the GPU.  Returns the average call time and its MFMA / gather rates."""
+    import compressed_sparse_kv_compress_amd as csa
+    dev = "cuda"
+    B, H, d, k, W, m = 1, 64, 512, 1024, 128, 4
+    T = queries
+    n_ctx = 262144 + T
+    L = -(-n_ctx // m)
+    R = T + W - 1
+    bf = torch.bfloat16
+
+    def gen(shape, name, scale, dtype=bf, kind="normal"):
+        t = torch.empty(shape, dtype=dtype, device=dev)
+        return syn.fill_(t, SEED, syn.TID[name], scale=scale, layer=0, kind=kind)
+
+    sd = d ** -0.5
+    q = gen((B, T, H, d), "q", sd)
+    kc, vc = gen((B, L, d), "kc", sd), gen((B, L, d), "vc", sd)
+    kr, vr = gen((B, R, d), "kr", sd), gen((B, R, d), "vr", sd)
+    sink = gen((H,), "sink", 1.0, torch.float32)
+    u = gen((B, T, k), "idx", 1.0, torch.float32, kind="uniform")  # seeded draws in [0, 1)
+    nv = (torch.arange(n_ctx - T, n_ctx, device=dev) // m).clamp(max=L)
+    idx = (u.double() * nv.view(1, T, 1)).long().sort(-1).values.int()
+    out = torch.empty_like(q)
+    ws = torch.empty(max(16, csa.csa_sparse_attn_workspace(B, T, H, d, k, W, csa.CSA_BF16)), dtype=torch.uint8,
+                     device=dev)
+    call = lambda: csa.csa_sparse_attn(q, kc, vc, idx, kr=kr, vr=vr, W=W, sink=sink, n_ctx=n_ctx,  # noqa: E731
+                                       out=out, ws=ws)
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    rows = k + W
+    flop = 2 * 2 * B * T * H * rows * d
+    gathered = B * T * rows * d * 2 * 2
+    del q, kc, vc, kr, vr, out, ws, idx, u
+    torch.cuda.empty_cache()
+    return {"queries": T, "prefix": 262144, "ms_per_call": ms,
+            "tflops": flop / (ms * 1e-3) / 1e12, "peak_tflops_bf16": 2500.0,
+            "frac_of_bf16_peak": flop / (ms * 1e-3) / 1e12 / 2500.0,
+            "gathered_GB": gathered / 1e9, "gathered_TBps": gathered / (ms * 1e-3) / 1e12,
+            "note": "per query 1152 K and V rows of 1 KiB gathered (no reuse across queries beyond the window: "
+                    "the index lists are independent uniform draws); flop = 4 * queries * heads * rows * d"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -392,6 +447,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle step until at least this much oracle time")
+    ap.add_argument("--prefill-queries", type=int, default=16384,
+                    help="queries of the prefill sparse-attention measurement (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run a plain device copy of BYTES bytes 3 times (counter calibration)")
     args = ap.parse_args()
@@ -450,6 +507,14 @@ def main():
     idx_gbps = idx_bytes / (idx_ms * 1e-3) / 1e9
     traffic = counter_traffic(INDEX_TOPK_SOURCES, st.B)
 
+    prefill = None
+    if args.prefill_queries > 0:
+        del state
+        torch.cuda.empty_cache()
+        prefill = prefill_sparse_attn(args.prefill_queries)
+        print("# prefill sparse attention: %.2f ms for %d queries (%.0f TFLOP/s)"
+              % (prefill["ms_per_call"], prefill["queries"], prefill["tflops"]), file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(st, args.cpu_sample, args.cpu_seconds)
@@ -483,6 +548,7 @@ def main():
                      "algorithmic_bytes_per_launch": idx_bytes},
         "per_call_ms": per_call,
         "per_call_note": "untimed pass with events around every call; compression runs on a second stream",
+        "prefill_sparse_attn": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

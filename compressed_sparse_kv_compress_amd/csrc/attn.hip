@@ -347,8 +347,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
       sv[4 + r] = ok1[r] ? s1[r] * sl2 : -INFINITY;
     }
     float cm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    cm = group_max4(cm);
     const float mnew = fmaxf(m_run, cm);
     if (__any(m_run != -INFINITY && mnew > m_run + kRebase)) {
       // rare: re-base this head's sum and the output rows (heads 4g+r) to the new max
@@ -393,9 +392,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
   __syncthreads();  // the ring is reused below
 
   // ---- epilogue: oacc[nb][r] = O[head 4g+r][dim dh*DH + 16nb + c16] --------
-  float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  const float l_tot = group_sum4(l_run);
   float* ot = reinterpret_cast<float*>(ring) + wave * kHeadsPerWave * C::OP;  // this wave's 16 x DH tile
   // One workgroup finishes in place (sink, normalisation, lse); a split
   // writes its unnormalised bf16 rows and (m, l) for the combine kernel.
@@ -445,15 +442,23 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
 
 // Merge split partials: O = sum_s 2^{m_s-M} O_s / (sum_s 2^{m_s-M} l_s + 2^{sig-M}).
 // One wavefront per (query, head), four per workgroup: lane s reads split s's
-// (m, l), then each lane merges 8 adjacent output dims (16-byte loads of the
-// bf16 partial rows) across the splits, eight splits per round trip.
+// (m, l) while every lane already requests its 8 output dims (16 bytes of the
+// bf16 partial row) of the first 16 splits, so the first group costs one
+// memory round trip; further groups of 16 follow.
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int nsplit) {
   __shared__ float fac[4][64];
+  constexpr int kGroup = 16;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t bh = static_cast<int64_t>(blockIdx.x) * 4 + w;  // (bt, h)
   const int64_t bt = bh / a.H;
   const int64_t h = bh % a.H;
   const int64_t D = a.d;
+  const bool has_dims = lane * 8 < D;
+  const uint16_t* src = attn_ws_o(a) + (bt * nsplit * a.H + h) * D + (has_dims ? lane * 8 : 0);
+  const int64_t sstride = a.H * D;
+  u32x4 v[kGroup];
+#pragma unroll
+  for (int q = 0; q < kGroup; ++q) v[q] = *reinterpret_cast<const u32x4*>(src + (q < nsplit ? q : 0) * sstride);
   const float* wml = attn_ws_ml(a, nsplit);
   const float ms = lane < nsplit ? wml[((bt * nsplit + lane) * a.H + h) * 2] : -INFINITY;
   const float ls = lane < nsplit ? wml[((bt * nsplit + lane) * a.H + h) * 2 + 1] : 0.f;
@@ -467,31 +472,28 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int nsplit) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  if (lane * 8 < D) {
-    float acc[8];
+  float acc[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    const uint16_t* src = attn_ws_o(a) + (bt * nsplit * a.H + h) * D + lane * 8;
-    const int64_t sstride = a.H * D;
-    // Eight splits' rows are requested together (one memory round trip per
-    // eight); missing splits of the last group read split 0 with weight 0.
-    for (int s0 = 0; s0 < nsplit; s0 += 8) {
-      u32x4 v[8];
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += kGroup) {
+    if (s0 > 0) {  // later groups (more than 16 splits)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int s = s0 + q < nsplit ? s0 + q : 0;
-        v[q] = *reinterpret_cast<const u32x4*>(src + s * sstride);
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float fs = s0 + q < nsplit ? fac[w][s0 + q] : 0.f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          acc[2 * u] = fmaf(lo_bf16(v[q][u]), fs, acc[2 * u]);
-          acc[2 * u + 1] = fmaf(hi_bf16(v[q][u]), fs, acc[2 * u + 1]);
-        }
+      for (int q = 0; q < kGroup; ++q) {
+        const int sp = s0 + q < nsplit ? s0 + q : 0;
+        v[q] = *reinterpret_cast<const u32x4*>(src + sp * sstride);
       }
     }
+#pragma unroll
+    for (int q = 0; q < kGroup; ++q) {
+      const float fs = s0 + q < nsplit ? fac[w][s0 + q] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc[2 * u] = fmaf(lo_bf16(v[q][u]), fs, acc[2 * u]);
+        acc[2 * u + 1] = fmaf(hi_bf16(v[q][u]), fs, acc[2 * u + 1]);
+      }
+    }
+  }
+  if (has_dims) {
     u32x4 o;
 #pragma unroll
     for (int u = 0; u < 4; ++u) o[u] = cvt_bf16x2(acc[2 * u] * inv, acc[2 * u + 1] * inv);

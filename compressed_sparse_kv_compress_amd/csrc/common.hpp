@@ -41,16 +41,63 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+// Cross-lane data movement by DPP (a VALU operand modifier, no LDS round
+// trip as with __shfl): row_shr:n reads lane i-n within a row of 16 lanes;
+// row_bcast:15 and row_bcast:31 read the last lane of the previous row
+// (rows 1, 3) and lane 31 (rows 2, 3).  Lanes with no source keep `id`.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ uint32_t dpp(uint32_t id, uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(id), static_cast<int>(v), CTRL, ROWS, 0xf, false));
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// Value of lane 63 as a wave-uniform scalar.
+__device__ __forceinline__ uint32_t last_lane(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+// Inclusive scan of op over the 64 lanes (identity id); lane 63 ends with the total.
+template <typename Op>
+__device__ __forceinline__ float wave_scan_f(float v, uint32_t id, Op op) {
+  v = op(v, __uint_as_float(dpp<kRowShr1>(id, __float_as_uint(v))));
+  v = op(v, __uint_as_float(dpp<kRowShr2>(id, __float_as_uint(v))));
+  v = op(v, __uint_as_float(dpp<kRowShr4>(id, __float_as_uint(v))));
+  v = op(v, __uint_as_float(dpp<kRowShr8>(id, __float_as_uint(v))));
+  v = op(v, __uint_as_float(dpp<kRowBcast15, 0xa>(id, __float_as_uint(v))));
+  v = op(v, __uint_as_float(dpp<kRowBcast31, 0xc>(id, __float_as_uint(v))));
   return v;
 }
 
+// Sum / max over the four 16-lane groups of a wavefront (lanes l, l^16, l^32,
+// l^48), returned to all four: the gfx950 row-swap permutes exchange the
+// groups pairwise without an LDS round trip.
+__device__ __forceinline__ float group_sum4(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const uint32_t v = __float_as_uint(y);
+  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+__device__ __forceinline__ float group_max4(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const uint32_t v = __float_as_uint(y);
+  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
+// Max / sum over the wavefront, returned to every lane (wave-uniform).
+__device__ __forceinline__ float wave_max(float v) {
+  v = wave_scan_f(v, 0xff800000u, [](float a, float b) { return fmaxf(a, b); });
+  return __uint_as_float(last_lane(__float_as_uint(v)));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v = wave_scan_f(v, 0u, [](float a, float b) { return a + b; });
+  return __uint_as_float(last_lane(__float_as_uint(v)));
 }
 
 // Order-preserving map float -> uint32 with -0 and +0 mapped together.

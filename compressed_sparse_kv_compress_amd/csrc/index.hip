@@ -92,15 +92,6 @@ __device__ __forceinline__ void dma16(const void* g, const uint8_t* lds) {
 
 // Sum of x over the four 16-lane groups (lanes c, c+16, c+32, c+48), in every
 // lane, by the gfx950 row-swap permutes (no LDS round trip).
-__device__ __forceinline__ float group_sum4(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float y = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-  const uint32_t v = __float_as_uint(y);
-  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
-}
-
 // Fused top-k, part stage: the workgroup's part of the row (nkv visible keys
 // starting at key kb, scores in LDS in the tile layout of the scan) keeps its
 // top-min(cap, nkv) entries, written as index-ordered (score, index) pairs in

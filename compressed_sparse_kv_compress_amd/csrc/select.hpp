@@ -35,18 +35,6 @@ constexpr int kSmall = 256;  // a threshold bin with at most this many keys is r
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63; }
 
-// Cross-lane data movement uses DPP (a VALU operand modifier, no LDS round
-// trip): row_shr:n reads lane i-n within a row of 16 lanes; row_bcast:15 and
-// row_bcast:31 read the last lane of the previous row (rows 1, 3) and lane 31
-// (rows 2, 3).  Lanes with no source keep `id`.
-template <int CTRL, int ROWS = 0xf>
-__device__ __forceinline__ uint32_t dpp(uint32_t id, uint32_t v) {
-  return static_cast<uint32_t>(
-      __builtin_amdgcn_update_dpp(static_cast<int>(id), static_cast<int>(v), CTRL, ROWS, 0xf, false));
-}
-constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
-constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
-
 // Inclusive prefix sum over the 64 lanes of a wavefront.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   v += dpp<kRowShr1>(0u, v);
@@ -56,11 +44,6 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   v += dpp<kRowBcast15, 0xa>(0u, v);
   v += dpp<kRowBcast31, 0xc>(0u, v);
   return v;
-}
-
-// Value of lane 63 as a wave-uniform scalar.
-__device__ __forceinline__ uint32_t last_lane(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
 // Wave-uniform max / min / sum over the 64 lanes.

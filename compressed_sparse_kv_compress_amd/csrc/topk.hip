@@ -42,46 +42,78 @@ using Sel = sel::Select<kThreads, kItems>;
 using Filt = sel::Filter<kThreads, kItems, 16>;
 using sel::lane_id;
 using sel::wave_incl_scan;
-constexpr int kStagePitch = kItems + 4;  // a thread's 32 staged scores, then 4 pad words (no bank conflicts)
+
+// A tile of up to 16384 scores staged in LDS: thread t of a THREADS-thread
+// workgroup owns entries t*ITEMS .. t*ITEMS+ITEMS-1, stored with 4 pad words
+// after every ITEMS entries so that the owners' 16-byte reads of their own
+// entries hit distinct bank groups.
+template <int THREADS, int ITEMS>
+struct Tile {
+  static constexpr int kPitch = ITEMS + 4;
+  static constexpr int kFloats = THREADS * kPitch;
+  static __device__ __forceinline__ int pos(int e) { return e + 4 * (e / ITEMS); }
+
+  // Issue the coalesced 16-byte loads of scores [0, n) (entries at and past
+  // n are NaN); store() then puts them into LDS.
+  struct Loads {
+    f32x4 v[ITEMS / 4];
+  };
+  static __device__ __forceinline__ Loads load(const float* src, int n) {
+    Loads r;
+    const int tid = threadIdx.x;
+    const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+#pragma unroll
+    for (int q = 0; q < ITEMS / 4; ++q) {
+      const int e = 4 * (q * THREADS + tid);
+      if (vec && e + 4 <= n) {
+        r.v[q] = *reinterpret_cast<const f32x4*>(src + e);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float t = src[e + u < n ? e + u : 0];
+          r.v[q][u] = e + u < n ? t : __builtin_nanf("");
+        }
+      }
+    }
+    return r;
+  }
+  // Store the loads, barrier, and read this thread's own entries into x.
+  static __device__ __forceinline__ void store(const Loads& r, float* stage, float (&x)[ITEMS]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < ITEMS / 4; ++q) *reinterpret_cast<f32x4*>(stage + pos(4 * (q * THREADS + tid))) = r.v[q];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < ITEMS / 4; ++q) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stage + tid * kPitch + 4 * q);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[4 * q + u] = v[u];
+    }
+  }
+};
+using PartTile = Tile<kThreads, kItems>;
 
 struct Shared {
   Filt::Shared fs;
   int32_t si[kStage];  // staged output: entry and score
   float sv[kStage];
-  alignas(16) float stage[kThreads * kStagePitch];  // the tile's scores, entry e at e + 4 * (e / 32)
+  alignas(16) float stage[PartTile::kFloats];
 };
 
-__device__ __forceinline__ int stage_pos(int e) { return e + 4 * (e / kItems); }
-
-// Scores [0, n) of a tile into LDS with coalesced 16-byte loads (entries at
-// and past n read as NaN), then thread t's entries t*32 .. t*32+31 into x.
-// Ends with the barrier that makes the staged tile visible.
-__device__ __forceinline__ void stage_tile(const float* src, int n, float* stage, float (&x)[kItems]) {
-  const int tid = threadIdx.x;
-  const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
-#pragma unroll
-  for (int r = 0; r < kItems / 4; ++r) {
-    const int e = 4 * (r * kThreads + tid);
-    f32x4 v;
-    if (vec && e + 4 <= n) {
-      v = *reinterpret_cast<const f32x4*>(src + e);
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float t = src[e + u < n ? e + u : 0];
-        v[u] = e + u < n ? t : __builtin_nanf("");
-      }
-    }
-    *reinterpret_cast<f32x4*>(stage + stage_pos(e)) = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < kItems / 4; ++q) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(stage + tid * kStagePitch + 4 * q);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) x[4 * q + u] = v[u];
-  }
-}
+// The merge: 512 threads, 32 candidate slots each (1024 x 16 measured slower:
+// more waves per barrier, no less latency per phase).
+constexpr int kMThreads = 512;
+constexpr int kMItems = 32;
+static_assert(kMThreads * kMItems == kPart, "merge tile");
+using MergeTile = Tile<kMThreads, kMItems>;
+using MFilt = sel::Filter<kMThreads, kMItems, 16>;
+struct MShared {
+  MFilt::Shared fs;
+  int32_t si[kStage];
+  float sv[kStage];
+  alignas(16) float stage[MergeTile::kFloats];
+  int wtot[kMThreads / 64];
+};
 
 __device__ __forceinline__ int64_t row_visible(const TopkArgs& a, int64_t row) {
   const int64_t tpos = a.n_ctx - a.T + row % a.T;
@@ -114,11 +146,11 @@ __global__ __launch_bounds__(kThreads) void topk_part_kernel(TopkArgs a, int64_t
   Filt::zero(sh.fs);
   const float* s = a.score + lrow * a.ld + base;
   float v[kItems];
-  stage_tile(s, static_cast<int>(cnt), sh.stage, v);
+  PartTile::store(PartTile::load(s, static_cast<int>(cnt)), sh.stage, v);
   const int i0 = tid * kItems;  // this thread's entries i0 .. i0+31 of the part
   if (cnt <= cap) {  // the whole part is kept; slots past it hold NaN
     for (int64_t i = tid; i < cap; i += kThreads) {
-      const float t = sh.stage[stage_pos(static_cast<int>(i < kPart ? i : 0))];
+      const float t = sh.stage[PartTile::pos(static_cast<int>(i < kPart ? i : 0))];
       ov[i] = i < cnt ? t : __builtin_nanf("");
       if (i < cnt) oi[i] = static_cast<int32_t>(base + i);
     }
@@ -128,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void topk_part_kernel(TopkArgs a, int64_t
   float vmin, vmax;
   Filt::block_range(v, sh.fs, &vmin, &vmax);
   const uint32_t ncnt = static_cast<uint32_t>(cnt), ucap = static_cast<uint32_t>(cap);
-  auto src = [&](uint32_t e) { return sh.stage[stage_pos(static_cast<int>(e))]; };
+  auto src = [&](uint32_t e) { return sh.stage[PartTile::pos(static_cast<int>(e))]; };
   if (cap <= kStage) {  // stage the kept entries in LDS, then store them coalesced
     Filt::run(
         v, src, ncnt, ucap, vmin, vmax, sh.fs,
@@ -138,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void topk_part_kernel(TopkArgs a, int64_t
         },
         [&](int j, uint32_t pos) {
           sh.si[pos] = i0 + j;
-          sh.sv[pos] = sh.stage[stage_pos(i0 + j)];
+          sh.sv[pos] = sh.stage[PartTile::pos(i0 + j)];
         });
     for (int i = tid; i < cap; i += kThreads) {
       ov[i] = sh.sv[i];
@@ -152,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void topk_part_kernel(TopkArgs a, int64_t
           oi[pos] = static_cast<int32_t>(base + e);
         },
         [&](int j, uint32_t pos) {
-          ov[pos] = sh.stage[stage_pos(i0 + j)];
+          ov[pos] = sh.stage[PartTile::pos(i0 + j)];
           oi[pos] = static_cast<int32_t>(base + i0 + j);
         });
   }
@@ -167,7 +199,7 @@ __device__ __forceinline__ bool merge_trivial(const TopkArgs& a, int64_t lrow) {
   int32_t* o = a.idx + lrow * a.k;
   float* os = a.out_score ? a.out_score + lrow * a.k : nullptr;
   const float* s = a.score + lrow * a.ld;
-  for (int64_t i = threadIdx.x; i < a.k; i += kThreads) {
+  for (int64_t i = threadIdx.x; i < a.k; i += blockDim.x) {
     o[i] = i < nv ? static_cast<int32_t>(i) : -1;
     if (os) os[i] = i < nv ? s[i] : -INFINITY;
   }
@@ -177,10 +209,9 @@ __device__ __forceinline__ bool merge_trivial(const TopkArgs& a, int64_t lrow) {
 // Fast merge: nparts * cap <= 16384 slots and nparts <= 256.  The candidate
 // values are staged in LDS with coalesced loads and thread t holds slots
 // 32t .. 32t+31; slots without a candidate hold NaN.
-__global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a, int nparts, int cap, const float* cval,
-                                                              const int32_t* cidx, const int32_t* ccnt, bool fused) {
-  __shared__ Shared sh;
-  __shared__ int wtot[kThreads / 64];
+__global__ __launch_bounds__(kMThreads) void topk_merge_kernel(TopkArgs a, int nparts, int cap, const float* cval,
+                                                               const int32_t* cidx, const int32_t* ccnt, bool fused) {
+  __shared__ MShared sh;
   const int64_t lrow = blockIdx.x;
   if (!fused && merge_trivial(a, lrow)) return;
   int32_t* o = a.idx + lrow * a.k;
@@ -190,35 +221,35 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a, int np
   const float* rv = cval + lrow * ns;
   const int32_t* ri = cidx + lrow * ns;
   const int32_t* rc = ccnt + lrow * nparts;
-  Filt::zero(sh.fs);
-  static_assert(kMaxMergeParts <= kThreads, "one part count per thread");
-  int pc = tid < nparts ? rc[tid] : 0;
-  pc = static_cast<int>(sel::wave_sum(static_cast<uint32_t>(pc)));
-  if (lane_id() == 0) wtot[tid >> 6] = pc;
-  __syncthreads();
-  int total = 0;  // valid candidates of the row
-#pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) total += wtot[w];
   // Candidate slots past their part's count hold NaN (written so by the part
   // stage), as does everything past the last part: no validity test here.
-  float v[kItems];
-  stage_tile(rv, ns, sh.stage, v);
-  const int s0 = tid * kItems;
+  // The candidate loads go out first; the part counts are summed meanwhile.
+  const MergeTile::Loads ld = MergeTile::load(rv, ns);
+  MFilt::zero(sh.fs);
+  static_assert(kMaxMergeParts <= kMThreads, "one part count per thread");
+  const int pc = static_cast<int>(sel::wave_sum(static_cast<uint32_t>(tid < nparts ? rc[tid] : 0)));
+  if (lane_id() == 0) sh.wtot[tid >> 6] = pc;
+  float v[kMItems];
+  MergeTile::store(ld, sh.stage, v);  // its barrier also publishes wtot
+  int total = 0;  // valid candidates of the row
+#pragma unroll
+  for (int w = 0; w < kMThreads / 64; ++w) total += sh.wtot[w];
+  const int s0 = tid * kMItems;
   if (total <= a.k) {  // every valid candidate is kept, in slot order; -1 padding after them
-    for (int64_t i = total + tid; i < a.k; i += kThreads) {
+    for (int64_t i = total + tid; i < a.k; i += kMThreads) {
       o[i] = -1;
       if (os) os[i] = -INFINITY;
     }
     uint32_t c = 0;
 #pragma unroll
-    for (int j = 0; j < kItems; ++j) c += v[j] == v[j];
+    for (int j = 0; j < kMItems; ++j) c += v[j] == v[j];
     const uint32_t incl = wave_incl_scan(c);
-    if (lane_id() == 63) sh.fs.core.wsum[tid >> 6] = incl;  // wtot may still be read
+    if (lane_id() == 63) sh.fs.core.wsum[tid >> 6] = incl;
     __syncthreads();
     uint32_t pos = incl - c;
     for (int w = 0; w < (tid >> 6); ++w) pos += sh.fs.core.wsum[w];
 #pragma unroll
-    for (int j = 0; j < kItems; ++j)
+    for (int j = 0; j < kMItems; ++j)
       if (v[j] == v[j]) {
         o[pos] = ri[s0 + j];
         if (os) os[pos] = v[j];
@@ -228,10 +259,10 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a, int np
   }
   const uint32_t uk = static_cast<uint32_t>(a.k);
   float vmin, vmax;
-  Filt::block_range(v, sh.fs, &vmin, &vmax);
-  auto src = [&](uint32_t e) { return sh.stage[stage_pos(static_cast<int>(e))]; };
+  MFilt::block_range(v, sh.fs, &vmin, &vmax);
+  auto src = [&](uint32_t e) { return sh.stage[MergeTile::pos(static_cast<int>(e))]; };
   if (a.k <= kStage) {  // stage the kept candidates in LDS, then store coalesced
-    Filt::run(
+    MFilt::run(
         v, src, static_cast<uint32_t>(total), uk, vmin, vmax, sh.fs,
         [&](uint32_t pos, float val, uint32_t e) {
           sh.si[pos] = static_cast<int32_t>(e);
@@ -239,14 +270,14 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a, int np
         },
         [&](int j, uint32_t pos) {
           sh.si[pos] = s0 + j;
-          sh.sv[pos] = sh.stage[stage_pos(s0 + j)];
+          sh.sv[pos] = sh.stage[MergeTile::pos(s0 + j)];
         });
-    for (int i = tid; i < a.k; i += kThreads) {
+    for (int i = tid; i < a.k; i += kMThreads) {
       o[i] = ri[sh.si[i]];
       if (os) os[i] = sh.sv[i];
     }
   } else {
-    Filt::run(
+    MFilt::run(
         v, src, static_cast<uint32_t>(total), uk, vmin, vmax, sh.fs,
         [&](uint32_t pos, float val, uint32_t e) {
           o[pos] = ri[e];
@@ -254,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a, int np
         },
         [&](int j, uint32_t pos) {
           o[pos] = ri[s0 + j];
-          if (os) os[pos] = sh.stage[stage_pos(s0 + j)];
+          if (os) os[pos] = sh.stage[MergeTile::pos(s0 + j)];
         });
   }
 }
@@ -371,7 +402,7 @@ hipError_t launch_topk_merge(const TopkArgs& a, int64_t np, int64_t cap, const f
                              const int32_t* ccnt, bool fused, hipStream_t s) {
   if (a.nrows == 0 || a.k == 0) return hipSuccess;
   if (np * cap <= kPart && np <= kMaxMergeParts) {
-    hipLaunchKernelGGL(topk_merge_kernel, dim3(static_cast<uint32_t>(a.nrows)), dim3(kThreads), 0, s, a,
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(static_cast<uint32_t>(a.nrows)), dim3(kMThreads), 0, s, a,
                        static_cast<int>(np), static_cast<int>(cap), cval, cidx, ccnt, fused);
   } else {
     if (fused) return hipErrorInvalidValue;  // the fused path only takes the fast merge
