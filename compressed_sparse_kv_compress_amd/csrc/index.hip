@@ -102,8 +102,10 @@ __device__ __forceinline__ void dma16(const void* g, const uint8_t* lds) {
 using PartSel = sel::Filter<64 * kWaves, 64, 24>;
 constexpr int kPartKeys = 64 * kWaves * 64;  // 16384 >= 4 * kMaxKeysPerWave
 constexpr int kCandStage = 2048;             // largest cap staged in LDS
+constexpr int kListStage = 1024;             // largest compact list staged in LDS
 static_assert(4 * kMaxKeysPerWave <= kPartKeys, "a part fits the selection tile");
-static_assert(sizeof(PartSel::Shared) + kCandStage * 8 <= kWaves * kDepth * kTileBytes, "selection state fits the ring");
+static_assert(sizeof(PartSel::Shared) + kCandStage * 8 + kListStage * 8 <= kWaves * kDepth * kTileBytes,
+              "selection state fits the ring");
 
 // Position of key c (0..15) of a wavefront's tile `it` in its score list: the
 // four 4-key chunks of a tile are rotated by the tile number, so that 16 lanes
@@ -129,12 +131,21 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
       ov[o] = o < nkv ? part_score(sbuf, o) : __builtin_nanf("");
       if (o < nkv) oi[o] = static_cast<int32_t>(kb + o);
     }
-    if (tid == 0) co.ccnt[slot] = nkv;
+    if (tid == 0) {
+      co.ccnt[slot] = nkv;
+      if (co.lval) {  // no compact list: an empty part contributes nothing, a short one sends the merge to the full lists
+        co.lcnt[slot] = nkv == 0 ? 0 : -1;
+        co.lthr[slot] = -INFINITY;
+      }
+    }
     return;
   }
   PartSel::Shared& ss = *reinterpret_cast<PartSel::Shared*>(scratch);
   int32_t* si = reinterpret_cast<int32_t*>(scratch + sizeof(PartSel::Shared));
   float* sv = reinterpret_cast<float*>(si + kCandStage);
+  int32_t* li = reinterpret_cast<int32_t*>(sv + kCandStage);
+  float* lv = reinterpret_cast<float*>(li + kListStage);
+  const int lcap = static_cast<int>(co.lcap);  // <= kListStage (4 or more parts, 4096 entries in all)
   PartSel::zero(ss);
   // Thread t holds entries 64t .. 64t+63 of the part: tiles 4t .. 4t+3, i.e.
   // tile t of each wavefront's list, 16 consecutive scores each; entries past
@@ -154,10 +165,11 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
   for (int j = 0; j < 64; ++j) x[j] = o0 + j < nkv ? x[j] : __builtin_nanf("");
   float vmin, vmax;
   PartSel::block_range(x, ss, &vmin, &vmax);
-  PartSel::run(
+  float thr2 = -INFINITY;
+  uint32_t cnt2 = 0;
+  PartSel::run2(
       x, [&](uint32_t e) { return part_score(sbuf, static_cast<int>(e) < nkv ? static_cast<int>(e) : 0); },
-      static_cast<uint32_t>(nkv),
-      static_cast<uint32_t>(cap), vmin, vmax, ss,
+      static_cast<uint32_t>(nkv), static_cast<uint32_t>(cap), vmin, vmax, ss,
       [&](uint32_t pos, float v, uint32_t e) {
         si[pos] = static_cast<int32_t>(e);
         sv[pos] = v;
@@ -165,10 +177,31 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
       [&](int j, uint32_t pos) {
         si[pos] = o0 + j;
         sv[pos] = part_score(sbuf, o0 + j);
-      });
+      },
+      co.lval ? static_cast<uint32_t>(co.lrank) : 0u,
+      [&](uint32_t pos, float v, uint32_t e) {
+        if (pos < static_cast<uint32_t>(lcap)) {
+          li[pos] = static_cast<int32_t>(e);
+          lv[pos] = v;
+        }
+      },
+      &thr2, &cnt2);
   for (int i = tid; i < cap; i += 64 * kWaves) {
     ov[i] = sv[i];
     oi[i] = static_cast<int32_t>(kb + si[i]);
+  }
+  if (co.lval) {
+    const bool fits = cnt2 <= static_cast<uint32_t>(lcap);
+    if (fits) {
+      for (int i = tid; i < static_cast<int>(cnt2); i += 64 * kWaves) {
+        co.lval[slot * co.lcap + i] = lv[i];
+        co.lidx[slot * co.lcap + i] = static_cast<int32_t>(kb + li[i]);
+      }
+    }
+    if (tid == 0) {
+      co.lcnt[slot] = fits ? static_cast<int32_t>(cnt2) : -1;
+      co.lthr[slot] = thr2;
+    }
   }
   if (tid == 0) co.ccnt[slot] = cap;
 }
@@ -494,10 +527,15 @@ bool index_topk_fusable(int64_t nrows, int64_t L, int64_t HI, int64_t dI, int64_
   return parts <= 256 && parts * k <= 16384;
 }
 
+// Workspace of the fused path: per (row, part) the top-k candidates (8 B
+// each) and their count, then the compact lists (8 B per entry) with their
+// count and threshold.
 size_t index_topk_fused_ws_bytes(int64_t nrows, int64_t L, int64_t k) {
-  int64_t parts, per_wave;
+  int64_t parts, per_wave, lrank, lcap;
   index_plan(nrows, L, &parts, &per_wave);
-  const size_t b = static_cast<size_t>(nrows) * parts * (static_cast<size_t>(k) * 8 + 4);
+  compact_list_plan(parts, k, &lrank, &lcap);
+  const size_t units = static_cast<size_t>(nrows) * parts;
+  const size_t b = units * (static_cast<size_t>(k) * 8 + 4) + units * (static_cast<size_t>(lcap) * 8 + 8);
   return (b + 255) / 256 * 256;
 }
 
@@ -505,14 +543,22 @@ hipError_t launch_index_topk_fused(const IndexScoreArgs& a, const TopkArgs& t, v
   if (a.nrows == 0) return hipSuccess;
   int64_t parts, per_wave;
   index_plan(a.nrows, a.L, &parts, &per_wave);
+  const int64_t units = a.nrows * parts;
   IndexCandidates co;
   co.cap = t.k;
   co.cval = static_cast<float*>(ws);
-  co.cidx = reinterpret_cast<int32_t*>(co.cval + a.nrows * parts * t.k);
-  co.ccnt = co.cidx + a.nrows * parts * t.k;
+  co.cidx = reinterpret_cast<int32_t*>(co.cval + units * t.k);
+  co.ccnt = co.cidx + units * t.k;
+  compact_list_plan(parts, t.k, &co.lrank, &co.lcap);
+  if (co.lrank > 0) {
+    co.lval = reinterpret_cast<float*>(co.ccnt + units);
+    co.lidx = reinterpret_cast<int32_t*>(co.lval + units * co.lcap);
+    co.lcnt = co.lidx + units * co.lcap;
+    co.lthr = reinterpret_cast<float*>(co.lcnt + units);
+  }
   const hipError_t e = launch_stream<true>(a, co, s);
   if (e != hipSuccess) return e;
-  return launch_topk_merge(t, parts, t.k, co.cval, co.cidx, co.ccnt, true, s);
+  return launch_topk_merge(t, parts, co, true, s);
 }
 
 bool index_shape_supported(int64_t HI, int64_t dI, bool bf16) {

@@ -30,12 +30,23 @@ struct IndexScoreArgs {
 hipError_t launch_index_score(const IndexScoreArgs& a, bool bf16, hipStream_t s);
 
 // Per-part top-k candidates: part p of row r keeps ccnt[r][p] <= cap
-// (score, index) pairs in index order at [r][p][0 ..].
+// (score, index) pairs in index order at [r][p][0 ..]; slots past them hold
+// NaN scores.  Optionally (lval != nullptr) a compact list per part: at
+// least its lrank largest scores and every score >= the smallest listed one,
+// lthr[r][p], in index order, lcnt[r][p] <= lcap of them; lcnt = -1 when
+// there is no list (it would be longer, the part has at most cap entries, or
+// its selection took the radix path): then the merge reads the full
+// candidates.
 struct IndexCandidates {
   float* cval;    // [rows][parts][cap]
   int32_t* cidx;  // [rows][parts][cap]
   int32_t* ccnt;  // [rows][parts]
   int64_t cap;
+  float* lval = nullptr;    // [rows][parts][lcap]
+  int32_t* lidx = nullptr;  // [rows][parts][lcap]
+  int32_t* lcnt = nullptr;  // [rows][parts]
+  float* lthr = nullptr;    // [rows][parts]
+  int64_t lrank = 0, lcap = 0;
 };
 // Geometry of the streaming indexer (d_I = 128, bf16): key-range parts per
 // row (one workgroup each) and keys per wavefront.
@@ -56,8 +67,20 @@ hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t s);
 // Merge stage alone over part candidates (fast path: nparts * cap <= 16384,
 // nparts <= 256).  fused: the candidates cover every visible entry of rows
 // with at most k of them (there is no score matrix to read).
-hipError_t launch_topk_merge(const TopkArgs& a, int64_t nparts, int64_t cap, const float* cval,
-                             const int32_t* cidx, const int32_t* ccnt, bool fused, hipStream_t s);
+hipError_t launch_topk_merge(const TopkArgs& a, int64_t nparts, const IndexCandidates& c, bool fused, hipStream_t s);
+// Compact-list geometry for nparts parts and top-k: the rank (0: no lists)
+// and the list capacity.  The merge stages at most kMergeUnion list entries.
+constexpr int64_t kMergeUnion = 4096;
+inline void compact_list_plan(int64_t nparts, int64_t k, int64_t* lrank, int64_t* lcap) {
+  const int64_t r = (2 * k + nparts - 1) / nparts;  // the lists hold at least 2k entries in all
+  if (nparts < 4 || 4 * r > k || nparts * 2 * r > kMergeUnion) {
+    *lrank = 0;
+    *lcap = 0;
+    return;
+  }
+  *lrank = r;
+  *lcap = 2 * r;
+}
 
 // Indexer scan fused with the part stage of the top-k (no score matrix): the
 // scan's workgroups select their parts' candidates from LDS, then the merge

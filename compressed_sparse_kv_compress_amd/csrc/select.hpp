@@ -384,6 +384,9 @@ __device__ __forceinline__ float wave_fmax(float v) {
 //      (ballots over one wavefront's lanes);
 //   4. ordered compaction of the survivors: one workgroup scan of per-thread
 //      (greater, equal) counts packed in 16-bit halves.
+// A short list for a second, smaller rank (run2) comes from the same
+// histogram: the survivors of the bins from that rank's bin upwards,
+// compacted in the same scan as the top-sel list (no second ranking).
 // Histograms have kFBins bins, few enough that every wavefront scans them on
 // its own (no broadcast barrier); cross-lane steps use DPP; passes over all
 // scores keep several independent accumulators (one wavefront per SIMD leaves
@@ -409,6 +412,7 @@ struct Filter {
     alignas(16) uint32_t hist2[kFBins];  // survivor histogram
     alignas(16) float ck[kSmall + 64];   // scores of the threshold bin; 64 lane-private dump slots after them
     uint32_t wsum[kWaves];
+    uint32_t wsum2[kWaves];
     float red[2][kWaves];
     uint32_t ncand;
   };
@@ -551,42 +555,6 @@ struct Filter {
     *take = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tt), src));
   }
 
-  // Ordered compaction of the survivors y[0 .. cnt) of every thread (thread
-  // order = entry order): kept are the scores > thr and the first `take`
-  // scores == thr; emit(pos, score, entry).  Ends with a barrier.
-  template <typename Emit>
-  static __device__ __forceinline__ void compact_survivors(const float (&y)[SMAX], const uint32_t (&ent)[SMAX],
-                                                           float thr, uint32_t take, Shared& sh, Emit emit) {
-    const int wave = threadIdx.x >> 6;
-    SMask gtm = 0, eqm = 0;
-#pragma unroll
-    for (int k = 0; k < SMAX; ++k) {
-      gtm |= static_cast<SMask>(y[k] > thr) << k;
-      eqm |= static_cast<SMask>(y[k] == thr) << k;
-    }
-    const uint32_t packed = (Small::popc(eqm) << 16) | Small::popc(gtm);
-    const uint32_t pin = wave_incl_scan(packed);
-    if (lane_id() == 63) sh.core.wsum[wave] = pin;
-    __syncthreads();
-    uint32_t excl = pin - packed;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) excl += w < wave ? sh.core.wsum[w] : 0u;
-    const uint32_t gt0 = excl & 0xffffu, eq0 = excl >> 16;
-    uint32_t keq = take > eq0 ? take - eq0 : 0u;
-    SMask km = gtm, em = eqm;
-    while (keq > 0 && em) {
-      const SMask lb = em & (0 - em);
-      km |= lb;
-      em ^= lb;
-      --keq;
-    }
-    uint32_t slot = gt0 + (eq0 < take ? eq0 : take);
-#pragma unroll
-    for (int k = 0; k < SMAX; ++k)
-      if (Small::bit(km, k)) emit(slot++, y[k], ent[k]);
-    __syncthreads();
-  }
-
   // Keeps the sel largest valid scores (1 <= sel <= nvalid = valid scores of
   // the workgroup, vmin / vmax their min and max).  Kept items get slots in
   // entry order: emit(pos, score, entry) on the sampled path, emit_item(j,
@@ -595,6 +563,23 @@ struct Filter {
   template <typename Src, typename Emit, typename EmitItem>
   static __device__ __forceinline__ void run(const float (&x)[ITEMS], Src src, uint32_t nvalid, uint32_t sel,
                                              float vmin, float vmax, Shared& sh, Emit emit, EmitItem emit_item) {
+    float t2;
+    uint32_t c2;
+    run2(x, src, nvalid, sel, vmin, vmax, sh, emit, emit_item, 0u, [](uint32_t, float, uint32_t) {}, &t2, &c2);
+  }
+
+  // run() plus a short list for a second rank sel2 (1 <= sel2 <= sel; 0:
+  // none): on the sampled path every survivor in the survivor-histogram bins
+  // from the one holding the sel2-th largest score upwards (so at least sel2
+  // scores) is emitted again, in entry order, through emit2(pos, score,
+  // entry); *cnt2 gets their number and *thr2 their smallest score, and since
+  // bins are monotone in the score, every valid score >= *thr2 is in the
+  // list.  On the radix paths no list is made (*cnt2 = 0xffffffff).  Ends
+  // with a barrier.
+  template <typename Src, typename Emit, typename EmitItem, typename Emit2>
+  static __device__ __forceinline__ void run2(const float (&x)[ITEMS], Src src, uint32_t nvalid, uint32_t sel,
+                                              float vmin, float vmax, Shared& sh, Emit emit, EmitItem emit_item,
+                                              uint32_t sel2, Emit2 emit2, float* thr2, uint32_t* cnt2) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const uint32_t lane = lane_id();
@@ -654,6 +639,8 @@ struct Filter {
       uint32_t thr, take, bg = 0, be = 0;
       Big::radix_select(keys, vm, sel, sh.core, &thr, &take);
       Big::compact(keys, vm, thr, take, sh.core, &bg, &be, emit_item);
+      *thr2 = 0.f;
+      *cnt2 = 0xffffffffu;  // no short list on this path
       return;
     }
     // This thread's survivors, in entry order, into registers (scores read
@@ -675,8 +662,11 @@ struct Filter {
     const float range2 = vmax - t0;
     const float scale2 = static_cast<float>(kFBins) / range2;
     const bool spread = range2 > 0.f && __builtin_isfinite(range2) && __builtin_isfinite(scale2);  // uniform
+    const bool two = sel2 != 0;                                                                   // uniform
     int bn[SMAX];
-    uint32_t cb2 = 0, ab2 = 0, b2 = 0;
+#pragma unroll
+    for (int k = 0; k < SMAX; ++k) bn[k] = -1;
+    uint32_t cb2 = 0, ab2 = 0, b2 = 0, b3 = 0;
     if (spread) {
 #pragma unroll
       for (int k = 0; k < SMAX; ++k) {
@@ -685,12 +675,14 @@ struct Filter {
         if (bn[k] >= 0) atomicAdd(&sh.hist2[bn[k]], 1u);
       }
       __syncthreads();
-      uint32_t n2;
+      uint32_t n2, ab3, cb3;
       hist_find(sh.hist2, [&](uint32_t) { return sel; }, &n2, &b2, &ab2, &cb2);
+      if (two) hist_find(sh.hist2, [&](uint32_t) { return sel2; }, &n2, &b3, &ab3, &cb3);
     }
     float thr;
     uint32_t take;
-    if (!spread || cb2 > static_cast<uint32_t>(kSmall)) {
+    const bool crowded = !spread || cb2 > static_cast<uint32_t>(kSmall);  // uniform
+    if (crowded) {
       // One value or a crowded bin: radix passes over the survivors' keys.
       uint32_t k2[SMAX];
       SMask v2 = 0;
@@ -720,8 +712,64 @@ struct Filter {
       __syncthreads();
       rank_small(sh.ck, cb2, sel - ab2, &thr, &take);
     }
-    compact_survivors(y, ent, thr, take, sh, emit);
+    // Ordered compaction of the survivors for both lists with one barrier:
+    // (greater, equal) counts packed in 16-bit halves for the top-sel list,
+    // the count in bins >= b3 for the short one (with their smallest score),
+    // two wavefront scans.
+    const bool list2 = two && !crowded;  // uniform
+    SMask gtm = 0, eqm = 0, gm2 = 0;
+    float lo2 = __builtin_inff();
+#pragma unroll
+    for (int k = 0; k < SMAX; ++k) {
+      gtm |= static_cast<SMask>(y[k] > thr) << k;
+      eqm |= static_cast<SMask>(y[k] == thr) << k;
+      const bool in2 = list2 && bn[k] >= static_cast<int>(b3);
+      gm2 |= static_cast<SMask>(in2) << k;
+      lo2 = in2 ? __builtin_fminf(lo2, y[k]) : lo2;
+    }
+    const uint32_t packed1 = (Small::popc(eqm) << 16) | Small::popc(gtm);
+    const uint32_t q2 = Small::popc(gm2);
+    const uint32_t pin = wave_incl_scan(packed1);
+    const uint32_t qin = wave_incl_scan(q2);
+    const float lo2w = wave_fmin(lo2);
+    if (lane == 63) {
+      sh.core.wsum[wave] = pin;
+      sh.wsum2[wave] = qin;
+      sh.red[0][wave] = lo2w;
+    }
+    __syncthreads();
+    uint32_t excl = pin - packed1, qpos = qin - q2, qtot = 0;
+    float tv2 = __builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      excl += w < wave ? sh.core.wsum[w] : 0u;
+      qpos += w < wave ? sh.wsum2[w] : 0u;
+      qtot += sh.wsum2[w];
+      tv2 = __builtin_fminf(tv2, sh.red[0][w]);
+    }
+    const uint32_t gt0 = excl & 0xffffu, eq0 = excl >> 16;
+    uint32_t keq = take > eq0 ? take - eq0 : 0u;
+    SMask km = gtm, em = eqm;
+    while (keq > 0 && em) {
+      const SMask lb = em & (0 - em);
+      km |= lb;
+      em ^= lb;
+      --keq;
+    }
+    uint32_t slot = gt0 + (eq0 < take ? eq0 : take);
+#pragma unroll
+    for (int k = 0; k < SMAX; ++k)
+      if (Small::bit(km, k)) emit(slot++, y[k], ent[k]);
+    if (two) {
+#pragma unroll
+      for (int k = 0; k < SMAX; ++k)
+        if (Small::bit(gm2, k)) emit2(qpos++, y[k], ent[k]);
+    }
+    __syncthreads();
+    *thr2 = tv2;
+    *cnt2 = list2 ? qtot : 0xffffffffu;
   }
+
 };
 
 }  // namespace sel

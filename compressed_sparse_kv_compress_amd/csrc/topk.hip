@@ -206,21 +206,131 @@ __device__ __forceinline__ bool merge_trivial(const TopkArgs& a, int64_t lrow) {
   return true;
 }
 
+// Merge from the compact lists when they are enough.  Every part's list
+// holds all its candidates >= V_p (its smallest listed score, at most its
+// lrank-th largest); U is their union, in index order.  With theta_U the k-th largest
+// of U (a subset of the row, so theta_U <= the row's k-th largest theta), an
+// entry of the row's top-k has a score >= theta >= theta_U; when every V_p <=
+// theta_U that score is >= its part's V_p, so the entry is in U and the
+// top-k of U is the row's.  Returns false (nothing written) when a list is
+// missing or too long, U has fewer than k entries, or some V_p > theta_U.
+constexpr int kUItems = kMergeUnion / kMThreads;  // 8
+using USel = sel::Select<kMThreads, kUItems>;
+static_assert(sizeof(float) * kMergeUnion * 2 <= sizeof(float) * MergeTile::kFloats, "the union fits the stage");
+
+__device__ __forceinline__ bool merge_compact(const TopkArgs& a, int64_t lrow, int nparts, const IndexCandidates& c,
+                                              MShared& sh, int32_t* o, float* os) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  // The staging below gives each list kMThreads / nparts threads of
+  // kMergeUnion / kMThreads entries each.
+  if (c.lcap > static_cast<int64_t>(kMergeUnion / kMThreads) * (kMThreads / nparts)) return false;
+  const int64_t unit0 = lrow * nparts;
+  const int lc = tid < nparts ? c.lcnt[unit0 + tid] : 0;
+  const float lt = tid < nparts ? c.lthr[unit0 + tid] : -INFINITY;
+  // per wave: any missing list, the lists' total, the largest V_p
+  const uint32_t neg = static_cast<uint32_t>(__popcll(__ballot(lc < 0)));
+  const uint32_t cnt = static_cast<uint32_t>(lc > 0 ? lc : 0);
+  const uint32_t incl = wave_incl_scan(cnt);
+  const float vmax_w = wave_max(lt);
+  uint32_t* uoff = reinterpret_cast<uint32_t*>(sh.si);  // list offsets in U (<= 256 parts)
+  if (sel::lane_id() == 63) {
+    sh.fs.wsum[wave] = incl;
+    sh.fs.red[0][wave] = vmax_w;
+    sh.fs.core.red[0][wave] = neg;
+  }
+  __syncthreads();
+  uint32_t before = 0, total = 0, nneg = 0;
+  float vmax = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kMThreads / 64; ++w) {
+    before += w < wave ? sh.fs.wsum[w] : 0u;
+    total += sh.fs.wsum[w];
+    nneg += sh.fs.core.red[0][w];
+    vmax = fmaxf(vmax, sh.fs.red[0][w]);
+  }
+  if (nneg != 0 || total < static_cast<uint32_t>(a.k) || total > static_cast<uint32_t>(kMergeUnion)) {
+    __syncthreads();  // the LDS read above is done before the full merge reuses it
+    return false;
+  }
+  if (tid < nparts) uoff[tid] = before + incl - cnt;
+  __syncthreads();
+  // U into LDS (values, then indices): kMThreads / nparts threads per list,
+  // all loads issued before any store (one memory round trip).
+  float* uval = sh.stage;
+  int32_t* uidx = reinterpret_cast<int32_t*>(sh.stage + kMergeUnion);
+  {
+    constexpr int kR = kMergeUnion / kMThreads;  // entries per thread: lcap * nparts <= kMergeUnion
+    const int tpp = kMThreads / nparts;          // >= 2 (nparts <= 256)
+    const int p = tid / tpp, li = tid % tpp;
+    const int n = p < nparts ? c.lcnt[unit0 + p] : 0;
+    const float* lvp = c.lval + (unit0 + (p < nparts ? p : 0)) * c.lcap;
+    const int32_t* lip = c.lidx + (unit0 + (p < nparts ? p : 0)) * c.lcap;
+    float tv[kR];
+    int32_t tx[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int i = li + r * tpp;
+      const int ic = i < n ? i : 0;  // in range: lcap >= 1
+      tv[r] = lvp[ic];
+      tx[r] = lip[ic];
+    }
+    const uint32_t off = p < nparts ? uoff[p] : 0u;
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int i = li + r * tpp;
+      if (i < n) {
+        uval[off + i] = tv[r];
+        uidx[off + i] = tx[r];
+      }
+    }
+  }
+  USel::zero(sh.fs.core);
+  __syncthreads();
+  uint32_t keys[kUItems];
+  uint32_t vm = 0;
+#pragma unroll
+  for (int j = 0; j < kUItems; ++j) {
+    const uint32_t u = static_cast<uint32_t>(tid * kUItems + j);
+    keys[j] = float_key(uval[u < total ? u : 0]);
+    vm |= static_cast<uint32_t>(u < total) << j;
+  }
+  uint32_t thr, take;
+  USel::radix_select(keys, vm, static_cast<uint32_t>(a.k), sh.fs.core, &thr, &take);
+  if (vmax > key_float(thr)) {  // uniform: some part's list may miss row top-k entries
+    __syncthreads();
+    return false;
+  }
+  uint32_t bg = 0, be = 0;
+  USel::compact(keys, vm, thr, take, sh.fs.core, &bg, &be, [&](int j, uint32_t pos) {
+    const int u = tid * kUItems + j;
+    sh.sv[pos] = uval[u];
+    sh.si[pos + kStage / 2] = uidx[u];  // past the list offsets
+  });
+  for (int i = tid; i < a.k; i += kMThreads) {
+    o[i] = sh.si[i + kStage / 2];
+    if (os) os[i] = sh.sv[i];
+  }
+  return true;
+}
+
 // Fast merge: nparts * cap <= 16384 slots and nparts <= 256.  The candidate
 // values are staged in LDS with coalesced loads and thread t holds slots
 // 32t .. 32t+31; slots without a candidate hold NaN.
-__global__ __launch_bounds__(kMThreads) void topk_merge_kernel(TopkArgs a, int nparts, int cap, const float* cval,
-                                                               const int32_t* cidx, const int32_t* ccnt, bool fused) {
+__global__ __launch_bounds__(kMThreads) void topk_merge_kernel(TopkArgs a, int nparts, IndexCandidates c,
+                                                               bool fused) {
   __shared__ MShared sh;
   const int64_t lrow = blockIdx.x;
   if (!fused && merge_trivial(a, lrow)) return;
   int32_t* o = a.idx + lrow * a.k;
   float* os = a.out_score ? a.out_score + lrow * a.k : nullptr;
   const int tid = threadIdx.x;
+  const int cap = static_cast<int>(c.cap);
   const int ns = nparts * cap;
-  const float* rv = cval + lrow * ns;
-  const int32_t* ri = cidx + lrow * ns;
-  const int32_t* rc = ccnt + lrow * nparts;
+  const float* rv = c.cval + lrow * ns;
+  const int32_t* ri = c.cidx + lrow * ns;
+  const int32_t* rc = c.ccnt + lrow * nparts;
+  if (c.lval && merge_compact(a, lrow, nparts, c, sh, o, os)) return;
   // Candidate slots past their part's count hold NaN (written so by the part
   // stage), as does everything past the last part: no validity test here.
   // The candidate loads go out first; the part counts are summed meanwhile.
@@ -395,19 +505,23 @@ hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t s) {
                      cap, cval, cidx, ccnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_topk_merge(a, np, cap, cval, cidx, ccnt, false, s);
+  IndexCandidates c;
+  c.cval = cval;
+  c.cidx = cidx;
+  c.ccnt = ccnt;
+  c.cap = cap;
+  return launch_topk_merge(a, np, c, false, s);
 }
 
-hipError_t launch_topk_merge(const TopkArgs& a, int64_t np, int64_t cap, const float* cval, const int32_t* cidx,
-                             const int32_t* ccnt, bool fused, hipStream_t s) {
+hipError_t launch_topk_merge(const TopkArgs& a, int64_t np, const IndexCandidates& c, bool fused, hipStream_t s) {
   if (a.nrows == 0 || a.k == 0) return hipSuccess;
-  if (np * cap <= kPart && np <= kMaxMergeParts) {
+  if (np * c.cap <= kPart && np <= kMaxMergeParts) {
     hipLaunchKernelGGL(topk_merge_kernel, dim3(static_cast<uint32_t>(a.nrows)), dim3(kMThreads), 0, s, a,
-                       static_cast<int>(np), static_cast<int>(cap), cval, cidx, ccnt, fused);
+                       static_cast<int>(np), c, fused);
   } else {
     if (fused) return hipErrorInvalidValue;  // the fused path only takes the fast merge
-    hipLaunchKernelGGL(topk_merge_general, dim3(static_cast<uint32_t>(a.nrows)), dim3(kThreads), 0, s, a, np, cap,
-                       cval, cidx, ccnt);
+    hipLaunchKernelGGL(topk_merge_general, dim3(static_cast<uint32_t>(a.nrows)), dim3(kThreads), 0, s, a, np, c.cap,
+                       c.cval, c.cidx, c.ccnt);
   }
   return hipGetLastError();
 }

@@ -206,14 +206,17 @@ def test_index_topk_bit_exact_on_grid_inputs():
 @pytest.mark.parametrize("B,T,L,HI,k,wts,boost", [(16, 1, 250000, 64, 1024, True, 1), (4, 3, 9000, 32, 512, False, 1),
                                                    (2, 2, 700, 64, 1024, True, 1), (4, 16, 60000, 128, 2048, True, 1),
                                                    (2, 8, 30000, 16, 256, False, 1), (4, 1, 250000, 64, 1024, True, 32),
-                                                   (4, 1, 250000, 64, 1024, False, 16)])
+                                                   (4, 1, 250000, 64, 1024, False, 16), (4, 1, 250000, 64, 1024, True, -1),
+                                                   (3, 2, 120000, 64, 512, True, -1)])
 def test_index_topk_single_pass_equals_score_then_select(B, T, L, HI, k, wts, boost):
     """Shapes where the indexer selects its parts' candidates itself (no score
     matrix) give the same indices and scores, bit for bit, as the scores
     written out and selected by the stand-alone top-k (rows with fewer
     visible entries than k are padded alike).  boost > 1: every boost-th key
     row is scaled by 4 (exact in bf16), a periodic structure that misleads a
-    sampled threshold."""
+    sampled threshold; boost = -1: the last sixteenth of the key rows is
+    scaled by 4, so the row's top-k sits in one part (the merge cannot use the
+    parts' short lists and reads the full ones)."""
     dI, m = 128, 4
     n_ctx = m * L
     seed = 40 + L
@@ -222,6 +225,9 @@ def test_index_topk_single_pass_equals_score_then_select(B, T, L, HI, k, wts, bo
     if boost > 1:
         kk[:, ::boost] *= 4
         k_c[:, ::boost] *= 4
+    elif boost == -1:
+        kk[:, L - L // 16:] *= 4
+        k_c[:, L - L // 16:] *= 4
     w = w_c = None
     if wts:
         w, w_c = both((B, T, HI), seed, "w_idx", dtype=torch.float32, scale=HI ** -0.5)
