@@ -166,7 +166,7 @@ class GpuState:
         self.side = torch.cuda.Stream(device=device)  # default priority
         torch.cuda.synchronize()
 
-    def step(self, ev=None, only=None):
+    def step(self, ev=None, only=None, csa_layer=None):
         """One decode step through all layers.
 
         Compression runs on a second stream: its inputs are raw tokens of
@@ -175,14 +175,17 @@ class GpuState:
         token; the HCA refresh is joined (event wait) before that layer's dense
         attention reads it.  ev: optional dict of event lists keyed by call
         name; events bracket calls (all, or the names in `only`) on the stream
-        that runs them."""
+        that runs them; csa_layer: bracket only that CSA layer's calls (every
+        timing event costs a few microseconds of idle GPU between kernels)."""
         csa, st = self.csa, self.st
         main = torch.cuda.current_stream()
         side = self.side
         side.wait_stream(main)
 
-        def mark(name):
+        def mark(name, ci=None):
             if ev is None or (only is not None and name.replace("_end", "") not in only):
+                return
+            if csa_layer is not None and ci != csa_layer:
                 return
             e = torch.cuda.Event(enable_timing=True)
             e.record()
@@ -214,13 +217,15 @@ class GpuState:
                     done.record()
                     joins.append(done)
 
+        ci = 0
         for lay, done in zip(self.layers, joins):
             if lay["kind"] == "csa":
                 m = st.m_csa
-                mark("index_topk")
+                mark("index_topk", ci)
                 csa.csa_index_topk(lay["qi"], lay["ki"], m, st.k, w_idx=lay["wi"], n_ctx=st.n_ctx, idx=lay["idx"],
                                    ws=lay["itk_ws"])
-                mark("index_topk_end")
+                mark("index_topk_end", ci)
+                ci += 1
                 mark("csa_sparse_attn")
                 csa.csa_sparse_attn(lay["q"], lay["kc"], lay["vc"], lay["idx"], kr=lay["kr"], vr=lay["vr"],
                                     W=st.W, sink=lay["sink"], n_ctx=st.n_ctx, out=lay["out"], ws=lay["ws"])
@@ -477,16 +482,18 @@ def main():
     torch.cuda.synchronize()
     print("# warmup done", file=sys.stderr, flush=True)
 
-    # Timed region: K steps; HIP events bracket only the csa_index_topk calls
-    # (the dominant call) on the stream they run on.
+    # Timed region: K steps; HIP events bracket one csa_index_topk call (the
+    # dominant call) per step, on the stream it runs on, taking the CSA layers
+    # in turn.
     ev = {}
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
-    for _ in range(args.steps):
-        state.step(ev, only=("index_topk",))
+    n_csa = st.kinds().count("csa")
+    for i in range(args.steps):
+        state.step(ev, only=("index_topk",), csa_layer=i % n_csa)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0

@@ -585,14 +585,19 @@ int attn_splits(int64_t B, int64_t T, int64_t H, int64_t d, int64_t max_rows, bo
   (void)d;
   if (!bf16) return 1;
   const int64_t base = B * T * (H / kHeadsPerWg);
-#ifndef CSA_ATTN_TARGET
-#define CSA_ATTN_TARGET 256
-#endif
-  const int64_t target = CSA_ATTN_TARGET;  // workgroups wanted per launch (one per CU)
+  const int64_t target = 256;  // workgroups wanted per launch (one per CU)
   int64_t ns = (target + base - 1) / base;
   const int64_t cap = (max_rows + 63) / 64;  // keep >= 64 rows per split
   if (ns > cap) ns = cap;
   if (ns > kAttnMaxSplits) ns = kAttnMaxSplits;
+  // A split costs its number of 32-row stages (each a gather round trip);
+  // for that many stages per split take the fewest splits: fewer partial rows
+  // to write and combine, and fewer workgroups re-reading the query.
+  if (ns > 1) {
+    const int64_t stages = (max_rows + 31) / 32;
+    const int64_t per = (stages + ns - 1) / ns;
+    ns = (stages + per - 1) / per;
+  }
   if (sparse) {  // a split caches at most kMaxIdx row indices
     const int64_t need = (max_rows + kMaxIdx - 1) / kMaxIdx;
     if (ns < need) ns = need;
