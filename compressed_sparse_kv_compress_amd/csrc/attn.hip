@@ -140,25 +140,39 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Direct global -> LDS load of one row piece: lane i's ESZ bytes at g land at
-// LDS byte address lds + ESZ * i (lds wave-uniform, through M0), nontemporal
-// (each row is read once per launch).  Issued as
+// LDS byte address lds + ESZ * i (lds wave-uniform, through M0).  NT marks the
+// load nontemporal: right for decode, where each row is read once per launch
+// (random 1 KiB gathers from HBM measured 6.8 TB/s with it, 6.3 without).  A
+// prefill launch re-reads every compressed row for many queries, and its
+// cache fits the Infinity Cache: there the default policy keeps rows cached
+// (7.3 TB/s against 7.1 for a 143 MB working set).  Issued as
 // inline asm on purpose: the compiler does not then see an asynchronous LDS
 // write, so it adds no "wait for every outstanding load" before each later LDS
 // read (which would drain the prefetch ring); completion is instead awaited
 // explicitly (vmcnt) and published with a barrier.  The instruction writes no
 // registers, and its address registers are read when it issues.
-template <int ESZ>
+template <int ESZ, bool NT>
 __device__ __forceinline__ void dma_row(const char* g, const uint8_t* lds) {
   typedef const uint8_t __attribute__((address_space(3))) * lds_ptr;
   const uint32_t la = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(lds)));
   uint32_t saved;  // M0 is restored, so the compiler's own uses of it are unaffected
-  if constexpr (ESZ == 16)
+  if constexpr (ESZ == 16 && NT)
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
                  : "=&s"(saved)
                  : "v"(g), "s"(la)
                  : "memory");
-  else
+  else if constexpr (ESZ == 16)
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(g), "s"(la)
+                 : "memory");
+  else if constexpr (NT)
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off nt\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(g), "s"(la)
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
                  : "=&s"(saved)
                  : "v"(g), "s"(la)
                  : "memory");
@@ -170,7 +184,7 @@ __device__ __forceinline__ void dma_row(const char* g, const uint8_t* lds) {
 // indices come from the split's index cache with one vector LDS read.  An
 // empty row (past the split's end, or a -1 / out-of-range index) is read from
 // the dummy row and flagged in okrow (K waves only), so its logit is masked.
-template <int D, bool SPARSE>
+template <int D, bool SPARSE, bool NT>
 __device__ __forceinline__ void issue_rows(const char* cbase, const char* rbase, const char* dummy, const int* sidx,
                                            uint8_t* lds, int pitch, int c0, int n_cmp, int r_begin, int r_end,
                                            int win0, int L, int lane, int* okrow) {
@@ -191,7 +205,7 @@ __device__ __forceinline__ void issue_rows(const char* cbase, const char* rbase,
     const char* src = ok ? row : dummy;
 #pragma unroll
     for (int p = 0; p < C::IPR; ++p)
-      dma_row<C::ESZ>(src + p * 64 * C::ESZ + lane * C::ESZ, lds + j * pitch + p * 64 * C::ESZ);
+      dma_row<C::ESZ, NT>(src + p * 64 * C::ESZ + lane * C::ESZ, lds + j * pitch + p * 64 * C::ESZ);
   }
   if (okrow && lane < C::RPW) {
     const int v = c0 + lane;
@@ -215,7 +229,7 @@ __device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
 // operand comes from the LDS transpose load: for 16-lane group g, lanes
 // 4j..4j+3 address row r0+j, 16 dims, and lane c receives dim c of those four
 // rows.  Two waves per SIMD hide each other's LDS and MFMA latency.
-template <int D, bool SPARSE>
+template <int D, bool SPARSE, bool NT>
 __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
   using C = Ring<D>;
   constexpr int KSQ = C::DH / 32;  // k-steps of the wave's half of Q K^T
@@ -268,7 +282,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
   // row flags have three buffers because K(c+2) sets them while stage c still
   // reads its own.
   auto issue = [&](int st) {
-    issue_rows<D, SPARSE>(cbase, rbase, dummy, sidx, ring + (st & 1) * C::STAGE + moff, pitch,
+    issue_rows<D, SPARSE, NT>(cbase, rbase, dummy, sidx, ring + (st & 1) * C::STAGE + moff, pitch,
                           rb0 + st * C::ROWS + row0, n_cmp, rb0, re0, win0, Lc, lane,
                           mat ? nullptr : okf[st % 3] + row0);
   };
@@ -619,10 +633,15 @@ hipError_t launch_attn(const AttnArgs& a, bool sparse, bool bf16, int nsplit, hi
     return hipGetLastError();
   }
   const dim3 grid(static_cast<uint32_t>(a.B * a.T * (a.H / kHeadsPerWg) * nsplit));
-#define CSA_ATTN_LAUNCH(D_)                                                                            \
-  case D_:                                                                                             \
-    if (sparse) hipLaunchKernelGGL((attn_mfma<D_, true>), grid, dim3(64 * kWaves), 0, s, a, nsplit);           \
-    else hipLaunchKernelGGL((attn_mfma<D_, false>), grid, dim3(64 * kWaves), 0, s, a, nsplit);                 \
+  // One query per sequence (decode): every row is read once, nontemporal.
+  // Several (prefill): rows are shared between the queries, cached.
+  const bool once = a.T == 1;
+#define CSA_ATTN_LAUNCH(D_)                                                                                         \
+  case D_:                                                                                                          \
+    if (sparse && once) hipLaunchKernelGGL((attn_mfma<D_, true, true>), grid, dim3(64 * kWaves), 0, s, a, nsplit);   \
+    else if (sparse) hipLaunchKernelGGL((attn_mfma<D_, true, false>), grid, dim3(64 * kWaves), 0, s, a, nsplit);     \
+    else if (once) hipLaunchKernelGGL((attn_mfma<D_, false, true>), grid, dim3(64 * kWaves), 0, s, a, nsplit);       \
+    else hipLaunchKernelGGL((attn_mfma<D_, false, false>), grid, dim3(64 * kWaves), 0, s, a, nsplit);                \
     break;
   switch (a.d) {
     CSA_ATTN_LAUNCH(128)
