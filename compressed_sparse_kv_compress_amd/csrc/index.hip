@@ -104,7 +104,7 @@ constexpr int kPartKeys = 64 * kWaves * 64;  // 16384 >= 4 * kMaxKeysPerWave
 constexpr int kCandStage = 2048;             // largest cap staged in LDS
 constexpr int kListStage = 1024;             // largest compact list staged in LDS
 static_assert(4 * kMaxKeysPerWave <= kPartKeys, "a part fits the selection tile");
-static_assert(sizeof(PartSel::Shared) + kCandStage * 8 + kListStage * 8 <= kWaves * kDepth * kTileBytes,
+static_assert(sizeof(PartSel::Shared) + (kCandStage + 64) * 8 + (kListStage + 64) * 8 <= kWaves * kDepth * kTileBytes,
               "selection state fits the ring");
 
 // Position of key c (0..15) of a wavefront's tile `it` in its score list: the
@@ -142,9 +142,10 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
   }
   PartSel::Shared& ss = *reinterpret_cast<PartSel::Shared*>(scratch);
   int32_t* si = reinterpret_cast<int32_t*>(scratch + sizeof(PartSel::Shared));
-  float* sv = reinterpret_cast<float*>(si + kCandStage);
-  int32_t* li = reinterpret_cast<int32_t*>(sv + kCandStage);
-  float* lv = reinterpret_cast<float*>(li + kListStage);
+  float* sv = reinterpret_cast<float*>(si + kCandStage + 64);  // each array: 64 dump slots at its end
+  int32_t* li = reinterpret_cast<int32_t*>(sv + kCandStage + 64);
+  float* lv = reinterpret_cast<float*>(li + kListStage + 64);
+  const uint32_t lane = threadIdx.x & 63;
   const int lcap = static_cast<int>(co.lcap);  // <= kListStage (4 or more parts, 4096 entries in all)
   PartSel::zero(ss);
   // Thread t holds entries 64t .. 64t+63 of the part: tiles 4t .. 4t+3, i.e.
@@ -171,8 +172,9 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
       x, [&](uint32_t e) { return part_score(sbuf, static_cast<int>(e) < nkv ? static_cast<int>(e) : 0); },
       static_cast<uint32_t>(nkv), static_cast<uint32_t>(cap), vmin, vmax, ss,
       [&](uint32_t pos, float v, uint32_t e) {
-        si[pos] = static_cast<int32_t>(e);
-        sv[pos] = v;
+        const uint32_t p = pos != sel::kNoSlot ? pos : kCandStage + lane;  // lane-private dump slot
+        si[p] = static_cast<int32_t>(e);
+        sv[p] = v;
       },
       [&](int j, uint32_t pos) {
         si[pos] = o0 + j;
@@ -180,10 +182,9 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
       },
       co.lval ? static_cast<uint32_t>(co.lrank) : 0u,
       [&](uint32_t pos, float v, uint32_t e) {
-        if (pos < static_cast<uint32_t>(lcap)) {
-          li[pos] = static_cast<int32_t>(e);
-          lv[pos] = v;
-        }
+        const uint32_t p = pos < static_cast<uint32_t>(lcap) ? pos : kListStage + lane;  // past lcap: dropped
+        li[p] = static_cast<int32_t>(e);
+        lv[p] = v;
       },
       &thr2, &cnt2);
   for (int i = tid; i < cap; i += 64 * kWaves) {

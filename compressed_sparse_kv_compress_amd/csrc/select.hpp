@@ -32,6 +32,7 @@ namespace sel {
 
 constexpr int kBins = 2048;
 constexpr int kSmall = 256;  // a threshold bin with at most this many keys is resolved by one wavefront
+constexpr uint32_t kNoSlot = 0xffffffffu;  // emit position of a survivor that is not kept
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63; }
 
@@ -558,8 +559,10 @@ struct Filter {
   // Keeps the sel largest valid scores (1 <= sel <= nvalid = valid scores of
   // the workgroup, vmin / vmax their min and max).  Kept items get slots in
   // entry order: emit(pos, score, entry) on the sampled path, emit_item(j,
-  // pos) (item j of this thread) on the radix path.  src(e) returns the score
-  // of entry e.  Ends with a barrier.
+  // pos) (item j of this thread) on the radix path.  On the sampled path
+  // emit is also called for items that are not kept, with pos == kNoSlot (to
+  // be dropped, for instance stored to a dump slot).  src(e) returns the
+  // score of entry e.  Ends with a barrier.
   template <typename Src, typename Emit, typename EmitItem>
   static __device__ __forceinline__ void run(const float (&x)[ITEMS], Src src, uint32_t nvalid, uint32_t sel,
                                              float vmin, float vmax, Shared& sh, Emit emit, EmitItem emit_item) {
@@ -572,7 +575,7 @@ struct Filter {
   // none): on the sampled path every survivor in the survivor-histogram bins
   // from the one holding the sel2-th largest score upwards (so at least sel2
   // scores) is emitted again, in entry order, through emit2(pos, score,
-  // entry); *cnt2 gets their number and *thr2 their smallest score, and since
+  // entry) (also called with pos == kNoSlot for the other survivors); *cnt2 gets their number and *thr2 their smallest score, and since
   // bins are monotone in the score, every valid score >= *thr2 is in the
   // list.  On the radix paths no list is made (*cnt2 = 0xffffffff).  Ends
   // with a barrier.
@@ -757,13 +760,22 @@ struct Filter {
       --keq;
     }
     uint32_t slot = gt0 + (eq0 < take ? eq0 : take);
+    // Every survivor slot calls the emitters, branch-free: a slot that is
+    // not kept gets kNoSlot (per-item exec-mask branches cost more than the
+    // stores they skip).
 #pragma unroll
-    for (int k = 0; k < SMAX; ++k)
-      if (Small::bit(km, k)) emit(slot++, y[k], ent[k]);
+    for (int k = 0; k < SMAX; ++k) {
+      const bool kp = Small::bit(km, k);
+      emit(kp ? slot : kNoSlot, y[k], ent[k]);
+      slot += kp;
+    }
     if (two) {
 #pragma unroll
-      for (int k = 0; k < SMAX; ++k)
-        if (Small::bit(gm2, k)) emit2(qpos++, y[k], ent[k]);
+      for (int k = 0; k < SMAX; ++k) {
+        const bool kp = Small::bit(gm2, k);
+        emit2(kp ? qpos : kNoSlot, y[k], ent[k]);
+        qpos += kp;
+      }
     }
     __syncthreads();
     *thr2 = tv2;

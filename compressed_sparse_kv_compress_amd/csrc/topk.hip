@@ -95,8 +95,8 @@ using PartTile = Tile<kThreads, kItems>;
 
 struct Shared {
   Filt::Shared fs;
-  int32_t si[kStage];  // staged output: entry and score
-  float sv[kStage];
+  int32_t si[kStage + 64];  // staged output: entry and score (64 lane-private dump slots at the end)
+  float sv[kStage + 64];
   alignas(16) float stage[PartTile::kFloats];
 };
 
@@ -109,8 +109,8 @@ using MergeTile = Tile<kMThreads, kMItems>;
 using MFilt = sel::Filter<kMThreads, kMItems, 16>;
 struct MShared {
   MFilt::Shared fs;
-  int32_t si[kStage];
-  float sv[kStage];
+  int32_t si[kStage + 64];  // 64 lane-private dump slots at the end
+  float sv[kStage + 64];
   alignas(16) float stage[MergeTile::kFloats];
   int wtot[kMThreads / 64];
 };
@@ -165,8 +165,9 @@ __global__ __launch_bounds__(kThreads) void topk_part_kernel(TopkArgs a, int64_t
     Filt::run(
         v, src, ncnt, ucap, vmin, vmax, sh.fs,
         [&](uint32_t pos, float val, uint32_t e) {
-          sh.si[pos] = static_cast<int>(e);
-          sh.sv[pos] = val;
+          const uint32_t p = pos != sel::kNoSlot ? pos : kStage + lane_id();
+          sh.si[p] = static_cast<int>(e);
+          sh.sv[p] = val;
         },
         [&](int j, uint32_t pos) {
           sh.si[pos] = i0 + j;
@@ -180,6 +181,7 @@ __global__ __launch_bounds__(kThreads) void topk_part_kernel(TopkArgs a, int64_t
     Filt::run(
         v, src, ncnt, ucap, vmin, vmax, sh.fs,
         [&](uint32_t pos, float val, uint32_t e) {
+          if (pos == sel::kNoSlot) return;
           ov[pos] = val;
           oi[pos] = static_cast<int32_t>(base + e);
         },
@@ -375,8 +377,9 @@ __global__ __launch_bounds__(kMThreads) void topk_merge_kernel(TopkArgs a, int n
     MFilt::run(
         v, src, static_cast<uint32_t>(total), uk, vmin, vmax, sh.fs,
         [&](uint32_t pos, float val, uint32_t e) {
-          sh.si[pos] = static_cast<int32_t>(e);
-          sh.sv[pos] = val;
+          const uint32_t p = pos != sel::kNoSlot ? pos : kStage + lane_id();
+          sh.si[p] = static_cast<int32_t>(e);
+          sh.sv[p] = val;
         },
         [&](int j, uint32_t pos) {
           sh.si[pos] = s0 + j;
@@ -390,6 +393,7 @@ __global__ __launch_bounds__(kMThreads) void topk_merge_kernel(TopkArgs a, int n
     MFilt::run(
         v, src, static_cast<uint32_t>(total), uk, vmin, vmax, sh.fs,
         [&](uint32_t pos, float val, uint32_t e) {
+          if (pos == sel::kNoSlot) return;
           o[pos] = ri[e];
           if (os) os[pos] = val;
         },
