@@ -124,15 +124,19 @@ __device__ __forceinline__ void fold_range(const CompressArgs& a, const Cands& c
 }
 
 // S = 1: one thread per (entry, 16-byte channel group), for bulk launches.
-// S > 1: the candidate tokens of each segment are split over S thread slices
-// whose partial (max, denominator, numerator) are merged through LDS; used
-// when a launch has too few entries to fill the GPU (decode-time refresh).
+// S > 1: the candidate tokens of each segment are split over S thread slices,
+// S consecutive lanes of one wavefront, whose partial (max, denominator,
+// numerator) are merged with lane exchanges; used when a launch has too few
+// entries to fill the GPU (decode-time refresh).  The kernel uses no LDS, so
+// its workgroups can share a CU with an LDS-heavy kernel running beside it
+// (the indexer scan holds almost all of a CU's LDS).
 template <bool BF16, int S>
 __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
+  static_assert(S >= 1 && S <= 64 && (S & (S - 1)) == 0, "slices: a power of two within a wavefront");
   constexpr int VEC = Io<BF16>::VEC;
-  constexpr int LANES = 256 / S;
-  const int slice = threadIdx.x / LANES;
-  const int lane = threadIdx.x % LANES;
+  constexpr int LANES = 256 / S;  // channel groups per workgroup
+  const int slice = threadIdx.x % S;
+  const int lane = threadIdx.x / S;
   const int64_t nvec = a.D / VEC;
   const int64_t ne = a.e1 - a.e0;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * LANES + lane;
@@ -167,34 +171,29 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
   if (live && lo < hi) fold_range<BF16>(a, cd, lo, hi, row_base, c0, mx, den, acc);
 
   if (S > 1) {
-    __shared__ float part[3][S][LANES][VEC];
+    // Pairwise merges over the S lanes (xor distance 1, 2, ...): both lanes
+    // of a pair evaluate the same expression with the lower lane's partial
+    // first, so they agree bit for bit.
 #pragma unroll
-    for (int c = 0; c < VEC; ++c) {
-      part[0][slice][lane][c] = mx[c];
-      part[1][slice][lane][c] = den[c];
-      part[2][slice][lane][c] = acc[c];
-    }
-    __syncthreads();
-    if (slice != 0) return;
+    for (int off = 1; off < S; off <<= 1) {
+      const bool low = (slice & off) == 0;
 #pragma unroll
-    for (int c = 0; c < VEC; ++c) {
-      float M = -INFINITY;
-#pragma unroll
-      for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, part[0][s2][lane][c]);
-      float dd = 0.f, aa = 0.f;
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int s2 = 0; s2 < S; ++s2) {
-          const float ms = part[0][s2][lane][c];
-          if (ms == -INFINITY) continue;
-          const float f = fast_exp2(ms - M);
-          dd = fmaf(part[1][s2][lane][c], f, dd);
-          aa = fmaf(part[2][s2][lane][c], f, aa);
-        }
+      for (int c = 0; c < VEC; ++c) {
+        const float m2 = __shfl_xor(mx[c], off, 64);
+        const float d2 = __shfl_xor(den[c], off, 64);
+        const float a2 = __shfl_xor(acc[c], off, 64);
+        const float ml = low ? mx[c] : m2, mh = low ? m2 : mx[c];
+        const float dl = low ? den[c] : d2, dh = low ? d2 : den[c];
+        const float al = low ? acc[c] : a2, ah = low ? a2 : acc[c];
+        const float M = fmaxf(ml, mh);
+        const float fl = ml == -INFINITY ? 0.f : fast_exp2(ml - M);
+        const float fh = mh == -INFINITY ? 0.f : fast_exp2(mh - M);
+        mx[c] = M;
+        den[c] = fmaf(dl, fl, dh * fh);
+        acc[c] = fmaf(al, fl, ah * fh);
       }
-      den[c] = dd;
-      acc[c] = aa;
     }
+    if (slice != 0) return;
   }
   if (!live) return;
   float o[VEC];
