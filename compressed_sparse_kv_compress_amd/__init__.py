@@ -28,7 +28,7 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-CSA_F32, CSA_BF16 = 0, 1
+CSA_F32, CSA_BF16, CSA_FP8 = 0, 1, 2
 _STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED",
            3: "CSA_ERR_WORKSPACE", 4: "CSA_ERR_HIP"}
 
@@ -80,7 +80,9 @@ def _dt(t: torch.Tensor) -> int:
         return CSA_BF16
     if t.dtype == torch.float32:
         return CSA_F32
-    raise TypeError("storage dtype must be bfloat16 or float32, got %s" % t.dtype)
+    if t.dtype == torch.float8_e4m3fn:  # OCP FP8 E4M3
+        return CSA_FP8
+    raise TypeError("storage dtype must be bfloat16, float32 or float8_e4m3fn, got %s" % t.dtype)
 
 
 def _ptr(t):

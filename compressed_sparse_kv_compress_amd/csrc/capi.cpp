@@ -51,7 +51,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
       return fail(CSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p);    \
   } while (0)
 
-bool dtype_ok(csa_dtype_t dt) { return dt == CSA_F32 || dt == CSA_BF16; }
+bool dtype_ok(csa_dtype_t dt) { return dt == CSA_F32 || dt == CSA_BF16 || dt == CSA_FP8; }
+csa::Dt to_dt(csa_dtype_t dt) { return static_cast<csa::Dt>(static_cast<int>(dt)); }
 
 csa_status_t compress_common(const void* x_a, const void* z_a, const void* x_b, const void* z_b,
                              const float* bias, void* out, int64_t B, int64_t n, int64_t D,
@@ -81,7 +82,7 @@ csa_status_t compress_common(const void* x_a, const void* z_a, const void* x_b, 
           "raw rows [%lld, %lld) do not cover the positions [%lld, %lld) the entries read",
           (long long)p0, (long long)(p0 + n_raw), (long long)lo, (long long)hi);
   csa::CompressArgs a{x_a, z_a, x_b, z_b, bias, out, B, n, D, m, p0, n_raw, e0, e1, out_ld};
-  return hip_status(csa::launch_compress(a, dt == CSA_BF16, static_cast<hipStream_t>(stream)),
+  return hip_status(csa::launch_compress(a, to_dt(dt), static_cast<hipStream_t>(stream)),
                     "compress launch");
 }
 
@@ -91,7 +92,7 @@ csa_status_t index_common(const void* q_idx, const float* w_idx, const void* k_i
   REQUIRE(dtype_ok(dt), "unknown dtype %d", static_cast<int>(dt));
   REQUIRE(B >= 0 && T >= 1 && n_ctx >= T && L >= 0 && m >= 1 && HI >= 1 && dI >= 1,
           "need B >= 0, 1 <= T <= n_ctx, L >= 0, m >= 1, H_I >= 1, d_I >= 1");
-  if (!csa::index_shape_supported(HI, dI, dt == CSA_BF16))
+  if (!csa::index_shape_supported(HI, dI, to_dt(dt)))
     return fail(CSA_ERR_UNSUPPORTED, "no indexer kernel for H_I=%lld d_I=%lld dtype=%d", (long long)HI,
                 (long long)dI, static_cast<int>(dt));
   if (B == 0) return CSA_OK;
@@ -107,6 +108,7 @@ csa_status_t attn_common(const void* q, const void* kc, const void* vc, int64_t 
                          int64_t B, int64_t T, int64_t n_ctx, int64_t H, int64_t d, void* out,
                          float* lse, csa_dtype_t dt) {
   REQUIRE(dtype_ok(dt), "unknown dtype %d", static_cast<int>(dt));
+  if (dt == CSA_FP8) return fail(CSA_ERR_UNSUPPORTED, "attention has no FP8 storage kernels");
   REQUIRE(B >= 0 && T >= 1 && n_ctx >= T && L >= 0 && H >= 1 && d >= 1 && W >= 0,
           "need B >= 0, 1 <= T <= n_ctx, L >= 0, H >= 1, d >= 1, W >= 0");
   REQUIRE(std::isfinite(scale), "scale is not finite");
@@ -168,9 +170,8 @@ csa_status_t csa_index_score(const void* q_idx, const float* w_idx, const void* 
   csa_status_t st = index_common(q_idx, w_idx, k_idx, B, T, n_ctx, L, H_I, d_I, m, dtype);
   if (st != CSA_OK || B == 0 || L == 0) return st;
   REQUIRE_PTR(score);
-  csa::IndexScoreArgs a{q_idx, w_idx, k_idx, score, L, 0, B * T, B, T, n_ctx, L, H_I, d_I, m};
-  return hip_status(csa::launch_index_score(a, dtype == CSA_BF16, static_cast<hipStream_t>(stream)),
-                    "index score launch");
+  csa::IndexScoreArgs a{q_idx, w_idx, k_idx, score, L, 0, B * T, B, T, n_ctx, L, H_I, d_I, m, to_dt(dtype)};
+  return hip_status(csa::launch_index_score(a, static_cast<hipStream_t>(stream)), "index score launch");
 }
 
 size_t csa_topk_select_workspace(int64_t B, int64_t T, int64_t L, int64_t k) {
@@ -219,11 +220,11 @@ csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k
   OPT_PTR(out_score);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t rows = B * T;
-  if (ws != nullptr && L > 0 && csa::index_topk_fusable(rows, L, H_I, d_I, k, dtype == CSA_BF16) &&
+  if (ws != nullptr && L > 0 && csa::index_topk_fusable(rows, L, H_I, d_I, k, to_dt(dtype)) &&
       ws_bytes >= csa::index_topk_fused_ws_bytes(rows, L, k)) {
     // The scan's workgroups keep their parts' candidates; no score matrix.
     if (!aligned16(ws)) return fail(CSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
-    csa::IndexScoreArgs a{q_idx, w_idx, k_idx, nullptr, L, 0, rows, B, T, n_ctx, L, H_I, d_I, m};
+    csa::IndexScoreArgs a{q_idx, w_idx, k_idx, nullptr, L, 0, rows, B, T, n_ctx, L, H_I, d_I, m, to_dt(dtype)};
     csa::TopkArgs t{nullptr, L, 0, rows, T, n_ctx, L, m, k, idx, out_score};
     return hip_status(csa::launch_index_topk_fused(a, t, ws, s), "fused index/top-k launch");
   }
@@ -239,8 +240,8 @@ csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k
   for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
     const int64_t nr = r0 + chunk < rows ? chunk : rows - r0;
     if (L > 0) {
-      csa::IndexScoreArgs a{q_idx, w_idx, k_idx, sc, L, r0, nr, B, T, n_ctx, L, H_I, d_I, m};
-      st = hip_status(csa::launch_index_score(a, dtype == CSA_BF16, s), "index score launch");
+      csa::IndexScoreArgs a{q_idx, w_idx, k_idx, sc, L, r0, nr, B, T, n_ctx, L, H_I, d_I, m, to_dt(dtype)};
+      st = hip_status(csa::launch_index_score(a, s), "index score launch");
       if (st != CSA_OK) return st;
     }
     csa::TopkArgs t{sc, L, r0, nr, T, n_ctx, L, m, k, idx + r0 * k,

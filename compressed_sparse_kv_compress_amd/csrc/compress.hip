@@ -20,13 +20,14 @@ namespace csa {
 
 namespace {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kChunk = 8;
 
-template <bool BF16>
+template <Dt DT>
 struct Io;
 
 template <>
-struct Io<true> {
+struct Io<kBF16> {
   static constexpr int VEC = 8;
   __device__ static void load(const void* base, int64_t off, float* v) {
     const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
@@ -45,8 +46,38 @@ struct Io<true> {
   }
 };
 
+// FP8 (OCP E4M3): 8 channels (8 bytes) per thread; the hardware converters
+// decode exactly and encode with round-to-nearest-even.
 template <>
-struct Io<false> {
+struct Io<kFP8> {
+  static constexpr int VEC = 8;
+  __device__ static void load(const void* base, int64_t off, float* v) {
+    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(base) + off);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int word = static_cast<int>(h ? w.y : w.x);
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+      v[4 * h + 0] = lo[0];
+      v[4 * h + 1] = lo[1];
+      v[4 * h + 2] = hi[0];
+      v[4 * h + 3] = hi[1];
+    }
+  }
+  __device__ static void store(void* base, int64_t off, const float* v) {
+    uint2 w;
+    int x = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    x = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], x, true);
+    int y = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+    y = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], y, true);
+    w.x = static_cast<uint32_t>(x);
+    w.y = static_cast<uint32_t>(y);
+    *reinterpret_cast<uint2*>(static_cast<uint8_t*>(base) + off) = w;
+  }
+};
+
+template <>
+struct Io<kF32> {
   static constexpr int VEC = 4;
   __device__ static void load(const void* base, int64_t off, float* v) {
     const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
@@ -67,10 +98,10 @@ struct Cands {
 
 // Fold candidates [lo, hi) of the virtual list into the running (max,
 // denominator, numerator) of VEC channels.  Logits are in log2 units.
-template <bool BF16>
+template <Dt DT>
 __device__ __forceinline__ void fold_range(const CompressArgs& a, const Cands& cd, int64_t lo, int64_t hi,
                                            int64_t row_base, int64_t c0, float* mx, float* den, float* acc) {
-  constexpr int VEC = Io<BF16>::VEC;
+  constexpr int VEC = Io<DT>::VEC;
   for (int64_t i0 = lo; i0 < hi; i0 += kChunk) {
     // All 2 x kChunk loads are issued unconditionally (candidates past the
     // end re-read the last one and are masked below), so they are all in
@@ -82,8 +113,8 @@ __device__ __forceinline__ void fold_range(const CompressArgs& a, const Cands& c
       const bool from_b = ci < cd.nb;
       const int64_t u = from_b ? cd.b_lo + ci : cd.a_lo + (ci - cd.nb);
       const int64_t off = (row_base + (u - a.p0)) * a.D + c0;
-      Io<BF16>::load(from_b ? a.x_b : a.x_a, off, xv[i]);
-      Io<BF16>::load(from_b ? a.z_b : a.z_a, off, lv[i]);
+      Io<DT>::load(from_b ? a.x_b : a.x_a, off, xv[i]);
+      Io<DT>::load(from_b ? a.z_b : a.z_a, off, lv[i]);
     }
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
@@ -130,10 +161,10 @@ __device__ __forceinline__ void fold_range(const CompressArgs& a, const Cands& c
 // entries to fill the GPU (decode-time refresh).  The kernel uses no LDS, so
 // its workgroups can share a CU with an LDS-heavy kernel running beside it
 // (the indexer scan holds almost all of a CU's LDS).
-template <bool BF16, int S>
+template <Dt DT, int S>
 __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
   static_assert(S >= 1 && S <= 64 && (S & (S - 1)) == 0, "slices: a power of two within a wavefront");
-  constexpr int VEC = Io<BF16>::VEC;
+  constexpr int VEC = Io<DT>::VEC;
   constexpr int LANES = 256 / S;  // channel groups per workgroup
   const int slice = threadIdx.x % S;
   const int lane = threadIdx.x / S;
@@ -168,7 +199,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
     lo = slice * per;
     hi = lo + per < total ? lo + per : total;
   }
-  if (live && lo < hi) fold_range<BF16>(a, cd, lo, hi, row_base, c0, mx, den, acc);
+  if (live && lo < hi) fold_range<DT>(a, cd, lo, hi, row_base, c0, mx, den, acc);
 
   if (S > 1) {
     // Pairwise merges over the S lanes (xor distance 1, 2, ...): both lanes
@@ -199,26 +230,27 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
   float o[VEC];
 #pragma unroll
   for (int c = 0; c < VEC; ++c) o[c] = den[c] > 0.f ? acc[c] / den[c] : 0.f;
-  Io<BF16>::store(a.out, (b * a.out_ld + jj) * a.D + c0, o);
+  Io<DT>::store(a.out, (b * a.out_ld + jj) * a.D + c0, o);
 }
 
 }  // namespace
 
-hipError_t launch_compress(const CompressArgs& a, bool bf16, hipStream_t s) {
-  const int vec = bf16 ? 8 : 4;
+hipError_t launch_compress(const CompressArgs& a, Dt dt, hipStream_t s) {
+  const int vec = dt == kF32 ? 4 : 8;
   const int64_t total = a.B * (a.e1 - a.e0) * (a.D / vec);
   if (total == 0) return hipSuccess;
   // Few entries with long blocks: spread each block's tokens over 16 slices.
   const bool sliced = total < 32768 && a.m >= 32;
-  if (sliced) {
-    const dim3 grid(static_cast<uint32_t>((total + 15) / 16));
-    if (bf16) hipLaunchKernelGGL((compress_kernel<true, 16>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((compress_kernel<false, 16>), grid, dim3(256), 0, s, a);
-  } else {
-    const dim3 grid(static_cast<uint32_t>((total + 255) / 256));
-    if (bf16) hipLaunchKernelGGL((compress_kernel<true, 1>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((compress_kernel<false, 1>), grid, dim3(256), 0, s, a);
+  const dim3 grid(static_cast<uint32_t>(sliced ? (total + 15) / 16 : (total + 255) / 256));
+#define CSA_COMPRESS_LAUNCH(DT_)                                                          \
+  if (sliced) hipLaunchKernelGGL((compress_kernel<DT_, 16>), grid, dim3(256), 0, s, a);  \
+  else hipLaunchKernelGGL((compress_kernel<DT_, 1>), grid, dim3(256), 0, s, a);
+  switch (dt) {
+    case kBF16: CSA_COMPRESS_LAUNCH(kBF16) break;
+    case kFP8: CSA_COMPRESS_LAUNCH(kFP8) break;
+    default: CSA_COMPRESS_LAUNCH(kF32) break;
   }
+#undef CSA_COMPRESS_LAUNCH
   return hipGetLastError();
 }
 

@@ -34,6 +34,11 @@ constexpr int kWaves = 4;
 constexpr int kTileKeys = 16;                 // keys per MFMA tile (the N dimension)
 constexpr int kDepth = CSA_INDEX_DEPTH;       // ring slots per wavefront (kDepth - 1 tiles in flight)
 constexpr int kTileBytes = kTileKeys * 256;   // d_I = 128 bf16 keys
+// FP8 keys (128 B): tiles of half the size and twice the slots, the same
+// ring bytes and about the same bytes in flight.
+constexpr int kDepth8 = 2 * kDepth;
+constexpr int kTileBytes8 = kTileKeys * 128;
+static_assert(kDepth8 * kTileBytes8 == kDepth * kTileBytes, "one ring size for both key types");
 constexpr int kMinKeysPerWave = 256;
 constexpr int kMaxKeysPerWave = 3968;         // scores of a workgroup stay in LDS (62 KiB)
 constexpr int kMaxTiles = kMaxKeysPerWave / kTileKeys;
@@ -47,21 +52,31 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Wait until at most 4 * n of this wave's loads are outstanding (n < kDepth).
+// Wait until at most LPT * n of this wave's loads are outstanding (LPT loads
+// per tile, n < ring depth).
+template <int LPT>
 __device__ __forceinline__ void wait_tiles(int n) {
   switch (n) {
     case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<4>(); break;
-    case 2: wait_vmcnt<8>(); break;
-    case 3: wait_vmcnt<12>(); break;
-    case 4: wait_vmcnt<16>(); break;
-    case 5: wait_vmcnt<20>(); break;
-    case 6: wait_vmcnt<24>(); break;
-    default: wait_vmcnt<28>(); break;
+    case 1: wait_vmcnt<LPT * 1>(); break;
+    case 2: wait_vmcnt<LPT * 2>(); break;
+    case 3: wait_vmcnt<LPT * 3>(); break;
+    case 4: wait_vmcnt<LPT * 4>(); break;
+    case 5: wait_vmcnt<LPT * 5>(); break;
+    case 6: wait_vmcnt<LPT * 6>(); break;
+    case 7: wait_vmcnt<LPT * 7>(); break;
+    case 8: wait_vmcnt<LPT * 8>(); break;
+    case 9: wait_vmcnt<LPT * 9>(); break;
+    case 10: wait_vmcnt<LPT * 10>(); break;
+    case 11: wait_vmcnt<LPT * 11>(); break;
+    case 12: wait_vmcnt<LPT * 12>(); break;
+    case 13: wait_vmcnt<LPT * 13>(); break;
+    default: wait_vmcnt<LPT * 14>(); break;
   }
   asm volatile("" ::: "memory");
 }
-static_assert(kDepth >= 2 && kDepth <= 8, "wait_tiles covers up to 7 tiles in flight");
+static_assert(kDepth >= 2 && kDepth8 <= 15, "wait_tiles covers up to 14 tiles in flight");
+static_assert(4 * (kDepth - 1) < 64 && 2 * (kDepth8 - 1) < 64, "vmcnt range");
 
 // 16 bytes per lane, global -> LDS at lds + 16 * lane (lds wave-uniform, via
 // M0), nontemporal (every key is read once: streaming through the caches
@@ -213,13 +228,21 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
 // Scores collect in LDS and leave in one coalesced pass at the end, so the
 // loop issues no stores (their completions would share the load counter the
 // ring waits on).
-template <int MB, bool HAS_W, bool TOPK>
+// FP8: keys and queries in OCP E4M3 (128 B per key).  A tile is two 1 KiB
+// loads; the MFMA is v_mfma_f32_16x16x32_fp8_fp8 with the same lane layout
+// as the bf16 one (lane (g, c) supplies row c, k-slots 8g .. 8g+7; checked
+// on the device against an fp64 product of the decoded values).
+template <int MB, bool HAS_W, bool TOPK, bool FP8>
 __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, int64_t parts, int64_t per_wave,
                                                              IndexCandidates co) {
   constexpr int HI = 16 * MB;
   constexpr int DI = 128;
   constexpr int KS = 4;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][kDepth][kTileBytes];
+  constexpr int KB = FP8 ? 128 : 256;                // bytes per key
+  constexpr int TB = FP8 ? kTileBytes8 : kTileBytes;  // bytes per tile
+  constexpr int DEPTH = FP8 ? kDepth8 : kDepth;       // ring slots per wavefront
+  constexpr int LPT = TB / 1024;                      // 1 KiB wave loads per tile
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][DEPTH][TB];
   __shared__ __attribute__((aligned(16))) float sbuf[kWaves][kMaxTiles * kTileKeys];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -242,44 +265,75 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
   const int64_t k0 = kb + static_cast<int64_t>(wave) * kTileKeys;  // first key of this wave's tile 0
   constexpr int64_t kStride = kWaves * kTileKeys;                    // keys between its tiles
 
-  // Tile layout in LDS: key kk (0..15) at kk*256; its 16-byte piece p at
-  // slot p ^ kk.  Load j of a tile covers keys 4j .. 4j+3 (1 KiB contiguous
-  // in HBM); lane l writes slot l%16 of key 4j + l/16, so it fetches piece
-  // (l%16) ^ kk.  Only a tile that runs past the last key (the very end of a
-  // row) takes per-lane clamped addresses.
-  const char* kbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + b * a.L * DI);
-  uint32_t voff[4];
+  // Tile layout in LDS.
+  //  bf16: key kk (0..15) at kk*256; its 16-byte piece p at slot p ^ kk.
+  //    Load j covers keys 4j .. 4j+3 (1 KiB contiguous in HBM); lane l writes
+  //    slot l%16 of key 4j + l/16, so it fetches piece (l%16) ^ kk.
+  //  FP8: key kk at kk*128, eight 16-byte pieces.  The dot product may take
+  //    its 128 dims in any order shared by both operands: k-step ks, lane
+  //    group g covers dims 32g + 8ks .. +8, so a lane's four k-steps are one
+  //    32-byte block (pieces 2g, 2g+1), stored at block position g ^ (kk & 3)
+  //    (16 keys 128 B apart then hit distinct bank groups).  Load j covers
+  //    keys 8j .. 8j+7; lane l writes slot s = l%8 of key 8j + l/8, so it
+  //    fetches piece 2((s/2) ^ (kk & 3)) + s%2.
+  // Only a tile that runs past the last key (the very end of a row) takes
+  // per-lane clamped addresses.
+  const char* kbase = static_cast<const char*>(a.k) + b * a.L * KB;
+  uint32_t voff[LPT];
+  int kkl[LPT];  // key of the tile this lane's piece of load j belongs to
 #pragma unroll
-  for (int j = 0; j < 4; ++j) voff[j] = (4 * j + g) * 256 + ((c16 ^ (4 * j + g)) << 4);
+  for (int j = 0; j < LPT; ++j) {
+    if constexpr (FP8) {
+      const int kk = 8 * j + (lane >> 3), sl = lane & 7;
+      kkl[j] = kk;
+      voff[j] = kk * 128 + ((2 * ((sl >> 1) ^ (kk & 3)) + (sl & 1)) << 4);
+    } else {
+      kkl[j] = 4 * j + g;
+      voff[j] = (4 * j + g) * 256 + ((c16 ^ (4 * j + g)) << 4);
+    }
+  }
   uint8_t* myring = &ring[wave][0][0];
   auto issue = [&](int it) {
-    uint8_t* slot = myring + (it % kDepth) * kTileBytes;
+    uint8_t* slot = myring + (it % DEPTH) * TB;
     const int64_t t0 = k0 + static_cast<int64_t>(it) * kStride;
     if (t0 + kTileKeys <= a.L) {
-      const char* tb = kbase + t0 * (DI * 2);
+      const char* tb = kbase + t0 * KB;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma16(tb, voff[j], slot + j * 1024);
+      for (int j = 0; j < LPT; ++j) dma16(tb, voff[j], slot + j * 1024);
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int64_t s = t0 + 4 * j + g;
+      for (int j = 0; j < LPT; ++j) {
+        int64_t s = t0 + kkl[j];
         s = s < a.L - 1 ? s : a.L - 1;
-        dma16(kbase + s * (DI * 2) + ((c16 ^ (4 * j + g)) << 4), slot + j * 1024);
+        dma16(kbase + s * KB + (voff[j] - kkl[j] * KB), slot + j * 1024);
       }
     }
   };
 #pragma unroll
-  for (int i = 0; i < kDepth - 1; ++i)
+  for (int i = 0; i < DEPTH - 1; ++i)
     if (i < ntv) issue(i);
 
   // A operand: query heads (rows) x index dims, resident for the whole kernel.
-  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + row * HI * DI;
-  bf16x8 afrag[MB][KS];
+  bf16x8 afrag[MB][FP8 ? 1 : KS];
+  uint64_t afrag8[MB][FP8 ? KS : 1];
+  if constexpr (FP8) {
+    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + row * HI * DI;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      afrag[mb][ks] = *reinterpret_cast<const bf16x8*>(qrow + (mb * 16 + c16) * DI + ks * 32 + g * 8);
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + (mb * 16 + c16) * DI + 32 * g + 16 * h);
+        afrag8[mb][2 * h] = (static_cast<uint64_t>(v[1]) << 32) | v[0];
+        afrag8[mb][2 * h + 1] = (static_cast<uint64_t>(v[3]) << 32) | v[2];
+      }
+  } else {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + row * HI * DI;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        afrag[mb][ks] = *reinterpret_cast<const bf16x8*>(qrow + (mb * 16 + c16) * DI + ks * 32 + g * 8);
+  }
   // Head weights for the 4 head rows this lane holds in each 16x16 block.
   float wr[MB][HAS_W ? 4 : 1];
   if (HAS_W) {
@@ -295,24 +349,38 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
 
   float* sb = sbuf[wave];
   for (int it = 0; it < ntv; ++it) {
-    if (it + kDepth - 1 < ntv) {
-      issue(it + kDepth - 1);
-      wait_tiles(kDepth - 1);
+    if (it + DEPTH - 1 < ntv) {
+      issue(it + DEPTH - 1);
+      wait_tiles<LPT>(DEPTH - 1);
     } else {
-      wait_tiles(ntv - 1 - it);
+      wait_tiles<LPT>(ntv - 1 - it);
     }
-    const uint8_t* t = myring + (it % kDepth) * kTileBytes + c16 * 256;
-    bf16x8 cur[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) cur[ks] = *reinterpret_cast<const bf16x8*>(t + (((4 * ks + g) ^ c16) << 4));
     f32x4 acc[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (FP8) {
+      const uint8_t* t = myring + (it % DEPTH) * TB + c16 * 128 + ((g ^ (c16 & 3)) << 5);
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(t);
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(t + 16);
+      const uint64_t cur8[KS] = {(static_cast<uint64_t>(x0[1]) << 32) | x0[0], (static_cast<uint64_t>(x0[3]) << 32) | x0[2],
+                                 (static_cast<uint64_t>(x1[1]) << 32) | x1[0], (static_cast<uint64_t>(x1[3]) << 32) | x1[2]};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[mb][ks], cur[ks], acc[mb], 0, 0, 0);
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(static_cast<long>(afrag8[mb][ks]),
+                                                              static_cast<long>(cur8[ks]), acc[mb], 0, 0, 0);
+    } else {
+      const uint8_t* t = myring + (it % DEPTH) * TB + c16 * 256;
+      bf16x8 cur[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) cur[ks] = *reinterpret_cast<const bf16x8*>(t + (((4 * ks + g) ^ c16) << 4));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[mb][ks], cur[ks], acc[mb], 0, 0, 0);
+    }
     // lane holds S[head mb*16 + 4g + r][key c16]: ReLU, head weights, and the
     // sum over heads (a short tree in-lane, then across the four lane groups).
     float ps[MB];
@@ -472,10 +540,13 @@ hipError_t launch_stream(const IndexScoreArgs& a, const IndexCandidates& co, hip
   const dim3 grid(static_cast<uint32_t>(a.nrows * parts));
   const int mb = static_cast<int>(a.HI / 16);
   const bool w = a.w != nullptr;
-#define CSA_INDEX_LAUNCH(MB_)                                                                                   \
-  case MB_:                                                                                                     \
-    if (w) hipLaunchKernelGGL((index_score_stream<MB_, true, TOPK>), grid, dim3(256), 0, s, a, parts, per_wave, co); \
-    else hipLaunchKernelGGL((index_score_stream<MB_, false, TOPK>), grid, dim3(256), 0, s, a, parts, per_wave, co); \
+  const bool f8 = a.dt == kFP8;
+#define CSA_INDEX_LAUNCH(MB_)                                                                                     \
+  case MB_:                                                                                                       \
+    if (f8 && w) hipLaunchKernelGGL((index_score_stream<MB_, true, TOPK, true>), grid, dim3(256), 0, s, a, parts, per_wave, co);     \
+    else if (f8) hipLaunchKernelGGL((index_score_stream<MB_, false, TOPK, true>), grid, dim3(256), 0, s, a, parts, per_wave, co);    \
+    else if (w) hipLaunchKernelGGL((index_score_stream<MB_, true, TOPK, false>), grid, dim3(256), 0, s, a, parts, per_wave, co);     \
+    else hipLaunchKernelGGL((index_score_stream<MB_, false, TOPK, false>), grid, dim3(256), 0, s, a, parts, per_wave, co);           \
     break;
   switch (mb) {
     CSA_INDEX_LAUNCH(1)
@@ -490,9 +561,13 @@ hipError_t launch_stream(const IndexScoreArgs& a, const IndexCandidates& co, hip
 
 }  // namespace
 
-hipError_t launch_index_score(const IndexScoreArgs& a, bool bf16, hipStream_t s) {
+hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t s) {
   if (a.nrows == 0 || a.L == 0) return hipSuccess;
-  if (bf16) {
+  if (a.dt == kFP8) {  // d_I = 128 only (index_shape_supported)
+    if (a.dI != 128) return hipErrorInvalidValue;
+    return launch_stream<false>(a, IndexCandidates{}, s);
+  }
+  if (a.dt == kBF16) {
     const int mb = static_cast<int>(a.HI / 16), ks = static_cast<int>(a.dI / 32);
     const bool w = a.w != nullptr;
     if (ks == 4) return launch_stream<false>(a, IndexCandidates{}, s);
@@ -520,8 +595,8 @@ hipError_t launch_index_score(const IndexScoreArgs& a, bool bf16, hipStream_t s)
   return hipGetLastError();
 }
 
-bool index_topk_fusable(int64_t nrows, int64_t L, int64_t HI, int64_t dI, int64_t k, bool bf16) {
-  if (!bf16 || dI != 128 || nrows <= 0 || L <= 0 || k < 1 || k > kCandStage) return false;
+bool index_topk_fusable(int64_t nrows, int64_t L, int64_t HI, int64_t dI, int64_t k, Dt dt) {
+  if ((dt != kBF16 && dt != kFP8) || dI != 128 || nrows <= 0 || L <= 0 || k < 1 || k > kCandStage) return false;
   if (!(HI == 16 || HI == 32 || HI == 64 || HI == 128)) return false;
   int64_t parts, per_wave;
   index_plan(nrows, L, &parts, &per_wave);
@@ -562,8 +637,9 @@ hipError_t launch_index_topk_fused(const IndexScoreArgs& a, const TopkArgs& t, v
   return launch_topk_merge(t, parts, co, true, s);
 }
 
-bool index_shape_supported(int64_t HI, int64_t dI, bool bf16) {
-  if (!bf16) return HI * dI * 4 <= 65536;
+bool index_shape_supported(int64_t HI, int64_t dI, Dt dt) {
+  if (dt == kFP8) return dI == 128 && (HI == 16 || HI == 32 || HI == 64 || HI == 128);
+  if (dt == kF32) return HI * dI * 4 <= 65536;
   if (HI % 16 || dI % 32) return false;
   const int64_t mb = HI / 16, ks = dI / 32;
   return (ks == 4 && (mb == 1 || mb == 2 || mb == 4 || mb == 8)) || (ks == 2 && (mb == 2 || mb == 4));

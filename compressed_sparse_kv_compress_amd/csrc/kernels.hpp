@@ -6,6 +6,9 @@
 
 namespace csa {
 
+// Storage types, numbered as csa_dtype_t: fp32, bf16, and FP8 (OCP E4M3).
+enum Dt : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
 struct CompressArgs {
   const void* x_a;
   const void* z_a;
@@ -15,7 +18,7 @@ struct CompressArgs {
   void* out;          // [B][out_ld][D], entry j at row j - e0
   int64_t B, n, D, m, p0, n_raw, e0, e1, out_ld;
 };
-hipError_t launch_compress(const CompressArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_compress(const CompressArgs& a, Dt dt, hipStream_t s);
 
 struct IndexScoreArgs {
   const void* q;      // [rows][HI][dI], rows = B*T (b-major)
@@ -26,8 +29,9 @@ struct IndexScoreArgs {
   int64_t row0;       // first (b,t) row handled by this launch
   int64_t nrows;      // rows handled
   int64_t B, T, n_ctx, L, HI, dI, m;
+  Dt dt;              // storage of q and k (scores are fp32)
 };
-hipError_t launch_index_score(const IndexScoreArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t s);
 
 // Per-part top-k candidates: part p of row r keeps ccnt[r][p] <= cap
 // (score, index) pairs in index order at [r][p][0 ..]; slots past them hold
@@ -84,9 +88,9 @@ inline void compact_list_plan(int64_t nparts, int64_t k, int64_t* lrank, int64_t
 
 // Indexer scan fused with the part stage of the top-k (no score matrix): the
 // scan's workgroups select their parts' candidates from LDS, then the merge
-// runs.  Available for bf16, d_I = 128, k <= 2048 when the scan's parts give
-// the merge's fast path; ws: index_topk_fused_ws_bytes(nrows, L, k).
-bool index_topk_fusable(int64_t nrows, int64_t L, int64_t HI, int64_t dI, int64_t k, bool bf16);
+// runs.  Available for bf16 and FP8, d_I = 128, k <= 2048 when the scan's
+// parts give the merge's fast path; ws: index_topk_fused_ws_bytes(nrows, L, k).
+bool index_topk_fusable(int64_t nrows, int64_t L, int64_t HI, int64_t dI, int64_t k, Dt dt);
 size_t index_topk_fused_ws_bytes(int64_t nrows, int64_t L, int64_t k);
 hipError_t launch_index_topk_fused(const IndexScoreArgs& a, const TopkArgs& t, void* ws, hipStream_t s);
 
@@ -118,6 +122,6 @@ int attn_splits(int64_t B, int64_t T, int64_t H, int64_t d, int64_t max_rows, bo
 size_t attn_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t d, int nsplit);
 hipError_t launch_attn(const AttnArgs& a, bool sparse, bool bf16, int nsplit, hipStream_t s);
 bool attn_shape_supported(int64_t H, int64_t d, bool bf16);
-bool index_shape_supported(int64_t HI, int64_t dI, bool bf16);
+bool index_shape_supported(int64_t HI, int64_t dI, Dt dt);
 
 }  // namespace csa

@@ -26,6 +26,16 @@
  *   - dtype selects the storage type of every bf16/fp32 tensor argument
  *     (declared `void*`).  Accumulation is fp32.  Scores, sinks, biases,
  *     head weights and lse are always fp32; indices are int32.
+ *   - CSA_FP8 is the OCP 8-bit float E4M3 (1 sign, 4 exponent bits with bias
+ *     7, 3 mantissa bits; exponent 0 holds subnormals m * 2^-9; codes 0x7F
+ *     and 0xFF are NaN; no infinities, largest finite value 448).  The pages
+ *     allow FP8 storage for the main KV and low precision for the indexer's
+ *     q.k path (shareware.cn article, the low-precision item of its list of
+ *     what is compressed) without naming an encoding.  Accepted by
+ *     csa_compress / hca_compress (inputs and output in FP8, arithmetic in
+ *     fp32, output rounded to nearest even) and by csa_index_score /
+ *     csa_index_topk (q_idx and k_idx in FP8, d_I = 128, H_I in {16, 32, 64,
+ *     128}).  The attention entry points return CSA_ERR_UNSUPPORTED for it.
  *   - Positions: a batch holds B sequences of n_ctx tokens (uniform length).
  *     The T queries of a sequence sit at positions t_i = n_ctx - T + i.
  *     Compressed entry s covers tokens [s*m, (s+1)*m) and is visible to the
@@ -45,7 +55,7 @@
 extern "C" {
 #endif
 
-typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype_t;
+typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8 = 2 } csa_dtype_t;
 
 typedef enum csa_status {
   CSA_OK = 0,

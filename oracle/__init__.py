@@ -22,6 +22,10 @@ see tests/test_oracle_*.py):
   sparse_attn / dense_attn    pinned (torch SDPA textbook MQA incl. sink as an
                               extra logit, one-hot probability mass, sink limits,
                               the 0.15 / 0.85 example, order invariance)
+  fp8_decode / fp8_encode     pinned (all 256 codes against torch's float8_e4m3fn,
+                              named values, ties to even, round trips); the
+                              choice of E4M3 itself is a reading of the pages
+                              (they name FP8 without an encoding)
 """
 from __future__ import annotations
 
@@ -85,11 +89,57 @@ def _load():
     return _lib
 
 
+# ---- FP8 storage (OCP 8-bit floating point, E4M3 flavour) -----------------
+# The pages let the indexer's q.k path run in low precision (FP8 / FP4) and the
+# main KV in FP8, without naming an encoding.  The reading taken here is the
+# OCP E4M3 format (the one gfx950's converters and fp8 MFMAs use): 1 sign bit,
+# 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 holds subnormals
+# m * 2**-9; exponent 15 with mantissa 7 is NaN; there are no infinities, so
+# the largest finite value is 1.75 * 2**8 = 448.
+
+
+def fp8_decode(codes) -> np.ndarray:
+    """E4M3 byte codes (any integer array) -> float64 values, from the format's
+    definition."""
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & ((c & 0x7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def fp8_encode(x) -> np.ndarray:
+    """float values -> E4M3 byte codes, rounding to nearest with ties to the
+    even code.  Magnitudes of 464 and above (past the midpoint above 448) and
+    NaN are rejected: the format has no infinities."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.isnan(x).any() or (np.abs(x) >= 464.0).any():
+        raise ValueError("fp8_encode: NaN or magnitude >= 464 has no E4M3 code")
+    # All finite non-negative values, ascending with the code (0x00 .. 0x7E).
+    grid = fp8_decode(np.arange(0x7F))
+    a = np.abs(x).reshape(-1)
+    hi = np.searchsorted(grid, a, side="left")  # first grid value >= a
+    hi = np.minimum(hi, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - grid[lo]
+    dhi = grid[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(a == grid[hi], hi, np.where(pick_hi, hi, lo))
+    neg = np.signbit(x.reshape(-1))
+    code = np.where(neg, code | 0x80, code)
+    return code.astype(np.uint8).reshape(x.shape)
+
+
 def _f64(a):
     if a is None:
         return None
     if hasattr(a, "detach"):  # torch tensor on the CPU
-        a = a.detach().to("cpu").double().numpy()
+        a = a.detach().to("cpu")
+        if str(a.dtype) == "torch.float8_e4m3fn":  # decoded here, not by torch
+            return np.ascontiguousarray(fp8_decode(a.view(dtype=__import__("torch").uint8).numpy()))
+        a = a.double().numpy()
     return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
 
 

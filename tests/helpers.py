@@ -7,6 +7,7 @@ import math
 import numpy as np
 import torch
 
+import oracle
 import synthetic as syn
 
 BF16_TOL = 2e-2   # max-abs, bf16 storage with fp32 accumulation
@@ -24,10 +25,14 @@ def both(shape, seed, name, *, dtype, scale=1.0, kind="normal", layer=0, grid=8)
     Each side is generated on its own device; the CPU copy never comes from the GPU."""
     g = gen(shape, seed, name, dtype=dtype, device="cuda", scale=scale, kind=kind, layer=layer, grid=grid)
     c = gen(shape, seed, name, dtype=dtype, device="cpu", scale=scale, kind=kind, layer=layer, grid=grid)
+    if dtype == torch.float8_e4m3fn:  # decoded by the oracle's own E4M3 decoder
+        return g, oracle.fp8_decode(c.view(torch.uint8).numpy())
     return g, c.double().numpy()
 
 
 def to_np(t):
+    if t.dtype == torch.float8_e4m3fn:
+        return oracle.fp8_decode(t.detach().cpu().view(torch.uint8).numpy())
     return t.detach().float().cpu().double().numpy()
 
 
@@ -79,6 +84,29 @@ def index_eps(q, w, k):
     wa = np.ones(H) if w is None else np.abs(w)
     mag = np.abs(k) @ (np.abs(q).T * 1.0)  # [L, H]
     return 2.0 * (dI + H) * 2.0 ** -24 * (mag @ wa)
+
+
+def index_eps_fp8(q, w, k):
+    """Per-entry bound for FP8 (E4M3) indexer scores on the GPU.
+
+    The products of two E4M3 values are exact in fp32, but gfx950's fp8
+    MFMA (v_mfma_f32_16x16x32_fp8_fp8) does not sum them at fp32 precision:
+    on 2000 random 16x128 x 128x16 products per input scale the error of one
+    instruction (32 products) reached ~1150 x 2^-24 of the sum of |products|,
+    and ~440 x 2^-24 for four chained ones (a 128-dim dot product).  The
+    bound takes 2^-12 (4096 x 2^-24) of sum_c |q_hc k_sc| per head, weighted
+    by |w_h|, plus the fp32 bound of the epilogue (ReLU, weights, head sum)."""
+    H, dI = q.shape
+    wa = np.ones(H) if w is None else np.abs(w)
+    mag = (np.abs(k) @ np.abs(q).T) @ wa
+    return 2.0 ** -12 * mag + index_eps(q, w, k)
+
+
+def fp8_ulp(x):
+    """Spacing of E4M3 values at |x| (2^-9 in the subnormal range)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return 2.0 ** (e - 3)
 
 
 def default_scale(d):

@@ -102,3 +102,34 @@ def test_index_and_attention_reject_bad_arguments(lib):
     # non-finite scale
     assert _call(lib, "hca_dense_attn", dense, FAKE, FAKE, FAKE, 7813, 128, None, None, 0, 0, None,
                  float("inf"), 4, 1, 1000000, 64, 512, FAKE, None, None, 0, 1, None) == 1
+
+
+def test_fp8_storage_is_validated(lib):
+    """CSA_FP8 (2) is a known dtype: accepted by compression and the indexer
+    (d_I = 128, H_I a multiple of 16 up to 128), rejected as unsupported by
+    attention; 3 is unknown."""
+    idx_args = [V] * 3 + [I] * 8 + [V, V, V, Z, ctypes.c_int, V]
+    # FP8 indexer with d_I = 64: no kernel
+    assert _call(lib, "csa_index_topk", idx_args, FAKE, None, FAKE, 1, 1, 100, 25, 64, 64, 4, 8,
+                 FAKE, None, FAKE, 1 << 20, 2, None) == 2
+    # FP8 indexer with H_I = 48: no kernel
+    assert _call(lib, "csa_index_topk", idx_args, FAKE, None, FAKE, 1, 1, 100, 25, 48, 128, 4, 8,
+                 FAKE, None, FAKE, 1 << 20, 2, None) == 2
+    # FP8 indexer, supported shape, but k = 0: an argument error, so the dtype itself passed
+    assert _call(lib, "csa_index_topk", idx_args, FAKE, None, FAKE, 1, 1, 100, 25, 64, 128, 4, 0,
+                 FAKE, None, FAKE, 1 << 20, 2, None) == 1
+    # unknown dtype 3
+    assert _call(lib, "csa_index_topk", idx_args, FAKE, None, FAKE, 1, 1, 100, 25, 64, 128, 4, 8,
+                 FAKE, None, FAKE, 1 << 20, 3, None) == 1
+    attn = [V] * 3 + [I, V, I, V, V, I, I, V, F] + [I] * 5 + [V, V, V, Z, ctypes.c_int, V]
+    assert _call(lib, "csa_sparse_attn", attn, FAKE, FAKE, FAKE, 10, FAKE, 4, None, None, 0, 0,
+                 None, 0.1, 1, 1, 40, 64, 512, FAKE, None, None, 0, 2, None) == 2
+    dense = [V] * 3 + [I, I, V, V, I, I, V, F] + [I] * 5 + [V, V, V, Z, ctypes.c_int, V]
+    assert _call(lib, "hca_dense_attn", dense, FAKE, FAKE, FAKE, 7813, 128, None, None, 0, 0, None,
+                 0.04, 4, 1, 1000000, 64, 512, FAKE, None, None, 0, 2, None) == 2
+    # FP8 compression: nothing to do is fine (no launch), D not a multiple of 8 is an error
+    args = [V] * 6 + [I] * 9 + [ctypes.c_int, V]
+    assert _call(lib, "csa_compress", args, None, None, None, None, None, None,
+                 1, 16, 16, 4, 0, 16, 2, 2, 0, 2, None) == 0
+    assert _call(lib, "csa_compress", args, FAKE, FAKE, None, None, None, FAKE,
+                 1, 16, 12, 4, 0, 16, 0, 4, 4, 2, None) == 1

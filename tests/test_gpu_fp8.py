@@ -1,0 +1,178 @@
+"""GPU parity of the FP8 (OCP E4M3) storage paths against the oracle.
+
+The pages let the indexer's q.k path and the main KV run in low precision
+(shareware.cn Hybrid Attention article, its list of what is compressed);
+CSA_FP8 is the E4M3 reading of that.  Inputs are generated on each device by
+``synthetic`` (E4M3 by round-to-nearest-even from the same fp32 values) and
+decoded for the oracle by the oracle's own E4M3 decoder."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import both, fp8_ulp, gen, index_eps_fp8, near_tie_check, to_np
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import compressed_sparse_kv_compress_amd as csa
+else:  # collected on the CPU, skipped by the marker selection
+    csa = None
+
+F8 = torch.float8_e4m3fn
+
+
+def test_generator_is_bit_identical_on_both_devices_fp8():
+    import synthetic as syn
+    for kind, scale in (("normal", 128 ** -0.5), ("normal", 3.0), ("uniform", 1.0), ("grid", 2.0 ** -4)):
+        a = syn.make((3, 1000, 72), 9, 4, dtype=F8, device="cuda", kind=kind, scale=scale)
+        b = syn.make((3, 1000, 72), 9, 4, dtype=F8, device="cpu", kind=kind, scale=scale)
+        assert torch.equal(a.cpu().view(torch.uint8), b.view(torch.uint8))
+
+
+# ---------------------------------------------------------------------------
+# compression with FP8 storage: fp32 arithmetic, output rounded to E4M3
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,m,D,two", [(1003, 4, 128, True), (1003, 4, 512, False), (1000, 128, 512, False),
+                                       (77, 128, 64, False), (40, 4, 32, True)])
+def test_compress_fp8_within_one_ulp_of_oracle(n, m, D, two):
+    """The exact (fp64) compressed value and the GPU's E4M3 output differ by
+    at most one E4M3 step: the GPU rounds its fp32 result to nearest, and the
+    fp32 arithmetic may move a value across a rounding midpoint."""
+    seed = 300 + n + D
+    B = 2
+    xa, xa_c = both((B, n, D), seed, "k_idx", dtype=F8, scale=D ** -0.5)
+    za, za_c = both((B, n, D), seed, "z_idx", dtype=F8, scale=0.5)
+    kw, kw_c = {}, {}
+    if two:
+        xb, xb_c = both((B, n, D), seed, "xb_idx", dtype=F8, scale=D ** -0.5)
+        zb, zb_c = both((B, n, D), seed, "zb_idx", dtype=F8, scale=0.5)
+        kw, kw_c = dict(x_b=xb, z_b=zb), dict(x_b=xb_c, z_b=zb_c)
+    got = csa.csa_compress(xa, za, m, **kw)
+    torch.cuda.synchronize()
+    assert got.dtype == F8
+    want = oracle.compress(xa_c, za_c, m, **kw_c)
+    g = to_np(got)
+    assert g.shape == want.shape
+    assert np.all(np.abs(g - want) <= fp8_ulp(want) * (1 + 1e-9))
+    # and most outputs are the nearest E4M3 value of the exact result
+    assert np.mean(g == oracle.fp8_decode(oracle.fp8_encode(want))) > 0.97
+
+
+def test_compress_fp8_decode_refresh_equals_bulk():
+    B, n, D, m = 2, 128 * 40, 128, 128
+    x = gen((B, n, D), 5, "k_idx", dtype=F8, device="cuda", scale=D ** -0.5)
+    z = gen((B, n, D), 5, "z_idx", dtype=F8, device="cuda", scale=0.5)
+    bulk = csa.hca_compress(x, z, m)
+    L = n // m
+    slot = torch.zeros((B, 1, D), dtype=F8, device="cuda")
+    p0 = n - m
+    csa.hca_compress(x[:, p0:].contiguous(), z[:, p0:].contiguous(), m, n=n, p0=p0, e0=L - 1, e1=L, out=slot,
+                     out_ld=1)
+    torch.cuda.synchronize()
+    # the single-entry launch slices each block over 16 lanes: same value within one E4M3 step
+    a, b = to_np(slot[:, 0]), to_np(bulk[:, L - 1])
+    assert np.all(np.abs(a - b) <= fp8_ulp(b) * (1 + 1e-9))
+
+
+# ---------------------------------------------------------------------------
+# indexer scores and top-k with FP8 q and k
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("HI", [64, 32, 16, 128])
+def test_index_scores_fp8_match_oracle(HI):
+    B, T, m, dI = 2, 3, 4, 128
+    n_ctx = 4 * 3001 + 2
+    L = -(-n_ctx // m)
+    seed = 500 + HI
+    q, q_c = both((B, T, HI, dI), seed, "q_idx", dtype=F8, scale=dI ** -0.5)
+    k, k_c = both((B, L, dI), seed, "k_idx", dtype=F8, scale=dI ** -0.5)
+    w, w_c = both((B, T, HI), seed, "w_idx", dtype=torch.float32, kind="uniform")
+    got = to_np(csa.csa_index_score(q, k, m, w_idx=w, n_ctx=n_ctx))
+    want = oracle.index_scores(q_c, k_c, m, w=w_c, n_ctx=n_ctx)
+    fin = np.isfinite(want)
+    assert np.array_equal(fin, np.isfinite(got))
+    assert np.all(np.isneginf(got[~fin]))
+    for b in range(B):
+        for t in range(T):
+            eps = index_eps_fp8(q_c[b, t], w_c[b, t], k_c[b])
+            f = fin[b, t]
+            assert np.all(np.abs(got[b, t][f] - want[b, t][f]) <= eps[f] + 1e-30)
+
+
+def test_index_fp8_exact_on_grid_inputs():
+    """Grid values k/16 (|k| <= 8, exact in E4M3) and weights in {1, 2}: every
+    partial sum has at most 11 significant bits, so the scores and the top-k
+    are exact, whatever the MFMA's internal summation precision."""
+    B, T, HI, dI, m, k = 2, 2, 64, 128, 4, 256
+    n_ctx = 4 * 6000 + 3
+    L = -(-n_ctx // m)
+    q, q_c = both((B, T, HI, dI), 19, "q_idx", dtype=F8, kind="grid", scale=2.0 ** -4)
+    kk, k_c = both((B, L, dI), 19, "k_idx", dtype=F8, kind="grid", scale=2.0 ** -4)
+    w = gen((B, T, HI), 19, "w_idx", dtype=torch.float32, device="cuda", kind="grid", grid=1).abs() + 1.0
+    w_c = (gen((B, T, HI), 19, "w_idx", dtype=torch.float32, device="cpu", kind="grid", grid=1).abs()
+           + 1.0).double().numpy()
+    got = to_np(csa.csa_index_score(q, kk, m, w_idx=w, n_ctx=n_ctx))
+    want = oracle.index_scores(q_c, k_c, m, w=w_c, n_ctx=n_ctx)
+    assert np.array_equal(got, want)
+    idx = csa.csa_index_topk(q, kk, m, k, w_idx=w, n_ctx=n_ctx).cpu().numpy()
+    widx, _ = oracle.index_topk(q_c, k_c, m, k, w=w_c, n_ctx=n_ctx)
+    assert np.array_equal(idx, widx)
+
+
+@pytest.mark.parametrize("B,T,L,HI,k,wts", [(16, 1, 250000, 64, 1024, True), (4, 3, 9000, 32, 512, False),
+                                             (2, 2, 700, 64, 1024, True), (2, 8, 30000, 16, 256, False),
+                                             (4, 4, 60000, 128, 2048, True)])
+def test_index_topk_fp8_single_pass_equals_score_then_select(B, T, L, HI, k, wts):
+    """The fused scan-and-select path on FP8 keys gives the same indices and
+    scores, bit for bit, as the scores written out and selected by the
+    stand-alone top-k; one row is also checked against the oracle (exact up
+    to certified near ties)."""
+    dI, m = 128, 4
+    n_ctx = m * L
+    seed = 600 + L
+    q, q_c = both((B, T, HI, dI), seed, "q_idx", dtype=F8, scale=dI ** -0.5)
+    kk, k_c = both((B, L, dI), seed, "k_idx", dtype=F8, scale=dI ** -0.5)
+    w = w_c = None
+    if wts:
+        w, w_c = both((B, T, HI), seed, "w_idx", dtype=torch.float32, scale=HI ** -0.5)
+    idx1, s1 = csa.csa_index_topk(q, kk, m, k, w_idx=w, n_ctx=n_ctx, want_scores=True)
+    sc = csa.csa_index_score(q, kk, m, w_idx=w, n_ctx=n_ctx)
+    idx2, s2 = csa.csa_topk_select(sc, m, k, n_ctx=n_ctx, want_scores=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx1, idx2)
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    b, t = B - 1, T - 1
+    nv = min(L, (n_ctx - T + t) // m)
+    want, osc = oracle.index_topk(q_c[b:b + 1, t:t + 1], k_c[b:b + 1], m, k, n_ctx=n_ctx,
+                                  tpos=np.array([n_ctx - T + t]), w=None if w_c is None else w_c[b:b + 1, t:t + 1])
+    eps = index_eps_fp8(q_c[b, t], None if w_c is None else w_c[b, t], k_c[b])[:nv]
+    assert near_tie_check(idx1[b, t].cpu().numpy(), want[0, 0], osc[0, 0], nv, k, eps) <= 4
+
+
+def test_index_topk_fp8_gaussian_exact_up_to_near_ties():
+    B, T, m, HI, dI, k = 2, 3, 4, 64, 128, 1024
+    n_ctx = 4 * 20000 + 1
+    L = -(-n_ctx // m)
+    q, q_c = both((B, T, HI, dI), 23, "q_idx", dtype=F8, scale=dI ** -0.5)
+    kk, k_c = both((B, L, dI), 23, "k_idx", dtype=F8, scale=dI ** -0.5)
+    got = csa.csa_index_topk(q, kk, m, k, n_ctx=n_ctx).cpu().numpy()
+    want, sc = oracle.index_topk(q_c, k_c, m, k, n_ctx=n_ctx)
+    ties = 0
+    for b in range(B):
+        for t in range(T):
+            nv = min(L, (n_ctx - T + t) // m)
+            ties += near_tie_check(got[b, t], want[b, t], sc[b, t], nv, k,
+                                   index_eps_fp8(q_c[b, t], None, k_c[b])[:nv])
+    assert ties <= 6
+
+
+def test_attention_rejects_fp8_storage():
+    B, T, H, d, L, k, W = 1, 1, 64, 128, 100, 8, 4
+    q = torch.zeros((B, T, H, d), dtype=F8, device="cuda")
+    kc = torch.zeros((B, L, d), dtype=F8, device="cuda")
+    idx = torch.zeros((B, T, k), dtype=torch.int32, device="cuda")
+    kr = torch.zeros((B, W, d), dtype=F8, device="cuda")
+    with pytest.raises(csa.CsaError, match="UNSUPPORTED"):
+        csa.csa_sparse_attn(q, kc, kc, idx, kr=kr, vr=kr, W=W, n_ctx=4 * L)
