@@ -27,6 +27,8 @@
 namespace csa {
 namespace {
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
 constexpr int kWaves = 4;
 #ifndef CSA_INDEX_DEPTH
 #define CSA_INDEX_DEPTH 6
@@ -229,9 +231,11 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
 // loop issues no stores (their completions would share the load counter the
 // ring waits on).
 // FP8: keys and queries in OCP E4M3 (128 B per key).  A tile is two 1 KiB
-// loads; the MFMA is v_mfma_f32_16x16x32_fp8_fp8 with the same lane layout
-// as the bf16 one (lane (g, c) supplies row c, k-slots 8g .. 8g+7; checked
-// on the device against an fp64 product of the decoded values).
+// loads, and one v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 operands, unit
+// scales) per 16-head block takes all 128 dims: lane (g, c) supplies 32
+// bytes of row c of each operand, the same bytes for the query and the key,
+// so the product is the full dot product (checked on the device against an
+// fp64 product of the decoded values, output in the usual 16x16 layout).
 template <int MB, bool HAS_W, bool TOPK, bool FP8>
 __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, int64_t parts, int64_t per_wave,
                                                              IndexCandidates co) {
@@ -269,13 +273,13 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
   //  bf16: key kk (0..15) at kk*256; its 16-byte piece p at slot p ^ kk.
   //    Load j covers keys 4j .. 4j+3 (1 KiB contiguous in HBM); lane l writes
   //    slot l%16 of key 4j + l/16, so it fetches piece (l%16) ^ kk.
-  //  FP8: key kk at kk*128, eight 16-byte pieces.  The dot product may take
-  //    its 128 dims in any order shared by both operands: k-step ks, lane
-  //    group g covers dims 32g + 8ks .. +8, so a lane's four k-steps are one
-  //    32-byte block (pieces 2g, 2g+1), stored at block position g ^ (kk & 3)
-  //    (16 keys 128 B apart then hit distinct bank groups).  Load j covers
-  //    keys 8j .. 8j+7; lane l writes slot s = l%8 of key 8j + l/8, so it
-  //    fetches piece 2((s/2) ^ (kk & 3)) + s%2.
+  //  FP8: key kk at kk*128, eight 16-byte pieces; lane group g of the MFMA
+  //    takes dims 32g .. 32g+31 (pieces 2g and 2g+1).  Piece p of key kk sits
+  //    at slot (p + kk/2) % 8, so the 16 keys of one 16-byte read (8 even
+  //    keys on one half of the 256-byte bank row, 8 odd keys on the other)
+  //    hit 16 distinct bank groups.  Load j covers keys 8j .. 8j+7; lane l
+  //    writes slot s = l%8 of key 8j + l/8, so it fetches piece
+  //    (s - kk/2) % 8.
   // Only a tile that runs past the last key (the very end of a row) takes
   // per-lane clamped addresses.
   const char* kbase = static_cast<const char*>(a.k) + b * a.L * KB;
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
     if constexpr (FP8) {
       const int kk = 8 * j + (lane >> 3), sl = lane & 7;
       kkl[j] = kk;
-      voff[j] = kk * 128 + ((2 * ((sl >> 1) ^ (kk & 3)) + (sl & 1)) << 4);
+      voff[j] = kk * 128 + (((sl - (kk >> 1)) & 7) << 4);
     } else {
       kkl[j] = 4 * j + g;
       voff[j] = (4 * j + g) * 256 + ((c16 ^ (4 * j + g)) << 4);
@@ -315,17 +319,11 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
 
   // A operand: query heads (rows) x index dims, resident for the whole kernel.
   bf16x8 afrag[MB][FP8 ? 1 : KS];
-  uint64_t afrag8[MB][FP8 ? KS : 1];
+  i32x8 afrag8[MB];
   if constexpr (FP8) {
     const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + row * HI * DI;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + (mb * 16 + c16) * DI + 32 * g + 16 * h);
-        afrag8[mb][2 * h] = (static_cast<uint64_t>(v[1]) << 32) | v[0];
-        afrag8[mb][2 * h + 1] = (static_cast<uint64_t>(v[3]) << 32) | v[2];
-      }
+    for (int mb = 0; mb < MB; ++mb) afrag8[mb] = *reinterpret_cast<const i32x8*>(qrow + (mb * 16 + c16) * DI + 32 * g);
   } else {
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + row * HI * DI;
 #pragma unroll
@@ -348,41 +346,10 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
   asm volatile("" ::: "memory");
 
   float* sb = sbuf[wave];
-  for (int it = 0; it < ntv; ++it) {
-    if (it + DEPTH - 1 < ntv) {
-      issue(it + DEPTH - 1);
-      wait_tiles<LPT>(DEPTH - 1);
-    } else {
-      wait_tiles<LPT>(ntv - 1 - it);
-    }
-    f32x4 acc[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (FP8) {
-      const uint8_t* t = myring + (it % DEPTH) * TB + c16 * 128 + ((g ^ (c16 & 3)) << 5);
-      const u32x4 x0 = *reinterpret_cast<const u32x4*>(t);
-      const u32x4 x1 = *reinterpret_cast<const u32x4*>(t + 16);
-      const uint64_t cur8[KS] = {(static_cast<uint64_t>(x0[1]) << 32) | x0[0], (static_cast<uint64_t>(x0[3]) << 32) | x0[2],
-                                 (static_cast<uint64_t>(x1[1]) << 32) | x1[0], (static_cast<uint64_t>(x1[3]) << 32) | x1[2]};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(static_cast<long>(afrag8[mb][ks]),
-                                                              static_cast<long>(cur8[ks]), acc[mb], 0, 0, 0);
-    } else {
-      const uint8_t* t = myring + (it % DEPTH) * TB + c16 * 256;
-      bf16x8 cur[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) cur[ks] = *reinterpret_cast<const bf16x8*>(t + (((4 * ks + g) ^ c16) << 4));
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[mb][ks], cur[ks], acc[mb], 0, 0, 0);
-    }
-    // lane holds S[head mb*16 + 4g + r][key c16]: ReLU, head weights, and the
-    // sum over heads (a short tree in-lane, then across the four lane groups).
+  // lane holds S[head mb*16 + 4g + r][key c16] of a tile: ReLU, head
+  // weights, and the sum over heads (a short tree in-lane, then across the
+  // four lane groups), stored at the tile's score slots.
+  auto finish = [&](int itx, const f32x4 (&acc)[MB]) {
     float ps[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -396,8 +363,42 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
 #pragma unroll
       for (int mb = 0; mb + w < MB; mb += 2 * w) ps[mb] += ps[mb + w];
     const float tot = group_sum4(ps[0]);
-    const int64_t s = k0 + static_cast<int64_t>(it) * kStride + c16;
-    if (g == 0) sb[sb_pos(it, c16)] = s < nv ? tot : -INFINITY;
+    const int64_t s = k0 + static_cast<int64_t>(itx) * kStride + c16;
+    if (g == 0) sb[sb_pos(itx, c16)] = s < nv ? tot : -INFINITY;
+  };
+  for (int it = 0; it < ntv; ++it) {
+    if (it + DEPTH - 1 < ntv) {
+      issue(it + DEPTH - 1);
+      wait_tiles<LPT>(DEPTH - 1);
+    } else {
+      wait_tiles<LPT>(ntv - 1 - it);
+    }
+    f32x4 acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (FP8) {
+      // Key c16's 128 bytes sit as eight rotated 16-byte blocks; lane (g, c16)
+      // takes blocks 2g and 2g+1, i.e. k = 32g .. 32g+31, matching afrag8.
+      const uint8_t* t = myring + (it % DEPTH) * TB + c16 * 128;
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(t + (((2 * g + (c16 >> 1)) & 7) << 4));
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(t + (((2 * g + 1 + (c16 >> 1)) & 7) << 4));
+      const i32x8 cur8{static_cast<int>(x0[0]), static_cast<int>(x0[1]), static_cast<int>(x0[2]), static_cast<int>(x0[3]),
+                       static_cast<int>(x1[0]), static_cast<int>(x1[1]), static_cast<int>(x1[2]), static_cast<int>(x1[3])};
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)  // format 0 = E4M3 for both operands, scale exponents 127 = 1.0
+        acc[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afrag8[mb], cur8, acc[mb], 0, 0, 0, 127, 0, 127);
+    } else {
+      const uint8_t* t = myring + (it % DEPTH) * TB + c16 * 256;
+      bf16x8 cur[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) cur[ks] = *reinterpret_cast<const bf16x8*>(t + (((4 * ks + g) ^ c16) << 4));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[mb][ks], cur[ks], acc[mb], 0, 0, 0);
+    }
+    finish(it, acc);
   }
 
   __syncthreads();
