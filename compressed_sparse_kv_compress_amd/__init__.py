@@ -85,6 +85,18 @@ def _dt(t: torch.Tensor) -> int:
     raise TypeError("storage dtype must be bfloat16, float32 or float8_e4m3fn, got %s" % t.dtype)
 
 
+def _attn_dt(q, kc) -> int:
+    """Attention's dtype code: the K/V storage type.  FP8 K/V comes with a
+    bf16 query (and output); otherwise q and the cache share one type."""
+    if kc.dtype == torch.float8_e4m3fn:
+        if q.dtype != torch.bfloat16:
+            raise TypeError("FP8 K/V attention takes a bfloat16 query, got %s" % q.dtype)
+        return CSA_FP8
+    if q.dtype != kc.dtype:
+        raise TypeError("q (%s) and the K/V cache (%s) differ" % (q.dtype, kc.dtype))
+    return _dt(q)
+
+
 def _ptr(t):
     if t is None:
         return None
@@ -232,10 +244,11 @@ def csa_sparse_attn(q, kc, vc, idx, *, kr=None, vr=None, W=0, sink=None, scale=N
     R = 0 if kr is None else kr.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     out, lse = _attn_out(q, out, lse, want_lse)
-    wp, wn = _ws(csa_sparse_attn_workspace(B, T, H, d, k, W, _dt(q)), q.device, ws)
+    dt = _attn_dt(q, kc)
+    wp, wn = _ws(csa_sparse_attn_workspace(B, T, H, d, k, W, dt), q.device, ws)
     st = _csa_sparse_attn(_ptr(q), _ptr(kc), _ptr(vc), L, _ptr(idx), k, _ptr(kr), _ptr(vr), R, W,
                           _ptr(sink), scale, B, T, n_ctx, H, d, out.data_ptr(), _ptr(lse), wp, wn,
-                          _dt(q), _stream(q.device))
+                          dt, _stream(q.device))
     _check(st, "csa_sparse_attn")
     return (out, lse) if want_lse else out
 
@@ -247,9 +260,10 @@ def hca_dense_attn(q, kc, vc, m, *, kr=None, vr=None, W=0, sink=None, scale=None
     R = 0 if kr is None else kr.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     out, lse = _attn_out(q, out, lse, want_lse)
-    wp, wn = _ws(hca_dense_attn_workspace(B, T, H, d, L, m, n_ctx, W, _dt(q)), q.device, ws)
+    dt = _attn_dt(q, kc)
+    wp, wn = _ws(hca_dense_attn_workspace(B, T, H, d, L, m, n_ctx, W, dt), q.device, ws)
     st = _hca_dense_attn(_ptr(q), _ptr(kc), _ptr(vc), L, m, _ptr(kr), _ptr(vr), R, W, _ptr(sink),
-                         scale, B, T, n_ctx, H, d, out.data_ptr(), _ptr(lse), wp, wn, _dt(q),
+                         scale, B, T, n_ctx, H, d, out.data_ptr(), _ptr(lse), wp, wn, dt,
                          _stream(q.device))
     _check(st, "hca_dense_attn")
     return (out, lse) if want_lse else out

@@ -89,6 +89,7 @@ __device__ __forceinline__ int64_t row_offset(const AttnArgs& a, bool sparse, co
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 hbf16x2 __attribute__((ext_vector_type(2)));
 
@@ -107,36 +108,58 @@ __device__ __forceinline__ float* attn_ws_ml(const AttnArgs& a, int nsplit) {
 
 // Staging geometry.  Rows move global -> LDS by direct-to-LDS loads
 // (global_load_lds: one wave instruction = 64 lanes x ESZ bytes of one row,
-// landing contiguously), 32 rows of K and 32 of V per stage, two stages; each
-// of the 8 waves stages 8 rows.  K rows are read as MFMA A operands (16 rows x
-// 16 bytes per 16-lane group): a pitch of 4 banks past a multiple of the bank
-// count keeps them apart.  V rows are read by the LDS transpose load (4 rows x
-// 32 bytes per 16-lane group): a pitch of 8 banks past a multiple does the
-// same for them.
-template <int D>
+// landing contiguously), 32 rows of K and 32 of V per stage, two stage buffers
+// (four for FP8 rows, so as many bytes are in flight); each of the 8 waves
+// stages 8 rows.  bf16 rows: K rows are read as MFMA A
+// operands (16 rows x 16 bytes per 16-lane group): a pitch of 4 banks past a
+// multiple of the bank count keeps them apart.  V rows are read by the LDS
+// transpose load (4 rows x 32 bytes per 16-lane group): a pitch of 8 banks
+// past a multiple does the same for them.  FP8 rows (E4M3, D bytes): K is
+// read 8 bytes per lane (16 rows per 16-lane group) and V by the 8-bit
+// transpose load (rows 4g..4g+3 and 16+4g..16+4g+3, 16 bytes each, per
+// group); one pitch of 6 banks past a multiple separates both.
+template <int D, bool F8>
 struct Ring {
-  static constexpr int ESZ = D == 512 ? 16 : 4;       // bytes per lane per load
-  static constexpr int IPR = D * 2 / (64 * ESZ);      // loads per row
-  static constexpr int ROWS = 32;                     // rows per stage
-  static constexpr int RPW = 2 * ROWS / kWaves;       // rows staged per wave
-  static constexpr int PK = D * 2 + 16;               // K row pitch (bytes)
-  static constexpr int PV = D * 2 + 32;               // V row pitch (bytes)
+  static constexpr int RB = F8 ? D : 2 * D;              // bytes per row
+  static constexpr int ESZ = RB == 1024 ? 16 : 4;        // bytes per lane per load
+  static constexpr int IPR = RB / (64 * ESZ);            // loads per row
+  static constexpr int ROWS = 32;                        // rows per stage
+  static constexpr int RPW = 2 * ROWS / kWaves;          // rows staged per wave
+  static constexpr int PK = F8 ? RB + 24 : RB + 16;      // K row pitch (bytes)
+  static constexpr int PV = F8 ? RB + 24 : RB + 32;      // V row pitch (bytes)
   static constexpr int KBYTES = ROWS * PK;
   static constexpr int STAGE = ROWS * (PK + PV);
-  static constexpr int NS = 2;
-  static constexpr int NI = RPW * IPR;                // loads per wave per stage
-  static constexpr int DH = D / 2;                    // dims per wave
-  static constexpr int OP = DH + 4;                   // epilogue LDS row pitch (floats)
-  static_assert(kWaves * kHeadsPerWave * OP * 4 <= NS * STAGE, "epilogue tile fits the ring");
-  static_assert(NI < 64, "vmcnt range");
+  static constexpr int NS = F8 ? 4 : 2;                 // stage buffers (equal bytes in flight)
+  static constexpr int NI = RPW * IPR;                   // loads per wave per stage
+  static constexpr int DH = D / 2;                       // dims per wave
+  static constexpr int OP = DH + 4;                      // epilogue LDS row pitch (floats)
+  static constexpr int EPI = kWaves * kHeadsPerWave * OP * 4;
+  static constexpr int BYTES = NS * STAGE > EPI ? NS * STAGE : EPI;  // the ring also holds the epilogue tile
+  static_assert(IPR * 64 * ESZ == RB, "whole rows per load group");
+  static_assert((NS - 1) * NI < 64, "vmcnt range");
 };
 constexpr int kMaxIdx = kAttnMaxIdx;  // cached row indices per split (CSA)
+
+// Source of every masked row (past the split's end, or a -1 / out-of-range
+// index): its logit is masked, so its P is 0, and zeros keep 0 * V finite
+// (an FP8 row holding a NaN code would not).  One row of the widest layout.
+__device__ __attribute__((aligned(16))) uint8_t kZeroRow[1024];
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until at most `ahead` stages of NI loads each are outstanding.
+template <int NI, int NS>
+__device__ __forceinline__ void wait_stages(int ahead) {
+  static_assert(NS == 2 || NS == 4, "stage buffers");
+  if (NS == 4 && ahead >= 3) wait_vmcnt<(NS == 4 ? 3 : 0) * NI>();
+  else if (NS == 4 && ahead == 2) wait_vmcnt<(NS == 4 ? 2 : 0) * NI>();
+  else if (ahead >= 1) wait_vmcnt<NI>();
+  else wait_vmcnt<0>();
 }
 
 // Direct global -> LDS load of one row piece: lane i's ESZ bytes at g land at
@@ -184,11 +207,11 @@ __device__ __forceinline__ void dma_row(const char* g, const uint8_t* lds) {
 // indices come from the split's index cache with one vector LDS read.  An
 // empty row (past the split's end, or a -1 / out-of-range index) is read from
 // the dummy row and flagged in okrow (K waves only), so its logit is masked.
-template <int D, bool SPARSE, bool NT>
+template <int D, bool F8, bool SPARSE, bool NT>
 __device__ __forceinline__ void issue_rows(const char* cbase, const char* rbase, const char* dummy, const int* sidx,
                                            uint8_t* lds, int pitch, int c0, int n_cmp, int r_begin, int r_end,
                                            int win0, int L, int lane, int* okrow) {
-  using C = Ring<D>;
+  using C = Ring<D, F8>;
   int sv = 0;
   if (SPARSE) {
     const int v = c0 + lane;
@@ -201,7 +224,7 @@ __device__ __forceinline__ void issue_rows(const char* cbase, const char* rbase,
     int s = v;
     if (SPARSE) s = cmp ? __builtin_amdgcn_readlane(sv, j) : 0;
     const bool ok = v < r_end && (!SPARSE || !cmp || (s >= 0 && s < L));
-    const char* row = cmp ? cbase + static_cast<int64_t>(s) * (2 * D) : rbase + static_cast<int64_t>(v + win0) * (2 * D);
+    const char* row = cmp ? cbase + static_cast<int64_t>(s) * C::RB : rbase + static_cast<int64_t>(v + win0) * C::RB;
     const char* src = ok ? row : dummy;
 #pragma unroll
     for (int p = 0; p < C::IPR; ++p)
@@ -219,6 +242,24 @@ __device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
+// 8-bit transpose load: for a 16-lane group, lanes 2j and 2j+1 address the
+// two 8-byte halves of a 16-byte piece of row j, and lane c receives byte c
+// of the eight rows, row j in byte j.
+__device__ __forceinline__ i32x2 lds_tr8(const uint8_t* p) {
+  typedef i32x2 __attribute__((address_space(3))) lds_i32x2;
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
+}
+
+// Eight E4M3 codes (byte i = element i) to bf16: exact, every E4M3 value is a
+// bf16 value (3 of bf16's 7 fraction bits, exponents 2^-9 .. 2^8).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(i32x2 w) {
+  const hbf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, false);
+  const hbf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, true);
+  const hbf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, false);
+  const hbf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // One workgroup = 64 heads of one query over one split of its row list;
 // wave w takes heads 16(w%4) .. +16 and half w/4 of d.  Per 32-row stage a
 // wave computes its half of S^T = K Q^T (rows x 16 heads, two 16x16x32 tiles)
@@ -229,16 +270,16 @@ __device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
 // operand comes from the LDS transpose load: for 16-lane group g, lanes
 // 4j..4j+3 address row r0+j, 16 dims, and lane c receives dim c of those four
 // rows.  Two waves per SIMD hide each other's LDS and MFMA latency.
-template <int D, bool SPARSE, bool NT>
+template <int D, bool F8, bool SPARSE, bool NT>
 __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
-  using C = Ring<D>;
+  using C = Ring<D, F8>;
   constexpr int KSQ = C::DH / 32;  // k-steps of the wave's half of Q K^T
   constexpr int NB = C::DH / 16;   // 16-dim output blocks of the wave
   constexpr float kRebase = 8.f;   // re-base the running max only when it grows by > 2^8
-  __shared__ __attribute__((aligned(16))) uint8_t ring[C::NS * C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[C::BYTES];
   __shared__ __attribute__((aligned(16))) f32x4 xs[kWaves][2][64];  // partial scores
   __shared__ int sidx[SPARSE ? kMaxIdx : 1];
-  __shared__ __attribute__((aligned(16))) int okf[3][C::ROWS];
+  __shared__ __attribute__((aligned(16))) int okf[C::NS + 1][C::ROWS];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hq = wave % kHeadGroups;  // head group
@@ -263,11 +304,10 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
   // Waves 0-3 stage K rows 8w .. 8w+7 of each stage; waves 4-7 the V rows.
   const int mat = wave / (kWaves / 2);
   const int row0 = (wave % (kWaves / 2)) * C::RPW;
-  const uint16_t* cb = static_cast<const uint16_t*>(mat ? a.vc : a.kc) + b * a.L * D;
-  const uint16_t* rb = static_cast<const uint16_t*>(mat ? a.vr : a.kr) + b * a.R * D;
-  const char* cbase = reinterpret_cast<const char*>(cb);
-  const char* rbase = reinterpret_cast<const char*>(rb);
-  const char* dummy = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.q) + bt * a.H * D);
+  const char* cbase = static_cast<const char*>(mat ? a.vc : a.kc) + b * a.L * C::RB;
+  const char* rbase = static_cast<const char*>(mat ? a.vr : a.kr) + b * a.R * C::RB;
+  const char* dummy = reinterpret_cast<const char*>(kZeroRow);
+  static_assert(C::RB <= static_cast<int>(sizeof(kZeroRow)), "zero row covers a row");
   const int pitch = mat ? C::PV : C::PK;
   const int moff = (mat ? C::KBYTES : 0) + row0 * pitch;
   const int n_cmp = static_cast<int>(rm.n_cmp);
@@ -276,19 +316,19 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
   const int Lc = static_cast<int>(a.L);
   const int nst = static_cast<int>((r_end - r_begin + C::ROWS - 1) / C::ROWS);
 
-  // Pipeline: K of stage c+2 is issued as soon as every wave is done with
-  // QK of stage c (barrier B), V of stage c+1 once every wave is done with PV
-  // of stage c-1 (barrier A); K therefore keeps two stages in flight.  The
-  // row flags have three buffers because K(c+2) sets them while stage c still
-  // reads its own.
+  // Pipeline over NS stage buffers: K of stage c+NS is issued as soon as
+  // every wave is done with QK of stage c (barrier B), V of stage c+NS-1 once
+  // every wave is done with PV of stage c-1 (barrier A); K therefore keeps NS
+  // stages in flight, V NS-1.  The row flags have NS+1 buffers because
+  // K(c+NS) sets them while stage c still reads its own.
   auto issue = [&](int st) {
-    issue_rows<D, SPARSE, NT>(cbase, rbase, dummy, sidx, ring + (st & 1) * C::STAGE + moff, pitch,
+    issue_rows<D, F8, SPARSE, NT>(cbase, rbase, dummy, sidx, ring + (st % C::NS) * C::STAGE + moff, pitch,
                           rb0 + st * C::ROWS + row0, n_cmp, rb0, re0, win0, Lc, lane,
-                          mat ? nullptr : okf[st % 3] + row0);
+                          mat ? nullptr : okf[st % (C::NS + 1)] + row0);
   };
   auto prime = [&]() {
-    if (nst > 0) issue(0);
-    if (mat == 0 && nst > 1) issue(1);
+    for (int st = 0; st < C::NS - 1 + (mat == 0 ? 1 : 0); ++st)
+      if (st < nst) issue(st);
   };
 
   // HCA rows need nothing but their position, so the first stages are on
@@ -319,41 +359,45 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
   const float sl2 = a.scale * kLog2e;
 
   for (int c = 0; c < nst; ++c) {
-    const int buf = c & 1;
-    if (mat == 0) {  // this wave's K rows of stage c (K of c+1 may stay in flight)
-      if (c + 1 < nst) wait_vmcnt<C::NI>();
-      else wait_vmcnt<0>();
-    }
+    const int buf = c % C::NS;
+    // stages after c already issued for this wave's matrix (K at this point,
+    // V after its issue below): they may stay in flight
+    const int ahead = C::NS - 1 < nst - 1 - c ? C::NS - 1 : nst - 1 - c;
+    if (mat == 0) wait_stages<C::NI, C::NS>(ahead);  // this wave's K rows of stage c
     __syncthreads();  // A: K(c) in LDS; every wave is done with PV(c-1)
-    if (mat == 1 && c + 1 < nst) issue(c + 1);
+    if (mat == 1 && c + C::NS - 1 < nst) issue(c + C::NS - 1);
     const uint8_t* Ks = ring + buf * C::STAGE;
     const uint8_t* Vs = Ks + C::KBYTES;
 
     // ---- this half's S^T = K Q^T: two 16-row tiles x 16 heads --------------
     f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-    const uint8_t* kp = Ks + c16 * C::PK + dh * C::DH * 2 + g * 16;
+    // lane (g, c16): row c16 (and 16 + c16), dims dh*DH + 32ks + 8g .. +8
+    const uint8_t* kp = Ks + c16 * C::PK + (dh * C::DH + g * 8) * (F8 ? 1 : 2);
 #pragma unroll
     for (int ks = 0; ks < KSQ; ++ks) {
-      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kp + ks * 64);
-      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kp + 16 * C::PK + ks * 64);
+      bf16x8 k0, k1;
+      if constexpr (F8) {
+        k0 = fp8x8_to_bf16(*reinterpret_cast<const i32x2*>(kp + ks * 32));
+        k1 = fp8x8_to_bf16(*reinterpret_cast<const i32x2*>(kp + 16 * C::PK + ks * 32));
+      } else {
+        k0 = *reinterpret_cast<const bf16x8*>(kp + ks * 64);
+        k1 = *reinterpret_cast<const bf16x8*>(kp + 16 * C::PK + ks * 64);
+      }
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks], s1, 0, 0, 0);
     }
     xs[wave][0][lane] = s0;
     xs[wave][1][lane] = s1;
-    if (mat == 1) {  // this wave's V rows of stage c (V of c+1 may stay in flight)
-      if (c + 1 < nst) wait_vmcnt<C::NI>();
-      else wait_vmcnt<0>();
-    }
+    if (mat == 1) wait_stages<C::NI, C::NS>(ahead);  // this wave's V rows of stage c
     __syncthreads();  // B: V(c) in LDS; every wave is done with K(c)
-    if (mat == 0 && c + 2 < nst) issue(c + 2);
+    if (mat == 0 && c + C::NS < nst) issue(c + C::NS);
     s0 += xs[wave ^ kHeadGroups][0][lane];
     s1 += xs[wave ^ kHeadGroups][1][lane];
 
     // Online softmax (log2 units) for head c16 over its 8 rows here and the
     // other groups' 24, against a lazily re-based running max.
-    const i32x4 ok0 = *reinterpret_cast<const i32x4*>(&okf[c % 3][4 * g]);
-    const i32x4 ok1 = *reinterpret_cast<const i32x4*>(&okf[c % 3][16 + 4 * g]);
+    const i32x4 ok0 = *reinterpret_cast<const i32x4*>(&okf[c % (C::NS + 1)][4 * g]);
+    const i32x4 ok1 = *reinterpret_cast<const i32x4*>(&okf[c % (C::NS + 1)][16 + 4 * g]);
     float sv[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -393,14 +437,25 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
 
     // ---- O += P V over the 32 rows: k slot 8g+j <-> row 4g+j (j < 4) or
     // row 16+4g+(j-4) -------------------------------------------------------
-    const uint8_t* v0 = Vs + (4 * g + (c16 >> 2)) * C::PV + (c16 & 3) * 8 + dh * C::DH * 2;
-    const uint8_t* v1 = v0 + 16 * C::PV;
+    if constexpr (F8) {
+      // lanes 2j, 2j+1 of group g address row 4g+j (j < 4) or 16+4g+(j-4)
+      const int j = c16 >> 1;
+      const uint8_t* v8 = Vs + (j < 4 ? 4 * g + j : 12 + 4 * g + j) * C::PV + (c16 & 1) * 8 + dh * C::DH;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const s16x4 lo = lds_tr16(v0 + nb * 32);
-      const s16x4 hi = lds_tr16(v1 + nb * 32);
-      const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bv, oacc[nb], 0, 0, 0);
+      for (int nb = 0; nb < NB; ++nb) {
+        const bf16x8 bv = fp8x8_to_bf16(lds_tr8(v8 + nb * 16));
+        oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bv, oacc[nb], 0, 0, 0);
+      }
+    } else {
+      const uint8_t* v0 = Vs + (4 * g + (c16 >> 2)) * C::PV + (c16 & 3) * 8 + dh * C::DH * 2;
+      const uint8_t* v1 = v0 + 16 * C::PV;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const s16x4 lo = lds_tr16(v0 + nb * 32);
+        const s16x4 hi = lds_tr16(v1 + nb * 32);
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bv, oacc[nb], 0, 0, 0);
+      }
     }
   }
   __syncthreads();  // the ring is reused below
@@ -595,9 +650,9 @@ __global__ __launch_bounds__(64) void attn_f32(AttnArgs a, int sparse_i) {
 
 }  // namespace
 
-int attn_splits(int64_t B, int64_t T, int64_t H, int64_t d, int64_t max_rows, bool bf16, bool sparse) {
+int attn_splits(int64_t B, int64_t T, int64_t H, int64_t d, int64_t max_rows, Dt dt, bool sparse) {
   (void)d;
-  if (!bf16) return 1;
+  if (dt == kF32) return 1;
   const int64_t base = B * T * (H / kHeadsPerWg);
   const int64_t target = 256;  // workgroups wanted per launch (one per CU)
   int64_t ns = (target + base - 1) / base;
@@ -625,9 +680,9 @@ size_t attn_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t d, int nsplit) {
   return static_cast<size_t>(B * T) * nsplit * H * (d * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
-hipError_t launch_attn(const AttnArgs& a, bool sparse, bool bf16, int nsplit, hipStream_t s) {
+hipError_t launch_attn(const AttnArgs& a, bool sparse, Dt dt, int nsplit, hipStream_t s) {
   if (a.B * a.T == 0) return hipSuccess;
-  if (!bf16) {
+  if (dt == kF32) {
     hipLaunchKernelGGL(attn_f32, dim3(static_cast<uint32_t>(a.B * a.T * a.H)), dim3(64),
                        a.d * sizeof(float), s, a, sparse ? 1 : 0);
     return hipGetLastError();
@@ -636,18 +691,21 @@ hipError_t launch_attn(const AttnArgs& a, bool sparse, bool bf16, int nsplit, hi
   // One query per sequence (decode): every row is read once, nontemporal.
   // Several (prefill): rows are shared between the queries, cached.
   const bool once = a.T == 1;
-#define CSA_ATTN_LAUNCH(D_)                                                                                         \
-  case D_:                                                                                                          \
-    if (sparse && once) hipLaunchKernelGGL((attn_mfma<D_, true, true>), grid, dim3(64 * kWaves), 0, s, a, nsplit);   \
-    else if (sparse) hipLaunchKernelGGL((attn_mfma<D_, true, false>), grid, dim3(64 * kWaves), 0, s, a, nsplit);     \
-    else if (once) hipLaunchKernelGGL((attn_mfma<D_, false, true>), grid, dim3(64 * kWaves), 0, s, a, nsplit);       \
-    else hipLaunchKernelGGL((attn_mfma<D_, false, false>), grid, dim3(64 * kWaves), 0, s, a, nsplit);                \
-    break;
-  switch (a.d) {
-    CSA_ATTN_LAUNCH(128)
-    CSA_ATTN_LAUNCH(256)
-    CSA_ATTN_LAUNCH(512)
-    default: return hipErrorInvalidValue;
+#define CSA_ATTN_LAUNCH(D_, F8_)                                                                                 \
+  if (sparse && once) hipLaunchKernelGGL((attn_mfma<D_, F8_, true, true>), grid, dim3(64 * kWaves), 0, s, a, nsplit);  \
+  else if (sparse) hipLaunchKernelGGL((attn_mfma<D_, F8_, true, false>), grid, dim3(64 * kWaves), 0, s, a, nsplit);    \
+  else if (once) hipLaunchKernelGGL((attn_mfma<D_, F8_, false, true>), grid, dim3(64 * kWaves), 0, s, a, nsplit);      \
+  else hipLaunchKernelGGL((attn_mfma<D_, F8_, false, false>), grid, dim3(64 * kWaves), 0, s, a, nsplit);
+  if (dt == kFP8) {
+    if (a.d != 512) return hipErrorInvalidValue;
+    CSA_ATTN_LAUNCH(512, true)
+  } else {
+    switch (a.d) {
+      case 128: CSA_ATTN_LAUNCH(128, false) break;
+      case 256: CSA_ATTN_LAUNCH(256, false) break;
+      case 512: CSA_ATTN_LAUNCH(512, false) break;
+      default: return hipErrorInvalidValue;
+    }
   }
 #undef CSA_ATTN_LAUNCH
   hipError_t e = hipGetLastError();
@@ -657,8 +715,9 @@ hipError_t launch_attn(const AttnArgs& a, bool sparse, bool bf16, int nsplit, hi
   return hipGetLastError();
 }
 
-bool attn_shape_supported(int64_t H, int64_t d, bool bf16) {
-  if (!bf16) return d >= 1 && d <= 512;
+bool attn_shape_supported(int64_t H, int64_t d, Dt dt) {
+  if (dt == kF32) return d >= 1 && d <= 512;
+  if (dt == kFP8) return H % kHeadsPerWg == 0 && d == 512;
   return H % kHeadsPerWg == 0 && (d == 128 || d == 256 || d == 512);
 }
 

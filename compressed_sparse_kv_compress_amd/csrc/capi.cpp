@@ -9,11 +9,6 @@
 #include "../../include/csa.h"
 #include "kernels.hpp"
 
-namespace csa {
-bool index_shape_supported(int64_t HI, int64_t dI, bool bf16);
-bool attn_shape_supported(int64_t H, int64_t d, bool bf16);
-}  // namespace csa
-
 namespace {
 
 thread_local char g_err[512] = "";
@@ -108,13 +103,12 @@ csa_status_t attn_common(const void* q, const void* kc, const void* vc, int64_t 
                          int64_t B, int64_t T, int64_t n_ctx, int64_t H, int64_t d, void* out,
                          float* lse, csa_dtype_t dt) {
   REQUIRE(dtype_ok(dt), "unknown dtype %d", static_cast<int>(dt));
-  if (dt == CSA_FP8) return fail(CSA_ERR_UNSUPPORTED, "attention has no FP8 storage kernels");
   REQUIRE(B >= 0 && T >= 1 && n_ctx >= T && L >= 0 && H >= 1 && d >= 1 && W >= 0,
           "need B >= 0, 1 <= T <= n_ctx, L >= 0, H >= 1, d >= 1, W >= 0");
   REQUIRE(std::isfinite(scale), "scale is not finite");
   REQUIRE(L <= (int64_t(1) << 30) && R <= (int64_t(1) << 30) && W <= (int64_t(1) << 30),
           "L, R and W must not exceed 2^30 rows");
-  if (!csa::attn_shape_supported(H, d, dt == CSA_BF16))
+  if (!csa::attn_shape_supported(H, d, to_dt(dt)))
     return fail(CSA_ERR_UNSUPPORTED, "no attention kernel for H=%lld d=%lld dtype=%d", (long long)H,
                 (long long)d, static_cast<int>(dt));
   if (W > 0) {
@@ -255,21 +249,20 @@ csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k
 size_t csa_sparse_attn_workspace(int64_t B, int64_t T, int64_t H, int64_t d, int64_t k, int64_t W,
                                  csa_dtype_t dtype) {
   if (B <= 0 || T <= 0) return 0;
-  const int ns = csa::attn_splits(B, T, H, d, k + W, dtype == CSA_BF16, true);
+  const int ns = csa::attn_splits(B, T, H, d, k + W, to_dt(dtype), true);
   return csa::attn_ws_bytes(B, T, H, d, ns);
 }
 
 size_t hca_dense_attn_workspace(int64_t B, int64_t T, int64_t H, int64_t d, int64_t L, int64_t m,
                                 int64_t n_ctx, int64_t W, csa_dtype_t dtype) {
   if (B <= 0 || T <= 0 || m <= 0) return 0;
-  const int ns = csa::attn_splits(B, T, H, d, dense_max_rows(L, m, n_ctx, W), dtype == CSA_BF16, false);
+  const int ns = csa::attn_splits(B, T, H, d, dense_max_rows(L, m, n_ctx, W), to_dt(dtype), false);
   return csa::attn_ws_bytes(B, T, H, d, ns);
 }
 
 static csa_status_t attn_launch(const csa::AttnArgs& a, bool sparse, int64_t max_rows, csa_dtype_t dt,
                                 void* ws, size_t ws_bytes, void* stream) {
-  const bool bf16 = dt == CSA_BF16;
-  const int ns = csa::attn_splits(a.B, a.T, a.H, a.d, max_rows, bf16, sparse);
+  const int ns = csa::attn_splits(a.B, a.T, a.H, a.d, max_rows, to_dt(dt), sparse);
   const size_t need = csa::attn_ws_bytes(a.B, a.T, a.H, a.d, ns);
   if (need > 0) {
     if (ws == nullptr || ws_bytes < need)
@@ -279,7 +272,7 @@ static csa_status_t attn_launch(const csa::AttnArgs& a, bool sparse, int64_t max
   csa::AttnArgs b = a;
   b.ws = static_cast<float*>(ws);
   b.ws_bytes = ws_bytes;
-  return hip_status(csa::launch_attn(b, sparse, bf16, ns, static_cast<hipStream_t>(stream)),
+  return hip_status(csa::launch_attn(b, sparse, to_dt(dt), ns, static_cast<hipStream_t>(stream)),
                     "attention launch");
 }
 
@@ -291,8 +284,8 @@ csa_status_t csa_sparse_attn(const void* q, const void* kc, const void* vc, int6
   csa_status_t st = attn_common(q, kc, vc, L, kr, vr, R, W, sink, scale, B, T, n_ctx, H, d, out, lse, dtype);
   if (st != CSA_OK) return st;
   REQUIRE(k >= 0, "k < 0");
-  if (dtype == CSA_BF16 && k + W > int64_t(csa::kAttnMaxSplits) * csa::kAttnMaxIdx)
-    return fail(CSA_ERR_UNSUPPORTED, "bf16 sparse attention supports k + W <= %lld rows (got %lld)",
+  if (dtype != CSA_F32 && k + W > int64_t(csa::kAttnMaxSplits) * csa::kAttnMaxIdx)
+    return fail(CSA_ERR_UNSUPPORTED, "MFMA sparse attention supports k + W <= %lld rows (got %lld)",
                 (long long)csa::kAttnMaxSplits * csa::kAttnMaxIdx, (long long)(k + W));
   if (B == 0) return CSA_OK;
   if (k > 0) REQUIRE_PTR(idx);

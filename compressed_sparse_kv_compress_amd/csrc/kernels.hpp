@@ -113,15 +113,16 @@ struct AttnArgs {
   size_t ws_bytes;
 };
 // Number of row splits the attention launch uses, and its workspace bytes.
-// bf16 attention: at most kAttnMaxSplits splits per query (the combine kernel
-// gives one lane to each), and a CSA split caches at most kAttnMaxIdx row
-// indices, so a sparse row list (k + W) is limited to their product.
+// MFMA attention (bf16, or FP8 K/V with bf16 q and out): at most
+// kAttnMaxSplits splits per query (the combine kernel gives one lane to each),
+// and a CSA split caches at most kAttnMaxIdx row indices, so a sparse row list
+// (k + W) is limited to their product.  dt names the K/V storage type.
 constexpr int kAttnMaxSplits = 64;
 constexpr int kAttnMaxIdx = 2048;
-int attn_splits(int64_t B, int64_t T, int64_t H, int64_t d, int64_t max_rows, bool bf16, bool sparse);
+int attn_splits(int64_t B, int64_t T, int64_t H, int64_t d, int64_t max_rows, Dt dt, bool sparse);
 size_t attn_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t d, int nsplit);
-hipError_t launch_attn(const AttnArgs& a, bool sparse, bool bf16, int nsplit, hipStream_t s);
-bool attn_shape_supported(int64_t H, int64_t d, bool bf16);
+hipError_t launch_attn(const AttnArgs& a, bool sparse, Dt dt, int nsplit, hipStream_t s);
+bool attn_shape_supported(int64_t H, int64_t d, Dt dt);
 bool index_shape_supported(int64_t HI, int64_t dI, Dt dt);
 
 }  // namespace csa

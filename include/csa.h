@@ -35,7 +35,11 @@
  *     csa_compress / hca_compress (inputs and output in FP8, arithmetic in
  *     fp32, output rounded to nearest even) and by csa_index_score /
  *     csa_index_topk (q_idx and k_idx in FP8, d_I = 128, H_I in {16, 32, 64,
- *     128}).  The attention entry points return CSA_ERR_UNSUPPORTED for it.
+ *     128}), and by the attention entry points for the cached K/V only
+ *     (kc, vc, kr, vr in FP8; q and out stay bf16; d = 512, H % 64 == 0):
+ *     each code converts exactly to bf16 and the arithmetic is the bf16
+ *     path's.  FP8 carries no scale argument: a per-tensor K scale folds into
+ *     `scale`, a V scale into the caller's use of `out`.
  *   - Positions: a batch holds B sequences of n_ctx tokens (uniform length).
  *     The T queries of a sequence sit at positions t_i = n_ctx - T + i.
  *     Compressed entry s covers tokens [s*m, (s+1)*m) and is visible to the
@@ -153,17 +157,20 @@ csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k
  * value:
  *   out[b][t][h] = sum_i e^{l_i} v_i / (e^{sigma_h} + sum_i e^{l_i})
  *   lse[b][t][h] = log(e^{sigma_h} + sum_i e^{l_i})        (natural log)
- *   q   : [B][T][H][d] dtype        kc, vc : [B][L][d] dtype
+ *   q   : [B][T][H][d] dtype (bf16 when dtype is CSA_FP8)
+ *   kc, vc : [B][L][d] dtype
  *   idx : int32 [B][T][k], entries in [0, L) or -1
  *   kr, vr : [B][R][d] raw positions n_ctx-R .. n_ctx-1 (NULL when W == 0);
  *            R >= T + W - 1 and R <= n_ctx when W > 0
- *   sink: fp32 [H] or NULL (= no sink)   out : [B][T][H][d] dtype
+ *   sink: fp32 [H] or NULL (= no sink)
+ *   out : [B][T][H][d] dtype (bf16 when dtype is CSA_FP8)
  *   lse : fp32 [B][T][H] or NULL
  *   ws  : csa_sparse_attn_workspace(...) bytes (may be 0 => ws may be NULL),
  *         16-byte aligned; holds the per-split partial rows of a launch
  *         split over the row list (its contents are scratch)
  * bf16 needs H % 64 == 0, d in {128, 256, 512} and k + W <= 131072;
- * fp32 needs d <= 512.  L, R and W are at most 2^30.  Unsupported shapes
+ * FP8 (K/V storage, bf16 q and out) needs H % 64 == 0, d = 512 and
+ * k + W <= 131072; fp32 needs d <= 512.  L, R and W are at most 2^30.  Unsupported shapes
  * return CSA_ERR_UNSUPPORTED, nothing is launched.
  * ------------------------------------------------------------------------- */
 size_t csa_sparse_attn_workspace(int64_t B, int64_t T, int64_t H, int64_t d, int64_t k, int64_t W,

@@ -105,9 +105,9 @@ def test_index_and_attention_reject_bad_arguments(lib):
 
 
 def test_fp8_storage_is_validated(lib):
-    """CSA_FP8 (2) is a known dtype: accepted by compression and the indexer
-    (d_I = 128, H_I a multiple of 16 up to 128), rejected as unsupported by
-    attention; 3 is unknown."""
+    """CSA_FP8 (2) is a known dtype: accepted by compression, the indexer
+    (d_I = 128, H_I a multiple of 16 up to 128) and attention over an FP8 K/V
+    cache (d = 512 only); 3 is unknown."""
     idx_args = [V] * 3 + [I] * 8 + [V, V, V, Z, ctypes.c_int, V]
     # FP8 indexer with d_I = 64: no kernel
     assert _call(lib, "csa_index_topk", idx_args, FAKE, None, FAKE, 1, 1, 100, 25, 64, 64, 4, 8,
@@ -122,11 +122,18 @@ def test_fp8_storage_is_validated(lib):
     assert _call(lib, "csa_index_topk", idx_args, FAKE, None, FAKE, 1, 1, 100, 25, 64, 128, 4, 8,
                  FAKE, None, FAKE, 1 << 20, 3, None) == 1
     attn = [V] * 3 + [I, V, I, V, V, I, I, V, F] + [I] * 5 + [V, V, V, Z, ctypes.c_int, V]
+    # FP8 K/V attention with d = 256: no kernel
     assert _call(lib, "csa_sparse_attn", attn, FAKE, FAKE, FAKE, 10, FAKE, 4, None, None, 0, 0,
-                 None, 0.1, 1, 1, 40, 64, 512, FAKE, None, None, 0, 2, None) == 2
+                 None, 0.1, 1, 1, 40, 64, 256, FAKE, None, None, 0, 2, None) == 2
     dense = [V] * 3 + [I, I, V, V, I, I, V, F] + [I] * 5 + [V, V, V, Z, ctypes.c_int, V]
     assert _call(lib, "hca_dense_attn", dense, FAKE, FAKE, FAKE, 7813, 128, None, None, 0, 0, None,
-                 0.04, 4, 1, 1000000, 64, 512, FAKE, None, None, 0, 2, None) == 2
+                 0.04, 4, 1, 1000000, 64, 256, FAKE, None, None, 0, 2, None) == 2
+    # d = 512 with H = 48: no kernel either
+    assert _call(lib, "hca_dense_attn", dense, FAKE, FAKE, FAKE, 7813, 128, None, None, 0, 0, None,
+                 0.04, 4, 1, 1000000, 48, 512, FAKE, None, None, 0, 2, None) == 2
+    # ... and with a supported shape, a missing workspace is the error (nothing is launched)
+    assert _call(lib, "hca_dense_attn", dense, FAKE, FAKE, FAKE, 7813, 128, None, None, 0, 0, None,
+                 0.04, 4, 1, 1000000, 64, 512, FAKE, None, None, 0, 2, None) == 3
     # FP8 compression: nothing to do is fine (no launch), D not a multiple of 8 is an error
     args = [V] * 6 + [I] * 9 + [ctypes.c_int, V]
     assert _call(lib, "csa_compress", args, None, None, None, None, None, None,

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import both, fp8_ulp, gen, index_eps_fp8, near_tie_check, to_np
+from helpers import BF16_TOL, both, fp8_ulp, gen, index_eps_fp8, near_tie_check, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -168,11 +168,109 @@ def test_index_topk_fp8_gaussian_exact_up_to_near_ties():
     assert ties <= 6
 
 
-def test_attention_rejects_fp8_storage():
-    B, T, H, d, L, k, W = 1, 1, 64, 128, 100, 8, 4
-    q = torch.zeros((B, T, H, d), dtype=F8, device="cuda")
+# ---------------------------------------------------------------------------
+# attention over an FP8 K/V cache (bf16 query and output)
+# ---------------------------------------------------------------------------
+
+def _attn_fp8_inputs(B, T, H, d, L, R, seed, kv_scale):
+    q, q_c = both((B, T, H, d), seed, "q", dtype=torch.bfloat16, scale=d ** -0.5)
+    kc, kc_c = both((B, L, d), seed, "kc", dtype=F8, scale=kv_scale)
+    vc, vc_c = both((B, L, d), seed, "vc", dtype=F8, scale=kv_scale)
+    kr, kr_c = both((B, R, d), seed, "kr", dtype=F8, scale=kv_scale)
+    vr, vr_c = both((B, R, d), seed, "vr", dtype=F8, scale=kv_scale)
+    sk, sk_c = both((H,), seed, "sink", dtype=torch.float32)
+    return (q, kc, vc, kr, vr, sk), (q_c, kc_c, vc_c, kr_c, vr_c, sk_c)
+
+
+# kv_scale 1/sqrt(d): K/V values as stored by the bf16 workloads (many E4M3
+# subnormals); kv_scale 1: unit-scale codes with the K scale folded into the
+# softmax scale (scale = 1/d), the way a per-tensor FP8 scale is applied.
+@pytest.mark.parametrize("B,T,L,k,W,kv_scale,use_sink", [
+    (2, 1, 4000, 1024, 128, 512 ** -0.5, True),
+    (1, 3, 300, 100, 7, 1.0, False),
+    (2, 2, 900, 64, 0, 1.0, True),
+    (1, 40, 500, 64, 16, 512 ** -0.5, True),
+    (1, 520, 300, 64, 16, 1.0, True),
+])
+def test_sparse_attn_fp8_matches_oracle(B, T, L, k, W, kv_scale, use_sink):
+    import synthetic as syn
+    H, d, m = 64, 512, 4
+    n_ctx = L * m
+    R = T + max(W, 1) - 1
+    g, c = _attn_fp8_inputs(B, T, H, d, L, R, 53 + T, kv_scale)
+    q, kc, vc, kr, vr, sk = g
+    q_c, kc_c, vc_c, kr_c, vr_c, sk_c = c
+    scale = d ** -0.5 if kv_scale != 1.0 else 1.0 / d
+    tpos = np.arange(n_ctx - T, n_ctx)
+    nv = np.minimum(tpos // m, L)
+    idx_c = syn.sample_indices(9, syn.TID["idx"], B * T, k, np.tile(nv, B) - 3).reshape(B, T, k)
+    idx = idx_c.cuda()
+    out, lse = csa.csa_sparse_attn(q, kc, vc, idx, kr=kr if W else None, vr=vr if W else None, W=W,
+                                   sink=sk if use_sink else None, scale=scale, n_ctx=n_ctx, want_lse=True)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.bfloat16
+    o_w, l_w = oracle.sparse_attn(q_c, kc_c, vc_c, idx_c.numpy(), kr_c, vr_c, W,
+                                  sink=sk_c if use_sink else None, scale=scale, n_ctx=n_ctx)
+    assert np.max(np.abs(to_np(out) - o_w)) <= BF16_TOL
+    assert np.max(np.abs(to_np(lse) - l_w)) <= 1e-3
+
+
+@pytest.mark.parametrize("B,T,L,m,W,kv_scale", [
+    (2, 1, 3000, 128, 0, 512 ** -0.5),
+    (1, 2, 700, 4, 128, 1.0),
+    (1, 40, 100, 4, 16, 512 ** -0.5),
+    (1, 1, 7813, 128, 128, 1.0),
+])
+def test_dense_attn_fp8_matches_oracle(B, T, L, m, W, kv_scale):
+    H, d = 64, 512
+    n_ctx = L * m - (m // 2)
+    R = T + max(W, 1) - 1
+    g, c = _attn_fp8_inputs(B, T, H, d, L, R, 61 + L, kv_scale)
+    q, kc, vc, kr, vr, sk = g
+    q_c, kc_c, vc_c, kr_c, vr_c, sk_c = c
+    scale = d ** -0.5 if kv_scale != 1.0 else 1.0 / d
+    out, lse = csa.hca_dense_attn(q, kc, vc, m, kr=kr if W else None, vr=vr if W else None, W=W, sink=sk,
+                                  scale=scale, n_ctx=n_ctx, want_lse=True)
+    torch.cuda.synchronize()
+    o_w, l_w = oracle.dense_attn(q_c, kc_c, vc_c, m, kr_c, vr_c, W, sink=sk_c, scale=scale, n_ctx=n_ctx)
+    assert np.max(np.abs(to_np(out) - o_w)) <= BF16_TOL
+    assert np.max(np.abs(to_np(lse) - l_w)) <= 1e-3
+
+
+@pytest.mark.parametrize("sparse,T", [(True, 1), (True, 24), (False, 1), (False, 24)])
+def test_attn_fp8_equals_bf16_path_on_the_same_values(sparse, T):
+    """Every E4M3 code is a bf16 value, and the FP8 kernels convert before the
+    same MFMA sequence: on the bf16 copy of the same cache the bf16 kernels
+    must give bit-identical outputs and lse."""
+    import synthetic as syn
+    B, H, d, L, m, k, W = 2, 64, 512, 1200, 4, 256, 128
+    n_ctx = L * m
+    R = T + W - 1
+    g, _ = _attn_fp8_inputs(B, T, H, d, L, R, 71, 1.0)
+    q, kc, vc, kr, vr, sk = g
+    up = [x.to(torch.bfloat16) for x in (kc, vc, kr, vr)]
+    nv = np.minimum(np.arange(n_ctx - T, n_ctx) // m, L)
+    idx = syn.sample_indices(5, syn.TID["idx"], B * T, k, np.tile(nv, B)).reshape(B, T, k).cuda()
+    if sparse:
+        f = lambda kc_, vc_, kr_, vr_: csa.csa_sparse_attn(q, kc_, vc_, idx, kr=kr_, vr=vr_, W=W, sink=sk,
+                                                           scale=1.0 / d, n_ctx=n_ctx, want_lse=True)
+    else:
+        f = lambda kc_, vc_, kr_, vr_: csa.hca_dense_attn(q, kc_, vc_, m, kr=kr_, vr=vr_, W=W, sink=sk,
+                                                          scale=1.0 / d, n_ctx=n_ctx, want_lse=True)
+    o8, l8 = f(kc, vc, kr, vr)
+    o16, l16 = f(*up)
+    torch.cuda.synchronize()
+    assert torch.equal(o8.view(torch.int16), o16.view(torch.int16))
+    assert torch.equal(l8, l16)
+
+
+def test_attn_fp8_shape_and_query_checks():
+    B, T, H, d, L, k, W = 1, 1, 64, 256, 100, 8, 4
+    q = torch.zeros((B, T, H, d), dtype=torch.bfloat16, device="cuda")
     kc = torch.zeros((B, L, d), dtype=F8, device="cuda")
     idx = torch.zeros((B, T, k), dtype=torch.int32, device="cuda")
     kr = torch.zeros((B, W, d), dtype=F8, device="cuda")
-    with pytest.raises(csa.CsaError, match="UNSUPPORTED"):
+    with pytest.raises(csa.CsaError, match="UNSUPPORTED"):  # FP8 K/V needs d = 512
         csa.csa_sparse_attn(q, kc, kc, idx, kr=kr, vr=kr, W=W, n_ctx=4 * L)
+    with pytest.raises(TypeError):  # an FP8 cache takes a bf16 query
+        csa.csa_sparse_attn(q.to(F8), kc, kc, idx, kr=kr, vr=kr, W=W, n_ctx=4 * L)
