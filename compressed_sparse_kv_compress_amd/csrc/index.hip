@@ -56,6 +56,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Wait until at most LPT * n of this wave's loads are outstanding (LPT loads
 // per tile, n < ring depth).
+// max(0, x) as one signed-integer max on the bits: a float with the sign bit
+// set is a negative integer and becomes +0; others are unchanged (fmaxf would
+// first canonicalise its input, one more instruction per value).  Equal to
+// fmaxf(x, 0) for every non-NaN x.
+__device__ __forceinline__ float relu_bits(float x) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+
 template <int LPT>
 __device__ __forceinline__ void wait_tiles(int n) {
   switch (n) {
@@ -349,13 +357,16 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
   // lane holds S[head mb*16 + 4g + r][key c16] of a tile: ReLU, head
   // weights, and the sum over heads (a short tree in-lane, then across the
   // four lane groups), stored at the tile's score slots.
+  // key k0 + it * kStride + c16 is visible iff it * kStride < vlim
+  const int64_t vl = nv - k0 - c16;
+  const int vlim = vl < 0 ? 0 : (vl > INT32_MAX ? INT32_MAX : static_cast<int>(vl));
   auto finish = [&](int itx, const f32x4 (&acc)[MB]) {
     float ps[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       float x[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = HAS_W ? wr[mb][HAS_W ? r : 0] * fmaxf(acc[mb][r], 0.f) : fmaxf(acc[mb][r], 0.f);
+      for (int r = 0; r < 4; ++r) x[r] = HAS_W ? wr[mb][HAS_W ? r : 0] * relu_bits(acc[mb][r]) : relu_bits(acc[mb][r]);
       ps[mb] = (x[0] + x[1]) + (x[2] + x[3]);
     }
 #pragma unroll
@@ -363,8 +374,7 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
 #pragma unroll
       for (int mb = 0; mb + w < MB; mb += 2 * w) ps[mb] += ps[mb + w];
     const float tot = group_sum4(ps[0]);
-    const int64_t s = k0 + static_cast<int64_t>(itx) * kStride + c16;
-    if (g == 0) sb[sb_pos(itx, c16)] = s < nv ? tot : -INFINITY;
+    if (g == 0) sb[sb_pos(itx, c16)] = itx * static_cast<int>(kStride) < vlim ? tot : -INFINITY;
   };
   for (int it = 0; it < ntv; ++it) {
     if (it + DEPTH - 1 < ntv) {
@@ -476,7 +486,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_direct(IndexScoreArgs a,
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float rl = fmaxf(acc[mb][r], 0.f);
+        const float rl = relu_bits(acc[mb][r]);
         part_sum = HAS_W ? fmaf(a.w[row * HI + mb * 16 + 4 * g + r], rl, part_sum) : part_sum + rl;
       }
     part_sum += __shfl_xor(part_sum, 16, 64);
