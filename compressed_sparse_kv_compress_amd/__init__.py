@@ -28,7 +28,7 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-CSA_F32, CSA_BF16, CSA_FP8 = 0, 1, 2
+CSA_F32, CSA_BF16, CSA_FP8, CSA_MXFP4 = 0, 1, 2, 3
 _STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED",
            3: "CSA_ERR_WORKSPACE", 4: "CSA_ERR_HIP"}
 
@@ -75,7 +75,37 @@ def _check(st, where):
         raise CsaError(st, where)
 
 
-def _dt(t: torch.Tensor) -> int:
+class MXFP4:
+    """An OCP MXFP4 tensor of logical shape `shape` (last dimension d, a
+    multiple of 32) held in one uint8 buffer `data`: prod(shape)/2 bytes of
+    E2M1 codes (element 2i in the low nibble of byte i), then prod(shape)/32
+    E8M0 scale bytes, one per 32 consecutive elements of a row."""
+
+    def __init__(self, data: torch.Tensor, shape):
+        shape = tuple(int(x) for x in shape)
+        n = 1
+        for x in shape:
+            n *= x
+        if data.dtype != torch.uint8 or not data.is_contiguous():
+            raise TypeError("MXFP4 data must be a contiguous uint8 tensor")
+        if shape[-1] % 32 or data.numel() != n // 2 + n // 32:
+            raise ValueError("MXFP4 buffer of %d bytes does not hold shape %s" % (data.numel(), shape))
+        self.data, self.shape = data, shape
+
+    @property
+    def device(self):
+        return self.data.device
+
+    def data_ptr(self):
+        return self.data.data_ptr()
+
+    def is_contiguous(self):
+        return True
+
+
+def _dt(t) -> int:
+    if isinstance(t, MXFP4):
+        return CSA_MXFP4
     if t.dtype == torch.bfloat16:
         return CSA_BF16
     if t.dtype == torch.float32:

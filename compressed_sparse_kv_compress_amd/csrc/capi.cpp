@@ -46,7 +46,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
       return fail(CSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p);    \
   } while (0)
 
-bool dtype_ok(csa_dtype_t dt) { return dt == CSA_F32 || dt == CSA_BF16 || dt == CSA_FP8; }
+bool dtype_ok(csa_dtype_t dt) { return dt == CSA_F32 || dt == CSA_BF16 || dt == CSA_FP8 || dt == CSA_MXFP4; }
 csa::Dt to_dt(csa_dtype_t dt) { return static_cast<csa::Dt>(static_cast<int>(dt)); }
 
 csa_status_t compress_common(const void* x_a, const void* z_a, const void* x_b, const void* z_b,
@@ -54,6 +54,7 @@ csa_status_t compress_common(const void* x_a, const void* z_a, const void* x_b, 
                              int64_t m, int64_t p0, int64_t n_raw, int64_t e0, int64_t e1,
                              int64_t out_ld, csa_dtype_t dt, void* stream) {
   REQUIRE(dtype_ok(dt), "unknown dtype %d", static_cast<int>(dt));
+  if (dt == CSA_MXFP4) return fail(CSA_ERR_UNSUPPORTED, "compression has no MXFP4 kernels");
   REQUIRE(B >= 0 && n >= 1 && m >= 1 && D >= 8 && D % 8 == 0,
           "need B >= 0, n >= 1, m >= 1, D a positive multiple of 8 (B=%lld n=%lld m=%lld D=%lld)",
           (long long)B, (long long)n, (long long)m, (long long)D);
@@ -103,6 +104,7 @@ csa_status_t attn_common(const void* q, const void* kc, const void* vc, int64_t 
                          int64_t B, int64_t T, int64_t n_ctx, int64_t H, int64_t d, void* out,
                          float* lse, csa_dtype_t dt) {
   REQUIRE(dtype_ok(dt), "unknown dtype %d", static_cast<int>(dt));
+  if (dt == CSA_MXFP4) return fail(CSA_ERR_UNSUPPORTED, "attention has no MXFP4 kernels");
   REQUIRE(B >= 0 && T >= 1 && n_ctx >= T && L >= 0 && H >= 1 && d >= 1 && W >= 0,
           "need B >= 0, 1 <= T <= n_ctx, L >= 0, H >= 1, d >= 1, W >= 0");
   REQUIRE(std::isfinite(scale), "scale is not finite");

@@ -41,6 +41,11 @@ constexpr int kTileBytes = kTileKeys * 256;   // d_I = 128 bf16 keys
 constexpr int kDepth8 = 2 * kDepth;
 constexpr int kTileBytes8 = kTileKeys * 128;
 static_assert(kDepth8 * kTileBytes8 == kDepth * kTileBytes, "one ring size for both key types");
+// MXFP4 keys (64 code bytes + 4 E8M0 scales): a tile is its 1 KiB of codes
+// and four copies of its 64 scale bytes (one dword load).
+constexpr int kDepth4 = 15;
+constexpr int kTileBytes4 = kTileKeys * 64 + 256;
+static_assert(kDepth4 * kTileBytes4 <= kDepth * kTileBytes, "the MXFP4 ring fits the same space");
 constexpr int kMinKeysPerWave = 256;
 constexpr int kMaxKeysPerWave = 3968;         // scores of a workgroup stay in LDS (62 KiB)
 constexpr int kMaxTiles = kMaxKeysPerWave / kTileKeys;
@@ -85,8 +90,8 @@ __device__ __forceinline__ void wait_tiles(int n) {
   }
   asm volatile("" ::: "memory");
 }
-static_assert(kDepth >= 2 && kDepth8 <= 15, "wait_tiles covers up to 14 tiles in flight");
-static_assert(4 * (kDepth - 1) < 64 && 2 * (kDepth8 - 1) < 64, "vmcnt range");
+static_assert(kDepth >= 2 && kDepth8 <= 15 && kDepth4 <= 15, "wait_tiles covers up to 14 tiles in flight");
+static_assert(4 * (kDepth - 1) < 64 && 2 * (kDepth8 - 1) < 64 && 2 * (kDepth4 - 1) < 64, "vmcnt range");
 
 // 16 bytes per lane, global -> LDS at lds + 16 * lane (lds wave-uniform, via
 // M0), nontemporal (every key is read once: streaming through the caches
@@ -110,6 +115,21 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, const ui
 __device__ __forceinline__ void dma16(const void* g, const uint8_t* lds) {
   uint32_t saved;
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(g), "s"(lds_addr(lds))
+               : "memory");
+}
+// The same with 4 bytes per lane (lane i's dword lands at lds + 4i).
+__device__ __forceinline__ void dma4(const char* sbase, uint32_t voff, const uint8_t* lds) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dword %1, %2 nt\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(voff), "s"(sbase), "s"(lds_addr(lds))
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, const uint8_t* lds) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off nt\n\ts_mov_b32 m0, %0"
                : "=&s"(saved)
                : "v"(g), "s"(lds_addr(lds))
                : "memory");
@@ -244,16 +264,21 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
 // bytes of row c of each operand, the same bytes for the query and the key,
 // so the product is the full dot product (checked on the device against an
 // fp64 product of the decoded values, output in the usual 16x16 layout).
-template <int MB, bool HAS_W, bool TOPK, bool FP8>
+// MXFP4: q^I and k^I as E2M1 codes (two per byte, element 2i in the low
+// nibble) with one E8M0 scale per 32 elements; the same instruction in its
+// FP4 form takes 16 code bytes per lane, and each lane's scale operand is the
+// scale of exactly its 32 elements (lane (g, c): row c, block g).
+template <int MB, bool HAS_W, bool TOPK, int KF>  // KF: key format, 0 bf16, 1 FP8, 2 MXFP4
 __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, int64_t parts, int64_t per_wave,
                                                              IndexCandidates co) {
+  constexpr bool FP8 = KF == 1, FP4 = KF == 2;
   constexpr int HI = 16 * MB;
   constexpr int DI = 128;
   constexpr int KS = 4;
-  constexpr int KB = FP8 ? 128 : 256;                // bytes per key
-  constexpr int TB = FP8 ? kTileBytes8 : kTileBytes;  // bytes per tile
-  constexpr int DEPTH = FP8 ? kDepth8 : kDepth;       // ring slots per wavefront
-  constexpr int LPT = TB / 1024;                      // 1 KiB wave loads per tile
+  constexpr int KB = FP4 ? 64 : (FP8 ? 128 : 256);                          // code bytes per key
+  constexpr int TB = FP4 ? kTileBytes4 : (FP8 ? kTileBytes8 : kTileBytes);  // LDS bytes per tile
+  constexpr int DEPTH = FP4 ? kDepth4 : (FP8 ? kDepth8 : kDepth);           // ring slots per wavefront
+  constexpr int LPT = FP4 ? 2 : TB / 1024;                                  // wave loads per tile
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][DEPTH][TB];
   __shared__ __attribute__((aligned(16))) float sbuf[kWaves][kMaxTiles * kTileKeys];
   const int lane = threadIdx.x & 63;
@@ -291,11 +316,20 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
   // Only a tile that runs past the last key (the very end of a row) takes
   // per-lane clamped addresses.
   const char* kbase = static_cast<const char*>(a.k) + b * a.L * KB;
+  //  MXFP4: key kk's codes at kk*64, four 16-byte blocks; block p of key kk
+  //    sits at slot (p + kk/4) % 4 (the 16 keys of one read then cover the 64
+  //    banks once).  Lane l of the code load writes slot l%4 of key l/4.
+  //    Scales: lane l of the dword load brings key l%16's four scales to
+  //    1024 + 4l, i.e. copy l/16; lane group g reads copy g.
   uint32_t voff[LPT];
   int kkl[LPT];  // key of the tile this lane's piece of load j belongs to
 #pragma unroll
   for (int j = 0; j < LPT; ++j) {
-    if constexpr (FP8) {
+    if constexpr (FP4) {
+      const int kk = j == 0 ? lane >> 2 : lane & 15;
+      kkl[j] = kk;
+      voff[j] = j == 0 ? kk * 64 + ((((lane & 3) - (kk >> 2)) & 3) << 4) : kk * 4;
+    } else if constexpr (FP8) {
       const int kk = 8 * j + (lane >> 3), sl = lane & 7;
       kkl[j] = kk;
       voff[j] = kk * 128 + (((sl - (kk >> 1)) & 7) << 4);
@@ -305,9 +339,24 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
     }
   }
   uint8_t* myring = &ring[wave][0][0];
+  // MXFP4 scales follow all B*L*64 code bytes, 4 per key.
+  const char* sbase = FP4 ? static_cast<const char*>(a.k) + a.B * a.L * KB + b * a.L * 4 : nullptr;
   auto issue = [&](int it) {
     uint8_t* slot = myring + (it % DEPTH) * TB;
     const int64_t t0 = k0 + static_cast<int64_t>(it) * kStride;
+    if constexpr (FP4) {
+      if (t0 + kTileKeys <= a.L) {
+        dma16(kbase + t0 * KB, voff[0], slot);
+        dma4(sbase + t0 * 4, voff[1], slot + 1024);
+      } else {
+        int64_t s0 = t0 + kkl[0], s1 = t0 + kkl[1];
+        s0 = s0 < a.L - 1 ? s0 : a.L - 1;
+        s1 = s1 < a.L - 1 ? s1 : a.L - 1;
+        dma16(kbase + s0 * KB + (voff[0] - kkl[0] * KB), slot);
+        dma4(sbase + s1 * 4, slot + 1024);
+      }
+      return;
+    }
     if (t0 + kTileKeys <= a.L) {
       const char* tb = kbase + t0 * KB;
 #pragma unroll
@@ -326,9 +375,20 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
     if (i < ntv) issue(i);
 
   // A operand: query heads (rows) x index dims, resident for the whole kernel.
-  bf16x8 afrag[MB][FP8 ? 1 : KS];
+  bf16x8 afrag[MB][KF ? 1 : KS];
   i32x8 afrag8[MB];
-  if constexpr (FP8) {
+  int qsc[MB];  // MXFP4: E8M0 scale of this lane's 32 query elements
+  if constexpr (FP4) {
+    const uint8_t* qb = static_cast<const uint8_t*>(a.q);
+    const uint8_t* qs = qb + a.B * a.T * HI * 64;  // scales follow all code bytes
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(qb + (row * HI + mb * 16 + c16) * 64 + 16 * g);
+      afrag8[mb] = i32x8{static_cast<int>(x[0]), static_cast<int>(x[1]), static_cast<int>(x[2]), static_cast<int>(x[3]),
+                         0, 0, 0, 0};
+      qsc[mb] = qs[(row * HI + mb * 16 + c16) * 4 + g];
+    }
+  } else if constexpr (FP8) {
     const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + row * HI * DI;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) afrag8[mb] = *reinterpret_cast<const i32x8*>(qrow + (mb * 16 + c16) * DI + 32 * g);
@@ -386,7 +446,15 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
     f32x4 acc[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (FP8) {
+    if constexpr (FP4) {
+      const uint8_t* t = myring + (it % DEPTH) * TB;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(t + c16 * 64 + (((g + (c16 >> 2)) & 3) << 4));
+      const int ksc = static_cast<int>((*reinterpret_cast<const uint32_t*>(t + 1024 + 64 * g + 4 * c16) >> (8 * g)) & 0xffu);
+      const i32x8 cur4{static_cast<int>(x[0]), static_cast<int>(x[1]), static_cast<int>(x[2]), static_cast<int>(x[3]), 0, 0, 0, 0};
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)  // format 4 = E2M1 for both operands, per-lane E8M0 scales
+        acc[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afrag8[mb], cur4, acc[mb], 4, 4, 0, qsc[mb], 0, ksc);
+    } else if constexpr (FP8) {
       // Key c16's 128 bytes sit as eight rotated 16-byte blocks; lane (g, c16)
       // takes blocks 2g and 2g+1, i.e. k = 32g .. 32g+31, matching afrag8.
       const uint8_t* t = myring + (it % DEPTH) * TB + c16 * 128;
@@ -551,13 +619,15 @@ hipError_t launch_stream(const IndexScoreArgs& a, const IndexCandidates& co, hip
   const dim3 grid(static_cast<uint32_t>(a.nrows * parts));
   const int mb = static_cast<int>(a.HI / 16);
   const bool w = a.w != nullptr;
-  const bool f8 = a.dt == kFP8;
-#define CSA_INDEX_LAUNCH(MB_)                                                                                     \
-  case MB_:                                                                                                       \
-    if (f8 && w) hipLaunchKernelGGL((index_score_stream<MB_, true, TOPK, true>), grid, dim3(256), 0, s, a, parts, per_wave, co);     \
-    else if (f8) hipLaunchKernelGGL((index_score_stream<MB_, false, TOPK, true>), grid, dim3(256), 0, s, a, parts, per_wave, co);    \
-    else if (w) hipLaunchKernelGGL((index_score_stream<MB_, true, TOPK, false>), grid, dim3(256), 0, s, a, parts, per_wave, co);     \
-    else hipLaunchKernelGGL((index_score_stream<MB_, false, TOPK, false>), grid, dim3(256), 0, s, a, parts, per_wave, co);           \
+  const int kf = a.dt == kMXFP4 ? 2 : (a.dt == kFP8 ? 1 : 0);
+#define CSA_INDEX_KF(MB_, KF_)                                                                                     \
+  if (w) hipLaunchKernelGGL((index_score_stream<MB_, true, TOPK, KF_>), grid, dim3(256), 0, s, a, parts, per_wave, co);  \
+  else hipLaunchKernelGGL((index_score_stream<MB_, false, TOPK, KF_>), grid, dim3(256), 0, s, a, parts, per_wave, co);
+#define CSA_INDEX_LAUNCH(MB_)                  \
+  case MB_:                                    \
+    if (kf == 2) { CSA_INDEX_KF(MB_, 2) }      \
+    else if (kf == 1) { CSA_INDEX_KF(MB_, 1) } \
+    else { CSA_INDEX_KF(MB_, 0) }              \
     break;
   switch (mb) {
     CSA_INDEX_LAUNCH(1)
@@ -567,6 +637,7 @@ hipError_t launch_stream(const IndexScoreArgs& a, const IndexCandidates& co, hip
     default: return hipErrorInvalidValue;
   }
 #undef CSA_INDEX_LAUNCH
+#undef CSA_INDEX_KF
   return hipGetLastError();
 }
 
@@ -574,7 +645,7 @@ hipError_t launch_stream(const IndexScoreArgs& a, const IndexCandidates& co, hip
 
 hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t s) {
   if (a.nrows == 0 || a.L == 0) return hipSuccess;
-  if (a.dt == kFP8) {  // d_I = 128 only (index_shape_supported)
+  if (a.dt == kFP8 || a.dt == kMXFP4) {  // d_I = 128 only (index_shape_supported)
     if (a.dI != 128) return hipErrorInvalidValue;
     return launch_stream<false>(a, IndexCandidates{}, s);
   }
@@ -607,7 +678,8 @@ hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t s) {
 }
 
 bool index_topk_fusable(int64_t nrows, int64_t L, int64_t HI, int64_t dI, int64_t k, Dt dt) {
-  if ((dt != kBF16 && dt != kFP8) || dI != 128 || nrows <= 0 || L <= 0 || k < 1 || k > kCandStage) return false;
+  if ((dt != kBF16 && dt != kFP8 && dt != kMXFP4) || dI != 128 || nrows <= 0 || L <= 0 || k < 1 || k > kCandStage)
+    return false;
   if (!(HI == 16 || HI == 32 || HI == 64 || HI == 128)) return false;
   int64_t parts, per_wave;
   index_plan(nrows, L, &parts, &per_wave);
@@ -649,7 +721,7 @@ hipError_t launch_index_topk_fused(const IndexScoreArgs& a, const TopkArgs& t, v
 }
 
 bool index_shape_supported(int64_t HI, int64_t dI, Dt dt) {
-  if (dt == kFP8) return dI == 128 && (HI == 16 || HI == 32 || HI == 64 || HI == 128);
+  if (dt == kFP8 || dt == kMXFP4) return dI == 128 && (HI == 16 || HI == 32 || HI == 64 || HI == 128);
   if (dt == kF32) return HI * dI * 4 <= 65536;
   if (HI % 16 || dI % 32) return false;
   const int64_t mb = HI / 16, ks = dI / 32;

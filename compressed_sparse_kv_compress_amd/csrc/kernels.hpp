@@ -7,7 +7,7 @@
 namespace csa {
 
 // Storage types, numbered as csa_dtype_t: fp32, bf16, and FP8 (OCP E4M3).
-enum Dt : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+enum Dt : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kMXFP4 = 3 };
 
 struct CompressArgs {
   const void* x_a;

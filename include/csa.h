@@ -40,6 +40,18 @@
  *     each code converts exactly to bf16 and the arithmetic is the bf16
  *     path's.  FP8 carries no scale argument: a per-tensor K scale folds into
  *     `scale`, a V scale into the caller's use of `out`.
+ *   - CSA_MXFP4 is the OCP microscaling FP4 format: elements E2M1 (1 sign,
+ *     2 exponent bits with bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1,
+ *     1.5, 2, 3, 4, 6), each block of 32 consecutive elements of a row
+ *     sharing one E8M0 scale byte e (value 2^(e-127); e = 255 is NaN).  An
+ *     MXFP4 tensor of N rows of d elements is one buffer: N*d/2 code bytes
+ *     (row-major; element 2i in the low nibble of byte i, 2i+1 in the high
+ *     nibble), then N*d/32 scale bytes (row-major; scale j of a row covers
+ *     its elements 32j .. 32j+31).  The pages run the indexer's q.k in FP4
+ *     (shareware.cn article, the low-precision item of its list of what is
+ *     compressed); accepted by csa_index_score / csa_index_topk for q_idx (N
+ *     = B*T*H_I) and k_idx (N = B*L) with d_I = 128, H_I in {16, 32, 64,
+ *     128}; compression and attention return CSA_ERR_UNSUPPORTED for it.
  *   - Positions: a batch holds B sequences of n_ctx tokens (uniform length).
  *     The T queries of a sequence sit at positions t_i = n_ctx - T + i.
  *     Compressed entry s covers tokens [s*m, (s+1)*m) and is visible to the
@@ -59,7 +71,7 @@
 extern "C" {
 #endif
 
-typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8 = 2 } csa_dtype_t;
+typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8 = 2, CSA_MXFP4 = 3 } csa_dtype_t;
 
 typedef enum csa_status {
   CSA_OK = 0,

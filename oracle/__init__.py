@@ -26,6 +26,15 @@ see tests/test_oracle_*.py):
                               named values, ties to even, round trips); the
                               choice of E4M3 itself is a reading of the pages
                               (they name FP8 without an encoding)
+  minifloat_decode            pinned (E4M3 and E5M2 against torch's float8 types
+                              on every finite code)
+  e2m1_decode / e8m0_decode / pinned (E2M1 is the decoder above with 2 exponent
+  mxfp4_decode                bits, bias 1, and its values are E4M3 values that
+                              round-trip through fp8_encode; E8M0 against torch's
+                              float8_e8m0fnu on all 256 codes; block layout by
+                              single-element and single-scale buffers); the
+                              MXFP4 reading of "FP4" and the buffer layout are
+                              conventions: parity unpinned for the layout
 """
 from __future__ import annotations
 
@@ -98,16 +107,60 @@ def _load():
 # the largest finite value is 1.75 * 2**8 = 448.
 
 
+def minifloat_decode(codes, ebits: int, mbits: int, bias: int) -> np.ndarray:
+    """Codes of a binary float with one sign bit (the top bit), `ebits`
+    exponent bits and `mbits` fraction bits -> float64, by the fields:
+    exponent 0 is subnormal (f * 2^(1 - bias - mbits)), otherwise
+    (1 + f / 2^mbits) * 2^(e - bias).  Special codes (NaN, infinities) are the
+    caller's to apply."""
+    c = np.asarray(codes).astype(np.int64)
+    nb = 1 + ebits + mbits
+    sign = np.where((c >> (nb - 1)) & 1, -1.0, 1.0)
+    e = (c >> mbits) & ((1 << ebits) - 1)
+    f = (c & ((1 << mbits) - 1)).astype(np.float64)
+    mag = np.where(e == 0, f * 2.0 ** (1 - bias - mbits),
+                   (1.0 + f / 2.0 ** mbits) * np.exp2(e.astype(np.float64) - bias))
+    return sign * mag
+
+
 def fp8_decode(codes) -> np.ndarray:
     """E4M3 byte codes (any integer array) -> float64 values, from the format's
-    definition."""
+    definition (bias 7; the all-ones exponent and fraction is NaN)."""
     c = np.asarray(codes).astype(np.int64) & 0xFF
-    sign = np.where(c & 0x80, -1.0, 1.0)
-    e = (c >> 3) & 0xF
-    m = (c & 0x7).astype(np.float64)
-    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
-    mag = np.where((e == 15) & ((c & 0x7) == 7), np.nan, mag)
-    return sign * mag
+    v = minifloat_decode(c, 4, 3, 7)
+    return np.where((c & 0x7F) == 0x7F, np.nan, v)
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """FP4 E2M1 nibble codes -> float64 (bias 1, no special codes)."""
+    return minifloat_decode(np.asarray(codes).astype(np.int64) & 0xF, 2, 1, 1)
+
+
+def e8m0_decode(codes) -> np.ndarray:
+    """E8M0 scale bytes -> 2^(e - 127); 255 is NaN."""
+    e = np.asarray(codes).astype(np.int64) & 0xFF
+    return np.where(e == 255, np.nan, np.exp2(e.astype(np.float64) - 127.0))
+
+
+def mxfp4_decode(buf, shape) -> np.ndarray:
+    """An MXFP4 buffer of logical shape `shape` -> float64 array of that shape.
+
+    Layout: prod(shape)/2 code bytes, element 2i in the low nibble of byte i
+    and 2i+1 in the high nibble, then prod(shape)/32 E8M0 scale bytes, scale
+    j of a row multiplying its elements 32j .. 32j+31 (OCP microscaling: a
+    block of 32 elements shares one power-of-two scale)."""
+    b = np.asarray(buf).astype(np.int64).reshape(-1)
+    shape = tuple(int(x) for x in shape)
+    n = int(np.prod(shape))
+    d = shape[-1]
+    assert d % 32 == 0 and b.size == n // 2 + n // 32
+    codes = b[: n // 2]
+    el = np.empty(n, dtype=np.int64)
+    el[0::2] = codes & 0xF
+    el[1::2] = codes >> 4
+    vals = e2m1_decode(el).reshape(n // d, d // 32, 32)
+    sc = e8m0_decode(b[n // 2:]).reshape(n // d, d // 32, 1)
+    return (vals * sc).reshape(shape)
 
 
 def fp8_encode(x) -> np.ndarray:

@@ -120,6 +120,22 @@ def fill_(out: torch.Tensor, seed: int, tid: int, *, kind: str = "normal",
     return out
 
 
+def mxfp4_(out: torch.Tensor, seed: int, tid: int, n: int, *, scale_lo: int = 127, scale_hi: int = 127,
+           layer: int = 0) -> torch.Tensor:
+    """Fill a uint8 buffer holding an MXFP4 tensor of n elements: n/2 bytes of
+    uniformly random E2M1 code pairs, then n/32 E8M0 scale bytes uniform in
+    [scale_lo, scale_hi].  Random codes, not a quantisation of values."""
+    assert out.dtype == torch.uint8 and out.numel() == n // 2 + n // 32
+    key = tensor_key(seed, tid, layer)
+    idx = torch.arange(out.numel(), dtype=torch.int64, device=out.device)
+    bits = hash_bits(idx, key)
+    span = scale_hi - scale_lo + 1
+    codes = bits & 0xFF
+    scales = scale_lo + (bits >> 8) % span
+    out.copy_(torch.where(idx < n // 2, codes, scales).to(torch.uint8))
+    return out
+
+
 def make(shape, seed: int, tid: int, *, dtype=torch.float32, device="cpu",
          kind: str = "normal", scale: float = 1.0, grid: int = 8, layer: int = 0) -> torch.Tensor:
     out = torch.empty(tuple(shape), dtype=dtype, device=device)

@@ -107,7 +107,7 @@ def test_index_and_attention_reject_bad_arguments(lib):
 def test_fp8_storage_is_validated(lib):
     """CSA_FP8 (2) is a known dtype: accepted by compression, the indexer
     (d_I = 128, H_I a multiple of 16 up to 128) and attention over an FP8 K/V
-    cache (d = 512 only); 3 is unknown."""
+    cache (d = 512 only); 4 is unknown."""
     idx_args = [V] * 3 + [I] * 8 + [V, V, V, Z, ctypes.c_int, V]
     # FP8 indexer with d_I = 64: no kernel
     assert _call(lib, "csa_index_topk", idx_args, FAKE, None, FAKE, 1, 1, 100, 25, 64, 64, 4, 8,
@@ -118,9 +118,9 @@ def test_fp8_storage_is_validated(lib):
     # FP8 indexer, supported shape, but k = 0: an argument error, so the dtype itself passed
     assert _call(lib, "csa_index_topk", idx_args, FAKE, None, FAKE, 1, 1, 100, 25, 64, 128, 4, 0,
                  FAKE, None, FAKE, 1 << 20, 2, None) == 1
-    # unknown dtype 3
+    # unknown dtype 4
     assert _call(lib, "csa_index_topk", idx_args, FAKE, None, FAKE, 1, 1, 100, 25, 64, 128, 4, 8,
-                 FAKE, None, FAKE, 1 << 20, 3, None) == 1
+                 FAKE, None, FAKE, 1 << 20, 4, None) == 1
     attn = [V] * 3 + [I, V, I, V, V, I, I, V, F] + [I] * 5 + [V, V, V, Z, ctypes.c_int, V]
     # FP8 K/V attention with d = 256: no kernel
     assert _call(lib, "csa_sparse_attn", attn, FAKE, FAKE, FAKE, 10, FAKE, 4, None, None, 0, 0,
@@ -140,3 +140,22 @@ def test_fp8_storage_is_validated(lib):
                  1, 16, 16, 4, 0, 16, 2, 2, 0, 2, None) == 0
     assert _call(lib, "csa_compress", args, FAKE, FAKE, None, None, None, FAKE,
                  1, 16, 12, 4, 0, 16, 0, 4, 4, 2, None) == 1
+
+
+def test_mxfp4_storage_is_validated(lib):
+    """CSA_MXFP4 (3): the indexer only (d_I = 128, H_I a multiple of 16 up to
+    128); compression and attention reject it as unsupported."""
+    idx_args = [V] * 3 + [I] * 8 + [V, V, V, Z, ctypes.c_int, V]
+    assert _call(lib, "csa_index_topk", idx_args, FAKE, None, FAKE, 1, 1, 100, 25, 64, 64, 4, 8,
+                 FAKE, None, FAKE, 1 << 20, 3, None) == 2
+    assert _call(lib, "csa_index_topk", idx_args, FAKE, None, FAKE, 1, 1, 100, 25, 48, 128, 4, 8,
+                 FAKE, None, FAKE, 1 << 20, 3, None) == 2
+    # supported shape, k = 0: an argument error, so the dtype itself passed
+    assert _call(lib, "csa_index_topk", idx_args, FAKE, None, FAKE, 1, 1, 100, 25, 64, 128, 4, 0,
+                 FAKE, None, FAKE, 1 << 20, 3, None) == 1
+    args = [V] * 6 + [I] * 9 + [ctypes.c_int, V]
+    assert _call(lib, "csa_compress", args, FAKE, FAKE, None, None, None, FAKE,
+                 1, 16, 16, 4, 0, 16, 0, 4, 4, 3, None) == 2
+    attn = [V] * 3 + [I, V, I, V, V, I, I, V, F] + [I] * 5 + [V, V, V, Z, ctypes.c_int, V]
+    assert _call(lib, "csa_sparse_attn", attn, FAKE, FAKE, FAKE, 10, FAKE, 4, None, None, 0, 0,
+                 None, 0.1, 1, 1, 40, 64, 512, FAKE, None, None, 0, 3, None) == 2

@@ -1,0 +1,95 @@
+"""Pins of the oracle's MXFP4 decoding (CPU).
+
+The pages run the indexer's q.k in FP4 without naming an encoding
+(shareware.cn Hybrid Attention article, its list of what is compressed); the
+MXFP4 reading (E2M1 elements, one E8M0 scale per 32) is pinned here through
+checks that do not restate the decoder: the generic minifloat decoder against
+torch's 8-bit float types, E8M0 against torch's float8_e8m0fnu, E2M1 values
+against the independently pinned E4M3 encoder, and the block layout through
+buffers with a single non-zero element or a single changed scale."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as syn
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _torch_decode(dtype):
+    return torch.arange(256, dtype=torch.uint8).view(dtype).to(torch.float64).numpy()
+
+
+def test_minifloat_decoder_matches_torch_e4m3_on_every_finite_code():
+    codes = np.arange(256)
+    want = _torch_decode(torch.float8_e4m3fn)
+    fin = (codes & 0x7F) != 0x7F
+    got = oracle.minifloat_decode(codes, 4, 3, 7)
+    assert np.array_equal(got[fin], want[fin])
+
+
+def test_minifloat_decoder_matches_torch_e5m2_on_every_finite_code():
+    codes = np.arange(256)
+    want = _torch_decode(torch.float8_e5m2)
+    fin = ((codes >> 2) & 0x1F) != 0x1F
+    got = oracle.minifloat_decode(codes, 5, 2, 15)
+    assert np.array_equal(got[fin], want[fin])
+
+
+def test_e8m0_matches_torch_on_all_codes():
+    want = _torch_decode(torch.float8_e8m0fnu)
+    got = oracle.e8m0_decode(np.arange(256))
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+
+
+def test_e2m1_values_are_e4m3_values_and_symmetric():
+    v = oracle.e2m1_decode(np.arange(16))
+    # every E2M1 value is exactly representable in E4M3 (3 fraction bits >= 1)
+    assert np.array_equal(oracle.fp8_decode(oracle.fp8_encode(v)), v)
+    assert np.array_equal(v[8:], -v[:8])            # the top bit is the sign
+    assert np.all(np.diff(v[:8]) > 0)               # codes ascend with the value
+    assert v[0] == 0.0 and v[1] == 0.5 and v[7] == 6.0  # smallest subnormal, largest finite
+    assert len(set(np.abs(v).tolist())) == 8
+
+
+def test_mxfp4_single_element_lands_at_its_position():
+    rows, d = 3, 64
+    n = rows * d
+    for r, e, code, sc in ((0, 0, 0x2, 127), (1, 33, 0x7, 130), (2, 63, 0xB, 120), (2, 2, 0x5, 127)):
+        buf = np.zeros(n // 2 + n // 32, dtype=np.uint8)
+        buf[n // 2:] = 127
+        flat = r * d + e
+        buf[flat // 2] = code << (4 * (flat % 2))
+        buf[n // 2 + r * (d // 32) + e // 32] = sc
+        got = oracle.mxfp4_decode(buf, (rows, d))
+        want = np.zeros((rows, d))
+        want[r, e] = oracle.e2m1_decode(code) * 2.0 ** (sc - 127)
+        assert np.array_equal(got, want)
+
+
+def test_mxfp4_scale_covers_exactly_its_32_elements():
+    rows, d = 2, 128
+    n = rows * d
+    buf = np.full(n // 2 + n // 32, 0x22, dtype=np.uint8)  # every element 1.0
+    buf[n // 2:] = 127
+    base = oracle.mxfp4_decode(buf, (rows, d))
+    assert np.all(base == 1.0)
+    buf[n // 2 + 1 * 4 + 2] = 129  # row 1, block 2
+    got = oracle.mxfp4_decode(buf, (rows, d))
+    changed = got != base
+    assert changed.sum() == 32 and np.all(changed[1, 64:96]) and np.all(got[1, 64:96] == 4.0)
+
+
+def test_mxfp4_generator_is_deterministic_and_in_range():
+    n = 64 * 128
+    a = syn.mxfp4_(torch.empty(n // 2 + n // 32, dtype=torch.uint8), 3, syn.TID["k_idx"], n, scale_lo=125,
+                   scale_hi=129)
+    b = syn.mxfp4_(torch.empty(n // 2 + n // 32, dtype=torch.uint8), 3, syn.TID["k_idx"], n, scale_lo=125,
+                   scale_hi=129)
+    assert torch.equal(a, b)
+    sc = a[n // 2:].numpy()
+    assert sc.min() >= 125 and sc.max() <= 129 and len(np.unique(sc)) == 5
+    assert len(np.unique(a[: n // 2].numpy())) > 100  # code bytes spread over the range
