@@ -494,6 +494,45 @@ def fp8_storage_step(B: int, steps: int, warmup: int):
     }
 
 
+def index_topk_mxfp4(B: int, reps: int = 20):
+    """One csa_index_topk call of the CSA decode shape with q^I and k^I in
+    MXFP4 (random E2M1 codes, E8M0 scales 2^-2 .. 2^2), timed over `reps`
+    back-to-back calls: reported beside the bf16 headline, never as it."""
+    import compressed_sparse_kv_compress_amd as csa
+    st = Stack(B=B)
+    L, HI, dI, k, m = st.L_csa, st.HI, st.dI, st.k, st.m_csa
+    nq, nk = B * HI * dI, B * L * dI
+    qb = syn.mxfp4_(torch.empty(nq // 2 + nq // 32, dtype=torch.uint8, device="cuda"), SEED, syn.TID["q_idx"], nq,
+                    scale_lo=125, scale_hi=129)
+    kb = syn.mxfp4_(torch.empty(nk // 2 + nk // 32, dtype=torch.uint8, device="cuda"), SEED, syn.TID["kic"], nk,
+                    scale_lo=125, scale_hi=129)
+    q, kk = csa.MXFP4(qb, (B, 1, HI, dI)), csa.MXFP4(kb, (B, L, dI))
+    w = syn.fill_(torch.empty((B, 1, HI), device="cuda"), SEED, syn.TID["w_idx"], scale=HI ** -0.5)
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(csa.csa_index_topk_workspace(B, 1, L, k), dtype=torch.uint8, device="cuda")
+
+    def call():
+        csa.csa_index_topk(q, kk, m, k, w_idx=w, n_ctx=st.n_ctx, idx=idx, ws=ws)
+
+    for _ in range(3):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    key_bytes = dI // 2 + dI // 32
+    byts = B * (st.nv_csa * key_bytes + HI * key_bytes + HI * 4 + k * 4)
+    del qb, kb, ws
+    torch.cuda.empty_cache()
+    return {"ms_per_call": ms, "algorithmic_bytes_per_call": byts, "GBps": byts / (ms * 1e-3) / 1e9,
+            "keys": "16 x %d visible keys of 68 B (64 code bytes + 4 scales), k = %d" % (st.nv_csa, k),
+            "note": "scan bound by its per-tile MFMA and epilogue chain (one wavefront per SIMD), not by bytes"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -573,6 +612,9 @@ def main():
     if not args.no_fp8:
         fp8 = fp8_storage_step(args.batch, args.steps, args.warmup)
         print("# fp8 storage: %.3f ms/step" % fp8["ms_per_step"], file=sys.stderr, flush=True)
+        fp8["index_topk_mxfp4"] = index_topk_mxfp4(args.batch)
+        print("# mxfp4 index_topk: %.3f ms/call" % fp8["index_topk_mxfp4"]["ms_per_call"], file=sys.stderr,
+              flush=True)
 
     prefill = None
     if args.prefill_queries > 0:
@@ -606,7 +648,7 @@ def main():
         },
         "hbm": {"algorithmic_bytes_per_step": st.step_bytes(), "achieved_GBps": step_gbps,
                 "frac_of_peak": step_gbps / HBM_PEAK_GBPS},
-        "roofline": {"kernel": "csa_index_topk (index_score_stream<4,true,true,false> then topk_merge_kernel)",
+        "roofline": {"kernel": "csa_index_topk (index_score_stream<4,true,true,0> then topk_merge_kernel)",
                      "bound": "hbm", "achieved": idx_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": idx_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "avg_launch_ms": idx_ms,
