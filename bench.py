@@ -494,6 +494,35 @@ def fp8_storage_step(B: int, steps: int, warmup: int):
     }
 
 
+def decode_step_b1(steps: int, warmup: int):
+    """The same bf16 8-layer step for one sequence (B = 1): the latency-bound
+    end of the decode workload, reported beside the B = 16 headline."""
+    st = Stack(B=1)
+    state = GpuState(st)
+    for _ in range(warmup):
+        state.step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        state.step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    ev = {}
+    for _ in range(3):
+        state.step(ev)
+    torch.cuda.synchronize()
+    per_call = event_means_ms(ev)
+    del state
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms, "tokens_per_s": 1.0 / (ms * 1e-3),
+            "algorithmic_bytes_per_step": st.step_bytes(),
+            "achieved_GBps": st.step_bytes() / (ms * 1e-3) / 1e9, "per_call_ms": per_call,
+            "note": "one query per call: bound by launch latency and by the stand-alone top-k (with one "
+                    "query row the single-pass scan-and-select plan does not apply)"}
+
+
 def index_topk_mxfp4(B: int, reps: int = 20):
     """One csa_index_topk call of the CSA decode shape with q^I and k^I in
     MXFP4 (random E2M1 codes, E8M0 scales 2^-2 .. 2^2), timed over `reps`
@@ -616,6 +645,11 @@ def main():
         print("# mxfp4 index_topk: %.3f ms/call" % fp8["index_topk_mxfp4"]["ms_per_call"], file=sys.stderr,
               flush=True)
 
+    b1 = None
+    if args.batch != 1:
+        b1 = decode_step_b1(args.steps, args.warmup)
+        print("# batch 1: %.3f ms/step" % b1["ms_per_step"], file=sys.stderr, flush=True)
+
     prefill = None
     if args.prefill_queries > 0:
         prefill = prefill_sparse_attn(args.prefill_queries)
@@ -657,6 +691,7 @@ def main():
         "per_call_note": "untimed pass with events around every call; compression runs on a second stream",
         "prefill_sparse_attn": prefill,
         "fp8_storage": fp8,
+        "decode_batch1": b1,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
