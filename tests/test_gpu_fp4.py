@@ -88,7 +88,8 @@ def test_index_topk_mxfp4_exact_with_unit_scales():
 
 
 @pytest.mark.parametrize("B,T,L,HI,k,lo,hi", [(16, 1, 250000, 64, 1024, 125, 129), (4, 3, 9000, 32, 512, 127, 127),
-                                              (2, 2, 700, 64, 1024, 120, 133), (4, 4, 60000, 128, 2048, 125, 129)])
+                                              (2, 2, 700, 64, 1024, 120, 133), (4, 4, 60000, 128, 2048, 125, 129),
+                                              (1, 1, 250000, 64, 1024, 125, 129)])
 def test_index_topk_mxfp4_single_pass_equals_score_then_select(B, T, L, HI, k, lo, hi):
     """Fused scan-and-select on MXFP4 keys == scores written out and selected
     by the stand-alone top-k, bit for bit; one row against the oracle (exact

@@ -123,7 +123,8 @@ def test_index_fp8_exact_on_grid_inputs():
 
 @pytest.mark.parametrize("B,T,L,HI,k,wts", [(16, 1, 250000, 64, 1024, True), (4, 3, 9000, 32, 512, False),
                                              (2, 2, 700, 64, 1024, True), (2, 8, 30000, 16, 256, False),
-                                             (4, 4, 60000, 128, 2048, True)])
+                                             (4, 4, 60000, 128, 2048, True), (1, 1, 250000, 64, 1024, True),
+                                             (8, 1, 32768, 64, 1024, False)])
 def test_index_topk_fp8_single_pass_equals_score_then_select(B, T, L, HI, k, wts):
     """The fused scan-and-select path on FP8 keys gives the same indices and
     scores, bit for bit, as the scores written out and selected by the

@@ -207,7 +207,10 @@ def test_index_topk_bit_exact_on_grid_inputs():
                                                    (2, 2, 700, 64, 1024, True, 1), (4, 16, 60000, 128, 2048, True, 1),
                                                    (2, 8, 30000, 16, 256, False, 1), (4, 1, 250000, 64, 1024, True, 32),
                                                    (4, 1, 250000, 64, 1024, False, 16), (4, 1, 250000, 64, 1024, True, -1),
-                                                   (3, 2, 120000, 64, 512, True, -1)])
+                                                   (3, 2, 120000, 64, 512, True, -1),
+                                                   (1, 1, 250000, 64, 1024, True, 1), (1, 1, 250000, 64, 1024, False, -1),
+                                                   (1, 1, 250000, 64, 1024, True, 16), (8, 1, 32768, 64, 1024, True, 1),
+                                                   (8, 1, 32768, 64, 1024, True, -1), (1, 2, 200000, 32, 512, False, 1)])
 def test_index_topk_single_pass_equals_score_then_select(B, T, L, HI, k, wts, boost):
     """Shapes where the indexer selects its parts' candidates itself (no score
     matrix) give the same indices and scores, bit for bit, as the scores
@@ -216,7 +219,9 @@ def test_index_topk_single_pass_equals_score_then_select(B, T, L, HI, k, wts, bo
     row is scaled by 4 (exact in bf16), a periodic structure that misleads a
     sampled threshold; boost = -1: the last sixteenth of the key rows is
     scaled by 4, so the row's top-k sits in one part (the merge cannot use the
-    parts' short lists and reads the full ones)."""
+    parts' short lists and reads the full ones).  Batch 1 and 8 rows of
+    32768 take the stand-alone top-k on both sides (too many parts for the
+    single-pass plan); they are checked here against the oracle row."""
     dI, m = 128, 4
     n_ctx = m * L
     seed = 40 + L
