@@ -494,6 +494,46 @@ def fp8_storage_step(B: int, steps: int, warmup: int):
     }
 
 
+def prefill_index_topk(queries: int = 4096, reps: int = 3):
+    """csa_index_topk on the CSA prefill-chunk shape: the last `queries` of a
+    65,536-token chunk after a 262,144-token prefix (81,920 compressed
+    entries, about 82 K visible per query), 64 index heads x 128, k = 1024."""
+    import compressed_sparse_kv_compress_amd as csa
+    HI, dI, m, k = 64, 128, 4, 1024
+    prefix, chunk = 262144, 65536
+    n_ctx = prefix + chunk
+    L = n_ctx // m
+    ki = syn.fill_(torch.empty((1, L, dI), dtype=torch.bfloat16, device="cuda"), 4, syn.TID["kic"], scale=dI ** -0.5)
+    qi = syn.fill_(torch.empty((1, queries, HI, dI), dtype=torch.bfloat16, device="cuda"), 4, syn.TID["q_idx"],
+                   scale=dI ** -0.5)
+    wi = syn.fill_(torch.empty((1, queries, HI), device="cuda"), 4, syn.TID["w_idx"], scale=HI ** -0.5)
+    ws = torch.empty(csa.csa_index_topk_workspace(1, queries, L, k), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((1, queries, k), dtype=torch.int32, device="cuda")
+
+    def call():
+        csa.csa_index_topk(qi, ki, m, k, w_idx=wi, n_ctx=n_ctx, idx=idx, ws=ws)
+
+    call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    t = torch.arange(n_ctx - queries, n_ctx, dtype=torch.float64)
+    pairs = float(torch.clamp(torch.floor(t / m), max=L).sum())
+    flop = pairs * HI * dI * 2
+    del ki, qi, ws
+    torch.cuda.empty_cache()
+    return {"queries": queries, "entries": L, "ms_per_call": ms, "tflops": flop / (ms * 1e-3) / 1e12,
+            "peak_tflops_bf16": 2500.0, "frac_of_bf16_peak": flop / (ms * 1e-3) / 1e12 / 2500.0,
+            "visible_pairs": pairs,
+            "note": "flop = 2 * visible (query, entry) pairs * index heads * index dim; each query row streams "
+                    "its keys (the decode scan), so the call is bound by key reads from the caches, not MFMA"}
+
+
 def decode_step_b1(steps: int, warmup: int):
     """The same bf16 8-layer step for one sequence (B = 1): the latency-bound
     end of the decode workload, reported beside the B = 16 headline."""
@@ -653,6 +693,9 @@ def main():
     prefill = None
     if args.prefill_queries > 0:
         prefill = prefill_sparse_attn(args.prefill_queries)
+        prefill["index_topk"] = prefill_index_topk()
+        print("# prefill index + top-k: %.2f ms (%.0f TFLOP/s)" % (prefill["index_topk"]["ms_per_call"],
+              prefill["index_topk"]["tflops"]), file=sys.stderr, flush=True)
         print("# prefill sparse attention: %.2f ms for %d queries (%.0f TFLOP/s)"
               % (prefill["ms_per_call"], prefill["queries"], prefill["tflops"]), file=sys.stderr, flush=True)
 

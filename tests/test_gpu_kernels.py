@@ -354,3 +354,47 @@ def test_generator_is_bit_identical_on_both_devices():
         a = syn.make((3, 1000, 72), 9, 4, dtype=torch.bfloat16, device="cuda", kind=kind, scale=0.25)
         b = syn.make((3, 1000, 72), 9, 4, dtype=torch.bfloat16, device="cpu", kind=kind, scale=0.25)
         assert torch.equal(a.cpu(), b)
+
+
+@pytest.mark.parametrize("B,T,L,HI,wts", [(2, 64, 9000, 64, True), (1, 128, 30000, 32, False),
+                                          (1, 64, 5000, 16, True), (1, 72, 4100, 128, False)])
+def test_index_scores_prefill_rows_equal_single_query_scan(B, T, L, HI, wts):
+    """Many queries per sequence take the 8-row prefill scoring kernel; every
+    row must equal, bit for bit, the same query scored alone (one query per
+    call takes the streaming scan), over all L entries incl. the -inf ones."""
+    dI, m = 128, 4
+    n_ctx = m * L - 3
+    seed = 70 + T
+    q, _ = both((B, T, HI, dI), seed, "q_idx", dtype=torch.bfloat16, scale=dI ** -0.5)
+    kk, _ = both((B, L, dI), seed, "k_idx", dtype=torch.bfloat16, scale=dI ** -0.5)
+    w = both((B, T, HI), seed, "w_idx", dtype=torch.float32, scale=HI ** -0.5)[0] if wts else None
+    full = csa.csa_index_score(q, kk, m, w_idx=w, n_ctx=n_ctx)
+    for b in {0, B - 1}:
+        for t in (0, 7, 8, T - 9, T - 1):
+            one = csa.csa_index_score(q[b:b + 1, t:t + 1].contiguous(), kk[b:b + 1].contiguous(), m,
+                                      w_idx=None if w is None else w[b:b + 1, t:t + 1].contiguous(),
+                                      n_ctx=n_ctx - T + t + 1)
+            torch.cuda.synchronize()
+            assert torch.equal(full[b, t].view(torch.int32), one[0, 0].view(torch.int32)), (b, t)
+
+
+def test_index_topk_prefill_rows_match_oracle():
+    """Index + top-k for 64 queries of one sequence (8-row scoring, then the
+    stand-alone top-k): exact on grid inputs, near-tie certified on Gaussian."""
+    B, T, HI, dI, m, k = 1, 64, 64, 128, 4, 512
+    n_ctx = 4 * 7000 + 1
+    L = -(-n_ctx // m)
+    q, q_c = both((B, T, HI, dI), 91, "q_idx", dtype=torch.bfloat16, kind="grid", scale=2.0 ** -4)
+    kk, k_c = both((B, L, dI), 91, "k_idx", dtype=torch.bfloat16, kind="grid", scale=2.0 ** -4)
+    idx = csa.csa_index_topk(q, kk, m, k, n_ctx=n_ctx).cpu().numpy()
+    want, _ = oracle.index_topk(q_c, k_c, m, k, n_ctx=n_ctx)
+    assert np.array_equal(idx, want)
+    q, q_c = both((B, T, HI, dI), 92, "q_idx", dtype=torch.bfloat16, scale=dI ** -0.5)
+    kk, k_c = both((B, L, dI), 92, "k_idx", dtype=torch.bfloat16, scale=dI ** -0.5)
+    got = csa.csa_index_topk(q, kk, m, k, n_ctx=n_ctx).cpu().numpy()
+    want, sc = oracle.index_topk(q_c, k_c, m, k, n_ctx=n_ctx)
+    ties = 0
+    for t in range(0, T, 9):
+        nv = min(L, (n_ctx - T + t) // m)
+        ties += near_tie_check(got[0, t], want[0, t], sc[0, t], nv, k, index_eps(q_c[0, t], None, k_c[0])[:nv])
+    assert ties <= 1
