@@ -530,8 +530,9 @@ def prefill_index_topk(queries: int = 4096, reps: int = 3):
     return {"queries": queries, "entries": L, "ms_per_call": ms, "tflops": flop / (ms * 1e-3) / 1e12,
             "peak_tflops_bf16": 2500.0, "frac_of_bf16_peak": flop / (ms * 1e-3) / 1e12 / 2500.0,
             "visible_pairs": pairs,
-            "note": "flop = 2 * visible (query, entry) pairs * index heads * index dim; each query row streams "
-                    "its keys (the decode scan), so the call is bound by key reads from the caches, not MFMA"}
+            "note": "flop = 2 * visible (query, entry) pairs * index heads * index dim; scores by the 16-row "
+                    "prefill kernel (each key tile read once per 16 queries), then the stand-alone top-k "
+                    "(about a fifth of the time)"}
 
 
 def decode_step_b1(steps: int, warmup: int):

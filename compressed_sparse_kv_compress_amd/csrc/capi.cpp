@@ -216,9 +216,9 @@ csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k
   OPT_PTR(out_score);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t rows = B * T;
-  // Many queries per sequence (prefill): the 8-row scoring kernel reads each
-  // key once per 8 queries; it writes scores, so the stand-alone top-k follows.
-  const bool multi = dtype == CSA_BF16 && d_I == 128 && csa::index_multi_rows(T, 0, rows);
+  // Many queries per sequence (prefill): the 16-row scoring kernel reads each
+  // key once per 16 queries; it writes scores, so the stand-alone top-k follows.
+  const bool multi = dtype == CSA_BF16 && d_I == 128 && csa::index_multi_rows(T, H_I, 0, rows);
   if (!multi && ws != nullptr && L > 0 && csa::index_topk_fusable(rows, L, H_I, d_I, k, to_dt(dtype)) &&
       ws_bytes >= csa::index_topk_fused_ws_bytes(rows, L, k)) {
     // The scan's workgroups keep their parts' candidates; no score matrix.
@@ -233,7 +233,7 @@ csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k
   if (!aligned16(ws)) return fail(CSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
   int64_t chunk = static_cast<int64_t>(ws_bytes / per_row);
   if (chunk > rows) chunk = rows;
-  if (multi && chunk >= 8) chunk -= chunk % 8;  // keep the 8-row blocks whole
+  if (multi && chunk >= 16) chunk -= chunk % 16;  // keep the 16-row blocks whole
   const size_t sc_bytes = (static_cast<size_t>(chunk) * (L > 0 ? L : 0) * sizeof(float) + 255) / 256 * 256;
   float* sc = static_cast<float*>(ws);
   void* sel_ws = static_cast<char*>(ws) + sc_bytes;

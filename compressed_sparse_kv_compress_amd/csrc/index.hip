@@ -507,18 +507,19 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
   }
 }
 
-// Prefill scoring (bf16, d_I = 128): a workgroup takes 8 query rows of one
-// sequence, one per wavefront with its query block resident as MFMA A
+// Prefill scoring (bf16, d_I = 128): a workgroup takes 16 query rows of one
+// sequence, two per wavefront with their query blocks resident as MFMA A
 // operands, and a part of up to kMultiKeys keys.  Each 16-key tile is staged
 // once in LDS (waves 0-3 load a quarter each; an 8-slot ring, one barrier per
-// tile) and read by all 8 wavefronts, so a key leaves the caches once per 8
-// queries instead of once per query.  Same MFMA order and epilogue as the
+// tile) and read by all 8 wavefronts, each B fragment feeding both rows'
+// MFMAs, so a key leaves the caches once per 16 queries.  Same MFMA order and epilogue as the
 // streaming scan, so the scores are bit-identical.  Scores collect in LDS
 // and leave at the end (no stores in the loop); keys past a row's visible
 // ones get -inf.
-constexpr int kMultiRows = 8;
+constexpr int kMultiRows = 16;
+constexpr int kMultiRpw = 2;  // rows per wavefront
 constexpr int kMultiDepth = 8;
-constexpr int kMultiKeys = 3840;  // keys per part: 8 rows x 15 KiB of scores in LDS
+constexpr int kMultiKeys = 1920;  // keys per part: 16 rows x 7.5 KiB of scores in LDS
 template <int MB, bool HAS_W>
 __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, int64_t parts) {
   constexpr int HI = 16 * MB;
@@ -535,11 +536,8 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
   const int c16 = lane & 15;
   const int64_t rblk = blockIdx.x / parts;
   const int64_t part = blockIdx.x % parts;
-  const int64_t row0 = a.row0 + rblk * kMultiRows;  // first row of the block (a multiple of 8; T % 8 == 0)
-  const int64_t row = row0 + wave;
+  const int64_t row0 = a.row0 + rblk * kMultiRows;  // first row of the block (a multiple of 16; T % 16 == 0)
   const int64_t b = row0 / a.T;
-  int64_t nv = (a.n_ctx - a.T + row % a.T) / a.m;
-  if (nv > a.L) nv = a.L;
   int64_t nvmax = (a.n_ctx - a.T + (row0 + kMultiRows - 1) % a.T) / a.m;  // the block's last row sees most
   if (nvmax > a.L) nvmax = a.L;
   const int64_t kb = part * kMultiKeys;
@@ -567,21 +565,22 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
     for (int i = 0; i < DEPTH - 1; ++i)
       if (i < ntiles) issue(i);
   }
-  bf16x8 afrag[MB][KS];
-  {
+  bf16x8 afrag[kMultiRpw][MB][KS];
+  float wr[kMultiRpw][MB][HAS_W ? 4 : 1];
+#pragma unroll
+  for (int i = 0; i < kMultiRpw; ++i) {
+    const int64_t row = row0 + kMultiRpw * wave + i;
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + row * HI * DI;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        afrag[mb][ks] = *reinterpret_cast<const bf16x8*>(qrow + (mb * 16 + c16) * DI + ks * 32 + g * 8);
+        afrag[i][mb][ks] = *reinterpret_cast<const bf16x8*>(qrow + (mb * 16 + c16) * DI + ks * 32 + g * 8);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < (HAS_W ? 4 : 1); ++r) wr[i][mb][r] = HAS_W ? a.w[row * HI + mb * 16 + 4 * g + r] : 1.f;
   }
-  float wr[MB][HAS_W ? 4 : 1];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < (HAS_W ? 4 : 1); ++r) wr[mb][r] = HAS_W ? a.w[row * HI + mb * 16 + 4 * g + r] : 1.f;
-  float* sb = sbuf[wave];
   for (int it = 0; it < ntiles; ++it) {
     if (wave < 4) {
       // this wave's loads issued after tile it's: they may stay in flight
@@ -590,9 +589,11 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
     }
     __syncthreads();  // tile it in LDS for every wave; every wave is done with tile it-1
     if (wave < 4 && it + DEPTH - 1 < ntiles) issue(it + DEPTH - 1);  // into tile it-1's slot
-    f32x4 acc[MB];
+    f32x4 acc[kMultiRpw][MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kMultiRpw; ++i)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[i][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint8_t* t = &ring[it % DEPTH][0] + c16 * 256;
     bf16x8 cur[KS];
 #pragma unroll
@@ -600,28 +601,41 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[mb][ks], cur[ks], acc[mb], 0, 0, 0);
-    float ps[MB];
+      for (int i = 0; i < kMultiRpw; ++i)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      float x[4];
+        for (int mb = 0; mb < MB; ++mb)
+          acc[i][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[i][mb][ks], cur[ks], acc[i][mb], 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = HAS_W ? wr[mb][HAS_W ? r : 0] * relu_bits(acc[mb][r]) : relu_bits(acc[mb][r]);
-      ps[mb] = (x[0] + x[1]) + (x[2] + x[3]);
+    for (int i = 0; i < kMultiRpw; ++i) {
+      float ps[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        float x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          x[r] = HAS_W ? wr[i][mb][HAS_W ? r : 0] * relu_bits(acc[i][mb][r]) : relu_bits(acc[i][mb][r]);
+        ps[mb] = (x[0] + x[1]) + (x[2] + x[3]);
+      }
+#pragma unroll
+      for (int w = 1; w < MB; w <<= 1)
+#pragma unroll
+        for (int mb = 0; mb + w < MB; mb += 2 * w) ps[mb] += ps[mb + w];
+      const float tot = group_sum4(ps[0]);
+      if (g == 0) sbuf[kMultiRpw * wave + i][it * kTileKeys + c16] = tot;
     }
-#pragma unroll
-    for (int w = 1; w < MB; w <<= 1)
-#pragma unroll
-      for (int mb = 0; mb + w < MB; mb += 2 * w) ps[mb] += ps[mb + w];
-    const float tot = group_sum4(ps[0]);
-    if (g == 0) sb[it * kTileKeys + c16] = tot;
   }
-  // this wave's row, keys [kb, ke): computed and visible, else -inf
-  float* srow = a.score + (row - a.row0) * a.ld;
+  // this wave's rows, keys [kb, ke): computed and visible, else -inf
   const int nk = static_cast<int>(ke - kb);
   const int nc = ntiles * kTileKeys;
-  for (int o = lane; o < nk; o += 64) srow[kb + o] = (o < nc && kb + o < nv) ? sb[o] : -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kMultiRpw; ++i) {
+    const int64_t row = row0 + kMultiRpw * wave + i;
+    int64_t nv = (a.n_ctx - a.T + row % a.T) / a.m;
+    if (nv > a.L) nv = a.L;
+    float* srow = a.score + (row - a.row0) * a.ld;
+    const float* sb = sbuf[kMultiRpw * wave + i];
+    for (int o = lane; o < nk; o += 64) srow[kb + o] = (o < nc && kb + o < nv) ? sb[o] : -INFINITY;
+  }
 }
 
 // Other d_I (64): MFMA operands straight from global memory (64 B per key
@@ -769,19 +783,19 @@ hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t s) {
   if (a.dt == kBF16) {
     const int mb = static_cast<int>(a.HI / 16), ks = static_cast<int>(a.dI / 32);
     const bool w = a.w != nullptr;
-    if (ks == 4 && index_multi_rows(a.T, a.row0, a.nrows)) {
+    if (ks == 4 && index_multi_rows(a.T, a.HI, a.row0, a.nrows)) {
       const int64_t parts = (a.L + kMultiKeys - 1) / kMultiKeys;
       const dim3 grid(static_cast<uint32_t>(a.nrows / kMultiRows * parts));
-#define CSA_INDEX_MULTI(MB_)                                                                               \
-  case MB_:                                                                                                \
-    if (w) hipLaunchKernelGGL((index_score_multi<MB_, true>), grid, dim3(64 * kMultiRows), 0, s, a, parts);  \
-    else hipLaunchKernelGGL((index_score_multi<MB_, false>), grid, dim3(64 * kMultiRows), 0, s, a, parts);   \
+      const dim3 block(64 * kMultiRows / kMultiRpw);
+#define CSA_INDEX_MULTI(MB_)                                                                        \
+  case MB_:                                                                                         \
+    if (w) hipLaunchKernelGGL((index_score_multi<MB_, true>), grid, block, 0, s, a, parts);          \
+    else hipLaunchKernelGGL((index_score_multi<MB_, false>), grid, block, 0, s, a, parts);           \
     break;
       switch (mb) {
         CSA_INDEX_MULTI(1)
         CSA_INDEX_MULTI(2)
         CSA_INDEX_MULTI(4)
-        CSA_INDEX_MULTI(8)
         default: return hipErrorInvalidValue;
       }
 #undef CSA_INDEX_MULTI
@@ -812,8 +826,10 @@ hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-bool index_multi_rows(int64_t T, int64_t row0, int64_t nrows) {
-  return T >= 64 && T % kMultiRows == 0 && row0 % kMultiRows == 0 && nrows % kMultiRows == 0 && nrows > 0;
+bool index_multi_rows(int64_t T, int64_t HI, int64_t row0, int64_t nrows) {
+  // H_I <= 64: two rows' query blocks stay in registers
+  return HI <= 64 && HI % 16 == 0 && T >= 64 && T % kMultiRows == 0 && row0 % kMultiRows == 0 &&
+         nrows % kMultiRows == 0 && nrows > 0;
 }
 
 bool index_topk_fusable(int64_t nrows, int64_t L, int64_t HI, int64_t dI, int64_t k, Dt dt) {

@@ -90,10 +90,10 @@ inline void compact_list_plan(int64_t nparts, int64_t k, int64_t* lrank, int64_t
 // scan's workgroups select their parts' candidates from LDS, then the merge
 // runs.  Available for bf16 and FP8, d_I = 128, k <= 2048 when the scan's
 // parts give the merge's fast path; ws: index_topk_fused_ws_bytes(nrows, L, k).
-// Prefill scoring of 8 rows per workgroup (bf16, d_I = 128) applies to a
-// launch of rows [row0, row0 + nrows) when every sequence has T >= 64 queries
-// with T, row0 and nrows multiples of 8.
-bool index_multi_rows(int64_t T, int64_t row0, int64_t nrows);
+// Prefill scoring of 16 rows per workgroup (bf16, d_I = 128, H_I <= 64)
+// applies to a launch of rows [row0, row0 + nrows) when every sequence has
+// T >= 64 queries with T, row0 and nrows multiples of 16.
+bool index_multi_rows(int64_t T, int64_t HI, int64_t row0, int64_t nrows);
 bool index_topk_fusable(int64_t nrows, int64_t L, int64_t HI, int64_t dI, int64_t k, Dt dt);
 size_t index_topk_fused_ws_bytes(int64_t nrows, int64_t L, int64_t k);
 hipError_t launch_index_topk_fused(const IndexScoreArgs& a, const TopkArgs& t, void* ws, hipStream_t s);

@@ -357,7 +357,7 @@ def test_generator_is_bit_identical_on_both_devices():
 
 
 @pytest.mark.parametrize("B,T,L,HI,wts", [(2, 64, 9000, 64, True), (1, 128, 30000, 32, False),
-                                          (1, 64, 5000, 16, True), (1, 72, 4100, 128, False)])
+                                          (1, 64, 5000, 16, True), (1, 72, 4100, 128, False), (1, 64, 3000, 128, True)])
 def test_index_scores_prefill_rows_equal_single_query_scan(B, T, L, HI, wts):
     """Many queries per sequence take the 8-row prefill scoring kernel; every
     row must equal, bit for bit, the same query scored alone (one query per
