@@ -616,6 +616,7 @@ def main():
     ap.add_argument("--prefill-queries", type=int, default=16384,
                     help="queries of the prefill sparse-attention measurement (0: skip)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-storage step")
+    ap.add_argument("--no-batch1", action="store_true", help="skip the batch-1 decode step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run a plain device copy of BYTES bytes 3 times (counter calibration)")
     args = ap.parse_args()
@@ -687,7 +688,7 @@ def main():
               flush=True)
 
     b1 = None
-    if args.batch != 1:
+    if args.batch != 1 and not args.no_batch1:
         b1 = decode_step_b1(args.steps, args.warmup)
         print("# batch 1: %.3f ms/step" % b1["ms_per_step"], file=sys.stderr, flush=True)
 
