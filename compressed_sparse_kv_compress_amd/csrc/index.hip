@@ -511,7 +511,7 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
 // sequence, two per wavefront with their query blocks resident as MFMA A
 // operands, and a part of up to kMultiKeys keys.  Each 16-key tile is staged
 // once in LDS (waves 0-3 load a quarter each; an 8-slot ring, one barrier per
-// tile) and read by all 8 wavefronts, each B fragment feeding both rows'
+// two tiles) and read by all 8 wavefronts, each B fragment feeding both rows'
 // MFMAs, so a key leaves the caches once per 16 queries.  Same MFMA order and epilogue as the
 // streaming scan, so the scores are bit-identical.  Scores collect in LDS
 // and leave at the end (no stores in the loop); keys past a row's visible
@@ -562,7 +562,7 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
   };
   if (wave < 4) {
 #pragma unroll
-    for (int i = 0; i < DEPTH - 1; ++i)
+    for (int i = 0; i < DEPTH - 2; ++i)
       if (i < ntiles) issue(i);
   }
   bf16x8 afrag[kMultiRpw][MB][KS];
@@ -581,20 +581,15 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
 #pragma unroll
       for (int r = 0; r < (HAS_W ? 4 : 1); ++r) wr[i][mb][r] = HAS_W ? a.w[row * HI + mb * 16 + 4 * g + r] : 1.f;
   }
-  for (int it = 0; it < ntiles; ++it) {
-    if (wave < 4) {
-      // this wave's loads issued after tile it's: they may stay in flight
-      const int ahead = DEPTH - 2 < ntiles - 1 - it ? DEPTH - 2 : ntiles - 1 - it;
-      wait_tiles<1>(ahead);
-    }
-    __syncthreads();  // tile it in LDS for every wave; every wave is done with tile it-1
-    if (wave < 4 && it + DEPTH - 1 < ntiles) issue(it + DEPTH - 1);  // into tile it-1's slot
+  // Two tiles per barrier: tiles it and it+1 (slots it%8, (it+1)%8); their
+  // slots are refilled with tiles it+6 and it+7 after the next barrier.
+  auto tile = [&](int tt) {
     f32x4 acc[kMultiRpw][MB];
 #pragma unroll
     for (int i = 0; i < kMultiRpw; ++i)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) acc[i][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint8_t* t = &ring[it % DEPTH][0] + c16 * 256;
+    const uint8_t* t = &ring[tt % DEPTH][0] + c16 * 256;
     bf16x8 cur[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) cur[ks] = *reinterpret_cast<const bf16x8*>(t + (((4 * ks + g) ^ c16) << 4));
@@ -621,8 +616,23 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
 #pragma unroll
         for (int mb = 0; mb + w < MB; mb += 2 * w) ps[mb] += ps[mb + w];
       const float tot = group_sum4(ps[0]);
-      if (g == 0) sbuf[kMultiRpw * wave + i][it * kTileKeys + c16] = tot;
+      if (g == 0) sbuf[kMultiRpw * wave + i][tt * kTileKeys + c16] = tot;
     }
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    if (wave < 4) {
+      // loads issued after tile it+1's (or it's, at the end) may stay in flight
+      const int last = it + 1 < ntiles ? it + 1 : it;
+      const int issued = it + DEPTH - 2 < ntiles ? it + DEPTH - 2 : ntiles;  // tiles [0, issued) issued
+      wait_tiles<1>(issued - 1 - last);
+    }
+    __syncthreads();  // tiles it, it+1 in LDS; every wave is done with it-2, it-1
+    if (wave < 4) {
+      if (it + DEPTH - 2 < ntiles) issue(it + DEPTH - 2);  // into tile it-2's slot
+      if (it + DEPTH - 1 < ntiles) issue(it + DEPTH - 1);  // into tile it-1's slot
+    }
+    tile(it);
+    if (it + 1 < ntiles) tile(it + 1);
   }
   // this wave's rows, keys [kb, ke): computed and visible, else -inf
   const int nk = static_cast<int>(ke - kb);
