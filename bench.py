@@ -161,7 +161,7 @@ class GpuState:
                         raw_rows(st, "zb_" + s, li, p0, 2 * m, D, device, 0.5, sto))
                 lay["p0"] = p0
                 lay["idx"] = torch.empty((B, 1, st.k), dtype=torch.int32, device=device)
-                lay["itk_ws"] = torch.empty(max(16, csa.csa_index_topk_workspace(B, 1, L, st.k)),
+                lay["itk_ws"] = torch.empty(max(16, csa.csa_index_topk_workspace(B, 1, L, st.HI, st.k)),
                                             dtype=torch.uint8, device=device)
                 nb = csa.csa_sparse_attn_workspace(B, 1, H, d, st.k, st.W, dt_code)
             else:
@@ -507,7 +507,7 @@ def prefill_index_topk(queries: int = 4096, reps: int = 3):
     qi = syn.fill_(torch.empty((1, queries, HI, dI), dtype=torch.bfloat16, device="cuda"), 4, syn.TID["q_idx"],
                    scale=dI ** -0.5)
     wi = syn.fill_(torch.empty((1, queries, HI), device="cuda"), 4, syn.TID["w_idx"], scale=HI ** -0.5)
-    ws = torch.empty(csa.csa_index_topk_workspace(1, queries, L, k), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(csa.csa_index_topk_workspace(1, queries, L, HI, k), dtype=torch.uint8, device="cuda")
     idx = torch.empty((1, queries, k), dtype=torch.int32, device="cuda")
 
     def call():
@@ -579,7 +579,7 @@ def index_topk_mxfp4(B: int, reps: int = 20):
     q, kk = csa.MXFP4(qb, (B, 1, HI, dI)), csa.MXFP4(kb, (B, L, dI))
     w = syn.fill_(torch.empty((B, 1, HI), device="cuda"), SEED, syn.TID["w_idx"], scale=HI ** -0.5)
     idx = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
-    ws = torch.empty(csa.csa_index_topk_workspace(B, 1, L, k), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(csa.csa_index_topk_workspace(B, 1, L, HI, k), dtype=torch.uint8, device="cuda")
 
     def call():
         csa.csa_index_topk(q, kk, m, k, w_idx=w, n_ctx=st.n_ctx, idx=idx, ws=ws)

@@ -51,8 +51,9 @@ _hca_compress = _sig("hca_compress", [_vp] * 4 + [_i64] * 9 + [_i32, _vp])
 _csa_index_score = _sig("csa_index_score", [_vp] * 3 + [_i64] * 7 + [_vp, _i32, _vp])
 _csa_topk_select_workspace = _sig("csa_topk_select_workspace", [_i64] * 4, _sz)
 _csa_topk_select = _sig("csa_topk_select", [_vp] + [_i64] * 6 + [_vp, _vp, _vp, _sz, _vp])
-_csa_index_topk_workspace = _sig("csa_index_topk_workspace", [_i64] * 4, _sz)
+_csa_index_topk_workspace = _sig("csa_index_topk_workspace", [_i64] * 5, _sz)
 _csa_index_topk = _sig("csa_index_topk", [_vp] * 3 + [_i64] * 8 + [_vp, _vp, _vp, _sz, _i32, _vp])
+_csa_attn_workspace = _sig("csa_attn_workspace", [_i64] * 5, _sz)
 _csa_sparse_attn_workspace = _sig("csa_sparse_attn_workspace", [_i64] * 6 + [_i32], _sz)
 _csa_sparse_attn = _sig("csa_sparse_attn", [_vp] * 3 + [_i64, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _f32]
                         + [_i64] * 5 + [_vp, _vp, _vp, _sz, _i32, _vp])
@@ -215,8 +216,8 @@ def csa_topk_select(score, m, k, *, n_ctx, idx=None, out_score=None, want_scores
     return (idx, out_score) if want_scores else idx
 
 
-def csa_index_topk_workspace(B, T, L, k) -> int:
-    return int(_csa_index_topk_workspace(B, T, L, k))
+def csa_index_topk_workspace(B, T, L, H_I, k) -> int:
+    return int(_csa_index_topk_workspace(B, T, L, H_I, k))
 
 
 def csa_index_topk(q_idx, k_idx, m, k, *, w_idx=None, n_ctx, ws=None, idx=None, out_score=None,
@@ -228,7 +229,7 @@ def csa_index_topk(q_idx, k_idx, m, k, *, w_idx=None, n_ctx, ws=None, idx=None, 
     if want_scores and out_score is None:
         out_score = torch.empty((B, T, k), dtype=torch.float32, device=q_idx.device)
     if ws is None:
-        nb = max(16, csa_index_topk_workspace(B, T, L, k))
+        nb = max(16, csa_index_topk_workspace(B, T, L, HI, k))
         ws = torch.empty(nb, dtype=torch.uint8, device=q_idx.device)
     st = _csa_index_topk(_ptr(q_idx), _ptr(w_idx), _ptr(k_idx), B, T, n_ctx, L, HI, dI, m, k,
                          idx.data_ptr(), _ptr(out_score), ws.data_ptr(), ws.numel() * ws.element_size(),
@@ -248,6 +249,10 @@ def _attn_out(q, out, lse, want_lse):
     if want_lse and lse is None:
         lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
     return out, lse
+
+
+def csa_attn_workspace(B, T, H, d, n_rows) -> int:
+    return int(_csa_attn_workspace(B, T, H, d, n_rows))
 
 
 def csa_sparse_attn_workspace(B, T, H, d, k, W, dtype) -> int:

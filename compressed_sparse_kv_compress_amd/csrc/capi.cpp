@@ -197,7 +197,8 @@ static size_t index_topk_row_bytes(int64_t L, int64_t k) {
   return sc + csa::topk_ws_bytes_per_row(L, k);
 }
 
-size_t csa_index_topk_workspace(int64_t B, int64_t T, int64_t L, int64_t k) {
+size_t csa_index_topk_workspace(int64_t B, int64_t T, int64_t L, int64_t H_I, int64_t k) {
+  (void)H_I;
   if (B <= 0 || T <= 0 || k <= 0) return 0;
   const size_t chunked = static_cast<size_t>(B) * T * index_topk_row_bytes(L, k);
   const size_t fused = L > 0 ? csa::index_topk_fused_ws_bytes(B * T, L, k) : 0;
@@ -264,6 +265,16 @@ size_t hca_dense_attn_workspace(int64_t B, int64_t T, int64_t H, int64_t d, int6
   if (B <= 0 || T <= 0 || m <= 0) return 0;
   const int ns = csa::attn_splits(B, T, H, d, dense_max_rows(L, m, n_ctx, W), to_dt(dtype), false);
   return csa::attn_ws_bytes(B, T, H, d, ns);
+}
+
+size_t csa_attn_workspace(int64_t B, int64_t T, int64_t H, int64_t d, int64_t n_rows) {
+  if (B <= 0 || T <= 0 || n_rows < 0) return 0;
+  // The split plan depends on the row count and on whether rows are gathered;
+  // the bf16 plan covers FP8 too, and fp32 needs none.
+  const int ns_s = csa::attn_splits(B, T, H, d, n_rows, csa::kBF16, true);
+  const int ns_d = csa::attn_splits(B, T, H, d, n_rows, csa::kBF16, false);
+  const size_t a = csa::attn_ws_bytes(B, T, H, d, ns_s), b = csa::attn_ws_bytes(B, T, H, d, ns_d);
+  return a > b ? a : b;
 }
 
 static csa_status_t attn_launch(const csa::AttnArgs& a, bool sparse, int64_t max_rows, csa_dtype_t dt,

@@ -150,11 +150,13 @@ csa_status_t csa_topk_select(const float* score, int64_t B, int64_t T, int64_t n
  * scan keeps each key range's top-k candidates itself and no score matrix is
  * written (two kernels); otherwise the fp32 score matrix and the selection
  * scratch are kept in the caller's workspace.  When ws_bytes is below
- * csa_index_topk_workspace(B, T, L, k) the queries are processed in groups
- * that fit; ws_bytes must cover at least one query
- * (csa_index_topk_workspace(1, 1, L, k)).  Results do not depend on ws_bytes.
- * The workspace is scratch: its contents on entry do not matter. */
-size_t csa_index_topk_workspace(int64_t B, int64_t T, int64_t L, int64_t k);
+ * csa_index_topk_workspace(B, T, L, H_I, k) the queries are processed in
+ * groups that fit; ws_bytes must cover at least one query
+ * (csa_index_topk_workspace(1, 1, L, H_I, k)).  Results do not depend on
+ * ws_bytes.  The workspace is scratch: its contents on entry do not matter.
+ * The size does not depend on H_I today; the argument keeps kernels free to
+ * stage per-head data. */
+size_t csa_index_topk_workspace(int64_t B, int64_t T, int64_t L, int64_t H_I, int64_t k);
 csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int64_t B,
                             int64_t T, int64_t n_ctx, int64_t L, int64_t H_I, int64_t d_I,
                             int64_t m, int64_t k, int32_t* idx, float* out_score, void* ws,
@@ -193,6 +195,13 @@ csa_status_t csa_sparse_attn(const void* q, const void* kc, const void* vc, int6
                              int64_t T, int64_t n_ctx, int64_t H, int64_t d, void* out,
                              float* lse, void* ws, size_t ws_bytes, csa_dtype_t dtype,
                              void* stream);
+
+/* csa_attn_workspace -- workspace bytes that serve any attention call of the
+ * given B, T, H, d whose per-query row list (csa_sparse_attn: k + W rows;
+ * hca_dense_attn: min(L, floor(t/m)) + W rows) is at most n_rows long, for
+ * every storage type.  It is at least csa_sparse_attn_workspace and
+ * hca_dense_attn_workspace of such calls, which give the exact need. */
+size_t csa_attn_workspace(int64_t B, int64_t T, int64_t H, int64_t d, int64_t n_rows);
 
 /* hca_dense_attn -- HCA attention: every visible compressed entry s <
  * min(L, floor(t/m)) densely, no indexer (shareware.cn article, section 八;

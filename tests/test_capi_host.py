@@ -28,8 +28,60 @@ def lib():
 def test_header_declares_the_hot_path_calls():
     names = _declared()
     for n in ("csa_compress", "hca_compress", "csa_index_topk", "csa_sparse_attn", "hca_dense_attn",
-              "csa_index_score", "csa_topk_select"):
+              "csa_index_score", "csa_topk_select", "csa_attn_workspace", "csa_index_topk_workspace"):
         assert n in names
+
+
+def _params(name):
+    """Parameter names of a function declared in the header."""
+    src = re.sub(r"/\*.*?\*/", "", open(HDR).read(), flags=re.S)
+    m = re.search(r"\b%s\s*\(([^)]*)\)\s*;" % name, src)
+    assert m, name
+    return [re.findall(r"(\w+)\s*$", p.strip())[0] for p in m.group(1).split(",") if p.strip() != "void"]
+
+
+# The boundary the hot path is built to: every call, in argument order.  The
+# stream is `stream` (a void* holding a hipStream_t) and the dtype `dtype`
+# everywhere.  csa_compress / hca_compress add (p0, n_raw, e0, e1, out_ld)
+# after m, so the same call writes a decode-time entry into a cache slot.
+CONTRACT = {
+    "csa_compress": ["x_a", "z_a", "x_b", "z_b", "bias", "out", "B", "n", "D", "m",
+                     "p0", "n_raw", "e0", "e1", "out_ld", "dtype", "stream"],
+    "hca_compress": ["x", "z", "bias", "out", "B", "n", "D", "m", "p0", "n_raw", "e0", "e1", "out_ld",
+                     "dtype", "stream"],
+    "csa_index_topk_workspace": ["B", "T", "L", "H_I", "k"],
+    "csa_index_topk": ["q_idx", "w_idx", "k_idx", "B", "T", "n_ctx", "L", "H_I", "d_I", "m", "k", "idx",
+                       "out_score", "ws", "ws_bytes", "dtype", "stream"],
+    "csa_attn_workspace": ["B", "T", "H", "d", "n_rows"],
+    "csa_sparse_attn": ["q", "kc", "vc", "L", "idx", "k", "kr", "vr", "R", "W", "sink", "scale", "B", "T",
+                        "n_ctx", "H", "d", "out", "lse", "ws", "ws_bytes", "dtype", "stream"],
+    "hca_dense_attn": ["q", "kc", "vc", "L", "m", "kr", "vr", "R", "W", "sink", "scale", "B", "T", "n_ctx",
+                       "H", "d", "out", "lse", "ws", "ws_bytes", "dtype", "stream"],
+    "csa_status_string": ["status"],
+}
+
+
+def test_header_matches_the_boundary_contract(lib):
+    names = _declared()
+    for name, params in CONTRACT.items():
+        assert name in names, name
+        assert hasattr(lib, name), name
+        assert _params(name) == params, (name, _params(name))
+
+
+def test_attn_workspace_covers_both_attention_calls(lib):
+    aw = lib.csa_attn_workspace
+    aw.argtypes, aw.restype = [I] * 5, Z
+    sw = lib.csa_sparse_attn_workspace
+    sw.argtypes, sw.restype = [I] * 6 + [ctypes.c_int], Z
+    dw = lib.hca_dense_attn_workspace
+    dw.argtypes, dw.restype = [I] * 8 + [ctypes.c_int], Z
+    for B, T in ((1, 1), (16, 1), (4, 1), (1, 300)):
+        # sparse: k + W rows; dense at 1M tokens, m = 128: 7812 visible + W
+        assert aw(B, T, 64, 512, 1024 + 128) >= sw(B, T, 64, 512, 1024, 128, 1)
+        assert aw(B, T, 64, 512, 7812 + 128) >= dw(B, T, 64, 512, 7813, 128, 1000000, 128, 1)
+        assert aw(B, T, 64, 512, 7812) >= dw(B, T, 64, 512, 7813, 128, 1000000, 0, 2)
+    assert aw(0, 1, 64, 512, 100) == 0
 
 
 def test_library_exports_every_declared_symbol(lib):

@@ -148,6 +148,11 @@ def test_config2_csa_decode_128k():
         kr_c = c_rows((B, n, d), seq_rows(b, n, n - W), seed, "k", BF, sd).reshape(1, W, d)
         vr_c = c_rows((B, n, d), seq_rows(b, n, n - W), seed, "v", BF, sd).reshape(1, W, d)
         sink_c = g_make((H,), seed, "sink", torch.float32, 1.0, "cpu").double().numpy()
+        # attention checked twice: the oracle fed the GPU's own selection, and
+        # end to end (the oracle's own selection)
+        o_g, l_g = oracle.sparse_attn(q_c, kc_c, vc_c, idx_g[b:b + 1], kr_c, vr_c, W, sink=sink_c, n_ctx=n)
+        assert max_abs(to_np(out[b:b + 1]), o_g) <= BF16_TOL
+        assert max_abs(to_np(lse[b:b + 1]), l_g) <= 1e-2
         o_c, l_c = oracle.sparse_attn(q_c, kc_c, vc_c, idx_c, kr_c, vr_c, W, sink=sink_c, n_ctx=n)
         assert max_abs(to_np(out[b:b + 1]), o_c) <= BF16_TOL
         assert max_abs(to_np(lse[b:b + 1]), l_c) <= 1e-2
@@ -246,7 +251,7 @@ def test_config4_csa_prefill_chunk(where):
                            w_c=wi_c[0])
     assert ties <= 1
     same = [i for i, s in enumerate(sample) if np.array_equal(idx_g[s], idx_c[0, i])]
-    assert len(same) >= len(sample) - 1
+    assert len(same) >= len(sample) - 1  # a near-tie swap may differ in at most one sampled row
     kc_c = g_make((1, L, d), seed, "kc", BF, sd, "cpu").double().numpy()
     vc_c = g_make((1, L, d), seed, "vc", BF, sd, "cpu").double().numpy()
     q_c = syn.rows((1, chunk, H, d), np.concatenate([np.arange((q0 + s) * H, (q0 + s + 1) * H) for s in sample]),
@@ -254,10 +259,15 @@ def test_config4_csa_prefill_chunk(where):
     kr_c = syn.rows((1, n_full, d), raw, seed, syn.TID["kr"], dtype=BF, scale=sd).double().numpy().reshape(1, R, d)
     vr_c = syn.rows((1, n_full, d), raw, seed, syn.TID["vr"], dtype=BF, scale=sd).double().numpy().reshape(1, R, d)
     sink_c = g_make((H,), seed, "sink", torch.float32, 1.0, "cpu").double().numpy()
-    o_c, _ = oracle.sparse_attn(q_c, kc_c, vc_c, idx_c, kr_c, vr_c, W, sink=sink_c, n_ctx=n_ctx, tpos=tpos)
     got = to_np(out)[0][sample]
-    for i in same:
-        assert max_abs(got[i], o_c[0, i]) <= BF16_TOL
+    # attention checked twice on every sampled query: the oracle fed the GPU's
+    # own selection, and end to end (the oracle's selection; a near-tie swap
+    # moves one row of weight ~1/1152, far inside the bound)
+    o_g, _ = oracle.sparse_attn(q_c, kc_c, vc_c, idx_g[sample][None], kr_c, vr_c, W, sink=sink_c, n_ctx=n_ctx,
+                                tpos=tpos)
+    assert max_abs(got, o_g[0]) <= BF16_TOL
+    o_c, _ = oracle.sparse_attn(q_c, kc_c, vc_c, idx_c, kr_c, vr_c, W, sink=sink_c, n_ctx=n_ctx, tpos=tpos)
+    assert max_abs(got, o_c[0]) <= BF16_TOL
 
 
 # ---------------------------------------------------------------------------
@@ -305,14 +315,19 @@ def test_config5_stack_step_sampled():
             ties = check_topk_rows(got_idx, idx_c[0], sc[0], qi_c[0], ki_c[0], np.array([st.nv_csa]), st.k,
                                    w_c=wi_c[0])
             assert ties <= 1
-            sel = idx_c[0, 0][idx_c[0, 0] >= 0]
+            # the rows either selection reads (the GPU's and the oracle's)
+            sel = np.union1d(idx_c[0, 0][idx_c[0, 0] >= 0], got_idx[0][got_idx[0] >= 0])
             kc_c = np.zeros((1, L, st.d))
             vc_c = np.zeros((1, L, st.d))
             kc_c[0, sel] = c_rows((st.B, L, st.d), b * L + sel, SEED, "kc", bf, sd, layer=li)
             vc_c[0, sel] = c_rows((st.B, L, st.d), b * L + sel, SEED, "vc", bf, sd, layer=li)
+            got_out = to_np(lay["out"][b:b + 1])
+            # attention checked twice: the oracle fed the GPU's selection, and end to end
+            o_g, _ = oracle.sparse_attn(q_c, kc_c, vc_c, got_idx[None], kr_c, vr_c, st.W, sink=sink_c,
+                                        n_ctx=st.n_ctx)
+            assert max_abs(got_out, o_g) <= BF16_TOL
             o_c, _ = oracle.sparse_attn(q_c, kc_c, vc_c, idx_c, kr_c, vr_c, st.W, sink=sink_c, n_ctx=st.n_ctx)
-            if np.array_equal(got_idx, idx_c[0]):
-                assert max_abs(to_np(lay["out"][b:b + 1]), o_c) <= BF16_TOL
+            assert max_abs(got_out, o_c) <= BF16_TOL
         else:
             m = st.m_hca
             p0 = lay["p0"]

@@ -134,7 +134,15 @@ def _seeded_scores(B, T, L, seed, device):
 
 
 @pytest.mark.parametrize("B,T,L,m,k", [(2, 3, 5000, 1, 64), (1, 4, 250000, 4, 1024),
-                                      (3, 1, 33000, 4, 1024), (2, 5, 700, 1, 1024), (1, 2, 9000, 1, 1)])
+                                      (3, 1, 33000, 4, 1024), (2, 5, 700, 1, 1024), (1, 2, 9000, 1, 1),
+                                      # general merge (parts x min(k, 16384) > 16384 slots), staged parts
+                                      (1, 2, 250000, 1, 2048),
+                                      # general merge with parts and merge emitting straight to memory
+                                      (1, 2, 250000, 1, 4096),
+                                      # k above one part: every part kept whole, general merge
+                                      (1, 2, 250000, 1, 20000),
+                                      # one part, k above the LDS staging size: direct emit in both kernels
+                                      (2, 2, 10000, 1, 4096)])
 def test_topk_select_bit_exact_on_seeded_scores(B, T, L, m, k):
     n_ctx = L * m
     sg = _seeded_scores(B, T, L, 5 + L, "cuda")
@@ -171,7 +179,7 @@ def _structured(s, pattern):
 
 
 @pytest.mark.parametrize("pattern", ["boost32", "sink16", "steps", "ramp"])
-@pytest.mark.parametrize("L,k", [(250000, 1024), (40000, 2048), (20000, 64)])
+@pytest.mark.parametrize("L,k", [(250000, 1024), (40000, 2048), (20000, 64), (250000, 2048), (10000, 4096)])
 def test_topk_select_exact_on_structured_scores(pattern, L, k):
     B, T, m = 2, 2, 1
     n_ctx = L * m
@@ -198,9 +206,28 @@ def test_index_topk_bit_exact_on_grid_inputs():
     want, _ = oracle.index_topk(q_c, k_c, m, k, n_ctx=n_ctx)
     assert np.array_equal(got, want)
     # a workspace holding one row at a time gives the same result
-    ws = torch.empty(csa.csa_index_topk_workspace(1, 1, L, k), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(csa.csa_index_topk_workspace(1, 1, L, HI, k), dtype=torch.uint8, device="cuda")
     got2 = csa.csa_index_topk(q, kk, m, k, n_ctx=n_ctx, ws=ws).cpu().numpy()
     assert np.array_equal(got2, want)
+
+
+@pytest.mark.parametrize("k", [2048, 4096])
+def test_index_topk_one_row_workspace_general_merge(k):
+    """csa_index_topk with a workspace of one query row at k = 2048 / 4096
+    over 250,000 entries: each row is scored, then selected by the part
+    kernel and the general merge (16 parts x k slots).  Grid inputs make every
+    fp32 score exact, so the indices must equal the oracle's bit for bit."""
+    B, T, HI, dI, m = 1, 2, 16, 128, 4
+    L = 250000
+    n_ctx = m * L
+    q, q_c = both((B, T, HI, dI), 17, "q_idx", dtype=torch.bfloat16, kind="grid", scale=2.0 ** -4)
+    kk, k_c = both((B, L, dI), 17, "k_idx", dtype=torch.bfloat16, kind="grid", scale=2.0 ** -4)
+    ws = torch.empty(csa.csa_index_topk_workspace(1, 1, L, HI, k), dtype=torch.uint8, device="cuda")
+    got = csa.csa_index_topk(q, kk, m, k, n_ctx=n_ctx, ws=ws).cpu().numpy()
+    full = csa.csa_index_topk(q, kk, m, k, n_ctx=n_ctx).cpu().numpy()
+    want, _ = oracle.index_topk(q_c, k_c, m, k, n_ctx=n_ctx)
+    assert np.array_equal(got, want)
+    assert np.array_equal(full, want)
 
 
 @pytest.mark.parametrize("B,T,L,HI,k,wts,boost", [(16, 1, 250000, 64, 1024, True, 1), (4, 3, 9000, 32, 512, False, 1),
@@ -242,6 +269,18 @@ def test_index_topk_single_pass_equals_score_then_select(B, T, L, HI, k, wts, bo
     torch.cuda.synchronize()
     assert torch.equal(idx1, idx2)
     assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    # every row: the selection over the GPU's own fp32 scores is the stable
+    # sort of those scores (no near-tie allowance), and the kept scores are
+    # those scores
+    sc_np = sc.cpu().double().numpy()
+    nv_all = np.minimum((n_ctx - T + np.arange(T)) // m, L)
+    want_all = oracle.topk(sc_np, np.broadcast_to(nv_all, (B, T)), k)
+    assert np.array_equal(idx1.cpu().numpy(), want_all)
+    s1_np = s1.cpu().double().numpy()
+    for bb in range(B):
+        for tt in range(T):
+            sel = want_all[bb, tt] >= 0
+            assert np.array_equal(s1_np[bb, tt][sel], sc_np[bb, tt][want_all[bb, tt][sel]])
     # one row against the oracle (exact up to certified near ties)
     b, t = B - 1, T - 1
     nv = min(L, (n_ctx - T + t) // m)
@@ -259,6 +298,7 @@ def test_index_topk_gaussian_exact_up_to_near_ties(dt, HI, dI, k):
     q, q_c = both((B, T, HI, dI), 21, "q_idx", dtype=DT[dt], scale=dI ** -0.5)
     kk, k_c = both((B, L, dI), 21, "k_idx", dtype=DT[dt], scale=dI ** -0.5)
     got = csa.csa_index_topk(q, kk, m, k, n_ctx=n_ctx).cpu().numpy()
+    sc_gpu = csa.csa_index_score(q, kk, m, n_ctx=n_ctx).cpu().double().numpy()
     want, sc = oracle.index_topk(q_c, k_c, m, k, n_ctx=n_ctx)
     ties = 0
     for b in range(B):
@@ -267,6 +307,9 @@ def test_index_topk_gaussian_exact_up_to_near_ties(dt, HI, dI, k):
             ties += near_tie_check(got[b, t], want[b, t], sc[b, t], nv, k,
                                    index_eps(q_c[b, t], None, k_c[b])[:nv])
     assert ties <= 1
+    # the selection on the GPU's own scores is exactly their stable sort
+    nv_all = np.minimum((n_ctx - T + np.arange(T)) // m, L)
+    assert np.array_equal(got, oracle.topk(sc_gpu, np.broadcast_to(nv_all, (B, T)), k))
 
 
 # ---------------------------------------------------------------------------
