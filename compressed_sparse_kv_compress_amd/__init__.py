@@ -53,6 +53,8 @@ _csa_topk_select_workspace = _sig("csa_topk_select_workspace", [_i64] * 4, _sz)
 _csa_topk_select = _sig("csa_topk_select", [_vp] + [_i64] * 6 + [_vp, _vp, _vp, _sz, _vp])
 _csa_index_topk_workspace = _sig("csa_index_topk_workspace", [_i64] * 5, _sz)
 _csa_index_topk = _sig("csa_index_topk", [_vp] * 3 + [_i64] * 8 + [_vp, _vp, _vp, _sz, _i32, _vp])
+_csa_index_topk_noalloc = _sig("csa_index_topk_noalloc", [_vp] * 3 + [_i64] * 8 + [_vp, _vp, _i32, _vp])
+_csa_index_topk_noalloc_max_bytes = _sig("csa_index_topk_noalloc_max_bytes", [], _sz)
 _csa_attn_workspace = _sig("csa_attn_workspace", [_i64] * 5, _sz)
 _csa_sparse_attn_workspace = _sig("csa_sparse_attn_workspace", [_i64] * 6 + [_i32], _sz)
 _csa_sparse_attn = _sig("csa_sparse_attn", [_vp] * 3 + [_i64, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _f32]
@@ -236,6 +238,21 @@ def csa_index_topk(q_idx, k_idx, m, k, *, w_idx=None, n_ctx, ws=None, idx=None, 
                          _dt(q_idx), _stream(q_idx.device))
     _check(st, "csa_index_topk")
     return (idx, out_score) if want_scores else idx
+
+
+def csa_index_topk_noalloc_max_bytes() -> int:
+    return int(_csa_index_topk_noalloc_max_bytes())
+
+
+def csa_index_topk_noalloc(q_idx, k_idx, m, k, *, w_idx, n_ctx, idx, out_score=None):
+    """csa_index_topk through the library's static scratch: no workspace, and
+    the caller passes the outputs (nothing is allocated by this call)."""
+    B, T, HI, dI = q_idx.shape
+    L = k_idx.shape[1]
+    st = _csa_index_topk_noalloc(_ptr(q_idx), _ptr(w_idx), _ptr(k_idx), B, T, n_ctx, L, HI, dI, m, k,
+                                 idx.data_ptr(), _ptr(out_score), _dt(q_idx), _stream(q_idx.device))
+    _check(st, "csa_index_topk_noalloc")
+    return idx
 
 
 # ---------------------------------------------------------------------------

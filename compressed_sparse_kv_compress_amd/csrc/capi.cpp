@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "../../include/csa.h"
 #include "kernels.hpp"
@@ -205,16 +206,30 @@ size_t csa_index_topk_workspace(int64_t B, int64_t T, int64_t L, int64_t H_I, in
   return chunked > fused ? chunked : fused;
 }
 
-csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int64_t B,
-                            int64_t T, int64_t n_ctx, int64_t L, int64_t H_I, int64_t d_I, int64_t m,
-                            int64_t k, int32_t* idx, float* out_score, void* ws, size_t ws_bytes,
-                            csa_dtype_t dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by csa_index_topk and csa_index_topk_noalloc.
+csa_status_t index_topk_check(const void* q_idx, const float* w_idx, const void* k_idx, int64_t B, int64_t T,
+                              int64_t n_ctx, int64_t L, int64_t H_I, int64_t d_I, int64_t m, int64_t k,
+                              int32_t* idx, float* out_score, csa_dtype_t dtype) {
   csa_status_t st = index_common(q_idx, w_idx, k_idx, B, T, n_ctx, L, H_I, d_I, m, dtype);
   if (st != CSA_OK) return st;
   REQUIRE(k >= 1 && k <= (1 << 20), "k=%lld outside [1, 2^20]", (long long)k);
   if (B == 0) return CSA_OK;
   REQUIRE_PTR(idx);
   OPT_PTR(out_score);
+  return CSA_OK;
+}
+
+// Index + top-k with a validated call and a workspace of ws_bytes at ws (the
+// caller's, or the static scratch of the allocation-free entry point).
+csa_status_t index_topk_run(const void* q_idx, const float* w_idx, const void* k_idx, int64_t B, int64_t T,
+                            int64_t n_ctx, int64_t L, int64_t H_I, int64_t d_I, int64_t m, int64_t k,
+                            int32_t* idx, float* out_score, void* ws, size_t ws_bytes, csa_dtype_t dtype,
+                            void* stream) {
+  csa_status_t st = CSA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t rows = B * T;
   // Many queries per sequence (prefill): the 16-row scoring kernel reads each
@@ -251,6 +266,71 @@ csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k
     if (st != CSA_OK) return st;
   }
   return CSA_OK;
+}
+
+// Static scratch of the allocation-free index + top-k: one array per device
+// (the code object's globals are per device), zero at load.  Host code uses
+// the per-device address from hipGetSymbolAddress, never the array's name.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of `scratch` on the calling thread's current device, looked up on
+// the first call made on that device.
+csa_status_t scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(CSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(CSA_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(CSA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k_idx, int64_t B,
+                            int64_t T, int64_t n_ctx, int64_t L, int64_t H_I, int64_t d_I, int64_t m,
+                            int64_t k, int32_t* idx, float* out_score, void* ws, size_t ws_bytes,
+                            csa_dtype_t dtype, void* stream) {
+  const csa_status_t st = index_topk_check(q_idx, w_idx, k_idx, B, T, n_ctx, L, H_I, d_I, m, k, idx, out_score,
+                                           dtype);
+  if (st != CSA_OK || B == 0) return st;
+  return index_topk_run(q_idx, w_idx, k_idx, B, T, n_ctx, L, H_I, d_I, m, k, idx, out_score, ws, ws_bytes, dtype,
+                        stream);
+}
+
+size_t csa_index_topk_noalloc_max_bytes(void) { return kScratchBytes; }
+
+csa_status_t csa_index_topk_noalloc(const void* q_idx, const float* w_idx, const void* k_idx, int64_t B,
+                                    int64_t T, int64_t n_ctx, int64_t L, int64_t H_I, int64_t d_I, int64_t m,
+                                    int64_t k, int32_t* idx, float* out_score, csa_dtype_t dtype,
+                                    void* stream) {
+  csa_status_t st = index_topk_check(q_idx, w_idx, k_idx, B, T, n_ctx, L, H_I, d_I, m, k, idx, out_score, dtype);
+  if (st != CSA_OK || B == 0) return st;
+  // The scratch must hold at least one query row (its scores and selection
+  // state); larger calls are processed in groups of rows that fit.
+  const size_t one_row = index_topk_row_bytes(L, k);
+  if (one_row > kScratchBytes)
+    return fail(CSA_ERR_UNSUPPORTED,
+                "one query row of L=%lld, k=%lld needs %zu bytes of scratch; the static scratch holds %zu",
+                (long long)L, (long long)k, one_row, kScratchBytes);
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != CSA_OK) return st;
+  return index_topk_run(q_idx, w_idx, k_idx, B, T, n_ctx, L, H_I, d_I, m, k, idx, out_score, ws, kScratchBytes,
+                        dtype, stream);
 }
 
 size_t csa_sparse_attn_workspace(int64_t B, int64_t T, int64_t H, int64_t d, int64_t k, int64_t W,

@@ -162,6 +162,25 @@ csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k
                             int64_t m, int64_t k, int32_t* idx, float* out_score, void* ws,
                             size_t ws_bytes, csa_dtype_t dtype, void* stream);
 
+/* csa_index_topk_noalloc -- csa_index_topk for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without ws / ws_bytes, the same
+ * kernels and the same results bit for bit.  Its scratch is a static device
+ * array of csa_index_topk_noalloc_max_bytes() bytes (32 MiB) that the library
+ * holds on every GPU it runs on until the process ends; the call allocates
+ * and frees nothing.  The scratch must hold one query row's scores and
+ * selection state (about 4 * L + 8 * 16 * k bytes, so L up to ~7.5M at
+ * k = 1024); larger rows return CSA_ERR_UNSUPPORTED before anything is
+ * enqueued.  Bigger batches are processed in groups of rows that fit.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (different streams or threads) race; calls in order on one stream do
+ * not.  The calling thread's current device must be the device of `stream`. */
+size_t csa_index_topk_noalloc_max_bytes(void);
+csa_status_t csa_index_topk_noalloc(const void* q_idx, const float* w_idx, const void* k_idx,
+                                    int64_t B, int64_t T, int64_t n_ctx, int64_t L, int64_t H_I,
+                                    int64_t d_I, int64_t m, int64_t k, int32_t* idx,
+                                    float* out_score, csa_dtype_t dtype, void* stream);
+
 /* ---------------------------------------------------------------------------
  * csa_sparse_attn -- CSA main attention (shareware.cn article, sections 三.1,
  * 十, 十一, 十二; trdm.cn section 4.3 改进三).  Per query (b, t) and head h the

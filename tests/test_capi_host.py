@@ -211,3 +211,20 @@ def test_mxfp4_storage_is_validated(lib):
     attn = [V] * 3 + [I, V, I, V, V, I, I, V, F] + [I] * 5 + [V, V, V, Z, ctypes.c_int, V]
     assert _call(lib, "csa_sparse_attn", attn, FAKE, FAKE, FAKE, 10, FAKE, 4, None, None, 0, 0,
                  None, 0.1, 1, 1, 40, 64, 512, FAKE, None, None, 0, 3, None) == 2
+
+
+def test_noalloc_rejects_rows_beyond_its_scratch(lib):
+    """The allocation-free index + top-k refuses, before enqueuing anything, a
+    query row whose scores and selection state exceed its static scratch."""
+    lib.csa_index_topk_noalloc_max_bytes.restype = Z
+    assert lib.csa_index_topk_noalloc_max_bytes() == 32 << 20
+    args = [V] * 3 + [I] * 8 + [V, V, ctypes.c_int, V]
+    # L = 10M entries: 40 MB of scores for one row
+    assert _call(lib, "csa_index_topk_noalloc", args, FAKE, None, FAKE, 1, 1, 40_000_000, 10_000_000, 64, 128,
+                 4, 1024, FAKE, None, 1, None) == 2
+    # invalid arguments are still reported as such
+    assert _call(lib, "csa_index_topk_noalloc", args, FAKE, None, FAKE, 1, 1, 100, 25, 64, 128, 4, 0,
+                 FAKE, None, 1, None) == 1
+    # batch 0: nothing to do
+    assert _call(lib, "csa_index_topk_noalloc", args, None, None, None, 0, 1, 100, 25, 64, 128, 4, 8,
+                 None, None, 1, None) == 0
