@@ -39,6 +39,29 @@ _i32 = ctypes.c_int
 _f32 = ctypes.c_float
 
 
+class Layout(ctypes.Structure):
+    """csa_layout_t: per-sequence lengths (device int64 [B]), a block table of
+    paged compressed caches (device int32 [B][bt_stride], `page` entries per
+    page, `num_pages` pages per pool) and ring-mode raw windows.  Build it
+    with layout(); keep the tensors alive while calls use it."""
+    _fields_ = [("seq_len", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("bt_stride", ctypes.c_int64),
+                ("page", ctypes.c_int64), ("num_pages", ctypes.c_int64), ("window_ring", ctypes.c_int32)]
+
+
+def layout(seq_len=None, block_table=None, page=0, num_pages=0, ring=False):
+    """A Layout from torch tensors (seq_len int64 [B], block_table int32 [B][bt_stride])."""
+    for t, dt in ((seq_len, torch.int64), (block_table, torch.int32)):
+        if t is not None and (t.dtype != dt or not t.is_contiguous()):
+            raise TypeError("seq_len must be contiguous int64 and block_table contiguous int32")
+    return Layout(None if seq_len is None else seq_len.data_ptr(),
+                  None if block_table is None else block_table.data_ptr(),
+                  0 if block_table is None else block_table.shape[1], page, num_pages, 1 if ring else 0)
+
+
+def _lay(lay):
+    return None if lay is None else ctypes.byref(lay)
+
+
 def _sig(name, args, res=_i32):
     fn = getattr(_lib, name)
     fn.argtypes = args
@@ -53,6 +76,14 @@ _csa_topk_select_workspace = _sig("csa_topk_select_workspace", [_i64] * 4, _sz)
 _csa_topk_select = _sig("csa_topk_select", [_vp] + [_i64] * 6 + [_vp, _vp, _vp, _sz, _vp])
 _csa_index_topk_workspace = _sig("csa_index_topk_workspace", [_i64] * 5, _sz)
 _csa_index_topk = _sig("csa_index_topk", [_vp] * 3 + [_i64] * 8 + [_vp, _vp, _vp, _sz, _i32, _vp])
+_LP = ctypes.POINTER(Layout)
+_csa_index_topk_ex = _sig("csa_index_topk_ex", [_LP] + [_vp] * 3 + [_i64] * 8 + [_vp, _vp, _vp, _sz, _i32, _vp])
+_csa_sparse_attn_ex = _sig("csa_sparse_attn_ex", [_LP] + [_vp] * 3 + [_i64, _vp, _i64, _vp, _vp, _i64, _i64, _vp,
+                                                                        _f32] + [_i64] * 5 + [_vp, _vp, _vp, _sz, _i32, _vp])
+_hca_dense_attn_ex = _sig("hca_dense_attn_ex", [_LP] + [_vp] * 3 + [_i64, _i64, _vp, _vp, _i64, _i64, _vp, _f32]
+                          + [_i64] * 5 + [_vp, _vp, _vp, _sz, _i32, _vp])
+_csa_compress_append = _sig("csa_compress_append", [_LP] + [_vp] * 9 + [_i64, _vp, _vp] + [_i64] * 4 + [_i32, _vp])
+_csa_window_append = _sig("csa_window_append", [_vp] * 5 + [_i64] * 3 + [_i32, _vp])
 _csa_index_topk_noalloc = _sig("csa_index_topk_noalloc", [_vp] * 3 + [_i64] * 8 + [_vp, _vp, _i32, _vp])
 _csa_index_topk_noalloc_max_bytes = _sig("csa_index_topk_noalloc_max_bytes", [], _sz)
 _csa_attn_workspace = _sig("csa_attn_workspace", [_i64] * 5, _sz)
@@ -184,6 +215,32 @@ def hca_compress(x, z, m=128, *, bias=None, n=None, p0=0, e0=0, e1=None, out=Non
     return out
 
 
+def csa_compress_append(x_a, z_a, m, rings, pos, cache, *, x_b=None, z_b=None, bias=None, layout=None, L=None):
+    """One new raw token per sequence (x_a, z_a [B][D]; x_b, z_b in two-path
+    mode): staged into `rings` (ring_xa, ring_za[, ring_xb, ring_zb], each
+    [B][S][D]) at slot pos % S; the entry pos // m is written to `cache` when
+    the token completes its block.  pos: device int64 [B]."""
+    B, D = x_a.shape
+    S = rings[0].shape[1]
+    rx_b = rings[2] if len(rings) > 2 else None
+    rz_b = rings[3] if len(rings) > 2 else None
+    L = cache.shape[1] if L is None else L
+    st = _csa_compress_append(_lay(layout), _ptr(x_a), _ptr(z_a), _ptr(x_b), _ptr(z_b), _ptr(bias), _ptr(rings[0]),
+                              _ptr(rings[1]), _ptr(rx_b), _ptr(rz_b), S, _ptr(pos), _ptr(cache), L, B, D, m,
+                              _dt(x_a), _stream(x_a.device))
+    _check(st, "csa_compress_append")
+    return cache
+
+
+def csa_window_append(k_new, v_new, kr, vr, pos):
+    """Raw window rows of one new token per sequence into ring slot pos % R."""
+    B, d = k_new.shape
+    R = kr.shape[1]
+    st = _csa_window_append(_ptr(k_new), _ptr(v_new), _ptr(kr), _ptr(vr), _ptr(pos), B, R, d, _dt(k_new),
+                            _stream(k_new.device))
+    _check(st, "csa_window_append")
+
+
 # ---------------------------------------------------------------------------
 # indexer and top-k
 # ---------------------------------------------------------------------------
@@ -223,9 +280,12 @@ def csa_index_topk_workspace(B, T, L, H_I, k) -> int:
 
 
 def csa_index_topk(q_idx, k_idx, m, k, *, w_idx=None, n_ctx, ws=None, idx=None, out_score=None,
-                   want_scores=False):
+                   want_scores=False, layout=None, L=None):
+    """Index + top-k.  layout (a Layout) selects csa_index_topk_ex: then
+    k_idx may be a paged pool and L (the longest sequence's capacity in
+    entries) must be given."""
     B, T, HI, dI = q_idx.shape
-    L = k_idx.shape[1]
+    L = k_idx.shape[1] if L is None else L
     if idx is None:
         idx = torch.empty((B, T, k), dtype=torch.int32, device=q_idx.device)
     if want_scores and out_score is None:
@@ -233,10 +293,12 @@ def csa_index_topk(q_idx, k_idx, m, k, *, w_idx=None, n_ctx, ws=None, idx=None, 
     if ws is None:
         nb = max(16, csa_index_topk_workspace(B, T, L, HI, k))
         ws = torch.empty(nb, dtype=torch.uint8, device=q_idx.device)
-    st = _csa_index_topk(_ptr(q_idx), _ptr(w_idx), _ptr(k_idx), B, T, n_ctx, L, HI, dI, m, k,
-                         idx.data_ptr(), _ptr(out_score), ws.data_ptr(), ws.numel() * ws.element_size(),
-                         _dt(q_idx), _stream(q_idx.device))
-    _check(st, "csa_index_topk")
+    args = (_ptr(q_idx), _ptr(w_idx), _ptr(k_idx), B, T, n_ctx, L, HI, dI, m, k, idx.data_ptr(), _ptr(out_score),
+            ws.data_ptr(), ws.numel() * ws.element_size(), _dt(q_idx), _stream(q_idx.device))
+    if layout is None:
+        _check(_csa_index_topk(*args), "csa_index_topk")
+    else:
+        _check(_csa_index_topk_ex(_lay(layout), *args), "csa_index_topk_ex")
     return (idx, out_score) if want_scores else idx
 
 
@@ -289,33 +351,46 @@ def _ws(nbytes, dev, ws):
 
 
 def csa_sparse_attn(q, kc, vc, idx, *, kr=None, vr=None, W=0, sink=None, scale=None, n_ctx,
-                    out=None, lse=None, want_lse=False, ws=None):
+                    out=None, lse=None, want_lse=False, ws=None, layout=None, L=None):
+    """CSA attention.  layout selects csa_sparse_attn_ex (paged kc / vc pools
+    need L, the capacity in entries)."""
     B, T, H, d = q.shape
-    L = kc.shape[1]
+    L = kc.shape[1] if L is None else L
     k = idx.shape[-1]
     R = 0 if kr is None else kr.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     out, lse = _attn_out(q, out, lse, want_lse)
     dt = _attn_dt(q, kc)
-    wp, wn = _ws(csa_sparse_attn_workspace(B, T, H, d, k, W, dt), q.device, ws)
-    st = _csa_sparse_attn(_ptr(q), _ptr(kc), _ptr(vc), L, _ptr(idx), k, _ptr(kr), _ptr(vr), R, W,
-                          _ptr(sink), scale, B, T, n_ctx, H, d, out.data_ptr(), _ptr(lse), wp, wn,
-                          dt, _stream(q.device))
-    _check(st, "csa_sparse_attn")
+    need = csa_sparse_attn_workspace(B, T, H, d, k, W, dt) if layout is None else csa_attn_workspace(B, T, H, d,
+                                                                                                     k + W)
+    wp, wn = _ws(need, q.device, ws)
+    args = (_ptr(q), _ptr(kc), _ptr(vc), L, _ptr(idx), k, _ptr(kr), _ptr(vr), R, W, _ptr(sink), scale, B, T,
+            n_ctx, H, d, out.data_ptr(), _ptr(lse), wp, wn, dt, _stream(q.device))
+    if layout is None:
+        _check(_csa_sparse_attn(*args), "csa_sparse_attn")
+    else:
+        _check(_csa_sparse_attn_ex(_lay(layout), *args), "csa_sparse_attn_ex")
     return (out, lse) if want_lse else out
 
 
 def hca_dense_attn(q, kc, vc, m, *, kr=None, vr=None, W=0, sink=None, scale=None, n_ctx, out=None,
-                   lse=None, want_lse=False, ws=None):
+                   lse=None, want_lse=False, ws=None, layout=None, L=None):
+    """HCA attention.  layout selects hca_dense_attn_ex (paged pools need L)."""
     B, T, H, d = q.shape
-    L = kc.shape[1]
+    L = kc.shape[1] if L is None else L
     R = 0 if kr is None else kr.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     out, lse = _attn_out(q, out, lse, want_lse)
     dt = _attn_dt(q, kc)
-    wp, wn = _ws(hca_dense_attn_workspace(B, T, H, d, L, m, n_ctx, W, dt), q.device, ws)
-    st = _hca_dense_attn(_ptr(q), _ptr(kc), _ptr(vc), L, m, _ptr(kr), _ptr(vr), R, W, _ptr(sink),
-                         scale, B, T, n_ctx, H, d, out.data_ptr(), _ptr(lse), wp, wn, dt,
-                         _stream(q.device))
-    _check(st, "hca_dense_attn")
+    if layout is None:
+        need = hca_dense_attn_workspace(B, T, H, d, L, m, n_ctx, W, dt)
+    else:
+        need = csa_attn_workspace(B, T, H, d, min(L, (n_ctx - 1) // m) + W)
+    wp, wn = _ws(need, q.device, ws)
+    args = (_ptr(q), _ptr(kc), _ptr(vc), L, m, _ptr(kr), _ptr(vr), R, W, _ptr(sink), scale, B, T, n_ctx, H, d,
+            out.data_ptr(), _ptr(lse), wp, wn, dt, _stream(q.device))
+    if layout is None:
+        _check(_hca_dense_attn(*args), "hca_dense_attn")
+    else:
+        _check(_hca_dense_attn_ex(_lay(layout), *args), "hca_dense_attn_ex")
     return (out, lse) if want_lse else out

@@ -47,9 +47,11 @@ struct RowMap {
   int64_t win_lo;  // first raw position of the window
 };
 
+// Rows of query t: a sparse call lists k compressed slots; a dense call (or
+// a gathered dense call over a paged cache, idx == null) every visible entry.
 __device__ __forceinline__ RowMap row_map(const AttnArgs& a, bool sparse, int64_t t) {
   RowMap r;
-  if (sparse) {
+  if (sparse && a.idx != nullptr) {
     r.n_cmp = a.k;
   } else {
     int64_t nv = t / a.m;
@@ -67,24 +69,29 @@ __device__ __forceinline__ RowMap row_map(const AttnArgs& a, bool sparse, int64_
   return r;
 }
 
+// Slot of raw position u in sequence b's window buffer of R rows: u % R for
+// a ring, else u - (n_b - R) (the buffer holds positions n_b - R .. n_b - 1).
+__device__ __forceinline__ int64_t window_slot(const AttnArgs& a, int64_t n_b, int64_t u) {
+  return a.lay.ring ? u % a.R : u - (n_b - a.R);
+}
+
 // Element offset of virtual row v of query (b, bt) in its source, or -1 if the
 // row is empty.  *from_raw tells which source (compressed cache or window).
-__device__ __forceinline__ int64_t row_offset(const AttnArgs& a, bool sparse, const RowMap& rm,
+__device__ __forceinline__ int64_t row_offset(const AttnArgs& a, bool sparse, const RowMap& rm, int64_t n_b,
                                               int64_t b, int64_t bt, int64_t v, bool* from_raw) {
   if (v < rm.n_cmp) {
     *from_raw = false;
     int64_t s = v;
-    if (sparse) {
+    if (sparse && a.idx != nullptr) {
       s = a.idx[bt * a.k + v];
       if (s < 0 || s >= a.L) return -1;
     }
-    return (b * a.L + s) * a.d;
+    return cache_row(a.lay, a.L, b, s) * a.d;
   }
   const int64_t w = v - rm.n_cmp;
   if (w >= rm.n_win) return -1;
   *from_raw = true;
-  const int64_t u = rm.win_lo + w - (a.n_ctx - a.R);
-  return (b * a.R + u) * a.d;
+  return (b * a.R + window_slot(a, n_b, rm.win_lo + w)) * a.d;
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -207,10 +214,14 @@ __device__ __forceinline__ void dma_row(const char* g, const uint8_t* lds) {
 // indices come from the split's index cache with one vector LDS read.  An
 // empty row (past the split's end, or a -1 / out-of-range index) is read from
 // the dummy row and flagged in okrow (K waves only), so its logit is masked.
+// Compressed rows: SPARSE gathers through the split's cached list of cache
+// rows (-1 = empty slot), else rows are consecutive from cbase.  Window row v
+// is raw slot v + win0, wrapped once by wrap (the ring size, or a bound no
+// slot reaches).
 template <int D, bool F8, bool SPARSE, bool NT>
 __device__ __forceinline__ void issue_rows(const char* cbase, const char* rbase, const char* dummy, const int* sidx,
                                            uint8_t* lds, int pitch, int c0, int n_cmp, int r_begin, int r_end,
-                                           int win0, int L, int lane, int* okrow) {
+                                           int win0, int wrap, int lane, int* okrow) {
   using C = Ring<D, F8>;
   int sv = 0;
   if (SPARSE) {
@@ -223,8 +234,10 @@ __device__ __forceinline__ void issue_rows(const char* cbase, const char* rbase,
     const bool cmp = v < n_cmp;
     int s = v;
     if (SPARSE) s = cmp ? __builtin_amdgcn_readlane(sv, j) : 0;
-    const bool ok = v < r_end && (!SPARSE || !cmp || (s >= 0 && s < L));
-    const char* row = cmp ? cbase + static_cast<int64_t>(s) * C::RB : rbase + static_cast<int64_t>(v + win0) * C::RB;
+    const bool ok = v < r_end && (!SPARSE || !cmp || s >= 0);
+    int wr = v + win0;
+    wr = wr >= wrap ? wr - wrap : wr;
+    const char* row = cmp ? cbase + static_cast<int64_t>(s) * C::RB : rbase + static_cast<int64_t>(wr) * C::RB;
     const char* src = ok ? row : dummy;
 #pragma unroll
     for (int p = 0; p < C::IPR; ++p)
@@ -233,7 +246,7 @@ __device__ __forceinline__ void issue_rows(const char* cbase, const char* rbase,
   if (okrow && lane < C::RPW) {
     const int v = c0 + lane;
     const bool cmp = v < n_cmp;
-    okrow[lane] = v < r_end && (!SPARSE || !cmp || (sv >= 0 && sv < L));
+    okrow[lane] = v < r_end && (!SPARSE || !cmp || sv >= 0);
   }
 }
 
@@ -294,7 +307,8 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
   const int64_t hg = id % hgroups;
   const int64_t bt = id / hgroups;
   const int64_t b = bt / a.T;
-  const int64_t t = a.n_ctx - a.T + bt % a.T;
+  const int64_t n_b = seq_len(a.lay, a.n_ctx, a.T, b);
+  const int64_t t = n_b - a.T + bt % a.T;
   const RowMap rm = row_map(a, SPARSE, t);
   const int64_t n_rows = rm.n_cmp + rm.n_win;
   const int64_t per = (n_rows + nsplit - 1) / nsplit;  // rows per split (the last stage may be partial)
@@ -304,7 +318,8 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
   // Waves 0-3 stage K rows 8w .. 8w+7 of each stage; waves 4-7 the V rows.
   const int mat = wave / (kWaves / 2);
   const int row0 = (wave % (kWaves / 2)) * C::RPW;
-  const char* cbase = static_cast<const char*>(mat ? a.vc : a.kc) + b * a.L * C::RB;
+  // gathered rows are absolute cache rows; consecutive ones start at sequence b's
+  const char* cbase = static_cast<const char*>(mat ? a.vc : a.kc) + (SPARSE ? 0 : b * a.L * C::RB);
   const char* rbase = static_cast<const char*>(mat ? a.vr : a.kr) + b * a.R * C::RB;
   const char* dummy = reinterpret_cast<const char*>(kZeroRow);
   static_assert(C::RB <= static_cast<int>(sizeof(kZeroRow)), "zero row covers a row");
@@ -312,8 +327,9 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
   const int moff = (mat ? C::KBYTES : 0) + row0 * pitch;
   const int n_cmp = static_cast<int>(rm.n_cmp);
   const int rb0 = static_cast<int>(r_begin), re0 = static_cast<int>(r_end);
-  const int win0 = static_cast<int>(rm.win_lo - (a.n_ctx - a.R) - rm.n_cmp);  // raw row of virtual row v is v + win0
-  const int Lc = static_cast<int>(a.L);
+  // raw slot of virtual row v is v + win0 (wrapped once for a ring)
+  const int win0 = static_cast<int>(window_slot(a, n_b, rm.win_lo) - rm.n_cmp);
+  const int wrap = a.lay.ring ? static_cast<int>(a.R) : INT32_MAX;
   const int nst = static_cast<int>((r_end - r_begin + C::ROWS - 1) / C::ROWS);
 
   // Pipeline over NS stage buffers: K of stage c+NS is issued as soon as
@@ -323,7 +339,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
   // K(c+NS) sets them while stage c still reads its own.
   auto issue = [&](int st) {
     issue_rows<D, F8, SPARSE, NT>(cbase, rbase, dummy, sidx, ring + (st % C::NS) * C::STAGE + moff, pitch,
-                          rb0 + st * C::ROWS + row0, n_cmp, rb0, re0, win0, Lc, lane,
+                          rb0 + st * C::ROWS + row0, n_cmp, rb0, re0, win0, wrap, lane,
                           mat ? nullptr : okf[st % (C::NS + 1)] + row0);
   };
   auto prime = [&]() {
@@ -336,9 +352,12 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
   // (cached in LDS once, so that the staging loop issues no loads into
   // registers, whose waits would also drain the ring).
   if (!SPARSE) prime();
-  if (SPARSE) {
+  if (SPARSE) {  // cache rows of the split's compressed slots (an implicit 0 .. nv-1 list when idx is null)
     const int64_t ce = r_end < rm.n_cmp ? r_end : rm.n_cmp;
-    for (int64_t v = r_begin + threadIdx.x; v < ce; v += 64 * kWaves) sidx[v - r_begin] = a.idx[bt * a.k + v];
+    for (int64_t v = r_begin + threadIdx.x; v < ce; v += 64 * kWaves) {
+      const int64_t s = a.idx ? a.idx[bt * a.k + v] : v;
+      sidx[v - r_begin] = (s >= 0 && s < a.L) ? static_cast<int>(cache_row(a.lay, a.L, b, s)) : -1;
+    }
   }
   const int h0 = static_cast<int>(hg * kHeadsPerWg + hq * kHeadsPerWave);
   // Q fragments (B operand of K Q^T): head h0 + c16, dims dh*DH + ks*32 + 8g .. +8.
@@ -583,7 +602,8 @@ __global__ __launch_bounds__(64) void attn_f32(AttnArgs a, int sparse_i) {
   const int64_t bt = bh / a.H;
   const int64_t h = bh % a.H;
   const int64_t b = bt / a.T;
-  const int64_t t = a.n_ctx - a.T + bt % a.T;
+  const int64_t n_b = seq_len(a.lay, a.n_ctx, a.T, b);
+  const int64_t t = n_b - a.T + bt % a.T;
   const int64_t D = a.d;
   const float* q = static_cast<const float*>(a.q) + bh * D;
   for (int64_t c = lane; c < D; c += 64) qs[c] = q[c];
@@ -602,7 +622,7 @@ __global__ __launch_bounds__(64) void attn_f32(AttnArgs a, int sparse_i) {
   for (int64_t c0 = 0; c0 < n_rows; c0 += 64) {
     const int64_t v = c0 + lane;
     bool raw = false;
-    const int64_t off = v < n_rows ? row_offset(a, sparse, rm, b, bt, v, &raw) : -1;
+    const int64_t off = v < n_rows ? row_offset(a, sparse, rm, n_b, b, bt, v, &raw) : -1;
     float lg = -INFINITY;
     if (off >= 0) {
       const float* kp = (raw ? krp : kcp) + off;
@@ -652,7 +672,8 @@ __global__ __launch_bounds__(64) void attn_f32(AttnArgs a, int sparse_i) {
 
 int attn_splits(int64_t B, int64_t T, int64_t H, int64_t d, int64_t max_rows, Dt dt, bool sparse) {
   (void)d;
-  if (dt == kF32) return 1;
+  // fp32 (and head counts the MFMA kernel does not take) run one workgroup per query
+  if (dt == kF32 || H < kHeadsPerWg || B * T <= 0) return 1;
   const int64_t base = B * T * (H / kHeadsPerWg);
   const int64_t target = 256;  // workgroups wanted per launch (one per CU)
   int64_t ns = (target + base - 1) / base;

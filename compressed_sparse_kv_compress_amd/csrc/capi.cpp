@@ -142,6 +142,36 @@ int64_t dense_max_rows(int64_t L, int64_t m, int64_t n_ctx, int64_t W) {
   return nv + W;
 }
 
+// Checks a serving layout against a call (L: cache capacity in entries; W, R:
+// window) and converts it; NULL is the plain layout.
+csa_status_t layout_from(const csa_layout_t* l, int64_t T, int64_t L, int64_t W, int64_t R, csa::SeqLayout* out) {
+  *out = csa::SeqLayout{};
+  if (l == nullptr) return CSA_OK;
+  if (l->seq_len != nullptr) {
+    REQUIRE((reinterpret_cast<uintptr_t>(l->seq_len) & 7u) == 0, "layout seq_len is not 8-byte aligned");
+    out->lens = l->seq_len;
+  }
+  if (l->block_table != nullptr) {
+    REQUIRE((reinterpret_cast<uintptr_t>(l->block_table) & 3u) == 0, "layout block_table is not 4-byte aligned");
+    REQUIRE(l->page >= 16 && l->page % 16 == 0 && l->page <= (int64_t(1) << 30),
+            "layout page=%lld must be a positive multiple of 16", (long long)l->page);
+    REQUIRE(l->num_pages >= 1 && l->num_pages <= ((int64_t(1) << 31) - 1) / l->page,
+            "layout num_pages=%lld: the pool must hold fewer than 2^31 rows", (long long)l->num_pages);
+    REQUIRE(l->bt_stride >= (L + l->page - 1) / l->page, "layout bt_stride=%lld below ceil(L / page)",
+            (long long)l->bt_stride);
+    out->bt = l->block_table;
+    out->bt_ld = l->bt_stride;
+    out->page = l->page;
+    out->npages = l->num_pages;
+  }
+  REQUIRE(l->window_ring == 0 || l->window_ring == 1, "layout window_ring must be 0 or 1");
+  if (l->window_ring) {
+    if (W > 0) REQUIRE(R >= T + W - 1 && R >= W, "a ring window needs R >= T+W-1 and R >= W (R=%lld)", (long long)R);
+    out->ring = 1;
+  }
+  return CSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -225,22 +255,22 @@ csa_status_t index_topk_check(const void* q_idx, const float* w_idx, const void*
 
 // Index + top-k with a validated call and a workspace of ws_bytes at ws (the
 // caller's, or the static scratch of the allocation-free entry point).
-csa_status_t index_topk_run(const void* q_idx, const float* w_idx, const void* k_idx, int64_t B, int64_t T,
-                            int64_t n_ctx, int64_t L, int64_t H_I, int64_t d_I, int64_t m, int64_t k,
-                            int32_t* idx, float* out_score, void* ws, size_t ws_bytes, csa_dtype_t dtype,
+csa_status_t index_topk_run(const csa::SeqLayout& lay, const void* q_idx, const float* w_idx, const void* k_idx,
+                            int64_t B, int64_t T, int64_t n_ctx, int64_t L, int64_t H_I, int64_t d_I, int64_t m,
+                            int64_t k, int32_t* idx, float* out_score, void* ws, size_t ws_bytes, csa_dtype_t dtype,
                             void* stream) {
   csa_status_t st = CSA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t rows = B * T;
   // Many queries per sequence (prefill): the 16-row scoring kernel reads each
   // key once per 16 queries; it writes scores, so the stand-alone top-k follows.
-  const bool multi = dtype == CSA_BF16 && d_I == 128 && csa::index_multi_rows(T, H_I, 0, rows);
+  const bool multi = dtype == CSA_BF16 && d_I == 128 && !lay.bt && csa::index_multi_rows(T, H_I, 0, rows);
   if (!multi && ws != nullptr && L > 0 && csa::index_topk_fusable(rows, L, H_I, d_I, k, to_dt(dtype)) &&
       ws_bytes >= csa::index_topk_fused_ws_bytes(rows, L, k)) {
     // The scan's workgroups keep their parts' candidates; no score matrix.
     if (!aligned16(ws)) return fail(CSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
-    csa::IndexScoreArgs a{q_idx, w_idx, k_idx, nullptr, L, 0, rows, B, T, n_ctx, L, H_I, d_I, m, to_dt(dtype)};
-    csa::TopkArgs t{nullptr, L, 0, rows, T, n_ctx, L, m, k, idx, out_score};
+    csa::IndexScoreArgs a{q_idx, w_idx, k_idx, nullptr, L, 0, rows, B, T, n_ctx, L, H_I, d_I, m, to_dt(dtype), lay};
+    csa::TopkArgs t{nullptr, L, 0, rows, T, n_ctx, L, m, k, idx, out_score, lay.lens};
     return hip_status(csa::launch_index_topk_fused(a, t, ws, s), "fused index/top-k launch");
   }
   const size_t per_row = index_topk_row_bytes(L, k);
@@ -256,12 +286,12 @@ csa_status_t index_topk_run(const void* q_idx, const float* w_idx, const void* k
   for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
     const int64_t nr = r0 + chunk < rows ? chunk : rows - r0;
     if (L > 0) {
-      csa::IndexScoreArgs a{q_idx, w_idx, k_idx, sc, L, r0, nr, B, T, n_ctx, L, H_I, d_I, m, to_dt(dtype)};
+      csa::IndexScoreArgs a{q_idx, w_idx, k_idx, sc, L, r0, nr, B, T, n_ctx, L, H_I, d_I, m, to_dt(dtype), lay};
       st = hip_status(csa::launch_index_score(a, s), "index score launch");
       if (st != CSA_OK) return st;
     }
     csa::TopkArgs t{sc, L, r0, nr, T, n_ctx, L, m, k, idx + r0 * k,
-                    out_score ? out_score + r0 * k : nullptr};
+                    out_score ? out_score + r0 * k : nullptr, lay.lens};
     st = hip_status(csa::launch_topk(t, sel_ws, s), "top-k launch");
     if (st != CSA_OK) return st;
   }
@@ -307,8 +337,21 @@ csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k
   const csa_status_t st = index_topk_check(q_idx, w_idx, k_idx, B, T, n_ctx, L, H_I, d_I, m, k, idx, out_score,
                                            dtype);
   if (st != CSA_OK || B == 0) return st;
-  return index_topk_run(q_idx, w_idx, k_idx, B, T, n_ctx, L, H_I, d_I, m, k, idx, out_score, ws, ws_bytes, dtype,
-                        stream);
+  return index_topk_run(csa::SeqLayout{}, q_idx, w_idx, k_idx, B, T, n_ctx, L, H_I, d_I, m, k, idx, out_score, ws,
+                        ws_bytes, dtype, stream);
+}
+
+csa_status_t csa_index_topk_ex(const csa_layout_t* layout, const void* q_idx, const float* w_idx,
+                               const void* k_idx, int64_t B, int64_t T, int64_t n_ctx, int64_t L, int64_t H_I,
+                               int64_t d_I, int64_t m, int64_t k, int32_t* idx, float* out_score, void* ws,
+                               size_t ws_bytes, csa_dtype_t dtype, void* stream) {
+  csa_status_t st = index_topk_check(q_idx, w_idx, k_idx, B, T, n_ctx, L, H_I, d_I, m, k, idx, out_score, dtype);
+  if (st != CSA_OK) return st;
+  csa::SeqLayout lay;
+  st = layout_from(layout, T, L, 0, 0, &lay);
+  if (st != CSA_OK || B == 0) return st;
+  return index_topk_run(lay, q_idx, w_idx, k_idx, B, T, n_ctx, L, H_I, d_I, m, k, idx, out_score, ws, ws_bytes,
+                        dtype, stream);
 }
 
 size_t csa_index_topk_noalloc_max_bytes(void) { return kScratchBytes; }
@@ -329,8 +372,8 @@ csa_status_t csa_index_topk_noalloc(const void* q_idx, const float* w_idx, const
   void* ws = nullptr;
   st = scratch_for_current_device(&ws);
   if (st != CSA_OK) return st;
-  return index_topk_run(q_idx, w_idx, k_idx, B, T, n_ctx, L, H_I, d_I, m, k, idx, out_score, ws, kScratchBytes,
-                        dtype, stream);
+  return index_topk_run(csa::SeqLayout{}, q_idx, w_idx, k_idx, B, T, n_ctx, L, H_I, d_I, m, k, idx, out_score, ws,
+                        kScratchBytes, dtype, stream);
 }
 
 size_t csa_sparse_attn_workspace(int64_t B, int64_t T, int64_t H, int64_t d, int64_t k, int64_t W,
@@ -359,6 +402,9 @@ size_t csa_attn_workspace(int64_t B, int64_t T, int64_t H, int64_t d, int64_t n_
 
 static csa_status_t attn_launch(const csa::AttnArgs& a, bool sparse, int64_t max_rows, csa_dtype_t dt,
                                 void* ws, size_t ws_bytes, void* stream) {
+  // MFMA kernels cache gathered rows as 32-bit cache-row numbers
+  if (dt != CSA_F32 && sparse && !a.lay.bt && a.B * a.L >= (int64_t(1) << 31))
+    return fail(CSA_ERR_UNSUPPORTED, "B * L = %lld cache rows exceed 2^31", (long long)(a.B * a.L));
   const int ns = csa::attn_splits(a.B, a.T, a.H, a.d, max_rows, to_dt(dt), sparse);
   const size_t need = csa::attn_ws_bytes(a.B, a.T, a.H, a.d, ns);
   if (need > 0) {
@@ -373,12 +419,15 @@ static csa_status_t attn_launch(const csa::AttnArgs& a, bool sparse, int64_t max
                     "attention launch");
 }
 
-csa_status_t csa_sparse_attn(const void* q, const void* kc, const void* vc, int64_t L,
-                             const int32_t* idx, int64_t k, const void* kr, const void* vr, int64_t R,
-                             int64_t W, const float* sink, float scale, int64_t B, int64_t T,
-                             int64_t n_ctx, int64_t H, int64_t d, void* out, float* lse, void* ws,
-                             size_t ws_bytes, csa_dtype_t dtype, void* stream) {
+csa_status_t csa_sparse_attn_ex(const csa_layout_t* layout, const void* q, const void* kc, const void* vc, int64_t L,
+                                const int32_t* idx, int64_t k, const void* kr, const void* vr, int64_t R,
+                                int64_t W, const float* sink, float scale, int64_t B, int64_t T,
+                                int64_t n_ctx, int64_t H, int64_t d, void* out, float* lse, void* ws,
+                                size_t ws_bytes, csa_dtype_t dtype, void* stream) {
   csa_status_t st = attn_common(q, kc, vc, L, kr, vr, R, W, sink, scale, B, T, n_ctx, H, d, out, lse, dtype);
+  if (st != CSA_OK) return st;
+  csa::SeqLayout lay;
+  st = layout_from(layout, T, L, W, R, &lay);
   if (st != CSA_OK) return st;
   REQUIRE(k >= 0, "k < 0");
   if (dtype != CSA_F32 && k + W > int64_t(csa::kAttnMaxSplits) * csa::kAttnMaxIdx)
@@ -387,8 +436,40 @@ csa_status_t csa_sparse_attn(const void* q, const void* kc, const void* vc, int6
   if (B == 0) return CSA_OK;
   if (k > 0) REQUIRE_PTR(idx);
   csa::AttnArgs a{q, kc, vc, L, 1, idx, k, kr, vr, R, W, sink, scale, B, T, n_ctx, H, d, out, lse,
-                  nullptr, 0};
+                  nullptr, 0, lay};
   return attn_launch(a, true, k + W, dtype, ws, ws_bytes, stream);
+}
+
+csa_status_t csa_sparse_attn(const void* q, const void* kc, const void* vc, int64_t L,
+                             const int32_t* idx, int64_t k, const void* kr, const void* vr, int64_t R,
+                             int64_t W, const float* sink, float scale, int64_t B, int64_t T,
+                             int64_t n_ctx, int64_t H, int64_t d, void* out, float* lse, void* ws,
+                             size_t ws_bytes, csa_dtype_t dtype, void* stream) {
+  return csa_sparse_attn_ex(nullptr, q, kc, vc, L, idx, k, kr, vr, R, W, sink, scale, B, T, n_ctx, H, d, out, lse,
+                            ws, ws_bytes, dtype, stream);
+}
+
+csa_status_t hca_dense_attn_ex(const csa_layout_t* layout, const void* q, const void* kc, const void* vc, int64_t L,
+                               int64_t m, const void* kr, const void* vr, int64_t R, int64_t W, const float* sink,
+                               float scale, int64_t B, int64_t T, int64_t n_ctx, int64_t H, int64_t d,
+                               void* out, float* lse, void* ws, size_t ws_bytes, csa_dtype_t dtype,
+                               void* stream) {
+  csa_status_t st = attn_common(q, kc, vc, L, kr, vr, R, W, sink, scale, B, T, n_ctx, H, d, out, lse, dtype);
+  if (st != CSA_OK) return st;
+  REQUIRE(m >= 1, "m < 1");
+  csa::SeqLayout lay;
+  st = layout_from(layout, T, L, W, R, &lay);
+  if (st != CSA_OK) return st;
+  const int64_t rows = dense_max_rows(L, m, n_ctx, W);
+  if (dtype != CSA_F32 && lay.bt && rows > int64_t(csa::kAttnMaxSplits) * csa::kAttnMaxIdx)
+    return fail(CSA_ERR_UNSUPPORTED, "paged dense attention supports at most %lld rows per query (got %lld)",
+                (long long)csa::kAttnMaxSplits * csa::kAttnMaxIdx, (long long)rows);
+  if (B == 0) return CSA_OK;
+  csa::AttnArgs a{q, kc, vc, L, m, nullptr, 0, kr, vr, R, W, sink, scale, B, T, n_ctx, H, d, out, lse,
+                  nullptr, 0, lay};
+  // A paged cache is read through the gathering kernel, over the implicit
+  // list of every visible entry.
+  return attn_launch(a, lay.bt != nullptr, rows, dtype, ws, ws_bytes, stream);
 }
 
 csa_status_t hca_dense_attn(const void* q, const void* kc, const void* vc, int64_t L, int64_t m,
@@ -396,13 +477,66 @@ csa_status_t hca_dense_attn(const void* q, const void* kc, const void* vc, int64
                             float scale, int64_t B, int64_t T, int64_t n_ctx, int64_t H, int64_t d,
                             void* out, float* lse, void* ws, size_t ws_bytes, csa_dtype_t dtype,
                             void* stream) {
-  csa_status_t st = attn_common(q, kc, vc, L, kr, vr, R, W, sink, scale, B, T, n_ctx, H, d, out, lse, dtype);
+  return hca_dense_attn_ex(nullptr, q, kc, vc, L, m, kr, vr, R, W, sink, scale, B, T, n_ctx, H, d, out, lse, ws,
+                           ws_bytes, dtype, stream);
+}
+
+csa_status_t csa_compress_append(const csa_layout_t* layout, const void* x_a, const void* z_a, const void* x_b,
+                                 const void* z_b, const float* bias, void* ring_xa, void* ring_za, void* ring_xb,
+                                 void* ring_zb, int64_t S, const int64_t* pos, void* cache, int64_t L, int64_t B,
+                                 int64_t D, int64_t m, csa_dtype_t dtype, void* stream) {
+  REQUIRE(dtype_ok(dtype), "unknown dtype %d", static_cast<int>(dtype));
+  if (dtype == CSA_MXFP4) return fail(CSA_ERR_UNSUPPORTED, "compression has no MXFP4 kernels");
+  REQUIRE(B >= 0 && m >= 1 && L >= 0 && D >= 8 && D % 8 == 0,
+          "need B >= 0, m >= 1, L >= 0, D a positive multiple of 8");
+  REQUIRE((x_b == nullptr) == (z_b == nullptr), "x_b and z_b must both be given or both be NULL");
+  const bool two = x_b != nullptr;
+  REQUIRE(S >= (two ? 2 * m : m), "staging rings of %lld rows: need at least %lld", (long long)S,
+          (long long)(two ? 2 * m : m));
+  csa::SeqLayout lay;
+  csa_status_t st = layout_from(layout, 1, L, 0, 0, &lay);
   if (st != CSA_OK) return st;
-  REQUIRE(m >= 1, "m < 1");
   if (B == 0) return CSA_OK;
-  csa::AttnArgs a{q, kc, vc, L, m, nullptr, 0, kr, vr, R, W, sink, scale, B, T, n_ctx, H, d, out, lse,
-                  nullptr, 0};
-  return attn_launch(a, false, dense_max_rows(L, m, n_ctx, W), dtype, ws, ws_bytes, stream);
+  REQUIRE_PTR(x_a);
+  REQUIRE_PTR(z_a);
+  REQUIRE_PTR(ring_xa);
+  REQUIRE_PTR(ring_za);
+  if (two) {
+    REQUIRE_PTR(x_b);
+    REQUIRE_PTR(z_b);
+    REQUIRE_PTR(ring_xb);
+    REQUIRE_PTR(ring_zb);
+  }
+  REQUIRE_PTR(pos);
+  if (L > 0) REQUIRE_PTR(cache);
+  if (bias != nullptr && (reinterpret_cast<uintptr_t>(bias) & 3u))
+    return fail(CSA_ERR_INVALID_ARG, "bias is not 4-byte aligned");
+  csa::CompressArgs a{x_a, z_a, x_b, z_b, bias, cache, B, int64_t(1) << 62, D, m, 0, S, 0, 0, L};
+  a.pos = pos;
+  a.ring_xa = ring_xa;
+  a.ring_za = ring_za;
+  a.ring_xb = ring_xb;
+  a.ring_zb = ring_zb;
+  a.lay = lay;
+  return hip_status(csa::launch_compress_append(a, to_dt(dtype), static_cast<hipStream_t>(stream)),
+                    "compress append launch");
+}
+
+csa_status_t csa_window_append(const void* k_new, const void* v_new, void* kr, void* vr, const int64_t* pos,
+                               int64_t B, int64_t R, int64_t d, csa_dtype_t dtype, void* stream) {
+  REQUIRE(dtype == CSA_F32 || dtype == CSA_BF16 || dtype == CSA_FP8, "window rows are fp32, bf16 or FP8");
+  REQUIRE(B >= 0 && R >= 1 && d >= 1, "need B >= 0, R >= 1, d >= 1");
+  const int64_t eb = dtype == CSA_F32 ? 4 : (dtype == CSA_BF16 ? 2 : 1);
+  REQUIRE((d * eb) % 16 == 0, "a row of d=%lld elements must be a multiple of 16 bytes", (long long)d);
+  if (B == 0) return CSA_OK;
+  REQUIRE_PTR(k_new);
+  REQUIRE_PTR(v_new);
+  REQUIRE_PTR(kr);
+  REQUIRE_PTR(vr);
+  REQUIRE_PTR(pos);
+  return hip_status(csa::launch_window_append(k_new, v_new, kr, vr, pos, B, R, d * eb,
+                                              static_cast<hipStream_t>(stream)),
+                    "window append launch");
 }
 
 const char* csa_status_string(csa_status_t status) {

@@ -96,11 +96,25 @@ struct Cands {
   int64_t nb, na, b_lo, a_lo, a_bias0;
 };
 
+// Where the raw rows of a bulk call live: row u of sequence b at
+// (b * n_raw + u - p0) of the streams.
+struct BulkRows {
+  const CompressArgs& a;
+  int64_t row_base;
+  __device__ void operator()(bool from_b, int64_t u, const void** x, const void** z, int64_t* off) const {
+    *x = from_b ? a.x_b : a.x_a;
+    *z = from_b ? a.z_b : a.z_a;
+    *off = row_base + (u - a.p0);
+  }
+};
+
 // Fold candidates [lo, hi) of the virtual list into the running (max,
-// denominator, numerator) of VEC channels.  Logits are in log2 units.
-template <Dt DT>
+// denominator, numerator) of VEC channels.  Logits are in log2 units.  rows
+// maps (stream, position) to the row holding it; the arithmetic does not
+// depend on where the rows are.
+template <Dt DT, typename Rows>
 __device__ __forceinline__ void fold_range(const CompressArgs& a, const Cands& cd, int64_t lo, int64_t hi,
-                                           int64_t row_base, int64_t c0, float* mx, float* den, float* acc) {
+                                           const Rows& rows, int64_t c0, float* mx, float* den, float* acc) {
   constexpr int VEC = Io<DT>::VEC;
   for (int64_t i0 = lo; i0 < hi; i0 += kChunk) {
     // All 2 x kChunk loads are issued unconditionally (candidates past the
@@ -112,9 +126,12 @@ __device__ __forceinline__ void fold_range(const CompressArgs& a, const Cands& c
       const int64_t ci = i0 + i < hi ? i0 + i : hi - 1;
       const bool from_b = ci < cd.nb;
       const int64_t u = from_b ? cd.b_lo + ci : cd.a_lo + (ci - cd.nb);
-      const int64_t off = (row_base + (u - a.p0)) * a.D + c0;
-      Io<DT>::load(from_b ? a.x_b : a.x_a, off, xv[i]);
-      Io<DT>::load(from_b ? a.z_b : a.z_a, off, lv[i]);
+      const void* xs;
+      const void* zs;
+      int64_t r;
+      rows(from_b, u, &xs, &zs, &r);
+      Io<DT>::load(xs, r * a.D + c0, xv[i]);
+      Io<DT>::load(zs, r * a.D + c0, lv[i]);
     }
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
@@ -154,33 +171,17 @@ __device__ __forceinline__ void fold_range(const CompressArgs& a, const Cands& c
   }
 }
 
-// S = 1: one thread per (entry, 16-byte channel group), for bulk launches.
-// S > 1: the candidate tokens of each segment are split over S thread slices,
-// S consecutive lanes of one wavefront, whose partial (max, denominator,
-// numerator) are merged with lane exchanges; used when a launch has too few
-// entries to fill the GPU (decode-time refresh).  The kernel uses no LDS, so
-// its workgroups can share a CU with an LDS-heavy kernel running beside it
-// (the indexer scan holds almost all of a CU's LDS).
-template <Dt DT, int S>
-__global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
-  static_assert(S >= 1 && S <= 64 && (S & (S - 1)) == 0, "slices: a power of two within a wavefront");
+// One entry j of one sequence for VEC channels from c0, with S thread
+// slices (S consecutive lanes) sharing its candidates; returns true in the
+// lane that holds the result (o).  S = 1: the thread folds every candidate.
+// S > 1: the candidates are split over the S slices, whose partial (max,
+// denominator, numerator) are merged with lane exchanges.  The slicing
+// depends only on the block size (S = 16 when m >= 32), so an entry comes
+// out bit for bit the same from a bulk launch and from a per-token append.
+template <Dt DT, int S, typename Rows>
+__device__ __forceinline__ bool compress_entry(const CompressArgs& a, const Rows& rows, bool live, int64_t j,
+                                               int64_t c0, int slice, float* o) {
   constexpr int VEC = Io<DT>::VEC;
-  constexpr int LANES = 256 / S;  // channel groups per workgroup
-  const int slice = threadIdx.x % S;
-  const int lane = threadIdx.x / S;
-  const int64_t nvec = a.D / VEC;
-  const int64_t ne = a.e1 - a.e0;
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * LANES + lane;
-  const bool live = gid < a.B * ne * nvec;
-  const int64_t g = live ? gid : 0;
-  const int64_t cv = g % nvec;
-  const int64_t tmp = g / nvec;
-  const int64_t jj = tmp % ne;
-  const int64_t b = tmp / ne;
-  const int64_t j = a.e0 + jj;
-  const int64_t c0 = cv * VEC;
-  const int64_t row_base = b * a.n_raw;
-
   float mx[VEC], den[VEC], acc[VEC];
 #pragma unroll
   for (int c = 0; c < VEC; ++c) { mx[c] = -INFINITY; den[c] = 0.f; acc[c] = 0.f; }
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
     lo = slice * per;
     hi = lo + per < total ? lo + per : total;
   }
-  if (live && lo < hi) fold_range<DT>(a, cd, lo, hi, row_base, c0, mx, den, acc);
+  if (live && lo < hi) fold_range<DT>(a, cd, lo, hi, rows, c0, mx, den, acc);
 
   if (S > 1) {
     // Pairwise merges over the S lanes (xor distance 1, 2, ...): both lanes
@@ -224,13 +225,101 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
         acc[c] = fmaf(al, fl, ah * fh);
       }
     }
-    if (slice != 0) return;
+    if (slice != 0) return false;
   }
-  if (!live) return;
-  float o[VEC];
+  if (!live) return false;
 #pragma unroll
   for (int c = 0; c < VEC; ++c) o[c] = den[c] > 0.f ? acc[c] / den[c] : 0.f;
-  Io<DT>::store(a.out, (b * a.out_ld + jj) * a.D + c0, o);
+  return true;
+}
+
+// Bulk: one (entry, 16-byte channel group) per S thread slices.  The kernel
+// uses no LDS, so its workgroups can share a CU with an LDS-heavy kernel
+// running beside it (the indexer scan holds almost all of a CU's LDS).
+template <Dt DT, int S>
+__global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
+  static_assert(S >= 1 && S <= 64 && (S & (S - 1)) == 0, "slices: a power of two within a wavefront");
+  constexpr int VEC = Io<DT>::VEC;
+  constexpr int LANES = 256 / S;  // channel groups per workgroup
+  const int slice = threadIdx.x % S;
+  const int lane = threadIdx.x / S;
+  const int64_t nvec = a.D / VEC;
+  const int64_t ne = a.e1 - a.e0;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * LANES + lane;
+  const bool live = gid < a.B * ne * nvec;
+  const int64_t g = live ? gid : 0;
+  const int64_t cv = g % nvec;
+  const int64_t tmp = g / nvec;
+  const int64_t jj = tmp % ne;
+  const int64_t b = tmp / ne;
+  const int64_t c0 = cv * VEC;
+  float o[VEC];
+  if (compress_entry<DT, S>(a, BulkRows{a, b * a.n_raw}, live, a.e0 + jj, c0, slice, o))
+    Io<DT>::store(a.out, (b * a.out_ld + jj) * a.D + c0, o);
+}
+
+// Per-token append: where the rows of sequence b live.  The new token
+// (position p) is read from the inputs; earlier positions from the staging
+// rings (slot u % n_raw).
+struct AppendRows {
+  const CompressArgs& a;
+  int64_t b, p;
+  __device__ void operator()(bool from_b, int64_t u, const void** x, const void** z, int64_t* off) const {
+    if (u == p) {  // only stream A reads the new token (stream B reads the previous block)
+      *x = a.x_a;
+      *z = a.z_a;
+      *off = b;
+      return;
+    }
+    *x = from_b ? a.ring_xb : a.ring_xa;
+    *z = from_b ? a.ring_zb : a.ring_za;
+    *off = b * a.n_raw + u % a.n_raw;
+  }
+};
+
+// One new token per sequence: slice 0 of each channel group stages the
+// token's rows (stream A, and stream B in two-path mode) into ring slot
+// p % n_raw; when the token completes its block (p + 1 divisible by m) the
+// entry p / m is folded from the rings and the new rows and written to the
+// cache.  No candidate of that entry occupies slot p % n_raw (n_raw >= 2m in
+// two-path mode, >= m otherwise), so the staging store races with no read.
+template <Dt DT, int S>
+__global__ __launch_bounds__(256) void compress_append_kernel(CompressArgs a) {
+  constexpr int VEC = Io<DT>::VEC;
+  constexpr int LANES = 256 / S;
+  const int slice = threadIdx.x % S;
+  const int lane = threadIdx.x / S;
+  const int64_t nvec = a.D / VEC;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * LANES + lane;
+  const bool in = gid < a.B * nvec;
+  const int64_t g = in ? gid : 0;
+  const int64_t cv = g % nvec;
+  const int64_t b = g / nvec;
+  const int64_t c0 = cv * VEC;
+  const int64_t p = a.pos[b];
+  const bool ok = in && p >= 0;  // a negative position stages nothing
+  if (ok && slice == 0) {
+    const int64_t src = b * a.D + c0, dst = (b * a.n_raw + p % a.n_raw) * a.D + c0;
+    float v[VEC];
+    Io<DT>::load(a.x_a, src, v);
+    Io<DT>::store(a.ring_xa, dst, v);
+    Io<DT>::load(a.z_a, src, v);
+    Io<DT>::store(a.ring_za, dst, v);
+    if (a.x_b) {
+      Io<DT>::load(a.x_b, src, v);
+      Io<DT>::store(a.ring_xb, dst, v);
+      Io<DT>::load(a.z_b, src, v);
+      Io<DT>::store(a.ring_zb, dst, v);
+    }
+  }
+  // uniform over the sequence's slices; entries past the cache are not written
+  const int64_t j = ok ? p / a.m : 0;
+  const bool emit = ok && (p + 1) % a.m == 0 && j < a.out_ld;
+  float o[VEC];
+  if (compress_entry<DT, S>(a, AppendRows{a, b, p}, emit, j, c0, slice, o)) {
+    const int64_t row = a.lay.bt ? cache_row(a.lay, a.out_ld, b, j) : b * a.out_ld + j;
+    Io<DT>::store(a.out, row * a.D + c0, o);
+  }
 }
 
 }  // namespace
@@ -239,8 +328,9 @@ hipError_t launch_compress(const CompressArgs& a, Dt dt, hipStream_t s) {
   const int vec = dt == kF32 ? 4 : 8;
   const int64_t total = a.B * (a.e1 - a.e0) * (a.D / vec);
   if (total == 0) return hipSuccess;
-  // Few entries with long blocks: spread each block's tokens over 16 slices.
-  const bool sliced = total < 32768 && a.m >= 32;
+  // Long blocks (m >= 32) spread each entry's tokens over 16 slices: the
+  // same fold order in bulk and in per-token appends.
+  const bool sliced = a.m >= 32;
   const dim3 grid(static_cast<uint32_t>(sliced ? (total + 15) / 16 : (total + 255) / 256));
 #define CSA_COMPRESS_LAUNCH(DT_)                                                          \
   if (sliced) hipLaunchKernelGGL((compress_kernel<DT_, 16>), grid, dim3(256), 0, s, a);  \
@@ -251,6 +341,49 @@ hipError_t launch_compress(const CompressArgs& a, Dt dt, hipStream_t s) {
     default: CSA_COMPRESS_LAUNCH(kF32) break;
   }
 #undef CSA_COMPRESS_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_compress_append(const CompressArgs& a, Dt dt, hipStream_t s) {
+  const int vec = dt == kF32 ? 4 : 8;
+  const int64_t total = a.B * (a.D / vec);
+  if (total == 0) return hipSuccess;
+  const bool sliced = a.m >= 32;
+  const dim3 grid(static_cast<uint32_t>(sliced ? (total + 15) / 16 : (total + 255) / 256));
+#define CSA_APPEND_LAUNCH(DT_)                                                                   \
+  if (sliced) hipLaunchKernelGGL((compress_append_kernel<DT_, 16>), grid, dim3(256), 0, s, a);  \
+  else hipLaunchKernelGGL((compress_append_kernel<DT_, 1>), grid, dim3(256), 0, s, a);
+  switch (dt) {
+    case kBF16: CSA_APPEND_LAUNCH(kBF16) break;
+    case kFP8: CSA_APPEND_LAUNCH(kFP8) break;
+    default: CSA_APPEND_LAUNCH(kF32) break;
+  }
+#undef CSA_APPEND_LAUNCH
+  return hipGetLastError();
+}
+
+// Raw window rows of one new token per sequence: position p goes to ring
+// slot p % R.  One thread per 16 bytes of a row.
+__global__ __launch_bounds__(256) void window_append_kernel(const uint4* k_new, const uint4* v_new, uint4* kr,
+                                                            uint4* vr, const int64_t* pos, int64_t B, int64_t R,
+                                                            int64_t row16) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (gid >= B * row16) return;
+  const int64_t b = gid / row16, c = gid % row16;
+  const int64_t p = pos[b];
+  if (p < 0) return;
+  const int64_t dst = (b * R + p % R) * row16 + c;
+  kr[dst] = k_new[gid];
+  vr[dst] = v_new[gid];
+}
+
+hipError_t launch_window_append(const void* k_new, const void* v_new, void* kr, void* vr, const int64_t* pos,
+                                int64_t B, int64_t R, int64_t row_bytes, hipStream_t s) {
+  const int64_t row16 = row_bytes / 16, total = B * row16;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(window_append_kernel, dim3(static_cast<uint32_t>((total + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new), static_cast<uint4*>(kr),
+                     static_cast<uint4*>(vr), pos, B, R, row16);
   return hipGetLastError();
 }
 

@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
   const int64_t part = blockIdx.x % parts;
   const int64_t row = a.row0 + lrow;
   const int64_t b = row / a.T;
-  const int64_t tpos = a.n_ctx - a.T + row % a.T;
+  const int64_t tpos = seq_len(a.lay, a.n_ctx, a.T, b) - a.T + row % a.T;
   int64_t nv = tpos / a.m;
   if (nv > a.L) nv = a.L;
   float* srow = a.score + lrow * a.ld;
@@ -314,8 +314,10 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
   //    writes slot s = l%8 of key 8j + l/8, so it fetches piece
   //    (s - kk/2) % 8.
   // Only a tile that runs past the last key (the very end of a row) takes
-  // per-lane clamped addresses.
-  const char* kbase = static_cast<const char*>(a.k) + b * a.L * KB;
+  // per-lane clamped addresses.  A tile's 16 keys are consecutive rows of the
+  // key cache: of sequence b's [L] rows, or of one page of a paged pool
+  // (pages hold a multiple of 16 entries and tiles start at multiples of 16).
+  const char* kpool = static_cast<const char*>(a.k);
   //  MXFP4: key kk's codes at kk*64, four 16-byte blocks; block p of key kk
   //    sits at slot (p + kk/4) % 4 (the 16 keys of one read then cover the 64
   //    banks once).  Lane l of the code load writes slot l%4 of key l/4.
@@ -339,26 +341,29 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
     }
   }
   uint8_t* myring = &ring[wave][0][0];
-  // MXFP4 scales follow all B*L*64 code bytes, 4 per key.
-  const char* sbase = FP4 ? static_cast<const char*>(a.k) + a.B * a.L * KB + b * a.L * 4 : nullptr;
+  // MXFP4 scales follow all code bytes (of B*L keys, or of the pool's
+  // npages*page keys), 4 per key.
+  const int64_t nkeys = a.lay.bt ? a.lay.npages * a.lay.page : a.B * a.L;
+  const char* sbase = FP4 ? kpool + nkeys * KB : nullptr;
   auto issue = [&](int it) {
     uint8_t* slot = myring + (it % DEPTH) * TB;
     const int64_t t0 = k0 + static_cast<int64_t>(it) * kStride;
+    const int64_t r0 = cache_row(a.lay, a.L, b, t0);  // row of key t0; keys t0 .. t0+15 follow it
     if constexpr (FP4) {
       if (t0 + kTileKeys <= a.L) {
-        dma16(kbase + t0 * KB, voff[0], slot);
-        dma4(sbase + t0 * 4, voff[1], slot + 1024);
+        dma16(kpool + r0 * KB, voff[0], slot);
+        dma4(sbase + r0 * 4, voff[1], slot + 1024);
       } else {
         int64_t s0 = t0 + kkl[0], s1 = t0 + kkl[1];
         s0 = s0 < a.L - 1 ? s0 : a.L - 1;
         s1 = s1 < a.L - 1 ? s1 : a.L - 1;
-        dma16(kbase + s0 * KB + (voff[0] - kkl[0] * KB), slot);
-        dma4(sbase + s1 * 4, slot + 1024);
+        dma16(kpool + (r0 + s0 - t0) * KB + (voff[0] - kkl[0] * KB), slot);
+        dma4(sbase + (r0 + s1 - t0) * 4, slot + 1024);
       }
       return;
     }
     if (t0 + kTileKeys <= a.L) {
-      const char* tb = kbase + t0 * KB;
+      const char* tb = kpool + r0 * KB;
 #pragma unroll
       for (int j = 0; j < LPT; ++j) dma16(tb, voff[j], slot + j * 1024);
     } else {
@@ -366,7 +371,7 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
       for (int j = 0; j < LPT; ++j) {
         int64_t s = t0 + kkl[j];
         s = s < a.L - 1 ? s : a.L - 1;
-        dma16(kbase + s * KB + (voff[j] - kkl[j] * KB), slot + j * 1024);
+        dma16(kpool + (r0 + s - t0) * KB + (voff[j] - kkl[j] * KB), slot + j * 1024);
       }
     }
   };
@@ -538,7 +543,8 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
   const int64_t part = blockIdx.x % parts;
   const int64_t row0 = a.row0 + rblk * kMultiRows;  // first row of the block (a multiple of 16; T % 16 == 0)
   const int64_t b = row0 / a.T;
-  int64_t nvmax = (a.n_ctx - a.T + (row0 + kMultiRows - 1) % a.T) / a.m;  // the block's last row sees most
+  const int64_t n_b = seq_len(a.lay, a.n_ctx, a.T, b);
+  int64_t nvmax = (n_b - a.T + (row0 + kMultiRows - 1) % a.T) / a.m;  // the block's last row sees most
   if (nvmax > a.L) nvmax = a.L;
   const int64_t kb = part * kMultiKeys;
   const int64_t ke = kb + kMultiKeys < a.L ? kb + kMultiKeys : a.L;
@@ -640,7 +646,7 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
 #pragma unroll
   for (int i = 0; i < kMultiRpw; ++i) {
     const int64_t row = row0 + kMultiRpw * wave + i;
-    int64_t nv = (a.n_ctx - a.T + row % a.T) / a.m;
+    int64_t nv = (n_b - a.T + row % a.T) / a.m;
     if (nv > a.L) nv = a.L;
     float* srow = a.score + (row - a.row0) * a.ld;
     const float* sb = sbuf[kMultiRpw * wave + i];
@@ -660,7 +666,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_direct(IndexScoreArgs a,
   const int64_t part = blockIdx.x % parts;
   const int64_t row = a.row0 + lrow;
   const int64_t b = row / a.T;
-  const int64_t tpos = a.n_ctx - a.T + row % a.T;
+  const int64_t tpos = seq_len(a.lay, a.n_ctx, a.T, b) - a.T + row % a.T;
   int64_t nv = tpos / a.m;
   if (nv > a.L) nv = a.L;
   float* srow = a.score + lrow * a.ld;
@@ -668,7 +674,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_direct(IndexScoreArgs a,
   if (wave_begin >= a.L) return;
   const int g = lane >> 4;
   const int c16 = lane & 15;
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.L * DI + g * 8;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + g * 8;
   const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + row * HI * DI;
   bf16x8 afrag[MB][KS];
 #pragma unroll
@@ -680,8 +686,9 @@ __global__ __launch_bounds__(256) void index_score_mfma_direct(IndexScoreArgs a,
     int64_t s = wave_begin + it * kTileKeys + c16;
     const int64_t sc = s < a.L - 1 ? s : a.L - 1;
     bf16x8 cur[KS];
+    const int64_t kr = cache_row(a.lay, a.L, b, sc);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) cur[ks] = *reinterpret_cast<const bf16x8*>(kbase + sc * DI + ks * 32);
+    for (int ks = 0; ks < KS; ++ks) cur[ks] = *reinterpret_cast<const bf16x8*>(kbase + kr * DI + ks * 32);
     f32x4 acc[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -712,7 +719,7 @@ __global__ __launch_bounds__(256) void index_score_f32(IndexScoreArgs a, int64_t
   const int64_t part = blockIdx.x % parts;
   const int64_t row = a.row0 + lrow;
   const int64_t b = row / a.T;
-  const int64_t tpos = a.n_ctx - a.T + row % a.T;
+  const int64_t tpos = seq_len(a.lay, a.n_ctx, a.T, b) - a.T + row % a.T;
   int64_t nv = tpos / a.m;
   if (nv > a.L) nv = a.L;
   const float* q = static_cast<const float*>(a.q) + row * a.HI * a.dI;
@@ -725,7 +732,7 @@ __global__ __launch_bounds__(256) void index_score_f32(IndexScoreArgs a, int64_t
     srow[s] = -INFINITY;
     return;
   }
-  const float* kr = static_cast<const float*>(a.k) + (b * a.L + s) * a.dI;
+  const float* kr = static_cast<const float*>(a.k) + cache_row(a.lay, a.L, b, s) * a.dI;
   float tot = 0.f;
   for (int64_t h = 0; h < a.HI; ++h) {
     float dot = 0.f;
@@ -793,7 +800,7 @@ hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t s) {
   if (a.dt == kBF16) {
     const int mb = static_cast<int>(a.HI / 16), ks = static_cast<int>(a.dI / 32);
     const bool w = a.w != nullptr;
-    if (ks == 4 && index_multi_rows(a.T, a.HI, a.row0, a.nrows)) {
+    if (ks == 4 && !a.lay.bt && index_multi_rows(a.T, a.HI, a.row0, a.nrows)) {
       const int64_t parts = (a.L + kMultiKeys - 1) / kMultiKeys;
       const dim3 grid(static_cast<uint32_t>(a.nrows / kMultiRows * parts));
       const dim3 block(64 * kMultiRows / kMultiRpw);

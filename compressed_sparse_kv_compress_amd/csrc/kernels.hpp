@@ -9,6 +9,39 @@ namespace csa {
 // Storage types, numbered as csa_dtype_t: fp32, bf16, and FP8 (OCP E4M3).
 enum Dt : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kMXFP4 = 3 };
 
+// How a batch's sequences and caches are laid out (all optional):
+//   lens  : per-sequence token counts n_b (device, [B]); null = every sequence
+//           has the launch's n_ctx.  Kernels clamp n_b into [T, n_ctx].
+//   bt    : block table (device, [B][bt_ld] int32) of paged compressed caches:
+//           entry s of sequence b is row bt[b][s / page] * page + s % page of
+//           a pool of npages * page rows; null = dense [B][L] caches.  Page
+//           ids outside [0, npages) are clamped to stay in bounds.
+//   ring  : raw-window buffers [B][R][d] hold position u at slot u % R
+//           (otherwise positions n_b - R .. n_b - 1 in order).
+struct SeqLayout {
+  const int64_t* lens = nullptr;
+  const int32_t* bt = nullptr;
+  int64_t bt_ld = 0, page = 0, npages = 0;
+  int ring = 0;
+};
+
+// Token count of sequence b (n_ctx when the lengths are uniform).
+__device__ __forceinline__ int64_t seq_len(const SeqLayout& l, int64_t n_ctx, int64_t T, int64_t b) {
+  if (!l.lens) return n_ctx;
+  int64_t n = l.lens[b];
+  n = n < T ? T : n;
+  return n > n_ctx ? n_ctx : n;
+}
+
+// Row of entry s of sequence b in its cache: b * L + s for dense caches, the
+// pool row through the block table for paged ones.
+__device__ __forceinline__ int64_t cache_row(const SeqLayout& l, int64_t L, int64_t b, int64_t s) {
+  if (!l.bt) return b * L + s;
+  int64_t pg = l.bt[b * l.bt_ld + s / l.page];
+  pg = pg < 0 ? 0 : (pg >= l.npages ? l.npages - 1 : pg);
+  return pg * l.page + s % l.page;
+}
+
 struct CompressArgs {
   const void* x_a;
   const void* z_a;
@@ -17,8 +50,26 @@ struct CompressArgs {
   const float* bias;  // null or [span][D]
   void* out;          // [B][out_ld][D], entry j at row j - e0
   int64_t B, n, D, m, p0, n_raw, e0, e1, out_ld;
+  // Per-token append (pos != null): sequence b's new token sits at position
+  // pos[b]; x_a.. hold only that token's rows ([B][D]); the raw rows of the
+  // earlier tokens of its block(s) are in staging rings [B][n_raw][D]
+  // (position u at slot u % n_raw), which receive the new rows too.  The
+  // entry pos[b] / m is written when the token completes it (to out, row
+  // b * out_ld + entry, or to the paged cache through lay).
+  const int64_t* pos = nullptr;
+  void* ring_xa = nullptr;
+  void* ring_za = nullptr;
+  void* ring_xb = nullptr;
+  void* ring_zb = nullptr;
+  SeqLayout lay;
 };
 hipError_t launch_compress(const CompressArgs& a, Dt dt, hipStream_t s);
+// Per-token append (a.pos, rings set; a.n_raw = ring rows; out_ld = L).
+hipError_t launch_compress_append(const CompressArgs& a, Dt dt, hipStream_t s);
+// Window rows of one new token per sequence into ring slot pos[b] % R
+// (row_bytes a multiple of 16).
+hipError_t launch_window_append(const void* k_new, const void* v_new, void* kr, void* vr, const int64_t* pos,
+                                int64_t B, int64_t R, int64_t row_bytes, hipStream_t s);
 
 struct IndexScoreArgs {
   const void* q;      // [rows][HI][dI], rows = B*T (b-major)
@@ -30,6 +81,7 @@ struct IndexScoreArgs {
   int64_t nrows;      // rows handled
   int64_t B, T, n_ctx, L, HI, dI, m;
   Dt dt;              // storage of q and k (scores are fp32)
+  SeqLayout lay;      // per-sequence lengths, paged keys
 };
 hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t s);
 
@@ -64,6 +116,7 @@ struct TopkArgs {
   int64_t T, n_ctx, L, m, k;
   int32_t* idx;        // [rows][k] (offset to row0 already)
   float* out_score;    // [rows][k] or null
+  const int64_t* lens = nullptr;  // per-sequence token counts (see SeqLayout)
 };
 // ws: topk_ws_bytes_per_row(L, k) bytes per row of the launch.
 size_t topk_ws_bytes_per_row(int64_t L, int64_t k);
@@ -115,6 +168,7 @@ struct AttnArgs {
   float* lse;           // [B*T][H] or null
   float* ws;            // split partials
   size_t ws_bytes;
+  SeqLayout lay;        // per-sequence lengths, paged caches, ring windows
 };
 // Number of row splits the attention launch uses, and its workspace bytes.
 // MFMA attention (bf16, or FP8 K/V with bf16 q and out): at most

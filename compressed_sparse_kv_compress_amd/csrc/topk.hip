@@ -116,7 +116,9 @@ struct MShared {
 };
 
 __device__ __forceinline__ int64_t row_visible(const TopkArgs& a, int64_t row) {
-  const int64_t tpos = a.n_ctx - a.T + row % a.T;
+  SeqLayout l;
+  l.lens = a.lens;
+  const int64_t tpos = seq_len(l, a.n_ctx, a.T, row / a.T) - a.T + row % a.T;
   int64_t nv = tpos / a.m;
   if (nv > a.L) nv = a.L;
   return nv < 0 ? 0 : nv;

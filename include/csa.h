@@ -82,6 +82,39 @@ typedef enum csa_status {
 } csa_status_t;
 
 /* ---------------------------------------------------------------------------
+ * csa_layout_t -- how a serving batch is laid out, for the *_ex calls and the
+ * per-token appends (trdm.cn, section 3, Paged Attention paragraph: a block
+ * table maps each sequence's logical blocks to physical ones, so sequences
+ * of mixed lengths share one pool).  Every field is optional:
+ *   seq_len      device int64 [B]: tokens of each sequence; the n_ctx
+ *                argument is then the largest.  Query i of sequence b sits
+ *                at seq_len[b] - T + i.  Values outside [T, n_ctx] are
+ *                clamped into it (keeping every access in bounds); NULL =
+ *                every sequence has n_ctx tokens.
+ *   block_table  device int32 [B][bt_stride]: the compressed caches (kc, vc,
+ *                k_idx) are pools of num_pages pages of `page` entries
+ *                (rows); entry s of sequence b is pool row
+ *                block_table[b][s / page] * page + s % page.  page is a
+ *                multiple of 16, bt_stride >= ceil(L / page), and
+ *                num_pages * page < 2^31.  Page ids outside [0, num_pages)
+ *                are clamped into it.  An MXFP4 key pool holds the codes of
+ *                all num_pages * page keys, then their scales.  NULL = dense
+ *                [B][L] caches.
+ *   window_ring  1: the raw-window buffers kr / vr [B][R][d] are rings that
+ *                hold position u at slot u % R (what csa_window_append
+ *                writes); R >= T + W - 1 and R >= W.  0: they hold
+ *                positions n_b - R .. n_b - 1 in order.
+ * ------------------------------------------------------------------------- */
+typedef struct csa_layout {
+  const int64_t* seq_len;
+  const int32_t* block_table;
+  int64_t bt_stride;
+  int64_t page;
+  int64_t num_pages;
+  int32_t window_ring;
+} csa_layout_t;
+
+/* ---------------------------------------------------------------------------
  * csa_compress -- block-weighted compression of one K/V/index-key stream.
  * shareware.cn article, section 四 (each entry is a dynamic, per-dimension
  * softmax-weighted sum of its block's raw rows) and section 五 / trdm.cn
@@ -115,6 +148,37 @@ csa_status_t hca_compress(const void* x, const void* z, const float* bias, void*
                           int64_t n, int64_t D, int64_t m, int64_t p0, int64_t n_raw,
                           int64_t e0, int64_t e1, int64_t out_ld, csa_dtype_t dtype,
                           void* stream);
+
+/* csa_compress_append -- decode-time cache maintenance of one stream: one new
+ * raw token per sequence (shareware.cn article, section 十: an entry exists
+ * once its block is complete, the window covers the rest; trdm.cn section 4.3
+ * 改进三).  Token p = pos[b] of sequence b (x_a, z_a, and x_b, z_b in
+ * two-path mode: [B][D] rows) is staged into the rings ring_xa, ring_za
+ * (ring_xb, ring_zb) [B][S][D] at slot p % S; when p + 1 is a multiple of m
+ * the entry p / m is compressed exactly as csa_compress does (same
+ * arithmetic, same result bit for bit) from the staged rows of its block
+ * (and of the previous block through stream B) and written to the cache:
+ * row b * L + p / m of cache [B][L][D], or its pool row through
+ * layout->block_table.  S >= 2m in two-path mode, >= m otherwise; bias as
+ * csa_compress.  pos is device int64 [B]; a negative position stages
+ * nothing, and entries at or past L are not written.  The rings must hold
+ * the sequence's earlier tokens of the current (and previous) block: a
+ * sequence's prefix is compressed in bulk with csa_compress and its last
+ * 2m raw rows copied into the rings (slot u % S) before the first append.
+ * layout: NULL, or only block_table / bt_stride / page / num_pages used. */
+csa_status_t csa_compress_append(const csa_layout_t* layout, const void* x_a, const void* z_a,
+                                 const void* x_b, const void* z_b, const float* bias, void* ring_xa,
+                                 void* ring_za, void* ring_xb, void* ring_zb, int64_t S,
+                                 const int64_t* pos, void* cache, int64_t L, int64_t B, int64_t D,
+                                 int64_t m, csa_dtype_t dtype, void* stream);
+
+/* csa_window_append -- the raw window rows (k_new, v_new [B][d]) of one new
+ * token per sequence into ring windows kr, vr [B][R][d] at slot pos[b] % R
+ * (shareware.cn article, section 三.1: the latest raw tokens stay
+ * uncompressed).  pos: device int64 [B], non-negative. */
+csa_status_t csa_window_append(const void* k_new, const void* v_new, void* kr, void* vr,
+                               const int64_t* pos, int64_t B, int64_t R, int64_t d,
+                               csa_dtype_t dtype, void* stream);
 
 /* ---------------------------------------------------------------------------
  * csa_index_score -- Lightning Indexer scores (shareware.cn article,
@@ -161,6 +225,15 @@ csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k
                             int64_t T, int64_t n_ctx, int64_t L, int64_t H_I, int64_t d_I,
                             int64_t m, int64_t k, int32_t* idx, float* out_score, void* ws,
                             size_t ws_bytes, csa_dtype_t dtype, void* stream);
+
+/* csa_index_topk_ex -- csa_index_topk over a serving layout (per-sequence
+ * lengths, paged index keys k_idx: a pool of layout->num_pages pages).  L is
+ * the capacity in entries of the longest sequence.  NULL layout = csa_index_topk. */
+csa_status_t csa_index_topk_ex(const csa_layout_t* layout, const void* q_idx, const float* w_idx,
+                               const void* k_idx, int64_t B, int64_t T, int64_t n_ctx, int64_t L,
+                               int64_t H_I, int64_t d_I, int64_t m, int64_t k, int32_t* idx,
+                               float* out_score, void* ws, size_t ws_bytes, csa_dtype_t dtype,
+                               void* stream);
 
 /* csa_index_topk_noalloc -- csa_index_topk for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
@@ -234,6 +307,24 @@ csa_status_t hca_dense_attn(const void* q, const void* kc, const void* vc, int64
                             const float* sink, float scale, int64_t B, int64_t T, int64_t n_ctx,
                             int64_t H, int64_t d, void* out, float* lse, void* ws,
                             size_t ws_bytes, csa_dtype_t dtype, void* stream);
+
+/* csa_sparse_attn_ex / hca_dense_attn_ex -- the attention calls over a
+ * serving layout: per-sequence lengths, paged kc / vc pools, ring windows.
+ * The workspace: csa_attn_workspace(B, T, H, d, rows) bytes with rows the
+ * longest row list (k + W, or the most visible entries + W).  NULL layout =
+ * csa_sparse_attn / hca_dense_attn. */
+csa_status_t csa_sparse_attn_ex(const csa_layout_t* layout, const void* q, const void* kc,
+                                const void* vc, int64_t L, const int32_t* idx, int64_t k,
+                                const void* kr, const void* vr, int64_t R, int64_t W,
+                                const float* sink, float scale, int64_t B, int64_t T, int64_t n_ctx,
+                                int64_t H, int64_t d, void* out, float* lse, void* ws,
+                                size_t ws_bytes, csa_dtype_t dtype, void* stream);
+csa_status_t hca_dense_attn_ex(const csa_layout_t* layout, const void* q, const void* kc,
+                               const void* vc, int64_t L, int64_t m, const void* kr, const void* vr,
+                               int64_t R, int64_t W, const float* sink, float scale, int64_t B,
+                               int64_t T, int64_t n_ctx, int64_t H, int64_t d, void* out,
+                               float* lse, void* ws, size_t ws_bytes, csa_dtype_t dtype,
+                               void* stream);
 
 /* Status names and the calling thread's last error detail (never NULL). */
 const char* csa_status_string(csa_status_t status);

@@ -82,6 +82,8 @@ def test_attn_workspace_covers_both_attention_calls(lib):
         assert aw(B, T, 64, 512, 7812 + 128) >= dw(B, T, 64, 512, 7813, 128, 1000000, 128, 1)
         assert aw(B, T, 64, 512, 7812) >= dw(B, T, 64, 512, 7813, 128, 1000000, 0, 2)
     assert aw(0, 1, 64, 512, 100) == 0
+    # fewer heads than one MFMA head group (the fp32 kernel's shapes): no split workspace, no fault
+    assert aw(3, 1, 8, 64, 440) == 0
 
 
 def test_library_exports_every_declared_symbol(lib):
