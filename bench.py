@@ -9,13 +9,15 @@ storage, fp32 accumulation; n_ctx = 1,000,000 tokens; batch 16.  All eight
 layers' compressed caches are resident in HBM (about 2.4 GB per sequence).
 
 One step decodes the token at position t = n_ctx - 1 of every sequence
-through all 8 layers.  Per CSA layer: csa_compress writes the entry whose
-block the new token completes (K, V and index keys, two-path), then the
-indexer scores every visible entry and keeps the top 1024 (csa_index_topk:
-one scan kernel that also selects each part's candidates, then a merge
-kernel), and csa_sparse_attn attends over them plus the window.  Per HCA layer: hca_compress refreshes the
-newest complete 128-token entry (K and V) and hca_dense_attn attends over all
-7812 visible entries plus the window.
+through all 8 layers, with the decode-time maintenance of the caches: on a
+second stream csa_window_append puts the token's raw K/V rows into every
+layer's window ring and csa_compress_append stages its compression inputs,
+writing the entry whose block it completes (every CSA step at t = 999,999; HCA
+blocks complete every 128th token); per CSA layer the indexer scores every
+visible entry and keeps the top 1024 (csa_index_topk: one scan kernel that
+also selects each part's candidates, then a merge kernel) and
+csa_sparse_attn attends over them plus the window; per HCA layer
+hca_dense_attn attends over all 7812 visible entries plus the window.
 
 Metric: queries/s, a query being one token of one sequence through the whole
 8-layer stack (B queries per step), plus achieved HBM GB/s of the step and
@@ -49,11 +51,19 @@ HBM_PEAK_GBPS = 8000.0
 SEED = 5
 
 
-class Stack:
-    """Shapes of the 8-layer decode workload."""
+# Layer schedules of the stack (trdm.cn, section 4.3, the layer-interleaving
+# paragraph): CSA and HCA alternate; V4-Flash-style stacks open with two
+# layers of sliding-window attention only, V4-Pro-style ones with two HCA
+# layers.
+SCHEDULES = ("alternate", "flash", "pro")
 
-    def __init__(self, B=16, n_ctx=1_000_000, layers=8, eb=2):
-        self.B, self.n_ctx, self.layers = B, n_ctx, layers
+
+class Stack:
+    """Shapes of the 8-layer decode workload and its algorithmic bytes."""
+
+    def __init__(self, B=16, n_ctx=1_000_000, layers=8, eb=2, schedule="alternate"):
+        assert schedule in SCHEDULES
+        self.B, self.n_ctx, self.layers, self.schedule = B, n_ctx, layers, schedule
         self.eb = eb  # bytes per stored element: caches, window, indexer q/k, compression inputs
         self.H, self.d = 64, 512
         self.HI, self.dI = 64, 128
@@ -61,17 +71,22 @@ class Stack:
         self.m_csa, self.m_hca = 4, 128
         self.L_csa = -(-n_ctx // self.m_csa)
         self.L_hca = -(-n_ctx // self.m_hca)
-        self.t = n_ctx - 1
+        self.t = n_ctx - 1  # the token each step decodes (the last of the history)
         self.nv_csa = min(self.L_csa, self.t // self.m_csa)
         self.nv_hca = min(self.L_hca, self.t // self.m_hca)
-        # CSA: the block holding t is complete after t arrives; its entry is new.
-        self.csa_new = self.t // self.m_csa if (self.t + 1) % self.m_csa == 0 else self.nv_csa - 1
-        # HCA: the newest complete 128-token entry (visible to t).
-        self.hca_new = self.nv_hca - 1
         self.scale = 1.0 / math.sqrt(self.d)
 
     def kinds(self):
-        return ["csa" if i % 2 == 0 else "hca" for i in range(self.layers)]
+        alt = ["csa" if i % 2 == 0 else "hca" for i in range(self.layers)]
+        if self.schedule == "flash":
+            return ["win", "win"] + alt[:self.layers - 2]
+        if self.schedule == "pro":
+            return ["hca", "hca"] + alt[:self.layers - 2]
+        return alt
+
+    def emits(self, m):
+        """Whether the decoded token completes its block (an entry is written)."""
+        return (self.t + 1) % m == 0
 
     # ---- algorithmic bytes (what the method must move), per query ----------
     def index_bytes(self):
@@ -79,27 +94,47 @@ class Stack:
         index heads and head weights, the selected indices written."""
         return self.nv_csa * self.dI * self.eb + self.HI * self.dI * self.eb + self.HI * 4 + self.k * 4
 
+    def _append_bytes(self, D, streams, m):
+        """csa_compress_append of one stream: the new token's rows read and
+        staged, and when its block completes the block's rows (and the
+        previous block's, two-path) read and the entry written."""
+        e = self.eb
+        b = 2 * streams * D * e
+        if self.emits(m):
+            b += streams * m * D * e + D * e
+        return b
+
+    def _window_bytes(self):
+        """Attention's raw window rows, and csa_window_append of the new token."""
+        e = self.eb
+        return self.W * self.d * 2 * e + 2 * 2 * self.d * e
+
     def csa_bytes(self):
         b = self.index_bytes()
         e = self.eb
         b += self.k * self.d * 2 * e            # gathered compressed K and V rows
-        b += self.W * self.d * 2 * e            # raw window K and V
+        b += self._window_bytes()
         b += 2 * self.H * self.d * 2            # q and out (bf16)
         b += self.k * 4                         # selected indices, read by the attention
-        m = self.m_csa
-        b += 4 * m * (2 * self.d + self.dI) * e  # compress: x/z, A and B paths, K V I
-        b += (2 * self.d + self.dI) * e         # new entries
+        for D in (self.d, self.d, self.dI):     # K, V and index keys, two-path (4 streams)
+            b += self._append_bytes(D, 4, self.m_csa)
         return b
 
     def hca_bytes(self):
         e = self.eb
-        b = self.nv_hca * self.d * 2 * e + self.W * self.d * 2 * e + 2 * self.H * self.d * 2
-        b += 2 * 2 * self.m_hca * self.d * e + 2 * self.d * e  # compress K, V
+        b = self.nv_hca * self.d * 2 * e + self._window_bytes() + 2 * self.H * self.d * 2
+        for D in (self.d, self.d):              # K and V, single path (2 streams)
+            b += self._append_bytes(D, 2, self.m_hca)
         return b
 
+    def win_bytes(self):
+        return self._window_bytes() + 2 * self.H * self.d * 2
+
+    def layer_bytes(self, kind):
+        return {"csa": self.csa_bytes, "hca": self.hca_bytes, "win": self.win_bytes}[kind]()
+
     def step_bytes(self):
-        per = sum(self.csa_bytes() if k == "csa" else self.hca_bytes() for k in self.kinds())
-        return per * self.B
+        return sum(self.layer_bytes(k) for k in self.kinds()) * self.B
 
 
 def raw_rows(st: Stack, name, layer, p0, cnt, D, device, scale, dtype=torch.bfloat16):
@@ -111,84 +146,114 @@ def raw_rows(st: Stack, name, layer, p0, cnt, D, device, scale, dtype=torch.bflo
                     scale=scale, layer=layer).reshape(st.B, cnt, D)
 
 
+def ring_of(rows, p0):
+    """Rows of positions p0 .. p0+S-1 ([B][S][D]) placed at ring slots u % S."""
+    S = rows.shape[1]
+    out = torch.empty_like(rows)
+    out[:, torch.arange(p0, p0 + S, device=rows.device) % S] = rows
+    return out
+
+
+# Raw-stream names of the compressed streams: (value A, logits A, value B, logits B).
+STREAMS = {"k": ("k", "z_k", "xb_k", "zb_k"), "v": ("v", "z_v", "xb_v", "zb_v"),
+           "idx": ("k_idx", "z_idx", "xb_idx", "zb_idx")}
+
+
 class GpuState:
-    """All device buffers of the workload, generated in place on the GPU."""
+    """All device buffers of the workload, generated in place on the GPU, and
+    the decode step over them."""
 
     def __init__(self, st: Stack, device="cuda"):
         """st.eb == 2: bf16 storage.  st.eb == 1: FP8 (E4M3) storage of the
         caches, the window, the indexer's q and keys and the compression
         inputs; the attention query and output stay bf16.  FP8 K/V rows are
         unit-scale codes with the K scale 1/sqrt(d) folded into the softmax
-        scale (the V scale would fold into the output's consumer)."""
+        scale (the V scale would fold into the output's consumer).
+
+        The caches hold the history (generated directly); the raw rows of the
+        decoded token and of the earlier tokens of its block(s) sit in the
+        per-stream staging rings and the new-token rows, the last W raw
+        positions in the window rings (slot = position % W)."""
         import compressed_sparse_kv_compress_amd as csa
         self.csa = csa
         self.st = st
         bf = torch.bfloat16
         sto = bf if st.eb == 2 else torch.float8_e4m3fn
-        B, d, dI, H = st.B, st.d, st.dI, st.H
+        B, d, dI, H, W, t = st.B, st.d, st.dI, st.H, st.W, st.t
         si = dI ** -0.5
         sd = d ** -0.5 if st.eb == 2 else 1.0          # K/V value scale
         self.ascale = st.scale if st.eb == 2 else st.scale * d ** -0.5
         dt_code = csa.CSA_BF16 if st.eb == 2 else csa.CSA_FP8
+        self.pos = torch.full((B,), t, dtype=torch.int64, device=device)
+        self.ring_layout = csa.layout(ring=True)
         self.layers = []
         for li, kind in enumerate(st.kinds()):
-            L = st.L_csa if kind == "csa" else st.L_hca
             lay = {"kind": kind}
 
             def gen(shape, name, scale, dtype=bf, li=li):
-                t = torch.empty(shape, dtype=dtype, device=device)
-                return syn.fill_(t, SEED, syn.TID[name], scale=scale, layer=li)
+                x = torch.empty(shape, dtype=dtype, device=device)
+                return syn.fill_(x, SEED, syn.TID[name], scale=scale, layer=li)
 
-            lay["kc"] = gen((B, L, d), "kc", sd, sto)
-            lay["vc"] = gen((B, L, d), "vc", sd, sto)
             lay["q"] = gen((B, 1, H, d), "q", d ** -0.5)
             lay["sink"] = gen((H,), "sink", 1.0, torch.float32)
-            lay["kr"] = raw_rows(st, "kr", li, st.n_ctx - st.W, st.W, d, device, sd, sto)
-            lay["vr"] = raw_rows(st, "vr", li, st.n_ctx - st.W, st.W, d, device, sd, sto)
+            lay["kr"] = ring_of(raw_rows(st, "kr", li, t - W + 1, W, d, device, sd, sto), t - W + 1)
+            lay["vr"] = ring_of(raw_rows(st, "vr", li, t - W + 1, W, d, device, sd, sto), t - W + 1)
+            lay["k_new"] = raw_rows(st, "kr", li, t, 1, d, device, sd, sto)[:, 0].contiguous()
+            lay["v_new"] = raw_rows(st, "vr", li, t, 1, d, device, sd, sto)[:, 0].contiguous()
             lay["out"] = torch.empty((B, 1, H, d), dtype=bf, device=device)
             if kind == "csa":
-                m = st.m_csa
+                m, S = st.m_csa, 2 * st.m_csa
+                L = st.L_csa
+                lay["kc"] = gen((B, L, d), "kc", sd, sto)
+                lay["vc"] = gen((B, L, d), "vc", sd, sto)
                 lay["ki"] = gen((B, L, dI), "kic", si, sto)
                 lay["qi"] = gen((B, 1, st.HI, dI), "q_idx", si, sto)
                 lay["wi"] = gen((B, 1, st.HI), "w_idx", st.HI ** -0.5, torch.float32)
-                p0 = (st.csa_new - 1) * m
                 for s, D, sc in (("k", d, sd), ("v", d, sd), ("idx", dI, si)):
-                    xa = "k" if s == "k" else ("v" if s == "v" else "k_idx")
-                    lay["raw_" + s] = (
-                        raw_rows(st, xa, li, p0, 2 * m, D, device, sc, sto),
-                        raw_rows(st, "z_" + s, li, p0, 2 * m, D, device, 0.5, sto),
-                        raw_rows(st, "xb_" + s, li, p0, 2 * m, D, device, sc, sto),
-                        raw_rows(st, "zb_" + s, li, p0, 2 * m, D, device, 0.5, sto))
-                lay["p0"] = p0
+                    scales = (sc, 0.5, sc, 0.5)
+                    lay["new_" + s] = [raw_rows(st, nm, li, t, 1, D, device, scl, sto)[:, 0].contiguous()
+                                       for nm, scl in zip(STREAMS[s], scales)]
+                    lay["ring_" + s] = [ring_of(raw_rows(st, nm, li, t - S + 1, S, D, device, scl, sto), t - S + 1)
+                                        for nm, scl in zip(STREAMS[s], scales)]
                 lay["idx"] = torch.empty((B, 1, st.k), dtype=torch.int32, device=device)
-                lay["itk_ws"] = torch.empty(max(16, csa.csa_index_topk_workspace(B, 1, L, st.HI, st.k)),
+                lay["itk_ws"] = torch.zeros(max(16, csa.csa_index_topk_workspace(B, 1, L, st.HI, st.k)),
                                             dtype=torch.uint8, device=device)
-                nb = csa.csa_sparse_attn_workspace(B, 1, H, d, st.k, st.W, dt_code)
-            else:
-                m = st.m_hca
-                p0 = st.hca_new * m
-                lay["raw_k"] = (raw_rows(st, "k", li, p0, m, d, device, sd, sto),
-                                raw_rows(st, "z_k", li, p0, m, d, device, 0.5, sto))
-                lay["raw_v"] = (raw_rows(st, "v", li, p0, m, d, device, sd, sto),
-                                raw_rows(st, "z_v", li, p0, m, d, device, 0.5, sto))
-                lay["p0"] = p0
-                nb = csa.hca_dense_attn_workspace(B, 1, H, d, L, m, st.n_ctx, st.W, dt_code)
+                nb = csa.csa_attn_workspace(B, 1, H, d, st.k + W)
+            elif kind == "hca":
+                m = S = st.m_hca
+                L = st.L_hca
+                lay["kc"] = gen((B, L, d), "kc", sd, sto)
+                lay["vc"] = gen((B, L, d), "vc", sd, sto)
+                for s in ("k", "v"):
+                    names = (s, "z_" + s)
+                    lay["new_" + s] = [raw_rows(st, nm, li, t, 1, d, device, scl, sto)[:, 0].contiguous()
+                                       for nm, scl in zip(names, (sd, 0.5))]
+                    lay["ring_" + s] = [ring_of(raw_rows(st, nm, li, t - S + 1, S, d, device, scl, sto), t - S + 1)
+                                        for nm, scl in zip(names, (sd, 0.5))]
+                nb = csa.csa_attn_workspace(B, 1, H, d, st.nv_hca + W)
+            else:  # sliding window only: no compressed cache
+                lay["kc"] = torch.empty((B, 0, d), dtype=sto, device=device)
+                lay["vc"] = torch.empty((B, 0, d), dtype=sto, device=device)
+                nb = csa.csa_attn_workspace(B, 1, H, d, W)
             lay["ws"] = torch.empty(max(nb, 16), dtype=torch.uint8, device=device)
             self.layers.append(lay)
         self.side = torch.cuda.Stream(device=device)  # default priority
         torch.cuda.synchronize()
 
     def step(self, ev=None, only=None, csa_layer=None):
-        """One decode step through all layers.
+        """One decode step of the token at t = n_ctx - 1 through all layers.
 
-        Compression runs on a second stream: its inputs are raw tokens of
-        blocks that are already complete, so it overlaps the HBM-bound indexer
-        scan.  The CSA entry written by this step is not visible to the current
-        token; the HCA refresh is joined (event wait) before that layer's dense
-        attention reads it.  ev: optional dict of event lists keyed by call
-        name; events bracket calls (all, or the names in `only`) on the stream
-        that runs them; csa_layer: bracket only that CSA layer's calls (every
-        timing event costs a few microseconds of idle GPU between kernels)."""
+        The side stream first appends the token's raw window rows to every
+        layer's window ring (joined before the first attention), then its
+        compression inputs to the staging rings, writing the entry whose block
+        it completes; that entry is not visible to the token itself, so
+        attention never waits for compression.  The main stream runs, per
+        CSA layer, the indexer + top-k and the sparse attention, per HCA
+        layer the dense attention, per window layer the window attention.
+        ev: optional dict of event lists keyed by call name; events bracket
+        calls (all, or the names in `only`) on the stream that runs them;
+        csa_layer: bracket only that CSA layer's index call (every timing
+        event costs a few microseconds of idle GPU between kernels)."""
         csa, st = self.csa, self.st
         main = torch.cuda.current_stream()
         side = self.side
@@ -203,54 +268,75 @@ class GpuState:
             e.record()
             ev.setdefault(name, []).append(e)
 
-        joins = []
         with torch.cuda.stream(side):
+            mark("window_append")
+            for lay in self.layers:
+                csa.csa_window_append(lay["k_new"], lay["v_new"], lay["kr"], lay["vr"], self.pos)
+            mark("window_append_end")
+            windows = torch.cuda.Event()
+            windows.record()
             for lay in self.layers:
                 if lay["kind"] == "csa":
-                    m = st.m_csa
                     mark("csa_compress")
                     for s, cache in (("k", "kc"), ("v", "vc"), ("idx", "ki")):
-                        xa, za, xb, zb = lay["raw_" + s]
-                        L = lay[cache].shape[1]
-                        csa.csa_compress(xa, za, m, x_b=xb, z_b=zb, n=st.n_ctx, p0=lay["p0"], e0=st.csa_new,
-                                         e1=st.csa_new + 1, out=lay[cache][:, st.csa_new:], out_ld=L)
+                        xa, za, xb, zb = lay["new_" + s]
+                        csa.csa_compress_append(xa, za, st.m_csa, lay["ring_" + s], self.pos, lay[cache], x_b=xb,
+                                                z_b=zb)
                     mark("csa_compress_end")
-                    joins.append(None)
-                else:
-                    m = st.m_hca
+                elif lay["kind"] == "hca":
                     mark("hca_compress")
                     for s, cache in (("k", "kc"), ("v", "vc")):
-                        x, z = lay["raw_" + s]
-                        L = lay[cache].shape[1]
-                        csa.hca_compress(x, z, m, n=st.n_ctx, p0=lay["p0"], e0=st.hca_new,
-                                         e1=st.hca_new + 1, out=lay[cache][:, st.hca_new:], out_ld=L)
+                        x, z = lay["new_" + s]
+                        csa.csa_compress_append(x, z, st.m_hca, lay["ring_" + s], self.pos, lay[cache])
                     mark("hca_compress_end")
-                    done = torch.cuda.Event()
-                    done.record()
-                    joins.append(done)
 
         ci = 0
-        for lay, done in zip(self.layers, joins):
+        joined = False
+        for lay in self.layers:
             if lay["kind"] == "csa":
-                m = st.m_csa
                 mark("index_topk", ci)
-                csa.csa_index_topk(lay["qi"], lay["ki"], m, st.k, w_idx=lay["wi"], n_ctx=st.n_ctx, idx=lay["idx"],
-                                   ws=lay["itk_ws"])
+                csa.csa_index_topk(lay["qi"], lay["ki"], st.m_csa, st.k, w_idx=lay["wi"], n_ctx=st.n_ctx,
+                                   idx=lay["idx"], ws=lay["itk_ws"])
                 mark("index_topk_end", ci)
                 ci += 1
+            if not joined:
+                main.wait_event(windows)
+                joined = True
+            if lay["kind"] == "csa":
                 mark("csa_sparse_attn")
                 csa.csa_sparse_attn(lay["q"], lay["kc"], lay["vc"], lay["idx"], kr=lay["kr"], vr=lay["vr"],
                                     W=st.W, sink=lay["sink"], scale=self.ascale, n_ctx=st.n_ctx, out=lay["out"],
-                                    ws=lay["ws"])
+                                    ws=lay["ws"], layout=self.ring_layout)
                 mark("csa_sparse_attn_end")
-            else:
-                m = st.m_hca
-                main.wait_event(done)
+            elif lay["kind"] == "hca":
                 mark("hca_dense_attn")
-                csa.hca_dense_attn(lay["q"], lay["kc"], lay["vc"], m, kr=lay["kr"], vr=lay["vr"], W=st.W,
-                                   sink=lay["sink"], scale=self.ascale, n_ctx=st.n_ctx, out=lay["out"], ws=lay["ws"])
+                csa.hca_dense_attn(lay["q"], lay["kc"], lay["vc"], st.m_hca, kr=lay["kr"], vr=lay["vr"], W=st.W,
+                                   sink=lay["sink"], scale=self.ascale, n_ctx=st.n_ctx, out=lay["out"],
+                                   ws=lay["ws"], layout=self.ring_layout)
                 mark("hca_dense_attn_end")
+            else:
+                mark("window_attn")
+                csa.hca_dense_attn(lay["q"], lay["kc"], lay["vc"], st.m_hca, kr=lay["kr"], vr=lay["vr"], W=st.W,
+                                   sink=lay["sink"],
+                                   scale=self.ascale, n_ctx=st.n_ctx, out=lay["out"], ws=lay["ws"],
+                                   layout=self.ring_layout)
+                mark("window_attn_end")
         main.wait_stream(side)
+
+    def capture(self):
+        """The step as one HIP graph (stream-ordered capture of the same calls
+        on both streams); returns a callable that replays it."""
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.step()  # warm the allocator and the kernels outside the graph
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            self.step()
+        torch.cuda.synchronize()
+        return g.replay
 
 
 def event_means_ms(ev):
@@ -313,7 +399,7 @@ def cpu_baseline(st: Stack, sample: int, min_seconds: float = 10.0, max_reps: in
         return syn.rows(shape, rows, SEED, syn.TID[name], dtype=dtype, scale=scale,
                         layer=li).double().numpy().reshape(-1, D)
 
-    sub = Stack(B=S, n_ctx=st.n_ctx, layers=st.layers)
+    sub = Stack(B=S, n_ctx=st.n_ctx, layers=st.layers, schedule=st.schedule)
     per_layer = min_seconds / st.layers
     step_s, total, reps_all = 0.0, 0.0, []
     for li, kind in enumerate(st.kinds()):
@@ -323,11 +409,20 @@ def cpu_baseline(st: Stack, sample: int, min_seconds: float = 10.0, max_reps: in
         reps_all.append(reps)
         print("# cpu oracle: layer %d (%s) %.2f s over %d repetition(s)" % (li, kind, t_layer, reps),
               file=sys.stderr, flush=True)
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": S / step_s, "unit": "queries/s", "cores": min(S, threads), "kind": "oracle",
+    threads = int(os.environ.get("OMP_NUM_THREADS", host_cores()))
+    return {"value": S / step_s, "unit": "queries/s", "cores": min(S, threads, host_cores()), "kind": "oracle",
+            "host_cores": host_cores(),
             "sample": "%d of %d sequences, one decode step through all %d layers, each layer's oracle calls "
-                      "repeated %s times on the same inputs (%.1f s of oracle time)"
-                      % (S, st.B, st.layers, "/".join(map(str, reps_all)), total)}
+                      "repeated %s times on the same inputs (%.1f s of oracle time); the oracle runs one "
+                      "OpenMP thread per (sequence, query)" % (S, st.B, st.layers, "/".join(map(str, reps_all)), total)}
+
+
+def host_cores():
+    """Host cores this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
 
 
 def _oracle_layer(st, sub, S, full, sd, si, li, kind, min_seconds, max_reps):
@@ -337,7 +432,7 @@ def _oracle_layer(st, sub, S, full, sd, si, li, kind, min_seconds, max_reps):
     import numpy as np
 
     import oracle
-    L = st.L_csa if kind == "csa" else st.L_hca
+    L = {"csa": st.L_csa, "hca": st.L_hca, "win": 0}[kind]
     seq_rows = lambda b, n: np.arange(b * n, (b + 1) * n)  # noqa: E731
     q = np.stack([full((st.B, 1, st.H, st.d), "q", sd, li, rows=np.arange(b * st.H, (b + 1) * st.H))
                   for b in range(S)]).reshape(S, 1, st.H, st.d)
@@ -349,7 +444,8 @@ def _oracle_layer(st, sub, S, full, sd, si, li, kind, min_seconds, max_reps):
     total, reps = 0.0, 0
     if kind == "csa":
         m = st.m_csa
-        p0 = (st.csa_new - 1) * m
+        e = st.t // m  # the entry the decoded token completes (when it does)
+        p0 = (e - 1) * m
         raws = {}
         for s, D, sc in (("k", st.d, sd), ("v", st.d, sd), ("idx", st.dI, si)):
             xa = "k" if s == "k" else ("v" if s == "v" else "k_idx")
@@ -367,8 +463,8 @@ def _oracle_layer(st, sub, S, full, sd, si, li, kind, min_seconds, max_reps):
             t0 = time.perf_counter()
             for s in ("k", "v", "idx"):
                 xa, za, xb, zb = raws[s]
-                oracle.compress(xa, za, m, x_b=xb, z_b=zb, n=st.n_ctx, p0=p0, e0=st.csa_new,
-                                e1=st.csa_new + 1)
+                if st.emits(m):
+                    oracle.compress(xa, za, m, x_b=xb, z_b=zb, n=st.n_ctx, p0=p0, e0=e, e1=e + 1)
             idx, _ = oracle.index_topk(qi, ki, m, st.k, w=wi, n_ctx=st.n_ctx)
             total += time.perf_counter() - t0
             if kc is None:  # gather only the selected rows of the compressed K/V caches (not timed)
@@ -383,18 +479,22 @@ def _oracle_layer(st, sub, S, full, sd, si, li, kind, min_seconds, max_reps):
             t0 = time.perf_counter()
             oracle.sparse_attn(q, kc, vc, loc, kr, vr, st.W, sink=sink, n_ctx=st.n_ctx)
             total += time.perf_counter() - t0
-    else:
+    else:  # HCA, or window only (no compressed entries)
         m = st.m_hca
-        p0 = st.hca_new * m
+        e = st.t // m
+        p0 = e * m
         raws = [raw_rows(sub, nm, li, p0, m, st.d, "cpu", scl).double().numpy()
-                for nm, scl in (("k", sd), ("z_k", 0.5), ("v", sd), ("z_v", 0.5))]
-        kc = np.stack([full((st.B, L, st.d), "kc", sd, li, rows=seq_rows(b, L)) for b in range(S)])
-        vc = np.stack([full((st.B, L, st.d), "vc", sd, li, rows=seq_rows(b, L)) for b in range(S)])
+                for nm, scl in (("k", sd), ("z_k", 0.5), ("v", sd), ("z_v", 0.5))] if kind == "hca" else None
+        kc = np.stack([full((st.B, L, st.d), "kc", sd, li, rows=seq_rows(b, L)) for b in range(S)]) if L else \
+            np.zeros((S, 0, st.d))
+        vc = np.stack([full((st.B, L, st.d), "vc", sd, li, rows=seq_rows(b, L)) for b in range(S)]) if L else \
+            np.zeros((S, 0, st.d))
         while reps < max_reps and (reps == 0 or total < min_seconds):
             reps += 1
             t0 = time.perf_counter()
-            oracle.compress(raws[0], raws[1], m, n=st.n_ctx, p0=p0, e0=st.hca_new, e1=st.hca_new + 1)
-            oracle.compress(raws[2], raws[3], m, n=st.n_ctx, p0=p0, e0=st.hca_new, e1=st.hca_new + 1)
+            if raws is not None and st.emits(m):
+                oracle.compress(raws[0], raws[1], m, n=st.n_ctx, p0=p0, e0=e, e1=e + 1)
+                oracle.compress(raws[2], raws[3], m, n=st.n_ctx, p0=p0, e0=e, e1=e + 1)
             oracle.dense_attn(q, kc, vc, m, kr, vr, st.W, sink=sink, n_ctx=st.n_ctx)
             total += time.perf_counter() - t0
     return total, reps
@@ -507,7 +607,7 @@ def prefill_index_topk(queries: int = 4096, reps: int = 3):
     qi = syn.fill_(torch.empty((1, queries, HI, dI), dtype=torch.bfloat16, device="cuda"), 4, syn.TID["q_idx"],
                    scale=dI ** -0.5)
     wi = syn.fill_(torch.empty((1, queries, HI), device="cuda"), 4, syn.TID["w_idx"], scale=HI ** -0.5)
-    ws = torch.empty(csa.csa_index_topk_workspace(1, queries, L, HI, k), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(csa.csa_index_topk_workspace(1, queries, L, HI, k), dtype=torch.uint8, device="cuda")
     idx = torch.empty((1, queries, k), dtype=torch.int32, device="cuda")
 
     def call():
@@ -535,33 +635,57 @@ def prefill_index_topk(queries: int = 4096, reps: int = 3):
                     "(about a fifth of the time)"}
 
 
-def decode_step_b1(steps: int, warmup: int):
-    """The same bf16 8-layer step for one sequence (B = 1): the latency-bound
-    end of the decode workload, reported beside the B = 16 headline."""
-    st = Stack(B=1)
-    state = GpuState(st)
+def timed_steps(run, steps, warmup):
+    """Average ms per call of run() over `steps` calls after `warmup`."""
     for _ in range(warmup):
-        state.step()
+        run()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(steps):
-        state.step()
+        run()
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    return e0.elapsed_time(e1) / steps
+
+
+def decode_step_b1(steps: int, warmup: int, schedule: str = "alternate"):
+    """The same bf16 8-layer step for one sequence (B = 1): the latency-bound
+    end of the decode workload, reported beside the B = 16 headline, eager
+    and as one HIP-graph replay per step."""
+    st = Stack(B=1, schedule=schedule)
+    state = GpuState(st)
+    ms = timed_steps(state.step, steps, warmup)
+    replay = state.capture()
+    ms_graph = timed_steps(replay, steps, warmup)
     ev = {}
     for _ in range(3):
         state.step(ev)
     torch.cuda.synchronize()
     per_call = event_means_ms(ev)
-    del state
+    del state, replay
     torch.cuda.empty_cache()
-    return {"ms_per_step": ms, "tokens_per_s": 1.0 / (ms * 1e-3),
+    best = min(ms, ms_graph)
+    return {"ms_per_step": ms, "graph_ms_per_step": ms_graph, "tokens_per_s": 1.0 / (best * 1e-3),
             "algorithmic_bytes_per_step": st.step_bytes(),
-            "achieved_GBps": st.step_bytes() / (ms * 1e-3) / 1e9, "per_call_ms": per_call,
-            "note": "one query per call: bound by launch latency and by the stand-alone top-k (with one "
-                    "query row the single-pass scan-and-select plan does not apply)"}
+            "achieved_GBps": st.step_bytes() / (best * 1e-3) / 1e9, "per_call_ms": per_call,
+            "note": "one query per call: bound by the latency of the calls' kernels; the graph replay submits the "
+                    "whole step (both streams) at once"}
+
+
+def schedules_b16(steps: int, warmup: int, B: int):
+    """The step under the V4-Flash- and V4-Pro-style layer schedules."""
+    res = {}
+    for sch in ("flash", "pro"):
+        st = Stack(B=B, schedule=sch)
+        state = GpuState(st)
+        ms = timed_steps(state.step, steps, warmup)
+        del state
+        torch.cuda.empty_cache()
+        res[sch] = {"layers": st.kinds(), "ms_per_step": ms, "queries_per_s": st.B / (ms * 1e-3),
+                    "algorithmic_bytes_per_step": st.step_bytes(),
+                    "achieved_GBps": st.step_bytes() / (ms * 1e-3) / 1e9}
+    return res
 
 
 def index_topk_mxfp4(B: int, reps: int = 20):
@@ -579,7 +703,7 @@ def index_topk_mxfp4(B: int, reps: int = 20):
     q, kk = csa.MXFP4(qb, (B, 1, HI, dI)), csa.MXFP4(kb, (B, L, dI))
     w = syn.fill_(torch.empty((B, 1, HI), device="cuda"), SEED, syn.TID["w_idx"], scale=HI ** -0.5)
     idx = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
-    ws = torch.empty(csa.csa_index_topk_workspace(B, 1, L, HI, k), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(csa.csa_index_topk_workspace(B, 1, L, HI, k), dtype=torch.uint8, device="cuda")
 
     def call():
         csa.csa_index_topk(q, kk, m, k, w_idx=w, n_ctx=st.n_ctx, idx=idx, ws=ws)
@@ -610,7 +734,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--batch", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=2)
+    ap.add_argument("--cpu-sample", type=int, default=0,
+                    help="sequences the CPU oracle decodes (0: one per host core, at most 16 and at most the batch)")
+    ap.add_argument("--schedule", choices=SCHEDULES, default="alternate",
+                    help="layer schedule of the headline stack (alternate CSA/HCA is the 1M configuration)")
+    ap.add_argument("--no-schedules", action="store_true", help="skip the flash / pro schedule measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle step until at least this much oracle time")
     ap.add_argument("--prefill-queries", type=int, default=16384,
@@ -634,7 +762,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         print("# calibration copy of %d bytes done" % args.copy_calibration, file=sys.stderr, flush=True)
-    st = Stack(B=args.batch)
+    st = Stack(B=args.batch, schedule=args.schedule)
     t_gen = time.perf_counter()
     state = GpuState(st)
     t_gen = time.perf_counter() - t_gen
@@ -689,8 +817,14 @@ def main():
 
     b1 = None
     if args.batch != 1 and not args.no_batch1:
-        b1 = decode_step_b1(args.steps, args.warmup)
-        print("# batch 1: %.3f ms/step" % b1["ms_per_step"], file=sys.stderr, flush=True)
+        b1 = decode_step_b1(args.steps, args.warmup, args.schedule)
+        print("# batch 1: %.3f ms/step eager, %.3f as a graph" % (b1["ms_per_step"], b1["graph_ms_per_step"]),
+              file=sys.stderr, flush=True)
+    sched = None
+    if not args.no_schedules:
+        sched = schedules_b16(args.steps, args.warmup, args.batch)
+        print("# schedules: " + ", ".join("%s %.3f ms/step" % (k, v["ms_per_step"]) for k, v in sched.items()),
+              file=sys.stderr, flush=True)
 
     prefill = None
     if args.prefill_queries > 0:
@@ -703,7 +837,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(st, args.cpu_sample, args.cpu_seconds)
+        sample = args.cpu_sample or min(16, host_cores(), st.B)
+        cpu = cpu_baseline(st, sample, args.cpu_seconds)
 
     line = {
         "metric": "CSA/HCA decode queries/s at 1M ctx + achieved HBM GB/s (% peak)",
@@ -721,7 +856,7 @@ def main():
         "config": {
             "workload": "csa_hca_stack8_decode_1M",
             "query": "one token of one sequence through all 8 layers",
-            "batch": st.B, "n_ctx": st.n_ctx, "layers": "4 CSA (two-path m=4) + 4 HCA (m=128), alternating",
+            "batch": st.B, "n_ctx": st.n_ctx, "schedule": st.schedule, "layers": ",".join(st.kinds()),
             "heads": st.H, "head_dim": st.d, "index_heads": st.HI, "index_dim": st.dI, "top_k": st.k,
             "window": st.W, "csa_entries": st.L_csa, "hca_entries": st.L_hca,
         },
@@ -737,6 +872,7 @@ def main():
         "prefill_sparse_attn": prefill,
         "fp8_storage": fp8,
         "decode_batch1": b1,
+        "schedules": sched,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

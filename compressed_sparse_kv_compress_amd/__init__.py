@@ -292,7 +292,7 @@ def csa_index_topk(q_idx, k_idx, m, k, *, w_idx=None, n_ctx, ws=None, idx=None, 
         out_score = torch.empty((B, T, k), dtype=torch.float32, device=q_idx.device)
     if ws is None:
         nb = max(16, csa_index_topk_workspace(B, T, L, HI, k))
-        ws = torch.empty(nb, dtype=torch.uint8, device=q_idx.device)
+        ws = torch.zeros(nb, dtype=torch.uint8, device=q_idx.device)
     args = (_ptr(q_idx), _ptr(w_idx), _ptr(k_idx), B, T, n_ctx, L, HI, dI, m, k, idx.data_ptr(), _ptr(out_score),
             ws.data_ptr(), ws.numel() * ws.element_size(), _dt(q_idx), _stream(q_idx.device))
     if layout is None:

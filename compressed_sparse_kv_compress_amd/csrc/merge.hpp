@@ -1,0 +1,281 @@
+// Per-row merge stages of the exact top-k, written for any workgroup size
+// (the stand-alone merge kernel runs them with 512 threads).
+//
+// Method: shareware.cn Hybrid Attention article, section 六 (score, then keep
+// the top-k entries); aimodeling.com news item, CSA paragraph (1024 per
+// query).  Equal scores (-0 == +0) go to the lower entry index; the kept
+// indices are written in ascending order, -1 padded.
+#pragma once
+#include "common.hpp"
+#include "kernels.hpp"
+#include "select.hpp"
+
+namespace csa {
+namespace mrg {
+
+constexpr int kStage = 2048;  // outputs up to this size are staged in LDS, then stored coalesced
+constexpr int kSlots = 16384;  // candidate slots one merge holds
+
+// A tile of up to THREADS * ITEMS scores staged in LDS: thread t owns entries
+// t*ITEMS .. t*ITEMS+ITEMS-1, stored with 4 pad words after every ITEMS
+// entries so that the owners' 16-byte reads of their own entries hit distinct
+// bank groups.
+template <int THREADS, int ITEMS>
+struct Tile {
+  static constexpr int kPitch = ITEMS + 4;
+  static constexpr int kFloats = THREADS * kPitch;
+  static __device__ __forceinline__ int pos(int e) { return e + 4 * (e / ITEMS); }
+
+  // Issue the coalesced 16-byte loads of scores [0, n) (entries at and past
+  // n are NaN); store() then puts them into LDS.
+  struct Loads {
+    f32x4 v[ITEMS / 4];
+  };
+  static __device__ __forceinline__ Loads load(const float* src, int n) {
+    Loads r;
+    const int tid = threadIdx.x;
+    const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+#pragma unroll
+    for (int q = 0; q < ITEMS / 4; ++q) {
+      const int e = 4 * (q * THREADS + tid);
+      if (vec && e + 4 <= n) {
+        r.v[q] = *reinterpret_cast<const f32x4*>(src + e);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float t = src[e + u < n ? e + u : 0];
+          r.v[q][u] = e + u < n ? t : __builtin_nanf("");
+        }
+      }
+    }
+    return r;
+  }
+  // Store the loads, barrier, and read this thread's own entries into x.
+  static __device__ __forceinline__ void store(const Loads& r, float* stage, float (&x)[ITEMS]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < ITEMS / 4; ++q) *reinterpret_cast<f32x4*>(stage + pos(4 * (q * THREADS + tid))) = r.v[q];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < ITEMS / 4; ++q) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stage + tid * kPitch + 4 * q);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[4 * q + u] = v[u];
+    }
+  }
+};
+
+// Visible entries of launch row `row` (positions from the end of its sequence).
+__device__ __forceinline__ int64_t row_visible(const TopkArgs& a, int64_t row) {
+  SeqLayout l;
+  l.lens = a.lens;
+  const int64_t tpos = seq_len(l, a.n_ctx, a.T, row / a.T) - a.T + row % a.T;
+  int64_t nv = tpos / a.m;
+  if (nv > a.L) nv = a.L;
+  return nv < 0 ? 0 : nv;
+}
+
+// Merge of one row's candidates by a THREADS-thread workgroup.
+template <int THREADS>
+struct Merge {
+  static constexpr int ITEMS = kSlots / THREADS;
+  static constexpr int SMAX = ITEMS <= 32 ? 16 : 24;  // survivors a thread keeps in registers
+  static constexpr int kWaves = THREADS / 64;
+  using T = Tile<THREADS, ITEMS>;
+  using F = sel::Filter<THREADS, ITEMS, SMAX>;
+  struct Shared {
+    typename F::Shared fs;
+    int32_t si[kStage + 64];  // 64 lane-private dump slots at the end
+    float sv[kStage + 64];
+    alignas(16) float stage[T::kFloats];
+    int wtot[kWaves];
+  };
+
+  // Merge from per-part short lists.  Part p's list holds, in index order,
+  // every entry of the part with a score >= lthr[p] (at least the part's
+  // lrank largest); lcnt[p] = -1 means no list.  U, the union of the lists in
+  // part (= index) order, has at most THREADS * UITEMS entries.  With theta_U
+  // the k-th largest of U (a subset of the row, so theta_U <= the row's k-th
+  // largest theta), an entry of the row's top-k has a score >= theta >=
+  // theta_U; when every lthr[p] <= theta_U that score is >= its part's
+  // threshold, so the entry is in U and the top-k of U is the row's.  Returns
+  // false (nothing written) when a list is missing, U holds fewer than k or
+  // more than THREADS * UITEMS entries, or some lthr[p] > theta_U.  nparts <=
+  // THREADS.  U is staged in `stage` (values, then indices).
+  template <int UITEMS>
+  static __device__ bool lists(int k, int nparts, const float* lval, const int32_t* lidx, const int32_t* lcnt,
+                               const float* lthr, int64_t lcap, Shared& sh, int32_t* o, float* os) {
+    static_assert(2 * THREADS * UITEMS <= T::kFloats, "the union fits the stage");
+    using USel = sel::Select<THREADS, UITEMS>;
+    constexpr int kU = THREADS * UITEMS;
+    if (k > kStage / 2) return false;  // the output is staged in half of si (past the list offsets)
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lc = tid < nparts ? lcnt[tid] : 0;
+    const float lt = tid < nparts ? lthr[tid] : -INFINITY;
+    // per wave: any missing list, the lists' total, the largest threshold
+    const uint32_t neg = static_cast<uint32_t>(__popcll(__ballot(lc < 0)));
+    const uint32_t cnt = static_cast<uint32_t>(lc > 0 ? lc : 0);
+    const uint32_t incl = sel::wave_incl_scan(cnt);
+    const float vmax_w = wave_max(lt);
+    uint32_t* uoff = reinterpret_cast<uint32_t*>(sh.si);  // list offsets in U (<= THREADS parts)
+    int32_t* ucnt = sh.si + THREADS;                        // list lengths
+    if (sel::lane_id() == 63) {
+      sh.fs.wsum[wave] = incl;
+      sh.fs.red[0][wave] = vmax_w;
+      sh.fs.core.red[0][wave] = neg;
+    }
+    __syncthreads();
+    uint32_t before = 0, total = 0, nneg = 0;
+    float vmax = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      before += w < wave ? sh.fs.wsum[w] : 0u;
+      total += sh.fs.wsum[w];
+      nneg += sh.fs.core.red[0][w];
+      vmax = fmaxf(vmax, sh.fs.red[0][w]);
+    }
+    if (nneg != 0 || total < static_cast<uint32_t>(k) || total > static_cast<uint32_t>(kU)) {
+      __syncthreads();  // the LDS reads above are done before the caller reuses it
+      return false;
+    }
+    if (tid < nparts) {
+      uoff[tid] = before + incl - cnt;
+      ucnt[tid] = static_cast<int32_t>(cnt);
+    }
+    __syncthreads();
+    // U into LDS: every (part, slot) pair, slots past a list's length
+    // skipped; each batch issues all its loads before any store.
+    float* uval = sh.stage;
+    int32_t* uidx = reinterpret_cast<int32_t*>(sh.stage + kU);
+    const int64_t nslots = static_cast<int64_t>(nparts) * lcap;
+    constexpr int kBatch = 16;
+    for (int64_t i0 = 0; i0 < nslots; i0 += static_cast<int64_t>(THREADS) * kBatch) {
+      float tv[kBatch];
+      int32_t tx[kBatch];
+#pragma unroll
+      for (int r = 0; r < kBatch; ++r) {
+        const int64_t i = i0 + r * THREADS + tid;
+        const int64_t ic = i < nslots ? i : 0;
+        tv[r] = lval[ic];
+        tx[r] = lidx[ic];
+      }
+#pragma unroll
+      for (int r = 0; r < kBatch; ++r) {
+        const int64_t i = i0 + r * THREADS + tid;
+        const int p = static_cast<int>(i / lcap);
+        const int j = static_cast<int>(i - static_cast<int64_t>(p) * lcap);
+        if (i < nslots && j < ucnt[p]) {
+          uval[uoff[p] + j] = tv[r];
+          uidx[uoff[p] + j] = tx[r];
+        }
+      }
+    }
+    USel::zero(sh.fs.core);
+    __syncthreads();
+    uint32_t keys[UITEMS];
+    typename USel::Mask vm = 0;
+#pragma unroll
+    for (int j = 0; j < UITEMS; ++j) {
+      const uint32_t u = static_cast<uint32_t>(tid * UITEMS + j);
+      keys[j] = float_key(uval[u < total ? u : 0]);
+      vm |= static_cast<typename USel::Mask>(u < total) << j;
+    }
+    uint32_t thr, take;
+    USel::radix_select(keys, vm, static_cast<uint32_t>(k), sh.fs.core, &thr, &take);
+    if (vmax > key_float(thr)) {  // uniform: some part's list may miss row top-k entries
+      __syncthreads();
+      return false;
+    }
+    uint32_t bg = 0, be = 0;
+    // outputs staged in sh.sv / sh.si past the list offsets (k <= kStage / 2 here)
+    USel::compact(keys, vm, thr, take, sh.fs.core, &bg, &be, [&](int j, uint32_t pos) {
+      const int u = tid * UITEMS + j;
+      sh.sv[pos] = uval[u];
+      sh.si[pos + kStage / 2] = uidx[u];
+    });
+    for (int i = tid; i < k; i += THREADS) {
+      o[i] = sh.si[i + kStage / 2];
+      if (os) os[i] = sh.sv[i];
+    }
+    return true;
+  }
+
+  // Merge over nparts * cap <= kSlots candidate slots (part order = index
+  // order; slots past a part's count hold NaN).  Every valid candidate is
+  // kept when there are at most k of them.
+  static __device__ void full(int k, int nparts, int cap, const float* rv, const int32_t* ri, const int32_t* rc,
+                              Shared& sh, int32_t* o, float* os) {
+    const int tid = threadIdx.x;
+    const int ns = nparts * cap;
+    // The candidate loads go out first; the part counts are summed meanwhile.
+    const typename T::Loads ld = T::load(rv, ns);
+    F::zero(sh.fs);
+    const int pc = static_cast<int>(sel::wave_sum(static_cast<uint32_t>(tid < nparts ? rc[tid] : 0)));
+    if (sel::lane_id() == 0) sh.wtot[tid >> 6] = pc;
+    float v[ITEMS];
+    T::store(ld, sh.stage, v);  // its barrier also publishes wtot
+    int total = 0;  // valid candidates of the row
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) total += sh.wtot[w];
+    const int s0 = tid * ITEMS;
+    if (total <= k) {  // every valid candidate is kept, in slot order; -1 padding after them
+      for (int i = total + tid; i < k; i += THREADS) {
+        o[i] = -1;
+        if (os) os[i] = -INFINITY;
+      }
+      uint32_t c = 0;
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j) c += v[j] == v[j];
+      const uint32_t incl = sel::wave_incl_scan(c);
+      if (sel::lane_id() == 63) sh.fs.core.wsum[tid >> 6] = incl;
+      __syncthreads();
+      uint32_t pos = incl - c;
+      for (int w = 0; w < (tid >> 6); ++w) pos += sh.fs.core.wsum[w];
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j)
+        if (v[j] == v[j]) {
+          o[pos] = ri[s0 + j];
+          if (os) os[pos] = v[j];
+          ++pos;
+        }
+      return;
+    }
+    const uint32_t uk = static_cast<uint32_t>(k);
+    float vmin, vmax;
+    F::block_range(v, sh.fs, &vmin, &vmax);
+    auto src = [&](uint32_t e) { return sh.stage[T::pos(static_cast<int>(e))]; };
+    if (k <= kStage) {  // stage the kept candidates in LDS, then store coalesced
+      F::run(
+          v, src, static_cast<uint32_t>(total), uk, vmin, vmax, sh.fs,
+          [&](uint32_t pos, float val, uint32_t e) {
+            const uint32_t p = pos != sel::kNoSlot ? pos : kStage + sel::lane_id();
+            sh.si[p] = static_cast<int32_t>(e);
+            sh.sv[p] = val;
+          },
+          [&](int j, uint32_t pos) {
+            sh.si[pos] = s0 + j;
+            sh.sv[pos] = sh.stage[T::pos(s0 + j)];
+          });
+      for (int i = tid; i < k; i += THREADS) {
+        o[i] = ri[sh.si[i]];
+        if (os) os[i] = sh.sv[i];
+      }
+    } else {
+      F::run(
+          v, src, static_cast<uint32_t>(total), uk, vmin, vmax, sh.fs,
+          [&](uint32_t pos, float val, uint32_t e) {
+            if (pos == sel::kNoSlot) return;
+            o[pos] = ri[e];
+            if (os) os[pos] = val;
+          },
+          [&](int j, uint32_t pos) {
+            o[pos] = ri[s0 + j];
+            if (os) os[pos] = sh.stage[T::pos(s0 + j)];
+          });
+    }
+  }
+};
+
+}  // namespace mrg
+}  // namespace csa

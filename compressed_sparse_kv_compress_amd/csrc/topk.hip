@@ -27,6 +27,7 @@
 // exact without a sort.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "merge.hpp"
 #include "select.hpp"
 
 namespace csa {
@@ -37,61 +38,13 @@ constexpr int kItems = 32;
 constexpr int64_t kPart = static_cast<int64_t>(kThreads) * kItems;  // 16384
 constexpr int kBins = sel::kBins;
 constexpr int kMaxMergeParts = 256;  // one part count per merge thread
-constexpr int kStage = 2048;         // outputs up to this size are staged in LDS, then stored coalesced
+constexpr int kStage = mrg::kStage;  // outputs up to this size are staged in LDS, then stored coalesced
 using Sel = sel::Select<kThreads, kItems>;
 using Filt = sel::Filter<kThreads, kItems, 16>;
 using sel::lane_id;
 using sel::wave_incl_scan;
 
-// A tile of up to 16384 scores staged in LDS: thread t of a THREADS-thread
-// workgroup owns entries t*ITEMS .. t*ITEMS+ITEMS-1, stored with 4 pad words
-// after every ITEMS entries so that the owners' 16-byte reads of their own
-// entries hit distinct bank groups.
-template <int THREADS, int ITEMS>
-struct Tile {
-  static constexpr int kPitch = ITEMS + 4;
-  static constexpr int kFloats = THREADS * kPitch;
-  static __device__ __forceinline__ int pos(int e) { return e + 4 * (e / ITEMS); }
-
-  // Issue the coalesced 16-byte loads of scores [0, n) (entries at and past
-  // n are NaN); store() then puts them into LDS.
-  struct Loads {
-    f32x4 v[ITEMS / 4];
-  };
-  static __device__ __forceinline__ Loads load(const float* src, int n) {
-    Loads r;
-    const int tid = threadIdx.x;
-    const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
-#pragma unroll
-    for (int q = 0; q < ITEMS / 4; ++q) {
-      const int e = 4 * (q * THREADS + tid);
-      if (vec && e + 4 <= n) {
-        r.v[q] = *reinterpret_cast<const f32x4*>(src + e);
-      } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float t = src[e + u < n ? e + u : 0];
-          r.v[q][u] = e + u < n ? t : __builtin_nanf("");
-        }
-      }
-    }
-    return r;
-  }
-  // Store the loads, barrier, and read this thread's own entries into x.
-  static __device__ __forceinline__ void store(const Loads& r, float* stage, float (&x)[ITEMS]) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int q = 0; q < ITEMS / 4; ++q) *reinterpret_cast<f32x4*>(stage + pos(4 * (q * THREADS + tid))) = r.v[q];
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < ITEMS / 4; ++q) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(stage + tid * kPitch + 4 * q);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) x[4 * q + u] = v[u];
-    }
-  }
-};
-using PartTile = Tile<kThreads, kItems>;
+using PartTile = mrg::Tile<kThreads, kItems>;
 
 struct Shared {
   Filt::Shared fs;
@@ -103,27 +56,9 @@ struct Shared {
 // The merge: 512 threads, 32 candidate slots each (1024 x 16 measured slower:
 // more waves per barrier, no less latency per phase).
 constexpr int kMThreads = 512;
-constexpr int kMItems = 32;
-static_assert(kMThreads * kMItems == kPart, "merge tile");
-using MergeTile = Tile<kMThreads, kMItems>;
-using MFilt = sel::Filter<kMThreads, kMItems, 16>;
-struct MShared {
-  MFilt::Shared fs;
-  int32_t si[kStage + 64];  // 64 lane-private dump slots at the end
-  float sv[kStage + 64];
-  alignas(16) float stage[MergeTile::kFloats];
-  int wtot[kMThreads / 64];
-};
-
-__device__ __forceinline__ int64_t row_visible(const TopkArgs& a, int64_t row) {
-  SeqLayout l;
-  l.lens = a.lens;
-  const int64_t tpos = seq_len(l, a.n_ctx, a.T, row / a.T) - a.T + row % a.T;
-  int64_t nv = tpos / a.m;
-  if (nv > a.L) nv = a.L;
-  return nv < 0 ? 0 : nv;
-}
-
+using Merge = mrg::Merge<kMThreads>;
+static_assert(Merge::ITEMS * kMThreads == kPart, "merge tile");
+using mrg::row_visible;
 
 // Stage 1: per-part local selection.
 __global__ __launch_bounds__(kThreads) void topk_part_kernel(TopkArgs a, int64_t nparts, int64_t cap,
@@ -210,200 +145,22 @@ __device__ __forceinline__ bool merge_trivial(const TopkArgs& a, int64_t lrow) {
   return true;
 }
 
-// Merge from the compact lists when they are enough.  Every part's list
-// holds all its candidates >= V_p (its smallest listed score, at most its
-// lrank-th largest); U is their union, in index order.  With theta_U the k-th largest
-// of U (a subset of the row, so theta_U <= the row's k-th largest theta), an
-// entry of the row's top-k has a score >= theta >= theta_U; when every V_p <=
-// theta_U that score is >= its part's V_p, so the entry is in U and the
-// top-k of U is the row's.  Returns false (nothing written) when a list is
-// missing or too long, U has fewer than k entries, or some V_p > theta_U.
-constexpr int kUItems = kMergeUnion / kMThreads;  // 8
-using USel = sel::Select<kMThreads, kUItems>;
-static_assert(sizeof(float) * kMergeUnion * 2 <= sizeof(float) * MergeTile::kFloats, "the union fits the stage");
-
-__device__ __forceinline__ bool merge_compact(const TopkArgs& a, int64_t lrow, int nparts, const IndexCandidates& c,
-                                              MShared& sh, int32_t* o, float* os) {
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  // The staging below gives each list kMThreads / nparts threads of
-  // kMergeUnion / kMThreads entries each.
-  if (c.lcap > static_cast<int64_t>(kMergeUnion / kMThreads) * (kMThreads / nparts)) return false;
-  const int64_t unit0 = lrow * nparts;
-  const int lc = tid < nparts ? c.lcnt[unit0 + tid] : 0;
-  const float lt = tid < nparts ? c.lthr[unit0 + tid] : -INFINITY;
-  // per wave: any missing list, the lists' total, the largest V_p
-  const uint32_t neg = static_cast<uint32_t>(__popcll(__ballot(lc < 0)));
-  const uint32_t cnt = static_cast<uint32_t>(lc > 0 ? lc : 0);
-  const uint32_t incl = wave_incl_scan(cnt);
-  const float vmax_w = wave_max(lt);
-  uint32_t* uoff = reinterpret_cast<uint32_t*>(sh.si);  // list offsets in U (<= 256 parts)
-  if (sel::lane_id() == 63) {
-    sh.fs.wsum[wave] = incl;
-    sh.fs.red[0][wave] = vmax_w;
-    sh.fs.core.red[0][wave] = neg;
-  }
-  __syncthreads();
-  uint32_t before = 0, total = 0, nneg = 0;
-  float vmax = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kMThreads / 64; ++w) {
-    before += w < wave ? sh.fs.wsum[w] : 0u;
-    total += sh.fs.wsum[w];
-    nneg += sh.fs.core.red[0][w];
-    vmax = fmaxf(vmax, sh.fs.red[0][w]);
-  }
-  if (nneg != 0 || total < static_cast<uint32_t>(a.k) || total > static_cast<uint32_t>(kMergeUnion)) {
-    __syncthreads();  // the LDS read above is done before the full merge reuses it
-    return false;
-  }
-  if (tid < nparts) uoff[tid] = before + incl - cnt;
-  __syncthreads();
-  // U into LDS (values, then indices): kMThreads / nparts threads per list,
-  // all loads issued before any store (one memory round trip).
-  float* uval = sh.stage;
-  int32_t* uidx = reinterpret_cast<int32_t*>(sh.stage + kMergeUnion);
-  {
-    constexpr int kR = kMergeUnion / kMThreads;  // entries per thread: lcap * nparts <= kMergeUnion
-    const int tpp = kMThreads / nparts;          // >= 2 (nparts <= 256)
-    const int p = tid / tpp, li = tid % tpp;
-    const int n = p < nparts ? c.lcnt[unit0 + p] : 0;
-    const float* lvp = c.lval + (unit0 + (p < nparts ? p : 0)) * c.lcap;
-    const int32_t* lip = c.lidx + (unit0 + (p < nparts ? p : 0)) * c.lcap;
-    float tv[kR];
-    int32_t tx[kR];
-#pragma unroll
-    for (int r = 0; r < kR; ++r) {
-      const int i = li + r * tpp;
-      const int ic = i < n ? i : 0;  // in range: lcap >= 1
-      tv[r] = lvp[ic];
-      tx[r] = lip[ic];
-    }
-    const uint32_t off = p < nparts ? uoff[p] : 0u;
-#pragma unroll
-    for (int r = 0; r < kR; ++r) {
-      const int i = li + r * tpp;
-      if (i < n) {
-        uval[off + i] = tv[r];
-        uidx[off + i] = tx[r];
-      }
-    }
-  }
-  USel::zero(sh.fs.core);
-  __syncthreads();
-  uint32_t keys[kUItems];
-  uint32_t vm = 0;
-#pragma unroll
-  for (int j = 0; j < kUItems; ++j) {
-    const uint32_t u = static_cast<uint32_t>(tid * kUItems + j);
-    keys[j] = float_key(uval[u < total ? u : 0]);
-    vm |= static_cast<uint32_t>(u < total) << j;
-  }
-  uint32_t thr, take;
-  USel::radix_select(keys, vm, static_cast<uint32_t>(a.k), sh.fs.core, &thr, &take);
-  if (vmax > key_float(thr)) {  // uniform: some part's list may miss row top-k entries
-    __syncthreads();
-    return false;
-  }
-  uint32_t bg = 0, be = 0;
-  USel::compact(keys, vm, thr, take, sh.fs.core, &bg, &be, [&](int j, uint32_t pos) {
-    const int u = tid * kUItems + j;
-    sh.sv[pos] = uval[u];
-    sh.si[pos + kStage / 2] = uidx[u];  // past the list offsets
-  });
-  for (int i = tid; i < a.k; i += kMThreads) {
-    o[i] = sh.si[i + kStage / 2];
-    if (os) os[i] = sh.sv[i];
-  }
-  return true;
-}
-
-// Fast merge: nparts * cap <= 16384 slots and nparts <= 256.  The candidate
-// values are staged in LDS with coalesced loads and thread t holds slots
-// 32t .. 32t+31; slots without a candidate hold NaN.
+// Fast merge: nparts * cap <= 16384 slots and nparts <= 256, from the
+// parts' compact lists when they settle the row, else from all candidates.
 __global__ __launch_bounds__(kMThreads) void topk_merge_kernel(TopkArgs a, int nparts, IndexCandidates c,
                                                                bool fused) {
-  __shared__ MShared sh;
+  __shared__ Merge::Shared sh;
   const int64_t lrow = blockIdx.x;
   if (!fused && merge_trivial(a, lrow)) return;
   int32_t* o = a.idx + lrow * a.k;
   float* os = a.out_score ? a.out_score + lrow * a.k : nullptr;
-  const int tid = threadIdx.x;
-  const int cap = static_cast<int>(c.cap);
-  const int ns = nparts * cap;
-  const float* rv = c.cval + lrow * ns;
-  const int32_t* ri = c.cidx + lrow * ns;
-  const int32_t* rc = c.ccnt + lrow * nparts;
-  if (c.lval && merge_compact(a, lrow, nparts, c, sh, o, os)) return;
-  // Candidate slots past their part's count hold NaN (written so by the part
-  // stage), as does everything past the last part: no validity test here.
-  // The candidate loads go out first; the part counts are summed meanwhile.
-  const MergeTile::Loads ld = MergeTile::load(rv, ns);
-  MFilt::zero(sh.fs);
-  static_assert(kMaxMergeParts <= kMThreads, "one part count per thread");
-  const int pc = static_cast<int>(sel::wave_sum(static_cast<uint32_t>(tid < nparts ? rc[tid] : 0)));
-  if (lane_id() == 0) sh.wtot[tid >> 6] = pc;
-  float v[kMItems];
-  MergeTile::store(ld, sh.stage, v);  // its barrier also publishes wtot
-  int total = 0;  // valid candidates of the row
-#pragma unroll
-  for (int w = 0; w < kMThreads / 64; ++w) total += sh.wtot[w];
-  const int s0 = tid * kMItems;
-  if (total <= a.k) {  // every valid candidate is kept, in slot order; -1 padding after them
-    for (int64_t i = total + tid; i < a.k; i += kMThreads) {
-      o[i] = -1;
-      if (os) os[i] = -INFINITY;
-    }
-    uint32_t c = 0;
-#pragma unroll
-    for (int j = 0; j < kMItems; ++j) c += v[j] == v[j];
-    const uint32_t incl = wave_incl_scan(c);
-    if (lane_id() == 63) sh.fs.core.wsum[tid >> 6] = incl;
-    __syncthreads();
-    uint32_t pos = incl - c;
-    for (int w = 0; w < (tid >> 6); ++w) pos += sh.fs.core.wsum[w];
-#pragma unroll
-    for (int j = 0; j < kMItems; ++j)
-      if (v[j] == v[j]) {
-        o[pos] = ri[s0 + j];
-        if (os) os[pos] = v[j];
-        ++pos;
-      }
+  const int k = static_cast<int>(a.k);
+  const int64_t u0 = lrow * nparts;
+  if (c.lval && Merge::lists<mrg::kSlots / 4 / kMThreads>(k, nparts, c.lval + u0 * c.lcap, c.lidx + u0 * c.lcap,
+                                                          c.lcnt + u0, c.lthr + u0, c.lcap, sh, o, os))
     return;
-  }
-  const uint32_t uk = static_cast<uint32_t>(a.k);
-  float vmin, vmax;
-  MFilt::block_range(v, sh.fs, &vmin, &vmax);
-  auto src = [&](uint32_t e) { return sh.stage[MergeTile::pos(static_cast<int>(e))]; };
-  if (a.k <= kStage) {  // stage the kept candidates in LDS, then store coalesced
-    MFilt::run(
-        v, src, static_cast<uint32_t>(total), uk, vmin, vmax, sh.fs,
-        [&](uint32_t pos, float val, uint32_t e) {
-          const uint32_t p = pos != sel::kNoSlot ? pos : kStage + lane_id();
-          sh.si[p] = static_cast<int32_t>(e);
-          sh.sv[p] = val;
-        },
-        [&](int j, uint32_t pos) {
-          sh.si[pos] = s0 + j;
-          sh.sv[pos] = sh.stage[MergeTile::pos(s0 + j)];
-        });
-    for (int i = tid; i < a.k; i += kMThreads) {
-      o[i] = ri[sh.si[i]];
-      if (os) os[i] = sh.sv[i];
-    }
-  } else {
-    MFilt::run(
-        v, src, static_cast<uint32_t>(total), uk, vmin, vmax, sh.fs,
-        [&](uint32_t pos, float val, uint32_t e) {
-          if (pos == sel::kNoSlot) return;
-          o[pos] = ri[e];
-          if (os) os[pos] = val;
-        },
-        [&](int j, uint32_t pos) {
-          o[pos] = ri[s0 + j];
-          if (os) os[pos] = sh.stage[MergeTile::pos(s0 + j)];
-        });
-  }
+  const int cap = static_cast<int>(c.cap);
+  Merge::full(k, nparts, cap, c.cval + u0 * cap, c.cidx + u0 * cap, c.ccnt + u0, sh, o, os);
 }
 
 // General merge (k >= 16384, or more than 256 parts): histogram passes over

@@ -274,37 +274,40 @@ def test_config4_csa_prefill_chunk(where):
 # config 5: the benchmark's 8-layer decode step (n = 1M, B = 16)
 # ---------------------------------------------------------------------------
 
-def test_config5_stack_step_sampled():
+def _check_stack_layers(st, state, b, layers):
+    """The given layers of a decode step of sequence b against the oracle: the
+    entry the decoded token completes (when it does) and each layer's output,
+    with the CSA attention checked twice (the GPU's selection, end to end)."""
     import bench
-    st = bench.Stack(B=16)
-    state = bench.GpuState(st)
-    state.step()
-    torch.cuda.synchronize()
     SEED, bf = bench.SEED, BF
     sd, si = st.d ** -0.5, st.dI ** -0.5
-    b = 11  # sampled sequence
-    sub = bench.Stack(B=b + 1)  # row numbering of sequences 0..b is the same as in the full batch
-    for li in (0, 1):  # one CSA and one HCA layer, checked end to end for sequence b
+    sub = bench.Stack(B=b + 1, n_ctx=st.n_ctx)  # row numbering of sequences 0..b is the same as in the full batch
+    t = st.t
+    for li in layers:
         lay = state.layers[li]
-        L = lay["kc"].shape[1]
+        kind = lay["kind"]
         q_c = c_rows((st.B, 1, st.H, st.d), np.arange(b * st.H, (b + 1) * st.H), SEED, "q", bf, sd,
                      layer=li).reshape(1, 1, st.H, st.d)
         sink_c = syn.make((st.H,), SEED, syn.TID["sink"], layer=li).double().numpy()
         kr_c = bench.raw_rows(sub, "kr", li, st.n_ctx - st.W, st.W, st.d, "cpu", sd)[b:].double().numpy()
         vr_c = bench.raw_rows(sub, "vr", li, st.n_ctx - st.W, st.W, st.d, "cpu", sd)[b:].double().numpy()
-        if lay["kind"] == "csa":
+        got_out = to_np(lay["out"][b:b + 1])
+        if kind == "csa":
             m = st.m_csa
-            p0 = lay["p0"]
-            # the entry completed by the new token (two-path), for K, V and the index keys
+            L = lay["kc"].shape[1]
+            e = t // m
+            assert st.emits(m)
+            # the entry completed by the decoded token (two-path), for K, V and the index keys
+            new = {}
             for s, cache, D, sc in (("k", "kc", st.d, sd), ("v", "vc", st.d, sd), ("idx", "ki", st.dI, si)):
-                xa = "k" if s == "k" else ("v" if s == "v" else "k_idx")
-                arrs = [bench.raw_rows(sub, nm, li, p0, 2 * m, D, "cpu", scl)[b:].double().numpy()
-                        for nm, scl in ((xa, sc), ("z_" + s, 0.5), ("xb_" + s, sc), ("zb_" + s, 0.5))]
-                want = oracle.compress(arrs[0], arrs[1], m, x_b=arrs[2], z_b=arrs[3], n=st.n_ctx, p0=p0,
-                                       e0=st.csa_new, e1=st.csa_new + 1)
-                assert max_abs(to_np(lay[cache][b:b + 1, st.csa_new:st.csa_new + 1]), want) <= BF16_TOL
+                arrs = [bench.raw_rows(sub, nm, li, (e - 1) * m, 2 * m, D, "cpu", scl)[b:].double().numpy()
+                        for nm, scl in zip(bench.STREAMS[s], (sc, 0.5, sc, 0.5))]
+                want = oracle.compress(arrs[0], arrs[1], m, x_b=arrs[2], z_b=arrs[3], n=st.n_ctx, p0=(e - 1) * m,
+                                       e0=e, e1=e + 1)
+                assert max_abs(to_np(lay[cache][b:b + 1, e:e + 1]), want) <= BF16_TOL
+                new[s] = round_to(want[0, 0], bf)
             ki_c = c_rows((st.B, L, st.dI), seq_rows(b, L), SEED, "kic", bf, si, layer=li)
-            ki_c[st.csa_new] = round_to(want[0, 0], bf)  # the step rewrote this (invisible) entry
+            ki_c[e] = new["idx"]  # rewritten by the step (not visible to the token)
             ki_c = ki_c.reshape(1, L, st.dI)
             qi_c = c_rows((st.B, 1, st.HI, st.dI), np.arange(b * st.HI, (b + 1) * st.HI), SEED, "q_idx", bf, si,
                           layer=li).reshape(1, 1, st.HI, st.dI)
@@ -321,29 +324,73 @@ def test_config5_stack_step_sampled():
             vc_c = np.zeros((1, L, st.d))
             kc_c[0, sel] = c_rows((st.B, L, st.d), b * L + sel, SEED, "kc", bf, sd, layer=li)
             vc_c[0, sel] = c_rows((st.B, L, st.d), b * L + sel, SEED, "vc", bf, sd, layer=li)
-            got_out = to_np(lay["out"][b:b + 1])
-            # attention checked twice: the oracle fed the GPU's selection, and end to end
             o_g, _ = oracle.sparse_attn(q_c, kc_c, vc_c, got_idx[None], kr_c, vr_c, st.W, sink=sink_c,
                                         n_ctx=st.n_ctx)
             assert max_abs(got_out, o_g) <= BF16_TOL
             o_c, _ = oracle.sparse_attn(q_c, kc_c, vc_c, idx_c, kr_c, vr_c, st.W, sink=sink_c, n_ctx=st.n_ctx)
             assert max_abs(got_out, o_c) <= BF16_TOL
-        else:
+        elif kind == "hca":
             m = st.m_hca
-            p0 = lay["p0"]
+            L = lay["kc"].shape[1]
             kc_c = c_rows((st.B, L, st.d), seq_rows(b, L), SEED, "kc", bf, sd, layer=li)
             vc_c = c_rows((st.B, L, st.d), seq_rows(b, L), SEED, "vc", bf, sd, layer=li)
-            for s, arr in (("k", kc_c), ("v", vc_c)):
-                x = bench.raw_rows(sub, s, li, p0, m, st.d, "cpu", sd)[b:].double().numpy()
-                z = bench.raw_rows(sub, "z_" + s, li, p0, m, st.d, "cpu", 0.5)[b:].double().numpy()
-                want = oracle.compress(x, z, m, n=st.n_ctx, p0=p0, e0=st.hca_new, e1=st.hca_new + 1)
-                got = to_np(lay["kc" if s == "k" else "vc"][b:b + 1, st.hca_new:st.hca_new + 1])
-                assert max_abs(got, want) <= BF16_TOL
-                arr[st.hca_new] = round_to(want[0, 0], bf)  # refreshed entry, as the GPU step wrote it
+            if st.emits(m):  # the entry the token completes is written (and is not visible to it)
+                e = t // m
+                for s, arr in (("k", kc_c), ("v", vc_c)):
+                    x = bench.raw_rows(sub, s, li, e * m, m, st.d, "cpu", sd)[b:].double().numpy()
+                    z = bench.raw_rows(sub, "z_" + s, li, e * m, m, st.d, "cpu", 0.5)[b:].double().numpy()
+                    want = oracle.compress(x, z, m, n=st.n_ctx, p0=e * m, e0=e, e1=e + 1)
+                    assert max_abs(to_np(lay["kc" if s == "k" else "vc"][b:b + 1, e:e + 1]), want) <= BF16_TOL
+                    arr[e] = round_to(want[0, 0], bf)
             o_c, _ = oracle.dense_attn(q_c, kc_c.reshape(1, L, st.d), vc_c.reshape(1, L, st.d), m, kr_c, vr_c,
                                        st.W, sink=sink_c, n_ctx=st.n_ctx)
-            assert max_abs(to_np(lay["out"][b:b + 1]), o_c) <= BF16_TOL
+            assert max_abs(got_out, o_c) <= BF16_TOL
+        else:  # window only
+            o_c, _ = oracle.dense_attn(q_c, np.zeros((1, 0, st.d)), np.zeros((1, 0, st.d)), st.m_hca, kr_c, vr_c,
+                                       st.W, sink=sink_c, n_ctx=st.n_ctx)
+            assert max_abs(got_out, o_c) <= BF16_TOL
+
+
+def test_config5_stack_step_sampled():
+    import bench
+    st = bench.Stack(B=16)
+    state = bench.GpuState(st)
+    state.step()
+    torch.cuda.synchronize()
+    _check_stack_layers(st, state, 11, (0, 1))  # one CSA and one HCA layer, sequence 11
     del state
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("schedule", ["alternate", "flash", "pro"])
+def test_batch1_step_every_layer_eager_and_graph(schedule):
+    """The batch-1 decode step at 1M tokens under each layer schedule: replayed
+    as one HIP graph it gives the eager step's outputs bit for bit (every
+    replay, with eager work between them), and every layer of it matches the
+    oracle."""
+    import bench
+    st = bench.Stack(B=1, schedule=schedule)
+    state = bench.GpuState(st)
+    state.step()
+    torch.cuda.synchronize()
+    eager = [(lay["out"].clone(), lay.get("idx", torch.zeros(1)).clone()) for lay in state.layers]
+    replay = state.capture()
+    for _ in range(3):
+        for lay in state.layers:
+            lay["out"].zero_()
+            if "idx" in lay:
+                lay["idx"].fill_(-5)
+        torch.cuda.synchronize()
+        replay()
+        torch.cuda.synchronize()
+        for (o, i), lay in zip(eager, state.layers):
+            assert torch.equal(o, lay["out"])
+            if "idx" in lay:
+                assert torch.equal(i, lay["idx"])
+        state.step()  # eager work between the replays
+        torch.cuda.synchronize()
+    _check_stack_layers(st, state, 0, range(st.layers))
+    del state, replay
     torch.cuda.empty_cache()
 
 

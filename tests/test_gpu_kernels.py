@@ -206,7 +206,7 @@ def test_index_topk_bit_exact_on_grid_inputs():
     want, _ = oracle.index_topk(q_c, k_c, m, k, n_ctx=n_ctx)
     assert np.array_equal(got, want)
     # a workspace holding one row at a time gives the same result
-    ws = torch.empty(csa.csa_index_topk_workspace(1, 1, L, HI, k), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(csa.csa_index_topk_workspace(1, 1, L, HI, k), dtype=torch.uint8, device="cuda")
     got2 = csa.csa_index_topk(q, kk, m, k, n_ctx=n_ctx, ws=ws).cpu().numpy()
     assert np.array_equal(got2, want)
 
@@ -222,7 +222,7 @@ def test_index_topk_one_row_workspace_general_merge(k):
     n_ctx = m * L
     q, q_c = both((B, T, HI, dI), 17, "q_idx", dtype=torch.bfloat16, kind="grid", scale=2.0 ** -4)
     kk, k_c = both((B, L, dI), 17, "k_idx", dtype=torch.bfloat16, kind="grid", scale=2.0 ** -4)
-    ws = torch.empty(csa.csa_index_topk_workspace(1, 1, L, HI, k), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(csa.csa_index_topk_workspace(1, 1, L, HI, k), dtype=torch.uint8, device="cuda")
     got = csa.csa_index_topk(q, kk, m, k, n_ctx=n_ctx, ws=ws).cpu().numpy()
     full = csa.csa_index_topk(q, kk, m, k, n_ctx=n_ctx).cpu().numpy()
     want, _ = oracle.index_topk(q_c, k_c, m, k, n_ctx=n_ctx)
