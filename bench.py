@@ -55,19 +55,19 @@ SEED = 5
 # paragraph): CSA and HCA alternate; V4-Flash-style stacks open with two
 # layers of sliding-window attention only, V4-Pro-style ones with two HCA
 # layers.
-SCHEDULES = ("alternate", "flash", "pro")
+SCHEDULES = ("alternate", "flash", "pro", "csa", "hca")
 
 
 class Stack:
     """Shapes of the 8-layer decode workload and its algorithmic bytes."""
 
-    def __init__(self, B=16, n_ctx=1_000_000, layers=8, eb=2, schedule="alternate"):
+    def __init__(self, B=16, n_ctx=1_000_000, layers=8, eb=2, schedule="alternate", W=128):
         assert schedule in SCHEDULES
         self.B, self.n_ctx, self.layers, self.schedule = B, n_ctx, layers, schedule
         self.eb = eb  # bytes per stored element: caches, window, indexer q/k, compression inputs
         self.H, self.d = 64, 512
         self.HI, self.dI = 64, 128
-        self.k, self.W = 1024, 128
+        self.k, self.W = 1024, W
         self.m_csa, self.m_hca = 4, 128
         self.L_csa = -(-n_ctx // self.m_csa)
         self.L_hca = -(-n_ctx // self.m_hca)
@@ -77,6 +77,8 @@ class Stack:
         self.scale = 1.0 / math.sqrt(self.d)
 
     def kinds(self):
+        if self.schedule in ("csa", "hca"):  # one layer kind throughout (the single-layer configurations)
+            return [self.schedule] * self.layers
         alt = ["csa" if i % 2 == 0 else "hca" for i in range(self.layers)]
         if self.schedule == "flash":
             return ["win", "win"] + alt[:self.layers - 2]
@@ -107,7 +109,7 @@ class Stack:
     def _window_bytes(self):
         """Attention's raw window rows, and csa_window_append of the new token."""
         e = self.eb
-        return self.W * self.d * 2 * e + 2 * 2 * self.d * e
+        return (self.W * self.d * 2 * e + 2 * 2 * self.d * e) if self.W else 0
 
     def csa_bytes(self):
         b = self.index_bytes()
@@ -196,10 +198,13 @@ class GpuState:
 
             lay["q"] = gen((B, 1, H, d), "q", d ** -0.5)
             lay["sink"] = gen((H,), "sink", 1.0, torch.float32)
-            lay["kr"] = ring_of(raw_rows(st, "kr", li, t - W + 1, W, d, device, sd, sto), t - W + 1)
-            lay["vr"] = ring_of(raw_rows(st, "vr", li, t - W + 1, W, d, device, sd, sto), t - W + 1)
-            lay["k_new"] = raw_rows(st, "kr", li, t, 1, d, device, sd, sto)[:, 0].contiguous()
-            lay["v_new"] = raw_rows(st, "vr", li, t, 1, d, device, sd, sto)[:, 0].contiguous()
+            if W:
+                lay["kr"] = ring_of(raw_rows(st, "kr", li, t - W + 1, W, d, device, sd, sto), t - W + 1)
+                lay["vr"] = ring_of(raw_rows(st, "vr", li, t - W + 1, W, d, device, sd, sto), t - W + 1)
+                lay["k_new"] = raw_rows(st, "kr", li, t, 1, d, device, sd, sto)[:, 0].contiguous()
+                lay["v_new"] = raw_rows(st, "vr", li, t, 1, d, device, sd, sto)[:, 0].contiguous()
+            else:
+                lay["kr"] = lay["vr"] = None
             lay["out"] = torch.empty((B, 1, H, d), dtype=bf, device=device)
             if kind == "csa":
                 m, S = st.m_csa, 2 * st.m_csa
@@ -271,7 +276,8 @@ class GpuState:
         with torch.cuda.stream(side):
             mark("window_append")
             for lay in self.layers:
-                csa.csa_window_append(lay["k_new"], lay["v_new"], lay["kr"], lay["vr"], self.pos)
+                if lay["kr"] is not None:
+                    csa.csa_window_append(lay["k_new"], lay["v_new"], lay["kr"], lay["vr"], self.pos)
             mark("window_append_end")
             windows = torch.cuda.Event()
             windows.record()
@@ -688,6 +694,73 @@ def schedules_b16(steps: int, warmup: int, B: int):
     return res
 
 
+def single_layer_decode(steps, warmup, kind, B, n_ctx, W):
+    """Decode of one layer (configurations 2 and 3): the same step machinery
+    with one CSA or one HCA layer; queries/s and algorithmic bytes."""
+    st = Stack(B=B, n_ctx=n_ctx, layers=1, schedule=kind, W=W)
+    state = GpuState(st)
+    ms = timed_steps(state.step, steps, warmup)
+    ev = {}
+    for _ in range(3):
+        state.step(ev)
+    torch.cuda.synchronize()
+    per_call = event_means_ms(ev)
+    del state
+    torch.cuda.empty_cache()
+    gbps = st.step_bytes() / (ms * 1e-3) / 1e9
+    return {"batch": B, "n_ctx": n_ctx, "layer": kind, "window": W, "ms_per_step": ms,
+            "queries_per_s": B / (ms * 1e-3), "algorithmic_bytes_per_step": st.step_bytes(), "achieved_GBps": gbps,
+            "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS, "per_call_ms": per_call}
+
+
+def bulk_compress(kind, B, n, reps=3):
+    """Bulk (prefill) compression of whole raw streams: CSA two-path (m = 4)
+    of the K, V and index-key streams of configuration 2, or HCA (m = 128) of
+    the K and V streams of configuration 3.  Bytes: every raw value and logit
+    read once, every entry written once."""
+    import compressed_sparse_kv_compress_amd as csa
+    m = 4 if kind == "csa" else 128
+    dims = (512, 512, 128) if kind == "csa" else (512, 512)
+    total_bytes, total_ms = 0, 0.0
+    for si, D in enumerate(dims):
+        arrs = [syn.fill_(torch.empty((B, n, D), dtype=torch.bfloat16, device="cuda"), 2, 30 + 4 * si + j,
+                          scale=0.5 if j % 2 else D ** -0.5) for j in range(4 if kind == "csa" else 2)]
+        L = -(-n // m)
+        out = torch.empty((B, L, D), dtype=torch.bfloat16, device="cuda")
+        if kind == "csa":
+            call = lambda: csa.csa_compress(arrs[0], arrs[1], m, x_b=arrs[2], z_b=arrs[3], out=out)  # noqa: E731
+        else:
+            call = lambda: csa.hca_compress(arrs[0], arrs[1], m, out=out)  # noqa: E731
+        total_ms += timed_steps(call, reps, 1)
+        total_bytes += sum(a.numel() for a in arrs) * 2 + out.numel() * 2
+        del arrs, out
+        torch.cuda.empty_cache()
+    gbps = total_bytes / (total_ms * 1e-3) / 1e9
+    return {"batch": B, "tokens": n, "m": m, "streams": len(dims), "ms": total_ms, "bytes": total_bytes,
+            "GBps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS,
+            "bytes_per_sequence": total_bytes / B}
+
+
+def measured_peaks():
+    """A plain 4 GiB device copy (read + write bytes / time) and a large bf16
+    GEMM through torch (hipBLASLt): the measured counterparts of the 8 TB/s
+    and 2.5 PFLOP/s spec peaks."""
+    src = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms = timed_steps(lambda: dst.copy_(src), 5, 2)
+    copy = 2 * src.numel() / (ms * 1e-3) / 1e9
+    del src, dst
+    a = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda")
+    b = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda")
+    ms = timed_steps(lambda: torch.matmul(a, b), 10, 3)
+    gemm = 2 * 8192 ** 3 / (ms * 1e-3) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_GBps": copy, "hbm_spec_GBps": HBM_PEAK_GBPS, "gemm_bf16_TFLOPs": gemm,
+            "mfma_bf16_spec_TFLOPs": 2500.0,
+            "note": "copy: torch device copy of 4 GiB; gemm: torch.matmul 8192^3 bf16"}
+
+
 def index_topk_mxfp4(B: int, reps: int = 20):
     """One csa_index_topk call of the CSA decode shape with q^I and k^I in
     MXFP4 (random E2M1 codes, E8M0 scales 2^-2 .. 2^2), timed over `reps`
@@ -741,8 +814,10 @@ def main():
     ap.add_argument("--no-schedules", action="store_true", help="skip the flash / pro schedule measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle step until at least this much oracle time")
-    ap.add_argument("--prefill-queries", type=int, default=16384,
-                    help="queries of the prefill sparse-attention measurement (0: skip)")
+    ap.add_argument("--prefill-queries", type=int, default=65536,
+                    help="queries of the prefill measurements (the CSA prefill chunk; 0: skip)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the single-layer decode configurations, bulk compression and the measured peaks")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-storage step")
     ap.add_argument("--no-batch1", action="store_true", help="skip the batch-1 decode step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -829,11 +904,25 @@ def main():
     prefill = None
     if args.prefill_queries > 0:
         prefill = prefill_sparse_attn(args.prefill_queries)
-        prefill["index_topk"] = prefill_index_topk()
+        prefill["index_topk"] = prefill_index_topk(args.prefill_queries)
         print("# prefill index + top-k: %.2f ms (%.0f TFLOP/s)" % (prefill["index_topk"]["ms_per_call"],
               prefill["index_topk"]["tflops"]), file=sys.stderr, flush=True)
         print("# prefill sparse attention: %.2f ms for %d queries (%.0f TFLOP/s)"
               % (prefill["ms_per_call"], prefill["queries"], prefill["tflops"]), file=sys.stderr, flush=True)
+
+    configs = None
+    if not args.no_configs:
+        configs = {"csa_decode_128k_b8": single_layer_decode(args.steps, args.warmup, "csa", 8, 131072, 128),
+                   "hca_decode_1m_b4": single_layer_decode(args.steps, args.warmup, "hca", 4, 1_000_000, 0)}
+        print("# config 2: %.4f ms/step; config 3: %.4f ms/step" % (configs["csa_decode_128k_b8"]["ms_per_step"],
+              configs["hca_decode_1m_b4"]["ms_per_step"]), file=sys.stderr, flush=True)
+        configs["csa_compress_bulk_128k_b8"] = bulk_compress("csa", 8, 131072)
+        configs["hca_compress_bulk_1m_b4"] = bulk_compress("hca", 4, 1_000_000)
+        print("# bulk compress: csa %.0f GB/s, hca %.0f GB/s" % (configs["csa_compress_bulk_128k_b8"]["GBps"],
+              configs["hca_compress_bulk_1m_b4"]["GBps"]), file=sys.stderr, flush=True)
+        configs["measured_peaks"] = measured_peaks()
+        print("# copy %.0f GB/s, bf16 gemm %.0f TFLOP/s" % (configs["measured_peaks"]["copy_GBps"],
+              configs["measured_peaks"]["gemm_bf16_TFLOPs"]), file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -873,6 +962,7 @@ def main():
         "fp8_storage": fp8,
         "decode_batch1": b1,
         "schedules": sched,
+        "configs": configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

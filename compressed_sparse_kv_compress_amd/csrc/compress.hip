@@ -112,10 +112,10 @@ struct BulkRows {
 // denominator, numerator) of VEC channels.  Logits are in log2 units.  rows
 // maps (stream, position) to the row holding it; the arithmetic does not
 // depend on where the rows are.
-template <Dt DT, typename Rows>
+template <typename IO, typename Rows>
 __device__ __forceinline__ void fold_range(const CompressArgs& a, const Cands& cd, int64_t lo, int64_t hi,
                                            const Rows& rows, int64_t c0, float* mx, float* den, float* acc) {
-  constexpr int VEC = Io<DT>::VEC;
+  constexpr int VEC = IO::VEC;
   for (int64_t i0 = lo; i0 < hi; i0 += kChunk) {
     // All 2 x kChunk loads are issued unconditionally (candidates past the
     // end re-read the last one and are masked below), so they are all in
@@ -130,8 +130,8 @@ __device__ __forceinline__ void fold_range(const CompressArgs& a, const Cands& c
       const void* zs;
       int64_t r;
       rows(from_b, u, &xs, &zs, &r);
-      Io<DT>::load(xs, r * a.D + c0, xv[i]);
-      Io<DT>::load(zs, r * a.D + c0, lv[i]);
+      IO::load(xs, r * a.D + c0, xv[i]);
+      IO::load(zs, r * a.D + c0, lv[i]);
     }
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
@@ -171,17 +171,34 @@ __device__ __forceinline__ void fold_range(const CompressArgs& a, const Cands& c
   }
 }
 
-// One entry j of one sequence for VEC channels from c0, with S thread
-// slices (S consecutive lanes) sharing its candidates; returns true in the
-// lane that holds the result (o).  S = 1: the thread folds every candidate.
-// S > 1: the candidates are split over the S slices, whose partial (max,
-// denominator, numerator) are merged with lane exchanges.  The slicing
-// depends only on the block size (S = 16 when m >= 32), so an entry comes
-// out bit for bit the same from a bulk launch and from a per-token append.
-template <Dt DT, int S, typename Rows>
+// Merge of two partial (max, denominator, numerator) states, the lower
+// candidate range first (both lanes of a pair evaluate this same expression,
+// so they agree bit for bit).
+__device__ __forceinline__ void merge_state(float ml, float dl, float al, float mh, float dh, float ah, float* m,
+                                            float* d, float* a) {
+  const float M = fmaxf(ml, mh);
+  const float fl = ml == -INFINITY ? 0.f : fast_exp2(ml - M);
+  const float fh = mh == -INFINITY ? 0.f : fast_exp2(mh - M);
+  *m = M;
+  *d = fmaf(dl, fl, dh * fh);
+  *a = fmaf(al, fl, ah * fh);
+}
+
+// Blocks of at least this many tokens fold on 16 lanes per channel group
+// when a launch has few entries (a decode-time refresh); bulk launches and
+// the per-token append fold every candidate in one thread, in candidate
+// order, so an appended entry equals the bulk one bit for bit.
+constexpr int kSplitM = 32;
+constexpr int kSplits = 16;
+
+// One entry j of one sequence for VEC channels from c0; returns true in the
+// lane that holds the result (o).  S = 1: the thread folds every candidate in
+// order.  S > 1: the candidates are split over S consecutive lanes whose
+// partial states are merged pairwise with lane exchanges.
+template <typename IO, int S, typename Rows>
 __device__ __forceinline__ bool compress_entry(const CompressArgs& a, const Rows& rows, bool live, int64_t j,
                                                int64_t c0, int slice, float* o) {
-  constexpr int VEC = Io<DT>::VEC;
+  constexpr int VEC = IO::VEC;
   float mx[VEC], den[VEC], acc[VEC];
 #pragma unroll
   for (int c = 0; c < VEC; ++c) { mx[c] = -INFINITY; den[c] = 0.f; acc[c] = 0.f; }
@@ -200,7 +217,7 @@ __device__ __forceinline__ bool compress_entry(const CompressArgs& a, const Rows
     lo = slice * per;
     hi = lo + per < total ? lo + per : total;
   }
-  if (live && lo < hi) fold_range<DT>(a, cd, lo, hi, rows, c0, mx, den, acc);
+  if (live && lo < hi) fold_range<IO>(a, cd, lo, hi, rows, c0, mx, den, acc);
 
   if (S > 1) {
     // Pairwise merges over the S lanes (xor distance 1, 2, ...): both lanes
@@ -214,15 +231,8 @@ __device__ __forceinline__ bool compress_entry(const CompressArgs& a, const Rows
         const float m2 = __shfl_xor(mx[c], off, 64);
         const float d2 = __shfl_xor(den[c], off, 64);
         const float a2 = __shfl_xor(acc[c], off, 64);
-        const float ml = low ? mx[c] : m2, mh = low ? m2 : mx[c];
-        const float dl = low ? den[c] : d2, dh = low ? d2 : den[c];
-        const float al = low ? acc[c] : a2, ah = low ? a2 : acc[c];
-        const float M = fmaxf(ml, mh);
-        const float fl = ml == -INFINITY ? 0.f : fast_exp2(ml - M);
-        const float fh = mh == -INFINITY ? 0.f : fast_exp2(mh - M);
-        mx[c] = M;
-        den[c] = fmaf(dl, fl, dh * fh);
-        acc[c] = fmaf(al, fl, ah * fh);
+        merge_state(low ? mx[c] : m2, low ? den[c] : d2, low ? acc[c] : a2, low ? m2 : mx[c], low ? d2 : den[c],
+                    low ? a2 : acc[c], &mx[c], &den[c], &acc[c]);
       }
     }
     if (slice != 0) return false;
@@ -236,10 +246,10 @@ __device__ __forceinline__ bool compress_entry(const CompressArgs& a, const Rows
 // Bulk: one (entry, 16-byte channel group) per S thread slices.  The kernel
 // uses no LDS, so its workgroups can share a CU with an LDS-heavy kernel
 // running beside it (the indexer scan holds almost all of a CU's LDS).
-template <Dt DT, int S>
-__global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
+template <typename IO, int S>
+__device__ __forceinline__ void compress_bulk(const CompressArgs& a) {
   static_assert(S >= 1 && S <= 64 && (S & (S - 1)) == 0, "slices: a power of two within a wavefront");
-  constexpr int VEC = Io<DT>::VEC;
+  constexpr int VEC = IO::VEC;
   constexpr int LANES = 256 / S;  // channel groups per workgroup
   const int slice = threadIdx.x % S;
   const int lane = threadIdx.x / S;
@@ -254,8 +264,13 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
   const int64_t b = tmp / ne;
   const int64_t c0 = cv * VEC;
   float o[VEC];
-  if (compress_entry<DT, S>(a, BulkRows{a, b * a.n_raw}, live, a.e0 + jj, c0, slice, o))
-    Io<DT>::store(a.out, (b * a.out_ld + jj) * a.D + c0, o);
+  if (compress_entry<IO, S>(a, BulkRows{a, b * a.n_raw}, live, a.e0 + jj, c0, slice, o))
+    IO::store(a.out, (b * a.out_ld + jj) * a.D + c0, o);
+}
+
+template <Dt DT, int S>
+__global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
+  compress_bulk<Io<DT>, S>(a);
 }
 
 // Per-token append: where the rows of sequence b live.  The new token
@@ -316,7 +331,7 @@ __global__ __launch_bounds__(256) void compress_append_kernel(CompressArgs a) {
   const int64_t j = ok ? p / a.m : 0;
   const bool emit = ok && (p + 1) % a.m == 0 && j < a.out_ld;
   float o[VEC];
-  if (compress_entry<DT, S>(a, AppendRows{a, b, p}, emit, j, c0, slice, o)) {
+  if (compress_entry<Io<DT>, S>(a, AppendRows{a, b, p}, emit, j, c0, slice, o)) {
     const int64_t row = a.lay.bt ? cache_row(a.lay, a.out_ld, b, j) : b * a.out_ld + j;
     Io<DT>::store(a.out, row * a.D + c0, o);
   }
@@ -328,12 +343,13 @@ hipError_t launch_compress(const CompressArgs& a, Dt dt, hipStream_t s) {
   const int vec = dt == kF32 ? 4 : 8;
   const int64_t total = a.B * (a.e1 - a.e0) * (a.D / vec);
   if (total == 0) return hipSuccess;
-  // Long blocks (m >= 32) spread each entry's tokens over 16 slices: the
-  // same fold order in bulk and in per-token appends.
-  const bool sliced = a.m >= 32;
-  const dim3 grid(static_cast<uint32_t>(sliced ? (total + 15) / 16 : (total + 255) / 256));
-#define CSA_COMPRESS_LAUNCH(DT_)                                                          \
-  if (sliced) hipLaunchKernelGGL((compress_kernel<DT_, 16>), grid, dim3(256), 0, s, a);  \
+  // Long blocks (m >= kSplitM): the split-range tree, in one thread per
+  // channel group (bulk: wavefronts read whole rows) or on 16 lanes per
+  // channel group when there are few entries (decode-time refresh).
+  const bool lanes = a.m >= kSplitM && total < 32768;
+  const dim3 grid(static_cast<uint32_t>(lanes ? (total + 15) / 16 : (total + 255) / 256));
+#define CSA_COMPRESS_LAUNCH(DT_)                                                             \
+  if (lanes) hipLaunchKernelGGL((compress_kernel<DT_, kSplits>), grid, dim3(256), 0, s, a);  \
   else hipLaunchKernelGGL((compress_kernel<DT_, 1>), grid, dim3(256), 0, s, a);
   switch (dt) {
     case kBF16: CSA_COMPRESS_LAUNCH(kBF16) break;
@@ -348,11 +364,8 @@ hipError_t launch_compress_append(const CompressArgs& a, Dt dt, hipStream_t s) {
   const int vec = dt == kF32 ? 4 : 8;
   const int64_t total = a.B * (a.D / vec);
   if (total == 0) return hipSuccess;
-  const bool sliced = a.m >= 32;
-  const dim3 grid(static_cast<uint32_t>(sliced ? (total + 15) / 16 : (total + 255) / 256));
-#define CSA_APPEND_LAUNCH(DT_)                                                                   \
-  if (sliced) hipLaunchKernelGGL((compress_append_kernel<DT_, 16>), grid, dim3(256), 0, s, a);  \
-  else hipLaunchKernelGGL((compress_append_kernel<DT_, 1>), grid, dim3(256), 0, s, a);
+  const dim3 grid(static_cast<uint32_t>((total + 255) / 256));
+#define CSA_APPEND_LAUNCH(DT_) hipLaunchKernelGGL((compress_append_kernel<DT_, 1>), grid, dim3(256), 0, s, a);
   switch (dt) {
     case kBF16: CSA_APPEND_LAUNCH(kBF16) break;
     case kFP8: CSA_APPEND_LAUNCH(kFP8) break;

@@ -155,8 +155,10 @@ csa_status_t hca_compress(const void* x, const void* z, const float* bias, void*
  * 改进三).  Token p = pos[b] of sequence b (x_a, z_a, and x_b, z_b in
  * two-path mode: [B][D] rows) is staged into the rings ring_xa, ring_za
  * (ring_xb, ring_zb) [B][S][D] at slot p % S; when p + 1 is a multiple of m
- * the entry p / m is compressed exactly as csa_compress does (same
- * arithmetic, same result bit for bit) from the staged rows of its block
+ * the entry p / m is compressed exactly as a bulk csa_compress launch does
+ * (every candidate folded in order: the same result bit for bit; launches of
+ * few entries with m >= 32 split each entry over 16 lanes instead, equal up
+ * to fp32 rounding) from the staged rows of its block
  * (and of the previous block through stream B) and written to the cache:
  * row b * L + p / m of cache [B][L][D], or its pool row through
  * layout->block_table.  S >= 2m in two-path mode, >= m otherwise; bias as
