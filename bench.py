@@ -358,7 +358,7 @@ def event_means_ms(ev):
 
 
 INDEX_TOPK_SOURCES = [os.path.join(ROOT, "compressed_sparse_kv_compress_amd", "csrc", f)
-                      for f in ("index.hip", "topk.hip", "select.hpp", "common.hpp")]
+                      for f in ("index.hip", "topk.hip", "select.hpp", "merge.hpp", "kernels.hpp", "common.hpp")]
 
 
 def source_hash(paths):
