@@ -343,9 +343,9 @@ hipError_t launch_compress(const CompressArgs& a, Dt dt, hipStream_t s) {
   const int vec = dt == kF32 ? 4 : 8;
   const int64_t total = a.B * (a.e1 - a.e0) * (a.D / vec);
   if (total == 0) return hipSuccess;
-  // Long blocks (m >= kSplitM): the split-range tree, in one thread per
-  // channel group (bulk: wavefronts read whole rows) or on 16 lanes per
-  // channel group when there are few entries (decode-time refresh).
+  // One thread per channel group folds every candidate in order (bulk:
+  // wavefronts read whole rows); long blocks (m >= kSplitM) in a launch of
+  // few entries (a decode-time refresh) fold on 16 lanes per channel group.
   const bool lanes = a.m >= kSplitM && total < 32768;
   const dim3 grid(static_cast<uint32_t>(lanes ? (total + 15) / 16 : (total + 255) / 256));
 #define CSA_COMPRESS_LAUNCH(DT_)                                                             \
