@@ -144,30 +144,62 @@ struct Merge {
       ucnt[tid] = static_cast<int32_t>(cnt);
     }
     __syncthreads();
-    // U into LDS: every (part, slot) pair, slots past a list's length
-    // skipped; each batch issues all its loads before any store.
+    // U into LDS (values, then indices).  Lists of at most UITEMS * tpp
+    // slots: tpp = THREADS / nparts threads per list, UITEMS slots each, all
+    // loads issued before any store (one memory round trip; the slots are
+    // read up to the list's capacity, so no load waits for its count).
+    // Longer lists: every (part, slot) pair in batches.  U holds at most kU
+    // entries (checked above), so the slot arithmetic fits 32 bits.
     float* uval = sh.stage;
     int32_t* uidx = reinterpret_cast<int32_t*>(sh.stage + kU);
-    const int64_t nslots = static_cast<int64_t>(nparts) * lcap;
-    constexpr int kBatch = 16;
-    for (int64_t i0 = 0; i0 < nslots; i0 += static_cast<int64_t>(THREADS) * kBatch) {
-      float tv[kBatch];
-      int32_t tx[kBatch];
+    const int tpp = THREADS / nparts;
+    if (lcap <= static_cast<int64_t>(UITEMS) * tpp) {
+      const int cap = static_cast<int>(lcap);
+      const int p = tid / tpp, li = tid - (tid / tpp) * tpp;
+      const int pp = p < nparts ? p : 0;
+      const float* lvp = lval + static_cast<int64_t>(pp) * cap;
+      const int32_t* lip = lidx + static_cast<int64_t>(pp) * cap;
+      float tv[UITEMS];
+      int32_t tx[UITEMS];
 #pragma unroll
-      for (int r = 0; r < kBatch; ++r) {
-        const int64_t i = i0 + r * THREADS + tid;
-        const int64_t ic = i < nslots ? i : 0;
-        tv[r] = lval[ic];
-        tx[r] = lidx[ic];
+      for (int r = 0; r < UITEMS; ++r) {
+        const int i = li + r * tpp;
+        const int ic = i < cap ? i : 0;
+        tv[r] = lvp[ic];
+        tx[r] = lip[ic];
       }
+      const int n = p < nparts ? ucnt[p] : 0;
+      const uint32_t off = p < nparts ? uoff[p] : 0u;
 #pragma unroll
-      for (int r = 0; r < kBatch; ++r) {
-        const int64_t i = i0 + r * THREADS + tid;
-        const int p = static_cast<int>(i / lcap);
-        const int j = static_cast<int>(i - static_cast<int64_t>(p) * lcap);
-        if (i < nslots && j < ucnt[p]) {
-          uval[uoff[p] + j] = tv[r];
-          uidx[uoff[p] + j] = tx[r];
+      for (int r = 0; r < UITEMS; ++r) {
+        const int i = li + r * tpp;
+        if (i < n) {
+          uval[off + i] = tv[r];
+          uidx[off + i] = tx[r];
+        }
+      }
+    } else {
+      const int64_t nslots = static_cast<int64_t>(nparts) * lcap;
+      constexpr int kBatch = 16;
+      for (int64_t i0 = 0; i0 < nslots; i0 += static_cast<int64_t>(THREADS) * kBatch) {
+        float tv[kBatch];
+        int32_t tx[kBatch];
+#pragma unroll
+        for (int r = 0; r < kBatch; ++r) {
+          const int64_t i = i0 + r * THREADS + tid;
+          const int64_t ic = i < nslots ? i : 0;
+          tv[r] = lval[ic];
+          tx[r] = lidx[ic];
+        }
+#pragma unroll
+        for (int r = 0; r < kBatch; ++r) {
+          const int64_t i = i0 + r * THREADS + tid;
+          const int p = static_cast<int>(i / lcap);
+          const int j = static_cast<int>(i - static_cast<int64_t>(p) * lcap);
+          if (i < nslots && j < ucnt[p]) {
+            uval[uoff[p] + j] = tv[r];
+            uidx[uoff[p] + j] = tx[r];
+          }
         }
       }
     }
