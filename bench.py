@@ -700,17 +700,22 @@ def single_layer_decode(steps, warmup, kind, B, n_ctx, W):
     st = Stack(B=B, n_ctx=n_ctx, layers=1, schedule=kind, W=W)
     state = GpuState(st)
     ms = timed_steps(state.step, steps, warmup)
+    replay = state.capture()
+    ms_graph = timed_steps(replay, steps, warmup)
     ev = {}
     for _ in range(3):
         state.step(ev)
     torch.cuda.synchronize()
     per_call = event_means_ms(ev)
-    del state
+    del state, replay
     torch.cuda.empty_cache()
-    gbps = st.step_bytes() / (ms * 1e-3) / 1e9
-    return {"batch": B, "n_ctx": n_ctx, "layer": kind, "window": W, "ms_per_step": ms,
-            "queries_per_s": B / (ms * 1e-3), "algorithmic_bytes_per_step": st.step_bytes(), "achieved_GBps": gbps,
-            "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS, "per_call_ms": per_call}
+    best = min(ms, ms_graph)
+    gbps = st.step_bytes() / (best * 1e-3) / 1e9
+    return {"batch": B, "n_ctx": n_ctx, "layer": kind, "window": W, "ms_per_step": ms, "graph_ms_per_step": ms_graph,
+            "queries_per_s": B / (best * 1e-3), "algorithmic_bytes_per_step": st.step_bytes(), "achieved_GBps": gbps,
+            "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS, "per_call_ms": per_call,
+            "note": "a few launches per step: bound by launch latency; rates use the faster of eager launches and "
+                    "one HIP-graph replay of the step (both streams)"}
 
 
 def bulk_compress(kind, B, n, reps=3):

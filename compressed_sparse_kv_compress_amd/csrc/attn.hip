@@ -529,32 +529,59 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
 }
 
 // Merge split partials: O = sum_s 2^{m_s-M} O_s / (sum_s 2^{m_s-M} l_s + 2^{sig-M}).
-// One wavefront per (query, head), four per workgroup: lane s reads split s's
-// (m, l) while every lane already requests its 8 output dims (16 bytes of the
-// bf16 partial row) of the first 16 splits, so the first group costs one
-// memory round trip; further groups of 16 follow.
+// One wavefront per (query, head, chunk of 8 * 64/G dims), four per
+// workgroup.  Its lanes form G groups of 64/G lanes; a lane holds 8 output
+// dims and group g takes splits g, g+G, g+2G, ...  Every lane requests its
+// first 16 splits' 16 bytes of bf16 partial row while the (m, l) pairs are
+// read (up to four per lane), so one memory round trip covers 16G splits;
+// the groups' sums meet by lane exchange at the end.  The launch takes the
+// fewest groups that cover every split in one round trip (G = 1: a whole
+// 512-dim row per wavefront; G = 8: 64-dim chunks).
+template <int G>
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int nsplit) {
-  __shared__ float fac[4][64];
-  constexpr int kGroup = 16;
+  constexpr int LPC = 64 / G;  // lanes per chunk
+  constexpr int kGroup = 16;   // splits per lane per round trip
+  __shared__ float fac[4][kAttnMaxSplits];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t bh = static_cast<int64_t>(blockIdx.x) * 4 + w;  // (bt, h)
+  const int64_t D = a.d;
+  const int64_t chunk = D < 8 * LPC ? D : 8 * LPC;
+  const int64_t nq = D / chunk;
+  const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + w;
+  const int64_t bh = gw / nq;  // (bt, h)
+  const int64_t d0 = (gw % nq) * chunk;
   const int64_t bt = bh / a.H;
   const int64_t h = bh % a.H;
-  const int64_t D = a.d;
-  const bool has_dims = lane * 8 < D;
-  const uint16_t* src = attn_ws_o(a) + (bt * nsplit * a.H + h) * D + (has_dims ? lane * 8 : 0);
+  const int grp = lane / LPC;
+  const int c = lane % LPC;
+  const bool has_dims = c * 8 < chunk;
+  const uint16_t* src = attn_ws_o(a) + (bt * nsplit * a.H + h) * D + d0 + (has_dims ? c * 8 : 0);
   const int64_t sstride = a.H * D;
   u32x4 v[kGroup];
 #pragma unroll
-  for (int q = 0; q < kGroup; ++q) v[q] = *reinterpret_cast<const u32x4*>(src + (q < nsplit ? q : 0) * sstride);
-  const float* wml = attn_ws_ml(a, nsplit);
-  const float ms = lane < nsplit ? wml[((bt * nsplit + lane) * a.H + h) * 2] : -INFINITY;
-  const float ls = lane < nsplit ? wml[((bt * nsplit + lane) * a.H + h) * 2 + 1] : 0.f;
+  for (int q = 0; q < kGroup; ++q) {
+    const int sp = grp + G * q;
+    v[q] = *reinterpret_cast<const u32x4*>(src + (sp < nsplit ? sp : 0) * sstride);
+  }
+  const float* wml = attn_ws_ml(a, nsplit) + (bt * nsplit * a.H + h) * 2;
+  float ms[kAttnMaxSplits / 64], ls[kAttnMaxSplits / 64];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < kAttnMaxSplits / 64; ++r) {
+    const int sp = lane + 64 * r;
+    ms[r] = sp < nsplit ? wml[sp * a.H * 2] : -INFINITY;
+    ls[r] = sp < nsplit ? wml[sp * a.H * 2 + 1] : 0.f;
+    mloc = fmaxf(mloc, ms[r]);
+  }
   const float sig = a.sink ? a.sink[h] * kLog2e : -INFINITY;
-  const float M = fmaxf(wave_max(ms), sig);
-  const float f = (M == -INFINITY || ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
-  fac[w][lane] = f;
-  float den = wave_sum(ls * f);
+  const float M = fmaxf(wave_max(mloc), sig);
+  float lsum = 0.f;
+#pragma unroll
+  for (int r = 0; r < kAttnMaxSplits / 64; ++r) {
+    const float f = (M == -INFINITY || ms[r] == -INFINITY) ? 0.f : fast_exp2(ms[r] - M);
+    if (lane + 64 * r < nsplit) fac[w][lane + 64 * r] = f;
+    lsum = fmaf(ls[r], f, lsum);
+  }
+  float den = wave_sum(lsum);
   if (M != -INFINITY && sig != -INFINITY) den += fast_exp2(sig - M);
   const float inv = den > 0.f ? 1.f / den : 0.f;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -563,17 +590,18 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int nsplit) {
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += kGroup) {
-    if (s0 > 0) {  // later groups (more than 16 splits)
+  for (int s0 = 0; s0 < nsplit; s0 += G * kGroup) {
+    if (s0 > 0) {  // later round trips (more than 16 G splits)
 #pragma unroll
       for (int q = 0; q < kGroup; ++q) {
-        const int sp = s0 + q < nsplit ? s0 + q : 0;
-        v[q] = *reinterpret_cast<const u32x4*>(src + sp * sstride);
+        const int sp = s0 + grp + G * q;
+        v[q] = *reinterpret_cast<const u32x4*>(src + (sp < nsplit ? sp : 0) * sstride);
       }
     }
 #pragma unroll
     for (int q = 0; q < kGroup; ++q) {
-      const float fs = s0 + q < nsplit ? fac[w][s0 + q] : 0.f;
+      const int sp = s0 + grp + G * q;
+      const float fs = sp < nsplit ? fac[w][sp] : 0.f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         acc[2 * u] = fmaf(lo_bf16(v[q][u]), fs, acc[2 * u]);
@@ -581,13 +609,17 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int nsplit) {
       }
     }
   }
-  if (has_dims) {
+#pragma unroll
+  for (int off = LPC; off < 64; off *= 2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off);
+  if (has_dims && grp == 0) {
     u32x4 o;
 #pragma unroll
     for (int u = 0; u < 4; ++u) o[u] = cvt_bf16x2(acc[2 * u] * inv, acc[2 * u + 1] * inv);
-    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + bh * D + lane * 8) = o;
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + bh * D + d0 + c * 8) = o;
   }
-  if (a.lse && lane == 0) a.lse[bh] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
+  if (a.lse && lane == 0 && d0 == 0) a.lse[bh] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
 }
 
 // fp32 storage: one wavefront per (query, head), VALU, 64 rows per step.
@@ -677,7 +709,11 @@ int attn_splits(int64_t B, int64_t T, int64_t H, int64_t d, int64_t max_rows, Dt
   const int64_t base = B * T * (H / kHeadsPerWg);
   const int64_t target = 256;  // workgroups wanted per launch (one per CU)
   int64_t ns = (target + base - 1) / base;
-  const int64_t cap = (max_rows + 63) / 64;  // keep >= 64 rows per split
+  // A split writes a partial row per head (64 heads x d, bf16: as many bytes
+  // as 32 K/V rows) that the combine reads back: long lists keep at least two
+  // 32-row stages per split, short ones (the sparse list) at least one.
+  const int64_t min_rows = max_rows >= 2048 ? 64 : 32;
+  const int64_t cap = (max_rows + min_rows - 1) / min_rows;
   if (ns > cap) ns = cap;
   if (ns > kAttnMaxSplits) ns = kAttnMaxSplits;
   // A split costs its number of 32-row stages (each a gather round trip);
@@ -731,8 +767,20 @@ hipError_t launch_attn(const AttnArgs& a, bool sparse, Dt dt, int nsplit, hipStr
 #undef CSA_ATTN_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
-  hipLaunchKernelGGL(attn_combine, dim3(static_cast<uint32_t>(a.B * a.T * a.H / 4)), dim3(256), 0, s, a,
-                     nsplit);
+  // Lane groups G: the fewest with one memory round trip for all splits
+  // (16 G >= nsplit), and at least enough that a group's 64/G lanes of 8
+  // dims do not exceed d.
+  int G = nsplit <= 16 ? 1 : (nsplit <= 32 ? 2 : (nsplit <= 64 ? 4 : 8));
+  const int gmin = static_cast<int>(512 / a.d);
+  if (G < gmin) G = gmin;
+  const int64_t waves = a.B * a.T * a.H * (a.d * G / 512);
+  const dim3 cgrid(static_cast<uint32_t>(waves / 4)), blk(256);
+  switch (G) {
+    case 1: hipLaunchKernelGGL(attn_combine<1>, cgrid, blk, 0, s, a, nsplit); break;
+    case 2: hipLaunchKernelGGL(attn_combine<2>, cgrid, blk, 0, s, a, nsplit); break;
+    case 4: hipLaunchKernelGGL(attn_combine<4>, cgrid, blk, 0, s, a, nsplit); break;
+    default: hipLaunchKernelGGL(attn_combine<8>, cgrid, blk, 0, s, a, nsplit); break;
+  }
   return hipGetLastError();
 }
 

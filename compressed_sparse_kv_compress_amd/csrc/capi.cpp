@@ -430,9 +430,9 @@ csa_status_t csa_sparse_attn_ex(const csa_layout_t* layout, const void* q, const
   st = layout_from(layout, T, L, W, R, &lay);
   if (st != CSA_OK) return st;
   REQUIRE(k >= 0, "k < 0");
-  if (dtype != CSA_F32 && k + W > int64_t(csa::kAttnMaxSplits) * csa::kAttnMaxIdx)
+  if (dtype != CSA_F32 && k + W > csa::kAttnMaxRows)
     return fail(CSA_ERR_UNSUPPORTED, "MFMA sparse attention supports k + W <= %lld rows (got %lld)",
-                (long long)csa::kAttnMaxSplits * csa::kAttnMaxIdx, (long long)(k + W));
+                (long long)csa::kAttnMaxRows, (long long)(k + W));
   if (B == 0) return CSA_OK;
   if (k > 0) REQUIRE_PTR(idx);
   csa::AttnArgs a{q, kc, vc, L, 1, idx, k, kr, vr, R, W, sink, scale, B, T, n_ctx, H, d, out, lse,
@@ -461,9 +461,9 @@ csa_status_t hca_dense_attn_ex(const csa_layout_t* layout, const void* q, const 
   st = layout_from(layout, T, L, W, R, &lay);
   if (st != CSA_OK) return st;
   const int64_t rows = dense_max_rows(L, m, n_ctx, W);
-  if (dtype != CSA_F32 && lay.bt && rows > int64_t(csa::kAttnMaxSplits) * csa::kAttnMaxIdx)
+  if (dtype != CSA_F32 && lay.bt && rows > csa::kAttnMaxRows)
     return fail(CSA_ERR_UNSUPPORTED, "paged dense attention supports at most %lld rows per query (got %lld)",
-                (long long)csa::kAttnMaxSplits * csa::kAttnMaxIdx, (long long)rows);
+                (long long)csa::kAttnMaxRows, (long long)rows);
   if (B == 0) return CSA_OK;
   csa::AttnArgs a{q, kc, vc, L, m, nullptr, 0, kr, vr, R, W, sink, scale, B, T, n_ctx, H, d, out, lse,
                   nullptr, 0, lay};

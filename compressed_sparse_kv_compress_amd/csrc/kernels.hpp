@@ -172,11 +172,12 @@ struct AttnArgs {
 };
 // Number of row splits the attention launch uses, and its workspace bytes.
 // MFMA attention (bf16, or FP8 K/V with bf16 q and out): at most
-// kAttnMaxSplits splits per query (the combine kernel gives one lane to each),
-// and a CSA split caches at most kAttnMaxIdx row indices, so a sparse row list
-// (k + W) is limited to their product.  dt names the K/V storage type.
-constexpr int kAttnMaxSplits = 64;
+// kAttnMaxSplits splits per query (the combine kernel keeps one merge factor
+// per split in LDS), and a CSA split caches at most kAttnMaxIdx row indices;
+// a row list is limited to kAttnMaxRows.  dt names the K/V storage type.
+constexpr int kAttnMaxSplits = 256;
 constexpr int kAttnMaxIdx = 2048;
+constexpr int64_t kAttnMaxRows = 131072;
 int attn_splits(int64_t B, int64_t T, int64_t H, int64_t d, int64_t max_rows, Dt dt, bool sparse);
 size_t attn_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t d, int nsplit);
 hipError_t launch_attn(const AttnArgs& a, bool sparse, Dt dt, int nsplit, hipStream_t s);

@@ -332,6 +332,7 @@ def _attn_inputs(dt, B, T, H, d, L, R, seed):
     ("bf16", 2, 2, 128, 128, 900, 64, 0, True),
     ("bf16", 1, 2, 64, 128, 50, 64, 16, True),
     ("bf16", 1, 520, 64, 128, 300, 64, 16, True),
+    ("bf16", 4, 4, 64, 256, 500, 128, 32, True),  # 1024 (query, head) pairs at d = 256: two lane groups per row
     ("f32", 1, 16, 8, 64, 1024, 64, 128, True),
 ])
 def test_sparse_attn_matches_oracle(dt, B, T, H, d, L, k, W, use_sink):
@@ -360,6 +361,7 @@ def test_sparse_attn_matches_oracle(dt, B, T, H, d, L, k, W, use_sink):
     ("bf16", 1, 2, 64, 512, 700, 4, 128),
     ("bf16", 1, 40, 64, 128, 100, 4, 16),
     ("bf16", 1, 520, 64, 128, 200, 4, 16),
+    ("bf16", 1, 1, 64, 512, 9000, 4, 128),  # one query, 9127 rows: 143 splits, merged in two round trips
     ("f32", 1, 2, 8, 64, 500, 4, 128),
 ])
 def test_dense_attn_matches_oracle(dt, B, T, H, d, L, m, W):
