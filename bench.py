@@ -746,6 +746,84 @@ def bulk_compress(kind, B, n, reps=3):
             "bytes_per_sequence": total_bytes / B}
 
 
+def paged_layout(B: int = 16, n_ctx: int = 1_000_000, page: int = 64, reps: int = 10):
+    """csa_index_topk and csa_sparse_attn of one CSA layer over a serving
+    layout: per-sequence lengths (n_ctx, n_ctx - 37,000, n_ctx - 74,000, ...
+    down the batch) and compressed caches held as pools of 64-entry pages at
+    seeded random places, against the same calls on dense [B][L] caches with
+    the same lengths.  The outputs must agree bit for bit (they are checked
+    here too); the rates count the visible index keys and gathered rows."""
+    import compressed_sparse_kv_compress_amd as csa
+    HI, dI, H, d, m, k, W = 64, 128, 64, 512, 4, 1024, 128
+    L = -(-n_ctx // m)
+    lens_l = [n_ctx - 37_000 * b for b in range(B)]
+    lens = torch.tensor(lens_l, dtype=torch.int64, device="cuda")
+    bf = torch.bfloat16
+
+    def gen(shape, tid, scale, dtype=bf):
+        return syn.fill_(torch.empty(shape, dtype=dtype, device="cuda"), 6, tid, scale=scale)
+
+    ki = gen((B, L, dI), syn.TID["kic"], dI ** -0.5)
+    qi = gen((B, 1, HI, dI), syn.TID["q_idx"], dI ** -0.5)
+    wi = gen((B, 1, HI), syn.TID["w_idx"], HI ** -0.5, torch.float32)
+    P = -(-L // page)
+    npages = B * P + 8
+    perm = torch.randperm(npages, generator=torch.Generator().manual_seed(6))[:B * P].reshape(B, P)
+    bt = perm.to(torch.int32).cuda()
+    pool = torch.empty((npages * page, dI), dtype=bf, device="cuda")
+    for b in range(B):  # page p of sequence b -> pool page bt[b][p]
+        rows = (bt[b].to(torch.int64).reshape(P, 1) * page + torch.arange(page, device="cuda")).reshape(-1)[:L]
+        pool[rows] = ki[b]
+    lay_d = csa.layout(seq_len=lens)
+    lay_p = csa.layout(seq_len=lens, block_table=bt, page=page, num_pages=npages)
+    ws = torch.zeros(csa.csa_index_topk_workspace(B, 1, L, HI, k), dtype=torch.uint8, device="cuda")
+    idx_d = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
+    idx_p = torch.empty_like(idx_d)
+    run_d = lambda: csa.csa_index_topk(qi, ki, m, k, w_idx=wi, n_ctx=n_ctx, layout=lay_d, idx=idx_d, ws=ws)  # noqa: E731
+    run_p = lambda: csa.csa_index_topk(qi, pool, m, k, w_idx=wi, n_ctx=n_ctx, layout=lay_p, L=L, idx=idx_p,  # noqa: E731
+                                       ws=ws)
+    ms_d = timed_steps(run_d, reps, 2)
+    ms_p = timed_steps(run_p, reps, 2)
+    same_idx = bool(torch.equal(idx_d, idx_p))
+    vis = sum(min(L, (n - 1) // m) for n in lens_l)
+    idx_bytes = vis * dI * 2 + B * (HI * dI * 2 + HI * 4 + k * 4)
+    del ki, pool, ws
+    torch.cuda.empty_cache()
+    # sparse attention over the selection, K and V paged the same way
+    kc = gen((B, L, d), syn.TID["kc"], d ** -0.5)
+    vc = gen((B, L, d), syn.TID["vc"], d ** -0.5)
+    q = gen((B, 1, H, d), syn.TID["q"], d ** -0.5)
+    kr = gen((B, W, d), syn.TID["kr"], d ** -0.5)
+    vr = gen((B, W, d), syn.TID["vr"], d ** -0.5)
+    sink = gen((H,), syn.TID["sink"], 1.0, torch.float32)
+    pk = torch.empty((npages * page, d), dtype=bf, device="cuda")
+    pv = torch.empty_like(pk)
+    for b in range(B):
+        rows = (bt[b].to(torch.int64).reshape(P, 1) * page + torch.arange(page, device="cuda")).reshape(-1)[:L]
+        pk[rows] = kc[b]
+        pv[rows] = vc[b]
+    aws = torch.empty(max(16, csa.csa_attn_workspace(B, 1, H, d, k + W)), dtype=torch.uint8, device="cuda")
+    o_d = torch.empty((B, 1, H, d), dtype=bf, device="cuda")
+    o_p = torch.empty_like(o_d)
+    att_d = lambda: csa.csa_sparse_attn(q, kc, vc, idx_d, kr=kr, vr=vr, W=W, sink=sink, n_ctx=n_ctx,  # noqa: E731
+                                        layout=lay_d, out=o_d, ws=aws)
+    att_p = lambda: csa.csa_sparse_attn(q, pk, pv, idx_d, kr=kr, vr=vr, W=W, sink=sink, n_ctx=n_ctx,  # noqa: E731
+                                        layout=lay_p, L=L, out=o_p, ws=aws)
+    am_d = timed_steps(att_d, reps, 2)
+    am_p = timed_steps(att_p, reps, 2)
+    same_out = bool(torch.equal(o_d, o_p))
+    att_bytes = B * ((k + W) * d * 2 * 2 + 2 * H * d * 2 + k * 4)
+    del kc, vc, pk, pv, aws
+    torch.cuda.empty_cache()
+    return {"batch": B, "page": page, "seq_len": lens_l,
+            "index_topk": {"dense_ms": ms_d, "paged_ms": ms_p, "bytes": idx_bytes,
+                           "dense_GBps": idx_bytes / (ms_d * 1e-3) / 1e9,
+                           "paged_GBps": idx_bytes / (ms_p * 1e-3) / 1e9, "identical": same_idx},
+            "csa_sparse_attn": {"dense_ms": am_d, "paged_ms": am_p, "bytes": att_bytes,
+                                "dense_GBps": att_bytes / (am_d * 1e-3) / 1e9,
+                                "paged_GBps": att_bytes / (am_p * 1e-3) / 1e9, "identical": same_out}}
+
+
 def measured_peaks():
     """A plain 4 GiB device copy (read + write bytes / time) and a large bf16
     GEMM through torch (hipBLASLt): the measured counterparts of the 8 TB/s
@@ -925,6 +1003,12 @@ def main():
         configs["hca_compress_bulk_1m_b4"] = bulk_compress("hca", 4, 1_000_000)
         print("# bulk compress: csa %.0f GB/s, hca %.0f GB/s" % (configs["csa_compress_bulk_128k_b8"]["GBps"],
               configs["hca_compress_bulk_1m_b4"]["GBps"]), file=sys.stderr, flush=True)
+        configs["paged_varlen_b16"] = paged_layout(args.batch)
+        pl = configs["paged_varlen_b16"]
+        print("# paged: index_topk %.3f vs %.3f ms dense, attention %.4f vs %.4f ms dense (identical %s/%s)"
+              % (pl["index_topk"]["paged_ms"], pl["index_topk"]["dense_ms"], pl["csa_sparse_attn"]["paged_ms"],
+                 pl["csa_sparse_attn"]["dense_ms"], pl["index_topk"]["identical"], pl["csa_sparse_attn"]["identical"]),
+              file=sys.stderr, flush=True)
         configs["measured_peaks"] = measured_peaks()
         print("# copy %.0f GB/s, bf16 gemm %.0f TFLOP/s" % (configs["measured_peaks"]["copy_GBps"],
               configs["measured_peaks"]["gemm_bf16_TFLOPs"]), file=sys.stderr, flush=True)

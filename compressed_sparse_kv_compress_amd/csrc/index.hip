@@ -36,16 +36,20 @@ constexpr int kWaves = 4;
 constexpr int kTileKeys = 16;                 // keys per MFMA tile (the N dimension)
 constexpr int kDepth = CSA_INDEX_DEPTH;       // ring slots per wavefront (kDepth - 1 tiles in flight)
 constexpr int kTileBytes = kTileKeys * 256;   // d_I = 128 bf16 keys
-// FP8 keys (128 B): tiles of half the size and twice the slots, the same
-// ring bytes and about the same bytes in flight.
-constexpr int kDepth8 = 2 * kDepth;
+// FP8 keys (128 B): tiles of half the size.
 constexpr int kTileBytes8 = kTileKeys * 128;
-static_assert(kDepth8 * kTileBytes8 == kDepth * kTileBytes, "one ring size for both key types");
 // MXFP4 keys (64 code bytes + 4 E8M0 scales): a tile is its 1 KiB of codes
 // and four copies of its 64 scale bytes (one dword load).
-constexpr int kDepth4 = 15;
 constexpr int kTileBytes4 = kTileKeys * 64 + 256;
-static_assert(kDepth4 * kTileBytes4 <= kDepth * kTileBytes, "the MXFP4 ring fits the same space");
+// FP8 and MXFP4 scans run two wavefronts per SIMD (8 per workgroup), so that
+// one wavefront's per-tile chain (LDS read, MFMA, ReLU / weight / head-sum
+// epilogue) overlaps another's; each keeps half the ring slots (the same
+// bytes in flight per CU).  A workgroup still scans 4 * per_wave keys.
+constexpr int kWaves8 = 8;
+constexpr int kDepthW8 = kDepth;  // FP8 slots per wavefront with 8 wavefronts
+constexpr int kDepthW4 = 8;       // MXFP4
+static_assert(kWaves8 * kDepthW8 * kTileBytes8 == kWaves * kDepth * kTileBytes, "FP8 ring of the bf16 size");
+static_assert(kWaves8 * kDepthW4 * kTileBytes4 <= kWaves * kDepth * kTileBytes, "MXFP4 ring fits the same space");
 constexpr int kMinKeysPerWave = 256;
 constexpr int kMaxKeysPerWave = 3968;         // scores of a workgroup stay in LDS (62 KiB)
 constexpr int kMaxTiles = kMaxKeysPerWave / kTileKeys;
@@ -90,8 +94,8 @@ __device__ __forceinline__ void wait_tiles(int n) {
   }
   asm volatile("" ::: "memory");
 }
-static_assert(kDepth >= 2 && kDepth8 <= 15 && kDepth4 <= 15, "wait_tiles covers up to 14 tiles in flight");
-static_assert(4 * (kDepth - 1) < 64 && 2 * (kDepth8 - 1) < 64 && 2 * (kDepth4 - 1) < 64, "vmcnt range");
+static_assert(kDepth >= 2 && kDepth <= 15 && kDepthW4 <= 15, "wait_tiles covers up to 14 tiles in flight");
+static_assert(4 * (kDepth - 1) < 64 && 2 * (kDepthW8 - 1) < 64 && 2 * (kDepthW4 - 1) < 64, "vmcnt range");
 
 // 16 bytes per lane, global -> LDS at lds + 16 * lane (lds wave-uniform, via
 // M0), nontemporal (every key is read once: streaming through the caches
@@ -144,13 +148,22 @@ __device__ __forceinline__ void dma4(const void* g, const uint8_t* lds) {
 // in its part's top-k (fewer entries beat it inside the part than in the whole
 // row), ties included.  The tile ring is free at this point and holds the
 // selection's state.
-using PartSel = sel::Filter<64 * kWaves, 64, 24>;
+template <int NW>
+using PartSel = sel::Filter<64 * NW, 64 * kWaves / NW, NW == kWaves ? 24 : 16>;
 constexpr int kPartKeys = 64 * kWaves * 64;  // 16384 >= 4 * kMaxKeysPerWave
 constexpr int kCandStage = 2048;             // largest cap staged in LDS
 constexpr int kListStage = 1024;             // largest compact list staged in LDS
 static_assert(4 * kMaxKeysPerWave <= kPartKeys, "a part fits the selection tile");
-static_assert(sizeof(PartSel::Shared) + (kCandStage + 64) * 8 + (kListStage + 64) * 8 <= kWaves * kDepth * kTileBytes,
+static_assert(sizeof(PartSel<kWaves>::Shared) + (kCandStage + 64) * 8 + (kListStage + 64) * 8 <=
+                  kWaves * kDepth * kTileBytes,
               "selection state fits the ring");
+static_assert(sizeof(PartSel<kWaves8>::Shared) + (kCandStage + 64) * 8 + (kListStage + 64) * 8 <=
+                  kWaves8 * kDepthW4 * kTileBytes4,
+              "selection state fits the 8-wavefront rings");
+// Score slots per wavefront: a workgroup's range holds at most
+// 4 * kMaxKeysPerWave keys, split over NW wavefronts.
+template <int NW>
+constexpr int kScoreSlots = kMaxTiles * kWaves / NW * kTileKeys;
 
 // Position of key c (0..15) of a wavefront's tile `it` in its score list: the
 // four 4-key chunks of a tile are rotated by the tile number, so that 16 lanes
@@ -158,22 +171,28 @@ static_assert(sizeof(PartSel::Shared) + (kCandStage + 64) * 8 + (kListStage + 64
 // different bank groups.
 __device__ __forceinline__ int sb_pos(int it, int c) { return it * kTileKeys + ((((c >> 2) + it) & 3) << 2) + (c & 3); }
 
-// Score of key o of the workgroup's range: tile T = o / 16 is tile T / 4 of
-// wavefront T % 4.
-__device__ __forceinline__ float part_score(const float (*sbuf)[kMaxTiles * kTileKeys], int o) {
+// Score of key o of the workgroup's range: tile T = o / 16 is tile T / NW of
+// wavefront T % NW.
+template <int NW>
+__device__ __forceinline__ float part_score(const float (*sbuf)[kScoreSlots<NW>], int o) {
   const int T = o / kTileKeys;
-  return sbuf[T % kWaves][sb_pos(T / kWaves, o % kTileKeys)];
+  return sbuf[T % NW][sb_pos(T / NW, o % kTileKeys)];
 }
 
+template <int NW>
 __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t slot, int64_t kb, int nkv,
-                                            const float (*sbuf)[kMaxTiles * kTileKeys], uint8_t* scratch) {
+                                            const float (*sbuf)[kScoreSlots<NW>], uint8_t* scratch) {
+  using PS = PartSel<NW>;
+  constexpr int IT = kPartKeys / (64 * NW);  // entries per thread
+  constexpr int TPT = IT / kTileKeys;        // tiles per thread
+  constexpr int MT = kScoreSlots<NW> / kTileKeys;
   const int tid = threadIdx.x;
   const int cap = static_cast<int>(co.cap);
   float* ov = co.cval + slot * co.cap;
   int32_t* oi = co.cidx + slot * co.cap;
   if (nkv <= cap) {  // the whole part is kept; the rest of the slots hold NaN (no candidate)
-    for (int o = tid; o < cap; o += 64 * kWaves) {
-      ov[o] = o < nkv ? part_score(sbuf, o) : __builtin_nanf("");
+    for (int o = tid; o < cap; o += 64 * NW) {
+      ov[o] = o < nkv ? part_score<NW>(sbuf, o) : __builtin_nanf("");
       if (o < nkv) oi[o] = static_cast<int32_t>(kb + o);
     }
     if (tid == 0) {
@@ -185,36 +204,39 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
     }
     return;
   }
-  PartSel::Shared& ss = *reinterpret_cast<PartSel::Shared*>(scratch);
-  int32_t* si = reinterpret_cast<int32_t*>(scratch + sizeof(PartSel::Shared));
+  typename PS::Shared& ss = *reinterpret_cast<typename PS::Shared*>(scratch);
+  int32_t* si = reinterpret_cast<int32_t*>(scratch + sizeof(typename PS::Shared));
   float* sv = reinterpret_cast<float*>(si + kCandStage + 64);  // each array: 64 dump slots at its end
   int32_t* li = reinterpret_cast<int32_t*>(sv + kCandStage + 64);
   float* lv = reinterpret_cast<float*>(li + kListStage + 64);
   const uint32_t lane = threadIdx.x & 63;
   const int lcap = static_cast<int>(co.lcap);  // <= kListStage (4 or more parts, 4096 entries in all)
-  PartSel::zero(ss);
-  // Thread t holds entries 64t .. 64t+63 of the part: tiles 4t .. 4t+3, i.e.
-  // tile t of each wavefront's list, 16 consecutive scores each; entries past
-  // the visible ones are NaN (never selected).
-  float x[64];
-  const int o0 = tid * 64;
-  const int tl = tid < kMaxTiles ? tid : kMaxTiles - 1;
+  PS::zero(ss);
+  // Thread t holds entries IT*t .. IT*t+IT-1 of the part: tiles TPT*t ..
+  // TPT*t+TPT-1 (tile T is tile T / NW of wavefront T % NW), 16 consecutive
+  // scores each; entries past the visible ones are NaN (never selected).
+  float x[IT];
+  const int o0 = tid * IT;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w)
+  for (int j = 0; j < TPT; ++j) {
+    const int T = TPT * tid + j;
+    const int w = T % NW;
+    const int tl = T / NW < MT ? T / NW : MT - 1;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f32x4 v = *reinterpret_cast<const f32x4*>(&sbuf[w][sb_pos(tl, 4 * q)]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[w * 16 + 4 * q + e] = v[e];
+      for (int e = 0; e < 4; ++e) x[j * 16 + 4 * q + e] = v[e];
     }
+  }
 #pragma unroll
-  for (int j = 0; j < 64; ++j) x[j] = o0 + j < nkv ? x[j] : __builtin_nanf("");
+  for (int j = 0; j < IT; ++j) x[j] = o0 + j < nkv ? x[j] : __builtin_nanf("");
   float vmin, vmax;
-  PartSel::block_range(x, ss, &vmin, &vmax);
+  PS::block_range(x, ss, &vmin, &vmax);
   float thr2 = -INFINITY;
   uint32_t cnt2 = 0;
-  PartSel::run2(
-      x, [&](uint32_t e) { return part_score(sbuf, static_cast<int>(e) < nkv ? static_cast<int>(e) : 0); },
+  PS::run2(
+      x, [&](uint32_t e) { return part_score<NW>(sbuf, static_cast<int>(e) < nkv ? static_cast<int>(e) : 0); },
       static_cast<uint32_t>(nkv), static_cast<uint32_t>(cap), vmin, vmax, ss,
       [&](uint32_t pos, float v, uint32_t e) {
         const uint32_t p = pos != sel::kNoSlot ? pos : kCandStage + lane;  // lane-private dump slot
@@ -223,7 +245,7 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
       },
       [&](int j, uint32_t pos) {
         si[pos] = o0 + j;
-        sv[pos] = part_score(sbuf, o0 + j);
+        sv[pos] = part_score<NW>(sbuf, o0 + j);
       },
       co.lval ? static_cast<uint32_t>(co.lrank) : 0u,
       [&](uint32_t pos, float v, uint32_t e) {
@@ -232,14 +254,14 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
         lv[p] = v;
       },
       &thr2, &cnt2);
-  for (int i = tid; i < cap; i += 64 * kWaves) {
+  for (int i = tid; i < cap; i += 64 * NW) {
     ov[i] = sv[i];
     oi[i] = static_cast<int32_t>(kb + si[i]);
   }
   if (co.lval) {
     const bool fits = cnt2 <= static_cast<uint32_t>(lcap);
     if (fits) {
-      for (int i = tid; i < static_cast<int>(cnt2); i += 64 * kWaves) {
+      for (int i = tid; i < static_cast<int>(cnt2); i += 64 * NW) {
         co.lval[slot * co.lcap + i] = lv[i];
         co.lidx[slot * co.lcap + i] = static_cast<int32_t>(kb + li[i]);
       }
@@ -269,18 +291,20 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
 // FP4 form takes 16 code bytes per lane, and each lane's scale operand is the
 // scale of exactly its 32 elements (lane (g, c): row c, block g).
 template <int MB, bool HAS_W, bool TOPK, int KF>  // KF: key format, 0 bf16, 1 FP8, 2 MXFP4
-__global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, int64_t parts, int64_t per_wave,
-                                                             IndexCandidates co) {
+__global__ __launch_bounds__(64 * (KF ? kWaves8 : kWaves), 1) void index_score_stream(IndexScoreArgs a, int64_t parts,
+                                                                                      int64_t per_wave,
+                                                                                      IndexCandidates co) {
   constexpr bool FP8 = KF == 1, FP4 = KF == 2;
+  constexpr int NW = KF ? kWaves8 : kWaves;  // wavefronts per workgroup
   constexpr int HI = 16 * MB;
   constexpr int DI = 128;
   constexpr int KS = 4;
   constexpr int KB = FP4 ? 64 : (FP8 ? 128 : 256);                          // code bytes per key
   constexpr int TB = FP4 ? kTileBytes4 : (FP8 ? kTileBytes8 : kTileBytes);  // LDS bytes per tile
-  constexpr int DEPTH = FP4 ? kDepth4 : (FP8 ? kDepth8 : kDepth);           // ring slots per wavefront
+  constexpr int DEPTH = FP4 ? kDepthW4 : (FP8 ? kDepthW8 : kDepth);         // ring slots per wavefront
   constexpr int LPT = FP4 ? 2 : TB / 1024;                                  // wave loads per tile
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][DEPTH][TB];
-  __shared__ __attribute__((aligned(16))) float sbuf[kWaves][kMaxTiles * kTileKeys];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NW][DEPTH][TB];
+  __shared__ __attribute__((aligned(16))) float sbuf[NW][kScoreSlots<NW>];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;    // 16-lane group: k-slots 8g .. 8g+7 of every k-step
@@ -298,9 +322,9 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
   const int64_t ke = kb + kWaves * per_wave < a.L ? kb + kWaves * per_wave : a.L;
   const int64_t kv = ke < nv ? ke : nv;  // keys [kb, kv) are visible
   const int ntiles = kv > kb ? static_cast<int>((kv - kb + kTileKeys - 1) / kTileKeys) : 0;
-  const int ntv = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+  const int ntv = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
   const int64_t k0 = kb + static_cast<int64_t>(wave) * kTileKeys;  // first key of this wave's tile 0
-  constexpr int64_t kStride = kWaves * kTileKeys;                    // keys between its tiles
+  constexpr int64_t kStride = NW * kTileKeys;                        // keys between its tiles
 
   // Tile layout in LDS.
   //  bf16: key kk (0..15) at kk*256; its 16-byte piece p at slot p ^ kk.
@@ -345,10 +369,35 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
   // npages*page keys), 4 per key.
   const int64_t nkeys = a.lay.bt ? a.lay.npages * a.lay.page : a.B * a.L;
   const char* sbase = FP4 ? kpool + nkeys * KB : nullptr;
+  // Paged keys: tiles are issued in order, kStride keys apart, so the page
+  // index and the offset of the next tile's first key are walked forward
+  // (no division per tile), and each page id is a scalar load (constant
+  // address space) made one tile ahead: a vector load of the table would
+  // need a vmcnt wait, which would drain the ring, and the scalar load's own
+  // wait falls on the loop's LDS wait.  The table is written before the
+  // launch; reads stay inside the sequence's table row.
+  typedef const __attribute__((address_space(4))) int32_t* ConstI32;
+  const ConstI32 btrow = a.lay.bt ? (ConstI32)(a.lay.bt + b * a.lay.bt_ld) : nullptr;
+  const int64_t bt_last = a.lay.bt ? a.lay.bt_ld - 1 : 0;
+  int64_t pw_idx = a.lay.bt ? k0 / a.lay.page : 0;
+  int64_t pw_off = a.lay.bt ? k0 - pw_idx * a.lay.page : 0;
+  int32_t pw_pg = a.lay.bt ? btrow[pw_idx < bt_last ? pw_idx : bt_last] : 0;
+  auto tile_row = [&](int64_t t0) -> int64_t {  // row of key t0; keys t0 .. t0+15 follow it
+    if (!a.lay.bt) return b * a.L + t0;
+    const int64_t pg = pw_pg < 0 ? 0 : (pw_pg >= a.lay.npages ? a.lay.npages - 1 : pw_pg);
+    const int64_t r = pg * a.lay.page + pw_off;
+    pw_off += kStride;
+    while (pw_off >= a.lay.page) {
+      pw_off -= a.lay.page;
+      ++pw_idx;
+    }
+    pw_pg = btrow[pw_idx < bt_last ? pw_idx : bt_last];
+    return r;
+  };
   auto issue = [&](int it) {
     uint8_t* slot = myring + (it % DEPTH) * TB;
     const int64_t t0 = k0 + static_cast<int64_t>(it) * kStride;
-    const int64_t r0 = cache_row(a.lay, a.L, b, t0);  // row of key t0; keys t0 .. t0+15 follow it
+    const int64_t r0 = tile_row(t0);
     if constexpr (FP4) {
       if (t0 + kTileKeys <= a.L) {
         dma16(kpool + r0 * KB, voff[0], slot);
@@ -486,8 +535,8 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
 
   __syncthreads();
   if constexpr (TOPK) {
-    part_select(co, lrow * parts + part, kb, ntiles > 0 ? static_cast<int>(kv - kb) : 0, sbuf,
-                &ring[0][0][0]);
+    part_select<NW>(co, lrow * parts + part, kb, ntiles > 0 ? static_cast<int>(kv - kb) : 0, sbuf,
+                    &ring[0][0][0]);
     return;
   }
   // Write the workgroup's scores [kb, ke) in key order; keys past the visible
@@ -497,9 +546,9 @@ __global__ __launch_bounds__(256, 1) void index_score_stream(IndexScoreArgs a, i
   const int nk = static_cast<int>(ke - kb);
   float* dst = srow + kb;
   const bool aligned = (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
-  for (int o = 4 * static_cast<int>(threadIdx.x); o < nk; o += 4 * 64 * kWaves) {
+  for (int o = 4 * static_cast<int>(threadIdx.x); o < nk; o += 4 * 64 * NW) {
     const int T = o / kTileKeys;
-    f32x4 x = *reinterpret_cast<const f32x4*>(&sbuf[T % kWaves][sb_pos(T / kWaves, o % kTileKeys)]);
+    f32x4 x = *reinterpret_cast<const f32x4*>(&sbuf[T % NW][sb_pos(T / NW, o % kTileKeys)]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[e] = (o + e) / kTileKeys < ntiles ? x[e] : -INFINITY;
     if (aligned && o + 4 <= nk) {
@@ -769,8 +818,10 @@ hipError_t launch_stream(const IndexScoreArgs& a, const IndexCandidates& co, hip
   const bool w = a.w != nullptr;
   const int kf = a.dt == kMXFP4 ? 2 : (a.dt == kFP8 ? 1 : 0);
 #define CSA_INDEX_KF(MB_, KF_)                                                                                     \
-  if (w) hipLaunchKernelGGL((index_score_stream<MB_, true, TOPK, KF_>), grid, dim3(256), 0, s, a, parts, per_wave, co);  \
-  else hipLaunchKernelGGL((index_score_stream<MB_, false, TOPK, KF_>), grid, dim3(256), 0, s, a, parts, per_wave, co);
+  if (w) hipLaunchKernelGGL((index_score_stream<MB_, true, TOPK, KF_>), grid, dim3(KF_ ? 64 * kWaves8 : 256), 0, s, a,   \
+                            parts, per_wave, co);                                                                     \
+  else hipLaunchKernelGGL((index_score_stream<MB_, false, TOPK, KF_>), grid, dim3(KF_ ? 64 * kWaves8 : 256), 0, s, a, \
+                          parts, per_wave, co);
 #define CSA_INDEX_LAUNCH(MB_)                  \
   case MB_:                                    \
     if (kf == 2) { CSA_INDEX_KF(MB_, 2) }      \
