@@ -600,10 +600,11 @@ def fp8_storage_step(B: int, steps: int, warmup: int):
     }
 
 
-def prefill_index_topk(queries: int = 4096, reps: int = 3):
+def prefill_index_topk(queries: int = 4096, reps: int = 3, fp8: bool = False):
     """csa_index_topk on the CSA prefill-chunk shape: the last `queries` of a
     65,536-token chunk after a 262,144-token prefix (81,920 compressed
-    entries, about 82 K visible per query), 64 index heads x 128, k = 1024."""
+    entries, about 82 K visible per query), 64 index heads x 128, k = 1024;
+    bf16, or E4M3 query and keys (the same values rounded to E4M3)."""
     import compressed_sparse_kv_compress_amd as csa
     HI, dI, m, k = 64, 128, 4, 1024
     prefix, chunk = 262144, 65536
@@ -612,6 +613,8 @@ def prefill_index_topk(queries: int = 4096, reps: int = 3):
     ki = syn.fill_(torch.empty((1, L, dI), dtype=torch.bfloat16, device="cuda"), 4, syn.TID["kic"], scale=dI ** -0.5)
     qi = syn.fill_(torch.empty((1, queries, HI, dI), dtype=torch.bfloat16, device="cuda"), 4, syn.TID["q_idx"],
                    scale=dI ** -0.5)
+    if fp8:
+        ki, qi = ki.to(torch.float8_e4m3fn), qi.to(torch.float8_e4m3fn)
     wi = syn.fill_(torch.empty((1, queries, HI), device="cuda"), 4, syn.TID["w_idx"], scale=HI ** -0.5)
     ws = torch.zeros(csa.csa_index_topk_workspace(1, queries, L, HI, k), dtype=torch.uint8, device="cuda")
     idx = torch.empty((1, queries, k), dtype=torch.int32, device="cuda")
@@ -633,12 +636,13 @@ def prefill_index_topk(queries: int = 4096, reps: int = 3):
     flop = pairs * HI * dI * 2
     del ki, qi, ws
     torch.cuda.empty_cache()
-    return {"queries": queries, "entries": L, "ms_per_call": ms, "tflops": flop / (ms * 1e-3) / 1e12,
-            "peak_tflops_bf16": 2500.0, "frac_of_bf16_peak": flop / (ms * 1e-3) / 1e12 / 2500.0,
+    peak = 5000.0 if fp8 else 2500.0
+    return {"queries": queries, "entries": L, "storage": "e4m3" if fp8 else "bf16", "ms_per_call": ms,
+            "tflops": flop / (ms * 1e-3) / 1e12, "peak_tflops": peak, "frac_of_peak": flop / (ms * 1e-3) / 1e12 / peak,
             "visible_pairs": pairs,
-            "note": "flop = 2 * visible (query, entry) pairs * index heads * index dim; scores by the 16-row "
-                    "prefill kernel (each key tile read once per 16 queries), then the stand-alone top-k "
-                    "(about a fifth of the time)"}
+            "note": "flop = 2 * visible (query, entry) pairs * index heads * index dim, against the dense MFMA peak "
+                    "of the storage type; scores by the 16-row prefill kernel (each key tile read once per 16 "
+                    "queries), then the stand-alone top-k (about a sixth of the bf16 call)"}
 
 
 def timed_steps(run, steps, warmup):
@@ -988,6 +992,11 @@ def main():
     if args.prefill_queries > 0:
         prefill = prefill_sparse_attn(args.prefill_queries)
         prefill["index_topk"] = prefill_index_topk(args.prefill_queries)
+        if not args.no_fp8:
+            prefill["index_topk_fp8"] = prefill_index_topk(args.prefill_queries, fp8=True)
+            print("# prefill index + top-k, E4M3 q and keys: %.2f ms (%.0f TFLOP/s)"
+                  % (prefill["index_topk_fp8"]["ms_per_call"], prefill["index_topk_fp8"]["tflops"]), file=sys.stderr,
+                  flush=True)
         print("# prefill index + top-k: %.2f ms (%.0f TFLOP/s)" % (prefill["index_topk"]["ms_per_call"],
               prefill["index_topk"]["tflops"]), file=sys.stderr, flush=True)
         print("# prefill sparse attention: %.2f ms for %d queries (%.0f TFLOP/s)"

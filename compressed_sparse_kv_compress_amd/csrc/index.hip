@@ -561,27 +561,30 @@ __global__ __launch_bounds__(64 * (KF ? kWaves8 : kWaves), 1) void index_score_s
   }
 }
 
-// Prefill scoring (bf16, d_I = 128): a workgroup takes 16 query rows of one
-// sequence, two per wavefront with their query blocks resident as MFMA A
-// operands, and a part of up to kMultiKeys keys.  Each 16-key tile is staged
-// once in LDS (waves 0-3 load a quarter each; an 8-slot ring, one barrier per
-// two tiles) and read by all 8 wavefronts, each B fragment feeding both rows'
-// MFMAs, so a key leaves the caches once per 16 queries.  Same MFMA order and epilogue as the
-// streaming scan, so the scores are bit-identical.  Scores collect in LDS
-// and leave at the end (no stores in the loop); keys past a row's visible
-// ones get -inf.
+// Prefill scoring (bf16 or FP8, d_I = 128): a workgroup takes 16 query rows
+// of one sequence, two per wavefront with their query blocks resident as MFMA
+// A operands, and a part of up to kMultiKeys keys.  Each 16-key tile is
+// staged once in LDS (bf16: waves 0-3 load 1 KiB each; FP8: waves 0-1; a
+// 32 KiB ring, one barrier per two tiles) and read by all 8 wavefronts, each
+// B fragment feeding both rows' MFMAs, so a key leaves the caches once per 16
+// queries.  Tile layout, MFMA order and epilogue are the streaming scan's, so
+// the scores are bit-identical.  Scores collect in LDS and leave at the end
+// (no stores in the loop); keys past a row's visible ones get -inf.
 constexpr int kMultiRows = 16;
 constexpr int kMultiRpw = 2;  // rows per wavefront
-constexpr int kMultiDepth = 8;
+constexpr int kMultiDepth = 8;  // bf16 ring slots (FP8: twice as many half-size tiles)
 constexpr int kMultiKeys = 1920;  // keys per part: 16 rows x 7.5 KiB of scores in LDS
-template <int MB, bool HAS_W>
+template <int MB, bool HAS_W, int KF>  // KF: 0 bf16, 1 FP8
 __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, int64_t parts) {
+  constexpr bool FP8 = KF == 1;
   constexpr int HI = 16 * MB;
   constexpr int DI = 128;
   constexpr int KS = 4;
-  constexpr int KB = 256;
-  constexpr int TB = kTileBytes;
-  constexpr int DEPTH = kMultiDepth;
+  constexpr int KB = FP8 ? 128 : 256;
+  constexpr int TB = FP8 ? kTileBytes8 : kTileBytes;
+  constexpr int DEPTH = FP8 ? 2 * kMultiDepth : kMultiDepth;
+  constexpr int NLW = TB / 1024;  // loading wavefronts, one 1 KiB load each per tile
+  static_assert(DEPTH <= 16, "wait_tiles covers the ring");
   __shared__ __attribute__((aligned(16))) uint8_t ring[DEPTH][TB];
   __shared__ __attribute__((aligned(16))) float sbuf[kMultiRows][kMultiKeys];
   const int lane = threadIdx.x & 63;
@@ -600,12 +603,13 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
   const int64_t kv = ke < nvmax ? ke : nvmax;
   const int ntiles = kv > kb ? static_cast<int>((kv - kb + kTileKeys - 1) / kTileKeys) : 0;
   const char* kbase = static_cast<const char*>(a.k) + b * a.L * KB;
-  // load w (w < 4) of a tile: keys 4w .. 4w+3 (1 KiB), the streaming scan's
-  // layout (piece p of key kk at slot p ^ kk)
-  const int kk = 4 * (wave & 3) + g;
-  const uint32_t voff = kk * 256 + ((c16 ^ kk) << 4);
+  // load w (w < NLW) of a tile, in the streaming scan's layout.  bf16: keys
+  // 4w .. 4w+3, piece p of key kk at slot p ^ kk.  FP8: keys 8w .. 8w+7,
+  // piece p of key kk at slot (p + kk/2) % 8.
+  const int kk = FP8 ? 8 * (wave % NLW) + (lane >> 3) : 4 * (wave % NLW) + g;
+  const uint32_t voff = FP8 ? kk * 128 + ((((lane & 7) - (kk >> 1)) & 7) << 4) : kk * 256 + ((c16 ^ kk) << 4);
   auto issue = [&](int it) {
-    uint8_t* slot = &ring[it % DEPTH][0] + (wave & 3) * 1024;
+    uint8_t* slot = &ring[it % DEPTH][0] + (wave % NLW) * 1024;
     const int64_t t0 = kb + static_cast<int64_t>(it) * kTileKeys;
     if (t0 + kTileKeys <= a.L) {
       dma16(kbase + t0 * KB, voff, slot);
@@ -615,46 +619,68 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
       dma16(kbase + s * KB + (voff - kk * KB), slot);
     }
   };
-  if (wave < 4) {
+  if (wave < NLW) {
 #pragma unroll
     for (int i = 0; i < DEPTH - 2; ++i)
       if (i < ntiles) issue(i);
   }
-  bf16x8 afrag[kMultiRpw][MB][KS];
+  bf16x8 afrag[kMultiRpw][MB][FP8 ? 1 : KS];
+  i32x8 afrag8[kMultiRpw][MB];
   float wr[kMultiRpw][MB][HAS_W ? 4 : 1];
 #pragma unroll
   for (int i = 0; i < kMultiRpw; ++i) {
     const int64_t row = row0 + kMultiRpw * wave + i;
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + row * HI * DI;
+    if constexpr (FP8) {
+      const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + row * HI * DI;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
+        afrag8[i][mb] = *reinterpret_cast<const i32x8*>(qrow + (mb * 16 + c16) * DI + 32 * g);
+    } else {
+      const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + row * HI * DI;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        afrag[i][mb][ks] = *reinterpret_cast<const bf16x8*>(qrow + (mb * 16 + c16) * DI + ks * 32 + g * 8);
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          afrag[i][mb][ks] = *reinterpret_cast<const bf16x8*>(qrow + (mb * 16 + c16) * DI + ks * 32 + g * 8);
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < (HAS_W ? 4 : 1); ++r) wr[i][mb][r] = HAS_W ? a.w[row * HI + mb * 16 + 4 * g + r] : 1.f;
   }
   // Two tiles per barrier: tiles it and it+1 (slots it%8, (it+1)%8); their
-  // slots are refilled with tiles it+6 and it+7 after the next barrier.
+  // slots are refilled with tiles it+DEPTH-2 and it+DEPTH-1 after the next barrier.
   auto tile = [&](int tt) {
     f32x4 acc[kMultiRpw][MB];
 #pragma unroll
     for (int i = 0; i < kMultiRpw; ++i)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) acc[i][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint8_t* t = &ring[tt % DEPTH][0] + c16 * 256;
-    bf16x8 cur[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) cur[ks] = *reinterpret_cast<const bf16x8*>(t + (((4 * ks + g) ^ c16) << 4));
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    if constexpr (FP8) {  // key c16's dims 32g .. 32g+31: blocks 2g, 2g+1 (rotated by c16 / 2)
+      const uint8_t* t = &ring[tt % DEPTH][0] + c16 * 128;
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(t + (((2 * g + (c16 >> 1)) & 7) << 4));
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(t + (((2 * g + 1 + (c16 >> 1)) & 7) << 4));
+      const i32x8 cur8{static_cast<int>(x0[0]), static_cast<int>(x0[1]), static_cast<int>(x0[2]), static_cast<int>(x0[3]),
+                       static_cast<int>(x1[0]), static_cast<int>(x1[1]), static_cast<int>(x1[2]), static_cast<int>(x1[3])};
 #pragma unroll
       for (int i = 0; i < kMultiRpw; ++i)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          acc[i][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[i][mb][ks], cur[ks], acc[i][mb], 0, 0, 0);
+          acc[i][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afrag8[i][mb], cur8, acc[i][mb], 0, 0, 0, 127, 0,
+                                                                        127);
+    } else {
+      const uint8_t* t = &ring[tt % DEPTH][0] + c16 * 256;
+      bf16x8 cur[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) cur[ks] = *reinterpret_cast<const bf16x8*>(t + (((4 * ks + g) ^ c16) << 4));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int i = 0; i < kMultiRpw; ++i)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            acc[i][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[i][mb][ks], cur[ks], acc[i][mb], 0, 0, 0);
+    }
 #pragma unroll
     for (int i = 0; i < kMultiRpw; ++i) {
       float ps[MB];
@@ -675,14 +701,14 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
     }
   };
   for (int it = 0; it < ntiles; it += 2) {
-    if (wave < 4) {
+    if (wave < NLW) {
       // loads issued after tile it+1's (or it's, at the end) may stay in flight
       const int last = it + 1 < ntiles ? it + 1 : it;
       const int issued = it + DEPTH - 2 < ntiles ? it + DEPTH - 2 : ntiles;  // tiles [0, issued) issued
       wait_tiles<1>(issued - 1 - last);
     }
     __syncthreads();  // tiles it, it+1 in LDS; every wave is done with it-2, it-1
-    if (wave < 4) {
+    if (wave < NLW) {
       if (it + DEPTH - 2 < ntiles) issue(it + DEPTH - 2);  // into tile it-2's slot
       if (it + DEPTH - 1 < ntiles) issue(it + DEPTH - 1);  // into tile it-1's slot
     }
@@ -844,31 +870,38 @@ hipError_t launch_stream(const IndexScoreArgs& a, const IndexCandidates& co, hip
 
 hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t s) {
   if (a.nrows == 0 || a.L == 0) return hipSuccess;
+  const int mb = static_cast<int>(a.HI / 16), ks = static_cast<int>(a.dI / 32);
+  const bool w = a.w != nullptr;
+  // Many query rows of one sequence (prefill), bf16 or FP8 keys in dense
+  // caches: the 16-row kernel reads each key tile once per 16 rows.
+  if ((a.dt == kBF16 || a.dt == kFP8) && ks == 4 && !a.lay.bt && index_multi_rows(a.T, a.HI, a.row0, a.nrows)) {
+    const int64_t parts = (a.L + kMultiKeys - 1) / kMultiKeys;
+    const dim3 grid(static_cast<uint32_t>(a.nrows / kMultiRows * parts));
+    const dim3 block(64 * kMultiRows / kMultiRpw);
+    const int kf = a.dt == kFP8 ? 1 : 0;
+#define CSA_INDEX_MULTI_KF(MB_, KF_)                                                                \
+  if (w) hipLaunchKernelGGL((index_score_multi<MB_, true, KF_>), grid, block, 0, s, a, parts);       \
+  else hipLaunchKernelGGL((index_score_multi<MB_, false, KF_>), grid, block, 0, s, a, parts);
+#define CSA_INDEX_MULTI(MB_)                            \
+  case MB_:                                             \
+    if (kf) { CSA_INDEX_MULTI_KF(MB_, 1) }              \
+    else { CSA_INDEX_MULTI_KF(MB_, 0) }                 \
+    break;
+    switch (mb) {
+      CSA_INDEX_MULTI(1)
+      CSA_INDEX_MULTI(2)
+      CSA_INDEX_MULTI(4)
+      default: return hipErrorInvalidValue;
+    }
+#undef CSA_INDEX_MULTI
+#undef CSA_INDEX_MULTI_KF
+    return hipGetLastError();
+  }
   if (a.dt == kFP8 || a.dt == kMXFP4) {  // d_I = 128 only (index_shape_supported)
     if (a.dI != 128) return hipErrorInvalidValue;
     return launch_stream<false>(a, IndexCandidates{}, s);
   }
   if (a.dt == kBF16) {
-    const int mb = static_cast<int>(a.HI / 16), ks = static_cast<int>(a.dI / 32);
-    const bool w = a.w != nullptr;
-    if (ks == 4 && !a.lay.bt && index_multi_rows(a.T, a.HI, a.row0, a.nrows)) {
-      const int64_t parts = (a.L + kMultiKeys - 1) / kMultiKeys;
-      const dim3 grid(static_cast<uint32_t>(a.nrows / kMultiRows * parts));
-      const dim3 block(64 * kMultiRows / kMultiRpw);
-#define CSA_INDEX_MULTI(MB_)                                                                        \
-  case MB_:                                                                                         \
-    if (w) hipLaunchKernelGGL((index_score_multi<MB_, true>), grid, block, 0, s, a, parts);          \
-    else hipLaunchKernelGGL((index_score_multi<MB_, false>), grid, block, 0, s, a, parts);           \
-    break;
-      switch (mb) {
-        CSA_INDEX_MULTI(1)
-        CSA_INDEX_MULTI(2)
-        CSA_INDEX_MULTI(4)
-        default: return hipErrorInvalidValue;
-      }
-#undef CSA_INDEX_MULTI
-      return hipGetLastError();
-    }
     if (ks == 4) return launch_stream<false>(a, IndexCandidates{}, s);
     if (ks == 2) {
       const int64_t parts = (a.L + kDirectKeysPerWg - 1) / kDirectKeysPerWg;

@@ -121,6 +121,45 @@ def test_index_fp8_exact_on_grid_inputs():
     assert np.array_equal(idx, widx)
 
 
+@pytest.mark.parametrize("HI,grid", [(64, False), (32, False), (64, True)])
+def test_index_fp8_prefill_rows_equal_single_rows_and_oracle(HI, grid):
+    """64 query rows of one sequence (the 16-row prefill kernel) give, row by
+    row, the bits of the same query scored alone (the streaming scan), match
+    the oracle within the fp8 summation bound (exactly on grid inputs), and
+    csa_index_topk keeps the oracle's selection of those scores."""
+    B, T, dI, m, k = 1, 64, 128, 4, 256
+    n_ctx = 4 * 5000 + 1  # three 1920-key parts; the rows' visible counts differ
+    L = -(-n_ctx // m)
+    seed = 700 + HI
+    kw = dict(kind="grid", scale=2.0 ** -4) if grid else dict(scale=dI ** -0.5)
+    q, q_c = both((B, T, HI, dI), seed, "q_idx", dtype=F8, **kw)
+    kk, k_c = both((B, L, dI), seed, "k_idx", dtype=F8, **kw)
+    if grid:
+        w = gen((B, T, HI), seed, "w_idx", dtype=torch.float32, device="cuda", kind="grid", grid=1).abs() + 1.0
+        w_c = (gen((B, T, HI), seed, "w_idx", dtype=torch.float32, device="cpu", kind="grid", grid=1).abs()
+               + 1.0).double().numpy()
+    else:
+        w, w_c = both((B, T, HI), seed, "w_idx", dtype=torch.float32, scale=HI ** -0.5)
+    got = to_np(csa.csa_index_score(q, kk, m, w_idx=w, n_ctx=n_ctx))
+    for t in range(T):
+        one = csa.csa_index_score(q[:, t:t + 1].contiguous(), kk, m, w_idx=w[:, t:t + 1].contiguous(),
+                                  n_ctx=n_ctx - T + 1 + t)
+        assert np.array_equal(got[:, t], to_np(one)[:, 0]), t
+    want = oracle.index_scores(q_c, k_c, m, w=w_c, n_ctx=n_ctx)
+    fin = np.isfinite(want)
+    assert np.array_equal(fin, np.isfinite(got))
+    if grid:
+        assert np.array_equal(got, want)
+    else:
+        for t in range(T):
+            eps = index_eps_fp8(q_c[0, t], w_c[0, t], k_c[0])
+            f = fin[0, t]
+            assert np.all(np.abs(got[0, t][f] - want[0, t][f]) <= eps[f] + 1e-30), t
+    idx = csa.csa_index_topk(q, kk, m, k, w_idx=w, n_ctx=n_ctx).cpu().numpy()
+    nv = np.minimum((n_ctx - T + np.arange(T)) // m, L)
+    assert np.array_equal(idx, oracle.topk(got.astype(np.float64), np.broadcast_to(nv, (B, T)), k))
+
+
 @pytest.mark.parametrize("B,T,L,HI,k,wts", [(16, 1, 250000, 64, 1024, True), (4, 3, 9000, 32, 512, False),
                                              (2, 2, 700, 64, 1024, True), (2, 8, 30000, 16, 256, False),
                                              (4, 4, 60000, 128, 2048, True), (1, 1, 250000, 64, 1024, True),
