@@ -101,7 +101,8 @@ struct Merge {
   // threshold, so the entry is in U and the top-k of U is the row's.  Returns
   // false (nothing written) when a list is missing, U holds fewer than k or
   // more than THREADS * UITEMS entries, or some lthr[p] > theta_U.  nparts <=
-  // THREADS.  U is staged in `stage` (values, then indices).
+  // THREADS.  lthr == nullptr: every list is its part's whole candidate set
+  // (nothing to test).  U is staged in `stage` (values, then indices).
   template <int UITEMS>
   static __device__ bool lists(int k, int nparts, const float* lval, const int32_t* lidx, const int32_t* lcnt,
                                const float* lthr, int64_t lcap, Shared& sh, int32_t* o, float* os) {
@@ -112,7 +113,7 @@ struct Merge {
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lc = tid < nparts ? lcnt[tid] : 0;
-    const float lt = tid < nparts ? lthr[tid] : -INFINITY;
+    const float lt = tid < nparts && lthr ? lthr[tid] : -INFINITY;
     // per wave: any missing list, the lists' total, the largest threshold
     const uint32_t neg = static_cast<uint32_t>(__popcll(__ballot(lc < 0)));
     const uint32_t cnt = static_cast<uint32_t>(lc > 0 ? lc : 0);

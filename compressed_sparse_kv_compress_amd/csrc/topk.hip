@@ -160,6 +160,15 @@ __global__ __launch_bounds__(kMThreads) void topk_merge_kernel(TopkArgs a, int n
                                                           c.lcnt + u0, c.lthr + u0, c.lcap, sh, o, os))
     return;
   const int cap = static_cast<int>(c.cap);
+  // Without short lists the parts' top-k lists serve as the lists when their
+  // union fits (each is its part's whole candidate set, so nothing is left
+  // to test): one selection over at most a quarter of the tile.  The
+  // full-tile path samples a threshold only when k is at most a quarter of
+  // the valid candidates, so two parts of k each would take its radix path.
+  if (!c.lval && static_cast<int64_t>(nparts) * cap <= mrg::kSlots / 4 &&
+      Merge::lists<mrg::kSlots / 4 / kMThreads>(k, nparts, c.cval + u0 * cap, c.cidx + u0 * cap, c.ccnt + u0,
+                                                nullptr, cap, sh, o, os))
+    return;
   Merge::full(k, nparts, cap, c.cval + u0 * cap, c.cidx + u0 * cap, c.ccnt + u0, sh, o, os);
 }
 
