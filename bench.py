@@ -600,11 +600,12 @@ def fp8_storage_step(B: int, steps: int, warmup: int):
     }
 
 
-def prefill_index_topk(queries: int = 4096, reps: int = 3, fp8: bool = False):
+def prefill_index_topk(queries: int = 4096, reps: int = 3, fp8: bool = False, mxfp4: bool = False):
     """csa_index_topk on the CSA prefill-chunk shape: the last `queries` of a
     65,536-token chunk after a 262,144-token prefix (81,920 compressed
     entries, about 82 K visible per query), 64 index heads x 128, k = 1024;
-    bf16, or E4M3 query and keys (the same values rounded to E4M3)."""
+    bf16, E4M3 query and keys (the same values rounded to E4M3), or MXFP4
+    (random E2M1 codes, E8M0 scales 2^-2 .. 2^2)."""
     import compressed_sparse_kv_compress_amd as csa
     HI, dI, m, k = 64, 128, 4, 1024
     prefix, chunk = 262144, 65536
@@ -615,6 +616,14 @@ def prefill_index_topk(queries: int = 4096, reps: int = 3, fp8: bool = False):
                    scale=dI ** -0.5)
     if fp8:
         ki, qi = ki.to(torch.float8_e4m3fn), qi.to(torch.float8_e4m3fn)
+    if mxfp4:
+        del ki, qi
+        nq, nk = queries * HI * dI, L * dI
+        qb = syn.mxfp4_(torch.empty(nq // 2 + nq // 32, dtype=torch.uint8, device="cuda"), 4, syn.TID["q_idx"], nq,
+                        scale_lo=125, scale_hi=129)
+        kb = syn.mxfp4_(torch.empty(nk // 2 + nk // 32, dtype=torch.uint8, device="cuda"), 4, syn.TID["kic"], nk,
+                        scale_lo=125, scale_hi=129)
+        qi, ki = csa.MXFP4(qb, (1, queries, HI, dI)), csa.MXFP4(kb, (1, L, dI))
     wi = syn.fill_(torch.empty((1, queries, HI), device="cuda"), 4, syn.TID["w_idx"], scale=HI ** -0.5)
     ws = torch.zeros(csa.csa_index_topk_workspace(1, queries, L, HI, k), dtype=torch.uint8, device="cuda")
     idx = torch.empty((1, queries, k), dtype=torch.int32, device="cuda")
@@ -636,8 +645,9 @@ def prefill_index_topk(queries: int = 4096, reps: int = 3, fp8: bool = False):
     flop = pairs * HI * dI * 2
     del ki, qi, ws
     torch.cuda.empty_cache()
-    peak = 5000.0 if fp8 else 2500.0
-    return {"queries": queries, "entries": L, "storage": "e4m3" if fp8 else "bf16", "ms_per_call": ms,
+    peak = 10100.0 if mxfp4 else (5000.0 if fp8 else 2500.0)
+    return {"queries": queries, "entries": L, "storage": "mxfp4" if mxfp4 else ("e4m3" if fp8 else "bf16"),
+            "ms_per_call": ms,
             "tflops": flop / (ms * 1e-3) / 1e12, "peak_tflops": peak, "frac_of_peak": flop / (ms * 1e-3) / 1e12 / peak,
             "visible_pairs": pairs,
             "note": "flop = 2 * visible (query, entry) pairs * index heads * index dim, against the dense MFMA peak "
@@ -1009,9 +1019,10 @@ def main():
         prefill["index_topk"] = prefill_index_topk(args.prefill_queries)
         if not args.no_fp8:
             prefill["index_topk_fp8"] = prefill_index_topk(args.prefill_queries, fp8=True)
-            print("# prefill index + top-k, E4M3 q and keys: %.2f ms (%.0f TFLOP/s)"
-                  % (prefill["index_topk_fp8"]["ms_per_call"], prefill["index_topk_fp8"]["tflops"]), file=sys.stderr,
-                  flush=True)
+            prefill["index_topk_mxfp4"] = prefill_index_topk(args.prefill_queries, mxfp4=True)
+            for key, name in (("index_topk_fp8", "E4M3"), ("index_topk_mxfp4", "MXFP4")):
+                print("# prefill index + top-k, %s q and keys: %.2f ms (%.0f TFLOP/s)"
+                      % (name, prefill[key]["ms_per_call"], prefill[key]["tflops"]), file=sys.stderr, flush=True)
         print("# prefill index + top-k: %.2f ms (%.0f TFLOP/s)" % (prefill["index_topk"]["ms_per_call"],
               prefill["index_topk"]["tflops"]), file=sys.stderr, flush=True)
         print("# prefill sparse attention: %.2f ms for %d queries (%.0f TFLOP/s)"

@@ -264,7 +264,7 @@ csa_status_t index_topk_run(const csa::SeqLayout& lay, const void* q_idx, const 
   const int64_t rows = B * T;
   // Many queries per sequence (prefill): the 16-row scoring kernel reads each
   // key once per 16 queries; it writes scores, so the stand-alone top-k follows.
-  const bool multi = (dtype == CSA_BF16 || dtype == CSA_FP8) && d_I == 128 && !lay.bt &&
+  const bool multi = (dtype == CSA_BF16 || dtype == CSA_FP8 || dtype == CSA_MXFP4) && d_I == 128 && !lay.bt &&
                      csa::index_multi_rows(T, H_I, 0, rows);
   if (!multi && ws != nullptr && L > 0 && csa::index_topk_fusable(rows, L, H_I, d_I, k, to_dt(dtype)) &&
       ws_bytes >= csa::index_topk_fused_ws_bytes(rows, L, k)) {

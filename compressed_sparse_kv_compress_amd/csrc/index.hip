@@ -561,11 +561,12 @@ __global__ __launch_bounds__(64 * (KF ? kWaves8 : kWaves), 1) void index_score_s
   }
 }
 
-// Prefill scoring (bf16 or FP8, d_I = 128): a workgroup takes 16 query rows
-// of one sequence, two per wavefront with their query blocks resident as MFMA
-// A operands, and a part of up to kMultiKeys keys.  Each 16-key tile is
-// staged once in LDS (bf16: waves 0-3 load 1 KiB each; FP8: waves 0-1; a
-// 32 KiB ring, one barrier per two tiles) and read by all 8 wavefronts, each
+// Prefill scoring (bf16, FP8 or MXFP4, d_I = 128): a workgroup takes 16 query
+// rows of one sequence, two per wavefront with their query blocks resident as
+// MFMA A operands, and a part of up to kMultiKeys keys.  Each 16-key tile is
+// staged once in LDS (bf16: waves 0-3 load 1 KiB each; FP8: waves 0-1;
+// MXFP4: wave 0 loads the codes and the scales; a ring of up to 32 KiB, one
+// barrier per two tiles) and read by all 8 wavefronts, each
 // B fragment feeding both rows' MFMAs, so a key leaves the caches once per 16
 // queries.  Tile layout, MFMA order and epilogue are the streaming scan's, so
 // the scores are bit-identical.  Scores collect in LDS and leave at the end
@@ -574,16 +575,17 @@ constexpr int kMultiRows = 16;
 constexpr int kMultiRpw = 2;  // rows per wavefront
 constexpr int kMultiDepth = 8;  // bf16 ring slots (FP8: twice as many half-size tiles)
 constexpr int kMultiKeys = 1920;  // keys per part: 16 rows x 7.5 KiB of scores in LDS
-template <int MB, bool HAS_W, int KF>  // KF: 0 bf16, 1 FP8
+template <int MB, bool HAS_W, int KF>  // KF: 0 bf16, 1 FP8, 2 MXFP4
 __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, int64_t parts) {
-  constexpr bool FP8 = KF == 1;
+  constexpr bool FP8 = KF == 1, FP4 = KF == 2;
   constexpr int HI = 16 * MB;
   constexpr int DI = 128;
   constexpr int KS = 4;
-  constexpr int KB = FP8 ? 128 : 256;
-  constexpr int TB = FP8 ? kTileBytes8 : kTileBytes;
-  constexpr int DEPTH = FP8 ? 2 * kMultiDepth : kMultiDepth;
-  constexpr int NLW = TB / 1024;  // loading wavefronts, one 1 KiB load each per tile
+  constexpr int KB = FP4 ? 64 : (FP8 ? 128 : 256);  // code bytes per key
+  constexpr int TB = FP4 ? kTileBytes4 : (FP8 ? kTileBytes8 : kTileBytes);
+  constexpr int DEPTH = KF ? 2 * kMultiDepth : kMultiDepth;
+  constexpr int NLW = FP4 ? 1 : TB / 1024;  // loading wavefronts
+  constexpr int LPT = FP4 ? 2 : 1;          // loads per tile and loading wavefront
   static_assert(DEPTH <= 16, "wait_tiles covers the ring");
   __shared__ __attribute__((aligned(16))) uint8_t ring[DEPTH][TB];
   __shared__ __attribute__((aligned(16))) float sbuf[kMultiRows][kMultiKeys];
@@ -603,20 +605,30 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
   const int64_t kv = ke < nvmax ? ke : nvmax;
   const int ntiles = kv > kb ? static_cast<int>((kv - kb + kTileKeys - 1) / kTileKeys) : 0;
   const char* kbase = static_cast<const char*>(a.k) + b * a.L * KB;
+  // MXFP4 scales follow the code bytes of all B * L keys, 4 per key.
+  const char* sbase = static_cast<const char*>(a.k) + a.B * a.L * KB + b * a.L * 4;
   // load w (w < NLW) of a tile, in the streaming scan's layout.  bf16: keys
   // 4w .. 4w+3, piece p of key kk at slot p ^ kk.  FP8: keys 8w .. 8w+7,
-  // piece p of key kk at slot (p + kk/2) % 8.
-  const int kk = FP8 ? 8 * (wave % NLW) + (lane >> 3) : 4 * (wave % NLW) + g;
-  const uint32_t voff = FP8 ? kk * 128 + ((((lane & 7) - (kk >> 1)) & 7) << 4) : kk * 256 + ((c16 ^ kk) << 4);
+  // piece p of key kk at slot (p + kk/2) % 8.  MXFP4: the codes (block p of
+  // key kk at slot (p + kk/4) % 4), then key l%16's four scales at 1024 + 4l.
+  const int kk = FP4 ? lane >> 2 : (FP8 ? 8 * (wave % NLW) + (lane >> 3) : 4 * (wave % NLW) + g);
+  const uint32_t voff = FP4 ? kk * 64 + ((((lane & 3) - (kk >> 2)) & 3) << 4)
+                            : (FP8 ? kk * 128 + ((((lane & 7) - (kk >> 1)) & 7) << 4) : kk * 256 + ((c16 ^ kk) << 4));
   auto issue = [&](int it) {
     uint8_t* slot = &ring[it % DEPTH][0] + (wave % NLW) * 1024;
     const int64_t t0 = kb + static_cast<int64_t>(it) * kTileKeys;
     if (t0 + kTileKeys <= a.L) {
       dma16(kbase + t0 * KB, voff, slot);
+      if constexpr (FP4) dma4(sbase + t0 * 4, c16 * 4, slot + 1024);
     } else {
       int64_t s = t0 + kk;
       s = s < a.L - 1 ? s : a.L - 1;
       dma16(kbase + s * KB + (voff - kk * KB), slot);
+      if constexpr (FP4) {
+        int64_t s1 = t0 + c16;
+        s1 = s1 < a.L - 1 ? s1 : a.L - 1;
+        dma4(sbase + s1 * 4, slot + 1024);
+      }
     }
   };
   if (wave < NLW) {
@@ -624,13 +636,24 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
     for (int i = 0; i < DEPTH - 2; ++i)
       if (i < ntiles) issue(i);
   }
-  bf16x8 afrag[kMultiRpw][MB][FP8 ? 1 : KS];
+  bf16x8 afrag[kMultiRpw][MB][KF ? 1 : KS];
   i32x8 afrag8[kMultiRpw][MB];
+  int qsc[kMultiRpw][MB];  // MXFP4: E8M0 scale of this lane's 32 query elements
   float wr[kMultiRpw][MB][HAS_W ? 4 : 1];
 #pragma unroll
   for (int i = 0; i < kMultiRpw; ++i) {
     const int64_t row = row0 + kMultiRpw * wave + i;
-    if constexpr (FP8) {
+    if constexpr (FP4) {
+      const uint8_t* qb = static_cast<const uint8_t*>(a.q);
+      const uint8_t* qs = qb + a.B * a.T * HI * 64;  // scales follow all code bytes
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(qb + (row * HI + mb * 16 + c16) * 64 + 16 * g);
+        afrag8[i][mb] = i32x8{static_cast<int>(x[0]), static_cast<int>(x[1]), static_cast<int>(x[2]),
+                              static_cast<int>(x[3]), 0, 0, 0, 0};
+        qsc[i][mb] = qs[(row * HI + mb * 16 + c16) * 4 + g];
+      }
+    } else if constexpr (FP8) {
       const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + row * HI * DI;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
@@ -656,7 +679,19 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
     for (int i = 0; i < kMultiRpw; ++i)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) acc[i][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (FP8) {  // key c16's dims 32g .. 32g+31: blocks 2g, 2g+1 (rotated by c16 / 2)
+    if constexpr (FP4) {  // key c16's code block g (rotated by c16 / 4) and its E8M0 scale (copy g)
+      const uint8_t* t = &ring[tt % DEPTH][0];
+      const u32x4 x = *reinterpret_cast<const u32x4*>(t + c16 * 64 + (((g + (c16 >> 2)) & 3) << 4));
+      const int ksc = static_cast<int>((*reinterpret_cast<const uint32_t*>(t + 1024 + 64 * g + 4 * c16) >> (8 * g)) & 0xffu);
+      const i32x8 cur4{static_cast<int>(x[0]), static_cast<int>(x[1]), static_cast<int>(x[2]), static_cast<int>(x[3]),
+                       0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < kMultiRpw; ++i)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)  // format 4 = E2M1 for both operands, per-lane E8M0 scales
+          acc[i][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afrag8[i][mb], cur4, acc[i][mb], 4, 4, 0,
+                                                                        qsc[i][mb], 0, ksc);
+    } else if constexpr (FP8) {  // key c16's dims 32g .. 32g+31: blocks 2g, 2g+1 (rotated by c16 / 2)
       const uint8_t* t = &ring[tt % DEPTH][0] + c16 * 128;
       const u32x4 x0 = *reinterpret_cast<const u32x4*>(t + (((2 * g + (c16 >> 1)) & 7) << 4));
       const u32x4 x1 = *reinterpret_cast<const u32x4*>(t + (((2 * g + 1 + (c16 >> 1)) & 7) << 4));
@@ -705,7 +740,7 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
       // loads issued after tile it+1's (or it's, at the end) may stay in flight
       const int last = it + 1 < ntiles ? it + 1 : it;
       const int issued = it + DEPTH - 2 < ntiles ? it + DEPTH - 2 : ntiles;  // tiles [0, issued) issued
-      wait_tiles<1>(issued - 1 - last);
+      wait_tiles<LPT>(issued - 1 - last);
     }
     __syncthreads();  // tiles it, it+1 in LDS; every wave is done with it-2, it-1
     if (wave < NLW) {
@@ -872,19 +907,21 @@ hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t s) {
   if (a.nrows == 0 || a.L == 0) return hipSuccess;
   const int mb = static_cast<int>(a.HI / 16), ks = static_cast<int>(a.dI / 32);
   const bool w = a.w != nullptr;
-  // Many query rows of one sequence (prefill), bf16 or FP8 keys in dense
-  // caches: the 16-row kernel reads each key tile once per 16 rows.
-  if ((a.dt == kBF16 || a.dt == kFP8) && ks == 4 && !a.lay.bt && index_multi_rows(a.T, a.HI, a.row0, a.nrows)) {
+  // Many query rows of one sequence (prefill), bf16, FP8 or MXFP4 keys in
+  // dense caches: the 16-row kernel reads each key tile once per 16 rows.
+  if ((a.dt == kBF16 || a.dt == kFP8 || a.dt == kMXFP4) && ks == 4 && !a.lay.bt &&
+      index_multi_rows(a.T, a.HI, a.row0, a.nrows)) {
     const int64_t parts = (a.L + kMultiKeys - 1) / kMultiKeys;
     const dim3 grid(static_cast<uint32_t>(a.nrows / kMultiRows * parts));
     const dim3 block(64 * kMultiRows / kMultiRpw);
-    const int kf = a.dt == kFP8 ? 1 : 0;
+    const int kf = a.dt == kMXFP4 ? 2 : (a.dt == kFP8 ? 1 : 0);
 #define CSA_INDEX_MULTI_KF(MB_, KF_)                                                                \
   if (w) hipLaunchKernelGGL((index_score_multi<MB_, true, KF_>), grid, block, 0, s, a, parts);       \
   else hipLaunchKernelGGL((index_score_multi<MB_, false, KF_>), grid, block, 0, s, a, parts);
 #define CSA_INDEX_MULTI(MB_)                            \
   case MB_:                                             \
-    if (kf) { CSA_INDEX_MULTI_KF(MB_, 1) }              \
+    if (kf == 2) { CSA_INDEX_MULTI_KF(MB_, 2) }         \
+    else if (kf == 1) { CSA_INDEX_MULTI_KF(MB_, 1) }    \
     else { CSA_INDEX_MULTI_KF(MB_, 0) }                 \
     break;
     switch (mb) {

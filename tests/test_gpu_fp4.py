@@ -110,3 +110,43 @@ def test_index_topk_mxfp4_single_pass_equals_score_then_select(B, T, L, HI, k, l
                                   tpos=np.array([n_ctx - T + t]))
     eps = index_eps(q_c[b, t], None, k_c[b])[:nv]
     assert near_tie_check(idx1[b, t].cpu().numpy(), want[0, 0], osc[0, 0], nv, k, eps) <= 2
+
+
+@pytest.mark.parametrize("scaled", [False, True])
+def test_index_mxfp4_prefill_rows_equal_single_rows_and_oracle(scaled):
+    """64 query rows of one sequence (the 16-row prefill kernel) give, row by
+    row, the bits of the same query scored alone (the streaming scan); with
+    unit scales they equal the oracle exactly, with scales 2^-2 .. 2^2 and fp32
+    head weights within the summation bound; csa_index_topk keeps the oracle's
+    selection of those scores."""
+    B, T, HI, dI, m, k = 1, 64, 64, 128, 4, 256
+    n_ctx = 4 * 5000 + 1  # three 1920-key parts; the rows' visible counts differ
+    L = -(-n_ctx // m)
+    lo, hi = (125, 129) if scaled else (127, 127)
+    q, q_c = mx_both((B, T, HI, dI), 900 + scaled, "q_idx", lo, hi)
+    kk, k_c = mx_both((B, L, dI), 900 + scaled, "k_idx", lo, hi)
+    w = w_c = None
+    if scaled:
+        w, w_c = both((B, T, HI), 900, "w_idx", dtype=torch.float32, kind="uniform")
+    got = to_np(csa.csa_index_score(q, kk, m, w_idx=w, n_ctx=n_ctx))
+    ncode = T * HI * dI // 2
+    for t in range(T):  # row t as its own one-query MXFP4 tensor: its codes, then its scales
+        codes = q.data[t * HI * dI // 2:(t + 1) * HI * dI // 2]
+        scales = q.data[ncode + t * HI * dI // 32:ncode + (t + 1) * HI * dI // 32]
+        qt = csa.MXFP4(torch.cat([codes, scales]).contiguous(), (1, 1, HI, dI))
+        one = csa.csa_index_score(qt, kk, m, w_idx=None if w is None else w[:, t:t + 1].contiguous(),
+                                  n_ctx=n_ctx - T + 1 + t)
+        assert np.array_equal(got[:, t], to_np(one)[:, 0]), t
+    want = oracle.index_scores(q_c, k_c, m, w=w_c, n_ctx=n_ctx)
+    fin = np.isfinite(want)
+    assert np.array_equal(fin, np.isfinite(got))
+    if not scaled:
+        assert np.array_equal(got, want)
+    else:
+        for t in range(T):
+            eps = index_eps(q_c[0, t], w_c[0, t], k_c[0])
+            f = fin[0, t]
+            assert np.all(np.abs(got[0, t][f] - want[0, t][f]) <= eps[f] + 1e-30), t
+    idx = csa.csa_index_topk(q, kk, m, k, w_idx=w, n_ctx=n_ctx).cpu().numpy()
+    nv = np.minimum((n_ctx - T + np.arange(T)) // m, L)
+    assert np.array_equal(idx, oracle.topk(got.astype(np.float64), np.broadcast_to(nv, (B, T)), k))
