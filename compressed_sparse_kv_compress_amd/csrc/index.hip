@@ -22,6 +22,7 @@
 // workgroup per CU, so every wavefront streams megabytes with one prologue.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "merge.hpp"
 #include "select.hpp"
 
 namespace csa {
@@ -154,6 +155,7 @@ constexpr int kPartKeys = 64 * kWaves * 64;  // 16384 >= 4 * kMaxKeysPerWave
 constexpr int kCandStage = 2048;             // largest cap staged in LDS
 constexpr int kListStage = 1024;             // largest compact list staged in LDS
 static_assert(4 * kMaxKeysPerWave <= kPartKeys, "a part fits the selection tile");
+static_assert(kListStage >= kListMax, "the longest list fits its LDS stage");
 static_assert(sizeof(PartSel<kWaves>::Shared) + (kCandStage + 64) * 8 + (kListStage + 64) * 8 <=
                   kWaves * kDepth * kTileBytes,
               "selection state fits the ring");
@@ -179,8 +181,12 @@ __device__ __forceinline__ float part_score(const float (*sbuf)[kScoreSlots<NW>]
   return sbuf[T % NW][sb_pos(T / NW, o % kTileKeys)];
 }
 
+// Compact lists: a row with P non-empty parts (nv visible entries, part_keys
+// keys per part) lists ceil(2k / P) per part; with P * cap <= kMergeUnion its
+// parts hand the merge their whole candidate sets (count kWholePart).
 template <int NW>
 __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t slot, int64_t kb, int nkv,
+                                            int64_t nv, int64_t part_keys,
                                             const float (*sbuf)[kScoreSlots<NW>], uint8_t* scratch) {
   using PS = PartSel<NW>;
   constexpr int IT = kPartKeys / (64 * NW);  // entries per thread
@@ -197,8 +203,8 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
     }
     if (tid == 0) {
       co.ccnt[slot] = nkv;
-      if (co.lval) {  // no compact list: an empty part contributes nothing, a short one sends the merge to the full lists
-        co.lcnt[slot] = nkv == 0 ? 0 : -1;
+      if (co.lval) {  // no compact list: an empty part contributes nothing, a short one its whole candidate set
+        co.lcnt[slot] = nkv == 0 ? 0 : mrg::kWholePart;
         co.lthr[slot] = -INFINITY;
       }
     }
@@ -210,7 +216,11 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
   int32_t* li = reinterpret_cast<int32_t*>(sv + kCandStage + 64);
   float* lv = reinterpret_cast<float*>(li + kListStage + 64);
   const uint32_t lane = threadIdx.x & 63;
-  const int lcap = static_cast<int>(co.lcap);  // <= kListStage (4 or more parts, 4096 entries in all)
+  const int lcap = static_cast<int>(co.lcap);  // <= kListStage
+  const int64_t prow = nv > 0 ? (nv + part_keys - 1) / part_keys : 1;  // the row's non-empty parts
+  const bool whole = co.lval && prow * co.cap <= kMergeUnion;
+  int64_t rrow = (2 * co.cap + prow - 1) / prow;
+  if (rrow > co.cap) rrow = co.cap;
   PS::zero(ss);
   // Thread t holds entries IT*t .. IT*t+IT-1 of the part: tiles TPT*t ..
   // TPT*t+TPT-1 (tile T is tile T / NW of wavefront T % NW), 16 consecutive
@@ -247,7 +257,7 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
         si[pos] = o0 + j;
         sv[pos] = part_score<NW>(sbuf, o0 + j);
       },
-      co.lval ? static_cast<uint32_t>(co.lrank) : 0u,
+      co.lval && !whole ? static_cast<uint32_t>(rrow) : 0u,
       [&](uint32_t pos, float v, uint32_t e) {
         const uint32_t p = pos < static_cast<uint32_t>(lcap) ? pos : kListStage + lane;  // past lcap: dropped
         li[p] = static_cast<int32_t>(e);
@@ -258,7 +268,12 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
     ov[i] = sv[i];
     oi[i] = static_cast<int32_t>(kb + si[i]);
   }
-  if (co.lval) {
+  if (co.lval && whole) {
+    if (tid == 0) {
+      co.lcnt[slot] = mrg::kWholePart;
+      co.lthr[slot] = -INFINITY;
+    }
+  } else if (co.lval) {
     const bool fits = cnt2 <= static_cast<uint32_t>(lcap);
     if (fits) {
       for (int i = tid; i < static_cast<int>(cnt2); i += 64 * NW) {
@@ -535,8 +550,8 @@ __global__ __launch_bounds__(64 * (KF ? kWaves8 : kWaves), 1) void index_score_s
 
   __syncthreads();
   if constexpr (TOPK) {
-    part_select<NW>(co, lrow * parts + part, kb, ntiles > 0 ? static_cast<int>(kv - kb) : 0, sbuf,
-                    &ring[0][0][0]);
+    part_select<NW>(co, lrow * parts + part, kb, ntiles > 0 ? static_cast<int>(kv - kb) : 0, nv,
+                    kWaves * per_wave, sbuf, &ring[0][0][0]);
     return;
   }
   // Write the workgroup's scores [kb, ke) in key order; keys past the visible

@@ -125,9 +125,14 @@ hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t s);
 // nparts <= 256).  fused: the candidates cover every visible entry of rows
 // with at most k of them (there is no score matrix to read).
 hipError_t launch_topk_merge(const TopkArgs& a, int64_t nparts, const IndexCandidates& c, bool fused, hipStream_t s);
-// Compact-list geometry for nparts parts and top-k: the rank (0: no lists)
-// and the list capacity.  The merge stages at most kMergeUnion list entries.
+// Compact-list geometry for nparts parts and top-k: the rank of a row whose
+// parts all hold entries (0: no lists) and the list capacity.  A row with
+// fewer non-empty parts P (a shorter sequence of a varlen batch) lists
+// ceil(2k / P) per part, so the capacity covers P >= 5; rows with P * k <=
+// kMergeUnion merge their parts' whole candidate sets instead.  The merge
+// stages at most kMergeUnion list entries.
 constexpr int64_t kMergeUnion = 4096;
+constexpr int64_t kListMax = 1024;  // longest list a part stages in LDS
 inline void compact_list_plan(int64_t nparts, int64_t k, int64_t* lrank, int64_t* lcap) {
   const int64_t r = (2 * k + nparts - 1) / nparts;  // the lists hold at least 2k entries in all
   if (nparts < 4 || 4 * r > k || nparts * 2 * r > kMergeUnion) {
@@ -136,7 +141,9 @@ inline void compact_list_plan(int64_t nparts, int64_t k, int64_t* lrank, int64_t
     return;
   }
   *lrank = r;
-  *lcap = 2 * r;
+  const int64_t r5 = (2 * k + 4) / 5;  // the rank of a row with 5 non-empty parts
+  *lcap = 2 * r5 < kListMax ? 2 * r5 : kListMax;
+  if (*lcap < 2 * r) *lcap = 2 * r;
 }
 
 // Indexer scan fused with the part stage of the top-k (no score matrix): the

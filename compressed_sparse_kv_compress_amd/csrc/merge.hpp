@@ -14,6 +14,7 @@ namespace csa {
 namespace mrg {
 
 constexpr int kStage = 2048;  // outputs up to this size are staged in LDS, then stored coalesced
+constexpr int32_t kWholePart = -2;  // list count of a part kept whole: its list is its candidate set
 constexpr int kSlots = 16384;  // candidate slots one merge holds
 
 // A tile of up to THREADS * ITEMS scores staged in LDS: thread t owns entries
@@ -102,18 +103,25 @@ struct Merge {
   // false (nothing written) when a list is missing, U holds fewer than k or
   // more than THREADS * UITEMS entries, or some lthr[p] > theta_U.  nparts <=
   // THREADS.  lthr == nullptr: every list is its part's whole candidate set
-  // (nothing to test).  U is staged in `stage` (values, then indices).
+  // (nothing to test).  lcnt[p] == kWholePart: part p was kept whole (at most
+  // k entries, no list); its list is its candidate set, the ccnt[p] entries
+  // at cval / cidx + p * ccap, all of them (threshold -inf).  U is staged in
+  // `stage` (values, then indices).
   template <int UITEMS>
   static __device__ bool lists(int k, int nparts, const float* lval, const int32_t* lidx, const int32_t* lcnt,
-                               const float* lthr, int64_t lcap, Shared& sh, int32_t* o, float* os) {
+                               const float* lthr, int64_t lcap, Shared& sh, int32_t* o, float* os,
+                               const float* cval = nullptr, const int32_t* cidx = nullptr,
+                               const int32_t* ccnt = nullptr, int64_t ccap = 0) {
     static_assert(2 * THREADS * UITEMS <= T::kFloats, "the union fits the stage");
     using USel = sel::Select<THREADS, UITEMS>;
     constexpr int kU = THREADS * UITEMS;
     if (k > kStage / 2) return false;  // the output is staged in half of si (past the list offsets)
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
-    const int lc = tid < nparts ? lcnt[tid] : 0;
-    const float lt = tid < nparts && lthr ? lthr[tid] : -INFINITY;
+    int lc = tid < nparts ? lcnt[tid] : 0;
+    const bool whole = lc == kWholePart && ccnt != nullptr;
+    if (whole) lc = ccnt[tid];
+    const float lt = tid < nparts && lthr && !whole ? lthr[tid] : -INFINITY;
     // per wave: any missing list, the lists' total, the largest threshold
     const uint32_t neg = static_cast<uint32_t>(__popcll(__ballot(lc < 0)));
     const uint32_t cnt = static_cast<uint32_t>(lc > 0 ? lc : 0);
@@ -142,65 +150,44 @@ struct Merge {
     }
     if (tid < nparts) {
       uoff[tid] = before + incl - cnt;
-      ucnt[tid] = static_cast<int32_t>(cnt);
+      ucnt[tid] = whole ? -static_cast<int32_t>(cnt) : static_cast<int32_t>(cnt);  // negative: a whole part
     }
     __syncthreads();
-    // U into LDS (values, then indices).  Lists of at most UITEMS * tpp
-    // slots: tpp = THREADS / nparts threads per list, UITEMS slots each, all
-    // loads issued before any store (one memory round trip; the slots are
-    // read up to the list's capacity, so no load waits for its count).
-    // Longer lists: every (part, slot) pair in batches.  U holds at most kU
-    // entries (checked above), so the slot arithmetic fits 32 bits.
+    // U into LDS (values, then indices).  Entry e of U is entry e - uoff[p]
+    // of part p's list (of its candidate set for a whole part), p the last
+    // part with uoff[p] <= e (a binary search over the offsets in LDS: empty
+    // parts share their successor's offset, so p is the part that holds e);
+    // each thread issues all its loads before its stores.  U holds at most
+    // kU entries (checked above), so the arithmetic fits 32 bits.
     float* uval = sh.stage;
     int32_t* uidx = reinterpret_cast<int32_t*>(sh.stage + kU);
-    const int tpp = THREADS / nparts;
-    if (lcap <= static_cast<int64_t>(UITEMS) * tpp) {
-      const int cap = static_cast<int>(lcap);
-      const int p = tid / tpp, li = tid - (tid / tpp) * tpp;
-      const int pp = p < nparts ? p : 0;
-      const float* lvp = lval + static_cast<int64_t>(pp) * cap;
-      const int32_t* lip = lidx + static_cast<int64_t>(pp) * cap;
+    {
       float tv[UITEMS];
       int32_t tx[UITEMS];
 #pragma unroll
       for (int r = 0; r < UITEMS; ++r) {
-        const int i = li + r * tpp;
-        const int ic = i < cap ? i : 0;
-        tv[r] = lvp[ic];
-        tx[r] = lip[ic];
+        const uint32_t e = static_cast<uint32_t>(r * THREADS + tid);
+        const uint32_t ec = e < total ? e : 0u;
+        int lo = 0, hi = nparts - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (uoff[mid] <= ec) lo = mid;
+          else hi = mid - 1;
+        }
+        const int64_t jj = static_cast<int64_t>(ec - uoff[lo]);
+        const bool wp = ucnt[lo] < 0;  // a whole part (only when ccnt was given)
+        const float* vb = wp ? cval : lval;
+        const int32_t* ib = wp ? cidx : lidx;
+        const int64_t at = static_cast<int64_t>(lo) * (wp ? ccap : lcap) + jj;
+        tv[r] = vb[at];
+        tx[r] = ib[at];
       }
-      const int n = p < nparts ? ucnt[p] : 0;
-      const uint32_t off = p < nparts ? uoff[p] : 0u;
 #pragma unroll
       for (int r = 0; r < UITEMS; ++r) {
-        const int i = li + r * tpp;
-        if (i < n) {
-          uval[off + i] = tv[r];
-          uidx[off + i] = tx[r];
-        }
-      }
-    } else {
-      const int64_t nslots = static_cast<int64_t>(nparts) * lcap;
-      constexpr int kBatch = 16;
-      for (int64_t i0 = 0; i0 < nslots; i0 += static_cast<int64_t>(THREADS) * kBatch) {
-        float tv[kBatch];
-        int32_t tx[kBatch];
-#pragma unroll
-        for (int r = 0; r < kBatch; ++r) {
-          const int64_t i = i0 + r * THREADS + tid;
-          const int64_t ic = i < nslots ? i : 0;
-          tv[r] = lval[ic];
-          tx[r] = lidx[ic];
-        }
-#pragma unroll
-        for (int r = 0; r < kBatch; ++r) {
-          const int64_t i = i0 + r * THREADS + tid;
-          const int p = static_cast<int>(i / lcap);
-          const int j = static_cast<int>(i - static_cast<int64_t>(p) * lcap);
-          if (i < nslots && j < ucnt[p]) {
-            uval[uoff[p] + j] = tv[r];
-            uidx[uoff[p] + j] = tx[r];
-          }
+        const uint32_t e = static_cast<uint32_t>(r * THREADS + tid);
+        if (e < total) {
+          uval[e] = tv[r];
+          uidx[e] = tx[r];
         }
       }
     }

@@ -156,10 +156,11 @@ __global__ __launch_bounds__(kMThreads) void topk_merge_kernel(TopkArgs a, int n
   float* os = a.out_score ? a.out_score + lrow * a.k : nullptr;
   const int k = static_cast<int>(a.k);
   const int64_t u0 = lrow * nparts;
-  if (c.lval && Merge::lists<mrg::kSlots / 4 / kMThreads>(k, nparts, c.lval + u0 * c.lcap, c.lidx + u0 * c.lcap,
-                                                          c.lcnt + u0, c.lthr + u0, c.lcap, sh, o, os))
-    return;
   const int cap = static_cast<int>(c.cap);
+  if (c.lval && Merge::lists<mrg::kSlots / 4 / kMThreads>(k, nparts, c.lval + u0 * c.lcap, c.lidx + u0 * c.lcap,
+                                                          c.lcnt + u0, c.lthr + u0, c.lcap, sh, o, os,
+                                                          c.cval + u0 * cap, c.cidx + u0 * cap, c.ccnt + u0, cap))
+    return;
   // Without short lists the parts' top-k lists serve as the lists when their
   // union fits (each is its part's whole candidate set, so nothing is left
   // to test): one selection over at most a quarter of the tile.  The
