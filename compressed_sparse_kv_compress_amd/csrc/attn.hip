@@ -335,30 +335,26 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
   // Pipeline over NS stage buffers: K of stage c+NS is issued as soon as
   // every wave is done with QK of stage c (barrier B), V of stage c+NS-1 once
   // every wave is done with PV of stage c-1 (barrier A); K therefore keeps NS
-  // stages in flight, V NS-1.  The row flags have NS+1 buffers because
-  // K(c+NS) sets them while stage c still reads its own.
+  // stages in flight, V NS-1.  Before the loop every buffer is free, so the
+  // first NS stages of both K and V are issued at once (a split of few stages
+  // then waits for one gather round trip less).  The row flags have NS+1
+  // buffers because K(c+NS) sets them while stage c still reads its own.
   auto issue = [&](int st) {
     issue_rows<D, F8, SPARSE, NT>(cbase, rbase, dummy, sidx, ring + (st % C::NS) * C::STAGE + moff, pitch,
                           rb0 + st * C::ROWS + row0, n_cmp, rb0, re0, win0, wrap, lane,
                           mat ? nullptr : okf[st % (C::NS + 1)] + row0);
   };
   auto prime = [&]() {
-    for (int st = 0; st < C::NS - 1 + (mat == 0 ? 1 : 0); ++st)
+    for (int st = 0; st < C::NS; ++st)
       if (st < nst) issue(st);
   };
 
   // HCA rows need nothing but their position, so the first stages are on
   // their way before Q is even requested; CSA rows need the split's indices
   // (cached in LDS once, so that the staging loop issues no loads into
-  // registers, whose waits would also drain the ring).
+  // registers, whose waits would also drain the ring), requested right after
+  // Q so that both arrive in one round trip.
   if (!SPARSE) prime();
-  if (SPARSE) {  // cache rows of the split's compressed slots (an implicit 0 .. nv-1 list when idx is null)
-    const int64_t ce = r_end < rm.n_cmp ? r_end : rm.n_cmp;
-    for (int64_t v = r_begin + threadIdx.x; v < ce; v += 64 * kWaves) {
-      const int64_t s = a.idx ? a.idx[bt * a.k + v] : v;
-      sidx[v - r_begin] = (s >= 0 && s < a.L) ? static_cast<int>(cache_row(a.lay, a.L, b, s)) : -1;
-    }
-  }
   const int h0 = static_cast<int>(hg * kHeadsPerWg + hq * kHeadsPerWave);
   // Q fragments (B operand of K Q^T): head h0 + c16, dims dh*DH + ks*32 + 8g .. +8.
   bf16x8 qf[KSQ];
@@ -366,6 +362,13 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (bt * a.H + h0 + c16) * D + dh * C::DH + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KSQ; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
+  }
+  if (SPARSE) {  // cache rows of the split's compressed slots (an implicit 0 .. nv-1 list when idx is null)
+    const int64_t ce = r_end < rm.n_cmp ? r_end : rm.n_cmp;
+    for (int64_t v = r_begin + threadIdx.x; v < ce; v += 64 * kWaves) {
+      const int64_t s = a.idx ? a.idx[bt * a.k + v] : v;
+      sidx[v - r_begin] = (s >= 0 && s < a.L) ? static_cast<int>(cache_row(a.lay, a.L, b, s)) : -1;
+    }
   }
   wait_vmcnt<0>();
   __syncthreads();
@@ -384,7 +387,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma(AttnArgs a, int nsplit) {
     const int ahead = C::NS - 1 < nst - 1 - c ? C::NS - 1 : nst - 1 - c;
     if (mat == 0) wait_stages<C::NI, C::NS>(ahead);  // this wave's K rows of stage c
     __syncthreads();  // A: K(c) in LDS; every wave is done with PV(c-1)
-    if (mat == 1 && c + C::NS - 1 < nst) issue(c + C::NS - 1);
+    if (mat == 1 && c >= 1 && c + C::NS - 1 < nst) issue(c + C::NS - 1);  // V(NS-1) went with the first stages
     const uint8_t* Ks = ring + buf * C::STAGE;
     const uint8_t* Vs = Ks + C::KBYTES;
 

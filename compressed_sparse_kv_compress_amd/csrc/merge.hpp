@@ -105,10 +105,17 @@ struct Merge {
   // THREADS.  lthr == nullptr: every list is its part's whole candidate set
   // (nothing to test).  lcnt[p] == kWholePart: part p was kept whole (at most
   // k entries, no list); its list is its candidate set, the ccnt[p] entries
-  // at cval / cidx + p * ccap, all of them (threshold -inf).  U is staged in
-  // `stage` (values, then indices).
+  // at cval / cidx + p * ccap, all of them (threshold -inf).
+  //
+  // U is read in one of two ways.  Usually every list holds at most
+  // S = THREADS * UITEMS / nparts entries: then U stays a padded grid, entry
+  // e = p * S + j being slot j of part p's list (valid for j < lcnt[p]),
+  // requested together with the counts, so one memory round trip brings it
+  // in; grid order is still index order.  Otherwise U is packed into LDS by
+  // a binary search of each entry's part over the list offsets (a second
+  // round trip, any list lengths).
   template <int UITEMS>
-  static __device__ bool lists(int k, int nparts, const float* lval, const int32_t* lidx, const int32_t* lcnt,
+  static __device__ __forceinline__ bool lists(int k, int nparts, const float* lval, const int32_t* lidx, const int32_t* lcnt,
                                const float* lthr, int64_t lcap, Shared& sh, int32_t* o, float* os,
                                const float* cval = nullptr, const int32_t* cidx = nullptr,
                                const int32_t* ccnt = nullptr, int64_t ccap = 0) {
@@ -118,24 +125,65 @@ struct Merge {
     if (k > kStage / 2) return false;  // the output is staged in half of si (past the list offsets)
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
+    // counts, thresholds and candidate counts are all requested at once
     int lc = tid < nparts ? lcnt[tid] : 0;
+    const float lt0 = tid < nparts && lthr ? lthr[tid] : -INFINITY;
+    const int cc = tid < nparts && ccnt ? ccnt[tid] : 0;
+    // the padded grid's loads go out with the counts (slots past a list's
+    // count are read but never used; every address stays in part p's lcap slots)
+    const int S = kU / (nparts > 0 ? nparts : 1);
+    float tv[UITEMS];
+    int32_t tx[UITEMS];
+    // 16-byte loads when a thread's slots are whole aligned vectors of one
+    // part's list (S a multiple of UITEMS, lists 16-byte aligned)
+    const bool vec = S % UITEMS == 0 && lcap % 4 == 0 && S <= lcap &&
+                     ((reinterpret_cast<uintptr_t>(lval) | reinterpret_cast<uintptr_t>(lidx)) & 15) == 0;  // uniform
+    if (vec) {
+      static_assert(UITEMS % 4 == 0, "whole vectors");
+      const int e0 = tid * UITEMS;
+      const int p = e0 / S;
+      const int64_t at = static_cast<int64_t>(p < nparts ? p : 0) * lcap + (e0 - p * S);
+#pragma unroll
+      for (int q = 0; q < UITEMS / 4; ++q) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(lval + at + 4 * q);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(lidx + at + 4 * q);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          tv[4 * q + u] = v[u];
+          tx[4 * q + u] = static_cast<int32_t>(x[u]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < UITEMS; ++j) {
+        const int e = tid * UITEMS + j;
+        const int p = e / S;
+        const int jj = e - p * S;
+        const int64_t at = static_cast<int64_t>(p < nparts ? p : 0) * lcap + (jj < lcap ? jj : 0);
+        tv[j] = lval[at];
+        tx[j] = lidx[at];
+      }
+    }
     const bool whole = lc == kWholePart && ccnt != nullptr;
-    if (whole) lc = ccnt[tid];
-    const float lt = tid < nparts && lthr && !whole ? lthr[tid] : -INFINITY;
-    // per wave: any missing list, the lists' total, the largest threshold
+    if (whole) lc = cc;
+    const float lt = whole ? -INFINITY : lt0;
+    // per wave: any missing list, the lists' total, the largest threshold,
+    // the longest list (a whole part counts as too long for the grid)
     const uint32_t neg = static_cast<uint32_t>(__popcll(__ballot(lc < 0)));
     const uint32_t cnt = static_cast<uint32_t>(lc > 0 ? lc : 0);
     const uint32_t incl = sel::wave_incl_scan(cnt);
     const float vmax_w = wave_max(lt);
+    const uint32_t cmax_w = sel::wave_max(whole ? 0xffffffffu : cnt);
     uint32_t* uoff = reinterpret_cast<uint32_t*>(sh.si);  // list offsets in U (<= THREADS parts)
     int32_t* ucnt = sh.si + THREADS;                        // list lengths
     if (sel::lane_id() == 63) {
       sh.fs.wsum[wave] = incl;
       sh.fs.red[0][wave] = vmax_w;
       sh.fs.core.red[0][wave] = neg;
+      sh.fs.core.red[1][wave] = cmax_w;
     }
     __syncthreads();
-    uint32_t before = 0, total = 0, nneg = 0;
+    uint32_t before = 0, total = 0, nneg = 0, cmax = 0;
     float vmax = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
@@ -143,6 +191,7 @@ struct Merge {
       total += sh.fs.wsum[w];
       nneg += sh.fs.core.red[0][w];
       vmax = fmaxf(vmax, sh.fs.red[0][w]);
+      cmax = cmax > sh.fs.core.red[1][w] ? cmax : sh.fs.core.red[1][w];
     }
     if (nneg != 0 || total < static_cast<uint32_t>(k) || total > static_cast<uint32_t>(kU)) {
       __syncthreads();  // the LDS reads above are done before the caller reuses it
@@ -153,17 +202,28 @@ struct Merge {
       ucnt[tid] = whole ? -static_cast<int32_t>(cnt) : static_cast<int32_t>(cnt);  // negative: a whole part
     }
     __syncthreads();
-    // U into LDS (values, then indices).  Entry e of U is entry e - uoff[p]
-    // of part p's list (of its candidate set for a whole part), p the last
-    // part with uoff[p] <= e (a binary search over the offsets in LDS: empty
-    // parts share their successor's offset, so p is the part that holds e);
-    // each thread issues all its loads before its stores.  U holds at most
-    // kU entries (checked above), so the arithmetic fits 32 bits.
-    float* uval = sh.stage;
-    int32_t* uidx = reinterpret_cast<int32_t*>(sh.stage + kU);
-    {
-      float tv[UITEMS];
-      int32_t tx[UITEMS];
+    const bool grid = cmax <= static_cast<uint32_t>(S) && static_cast<int64_t>(S) <= lcap;  // uniform
+    uint32_t keys[UITEMS];
+    typename USel::Mask vm = 0;
+    if (grid) {
+#pragma unroll
+      for (int j = 0; j < UITEMS; ++j) {
+        const int e = tid * UITEMS + j;
+        const int p = e / S;
+        const int jj = e - p * S;
+        const bool ok = p < nparts && jj < ucnt[p < nparts ? p : 0];
+        keys[j] = float_key(tv[j]);
+        vm |= static_cast<typename USel::Mask>(ok) << j;
+      }
+    } else {
+      // U packed into LDS (values, then indices).  Entry e of U is entry
+      // e - uoff[p] of part p's list (of its candidate set for a whole part),
+      // p the last part with uoff[p] <= e (empty parts share their
+      // successor's offset, so p is the part that holds e); each thread
+      // issues all its loads before its stores.  U holds at most kU entries
+      // (checked above), so the arithmetic fits 32 bits.
+      float* uval = sh.stage;
+      int32_t* uidx = reinterpret_cast<int32_t*>(sh.stage + kU);
 #pragma unroll
       for (int r = 0; r < UITEMS; ++r) {
         const uint32_t e = static_cast<uint32_t>(r * THREADS + tid);
@@ -190,17 +250,18 @@ struct Merge {
           uidx[e] = tx[r];
         }
       }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < UITEMS; ++j) {
+        const uint32_t u = static_cast<uint32_t>(tid * UITEMS + j);
+        tv[j] = uval[u < total ? u : 0];
+        tx[j] = uidx[u < total ? u : 0];
+        keys[j] = float_key(tv[j]);
+        vm |= static_cast<typename USel::Mask>(u < total) << j;
+      }
     }
     USel::zero(sh.fs.core);
     __syncthreads();
-    uint32_t keys[UITEMS];
-    typename USel::Mask vm = 0;
-#pragma unroll
-    for (int j = 0; j < UITEMS; ++j) {
-      const uint32_t u = static_cast<uint32_t>(tid * UITEMS + j);
-      keys[j] = float_key(uval[u < total ? u : 0]);
-      vm |= static_cast<typename USel::Mask>(u < total) << j;
-    }
     uint32_t thr, take;
     USel::radix_select(keys, vm, static_cast<uint32_t>(k), sh.fs.core, &thr, &take);
     if (vmax > key_float(thr)) {  // uniform: some part's list may miss row top-k entries
@@ -210,9 +271,8 @@ struct Merge {
     uint32_t bg = 0, be = 0;
     // outputs staged in sh.sv / sh.si past the list offsets (k <= kStage / 2 here)
     USel::compact(keys, vm, thr, take, sh.fs.core, &bg, &be, [&](int j, uint32_t pos) {
-      const int u = tid * UITEMS + j;
-      sh.sv[pos] = uval[u];
-      sh.si[pos + kStage / 2] = uidx[u];
+      sh.sv[pos] = tv[j];
+      sh.si[pos + kStage / 2] = tx[j];
     });
     for (int i = tid; i < k; i += THREADS) {
       o[i] = sh.si[i + kStage / 2];
@@ -224,7 +284,7 @@ struct Merge {
   // Merge over nparts * cap <= kSlots candidate slots (part order = index
   // order; slots past a part's count hold NaN).  Every valid candidate is
   // kept when there are at most k of them.
-  static __device__ void full(int k, int nparts, int cap, const float* rv, const int32_t* ri, const int32_t* rc,
+  static __device__ __forceinline__ void full(int k, int nparts, int cap, const float* rv, const int32_t* ri, const int32_t* rc,
                               Shared& sh, int32_t* o, float* os) {
     const int tid = threadIdx.x;
     const int ns = nparts * cap;
