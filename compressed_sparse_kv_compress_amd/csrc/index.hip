@@ -604,6 +604,7 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
   static_assert(DEPTH <= 16, "wait_tiles covers the ring");
   __shared__ __attribute__((aligned(16))) uint8_t ring[DEPTH][TB];
   __shared__ __attribute__((aligned(16))) float sbuf[kMultiRows][kMultiKeys];
+  __shared__ float sdump[64];  // stores of tiles past the end
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
@@ -687,9 +688,16 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
       for (int r = 0; r < (HAS_W ? 4 : 1); ++r) wr[i][mb][r] = HAS_W ? a.w[row * HI + mb * 16 + 4 * g + r] : 1.f;
   }
   // Two tiles per barrier: tiles it and it+1 (slots it%8, (it+1)%8); their
-  // slots are refilled with tiles it+DEPTH-2 and it+DEPTH-1 after the next barrier.
-  auto tile = [&](int tt) {
-    f32x4 acc[kMultiRpw][MB];
+  // slots are refilled with tiles it+DEPTH-2 and it+DEPTH-1 after the next
+  // barrier.  Software pipelined: the epilogue of a tile (ReLU, head weights,
+  // head sum: VALU work that depends on its accumulators) is issued between
+  // the MFMAs of the next tile, so one wavefront's matrix unit is not idle
+  // while it finishes a tile, and the two wavefronts of a SIMD, which the
+  // barriers keep in step, no longer reach their epilogues together.  The
+  // last tile of a pair is finished after the next barrier.  A tile past the
+  // end is computed on a stale ring slot and its scores are dropped.
+  using Acc = f32x4[kMultiRpw][MB];
+  auto mfma_tile = [&](int tt, Acc& acc) {
 #pragma unroll
     for (int i = 0; i < kMultiRpw; ++i)
 #pragma unroll
@@ -731,6 +739,10 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
           for (int mb = 0; mb < MB; ++mb)
             acc[i][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[i][mb][ks], cur[ks], acc[i][mb], 0, 0, 0);
     }
+  };
+  // Every lane group holds the head sum after group_sum4 (the same value: the
+  // additions commute), so all lanes store it, a dropped tile to a dump slot.
+  auto epi_tile = [&](int tt, bool keep, const Acc& acc) {
 #pragma unroll
     for (int i = 0; i < kMultiRpw; ++i) {
       float ps[MB];
@@ -747,9 +759,26 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
 #pragma unroll
         for (int mb = 0; mb + w < MB; mb += 2 * w) ps[mb] += ps[mb + w];
       const float tot = group_sum4(ps[0]);
-      if (g == 0) sbuf[kMultiRpw * wave + i][tt * kTileKeys + c16] = tot;
+      float* dst = keep ? &sbuf[kMultiRpw * wave + i][(keep ? tt : 0) * kTileKeys + c16] : &sdump[lane];
+      *dst = tot;
     }
   };
+  // Interleave n MFMAs with the VALU work around them, m VALU per MFMA.
+  auto interleave = [](auto n, auto m) {
+#pragma unroll
+    for (int q = 0; q < decltype(n)::value; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, decltype(m)::value, 0);
+    }
+  };
+  using NM = std::integral_constant<int, kMultiRpw * MB * (KF ? 1 : KS)>;  // MFMAs per tile
+  using NV = std::integral_constant<int, (MB * 11 + 8) * kMultiRpw / (kMultiRpw * MB * (KF ? 1 : KS)) + 1>;
+  Acc accp;  // the previous pair's second tile, finished after this barrier
+  int ttp = -1;
+#pragma unroll
+  for (int i = 0; i < kMultiRpw; ++i)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) accp[i][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int it = 0; it < ntiles; it += 2) {
     if (wave < NLW) {
       // loads issued after tile it+1's (or it's, at the end) may stay in flight
@@ -762,9 +791,20 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
       if (it + DEPTH - 2 < ntiles) issue(it + DEPTH - 2);  // into tile it-2's slot
       if (it + DEPTH - 1 < ntiles) issue(it + DEPTH - 1);  // into tile it-1's slot
     }
-    tile(it);
-    if (it + 1 < ntiles) tile(it + 1);
+    Acc acc0, acc1;
+    mfma_tile(it, acc0);
+    epi_tile(ttp, ttp >= 0, accp);
+    interleave(NM{}, NV{});
+    mfma_tile(it + 1, acc1);
+    epi_tile(it, true, acc0);
+    interleave(NM{}, NV{});
+#pragma unroll
+    for (int i = 0; i < kMultiRpw; ++i)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) accp[i][mb] = acc1[i][mb];
+    ttp = it + 1 < ntiles ? it + 1 : -1;
   }
+  epi_tile(ttp, ttp >= 0, accp);
   // this wave's rows, keys [kb, ke): computed and visible, else -inf
   const int nk = static_cast<int>(ke - kb);
   const int nc = ntiles * kTileKeys;
