@@ -74,6 +74,38 @@ __device__ __forceinline__ float relu_bits(float x) {
   return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
 }
 
+// A key's score from a wavefront's 16 x 16 MFMA blocks (heads as rows):
+// lane (g, c16) holds heads 16 mb + 4g + r of key c16.  It sums w_h *
+// ReLU(q_h . k) over its 4 MB heads as two FMA chains (r = 0, 1 and r = 2, 3),
+// one VALU instruction per head after the ReLU, and group_sum4 adds the four
+// lane groups (every lane then holds the total).  The decode scan and the
+// 16-row prefill scorer both call it, so a query's scores are the same bit for
+// bit whichever kernel computes them.
+template <int MB, bool HAS_W>
+__device__ __forceinline__ float head_sum(const f32x4 (&acc)[MB], const float (&wr)[MB][HAS_W ? 4 : 1]) {
+  float sa, sb;
+  if constexpr (HAS_W) {
+    sa = __builtin_fmaf(wr[0][1], relu_bits(acc[0][1]), wr[0][0] * relu_bits(acc[0][0]));
+    sb = __builtin_fmaf(wr[0][3], relu_bits(acc[0][3]), wr[0][2] * relu_bits(acc[0][2]));
+#pragma unroll
+    for (int mb = 1; mb < MB; ++mb) {
+      sa = __builtin_fmaf(wr[mb][0], relu_bits(acc[mb][0]), sa);
+      sb = __builtin_fmaf(wr[mb][2], relu_bits(acc[mb][2]), sb);
+      sa = __builtin_fmaf(wr[mb][1], relu_bits(acc[mb][1]), sa);
+      sb = __builtin_fmaf(wr[mb][3], relu_bits(acc[mb][3]), sb);
+    }
+  } else {
+    sa = relu_bits(acc[0][0]) + relu_bits(acc[0][1]);
+    sb = relu_bits(acc[0][2]) + relu_bits(acc[0][3]);
+#pragma unroll
+    for (int mb = 1; mb < MB; ++mb) {
+      sa = (sa + relu_bits(acc[mb][0])) + relu_bits(acc[mb][1]);
+      sb = (sb + relu_bits(acc[mb][2])) + relu_bits(acc[mb][3]);
+    }
+  }
+  return group_sum4(sa + sb);
+}
+
 template <int LPT>
 __device__ __forceinline__ void wait_tiles(int n) {
   switch (n) {
@@ -490,19 +522,7 @@ __global__ __launch_bounds__(64 * (KF ? kWaves8 : kWaves), 1) void index_score_s
   const int64_t vl = nv - k0 - c16;
   const int vlim = vl < 0 ? 0 : (vl > INT32_MAX ? INT32_MAX : static_cast<int>(vl));
   auto finish = [&](int itx, const f32x4 (&acc)[MB]) {
-    float ps[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      float x[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = HAS_W ? wr[mb][HAS_W ? r : 0] * relu_bits(acc[mb][r]) : relu_bits(acc[mb][r]);
-      ps[mb] = (x[0] + x[1]) + (x[2] + x[3]);
-    }
-#pragma unroll
-    for (int w = 1; w < MB; w <<= 1)
-#pragma unroll
-      for (int mb = 0; mb + w < MB; mb += 2 * w) ps[mb] += ps[mb + w];
-    const float tot = group_sum4(ps[0]);
+    const float tot = head_sum<MB, HAS_W>(acc, wr);
     if (g == 0) sb[sb_pos(itx, c16)] = itx * static_cast<int>(kStride) < vlim ? tot : -INFINITY;
   };
   for (int it = 0; it < ntv; ++it) {
@@ -697,11 +717,10 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
   // last tile of a pair is finished after the next barrier.  A tile past the
   // end is computed on a stale ring slot and its scores are dropped.
   using Acc = f32x4[kMultiRpw][MB];
+  // The first k-step takes a zero accumulator operand (an inline constant:
+  // no register clearing).
+  constexpr f32x4 kZero4{0.f, 0.f, 0.f, 0.f};
   auto mfma_tile = [&](int tt, Acc& acc) {
-#pragma unroll
-    for (int i = 0; i < kMultiRpw; ++i)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[i][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (FP4) {  // key c16's code block g (rotated by c16 / 4) and its E8M0 scale (copy g)
       const uint8_t* t = &ring[tt % DEPTH][0];
       const u32x4 x = *reinterpret_cast<const u32x4*>(t + c16 * 64 + (((g + (c16 >> 2)) & 3) << 4));
@@ -712,7 +731,7 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
       for (int i = 0; i < kMultiRpw; ++i)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)  // format 4 = E2M1 for both operands, per-lane E8M0 scales
-          acc[i][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afrag8[i][mb], cur4, acc[i][mb], 4, 4, 0,
+          acc[i][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afrag8[i][mb], cur4, kZero4, 4, 4, 0,
                                                                         qsc[i][mb], 0, ksc);
     } else if constexpr (FP8) {  // key c16's dims 32g .. 32g+31: blocks 2g, 2g+1 (rotated by c16 / 2)
       const uint8_t* t = &ring[tt % DEPTH][0] + c16 * 128;
@@ -724,7 +743,7 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
       for (int i = 0; i < kMultiRpw; ++i)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          acc[i][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afrag8[i][mb], cur8, acc[i][mb], 0, 0, 0, 127, 0,
+          acc[i][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afrag8[i][mb], cur8, kZero4, 0, 0, 0, 127, 0,
                                                                         127);
     } else {
       const uint8_t* t = &ring[tt % DEPTH][0] + c16 * 256;
@@ -737,7 +756,8 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
         for (int i = 0; i < kMultiRpw; ++i)
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
-            acc[i][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[i][mb][ks], cur[ks], acc[i][mb], 0, 0, 0);
+            acc[i][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[i][mb][ks], cur[ks], ks == 0 ? kZero4 : acc[i][mb],
+                                                                 0, 0, 0);
     }
   };
   // Every lane group holds the head sum after group_sum4 (the same value: the
@@ -745,20 +765,7 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
   auto epi_tile = [&](int tt, bool keep, const Acc& acc) {
 #pragma unroll
     for (int i = 0; i < kMultiRpw; ++i) {
-      float ps[MB];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        float x[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          x[r] = HAS_W ? wr[i][mb][HAS_W ? r : 0] * relu_bits(acc[i][mb][r]) : relu_bits(acc[i][mb][r]);
-        ps[mb] = (x[0] + x[1]) + (x[2] + x[3]);
-      }
-#pragma unroll
-      for (int w = 1; w < MB; w <<= 1)
-#pragma unroll
-        for (int mb = 0; mb + w < MB; mb += 2 * w) ps[mb] += ps[mb + w];
-      const float tot = group_sum4(ps[0]);
+      const float tot = head_sum<MB, HAS_W>(acc[i], wr[i]);
       float* dst = keep ? &sbuf[kMultiRpw * wave + i][(keep ? tt : 0) * kTileKeys + c16] : &sdump[lane];
       *dst = tot;
     }
@@ -772,8 +779,8 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
     }
   };
   using NM = std::integral_constant<int, kMultiRpw * MB * (KF ? 1 : KS)>;  // MFMAs per tile
-  using NV = std::integral_constant<int, (MB * 11 + 8) * kMultiRpw / (kMultiRpw * MB * (KF ? 1 : KS)) + 1>;
-  Acc accp;  // the previous pair's second tile, finished after this barrier
+  using NV = std::integral_constant<int, (MB * 8 + 6) * kMultiRpw / (kMultiRpw * MB * (KF ? 1 : KS)) + 1>;
+  Acc accp;  // the previous pair's second tile, finished after this barrier (then reused for this pair's)
   int ttp = -1;
 #pragma unroll
   for (int i = 0; i < kMultiRpw; ++i)
@@ -791,17 +798,13 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
       if (it + DEPTH - 2 < ntiles) issue(it + DEPTH - 2);  // into tile it-2's slot
       if (it + DEPTH - 1 < ntiles) issue(it + DEPTH - 1);  // into tile it-1's slot
     }
-    Acc acc0, acc1;
+    Acc acc0;
     mfma_tile(it, acc0);
     epi_tile(ttp, ttp >= 0, accp);
     interleave(NM{}, NV{});
-    mfma_tile(it + 1, acc1);
+    mfma_tile(it + 1, accp);
     epi_tile(it, true, acc0);
     interleave(NM{}, NV{});
-#pragma unroll
-    for (int i = 0; i < kMultiRpw; ++i)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) accp[i][mb] = acc1[i][mb];
     ttp = it + 1 < ntiles ? it + 1 : -1;
   }
   epi_tile(ttp, ttp >= 0, accp);
