@@ -75,14 +75,14 @@ __device__ __forceinline__ float relu_bits(float x) {
 }
 
 // A key's score from a wavefront's 16 x 16 MFMA blocks (heads as rows):
-// lane (g, c16) holds heads 16 mb + 4g + r of key c16.  It sums w_h *
-// ReLU(q_h . k) over its 4 MB heads as two FMA chains (r = 0, 1 and r = 2, 3),
-// one VALU instruction per head after the ReLU, and group_sum4 adds the four
-// lane groups (every lane then holds the total).  The decode scan and the
-// 16-row prefill scorer both call it, so a query's scores are the same bit for
-// bit whichever kernel computes them.
+// lane (g, c16) holds heads 16 mb + 4g + r of key c16.  head_part sums w_h *
+// ReLU(q_h . k) over the lane's 4 MB heads as two FMA chains (r = 0, 1 and
+// r = 2, 3), one VALU instruction per head after the ReLU; group_sum4_pair
+// then adds the four lane groups.  The decode scan and the 16-row prefill
+// scorer both use them, so a query's scores are the same bit for bit
+// whichever kernel computes them.
 template <int MB, bool HAS_W>
-__device__ __forceinline__ float head_sum(const f32x4 (&acc)[MB], const float (&wr)[MB][HAS_W ? 4 : 1]) {
+__device__ __forceinline__ float head_part(const f32x4 (&acc)[MB], const float (&wr)[MB][HAS_W ? 4 : 1]) {
   float sa, sb;
   if constexpr (HAS_W) {
     sa = __builtin_fmaf(wr[0][1], relu_bits(acc[0][1]), wr[0][0] * relu_bits(acc[0][0]));
@@ -103,7 +103,20 @@ __device__ __forceinline__ float head_sum(const f32x4 (&acc)[MB], const float (&
       sb = (sb + relu_bits(acc[mb][2])) + relu_bits(acc[mb][3]);
     }
   }
-  return group_sum4(sa + sb);
+  return sa + sb;
+}
+
+// Sums over the four 16-lane groups of two values at once, each as
+// (g0 + g2) + (g1 + g3): the upper half-wave's values meet the lower half's
+// (x0's in lanes 0-31, x1's in lanes 32-63), then odd rows meet even rows.
+// Lanes of groups 0 and 1 end with x0's total, groups 2 and 3 with x1's; with
+// x1 = x0 every lane holds x0's total, the same bits (additions commute).
+__device__ __forceinline__ float group_sum4_pair(float x0, float x1) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x1), false, false);
+  const float y = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const uint32_t v = __float_as_uint(y);
+  const auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 template <int LPT>
@@ -522,7 +535,8 @@ __global__ __launch_bounds__(64 * (KF ? kWaves8 : kWaves), 1) void index_score_s
   const int64_t vl = nv - k0 - c16;
   const int vlim = vl < 0 ? 0 : (vl > INT32_MAX ? INT32_MAX : static_cast<int>(vl));
   auto finish = [&](int itx, const f32x4 (&acc)[MB]) {
-    const float tot = head_sum<MB, HAS_W>(acc, wr);
+    const float hp = head_part<MB, HAS_W>(acc, wr);
+    const float tot = group_sum4_pair(hp, hp);
     if (g == 0) sb[sb_pos(itx, c16)] = itx * static_cast<int>(kStride) < vlim ? tot : -INFINITY;
   };
   for (int it = 0; it < ntv; ++it) {
@@ -760,15 +774,14 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
                                                                  0, 0, 0);
     }
   };
-  // Every lane group holds the head sum after group_sum4 (the same value: the
-  // additions commute), so all lanes store it, a dropped tile to a dump slot.
+  // Both rows' group sums in one exchange: lane groups 0, 1 then hold row 0's
+  // score and groups 2, 3 row 1's, so every lane stores one (the pairs store
+  // equal values to one slot), a dropped tile to a dump slot.
+  static_assert(kMultiRpw == 2, "two rows per wavefront share the group sums");
   auto epi_tile = [&](int tt, bool keep, const Acc& acc) {
-#pragma unroll
-    for (int i = 0; i < kMultiRpw; ++i) {
-      const float tot = head_sum<MB, HAS_W>(acc[i], wr[i]);
-      float* dst = keep ? &sbuf[kMultiRpw * wave + i][(keep ? tt : 0) * kTileKeys + c16] : &sdump[lane];
-      *dst = tot;
-    }
+    const float tot = group_sum4_pair(head_part<MB, HAS_W>(acc[0], wr[0]), head_part<MB, HAS_W>(acc[1], wr[1]));
+    float* dst = keep ? &sbuf[kMultiRpw * wave + (g >> 1)][(keep ? tt : 0) * kTileKeys + c16] : &sdump[lane];
+    *dst = tot;
   };
   // Interleave n MFMAs with the VALU work around them, m VALU per MFMA.
   auto interleave = [](auto n, auto m) {
