@@ -335,8 +335,9 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
 }
 
 // d_I = 128 (KS = 4), MB = H_I / 16 head blocks.  Workgroup (row, part)
-// scores keys [part * 4 * per_wave, +4 * per_wave); its wavefront w takes
-// tiles w, w+4, w+8, ... so that the four stream through adjacent memory.
+// scores keys [part * 4 * per_wave, +4 * per_wave); with NW wavefronts (4 for
+// bf16 keys, 8 for FP8 / MXFP4) wavefront w takes tiles w, w+NW, w+2NW, ...
+// so that they stream through adjacent memory.
 // Scores collect in LDS and leave in one coalesced pass at the end, so the
 // loop issues no stores (their completions would share the load counter the
 // ring waits on).
