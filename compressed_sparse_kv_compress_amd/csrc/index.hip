@@ -726,11 +726,10 @@ __global__ __launch_bounds__(512, 1) void index_score_multi(IndexScoreArgs a, in
   // slots are refilled with tiles it+DEPTH-2 and it+DEPTH-1 after the next
   // barrier.  Software pipelined: the epilogue of a tile (ReLU, head weights,
   // head sum: VALU work that depends on its accumulators) is issued between
-  // the MFMAs of the next tile, so one wavefront's matrix unit is not idle
-  // while it finishes a tile, and the two wavefronts of a SIMD, which the
-  // barriers keep in step, no longer reach their epilogues together.  The
-  // last tile of a pair is finished after the next barrier.  A tile past the
-  // end is computed on a stale ring slot and its scores are dropped.
+  // the MFMAs of the next tile rather than after them, so the matrix unit is
+  // not left idle while a wavefront finishes a tile.  The last tile of a pair
+  // is finished after the next barrier.  A tile past the end is computed on
+  // a stale ring slot and its scores are dropped.
   using Acc = f32x4[kMultiRpw][MB];
   // The first k-step takes a zero accumulator operand (an inline constant:
   // no register clearing).
