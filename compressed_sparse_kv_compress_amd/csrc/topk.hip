@@ -40,18 +40,23 @@ constexpr int kBins = sel::kBins;
 constexpr int kMaxMergeParts = 256;  // one part count per merge thread
 constexpr int kStage = mrg::kStage;  // outputs up to this size are staged in LDS, then stored coalesced
 using Sel = sel::Select<kThreads, kItems>;
-using Filt = sel::Filter<kThreads, kItems, 16>;
 using sel::lane_id;
 using sel::wave_incl_scan;
 
-using PartTile = mrg::Tile<kThreads, kItems>;
-
-struct Shared {
-  Filt::Shared fs;
+// Part kernel state for parts of kThreads * IT scores.
+template <int IT>
+struct PartShared {
+  typename sel::Filter<kThreads, IT, 16>::Shared fs;
   int32_t si[kStage + 64];  // staged output: entry and score (64 lane-private dump slots at the end)
   float sv[kStage + 64];
-  alignas(16) float stage[PartTile::kFloats];
+  alignas(16) float stage[mrg::Tile<kThreads, IT>::kFloats];
 };
+// Half-size parts (8192 scores, 16 per thread) for launches whose candidates
+// still fit the merge's tile: a workgroup then holds ~78 KiB of LDS and at
+// most 128 VGPRs, so two share a CU, and each selection has half the items.
+constexpr int kItemsHalf = 16;
+constexpr int64_t kPartHalf = static_cast<int64_t>(kThreads) * kItemsHalf;  // 8192
+static_assert(2 * sizeof(PartShared<kItemsHalf>) <= 160 * 1024, "two half-size part workgroups share a CU");
 
 // The merge: 512 threads, 32 candidate slots each (1024 x 16 measured slower:
 // more waves per barrier, no less latency per phase).
@@ -60,10 +65,15 @@ using Merge = mrg::Merge<kMThreads>;
 static_assert(Merge::ITEMS * kMThreads == kPart, "merge tile");
 using mrg::row_visible;
 
-// Stage 1: per-part local selection.
-__global__ __launch_bounds__(kThreads) void topk_part_kernel(TopkArgs a, int64_t nparts, int64_t cap,
-                                                             float* cval, int32_t* cidx, int32_t* ccnt) {
-  __shared__ Shared sh;
+// Stage 1: per-part local selection over parts of P = kThreads * IT scores.
+template <int IT>
+__global__ __launch_bounds__(kThreads, IT == kItemsHalf ? 2 : 1) void topk_part_kernel(TopkArgs a, int64_t nparts,
+                                                                                      int64_t cap, float* cval,
+                                                                                      int32_t* cidx, int32_t* ccnt) {
+  using Filt = sel::Filter<kThreads, IT, 16>;
+  using PartTile = mrg::Tile<kThreads, IT>;
+  constexpr int64_t kPart = static_cast<int64_t>(kThreads) * IT;
+  __shared__ PartShared<IT> sh;
   const int64_t lrow = blockIdx.x / nparts;
   const int64_t part = blockIdx.x % nparts;
   const int64_t nv = row_visible(a, a.row0 + lrow);
@@ -82,9 +92,9 @@ __global__ __launch_bounds__(kThreads) void topk_part_kernel(TopkArgs a, int64_t
   }
   Filt::zero(sh.fs);
   const float* s = a.score + lrow * a.ld + base;
-  float v[kItems];
+  float v[IT];
   PartTile::store(PartTile::load(s, static_cast<int>(cnt)), sh.stage, v);
-  const int i0 = tid * kItems;  // this thread's entries i0 .. i0+31 of the part
+  const int i0 = tid * IT;  // this thread's entries i0 .. i0+IT-1 of the part
   if (cnt <= cap) {  // the whole part is kept; slots past it hold NaN
     for (int64_t i = tid; i < cap; i += kThreads) {
       const float t = sh.stage[PartTile::pos(static_cast<int>(i < kPart ? i : 0))];
@@ -259,23 +269,36 @@ __global__ __launch_bounds__(kThreads) void topk_merge_general(TopkArgs a, int64
 
 }  // namespace
 
-int64_t topk_parts(int64_t L) { return L <= 0 ? 1 : (L + kPart - 1) / kPart; }
 int64_t topk_cap(int64_t k) { return k < kPart ? k : kPart; }
+// Half-size parts when their candidates fit the merge's tile and k is at most
+// a quarter of a part (the sampled selection's range); else 16384-score parts.
+bool topk_half_parts(int64_t L, int64_t k) {
+  const int64_t np = L <= 0 ? 1 : (L + kPartHalf - 1) / kPartHalf;
+  return 4 * k <= kPartHalf && np * topk_cap(k) <= kPart && np <= kMaxMergeParts;
+}
+int64_t topk_parts(int64_t L, int64_t k) {
+  const int64_t ps = topk_half_parts(L, k) ? kPartHalf : kPart;
+  return L <= 0 ? 1 : (L + ps - 1) / ps;
+}
 
 size_t topk_ws_bytes_per_row(int64_t L, int64_t k) {
-  const int64_t np = topk_parts(L);
+  const int64_t np = topk_parts(L, k);
   const size_t b = static_cast<size_t>(np) * topk_cap(k) * 8 + static_cast<size_t>(np) * 4;
   return (b + 255) / 256 * 256;
 }
 
 hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t s) {
   if (a.nrows == 0 || a.k == 0) return hipSuccess;
-  const int64_t np = topk_parts(a.L), cap = topk_cap(a.k);
+  const int64_t np = topk_parts(a.L, a.k), cap = topk_cap(a.k);
   float* cval = static_cast<float*>(ws);
   int32_t* cidx = reinterpret_cast<int32_t*>(cval + a.nrows * np * cap);
   int32_t* ccnt = cidx + a.nrows * np * cap;
-  hipLaunchKernelGGL(topk_part_kernel, dim3(static_cast<uint32_t>(a.nrows * np)), dim3(kThreads), 0, s, a, np,
-                     cap, cval, cidx, ccnt);
+  if (topk_half_parts(a.L, a.k))
+    hipLaunchKernelGGL(topk_part_kernel<kItemsHalf>, dim3(static_cast<uint32_t>(a.nrows * np)), dim3(kThreads), 0, s,
+                       a, np, cap, cval, cidx, ccnt);
+  else
+    hipLaunchKernelGGL(topk_part_kernel<kItems>, dim3(static_cast<uint32_t>(a.nrows * np)), dim3(kThreads), 0, s, a,
+                       np, cap, cval, cidx, ccnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   IndexCandidates c;
