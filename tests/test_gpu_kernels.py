@@ -142,7 +142,12 @@ def _seeded_scores(B, T, L, seed, device):
                                       # k above one part: every part kept whole, general merge
                                       (1, 2, 250000, 1, 20000),
                                       # one part, k above the LDS staging size: direct emit in both kernels
-                                      (2, 2, 10000, 1, 4096)])
+                                      (2, 2, 10000, 1, 4096),
+                                      # the edges of the 8192-score parts: k = a quarter of a part (taken),
+                                      # k one above (16384-score parts), 16 half parts filling the merge
+                                      # tile exactly (taken), and one more (16384-score parts)
+                                      (2, 2, 16384, 1, 2048), (2, 2, 16385, 1, 2049),
+                                      (1, 2, 131072, 1, 1024), (1, 2, 131073, 1, 1024)])
 def test_topk_select_bit_exact_on_seeded_scores(B, T, L, m, k):
     n_ctx = L * m
     sg = _seeded_scores(B, T, L, 5 + L, "cuda")
