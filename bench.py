@@ -911,7 +911,7 @@ def index_topk_mxfp4(B: int, reps: int = 20):
     torch.cuda.empty_cache()
     return {"ms_per_call": ms, "algorithmic_bytes_per_call": byts, "GBps": byts / (ms * 1e-3) / 1e9,
             "keys": "16 x %d visible keys of 68 B (64 code bytes + 4 scales), k = %d" % (st.nv_csa, k),
-            "note": "scan bound by its per-tile MFMA and epilogue chain (one wavefront per SIMD), not by bytes"}
+            "note": "scan bound by its per-tile chain (LDS read, MFMA, ReLU and head sum), which two wavefronts per SIMD only partly overlap, not by bytes"}
 
 
 def main():
