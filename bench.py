@@ -765,12 +765,24 @@ def bulk_compress(kind, B, n, reps=3):
             call = lambda: csa.hca_compress(arrs[0], arrs[1], m, out=out)  # noqa: E731
         total_ms += timed_steps(call, reps, 1)
         total_bytes += sum(a.numel() for a in arrs) * 2 + out.numel() * 2
+        if kind == "csa" and D == 128:  # the index keys again, written as MXFP4 entries
+            nel = B * L * D
+            mx = csa.MXFP4(torch.empty(nel // 2 + nel // 32, dtype=torch.uint8, device="cuda"), (B, L, D))
+            mx_ms = timed_steps(lambda: csa.csa_compress(arrs[0], arrs[1], m, x_b=arrs[2], z_b=arrs[3], out=mx),
+                                reps, 1)
+            mx_bytes = sum(a.numel() for a in arrs) * 2 + mx.data.numel()
+            mx_entry = {"ms": mx_ms, "bytes": mx_bytes, "GBps": mx_bytes / (mx_ms * 1e-3) / 1e9,
+                        "bf16_out_ms": timed_steps(call, reps, 1)}
+            del mx
         del arrs, out
         torch.cuda.empty_cache()
     gbps = total_bytes / (total_ms * 1e-3) / 1e9
-    return {"batch": B, "tokens": n, "m": m, "streams": len(dims), "ms": total_ms, "bytes": total_bytes,
-            "GBps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS,
-            "bytes_per_sequence": total_bytes / B}
+    res = {"batch": B, "tokens": n, "m": m, "streams": len(dims), "ms": total_ms, "bytes": total_bytes,
+           "GBps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS,
+           "bytes_per_sequence": total_bytes / B}
+    if kind == "csa":
+        res["index_keys_mxfp4"] = mx_entry
+    return res
 
 
 def paged_layout(B: int = 16, n_ctx: int = 1_000_000, page: int = 64, reps: int = 10):

@@ -181,36 +181,48 @@ def status_string(st: int) -> str:
 # compression
 # ---------------------------------------------------------------------------
 
+def _compress_out(x, B, ne, D, out, out_ld, mxfp4):
+    """The output of a bulk compression and its dtype code: bf16 rows in and
+    MXFP4 entries out when `mxfp4` is set or `out` is an MXFP4 tensor."""
+    mx = mxfp4 or isinstance(out, MXFP4)
+    if mx and x.dtype != torch.bfloat16:
+        raise TypeError("MXFP4 entries are compressed from bfloat16 rows, got %s" % x.dtype)
+    if out is None:
+        if mx:
+            nel = B * ne * D
+            out = MXFP4(torch.empty(nel // 2 + nel // 32, dtype=torch.uint8, device=x.device), (B, ne, D))
+        else:
+            out = torch.empty((B, ne, D), dtype=x.dtype, device=x.device)
+        out_ld = ne
+    elif out_ld is None:
+        out_ld = out.shape[1]
+    return out, out_ld, (CSA_MXFP4 if mx else _dt(x))
+
+
 def csa_compress(x_a, z_a, m, *, x_b=None, z_b=None, bias=None, n=None, p0=0, e0=0, e1=None,
-                 out=None, out_ld=None):
+                 out=None, out_ld=None, mxfp4=False):
     """Block-weighted compression of [B][n_raw][D] raw rows (positions p0..).
 
-    Returns out [B][e1-e0][D] (or writes into ``out`` with row stride out_ld)."""
+    Returns out [B][e1-e0][D] (or writes into ``out`` with row stride out_ld);
+    with ``mxfp4`` (bf16 rows) the entries come back as an MXFP4 tensor."""
     B, n_raw, D = x_a.shape
     n = p0 + n_raw if n is None else n
     e1 = -(-n // m) if e1 is None else e1
-    if out is None:
-        out = torch.empty((B, e1 - e0, D), dtype=x_a.dtype, device=x_a.device)
-        out_ld = e1 - e0
-    elif out_ld is None:
-        out_ld = out.shape[1]
+    out, out_ld, dt = _compress_out(x_a, B, e1 - e0, D, out, out_ld, mxfp4)
     st = _csa_compress(_ptr(x_a), _ptr(z_a), _ptr(x_b), _ptr(z_b), _ptr(bias), out.data_ptr(), B, n, D,
-                       m, p0, n_raw, e0, e1, out_ld, _dt(x_a), _stream(x_a.device))
+                       m, p0, n_raw, e0, e1, out_ld, dt, _stream(x_a.device))
     _check(st, "csa_compress")
     return out
 
 
-def hca_compress(x, z, m=128, *, bias=None, n=None, p0=0, e0=0, e1=None, out=None, out_ld=None):
+def hca_compress(x, z, m=128, *, bias=None, n=None, p0=0, e0=0, e1=None, out=None, out_ld=None,
+                 mxfp4=False):
     B, n_raw, D = x.shape
     n = p0 + n_raw if n is None else n
     e1 = -(-n // m) if e1 is None else e1
-    if out is None:
-        out = torch.empty((B, e1 - e0, D), dtype=x.dtype, device=x.device)
-        out_ld = e1 - e0
-    elif out_ld is None:
-        out_ld = out.shape[1]
+    out, out_ld, dt = _compress_out(x, B, e1 - e0, D, out, out_ld, mxfp4)
     st = _hca_compress(_ptr(x), _ptr(z), _ptr(bias), out.data_ptr(), B, n, D, m, p0, n_raw, e0, e1,
-                       out_ld, _dt(x), _stream(x.device))
+                       out_ld, dt, _stream(x.device))
     _check(st, "hca_compress")
     return out
 
@@ -219,15 +231,22 @@ def csa_compress_append(x_a, z_a, m, rings, pos, cache, *, x_b=None, z_b=None, b
     """One new raw token per sequence (x_a, z_a [B][D]; x_b, z_b in two-path
     mode): staged into `rings` (ring_xa, ring_za[, ring_xb, ring_zb], each
     [B][S][D]) at slot pos % S; the entry pos // m is written to `cache` when
-    the token completes its block.  pos: device int64 [B]."""
+    the token completes its block.  pos: device int64 [B].  An MXFP4 `cache`
+    (bf16 rows and rings) receives MXFP4 entries."""
     B, D = x_a.shape
     S = rings[0].shape[1]
     rx_b = rings[2] if len(rings) > 2 else None
     rz_b = rings[3] if len(rings) > 2 else None
     L = cache.shape[1] if L is None else L
+    if isinstance(cache, MXFP4):
+        if x_a.dtype != torch.bfloat16:
+            raise TypeError("MXFP4 entries are compressed from bfloat16 rows, got %s" % x_a.dtype)
+        dt = CSA_MXFP4
+    else:
+        dt = _dt(x_a)
     st = _csa_compress_append(_lay(layout), _ptr(x_a), _ptr(z_a), _ptr(x_b), _ptr(z_b), _ptr(bias), _ptr(rings[0]),
                               _ptr(rings[1]), _ptr(rx_b), _ptr(rz_b), S, _ptr(pos), _ptr(cache), L, B, D, m,
-                              _dt(x_a), _stream(x_a.device))
+                              dt, _stream(x_a.device))
     _check(st, "csa_compress_append")
     return cache
 

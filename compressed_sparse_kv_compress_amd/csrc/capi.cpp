@@ -55,10 +55,10 @@ csa_status_t compress_common(const void* x_a, const void* z_a, const void* x_b, 
                              int64_t m, int64_t p0, int64_t n_raw, int64_t e0, int64_t e1,
                              int64_t out_ld, csa_dtype_t dt, void* stream) {
   REQUIRE(dtype_ok(dt), "unknown dtype %d", static_cast<int>(dt));
-  if (dt == CSA_MXFP4) return fail(CSA_ERR_UNSUPPORTED, "compression has no MXFP4 kernels");
   REQUIRE(B >= 0 && n >= 1 && m >= 1 && D >= 8 && D % 8 == 0,
           "need B >= 0, n >= 1, m >= 1, D a positive multiple of 8 (B=%lld n=%lld m=%lld D=%lld)",
           (long long)B, (long long)n, (long long)m, (long long)D);
+  REQUIRE(dt != CSA_MXFP4 || D % 32 == 0, "MXFP4 entries need D a multiple of 32 (D=%lld)", (long long)D);
   const int64_t L = (n + m - 1) / m;
   REQUIRE(e0 >= 0 && e0 <= e1 && e1 <= L, "entry range [%lld, %lld) outside [0, %lld]",
           (long long)e0, (long long)e1, (long long)L);
@@ -487,9 +487,9 @@ csa_status_t csa_compress_append(const csa_layout_t* layout, const void* x_a, co
                                  void* ring_zb, int64_t S, const int64_t* pos, void* cache, int64_t L, int64_t B,
                                  int64_t D, int64_t m, csa_dtype_t dtype, void* stream) {
   REQUIRE(dtype_ok(dtype), "unknown dtype %d", static_cast<int>(dtype));
-  if (dtype == CSA_MXFP4) return fail(CSA_ERR_UNSUPPORTED, "compression has no MXFP4 kernels");
   REQUIRE(B >= 0 && m >= 1 && L >= 0 && D >= 8 && D % 8 == 0,
           "need B >= 0, m >= 1, L >= 0, D a positive multiple of 8");
+  REQUIRE(dtype != CSA_MXFP4 || D % 32 == 0, "MXFP4 entries need D a multiple of 32 (D=%lld)", (long long)D);
   REQUIRE((x_b == nullptr) == (z_b == nullptr), "x_b and z_b must both be given or both be NULL");
   const bool two = x_b != nullptr;
   REQUIRE(S >= (two ? 2 * m : m), "staging rings of %lld rows: need at least %lld", (long long)S,

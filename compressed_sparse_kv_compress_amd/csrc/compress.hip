@@ -88,6 +88,57 @@ struct Io<kF32> {
   }
 };
 
+// MXFP4 output (OCP microscaling FP4; the pages run the indexer's q.k in FP4,
+// shareware.cn article, the low-precision item of its list of what is
+// compressed).  The compressed values stay fp32 until this point; a block of
+// 32 channels of one entry is 4 consecutive lanes' 8 values.  The block
+// shares the scale 2^E with E = floor(log2 max|v|) - 2 (2 is the exponent of
+// E2M1's largest magnitude, 6 = 1.5 * 2^2), clamped below at -127 (E8M0's
+// smallest; an all-zero block takes it), and each value becomes the E2M1 code
+// nearest to v / 2^E, ties to the even code, magnitudes past 6 saturating;
+// the sign bit is v's own.  v / 2^E is exact (a power-of-two scaling that
+// stays normal), so every decision is taken on the fp32 value itself.
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+  const float a = fabsf(y);
+  // midpoints between neighbouring magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; a
+  // tie goes to the even code: > where the lower code is even, >= otherwise
+  const uint32_t c = static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f) +
+                     static_cast<uint32_t>(a > 1.25f) + static_cast<uint32_t>(a >= 1.75f) +
+                     static_cast<uint32_t>(a > 2.5f) + static_cast<uint32_t>(a >= 3.5f) +
+                     static_cast<uint32_t>(a > 5.f);
+  return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+// Writes 8 channels c0 .. c0+7 of row `row` of an MXFP4 tensor of `nrows`
+// rows of D channels (codes first, then scales).  Every lane of the
+// wavefront must call it (the block maximum is a 4-lane exchange); only
+// lanes with `store` set write.
+__device__ __forceinline__ void mx4_store(void* base, int64_t nrows, int64_t D, int64_t row, int64_t c0,
+                                          const float* v, bool store) {
+  uint32_t amax = 0;  // |v| bit patterns order as the magnitudes do
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t b = __float_as_uint(v[c]) & 0x7fffffffu;
+    amax = b > amax ? b : amax;
+  }
+  // lanes 4i .. 4i+3 hold one block: max over xor-1 and xor-2 neighbours
+  uint32_t o = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(amax), 0xB1, 0xF, 0xF, false));
+  amax = o > amax ? o : amax;
+  o = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(amax), 0x4E, 0xF, 0xF, false));
+  amax = o > amax ? o : amax;
+  // floor(log2 amax) is the biased exponent field less 127 for a normal
+  // amax; a subnormal or zero amax clamps to the smallest scale anyway
+  int e = static_cast<int>(amax >> 23) - 127 - 2;
+  e = e < -127 ? -127 : e;
+  uint32_t w = 0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) w |= e2m1_code(ldexpf(v[c], -e)) << (4 * c);
+  if (!store) return;
+  uint8_t* p = static_cast<uint8_t*>(base);
+  *reinterpret_cast<uint32_t*>(p + (row * D + c0) / 2) = w;
+  if ((c0 & 31) == 0) p[nrows * D / 2 + (row * D + c0) / 32] = static_cast<uint8_t>(e + 127);
+}
+
 // The candidates of entry j form one virtual list: stream-B tokens
 // (j-1)*m .. j*m-1 first (two-path, j >= 1), then stream-A tokens
 // j*m .. min((j+1)*m, n)-1.  Candidate i maps to its stream, raw row and
@@ -246,9 +297,12 @@ __device__ __forceinline__ bool compress_entry(const CompressArgs& a, const Rows
 // Bulk: one (entry, 16-byte channel group) per S thread slices.  The kernel
 // uses no LDS, so its workgroups can share a CU with an LDS-heavy kernel
 // running beside it (the indexer scan holds almost all of a CU's LDS).
-template <typename IO, int S>
+// MX: bf16 inputs, MXFP4 entries (S = 1 only: every lane of a block holds a
+// result).
+template <typename IO, int S, bool MX>
 __device__ __forceinline__ void compress_bulk(const CompressArgs& a) {
   static_assert(S >= 1 && S <= 64 && (S & (S - 1)) == 0, "slices: a power of two within a wavefront");
+  static_assert(!MX || S == 1, "MXFP4 entries need whole 32-channel blocks in consecutive lanes");
   constexpr int VEC = IO::VEC;
   constexpr int LANES = 256 / S;  // channel groups per workgroup
   const int slice = threadIdx.x % S;
@@ -264,13 +318,21 @@ __device__ __forceinline__ void compress_bulk(const CompressArgs& a) {
   const int64_t b = tmp / ne;
   const int64_t c0 = cv * VEC;
   float o[VEC];
-  if (compress_entry<IO, S>(a, BulkRows{a, b * a.n_raw}, live, a.e0 + jj, c0, slice, o))
+  const bool have = compress_entry<IO, S>(a, BulkRows{a, b * a.n_raw}, live, a.e0 + jj, c0, slice, o);
+  if constexpr (MX) {
+    if (!have) {
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) o[c] = 0.f;
+    }
+    mx4_store(a.out, a.B * a.out_ld, a.D, b * a.out_ld + jj, c0, o, have);
+  } else if (have) {
     IO::store(a.out, (b * a.out_ld + jj) * a.D + c0, o);
+  }
 }
 
-template <Dt DT, int S>
+template <Dt DT, int S, bool MX = false>
 __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
-  compress_bulk<Io<DT>, S>(a);
+  compress_bulk<Io<DT>, S, MX>(a);
 }
 
 // Per-token append: where the rows of sequence b live.  The new token
@@ -298,8 +360,11 @@ struct AppendRows {
 // entry p / m is folded from the rings and the new rows and written to the
 // cache.  No candidate of that entry occupies slot p % n_raw (n_raw >= 2m in
 // two-path mode, >= m otherwise), so the staging store races with no read.
-template <Dt DT, int S>
+// MX: the rings and new rows are bf16, the cache MXFP4 (every lane of a block
+// reaches the store together: the entry flag is uniform over a sequence).
+template <Dt DT, int S, bool MX = false>
 __global__ __launch_bounds__(256) void compress_append_kernel(CompressArgs a) {
+  static_assert(!MX || (DT == kBF16 && S == 1), "MXFP4 entries come from bf16 rows, one lane per channel group");
   constexpr int VEC = Io<DT>::VEC;
   constexpr int LANES = 256 / S;
   const int slice = threadIdx.x % S;
@@ -331,8 +396,17 @@ __global__ __launch_bounds__(256) void compress_append_kernel(CompressArgs a) {
   const int64_t j = ok ? p / a.m : 0;
   const bool emit = ok && (p + 1) % a.m == 0 && j < a.out_ld;
   float o[VEC];
-  if (compress_entry<Io<DT>, S>(a, AppendRows{a, b, p}, emit, j, c0, slice, o)) {
-    const int64_t row = a.lay.bt ? cache_row(a.lay, a.out_ld, b, j) : b * a.out_ld + j;
+  const bool have = compress_entry<Io<DT>, S>(a, AppendRows{a, b, p}, emit, j, c0, slice, o);
+  // the block table is read only for an entry that is written (j < L)
+  const int64_t row = !have ? 0 : (a.lay.bt ? cache_row(a.lay, a.out_ld, b, j) : b * a.out_ld + j);
+  if constexpr (MX) {
+    if (!have) {
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) o[c] = 0.f;
+    }
+    const int64_t nrows = a.lay.bt ? a.lay.npages * a.lay.page : a.B * a.out_ld;
+    mx4_store(a.out, nrows, a.D, row, c0, o, have);
+  } else if (have) {
     Io<DT>::store(a.out, row * a.D + c0, o);
   }
 }
@@ -346,6 +420,12 @@ hipError_t launch_compress(const CompressArgs& a, Dt dt, hipStream_t s) {
   // One thread per channel group folds every candidate in order (bulk:
   // wavefronts read whole rows); long blocks (m >= kSplitM) in a launch of
   // few entries (a decode-time refresh) fold on 16 lanes per channel group.
+  // MXFP4 entries (bf16 rows in) always fold in one lane per channel group.
+  if (dt == kMXFP4) {
+    hipLaunchKernelGGL((compress_kernel<kBF16, 1, true>), dim3(static_cast<uint32_t>((total + 255) / 256)),
+                       dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const bool lanes = a.m >= kSplitM && total < 32768;
   const dim3 grid(static_cast<uint32_t>(lanes ? (total + 15) / 16 : (total + 255) / 256));
 #define CSA_COMPRESS_LAUNCH(DT_)                                                             \
@@ -367,6 +447,7 @@ hipError_t launch_compress_append(const CompressArgs& a, Dt dt, hipStream_t s) {
   const dim3 grid(static_cast<uint32_t>((total + 255) / 256));
 #define CSA_APPEND_LAUNCH(DT_) hipLaunchKernelGGL((compress_append_kernel<DT_, 1>), grid, dim3(256), 0, s, a);
   switch (dt) {
+    case kMXFP4: hipLaunchKernelGGL((compress_append_kernel<kBF16, 1, true>), grid, dim3(256), 0, s, a); break;
     case kBF16: CSA_APPEND_LAUNCH(kBF16) break;
     case kFP8: CSA_APPEND_LAUNCH(kFP8) break;
     default: CSA_APPEND_LAUNCH(kF32) break;

@@ -51,7 +51,16 @@
  *     (shareware.cn article, the low-precision item of its list of what is
  *     compressed); accepted by csa_index_score / csa_index_topk for q_idx (N
  *     = B*T*H_I) and k_idx (N = B*L) with d_I = 128, H_I in {16, 32, 64,
- *     128}; compression and attention return CSA_ERR_UNSUPPORTED for it.
+ *     128}.  As the dtype of csa_compress / hca_compress /
+ *     csa_compress_append it names the output only: raw rows (and staging
+ *     rings) are bf16, the entries are written as MXFP4 (out holds N =
+ *     B*out_ld rows; an append's cache N = B*L rows, or num_pages*page pool
+ *     rows), D a multiple of 32.  Each entry is computed in fp32 as for bf16
+ *     output, then every block of 32 channels takes the scale 2^E, E =
+ *     floor(log2 of the block's largest magnitude) - 2, at least -127 (an
+ *     all-zero block: E = -127), and each channel the E2M1 code nearest to
+ *     v / 2^E (ties to the even code, past 6 saturating to 6, sign bit of
+ *     v).  Attention returns CSA_ERR_UNSUPPORTED for it.
  *   - Positions: a batch holds B sequences of n_ctx tokens (uniform length).
  *     The T queries of a sequence sit at positions t_i = n_ctx - T + i.
  *     Compressed entry s covers tokens [s*m, (s+1)*m) and is visible to the

@@ -35,6 +35,13 @@ see tests/test_oracle_*.py):
                               single-element and single-scale buffers); the
                               MXFP4 reading of "FP4" and the buffer layout are
                               conventions: parity unpinned for the layout
+  mxfp4_encode                pinned (round trip of every representable block
+                              through mxfp4_decode, the nearest-value property
+                              by brute force over all 15 values at the block's
+                              scale, named ties to even, 4 <= amax / 2^E < 8,
+                              saturation, clamped scales); the scale rule is
+                              the OCP conversion, a reading (the pages name no
+                              encoding)
 """
 from __future__ import annotations
 
@@ -161,6 +168,43 @@ def mxfp4_decode(buf, shape) -> np.ndarray:
     vals = e2m1_decode(el).reshape(n // d, d // 32, 32)
     sc = e8m0_decode(b[n // 2:]).reshape(n // d, d // 32, 1)
     return (vals * sc).reshape(shape)
+
+
+def mxfp4_encode(x) -> np.ndarray:
+    """float values of shape (..., d), d a multiple of 32 -> an MXFP4 buffer
+    (uint8, the layout mxfp4_decode reads), by the OCP microscaling
+    conversion: a block of 32 consecutive elements of a row shares the scale
+    2^E, E = floor(log2(largest magnitude in the block)) - 2 (2 being the
+    exponent of E2M1's largest magnitude, 6 = 1.5 * 2^2), E clamped to E8M0's
+    range [-127, 127] and an all-zero block taking -127; each element is the
+    E2M1 magnitude nearest to |x| / 2^E (of two equally near, the one with
+    the even code; beyond 6 the nearest is 6, so large values saturate) with
+    x's own sign bit (a negative value that rounds to 0 keeps code 8).
+    NaN and infinities are rejected."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.isfinite(x).all():
+        raise ValueError("mxfp4_encode: NaN or infinity has no MXFP4 code")
+    d = x.shape[-1]
+    assert d % 32 == 0
+    blk = x.reshape(-1, 32)
+    amax = np.abs(blk).max(axis=1)
+    _, ex = np.frexp(amax)  # amax = f * 2^ex, 0.5 <= f < 1: floor(log2 amax) = ex - 1
+    E = np.where(amax > 0, ex - 1 - 2, -127)
+    E = np.clip(E, -127, 127)
+    y = np.abs(blk) / np.exp2(E.astype(np.float64))[:, None]  # exact: a power-of-two scaling
+    grid = e2m1_decode(np.arange(8))  # 0, .5, 1, 1.5, 2, 3, 4, 6
+    dist = np.abs(y[..., None] - grid)
+    best = dist.min(axis=-1, keepdims=True)
+    near = dist == best
+    # of the nearest codes (one, or two on a tie) take the even one
+    code = np.where(near[..., 0::2].any(axis=-1), np.argmax(near[..., 0::2], axis=-1) * 2,
+                    np.argmax(near, axis=-1))
+    code = code + np.where(np.signbit(blk), 8, 0)
+    flat = code.reshape(-1)
+    out = np.empty(flat.size // 2 + flat.size // 32, dtype=np.uint8)
+    out[: flat.size // 2] = (flat[0::2] | (flat[1::2] << 4)).astype(np.uint8)
+    out[flat.size // 2:] = (E + 127).astype(np.uint8)
+    return out
 
 
 def fp8_encode(x) -> np.ndarray:

@@ -197,8 +197,9 @@ def test_fp8_storage_is_validated(lib):
 
 
 def test_mxfp4_storage_is_validated(lib):
-    """CSA_MXFP4 (3): the indexer only (d_I = 128, H_I a multiple of 16 up to
-    128); compression and attention reject it as unsupported."""
+    """CSA_MXFP4 (3): the indexer (d_I = 128, H_I a multiple of 16 up to 128)
+    and the output of compression (D a multiple of 32); attention rejects it
+    as unsupported."""
     idx_args = [V] * 3 + [I] * 8 + [V, V, V, Z, ctypes.c_int, V]
     assert _call(lib, "csa_index_topk", idx_args, FAKE, None, FAKE, 1, 1, 100, 25, 64, 64, 4, 8,
                  FAKE, None, FAKE, 1 << 20, 3, None) == 2
@@ -208,8 +209,12 @@ def test_mxfp4_storage_is_validated(lib):
     assert _call(lib, "csa_index_topk", idx_args, FAKE, None, FAKE, 1, 1, 100, 25, 64, 128, 4, 0,
                  FAKE, None, FAKE, 1 << 20, 3, None) == 1
     args = [V] * 6 + [I] * 9 + [ctypes.c_int, V]
+    # D = 16 holds no 32-element block
     assert _call(lib, "csa_compress", args, FAKE, FAKE, None, None, None, FAKE,
-                 1, 16, 16, 4, 0, 16, 0, 4, 4, 3, None) == 2
+                 1, 16, 16, 4, 0, 16, 0, 4, 4, 3, None) == 1
+    # D = 32, empty entry range: accepted, nothing to do
+    assert _call(lib, "csa_compress", args, FAKE, FAKE, None, None, None, FAKE,
+                 1, 16, 32, 4, 0, 16, 2, 2, 4, 3, None) == 0
     attn = [V] * 3 + [I, V, I, V, V, I, I, V, F] + [I] * 5 + [V, V, V, Z, ctypes.c_int, V]
     assert _call(lib, "csa_sparse_attn", attn, FAKE, FAKE, FAKE, 10, FAKE, 4, None, None, 0, 0,
                  None, 0.1, 1, 1, 40, 64, 512, FAKE, None, None, 0, 3, None) == 2

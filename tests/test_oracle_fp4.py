@@ -93,3 +93,71 @@ def test_mxfp4_generator_is_deterministic_and_in_range():
     sc = a[n // 2:].numpy()
     assert sc.min() >= 125 and sc.max() <= 129 and len(np.unique(sc)) == 5
     assert len(np.unique(a[: n // 2].numpy())) > 100  # code bytes spread over the range
+
+
+# ---- the encoder (compression writes MXFP4 index keys) ----------------------
+# Pinned against the decoder above and by brute force, never by retyping its
+# rule: every representable block survives a round trip, each element is the
+# nearest of the 15 values at its block's scale, the named midpoints go to the
+# even code, and the scale is the one power of two that puts the block's
+# largest magnitude in [4, 8).
+
+def _all_values_at(E):
+    return oracle.e2m1_decode(np.arange(16)) * 2.0 ** E
+
+
+def test_mxfp4_encode_round_trips_every_representable_block():
+    rng = np.random.default_rng(3)
+    rows, d = 64, 128
+    codes = rng.integers(0, 16, size=(rows * d // 32, 32))
+    # one element per block of magnitude 4 or 6 (codes 6 / 7, either sign) fixes
+    # the block's scale as the one it was drawn with
+    codes[np.arange(codes.shape[0]), rng.integers(0, 32, size=codes.shape[0])] = \
+        rng.choice([6, 7, 14, 15], size=codes.shape[0])
+    flat = codes.reshape(-1)
+    scales = rng.integers(1, 250, size=rows * d // 32)
+    buf = np.concatenate([(flat[0::2] | (flat[1::2] << 4)), scales]).astype(np.uint8)
+    x = oracle.mxfp4_decode(buf, (rows, d))
+    assert np.array_equal(oracle.mxfp4_encode(x), buf)
+
+
+def test_mxfp4_encode_picks_the_nearest_value_at_the_block_scale():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((40, 64)) * np.exp2(rng.integers(-20, 20, size=(40, 1)))
+    buf = oracle.mxfp4_encode(x)
+    got = oracle.mxfp4_decode(buf, x.shape)
+    scale = oracle.e8m0_decode(buf[x.size // 2:]).reshape(40, 2)
+    for r in range(40):
+        for j in range(2):
+            blk = x[r, 32 * j:32 * j + 32]
+            s = scale[r, j]
+            assert 4.0 <= np.abs(blk).max() / s < 8.0
+            vals = _all_values_at(np.log2(s))
+            best = np.abs(blk[:, None] - vals[None, :]).min(axis=1)
+            assert np.array_equal(np.abs(got[r, 32 * j:32 * j + 32] - blk), best)
+
+
+def test_mxfp4_encode_named_ties_saturation_and_signs():
+    # scale 2^0 (the block holds 4.0); each midpoint goes to the even code
+    vals = [4.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.5, -0.3, -0.1, 0.0, -0.0, 6.0, 5.5, 2.75]
+    want = [4.0, 0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 6.0, -0.5, -0.0, 0.0, -0.0, 6.0, 6.0, 3.0]
+    x = np.array([vals + [0.0] * 16])
+    buf = oracle.mxfp4_encode(x)
+    assert buf[-1] == 127
+    got = oracle.mxfp4_decode(buf, x.shape)[0, :16]
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(np.array(want)))
+    # codes: -0.1 rounds to zero but keeps the sign bit (code 8)
+    assert (buf[5] & 0xF) == 8
+
+
+def test_mxfp4_encode_scale_clamps():
+    x = np.zeros((1, 32))
+    assert oracle.mxfp4_encode(x)[-1] == 0            # an all-zero block: the smallest scale
+    x[0, 3] = 2.0 ** -140                              # below 4 * 2^-127: still the smallest scale
+    buf = oracle.mxfp4_encode(x)
+    assert buf[-1] == 0 and np.array_equal(oracle.mxfp4_decode(buf, x.shape), np.zeros((1, 32)))
+    x[0, 3] = 2.0 ** -120 * 3                          # floor(log2) = -119 -> E = -121
+    assert oracle.mxfp4_encode(x)[-1] == 127 - 121
+    with pytest.raises(ValueError):
+        oracle.mxfp4_encode(np.full((1, 32), np.nan))
