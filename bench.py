@@ -61,10 +61,15 @@ SCHEDULES = ("alternate", "flash", "pro", "csa", "hca")
 class Stack:
     """Shapes of the 8-layer decode workload and its algorithmic bytes."""
 
-    def __init__(self, B=16, n_ctx=1_000_000, layers=8, eb=2, schedule="alternate", W=128):
-        assert schedule in SCHEDULES
+    def __init__(self, B=16, n_ctx=1_000_000, layers=8, eb=2, schedule="alternate", W=128, index_fmt=None):
+        assert schedule in SCHEDULES and index_fmt in (None, "mxfp4")
         self.B, self.n_ctx, self.layers, self.schedule = B, n_ctx, layers, schedule
         self.eb = eb  # bytes per stored element: caches, window, indexer q/k, compression inputs
+        # "mxfp4": the indexer's q and keys are MXFP4 (E2M1 + one E8M0 scale per
+        # 32 elements: 17/32 B per element), its raw key rows bf16, and the
+        # appends compress them straight to MXFP4 entries
+        self.ix = index_fmt
+        self.ieb = 17 / 32 if index_fmt == "mxfp4" else eb
         self.H, self.d = 64, 512
         self.HI, self.dI = 64, 128
         self.k, self.W = 1024, W
@@ -94,16 +99,16 @@ class Stack:
     def index_bytes(self):
         """csa_index_topk per query: the visible indexer keys, the query's
         index heads and head weights, the selected indices written."""
-        return self.nv_csa * self.dI * self.eb + self.HI * self.dI * self.eb + self.HI * 4 + self.k * 4
+        return self.nv_csa * self.dI * self.ieb + self.HI * self.dI * self.ieb + self.HI * 4 + self.k * 4
 
-    def _append_bytes(self, D, streams, m):
+    def _append_bytes(self, D, streams, m, e_in=None, e_out=None):
         """csa_compress_append of one stream: the new token's rows read and
         staged, and when its block completes the block's rows (and the
         previous block's, two-path) read and the entry written."""
-        e = self.eb
+        e = self.eb if e_in is None else e_in
         b = 2 * streams * D * e
         if self.emits(m):
-            b += streams * m * D * e + D * e
+            b += streams * m * D * e + D * (e if e_out is None else e_out)
         return b
 
     def _window_bytes(self):
@@ -118,8 +123,12 @@ class Stack:
         b += self._window_bytes()
         b += 2 * self.H * self.d * 2            # q and out (bf16)
         b += self.k * 4                         # selected indices, read by the attention
-        for D in (self.d, self.d, self.dI):     # K, V and index keys, two-path (4 streams)
+        for D in (self.d, self.d):              # K and V, two-path (4 streams)
             b += self._append_bytes(D, 4, self.m_csa)
+        if self.ix == "mxfp4":                  # index keys: bf16 rows in, MXFP4 entries out
+            b += self._append_bytes(self.dI, 4, self.m_csa, 2, self.ieb)
+        else:
+            b += self._append_bytes(self.dI, 4, self.m_csa)
         return b
 
     def hca_bytes(self):
@@ -161,6 +170,20 @@ STREAMS = {"k": ("k", "z_k", "xb_k", "zb_k"), "v": ("v", "z_v", "xb_v", "zb_v"),
            "idx": ("k_idx", "z_idx", "xb_idx", "zb_idx")}
 
 
+# E8M0 scales of the generated MXFP4 indexer tensors: 2^-2 .. 2^2
+MX_SCALES = (125, 129)
+
+
+def mxfp4_tensor(shape, name, layer, device):
+    """A seeded MXFP4 tensor of logical shape `shape` (random E2M1 codes,
+    E8M0 scales in MX_SCALES), wrapped for the binding."""
+    import compressed_sparse_kv_compress_amd as csa
+    n = math.prod(shape)
+    buf = syn.mxfp4_(torch.empty(n // 2 + n // 32, dtype=torch.uint8, device=device), SEED, syn.TID[name], n,
+                     scale_lo=MX_SCALES[0], scale_hi=MX_SCALES[1], layer=layer)
+    return csa.MXFP4(buf, shape)
+
+
 class GpuState:
     """All device buffers of the workload, generated in place on the GPU, and
     the decode step over them."""
@@ -185,7 +208,6 @@ class GpuState:
         si = dI ** -0.5
         sd = d ** -0.5 if st.eb == 2 else 1.0          # K/V value scale
         self.ascale = st.scale if st.eb == 2 else st.scale * d ** -0.5
-        dt_code = csa.CSA_BF16 if st.eb == 2 else csa.CSA_FP8
         self.pos = torch.full((B,), t, dtype=torch.int64, device=device)
         self.ring_layout = csa.layout(ring=True)
         self.layers = []
@@ -211,14 +233,19 @@ class GpuState:
                 L = st.L_csa
                 lay["kc"] = gen((B, L, d), "kc", sd, sto)
                 lay["vc"] = gen((B, L, d), "vc", sd, sto)
-                lay["ki"] = gen((B, L, dI), "kic", si, sto)
-                lay["qi"] = gen((B, 1, st.HI, dI), "q_idx", si, sto)
+                if st.ix == "mxfp4":
+                    lay["ki"] = mxfp4_tensor((B, L, dI), "kic", li, device)
+                    lay["qi"] = mxfp4_tensor((B, 1, st.HI, dI), "q_idx", li, device)
+                else:
+                    lay["ki"] = gen((B, L, dI), "kic", si, sto)
+                    lay["qi"] = gen((B, 1, st.HI, dI), "q_idx", si, sto)
                 lay["wi"] = gen((B, 1, st.HI), "w_idx", st.HI ** -0.5, torch.float32)
                 for s, D, sc in (("k", d, sd), ("v", d, sd), ("idx", dI, si)):
                     scales = (sc, 0.5, sc, 0.5)
-                    lay["new_" + s] = [raw_rows(st, nm, li, t, 1, D, device, scl, sto)[:, 0].contiguous()
+                    rdt = bf if (s == "idx" and st.ix == "mxfp4") else sto
+                    lay["new_" + s] = [raw_rows(st, nm, li, t, 1, D, device, scl, rdt)[:, 0].contiguous()
                                        for nm, scl in zip(STREAMS[s], scales)]
-                    lay["ring_" + s] = [ring_of(raw_rows(st, nm, li, t - S + 1, S, D, device, scl, sto), t - S + 1)
+                    lay["ring_" + s] = [ring_of(raw_rows(st, nm, li, t - S + 1, S, D, device, scl, rdt), t - S + 1)
                                         for nm, scl in zip(STREAMS[s], scales)]
                 lay["idx"] = torch.empty((B, 1, st.k), dtype=torch.int32, device=device)
                 lay["itk_ws"] = torch.zeros(max(16, csa.csa_index_topk_workspace(B, 1, L, st.HI, st.k)),
@@ -567,10 +594,12 @@ def prefill_sparse_attn(queries: int, reps: int = 3):
                     "top out near 7.3 TB/s on this GPU, i.e. about 18.7% of the bf16 peak"}
 
 
-def fp8_storage_step(B: int, steps: int, warmup: int):
+def fp8_storage_step(B: int, steps: int, warmup: int, index_fmt=None):
     """The same 8-layer decode step with FP8 (E4M3) storage: reported beside
-    the bf16 headline, never as it."""
-    st = Stack(B=B, eb=1)
+    the bf16 headline, never as it.  index_fmt "mxfp4": the pages' own mix,
+    FP8 main KV with the indexer's q.k in FP4 (MXFP4 q and keys, the appends
+    compressing bf16 index-key rows straight to MXFP4 entries)."""
+    st = Stack(B=B, eb=1, index_fmt=index_fmt)
     state = GpuState(st)
     for _ in range(warmup):
         state.step()
@@ -592,7 +621,9 @@ def fp8_storage_step(B: int, steps: int, warmup: int):
     torch.cuda.empty_cache()
     idx_bytes = st.index_bytes() * st.B
     return {
-        "storage": "E4M3 caches, window, indexer q/k and compression inputs; bf16 query and output",
+        "storage": ("E4M3 K/V caches, window and K/V compression inputs; MXFP4 indexer q and keys (bf16 index-key "
+                    "rows compressed to MXFP4 by the appends); bf16 query and output" if index_fmt else
+                    "E4M3 caches, window, indexer q/k and compression inputs; bf16 query and output"),
         "ms_per_step": ms, "queries_per_s": st.B / (ms * 1e-3),
         "algorithmic_bytes_per_step": st.step_bytes(),
         "achieved_GBps": st.step_bytes() / (ms * 1e-3) / 1e9,
@@ -1028,6 +1059,9 @@ def main():
         fp8 = fp8_storage_step(args.batch, args.steps, args.warmup)
         print("# fp8 storage: %.3f ms/step" % fp8["ms_per_step"], file=sys.stderr, flush=True)
         fp8["index_topk_mxfp4"] = index_topk_mxfp4(args.batch)
+        fp8["fp8_kv_mxfp4_index_step"] = fp8_storage_step(args.batch, args.steps, args.warmup, index_fmt="mxfp4")
+        print("# fp8 K/V + mxfp4 indexer: %.3f ms/step" % fp8["fp8_kv_mxfp4_index_step"]["ms_per_step"],
+              file=sys.stderr, flush=True)
         print("# mxfp4 index_topk: %.3f ms/call" % fp8["index_topk_mxfp4"]["ms_per_call"], file=sys.stderr,
               flush=True)
 

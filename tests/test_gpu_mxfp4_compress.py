@@ -172,3 +172,78 @@ def test_index_topk_on_compressed_mxfp4_keys_matches_oracle():
             nv = min(k_c.shape[1], (n - T + t) // m)
             eps = index_eps(q_c[b, t], None, k_c[b])[:nv]
             assert near_tie_check(idx[b, t], want[b, t], osc[b, t], nv, k, eps) <= 2
+
+
+def test_fp8_kv_mxfp4_index_step_csa_layer_matches_oracle():
+    """The decode step with the pages' storage mix (FP8 main KV, MXFP4 indexer
+    q and keys, the appends compressing bf16 index-key rows to MXFP4), first
+    CSA layer of sequence 1: the index-key entry the token completes equals
+    bulk MXFP4 compression of the same raw rows byte for byte and decodes to
+    the fp64 compression within the format's rounding; the selection matches
+    the oracle on the decoded q and keys up to certified near-ties; the
+    attention matches the oracle fed the GPU's selection."""
+    import bench
+    from helpers import BF16_TOL, max_abs, to_np
+    st = bench.Stack(B=2, n_ctx=65536, eb=1, index_fmt="mxfp4")
+    state = bench.GpuState(st)
+    state.step()
+    torch.cuda.synchronize()
+    li, b = 0, 1
+    lay = state.layers[li]
+    assert lay["kind"] == "csa" and st.emits(st.m_csa)
+    m, t, L, dI, HI, d, H, W, k = st.m_csa, st.t, st.L_csa, st.dI, st.HI, st.d, st.H, st.W, st.k
+    e, si = t // m, dI ** -0.5
+    scales = (si, 0.5, si, 0.5)
+
+    # the completed entry: byte for byte the bulk MXFP4 entry of the same rows
+    raw = [bench.raw_rows(st, nm, li, (e - 1) * m, 2 * m, dI, "cuda", sc) for nm, sc in zip(bench.STREAMS["idx"], scales)]
+    bulk = csa.csa_compress(raw[0], raw[1], m, x_b=raw[2], z_b=raw[3], n=st.n_ctx, p0=(e - 1) * m, e0=e, e1=e + 1,
+                            mxfp4=True)
+    cache, one = mx_bytes(lay["ki"]), mx_bytes(bulk)
+    row, half = b * L + e, st.B * L * dI // 2
+    assert np.array_equal(cache[row * dI // 2:(row + 1) * dI // 2], one[b * dI // 2:(b + 1) * dI // 2])
+    assert np.array_equal(cache[half + row * dI // 32:half + (row + 1) * dI // 32],
+                          one[st.B * dI // 2 + b * dI // 32:st.B * dI // 2 + (b + 1) * dI // 32])
+    raw_c = [bench.raw_rows(st, nm, li, (e - 1) * m, 2 * m, dI, "cpu", sc).double().numpy()
+             for nm, sc in zip(bench.STREAMS["idx"], scales)]
+    want = oracle.compress(raw_c[0], raw_c[1], m, x_b=raw_c[2], z_b=raw_c[3], n=st.n_ctx, p0=(e - 1) * m, e0=e,
+                           e1=e + 1)[b, 0]
+    dec = oracle.mxfp4_decode(cache[row * dI // 2:(row + 1) * dI // 2].tolist() +
+                              cache[half + row * dI // 32:half + (row + 1) * dI // 32].tolist(), (1, dI))[0]
+    blk_scale = np.repeat(oracle.e8m0_decode(cache[half + row * dI // 32:half + (row + 1) * dI // 32]), 32)
+    assert np.all(np.abs(dec - want) <= 2.0 * blk_scale + 1e-5)
+
+    # the selection over the generated MXFP4 q and keys (the rewritten entry is not visible)
+    def mx_cpu(shape, name):
+        n = int(np.prod(shape))
+        buf = syn.mxfp4_(torch.empty(n // 2 + n // 32, dtype=torch.uint8), bench.SEED, syn.TID[name], n,
+                         scale_lo=bench.MX_SCALES[0], scale_hi=bench.MX_SCALES[1], layer=li)
+        return oracle.mxfp4_decode(buf.numpy(), shape)
+    q_c = mx_cpu((st.B, 1, HI, dI), "q_idx")[b:b + 1]
+    k_c = mx_cpu((st.B, L, dI), "kic")[b:b + 1]
+    w_c = syn.make((st.B, 1, HI), bench.SEED, syn.TID["w_idx"], scale=HI ** -0.5, layer=li).double().numpy()[b:b + 1]
+    idx_c, sc = oracle.index_topk(q_c, k_c, m, k, w=w_c, n_ctx=st.n_ctx)
+    got_idx = lay["idx"].cpu().numpy()[b, 0]
+    nv = st.nv_csa
+    eps = index_eps(q_c[0, 0], w_c[0, 0], k_c[0])[:nv]
+    assert near_tie_check(got_idx, idx_c[0, 0], sc[0, 0], nv, k, eps) <= 2
+
+    # attention over the GPU's selection: FP8 K/V rows and window, bf16 query
+    f8 = torch.float8_e4m3fn
+    sel = got_idx[got_idx >= 0]
+    kc_c = np.zeros((1, L, d))
+    vc_c = np.zeros((1, L, d))
+    for name, arr in (("kc", kc_c), ("vc", vc_c)):
+        rows = syn.rows((st.B, L, d), b * L + sel, bench.SEED, syn.TID[name], dtype=f8, scale=1.0, layer=li)
+        arr[0, sel] = oracle.fp8_decode(rows.view(torch.uint8).numpy())
+    kr_c = oracle.fp8_decode(bench.raw_rows(st, "kr", li, t - W + 1, W, d, "cpu", 1.0, f8)[b:b + 1]
+                             .view(torch.uint8).numpy())
+    vr_c = oracle.fp8_decode(bench.raw_rows(st, "vr", li, t - W + 1, W, d, "cpu", 1.0, f8)[b:b + 1]
+                             .view(torch.uint8).numpy())
+    q = syn.make((st.B, 1, H, d), bench.SEED, syn.TID["q"], dtype=BF, scale=d ** -0.5, layer=li).double().numpy()
+    sink = syn.make((H,), bench.SEED, syn.TID["sink"], layer=li).double().numpy()
+    o_g, _ = oracle.sparse_attn(q[b:b + 1], kc_c, vc_c, got_idx[None, None], kr_c, vr_c, W, sink=sink,
+                                scale=state.ascale, n_ctx=st.n_ctx)
+    assert max_abs(to_np(lay["out"][b:b + 1]), o_g) <= BF16_TOL
+    del state
+    torch.cuda.empty_cache()
