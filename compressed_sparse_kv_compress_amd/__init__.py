@@ -187,6 +187,8 @@ def _compress_out(x, B, ne, D, out, out_ld, mxfp4):
     mx = mxfp4 or isinstance(out, MXFP4)
     if mx and x.dtype != torch.bfloat16:
         raise TypeError("MXFP4 entries are compressed from bfloat16 rows, got %s" % x.dtype)
+    if mx and out is not None and not isinstance(out, MXFP4):
+        raise TypeError("MXFP4 entries need an MXFP4 output tensor")
     if out is None:
         if mx:
             nel = B * ne * D
