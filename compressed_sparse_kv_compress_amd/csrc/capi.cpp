@@ -233,7 +233,9 @@ size_t csa_index_topk_workspace(int64_t B, int64_t T, int64_t L, int64_t H_I, in
   if (B <= 0 || T <= 0 || k <= 0) return 0;
   const size_t chunked = static_cast<size_t>(B) * T * index_topk_row_bytes(L, k);
   const size_t fused = L > 0 ? csa::index_topk_fused_ws_bytes(B * T, L, k) : 0;
-  return chunked > fused ? chunked : fused;
+  const size_t listed = L > 0 ? csa::index_topk_listed_ws_bytes(B * T, L, k) : 0;
+  const size_t most = chunked > fused ? chunked : fused;
+  return most > listed ? most : listed;
 }
 
 }  // extern "C"
@@ -273,6 +275,15 @@ csa_status_t index_topk_run(const csa::SeqLayout& lay, const void* q_idx, const 
     csa::IndexScoreArgs a{q_idx, w_idx, k_idx, nullptr, L, 0, rows, B, T, n_ctx, L, H_I, d_I, m, to_dt(dtype), lay};
     csa::TopkArgs t{nullptr, L, 0, rows, T, n_ctx, L, m, k, idx, out_score, lay.lens};
     return hip_status(csa::launch_index_topk_fused(a, t, ws, s), "fused index/top-k launch");
+  }
+  if (!multi && ws != nullptr && L > 0 && csa::index_topk_listable(rows, L, H_I, d_I, k, to_dt(dtype)) &&
+      ws_bytes >= csa::index_topk_listed_ws_bytes(rows, L, k)) {
+    // More parts than the fused path takes: scores plus exact per-part lists,
+    // a list merge per row, the stand-alone top-k only for unsettled rows.
+    if (!aligned16(ws)) return fail(CSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+    csa::IndexScoreArgs a{q_idx, w_idx, k_idx, nullptr, L, 0, rows, B, T, n_ctx, L, H_I, d_I, m, to_dt(dtype), lay};
+    csa::TopkArgs t{nullptr, L, 0, rows, T, n_ctx, L, m, k, idx, out_score, lay.lens};
+    return hip_status(csa::launch_index_topk_listed(a, t, ws, s), "listed index/top-k launch");
   }
   const size_t per_row = index_topk_row_bytes(L, k);
   if (ws == nullptr || ws_bytes < per_row)

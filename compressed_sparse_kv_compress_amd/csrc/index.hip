@@ -334,6 +334,106 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
   if (tid == 0) co.ccnt[slot] = cap;
 }
 
+// Exact short list of a part of at most kListPartKeys keys, for the listed
+// path: every visible entry whose score is >= V, V the part's r-th largest
+// score (r = co.lrank; every entry when the part holds at most r, V = -inf),
+// in index order, with its count and V.  More than co.lcap entries (ties at
+// V) leave no list (count -1).  V comes from a radix select on
+// order-preserving keys, four 8-bit digits (one wavefront reads 4 bins per
+// lane with one 16-byte LDS read); the bins and the per-pass results live in
+// the idle tile ring.
+constexpr int kListPartKeys = 1024;
+template <int NW>
+__device__ __forceinline__ void part_list(const IndexCandidates& co, int64_t slot, int64_t kb, int n,
+                                          const float (*sbuf)[kScoreSlots<NW>], uint8_t* scratch) {
+  constexpr int NT = 64 * NW;
+  constexpr int IT = kListPartKeys / NT;  // entries per thread: 4 (bf16) or 2 (eight wavefronts)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const uint32_t r = static_cast<uint32_t>(co.lrank);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(scratch);  // two sets of 256 bins
+  uint32_t* pick = hist + 512;                             // per set: digit, entries above it
+  uint32_t* wsum = pick + 4;                               // per-wavefront counts
+  float x[IT];
+  uint32_t key[IT];
+  uint32_t valid = 0;
+#pragma unroll
+  for (int j = 0; j < IT; ++j) {
+    const int o = tid * IT + j;
+    x[j] = part_score<NW>(sbuf, o < n ? o : 0);
+    key[j] = float_key(x[j]);
+    valid |= static_cast<uint32_t>(o < n) << j;
+  }
+  uint32_t kth = 0;  // key of the r-th largest score (0: keep every valid entry)
+  if (static_cast<uint32_t>(n) > r) {
+    // four 8-bit digits, most significant first; bins double-buffered so
+    // that one pass's counting can follow the previous pass's search
+    uint32_t prefix = 0, mask = 0, need = r;
+    hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      uint32_t* h = hist + 256 * (pass & 1);
+#pragma unroll
+      for (int j = 0; j < IT; ++j)
+        if (((valid >> j) & 1) && (key[j] & mask) == prefix) atomicAdd(&h[(key[j] >> shift) & 255u], 1u);
+      hist[256 * ((pass + 1) & 1) + (tid & 255)] = 0;  // the next pass's bins
+      __syncthreads();
+      if (wave == 0) {  // lane l holds bins 255-4l .. 252-4l (highest first)
+        const u32x4 c = *reinterpret_cast<const u32x4*>(h + 252 - 4 * lane);
+        const uint32_t sum = c[0] + c[1] + c[2] + c[3];
+        uint32_t above = sel::wave_incl_scan(sum) - sum;
+#pragma unroll
+        for (int q = 3; q >= 0; --q) {
+          if (above < need && above + c[q] >= need) {
+            pick[2 * (pass & 1)] = static_cast<uint32_t>(252 - 4 * lane + q);
+            pick[2 * (pass & 1) + 1] = above;
+          }
+          above += c[q];
+        }
+      }
+      __syncthreads();
+      prefix |= pick[2 * (pass & 1)] << shift;
+      mask |= 255u << shift;
+      need -= pick[2 * (pass & 1) + 1];
+    }
+    kth = prefix;
+  }
+  // ordered compaction of the entries with key >= kth
+  uint32_t keep = 0;
+#pragma unroll
+  for (int j = 0; j < IT; ++j) keep |= static_cast<uint32_t>(((valid >> j) & 1) && key[j] >= kth) << j;
+  const uint32_t cnt = static_cast<uint32_t>(__builtin_popcount(keep));
+  const uint32_t incl = sel::wave_incl_scan(cnt);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t pos = incl - cnt, total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    pos += w < wave ? wsum[w] : 0u;
+    total += wsum[w];
+  }
+  const bool fits = total <= static_cast<uint32_t>(co.lcap);
+  if (fits) {
+    float* lv = co.lval + slot * co.lcap;
+    int32_t* li = co.lidx + slot * co.lcap;
+#pragma unroll
+    for (int j = 0; j < IT; ++j) {
+      if ((keep >> j) & 1) {
+        lv[pos] = x[j];
+        li[pos] = static_cast<int32_t>(kb + tid * IT + j);
+        ++pos;
+      }
+    }
+  }
+  if (tid == 0) {
+    co.lcnt[slot] = fits ? static_cast<int32_t>(total) : -1;
+    co.lthr[slot] = kth == 0 ? -INFINITY : key_float(kth);
+  }
+}
+
 // d_I = 128 (KS = 4), MB = H_I / 16 head blocks.  Workgroup (row, part)
 // scores keys [part * 4 * per_wave, +4 * per_wave); with NW wavefronts (4 for
 // bf16 keys, 8 for FP8 / MXFP4) wavefront w takes tiles w, w+NW, w+2NW, ...
@@ -609,6 +709,9 @@ __global__ __launch_bounds__(64 * (KF ? kWaves8 : kWaves), 1) void index_score_s
         if (o + e < nk) dst[o + e] = x[e];
     }
   }
+  // listed path (parts of at most kListPartKeys keys): the part's exact list
+  if (co.lval != nullptr)
+    part_list<NW>(co, lrow * parts + part, kb, ntiles > 0 ? static_cast<int>(kv - kb) : 0, sbuf, &ring[0][0][0]);
 }
 
 // Prefill scoring (bf16, FP8 or MXFP4, d_I = 128): a workgroup takes 16 query
@@ -1082,6 +1185,78 @@ hipError_t launch_index_topk_fused(const IndexScoreArgs& a, const TopkArgs& t, v
   const hipError_t e = launch_stream<true>(a, co, s);
   if (e != hipSuccess) return e;
   return launch_topk_merge(t, parts, co, true, s);
+}
+
+// Listed path geometry: r = kMergeUnion / parts (at least twice a part's
+// share k / parts of the row's top-k, so that a part rarely holds more than
+// its list), list capacity 2r for ties.
+static void listed_plan(int64_t nrows, int64_t L, int64_t k, int64_t* parts, int64_t* r) {
+  int64_t per_wave;
+  index_plan(nrows, L, parts, &per_wave);
+  *r = kMergeUnion / *parts;
+  if (kWaves * per_wave > kListPartKeys || *parts > 512 || *r * *parts < k || *r < 2 * ((k + *parts - 1) / *parts) ||
+      2 * k > mrg::kStage)
+    *r = 0;
+}
+
+bool index_topk_listable(int64_t nrows, int64_t L, int64_t HI, int64_t dI, int64_t k, Dt dt) {
+  if ((dt != kBF16 && dt != kFP8 && dt != kMXFP4) || dI != 128 || nrows <= 0 || L <= 0 || k < 1) return false;
+  if (!(HI == 16 || HI == 32 || HI == 64 || HI == 128)) return false;
+  int64_t parts, r;
+  listed_plan(nrows, L, k, &parts, &r);
+  return r > 0;
+}
+
+// Workspace of the listed path: the scores [nrows][L], the stand-alone
+// top-k's state for every row (the fallback), then per (row, part) a list of
+// 2r entries (8 B each), its count and threshold, then one flag per row.
+static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+size_t index_topk_listed_ws_bytes(int64_t nrows, int64_t L, int64_t k) {
+  int64_t parts, r;
+  listed_plan(nrows, L, k, &parts, &r);
+  const size_t units = static_cast<size_t>(nrows) * parts;
+  return align256(static_cast<size_t>(nrows) * L * sizeof(float)) + nrows * topk_ws_bytes_per_row(L, k) +
+         align256(units * (2 * r * 8 + 8)) + align256(static_cast<size_t>(nrows) * 4);
+}
+
+hipError_t launch_index_topk_listed(const IndexScoreArgs& a0, const TopkArgs& t0, void* ws, hipStream_t s) {
+  if (a0.nrows == 0) return hipSuccess;
+  int64_t parts, r;
+  listed_plan(a0.nrows, a0.L, t0.k, &parts, &r);
+  if (r == 0) return hipErrorInvalidValue;
+  const int64_t units = a0.nrows * parts;
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  float* sc = reinterpret_cast<float*>(p);
+  p += align256(static_cast<size_t>(a0.nrows) * a0.L * sizeof(float));
+  void* sel_ws = p;
+  p += a0.nrows * topk_ws_bytes_per_row(a0.L, t0.k);
+  IndexCandidates co;
+  co.cap = 0;
+  co.cval = nullptr;
+  co.cidx = nullptr;
+  co.ccnt = nullptr;
+  co.lrank = r;
+  co.lcap = 2 * r;
+  co.lval = reinterpret_cast<float*>(p);
+  co.lidx = reinterpret_cast<int32_t*>(co.lval + units * co.lcap);
+  co.lcnt = co.lidx + units * co.lcap;
+  co.lthr = reinterpret_cast<float*>(co.lcnt + units);
+  p += align256(static_cast<size_t>(units) * (2 * r * 8 + 8));
+  int32_t* done = reinterpret_cast<int32_t*>(p);
+  IndexScoreArgs a = a0;
+  a.score = sc;
+  a.ld = a0.L;
+  a.row0 = 0;
+  hipError_t e = launch_stream<false>(a, co, s);
+  if (e != hipSuccess) return e;
+  TopkArgs t = t0;
+  t.score = sc;
+  t.ld = a0.L;
+  t.row0 = 0;
+  e = launch_topk_list_merge(t, parts, co, done, s);
+  if (e != hipSuccess) return e;
+  t.done = done;
+  return launch_topk(t, sel_ws, s);  // rows the lists did not settle
 }
 
 bool index_shape_supported(int64_t HI, int64_t dI, Dt dt) {

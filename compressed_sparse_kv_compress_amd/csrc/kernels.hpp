@@ -117,6 +117,9 @@ struct TopkArgs {
   int32_t* idx;        // [rows][k] (offset to row0 already)
   float* out_score;    // [rows][k] or null
   const int64_t* lens = nullptr;  // per-sequence token counts (see SeqLayout)
+  // [rows] or null: rows a list merge already settled (nonzero); the part and
+  // merge kernels skip them
+  const int32_t* done = nullptr;
 };
 // ws: topk_ws_bytes_per_row(L, k) bytes per row of the launch.
 size_t topk_ws_bytes_per_row(int64_t L, int64_t k);
@@ -156,6 +159,19 @@ inline void compact_list_plan(int64_t nparts, int64_t k, int64_t* lrank, int64_t
 bool index_multi_rows(int64_t T, int64_t HI, int64_t row0, int64_t nrows);
 bool index_topk_fusable(int64_t nrows, int64_t L, int64_t HI, int64_t dI, int64_t k, Dt dt);
 size_t index_topk_fused_ws_bytes(int64_t nrows, int64_t L, int64_t k);
+// Listed path, for decode shapes with more parts than the fused path takes
+// (one query at 1M entries, or 8 at 131,072): the scan writes the scores and
+// each part's exact top-r list (r = kMergeUnion / parts per row); one
+// workgroup per row merges the lists, and only rows whose lists do not
+// settle them go through the stand-alone top-k on the written scores.
+// ws: index_topk_listed_ws_bytes(nrows, L, k) bytes for all rows at once.
+bool index_topk_listable(int64_t nrows, int64_t L, int64_t HI, int64_t dI, int64_t k, Dt dt);
+size_t index_topk_listed_ws_bytes(int64_t nrows, int64_t L, int64_t k);
+hipError_t launch_index_topk_listed(const IndexScoreArgs& a, const TopkArgs& t, void* ws, hipStream_t s);
+// One workgroup per row merges the parts' exact lists (IndexCandidates
+// lval/lidx/lcnt/lthr, lcap) and sets done[row] when they settle it.
+hipError_t launch_topk_list_merge(const TopkArgs& a, int64_t nparts, const IndexCandidates& c, int32_t* done,
+                                  hipStream_t s);
 hipError_t launch_index_topk_fused(const IndexScoreArgs& a, const TopkArgs& t, void* ws, hipStream_t s);
 
 struct AttnArgs {

@@ -76,6 +76,7 @@ __global__ __launch_bounds__(kThreads, IT == kItemsHalf ? 2 : 1) void topk_part_
   __shared__ PartShared<IT> sh;
   const int64_t lrow = blockIdx.x / nparts;
   const int64_t part = blockIdx.x % nparts;
+  if (a.done && a.done[lrow]) return;  // settled by the list merge
   const int64_t nv = row_visible(a, a.row0 + lrow);
   if (nv <= a.k) return;  // the merge kernel keeps every visible entry
   const int64_t base = part * kPart;
@@ -161,6 +162,7 @@ __global__ __launch_bounds__(kMThreads) void topk_merge_kernel(TopkArgs a, int n
                                                                bool fused) {
   __shared__ Merge::Shared sh;
   const int64_t lrow = blockIdx.x;
+  if (a.done && a.done[lrow]) return;  // settled by the list merge
   if (!fused && merge_trivial(a, lrow)) return;
   int32_t* o = a.idx + lrow * a.k;
   float* os = a.out_score ? a.out_score + lrow * a.k : nullptr;
@@ -183,6 +185,26 @@ __global__ __launch_bounds__(kMThreads) void topk_merge_kernel(TopkArgs a, int n
   Merge::full(k, nparts, cap, c.cval + u0 * cap, c.cidx + u0 * cap, c.ccnt + u0, sh, o, os);
 }
 
+// List merge of the listed path: the union of the parts' exact lists settles
+// the row when every part's threshold is at most the union's k-th largest
+// (then the output is written and done[row] set); otherwise done[row] is
+// cleared and the stand-alone top-k runs on the row's scores.  Rows with at
+// most k visible entries keep all of them here.
+__global__ __launch_bounds__(kMThreads) void topk_list_merge_kernel(TopkArgs a, int nparts, IndexCandidates c,
+                                                                    int32_t* done) {
+  __shared__ Merge::Shared sh;
+  const int64_t lrow = blockIdx.x;
+  bool ok = merge_trivial(a, lrow);
+  if (!ok) {
+    const int64_t u0 = lrow * nparts;
+    ok = Merge::lists<mrg::kSlots / 4 / kMThreads>(static_cast<int>(a.k), nparts, c.lval + u0 * c.lcap,
+                                                   c.lidx + u0 * c.lcap, c.lcnt + u0, c.lthr + u0, c.lcap, sh,
+                                                   a.idx + lrow * a.k,
+                                                   a.out_score ? a.out_score + lrow * a.k : nullptr);
+  }
+  if (threadIdx.x == 0) done[lrow] = ok ? 1 : 0;
+}
+
 // General merge (k >= 16384, or more than 256 parts): histogram passes over
 // the slots in L2, then ordered compaction tile by tile.
 __global__ __launch_bounds__(kThreads) void topk_merge_general(TopkArgs a, int64_t nparts, int64_t cap,
@@ -190,6 +212,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_general(TopkArgs a, int64
                                                                const int32_t* ccnt) {
   __shared__ struct { Sel::Shared core; } sh;
   const int64_t lrow = blockIdx.x;
+  if (a.done && a.done[lrow]) return;  // settled by the list merge
   if (merge_trivial(a, lrow)) return;
   int32_t* o = a.idx + lrow * a.k;
   float* os = a.out_score ? a.out_score + lrow * a.k : nullptr;
@@ -307,6 +330,15 @@ hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t s) {
   c.ccnt = ccnt;
   c.cap = cap;
   return launch_topk_merge(a, np, c, false, s);
+}
+
+hipError_t launch_topk_list_merge(const TopkArgs& a, int64_t np, const IndexCandidates& c, int32_t* done,
+                                  hipStream_t s) {
+  if (a.nrows == 0 || a.k == 0) return hipSuccess;
+  if (np > kMThreads || 2 * a.k > kStage) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_list_merge_kernel, dim3(static_cast<uint32_t>(a.nrows)), dim3(kMThreads), 0, s, a,
+                     static_cast<int>(np), c, done);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk_merge(const TopkArgs& a, int64_t np, const IndexCandidates& c, bool fused, hipStream_t s) {

@@ -252,8 +252,10 @@ def test_index_topk_single_pass_equals_score_then_select(B, T, L, HI, k, wts, bo
     sampled threshold; boost = -1: the last sixteenth of the key rows is
     scaled by 4, so the row's top-k sits in one part (the merge cannot use the
     parts' short lists and reads the full ones).  Batch 1 and 8 rows of
-    32768 take the stand-alone top-k on both sides (too many parts for the
-    single-pass plan); they are checked here against the oracle row."""
+    32768 have too many parts for the single-pass plan: csa_index_topk writes
+    the scores with exact per-part lists and merges those (boost = 1), or,
+    when the lists do not settle a row (boost = -1, 16), runs the stand-alone
+    top-k on the written scores; they are checked against the oracle row."""
     dI, m = 128, 4
     n_ctx = m * L
     seed = 40 + L
