@@ -47,11 +47,16 @@ def paged(dense, npages_extra, seed):
 
 
 LENS = (40000, 27003, 33337)
+# eight sequences of up to 131,072 tokens, k = 1024: more key ranges per row
+# than the single-pass scan takes, so index + top-k runs the listed path
+LENS8 = (131072, 118003, 99999, 131000, 64001, 120000, 100003, 77777)
 
 
-@pytest.mark.parametrize("dt", ["bf16", "fp8"])
-def test_paged_varlen_index_topk(dt):
-    B, HI, dI, m, k = len(LENS), 64, 128, 4, 512
+@pytest.mark.parametrize("dt,lens,k", [("bf16", LENS, 512), ("fp8", LENS, 512), ("bf16", LENS8, 1024),
+                                       ("fp8", LENS8, 1024)])
+def test_paged_varlen_index_topk(dt, lens, k):
+    LENS = lens
+    B, HI, dI, m = len(LENS), 64, 128, 4
     n_max = max(LENS)
     L = n_max // m + 3  # capacity in entries
     sto = torch.bfloat16 if dt == "bf16" else torch.float8_e4m3fn
