@@ -20,6 +20,9 @@
 //   2. merge kernel: one workgroup per row runs the same selection over the
 //      concatenated part candidates (part order = index order) and compacts
 //      the winners in order.
+//   A third kernel serves the listed index path: one workgroup per row merges
+//   the exact short lists the scan wrote for its key ranges and flags the
+//   rows they settle; the two kernels above then return at once for those.
 // Latency, not bandwidth, bounds both (a part is 64 KiB), so each histogram
 // pass costs three barriers (double-buffered bins, wave scans), and the
 // ordered compaction is one 32-bit workgroup scan of per-thread (greater,
