@@ -1214,6 +1214,7 @@ static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 size_t index_topk_listed_ws_bytes(int64_t nrows, int64_t L, int64_t k) {
   int64_t parts, r;
   listed_plan(nrows, L, k, &parts, &r);
+  if (r == 0) return 0;  // not a listed shape
   const size_t units = static_cast<size_t>(nrows) * parts;
   return align256(static_cast<size_t>(nrows) * L * sizeof(float)) + nrows * topk_ws_bytes_per_row(L, k) +
          align256(units * (2 * r * 8 + 8)) + align256(static_cast<size_t>(nrows) * 4);
