@@ -272,7 +272,7 @@ class GpuState:
         self.side = torch.cuda.Stream(device=device)  # default priority
         torch.cuda.synchronize()
 
-    def step(self, ev=None, only=None, csa_layer=None):
+    def step(self, ev=None, only=None, csa_layer=None, scan_ev=None):
         """One decode step of the token at t = n_ctx - 1 through all layers.
 
         The side stream first appends the token's raw window rows to every
@@ -285,7 +285,9 @@ class GpuState:
         ev: optional dict of event lists keyed by call name; events bracket
         calls (all, or the names in `only`) on the stream that runs them;
         csa_layer: bracket only that CSA layer's index call (every timing
-        event costs a few microseconds of idle GPU between kernels)."""
+        event costs a few microseconds of idle GPU between kernels);
+        scan_ev: (CSA layer, (start, stop)): that layer's scan kernel records
+        the two events itself as it starts and ends (no idle gap)."""
         csa, st = self.csa, self.st
         main = torch.cuda.current_stream()
         side = self.side
@@ -328,6 +330,8 @@ class GpuState:
         for lay in self.layers:
             if lay["kind"] == "csa":
                 mark("index_topk", ci)
+                if scan_ev is not None and scan_ev[0] == ci:
+                    csa.time_next_scan(*scan_ev[1])
                 csa.csa_index_topk(lay["qi"], lay["ki"], st.m_csa, st.k, w_idx=lay["wi"], n_ctx=st.n_ctx,
                                    idx=lay["idx"], ws=lay["itk_ws"])
                 mark("index_topk_end", ci)
@@ -400,16 +404,17 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def counter_traffic(kernel_src, per_launch_units):
-    """HBM bytes per csa_index_topk call (its two kernels) from the committed
-    rocprofv3 counter summary, or None when it is missing or the kernels'
-    sources changed since."""
+def counter_traffic(kernel_src, per_launch_units, key="hbm_bytes_per_launch"):
+    """HBM bytes per csa_index_topk call (its two kernels; key names the scan
+    kernel alone with index_score_stream_hbm_bytes_per_launch) from the
+    committed rocprofv3 counter summary, or None when it is missing or the
+    kernels' sources changed since."""
     path = os.path.join(ROOT, "profiles", "index_topk_stack8_b16_counters.txt")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
     m_src = re.search(r"^source_sha256_16:\s*(\w+)", txt, re.M)
-    m_b = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    m_b = re.search(r"^" + key + r":\s*([0-9.eE+]+)", txt, re.M)
     m_u = re.search(r"^queries_per_launch:\s*(\d+)", txt, re.M)
     if not (m_src and m_b and m_u) or m_src.group(1) != source_hash(kernel_src):
         return None
@@ -1008,24 +1013,34 @@ def main():
     # Timed region: K steps; HIP events bracket one csa_index_topk call (the
     # dominant call) in every fourth step, on the stream it runs on, taking the
     # CSA layers in turn (each bracketed call leaves the GPU idle for a few
-    # microseconds around its events, so not every step carries them).
+    # microseconds around its events, so not every step carries them), and in
+    # every step one CSA layer's scan kernel stamps its own start and end.
     ev = {}
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    n_csa = st.kinds().count("csa")
+    # every step's scan kernel of one CSA layer (in turn) stamps its own start
+    # and end (hipExtLaunchKernel events: no command between the kernels)
+    scan_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
+    for a_, b_ in scan_evs:  # create the events before the timed region
+        a_.record()
+        b_.record()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
-    n_csa = st.kinds().count("csa")
     for i in range(args.steps):
+        sev = (i % n_csa, scan_evs[i]) if n_csa else None
         if i % 4 == 0 or args.steps < 4:
-            state.step(ev, only=("index_topk",), csa_layer=(i // 4) % n_csa)
+            state.step(ev, only=("index_topk",), csa_layer=(i // 4) % n_csa, scan_ev=sev)
         else:
-            state.step()
+            state.step(scan_ev=sev)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = start.elapsed_time(stop) / args.steps
-    idx_ms = event_means_ms(ev)["index_topk"]
+    idx_ms = event_means_ms(ev)["index_topk"] if ev else None
+    scan_ms = sum(a_.elapsed_time(b_) for a_, b_ in scan_evs) / len(scan_evs) if n_csa else None
     print("# timed %d steps: %.3f ms/step (wall %.3f ms/step)" % (args.steps, ms_step, 1e3 * wall / args.steps),
           file=sys.stderr, flush=True)
     # Untimed pass of K steps, each step bracketed by its own events: the
@@ -1051,6 +1066,10 @@ def main():
     idx_bytes = st.index_bytes() * st.B
     idx_gbps = idx_bytes / (idx_ms * 1e-3) / 1e9
     traffic = counter_traffic(INDEX_TOPK_SOURCES, st.B)
+    # the scan kernel alone: the visible keys, the query blocks and head weights
+    scan_bytes = (st.nv_csa * st.dI * st.ieb + st.HI * st.dI * st.ieb + st.HI * 4) * st.B
+    scan_gbps = scan_bytes / (scan_ms * 1e-3) / 1e9
+    scan_traffic = counter_traffic(INDEX_TOPK_SOURCES, st.B, key="index_score_stream_hbm_bytes_per_launch")
 
     del state
     torch.cuda.empty_cache()
@@ -1139,11 +1158,19 @@ def main():
         },
         "hbm": {"algorithmic_bytes_per_step": st.step_bytes(), "achieved_GBps": step_gbps,
                 "frac_of_peak": step_gbps / HBM_PEAK_GBPS},
-        "roofline": {"kernel": "csa_index_topk (index_score_stream<4,true,true,0> then topk_merge_kernel)",
-                     "bound": "hbm", "achieved": idx_gbps,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": idx_gbps / HBM_PEAK_GBPS,
-                     "traffic": traffic, "avg_launch_ms": idx_ms,
-                     "algorithmic_bytes_per_launch": idx_bytes},
+        "roofline": {"kernel": "index_score_stream<4,true,true,0> (the scan of csa_index_topk, with its part "
+                               "selection)",
+                     "bound": "hbm", "achieved": scan_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": scan_gbps / HBM_PEAK_GBPS,
+                     "traffic": scan_traffic, "avg_launch_ms": scan_ms,
+                     "algorithmic_bytes_per_launch": scan_bytes,
+                     "timing": "the kernel's own start and end (hipExtLaunchKernel events), one CSA layer per step "
+                               "in turn over the timed region",
+                     "call": {"kernels": "index_score_stream<4,true,true,0> then topk_merge_kernel",
+                              "avg_ms": idx_ms, "algorithmic_bytes": idx_bytes, "achieved": idx_gbps,
+                              "frac": idx_gbps / HBM_PEAK_GBPS, "traffic": traffic,
+                              "timing": "HIP events around the call in every fourth step (a few us of idle "
+                                        "GPU at each event)"}},
         "per_call_ms": per_call,
         "per_call_note": "untimed pass with events around every call; compression runs on a second stream",
         "prefill_sparse_attn": prefill,

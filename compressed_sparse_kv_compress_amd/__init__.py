@@ -95,6 +95,7 @@ _hca_dense_attn = _sig("hca_dense_attn", [_vp] * 3 + [_i64, _i64, _vp, _vp, _i64
                        + [_i64] * 5 + [_vp, _vp, _vp, _sz, _i32, _vp])
 _csa_status_string = _sig("csa_status_string", [_i32], ctypes.c_char_p)
 _csa_last_error = _sig("csa_last_error", [], ctypes.c_char_p)
+_csa_time_next_scan = _sig("csa_time_next_scan", [_vp, _vp])
 
 
 class CsaError(RuntimeError):
@@ -415,3 +416,17 @@ def hca_dense_attn(q, kc, vc, m, *, kr=None, vr=None, W=0, sink=None, scale=None
     else:
         _check(_hca_dense_attn_ex(_lay(layout), *args), "hca_dense_attn_ex")
     return (out, lse) if want_lse else out
+
+
+def time_next_scan(start, stop):
+    """The next indexer scan kernel launched from this thread records the
+    torch.cuda.Event pair `start` / `stop` (created with enable_timing=True)
+    as it starts and ends; start.elapsed_time(stop) is then that kernel's
+    duration.  None, None clears a pending request."""
+    if start is None and stop is None:
+        _check(_csa_time_next_scan(None, None), "csa_time_next_scan")
+        return
+    for e in (start, stop):
+        if e.cuda_event == 0:  # torch creates the event on its first record
+            e.record()
+    _check(_csa_time_next_scan(start.cuda_event, stop.cuda_event), "csa_time_next_scan")

@@ -562,6 +562,12 @@ const char* csa_status_string(csa_status_t status) {
   return "CSA_ERR_UNKNOWN";
 }
 
+csa_status_t csa_time_next_scan(void* start_event, void* stop_event) {
+  REQUIRE((start_event == nullptr) == (stop_event == nullptr), "give both events or neither");
+  csa::time_next_scan(static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
+  return CSA_OK;
+}
+
 const char* csa_last_error(void) { return g_err; }
 
 }  // extern "C"

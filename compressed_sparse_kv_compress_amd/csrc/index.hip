@@ -20,6 +20,8 @@
 // weighted head sum are in-register FMAs plus two lane exchanges; the
 // epilogue writes 16 fp32 scores (64 B) per tile.  The grid is about one
 // workgroup per CU, so every wavefront streams megabytes with one prologue.
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "merge.hpp"
@@ -1044,6 +1046,22 @@ void index_plan(int64_t nrows, int64_t L, int64_t* parts_out, int64_t* per_wave_
 
 namespace {
 
+// Timing request for the next streaming scan launched by this host thread:
+// its kernel records these events as it starts and ends (hipExtLaunchKernel
+// stamps the dispatch itself, so no event packet sits between kernels).
+thread_local hipEvent_t t_scan_start = nullptr, t_scan_stop = nullptr;
+
+template <typename K>
+void launch_scan_kernel(K kern, dim3 grid, dim3 block, hipStream_t s, const IndexScoreArgs& a, int64_t parts,
+                        int64_t per_wave, const IndexCandidates& co) {
+  if (t_scan_start != nullptr && t_scan_stop != nullptr) {
+    hipExtLaunchKernelGGL(kern, grid, block, 0, s, t_scan_start, t_scan_stop, 0, a, parts, per_wave, co);
+    t_scan_start = t_scan_stop = nullptr;
+  } else {
+    hipLaunchKernelGGL(kern, grid, block, 0, s, a, parts, per_wave, co);
+  }
+}
+
 template <bool TOPK>
 hipError_t launch_stream(const IndexScoreArgs& a, const IndexCandidates& co, hipStream_t s) {
   int64_t parts, per_wave;
@@ -1052,10 +1070,10 @@ hipError_t launch_stream(const IndexScoreArgs& a, const IndexCandidates& co, hip
   const int mb = static_cast<int>(a.HI / 16);
   const bool w = a.w != nullptr;
   const int kf = a.dt == kMXFP4 ? 2 : (a.dt == kFP8 ? 1 : 0);
-#define CSA_INDEX_KF(MB_, KF_)                                                                                     \
-  if (w) hipLaunchKernelGGL((index_score_stream<MB_, true, TOPK, KF_>), grid, dim3(KF_ ? 64 * kWaves8 : 256), 0, s, a,   \
-                            parts, per_wave, co);                                                                     \
-  else hipLaunchKernelGGL((index_score_stream<MB_, false, TOPK, KF_>), grid, dim3(KF_ ? 64 * kWaves8 : 256), 0, s, a, \
+#define CSA_INDEX_KF(MB_, KF_)                                                                                    \
+  if (w) launch_scan_kernel(index_score_stream<MB_, true, TOPK, KF_>, grid, dim3(KF_ ? 64 * kWaves8 : 256), s, a,   \
+                            parts, per_wave, co);                                                                    \
+  else launch_scan_kernel(index_score_stream<MB_, false, TOPK, KF_>, grid, dim3(KF_ ? 64 * kWaves8 : 256), s, a,    \
                           parts, per_wave, co);
 #define CSA_INDEX_LAUNCH(MB_)                  \
   case MB_:                                    \
@@ -1076,6 +1094,11 @@ hipError_t launch_stream(const IndexScoreArgs& a, const IndexCandidates& co, hip
 }
 
 }  // namespace
+
+void time_next_scan(hipEvent_t start, hipEvent_t stop) {
+  t_scan_start = start;
+  t_scan_stop = stop;
+}
 
 hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t s) {
   if (a.nrows == 0 || a.L == 0) return hipSuccess;

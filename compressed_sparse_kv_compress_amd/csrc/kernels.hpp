@@ -84,6 +84,9 @@ struct IndexScoreArgs {
   SeqLayout lay;      // per-sequence lengths, paged keys
 };
 hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t s);
+// The next streaming index scan this host thread launches records start and
+// stop as its kernel starts and ends; the request is then cleared.
+void time_next_scan(hipEvent_t start, hipEvent_t stop);
 
 // Per-part top-k candidates: part p of row r keeps ccnt[r][p] <= cap
 // (score, index) pairs in index order at [r][p][0 ..]; slots past them hold

@@ -341,6 +341,15 @@ csa_status_t hca_dense_attn_ex(const csa_layout_t* layout, const void* q, const 
                                float* lse, void* ws, size_t ws_bytes, csa_dtype_t dtype,
                                void* stream);
 
+/* csa_time_next_scan -- instrumentation: the next indexer scan kernel that a
+ * csa_index_score / csa_index_topk call on this host thread launches records
+ * start_event (hipEvent_t) as the kernel starts and stop_event as it ends
+ * (both stamped by the kernel's own dispatch, so no event command sits
+ * between the call's kernels); the request then clears.  Both NULL clears a
+ * pending request.  The events belong to the caller and must exist on the
+ * scan's device; the call itself enqueues nothing. */
+csa_status_t csa_time_next_scan(void* start_event, void* stop_event);
+
 /* Status names and the calling thread's last error detail (never NULL). */
 const char* csa_status_string(csa_status_t status);
 const char* csa_last_error(void);
