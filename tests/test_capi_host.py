@@ -235,3 +235,12 @@ def test_noalloc_rejects_rows_beyond_its_scratch(lib):
     # batch 0: nothing to do
     assert _call(lib, "csa_index_topk_noalloc", args, None, None, None, 0, 1, 100, 25, 64, 128, 4, 8,
                  None, None, 1, None) == 0
+
+
+def test_time_next_scan_takes_both_events_or_neither(lib):
+    """The scan-timing request needs an event pair; NULL, NULL clears it and
+    enqueues nothing (no GPU needed)."""
+    args = [V, V]
+    assert _call(lib, "csa_time_next_scan", args, FAKE, None) == 1
+    assert _call(lib, "csa_time_next_scan", args, None, FAKE) == 1
+    assert _call(lib, "csa_time_next_scan", args, None, None) == 0
