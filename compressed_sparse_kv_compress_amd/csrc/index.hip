@@ -355,8 +355,8 @@ __device__ __forceinline__ void part_list(const IndexCandidates& co, int64_t slo
   const int wave = tid >> 6;
   const uint32_t r = static_cast<uint32_t>(co.lrank);
   uint32_t* hist = reinterpret_cast<uint32_t*>(scratch);  // two sets of 256 bins
-  uint32_t* pick = hist + 512;                             // per set: digit, entries above it
-  uint32_t* wsum = pick + 4;                               // per-wavefront counts
+  uint32_t* pick = hist + 512;                             // per set: digit, entries above it, entries in it
+  uint32_t* wsum = pick + 8;                               // per-wavefront counts
   float x[IT];
   uint32_t key[IT];
   uint32_t valid = 0;
@@ -367,10 +367,14 @@ __device__ __forceinline__ void part_list(const IndexCandidates& co, int64_t slo
     key[j] = float_key(x[j]);
     valid |= static_cast<uint32_t>(o < n) << j;
   }
-  uint32_t kth = 0;  // key of the r-th largest score (0: keep every valid entry)
-  if (static_cast<uint32_t>(n) > r) {
+  const bool keep_all = static_cast<uint32_t>(n) <= r;
+  uint32_t kth = 0;  // every valid key >= kth is listed
+  if (!keep_all) {
     // four 8-bit digits, most significant first; bins double-buffered so
-    // that one pass's counting can follow the previous pass's search
+    // that one pass's counting can follow the previous pass's search.  When
+    // the chosen bin holds exactly the entries still needed, every key at or
+    // above the bin's lowest key is listed and the search stops there (V is
+    // then that lower bound, at most the r-th largest score).
     uint32_t prefix = 0, mask = 0, need = r;
     hist[tid] = 0;
     __syncthreads();
@@ -390,23 +394,25 @@ __device__ __forceinline__ void part_list(const IndexCandidates& co, int64_t slo
 #pragma unroll
         for (int q = 3; q >= 0; --q) {
           if (above < need && above + c[q] >= need) {
-            pick[2 * (pass & 1)] = static_cast<uint32_t>(252 - 4 * lane + q);
-            pick[2 * (pass & 1) + 1] = above;
+            pick[4 * (pass & 1)] = static_cast<uint32_t>(252 - 4 * lane + q);
+            pick[4 * (pass & 1) + 1] = above;
+            pick[4 * (pass & 1) + 2] = c[q];
           }
           above += c[q];
         }
       }
       __syncthreads();
-      prefix |= pick[2 * (pass & 1)] << shift;
+      prefix |= pick[4 * (pass & 1)] << shift;
       mask |= 255u << shift;
-      need -= pick[2 * (pass & 1) + 1];
+      need -= pick[4 * (pass & 1) + 1];
+      if (pick[4 * (pass & 1) + 2] == need) break;  // uniform: every entry of the bin is listed
     }
     kth = prefix;
   }
   // ordered compaction of the entries with key >= kth
   uint32_t keep = 0;
 #pragma unroll
-  for (int j = 0; j < IT; ++j) keep |= static_cast<uint32_t>(((valid >> j) & 1) && key[j] >= kth) << j;
+  for (int j = 0; j < IT; ++j) keep |= static_cast<uint32_t>(((valid >> j) & 1) && (keep_all || key[j] >= kth)) << j;
   const uint32_t cnt = static_cast<uint32_t>(__builtin_popcount(keep));
   const uint32_t incl = sel::wave_incl_scan(cnt);
   if (lane == 63) wsum[wave] = incl;
@@ -432,7 +438,7 @@ __device__ __forceinline__ void part_list(const IndexCandidates& co, int64_t slo
   }
   if (tid == 0) {
     co.lcnt[slot] = fits ? static_cast<int32_t>(total) : -1;
-    co.lthr[slot] = kth == 0 ? -INFINITY : key_float(kth);
+    co.lthr[slot] = keep_all ? -INFINITY : key_float(kth);
   }
 }
 
