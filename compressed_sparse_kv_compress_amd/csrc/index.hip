@@ -344,12 +344,16 @@ __device__ __forceinline__ void part_select(const IndexCandidates& co, int64_t s
 // order-preserving keys, four 8-bit digits (one wavefront reads 4 bins per
 // lane with one 16-byte LDS read); the bins and the per-pass results live in
 // the idle tile ring.
+// Two size classes: ranges of up to 1,024 keys (batch 1 at 1M, batch 8 at
+// 131,072) and up to 4,096 (batch 2 and 4 at 1M).
 constexpr int kListPartKeys = 1024;
-template <int NW>
+constexpr int kListPartKeysMax = 4096;
+template <int NW, int KEYS>
 __device__ __forceinline__ void part_list(const IndexCandidates& co, int64_t slot, int64_t kb, int n,
                                           const float (*sbuf)[kScoreSlots<NW>], uint8_t* scratch) {
   constexpr int NT = 64 * NW;
-  constexpr int IT = kListPartKeys / NT;  // entries per thread: 4 (bf16) or 2 (eight wavefronts)
+  constexpr int IT = KEYS / NT;  // entries per thread (4 or 16 with four wavefronts, half with eight)
+  static_assert(IT >= 1 && IT <= 32 && KEYS % NT == 0, "entries per thread fit the 32-bit masks");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -717,9 +721,14 @@ __global__ __launch_bounds__(64 * (KF ? kWaves8 : kWaves), 1) void index_score_s
         if (o + e < nk) dst[o + e] = x[e];
     }
   }
-  // listed path (parts of at most kListPartKeys keys): the part's exact list
-  if (co.lval != nullptr)
-    part_list<NW>(co, lrow * parts + part, kb, ntiles > 0 ? static_cast<int>(kv - kb) : 0, sbuf, &ring[0][0][0]);
+  // listed path (ranges of at most kListPartKeysMax keys): the range's exact list
+  if (co.lval != nullptr) {
+    const int nvis = ntiles > 0 ? static_cast<int>(kv - kb) : 0;
+    if (nk <= kListPartKeys)
+      part_list<NW, kListPartKeys>(co, lrow * parts + part, kb, nvis, sbuf, &ring[0][0][0]);
+    else
+      part_list<NW, kListPartKeysMax>(co, lrow * parts + part, kb, nvis, sbuf, &ring[0][0][0]);
+  }
 }
 
 // Prefill scoring (bf16, FP8 or MXFP4, d_I = 128): a workgroup takes 16 query
@@ -1223,7 +1232,7 @@ static void listed_plan(int64_t nrows, int64_t L, int64_t k, int64_t* parts, int
   int64_t per_wave;
   index_plan(nrows, L, parts, &per_wave);
   *r = kMergeUnion / *parts;
-  if (kWaves * per_wave > kListPartKeys || *parts > 512 || *r * *parts < k || *r < 2 * ((k + *parts - 1) / *parts) ||
+  if (kWaves * per_wave > kListPartKeysMax || *parts > 512 || *r * *parts < k || *r < 2 * ((k + *parts - 1) / *parts) ||
       2 * k > mrg::kStage)
     *r = 0;
 }

@@ -163,7 +163,7 @@ bool index_multi_rows(int64_t T, int64_t HI, int64_t row0, int64_t nrows);
 bool index_topk_fusable(int64_t nrows, int64_t L, int64_t HI, int64_t dI, int64_t k, Dt dt);
 size_t index_topk_fused_ws_bytes(int64_t nrows, int64_t L, int64_t k);
 // Listed path, for decode shapes with more parts than the fused path takes
-// (one query at 1M entries, or 8 at 131,072): the scan writes the scores and
+// (1, 2 or 4 queries at 1M entries, 8 at 131,072): the scan writes the scores and
 // each part's exact top-r list (r = kMergeUnion / parts per row); one
 // workgroup per row merges the lists, and only rows whose lists do not
 // settle them go through the stand-alone top-k on the written scores.

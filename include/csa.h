@@ -223,8 +223,8 @@ csa_status_t csa_topk_select(const float* score, int64_t B, int64_t T, int64_t n
  * results bit for bit.  For bf16, d_I = 128 and decode-like shapes (the scan's
  * key ranges times k at most 16384, k <= 2048) with a full-size workspace the
  * scan keeps each key range's top-k candidates itself and no score matrix is
- * written (two kernels); decode shapes with more key ranges (one query at
- * 1M entries, eight at 131,072) write the scores and each key range's exact
+ * written (two kernels); decode shapes with more key ranges (one to four
+ * queries at 1M entries, eight at 131,072) write the scores and each key range's exact
  * short list, merge the lists per query and run the stand-alone selection
  * only for queries whose lists do not settle them (same results); otherwise
  * the fp32 score matrix and the selection scratch are kept in the caller's
