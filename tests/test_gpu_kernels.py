@@ -450,3 +450,21 @@ def test_index_topk_prefill_rows_match_oracle():
         nv = min(L, (n_ctx - T + t) // m)
         ties += near_tie_check(got[0, t], want[0, t], sc[0, t], nv, k, index_eps(q_c[0, t], None, k_c[0])[:nv])
     assert ties <= 1
+
+
+def test_timed_scan_launch_gives_the_same_selection():
+    """A scan launched with csa_time_next_scan's event pair (hipExtLaunchKernel)
+    selects exactly what the ordinary launch selects, and its events time it."""
+    B, T, L, HI, dI, m, k = 16, 1, 250000, 64, 128, 4, 1024
+    n_ctx = m * L
+    q, _ = both((B, T, HI, dI), 91, "q_idx", dtype=torch.bfloat16, scale=dI ** -0.5)
+    kk, _ = both((B, L, dI), 91, "k_idx", dtype=torch.bfloat16, scale=dI ** -0.5)
+    idx1 = csa.csa_index_topk(q, kk, m, k, n_ctx=n_ctx)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    csa.time_next_scan(start, stop)
+    idx2 = csa.csa_index_topk(q, kk, m, k, n_ctx=n_ctx)
+    torch.cuda.synchronize()
+    assert torch.equal(idx1, idx2)
+    ms = start.elapsed_time(stop)
+    assert 0.0 < ms < 100.0
+    csa.time_next_scan(None, None)  # nothing pending afterwards
